@@ -1,0 +1,183 @@
+"""Pins for the KIVI oracle: the KIVI page's stated figures, hand-worked
+quantizer cases, bounds, the residual-window rules and the joint softmax.  CPU only."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import kivi as kv
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_memory_formula_matches_page():
+    g = _golden("accounting.json")["kivi_memory_formula"]
+    per_tok = kv.kv_cache_bytes(g["n_layer"], g["h_kv"], g["d_head"], 1, g["bytes_per_elem"])
+    assert per_tok == g["bytes_per_token"]
+    assert kv.kv_cache_bytes(g["n_layer"], g["h_kv"], g["d_head"], 4096, 2) == g["bytes_4k_request"]
+    assert 16 * kv.kv_cache_bytes(g["n_layer"], g["h_kv"], g["d_head"], 4096, 2) == g["bytes_4k_batch16"]
+
+
+def test_bytes_per_element_matches_page():
+    g = _golden("accounting.json")["kivi_bytes_per_element"]
+    assert kv.bytes_per_element(g["bits"], g["group"], g["param_bytes"]) == g["bytes"]
+
+
+@pytest.mark.parametrize("case", _golden("kivi_quantizer_cases.json")["cases"], ids=lambda c: c["name"])
+def test_hand_worked_groups(case):
+    x = np.array(case["x"], dtype=np.float16)
+    s, z = kv.group_params(x)
+    assert float(s) == case["s"] and float(z) == case["z"]
+    if "s_hex" in case:
+        assert int(np.array([s], dtype=np.float16).view(np.uint16)[0]) == int(case["s_hex"], 16)
+    codes = kv.quantize(x, s, z)
+    assert codes.tolist() == case["codes"]
+    assert kv.dequantize(codes, s, z).tolist() == case["x_hat"]
+
+
+def _groups(seed, n=2000, size=32, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((n, size)) * scale).astype(np.float16)
+
+
+@pytest.mark.parametrize("scale", [1.0, 20.0, 1e-3])
+def test_codes_in_range_and_error_bound(scale):
+    """Every code lies in [0, 3]; |x - x_hat| <= s/2 + s|z - z_exact| + a few
+    ulps, where z_exact = -min/s before fp16 rounding."""
+    for x in _groups(1, scale=scale):
+        s, z = kv.group_params(x)
+        q = kv.quantize(x, s, z)
+        assert q.min() >= 0 and q.max() <= 3
+        xh = kv.dequantize(q, s, z).astype(np.float64)
+        xf = x.astype(np.float64)
+        z_exact = -xf.min() / float(s)
+        bound = float(s) / 2 + float(s) * abs(float(z) - z_exact) + 4e-7 * (abs(xf).max() + float(s))
+        assert np.abs(xf - xh).max() <= bound
+
+
+def test_end_points_map_to_extreme_codes():
+    """min -> 0 and max -> 3 unless fp16 rounding of z moves the value across a
+    rounding boundary (checked by recomputing with the exact z)."""
+    n_checked = 0
+    for x in _groups(2):
+        s, z = kv.group_params(x)
+        q = kv.quantize(x, s, z)
+        xf = x.astype(np.float32)
+        u_min = np.float32(np.float32(xf.min()) / np.float32(s)) + np.float32(z)
+        u_max = np.float32(np.float32(xf.max()) / np.float32(s)) + np.float32(z)
+        if abs(u_min) < 0.49:
+            assert q[np.argmin(xf)] == 0
+            n_checked += 1
+        if abs(u_max - 3) < 0.49:
+            assert q[np.argmax(xf)] == 3
+    assert n_checked > 1500
+
+
+def test_exactly_representable_group_is_lossless():
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        s = float(2.0 ** rng.integers(-4, 4))
+        a = float(rng.integers(-8, 8)) * s     # min on the grid so z = -a/s is an integer
+        levels = np.array([0, 1, 2, 3])
+        x = (a + s * rng.choice(levels, size=32)).astype(np.float16)
+        x[0], x[1] = a, a + 3 * s            # make min and max exact
+        s16, z16 = kv.group_params(x)
+        q = kv.quantize(x, s16, z16)
+        np.testing.assert_array_equal(kv.dequantize(q, s16, z16), x.astype(np.float32))
+
+
+def test_round_half_to_even():
+    """x/s + z landing exactly on k + 1/2 rounds to the even neighbour."""
+    x = np.array([0.0, 0.5, 1.5, 2.5, 3.0], dtype=np.float16)
+    s, z = kv.group_params(x)
+    assert kv.quantize(x, s, z).tolist() == [0, 0, 2, 2, 3]
+
+
+def test_key_and_value_grouping_directions():
+    """Keys share (s, z) down a column of `group` tokens; values along a row of
+    `group` channels.  A key outlier channel only changes its own column's
+    scale; a value outlier only its own row's."""
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((64, 128)).astype(np.float16)
+    k2 = k.copy()
+    k2[:, 5] *= 20
+    _, s1, _ = kv.quantize_keys(k)
+    _, s2, _ = kv.quantize_keys(k2)
+    assert s1.shape == (2, 128)
+    changed = np.nonzero((s1 != s2).any(axis=0))[0]
+    assert changed.tolist() == [5]
+    v = rng.standard_normal((10, 128)).astype(np.float16)
+    v2 = v.copy()
+    v2[3, 40] = 50
+    _, t1, _ = kv.quantize_values(v)
+    _, t2, _ = kv.quantize_values(v2)
+    assert t1.shape == (10, 4)
+    assert np.argwhere(t1 != t2).tolist() == [[3, 1]]
+
+
+def _state(L, seed=5, D=128, R=128, group=32):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((L, D)).astype(np.float16)
+    v = rng.standard_normal((L, D)).astype(np.float16)
+    st = kv.KiviState(D=D, R=R, group=group)
+    st.prefill(k, v)
+    return st, k, v, rng
+
+
+def test_prefill_split_matches_pseudo_code():
+    """Prefill keeps the last R tokens fp16 (pseudo-code: X_K[:l-R] grouped,
+    X_K[l-R:] residual); at L = 4096, R = 128 both quantized parts hold 3968 tokens."""
+    st, _, _, _ = _state(4096, D=32)
+    assert st.n_kq == 3968 and len(st.k_res) == 128
+    assert st.n_vq == 3968 and len(st.v_res) == 128
+    st, _, _, _ = _state(300, D=32)          # (L - R) not a multiple of the group
+    assert st.n_kq == 160 and len(st.k_res) == 140 and st.n_vq == 172 and len(st.v_res) == 128
+    st, _, _, _ = _state(100, D=32)          # shorter than the residual
+    assert st.n_kq == 0 and st.n_vq == 0 and len(st.k_res) == 100
+
+
+def test_decode_appends_follow_flush_rules():
+    st, _, _, rng = _state(300, D=32)
+    for step in range(400):
+        st.append(rng.standard_normal(32).astype(np.float16), rng.standard_normal(32).astype(np.float16))
+        assert len(st.k_res) < st.R            # keys flush whole groups once R rows are waiting
+        assert st.n_kq % st.group == 0
+        assert len(st.v_res) == st.R           # values keep exactly the newest R rows
+        assert st.length == 300 + step + 1 == st.n_vq + len(st.v_res)
+
+
+def test_residual_only_state_is_plain_attention():
+    st, k, v, rng = _state(100)
+    q = rng.standard_normal(128)
+    o, lse = kv.attention(q, st, 1 / math.sqrt(128))
+    s = k.astype(np.float64) @ q / math.sqrt(128)
+    w = np.exp(s - s.max())
+    np.testing.assert_allclose(o, w @ v.astype(np.float64) / w.sum(), atol=1e-13)
+    assert abs(lse - (s.max() + math.log(w.sum()))) < 1e-12
+
+
+def test_joint_softmax_equals_merged_segments_and_differs_from_separate():
+    st, _, _, rng = _state(700)
+    q = rng.standard_normal(128) * 2
+    o, lse = kv.attention(q, st, 1 / math.sqrt(128))
+    keys, vals = st.keys(), st.values()
+    parts = []
+    for sl in (slice(0, 300), slice(300, 700)):
+        s = keys[sl] @ q / math.sqrt(128)
+        w = np.exp(s - s.max())
+        parts.append(((w @ vals[sl]) / w.sum(), s.max() + math.log(w.sum())))
+    M = max(p[1] for p in parts)
+    lse2 = M + math.log(sum(math.exp(p[1] - M) for p in parts))
+    o2 = sum(math.exp(p[1] - lse2) * p[0] for p in parts)
+    np.testing.assert_allclose(o, o2, atol=1e-12)
+    assert abs(lse - lse2) < 1e-12
+    bad = kv.attention_per_segment_softmax(q, st, 1 / math.sqrt(128))
+    assert np.abs(bad - o).max() > 1e-2
