@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of LoopVQ quantized-KV decode attention on one MI355X.
+
+Workload: 0.5 bit per element (T=4 loop steps, T_c=2, G=16, K=256 bf16
+codebooks), batch 64, 16 heads, 6144-token context with 8 sinks and a
+64-token recent window in bf16 and 759 index pages per request, seeded
+synthetic data (the LoopVQ page's "method steps" step 5 quotes its
+two-requests-per-block saving at this batch and context).
+
+One step is one decode step of a model with `--layers` attention layers that
+each own an independent copy of that cache: for each of the T loop steps,
+every layer runs lvq_decode_attn (index-page partial, bf16-window partial,
+logsumexp merge).  Rotating over the copies (3.4 GB) keeps the 256 MB
+Infinity Cache from serving repeated reads, as layers would in a real model.
+
+Printed: one JSON line with the whole-call rate (algorithmic GB/s, fraction
+of the 8 TB/s HBM peak, token-heads/s), the roofline entry of the dominant
+kernel (the index-page partial, timed alone with HIP events on the stream it
+runs on), and the fp64 oracle timed on a bounded sample on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+WORKLOAD = "loopvq-b64-6k"
+METRIC = "quantized-KV decode attention HBM GB/s (% of peak) + token-heads/s, B=64 6K"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def call_bytes(g, lengths, max_len, cb_bytes):
+    """Algorithmic bytes of one lvq_decode_attn call, split by stream."""
+    from decode_attention_loopvq_amd.layout import index_groups, n_index_pages
+    NG = index_groups(g)
+    idx = win = pt = 0
+    for L in lengths:
+        n = n_index_pages(L, g)
+        nq = g.page * n
+        idx += g.H * nq * 2 * NG                      # K and V index rows
+        win += g.H * (L - nq) * 2 * g.D * 2           # bf16 K and V of sinks + recent tokens
+        pt += 4 * n                                   # page ids
+    cb = g.H * 2 * g.K * g.D * cb_bytes               # the step's K and V slices
+    rope = max_len * g.D * 4                          # cos + sin fp32
+    qo = len(lengths) * g.H * g.D * (2 + 4)           # bf16 q in, fp32 out
+    return {"index": idx, "window": win, "page_table": pt, "codebook": cb, "rope": rope, "q_out": qo}
+
+
+def quant_kernel_bytes(g, lengths, cb_bytes, splits):
+    """Algorithmic bytes of one index-page partial launch: index rows, page ids,
+    codebook slices, cos/sin of the paged positions, q, and the partials written."""
+    from decode_attention_loopvq_amd.layout import index_groups, n_index_pages
+    NG = index_groups(g)
+    idx = pt = 0
+    max_q = 0
+    for L in lengths:
+        n = n_index_pages(L, g)
+        idx += g.H * g.page * n * 2 * NG
+        pt += 4 * n
+        max_q = max(max_q, g.page * n)
+    cb = g.H * 2 * g.K * g.D * cb_bytes
+    rope = max_q * g.D * 4
+    q = len(lengths) * g.H * g.D * 2
+    parts = len(lengths) * g.H * splits * (g.D + 1) * 4
+    return idx + pt + cb + rope + q + parts
+
+
+def cpu_baseline(prob, rows, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import loopvq as lv
+    from tests import harness
+
+    cfg = prob.cfg
+    geo = lv.Geometry(D=cfg.D, T=cfg.T, Tc=cfg.Tc, G=cfg.G, K=cfg.K, sink=cfg.sink, window=cfg.window,
+                      page=cfg.page)
+    prepared = []
+    with threadpool_limits(limits=1):
+        for (b, h) in rows:
+            L = prob.lengths[b]
+            E_k, E_v = harness.host_codebooks(prob, h, "k"), harness.host_codebooks(prob, h, "v")
+            raw_k, raw_v = prob.raw[("k", b, h)], prob.raw[("v", b, h)]
+            idx_k = lv.encode_request(raw_k, E_k, geo, L)
+            idx_v = lv.encode_request(raw_v, E_v, geo, L)
+            q = prob.q[:, b, h].float().cpu().numpy().astype(np.float64)
+            prepared.append((L, q, raw_k, raw_v, idx_k, idx_v, E_k, E_v))
+        n_rows = 0
+        t0 = time.perf_counter()
+        while True:
+            for (L, q, raw_k, raw_v, idx_k, idx_v, E_k, E_v) in prepared:
+                for t in range(cfg.T):
+                    lv.decode_step(q[t], t, raw_k, raw_v, idx_k, idx_v, E_k, E_v, geo, L, prob.sm_scale,
+                                   cfg.rope_base)
+                    n_rows += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return n_rows, el
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=6, help="independent cache copies rotated through")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the path "
+              "shards by (request, head) with no exchange, so N GPUs run N independent copies of this "
+              "benchmark.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_loopvq_amd as lvq
+    from decode_attention_loopvq_amd._lib import lib
+    from synth.configs import loopvq_config
+    from tests import harness
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = loopvq_config(WORKLOAD)
+    sample_rows = [(0, 0), (37, 9)]
+    log(f"[bench] building {WORKLOAD}: B={cfg.B} H={cfg.H} L={cfg.L} T={cfg.T} Tc={cfg.Tc} G={cfg.G}")
+    t0 = time.perf_counter()
+    prob = harness.build_loopvq(cfg, keep=[] if args.no_cpu_baseline else sample_rows)
+    g, cache = prob.g, prob.cache
+    log(f"[bench] built in {time.perf_counter() - t0:.1f}s; copying to {args.layers} layers")
+    pools = [cache.pool] + [cache.pool.clone() for _ in range(args.layers - 1)]
+    wks = [cache.win_k] + [cache.win_k.clone() for _ in range(args.layers - 1)]
+    wvs = [cache.win_v] + [cache.win_v.clone() for _ in range(args.layers - 1)]
+    B = cfg.B
+    S = args.num_splits or lvq.lvq_decode_attn_splits(g, B, cache.max_len)
+    ws_bytes = lvq.lvq_decode_attn_workspace(g, B, cache.max_len, S)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((B, g.H, g.D), dtype=torch.float32, device="cuda") for _ in range(args.layers)]
+    qs = [prob.q[t].contiguous() for t in range(cfg.T)]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    gref = C.byref(g)
+    rope_len = prob.rope_cos.shape[0]
+
+    def full_args(t, l):
+        return (gref, t, qs[t].data_ptr(), pools[l].data_ptr(), cache.page_table.data_ptr(),
+                int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, wks[l].data_ptr(),
+                wvs[l].data_ptr(), prob.slices.data_ptr(), prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(),
+                rope_len, C.c_float(prob.sm_scale), outs[l].data_ptr(), None, ws.data_ptr(), ws_bytes, S, B, sh)
+
+    calls = [full_args(t, l) for t in range(cfg.T) for l in range(args.layers)]
+
+    def one_step():
+        for a in calls:
+            st = lib.lvq_decode_attn(*a)
+            if st != 0:
+                raise RuntimeError(lib.lvq_last_error().decode())
+
+    # Dominant kernel alone: the index-page partial into the same workspace.
+    rows_tot = B * g.H * (S + 1)
+    part_o = ws.view(torch.float32)[: rows_tot * g.D]
+    part_lse = ws.view(torch.float32)[rows_tot * g.D: rows_tot * (g.D + 1)]
+
+    def quant_args(t, l):
+        return (gref, t, qs[t].data_ptr(), pools[l].data_ptr(), cache.page_table.data_ptr(),
+                int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, prob.slices.data_ptr(),
+                prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(), rope_len, C.c_float(prob.sm_scale),
+                part_o.data_ptr(), part_lse.data_ptr(), S, S + 1, B, sh)
+
+    qcalls = [quant_args(t, l) for t in range(cfg.T) for l in range(args.layers)]
+
+    def quant_only():
+        for a in qcalls:
+            st = lib.lvq_quant_partial(*a)
+            if st != 0:
+                raise RuntimeError(lib.lvq_last_error().decode())
+
+    log(f"[bench] warmup {args.warmup} steps ({len(calls)} calls each, num_splits={S})")
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    log(f"[bench] timed {args.steps} steps: {ms_total:.3f} ms")
+
+    # The dominant kernel alone, same rotation.
+    for _ in range(2):
+        quant_only()
+    torch.cuda.synchronize()
+    q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    q0.record(stream)
+    for _ in range(args.steps):
+        quant_only()
+    q1.record(stream)
+    torch.cuda.synchronize()
+    ms_quant = q0.elapsed_time(q1) / (args.steps * len(qcalls))
+    log(f"[bench] index-page partial alone: {ms_quant * 1e3:.2f} us per launch")
+
+    cb_bytes = 2 if cfg.cb_dtype == "bf16" else 4
+    parts = call_bytes(g, prob.lengths, cache.max_len, cb_bytes)
+    per_call = sum(parts.values())
+    n_calls = args.steps * len(calls)
+    sec = ms_total / 1e3
+    gbps = per_call * n_calls / sec / 1e9
+    token_heads = sum(prob.lengths) * g.H
+    qbytes = quant_kernel_bytes(g, prob.lengths, cb_bytes, S)
+    q_gbps = qbytes / (ms_quant / 1e3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_total / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD, "B": cfg.B, "H": cfg.H, "L": cfg.L, "T": cfg.T, "Tc": cfg.Tc, "G": cfg.G,
+            "K": cfg.K, "codebook": cfg.cb_dtype, "sink": cfg.sink, "window": cfg.window, "page": cfg.page,
+            "layers_rotated": args.layers, "calls_per_step": len(calls), "num_splits": S,
+            "requests_per_workgroup": 2,
+        },
+        "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+        "token_heads_per_s": round(token_heads * n_calls / sec, 1),
+        "us_per_call": round(ms_total * 1e3 / n_calls, 2),
+        "bytes_per_call": parts,
+        "roofline": {
+            "kernel": "quant_partial_kernel (index-page partial)",
+            "bound": "hbm",
+            "achieved": round(q_gbps, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+            "us_per_launch": round(ms_quant * 1e3, 2),
+            "algorithmic_bytes_per_launch": qbytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: fp64 oracle on {len(sample_rows)} rows, about {args.cpu_seconds:.0f}s")
+        n_rows, el = cpu_baseline(prob, sample_rows, args.cpu_seconds)
+        share = per_call / (B * g.H)
+        result["cpu_baseline"] = {
+            "value": round(n_rows * share / el / 1e9, 6),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_rows} (request, head, loop step) rows of {WORKLOAD} from requests/heads {sample_rows}, "
+                      f"attention over the cache only (indices from the oracle's own encode, not timed), "
+                      f"{el:.1f}s single-threaded; bytes per row = 1/(B*H) of one call",
+            "token_heads_per_s": round(n_rows * cfg.L / el, 1),
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

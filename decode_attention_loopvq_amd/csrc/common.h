@@ -1,0 +1,86 @@
+// Internal helpers shared by the liblvq sources (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "lvq.h"
+
+namespace lvq {
+
+// ---------------------------------------------------------------------------
+// Error reporting: every entry point validates, sets a thread-local message
+// and returns a status before launching anything.
+// ---------------------------------------------------------------------------
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define LVQ_REQUIRE(cond, status, ...)          \
+    do {                                        \
+        if (!(cond)) {                          \
+            ::lvq::set_error(__VA_ARGS__);      \
+            return (status);                    \
+        }                                       \
+    } while (0)
+
+// Check the launch that was just enqueued.
+lvq_status check_launch(const char* what);
+
+// ---------------------------------------------------------------------------
+// Device-side scalar conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    _Float16 v;
+    __builtin_memcpy(&v, &h, 2);
+    return float(v);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+    _Float16 v = (_Float16)f;   // v_cvt_f16_f32: round to nearest even
+    uint16_t h;
+    __builtin_memcpy(&h, &v, 2);
+    return h;
+}
+
+// Wave64 reductions through cross-lane moves.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+constexpr int kWave = 64;
+
+inline int ceil_div(long a, long b) { return int((a + b - 1) / b); }
+
+}  // namespace lvq
+
+namespace lvq {
+
+// LoopVQ geometry with the derived sizes every kernel uses.
+struct Geo {
+    int D, T, Tc, G, K, page, sink, W, H, cb;
+    int c;        // channels per codeword per step, G / Tc
+    int NG;       // index groups per token and step, D / c
+    int NB;       // loop blocks, T / Tc
+    int Wcap;     // window slots per (request, step, head): sink + W + page
+    long page_bytes;   // bytes of one physical pool page: NB*H*2*page*NG
+    int cb_bytes;      // bytes per codebook element
+};
+
+// Validate a caller's geometry; fills `out` on success.
+lvq_status validate_geom(const lvq_geom* g, Geo* out);
+
+}  // namespace lvq

@@ -1,0 +1,294 @@
+/*
+ * lvq.h -- C ABI of liblvq: decode attention read directly from a
+ * sub-2-bit quantized KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * Two cache formats share one engine:
+ *
+ *  - LoopVQ ("LoopVQ: Sub 1-bit KV Cache Quantization for Looped
+ *    Transformers", Cheong & Yoo).  Each (loop block, layer, head, channel
+ *    group) has a codebook of K = 256 codewords of G coordinates; one 8-bit
+ *    index covers c = G/T_c channels at each of T_c consecutive loop steps
+ *    ("method steps", step 1).  Sinks and the recent window stay bf16 at
+ *    every loop step; older tokens live as indices in 8-token pages (step 4,
+ *    Figure 5).  Loop step t rebuilds pre-RoPE keys and values through its own
+ *    slice B_t of each codeword, rotates keys by their positions, and attends;
+ *    index pages and bf16 tokens are attended separately and merged exactly
+ *    through logsumexp (step 5, Figure 5; background "SGLang and
+ *    Flash-Decoding").
+ *
+ *  - KIVI ("KIVI 完全拆解" walkthrough of KIVI): 2-bit asymmetric uniform
+ *    quantization q = clamp(round(x/s + z), 0, 3), x_hat = s (q - z) with
+ *    fp16 s and z ("definitions" section); keys per channel over groups of
+ *    32 tokens, values per token over groups of 32 channels, the newest
+ *    tokens kept fp16 in a residual window of R = 128 ("core design").
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller, unless a
+ *    parameter says "host".  The library never allocates, frees or
+ *    synchronizes; callers size buffers with the *_workspace queries.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *  - Arguments are validated before anything is launched.  On failure the
+ *    call returns a non-zero lvq_status, launches nothing, and
+ *    lvq_last_error() returns a message (thread-local) describing it.
+ *  - LVQ_ERR_HIP is returned if the launch itself fails (hipGetLastError).
+ *  - Device-side contents (lengths, page ids) are trusted: the caller
+ *    guarantees page ids < the pool's page count and lengths <= the
+ *    max_len it passes.
+ *  - Calls that write the same buffers must not overlap across streams.
+ *  - Element types: bf16 and fp16 arrays are passed as void* holding 16-bit
+ *    IEEE-style bf16 / binary16 values.
+ */
+#ifndef LVQ_H
+#define LVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LVQ_API __attribute__((visibility("default")))
+
+typedef enum {
+    LVQ_OK = 0,
+    LVQ_ERR_INVALID_ARG = 1,  /* null pointer, negative size, inconsistent geometry */
+    LVQ_ERR_UNSUPPORTED = 2,  /* a shape this build has no kernel for */
+    LVQ_ERR_WORKSPACE = 3,    /* workspace smaller than the *_workspace query */
+    LVQ_ERR_HIP = 4           /* the HIP runtime reported an error */
+} lvq_status;
+
+typedef enum { LVQ_BF16 = 0, LVQ_FP32 = 1 } lvq_dtype;
+
+/* Thread-local description of the last failure of a call on this thread. */
+LVQ_API const char* lvq_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* LoopVQ geometry                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * D       head dimension (128 supported)
+ * T       loop steps; T_c must divide T and G ("method steps", step 1)
+ * Tc      loop steps that share one index row
+ * G       codeword dimension; c = G/Tc channels per codeword per step
+ *         (c = 4 or 8 supported); NG = D/c index groups per token and step
+ * K       codewords per codebook (256: 8-bit indices)
+ * page    tokens per index page (8)
+ * sink    leading tokens kept bf16 (8)
+ * window  recent-window length W; a request of length L keeps
+ *         n_pages = max(0, (L - sink - W) / page) index pages covering
+ *         positions [sink, sink + page*n_pages) and bf16 tokens elsewhere,
+ *         so the recent part holds W .. W+page-1 tokens (step 4, Figure 5)
+ * H       KV heads (multi-head: one query head per KV head)
+ * cb_dtype  element type of codebooks and slices (LVQ_BF16 or LVQ_FP32)
+ *
+ * Memory layouts (row-major, innermost last):
+ *  codebooks  [NB=T/Tc][H][2 (0=K,1=V)][NG][K][G]          cb_dtype
+ *  slices     [T][H][2][NG][K][c]   slice[t][h][kv][g][r][i] =
+ *             codebooks[t/Tc][h][kv][g][r][i*Tc + t%Tc]       cb_dtype
+ *  pool       [P][NB][H][2][page][NG] uint8 index pages; one physical page
+ *             holds 8 tokens of one request for every block and head
+ *  page_table [B][pt_stride] int32, logical page -> physical page
+ *  window     [B][T][H][Wcap][D] bf16, Wcap = sink + W + page; pre-RoPE
+ *             K (and separately V) of every loop step; position p < sink sits
+ *             in slot p, position p >= sink in slot sink + (p - sink) % (W + page)
+ *  rope       cos, sin fp32 [rope_len][D/2]: cos/sin(p * base^(-2i/D))
+ */
+typedef struct {
+    int32_t D, T, Tc, G, K, page, sink, window, H, cb_dtype;
+} lvq_geom;
+
+/*
+ * Cut the per-step codebook slices B_t out of the full codebooks, once at
+ * load time ("method steps", step 5; Figure 3).  Layouts above.
+ */
+LVQ_API lvq_status lvq_slice_codebooks(const lvq_geom* g, const void* codebooks, void* slices,
+                               hipStream_t stream);
+
+/*
+ * RoPE table: cos_out[p][i] = fp32(cos(p * base^(-2i/D))), same for sin,
+ * for p < len, i < D/2; angles and the functions are evaluated in fp64 and
+ * rounded once (background "RoPE": keys are rotated by their position after
+ * reconstruction, with a precomputed table).  The rotation pairs channel i
+ * with channel i + D/2 (rotate-half form).
+ */
+LVQ_API lvq_status lvq_rope_table(int32_t len, int32_t D, double base, float* cos_out, float* sin_out,
+                          hipStream_t stream);
+
+/*
+ * Encode index pages of loop block `block` ("method steps", step 4; Figure 5):
+ * for each request b and each logical page lp in
+ * [first_page[b], first_page[b] + n_pages[b]), the 8 tokens of the page are
+ * coupled across the block's T_c loop steps and each coupled sub-vector is
+ * replaced by the index of its nearest codeword, argmin_r ||z - e_r||^2
+ * (ties and distances within rounding resolve to the lowest index), and
+ * written to pool page page_table[b*pt_stride + lp] at [block][h][kv].
+ * The same call serves prefill (many pages) and decode (the oldest window
+ * page, every 8 generated tokens).
+ *
+ *  x_k, x_v      bf16 pre-RoPE keys / values (either may be NULL to skip).
+ *                Element (b, h, token j, step m, d) is read from
+ *                x + b*x_strides[0] + h*x_strides[1] + (x_tok0[b] + j)*x_strides[2]
+ *                  + m*x_strides[3] + d          (strides in elements),
+ *                where m in [0, Tc) is the step inside the block and j counts
+ *                tokens from the first encoded page (j = 8*(lp - first_page[b]) + i).
+ *  x_tok0        device int64 [B] token-row offsets, or NULL for all zero.
+ *  codebooks     full codebooks (layout above).
+ *  first_page, n_pages   device int32 [B].
+ *  max_pages     host: an upper bound of n_pages[b] over the batch (grid size).
+ */
+LVQ_API lvq_status lvq_encode(const lvq_geom* g, int32_t block,
+                      const void* x_k, const void* x_v, const int64_t x_strides[4],
+                      const int64_t* x_tok0, const void* codebooks,
+                      uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
+                      const int32_t* first_page, const int32_t* n_pages,
+                      int32_t B, int32_t max_pages, hipStream_t stream);
+
+/*
+ * Bytes of workspace lvq_decode_attn needs for B requests of length at most
+ * max_len with the given split count (0 = the library's choice).
+ */
+LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t max_len, int32_t num_splits);
+
+/*
+ * Decode attention of loop step `step` (0-based) for B requests (step 5,
+ * Figure 5): out[b][h] = softmax(sm_scale * q . RoPE(k_p)) V over positions
+ * p in [0, seq_len[b]), where keys and values of paged positions are rebuilt
+ * from their indices through the step's codebook slice, and sink/recent
+ * positions come from the window buffers; keys are rotated at their absolute
+ * position.  The index pages are attended in `num_splits` splits per request
+ * (Flash-Decoding) and the bf16 window by a second kernel; a third merges all
+ * partials exactly through logsumexp.  Two requests share one workgroup
+ * (and with it the codebook slice and RoPE table loads).
+ *
+ *  q          bf16 [B][H][D], already rotated at position seq_len[b] - 1.
+ *  seq_len    device int32 [B], 1 <= seq_len[b] <= max_len <= rope_len.
+ *  slices     slices of ALL steps (layout above); the call reads step `step`.
+ *  out        fp32 [B][H][D];  lse_out fp32 [B][H] or NULL.
+ *  ws         device workspace of at least lvq_decode_attn_workspace() bytes.
+ *  num_splits 0 lets the library choose; otherwise 1..1024.
+ */
+LVQ_API lvq_status lvq_decode_attn(const lvq_geom* g, int32_t step, const void* q,
+                           const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
+                           const int32_t* seq_len, int32_t max_len,
+                           const void* win_k, const void* win_v,
+                           const void* slices, const float* rope_cos, const float* rope_sin,
+                           int32_t rope_len, float sm_scale, float* out, float* lse_out,
+                           void* ws, size_t ws_bytes, int32_t num_splits, int32_t B,
+                           hipStream_t stream);
+
+/* The split count lvq_decode_attn uses when passed num_splits = 0 (0 on bad arguments). */
+LVQ_API int32_t lvq_decode_attn_splits(const lvq_geom* g, int32_t B, int32_t max_len);
+
+/*
+ * The two partial passes lvq_decode_attn is made of, callable on their own
+ * (Figure 5 of the LoopVQ page: one kernel attends the index pages, another
+ * the bf16 pages, and their outputs are merged).  Both write normalised
+ * partials part_o fp32 [B*H][S_tot][D] and their logsumexp part_lse fp32
+ * [B*H][S_tot]; splitk_lse_merge(part_o, part_lse, B*H, S_tot, D, ...) then
+ * gives the attention output.  Rows are (request b, head h) -> b*H + h.
+ *
+ * lvq_quant_partial: the index pages of each request are cut into
+ *   num_splits ranges of ceil(max_pages / num_splits) pages and split s writes
+ *   slot s; an empty range writes part_o = 0, part_lse = -inf.
+ *   S_tot >= num_splits.  Two requests share one workgroup.
+ * lvq_window_partial: the sink and recent bf16 tokens of step `step`, written
+ *   to slot `slot` (< S_tot).  Never empty for seq_len >= 1.
+ * Other arguments as for lvq_decode_attn.
+ */
+LVQ_API lvq_status lvq_quant_partial(const lvq_geom* g, int32_t step, const void* q,
+                                     const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
+                                     const int32_t* seq_len, int32_t max_len, const void* slices,
+                                     const float* rope_cos, const float* rope_sin, int32_t rope_len,
+                                     float sm_scale, float* part_o, float* part_lse, int32_t num_splits,
+                                     int32_t S_tot, int32_t B, hipStream_t stream);
+LVQ_API lvq_status lvq_window_partial(const lvq_geom* g, int32_t step, const void* q,
+                                      const int32_t* seq_len, int32_t max_len,
+                                      const void* win_k, const void* win_v,
+                                      const float* rope_cos, const float* rope_sin, int32_t rope_len,
+                                      float sm_scale, float* part_o, float* part_lse, int32_t slot,
+                                      int32_t S_tot, int32_t B, hipStream_t stream);
+
+/*
+ * Exact merge of split partials (background "SGLang and Flash-Decoding"):
+ *   lse[n] = M + ln sum_s exp(part_lse[n][s] - M),  M = max_s part_lse[n][s]
+ *   out[n] = sum_s exp(part_lse[n][s] - lse[n]) * part_o[n][s]
+ * Splits with part_lse = -inf contribute nothing; a row whose splits are all
+ * empty gets out = 0, lse = -inf.
+ *  part_o fp32 [n][S][D], part_lse fp32 [n][S], out fp32 [n][D], lse_out [n] or NULL.
+ */
+LVQ_API lvq_status splitk_lse_merge(const float* part_o, const float* part_lse, int32_t n, int32_t S,
+                            int32_t D, float* out, float* lse_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* KIVI                                                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * D      head dimension (128 supported)     H      KV heads
+ * bits   2                                   group  32 (tokens per key group, channels per value group)
+ * R      residual length (a multiple of group)
+ * cap    token capacity per request (a multiple of group)
+ */
+typedef struct {
+    int32_t D, H, bits, group, R, cap;
+} kivi_geom;
+
+/*
+ * Cache of B requests, all device pointers:
+ *  k_codes  uint8 [B][H][cap][D/4]   key codes, token-major; channel d of a
+ *                                    token sits in byte d/4 at bits 2*(d%4)
+ *  k_scale, k_zero  fp16 [B][H][cap/group][D]   per (32-token group, channel)
+ *  v_codes  uint8 [B][H][cap][D/4]   value codes, same packing
+ *  v_scale, v_zero  fp16 [B][H][cap][D/group]   per (token, 32-channel group)
+ *  k_res, v_res     fp16 [B][H][R+group][D]     residual rings: position p in slot p % (R+group)
+ *  len, n_kq, n_vq  int32 [B]        tokens held; keys [0, n_kq) and values
+ *                                    [0, n_vq) are quantized, the rest fp16
+ */
+typedef struct {
+    uint8_t* k_codes; void* k_scale; void* k_zero;
+    uint8_t* v_codes; void* v_scale; void* v_zero;
+    void* k_res; void* v_res;
+    int32_t* len; int32_t* n_kq; int32_t* n_vq;
+} kivi_cache;
+
+/*
+ * Append n_new tokens per request ("core design", pseudo-code):
+ *  - prefill (n_new >= 1, cache empty: len[b] == 0 for all b): keys
+ *    [0, group*floor((n_new-R)/group)) are quantized per channel, values
+ *    [0, n_new-R) per token, the rest kept fp16;
+ *  - decode (n_new == 1, cache non-empty): the token goes to the residuals;
+ *    then, if the key residual holds R or more rows, its oldest R rows are
+ *    quantized (R/group whole groups) and dropped; if the value residual holds
+ *    more than R rows, the rows beyond the newest R are quantized.
+ * Codes, s and z follow q = clamp(rint(fl32(fl32(x/s) + z)), 0, 3) with
+ * s = fp16(fl32(fl32(max - min)/3)) (1 if that is 0) and z = fp16(fl32(-min/s)),
+ * each step IEEE binary32 round-to-nearest-even.
+ *  k_new, v_new  fp16; element (b, h, j, d) at b*new_strides[0] + h*new_strides[1]
+ *                + j*new_strides[2] + d   (strides in elements, host array).
+ *  prefill       host flag: 1 = prefill, 0 = decode.
+ */
+LVQ_API lvq_status kivi_append(const kivi_geom* g, const void* k_new, const void* v_new,
+                       const int64_t new_strides[3], int32_t n_new, int32_t prefill,
+                       const kivi_cache* c, int32_t B, hipStream_t stream);
+
+LVQ_API size_t kivi_decode_attn_workspace(const kivi_geom* g, int32_t B, int32_t max_len, int32_t num_splits);
+
+/*
+ * Decode attention over the quantized and fp16 segments with ONE softmax over
+ * all logits ("core design", segment attention; "engineering": the segments
+ * must share the normaliser).  Keys are used as stored (post-RoPE in KIVI).
+ *  q  fp16 [B][H][D];  out fp32 [B][H][D];  lse_out fp32 [B][H] or NULL.
+ *  max_len (host) bounds len[b]; num_splits 0 = the library's choice.
+ */
+LVQ_API lvq_status kivi_decode_attn(const kivi_geom* g, const void* q, const kivi_cache* c, int32_t max_len,
+                            float sm_scale, float* out, float* lse_out, void* ws, size_t ws_bytes,
+                            int32_t num_splits, int32_t B, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LVQ_H */

@@ -1,0 +1,138 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status before any
+device work.  No kernel is launched here (CPU only)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import decode_attention_loopvq_amd as lvq
+from decode_attention_loopvq_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lvq.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = C.c_void_p(4096)      # never dereferenced: validation fails before any use
+
+
+def _declared():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"LVQ_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("lvq_encode", "lvq_decode_attn", "kivi_append", "kivi_decode_attn", "splitk_lse_merge"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert names == sorted(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(_lib.lib, n), n
+
+
+def _geom(**kw):
+    return lvq.make_geom(H=2, **kw)
+
+
+def _attn(g, **over):
+    args = dict(step=0, q=FAKE, pool=FAKE, pt=FAKE, pt_stride=1000, seq_len=FAKE, max_len=1024, wk=FAKE,
+                wv=FAKE, slices=FAKE, cos=FAKE, sin=FAKE, rope_len=2048, scale=0.1, out=FAKE, lse=None, ws=FAKE,
+                ws_bytes=1 << 30, splits=0, B=4)
+    args.update(over)
+    gp = C.byref(g) if g is not None else None
+    return _lib.lib.lvq_decode_attn(gp, args["step"], args["q"], args["pool"], args["pt"], args["pt_stride"],
+                                    args["seq_len"], args["max_len"], args["wk"], args["wv"], args["slices"],
+                                    args["cos"], args["sin"], args["rope_len"], args["scale"], args["out"],
+                                    args["lse"], args["ws"], args["ws_bytes"], args["splits"], args["B"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(step=4), INVALID), (dict(step=-1), INVALID), (dict(max_len=0), INVALID),
+    (dict(max_len=4096), INVALID),             # beyond the RoPE table
+    (dict(splits=2000), INVALID), (dict(q=None), INVALID), (dict(ws=None), INVALID),
+    (dict(pool=None), INVALID), (dict(pt_stride=3), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(ws_bytes=16), WORKSPACE),
+])
+def test_decode_attn_rejects(over, status):
+    assert _attn(_geom(), **over) == status
+    assert _lib.lib.lvq_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), UNSUPPORTED), (dict(K=128), UNSUPPORTED), (dict(page=16), UNSUPPORTED),
+    (dict(T=4, Tc=3), INVALID), (dict(G=12, Tc=2), UNSUPPORTED), (dict(G=64, Tc=2), UNSUPPORTED),
+    (dict(window=60), UNSUPPORTED), (dict(T=0), INVALID),
+])
+def test_geometry_rejects(kw, status):
+    assert _attn(_geom(**kw)) == status
+    assert _attn(None) == INVALID
+
+
+def test_decode_attn_empty_batch_is_a_no_op():
+    assert _attn(_geom(), B=0, q=None, ws=None) == OK
+
+
+def test_workspace_query():
+    g = _geom()
+    n = _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 3)
+    assert n == 64 * 2 * 4 * (128 + 1) * 4
+    assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 0) > 0
+    assert _lib.lib.lvq_decode_attn_workspace(None, 64, 6144, 0) == 0
+
+
+def test_encode_rejects():
+    g = _geom()
+    strides = (C.c_int64 * 4)(1, 1, 1, 1)
+    f = _lib.lib.lvq_encode
+    assert f(C.byref(g), 2, FAKE, FAKE, strides, None, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 4, 8, None) == INVALID
+    assert f(C.byref(g), 0, None, None, strides, None, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 4, 8, None) == INVALID
+    assert f(C.byref(g), 0, FAKE, None, strides, None, FAKE, None, FAKE, 8, FAKE, FAKE, 4, 8, None) == INVALID
+    assert f(C.byref(g), 0, FAKE, None, strides, None, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 0, 8, None) == OK
+
+
+def test_merge_and_tables_reject():
+    assert _lib.lib.splitk_lse_merge(FAKE, FAKE, 4, 0, 128, FAKE, None, None) == INVALID
+    assert _lib.lib.splitk_lse_merge(None, FAKE, 4, 2, 128, FAKE, None, None) == INVALID
+    assert _lib.lib.splitk_lse_merge(None, None, 0, 2, 128, None, None, None) == OK
+    assert _lib.lib.lvq_rope_table(0, 128, 10000.0, FAKE, FAKE, None) == INVALID
+    assert _lib.lib.lvq_rope_table(16, 127, 10000.0, FAKE, FAKE, None) == INVALID
+    g = _geom(D=64)
+    assert _lib.lib.lvq_slice_codebooks(C.byref(g), FAKE, FAKE, None) == UNSUPPORTED
+
+
+def _kc():
+    return _lib.kivi_cache(*([4096] * 11))
+
+
+def test_kivi_rejects():
+    g = lvq.make_kivi_geom(H=2, cap=4096)
+    c = _kc()
+    strides = (C.c_int64 * 3)(1, 1, 1)
+    f = _lib.lib.kivi_append
+    assert f(C.byref(g), FAKE, FAKE, strides, 2, 0, C.byref(c), 4, None) == UNSUPPORTED   # decode of 2 tokens
+    assert f(C.byref(g), FAKE, FAKE, strides, 0, 1, C.byref(c), 4, None) == INVALID
+    assert f(C.byref(g), FAKE, FAKE, strides, 5000, 1, C.byref(c), 4, None) == INVALID   # over capacity
+    bad = lvq.make_kivi_geom(H=2, bits=4)
+    assert f(C.byref(bad), FAKE, FAKE, strides, 1, 0, C.byref(c), 4, None) == UNSUPPORTED
+    bad = lvq.make_kivi_geom(H=2, R=100)
+    assert f(C.byref(bad), FAKE, FAKE, strides, 1, 0, C.byref(c), 4, None) == INVALID
+    c.len = None
+    assert f(C.byref(g), FAKE, FAKE, strides, 1, 0, C.byref(c), 4, None) == INVALID
+    c = _kc()
+    a = _lib.lib.kivi_decode_attn
+    assert a(C.byref(g), FAKE, C.byref(c), 4097, 0.1, FAKE, None, FAKE, 1 << 30, 0, 4, None) == INVALID
+    assert a(C.byref(g), FAKE, C.byref(c), 4096, 0.1, FAKE, None, FAKE, 8, 0, 4, None) == WORKSPACE
+    assert a(C.byref(g), None, C.byref(c), 4096, 0.1, FAKE, None, FAKE, 1 << 30, 0, 4, None) == INVALID
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+    g = _geom()
+    with pytest.raises(ValueError):
+        lvq.lvq_slice_codebooks(g, torch.zeros((2, 2, 2, 16, 256, 16), dtype=torch.bfloat16))

@@ -1,0 +1,137 @@
+"""Parity of the HIP KIVI path with the oracle (GPU).
+
+Codes, fp16 scales and zero-points and the fp16 residual rings must match
+bit for bit; attention outputs within max relative error 2e-3 per row.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kivi as kv
+from synth.configs import kivi_config
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 2e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _unpack(codes: np.ndarray) -> np.ndarray:
+    """[n][D/4] bytes -> [n][D] codes, channel d at bits 2*(d%4) of byte d/4."""
+    n, nb = codes.shape
+    out = np.empty((n, nb * 4), dtype=np.uint8)
+    for u in range(4):
+        out[:, u::4] = (codes >> (2 * u)) & 3
+    return out
+
+
+def _u16(x):
+    return np.ascontiguousarray(x).view(np.uint16)
+
+
+def _compare_state(cache, g, b, h, st: kv.KiviState):
+    ring = g.R + g.group
+    L, nk, nv = int(cache.len[b]), int(cache.n_kq[b]), int(cache.n_vq[b])
+    assert (L, nk, nv) == (st.length, st.n_kq, st.n_vq), ((L, nk, nv), (st.length, st.n_kq, st.n_vq))
+    if nk:
+        np.testing.assert_array_equal(_unpack(cache.k_codes[b, h, :nk].cpu().numpy()), np.concatenate(st.k_codes))
+        np.testing.assert_array_equal(_u16(cache.k_scale[b, h, :nk // g.group].cpu().numpy()), _u16(np.stack(st.k_s)))
+        np.testing.assert_array_equal(_u16(cache.k_zero[b, h, :nk // g.group].cpu().numpy()), _u16(np.stack(st.k_z)))
+    if nv:
+        np.testing.assert_array_equal(_unpack(cache.v_codes[b, h, :nv].cpu().numpy()), np.stack(st.v_codes))
+        np.testing.assert_array_equal(_u16(cache.v_scale[b, h, :nv].cpu().numpy()), _u16(np.stack(st.v_s)))
+        np.testing.assert_array_equal(_u16(cache.v_zero[b, h, :nv].cpu().numpy()), _u16(np.stack(st.v_z)))
+    kres = cache.k_res[b, h].cpu().numpy()
+    vres = cache.v_res[b, h].cpu().numpy()
+    for j, p in enumerate(range(nk, L)):
+        np.testing.assert_array_equal(_u16(kres[p % ring]), _u16(st.k_res[j]))
+    for j, p in enumerate(range(nv, L)):
+        np.testing.assert_array_equal(_u16(vres[p % ring]), _u16(st.v_res[j]))
+
+
+def _check_attn(prob, rows, states):
+    import decode_attention_loopvq_amd as lvq
+    g, cache = prob.g, prob.cache
+    max_len = int(cache.len.max())
+    worst = 0.0
+    for ns in (0, 1, 5):
+        lse = torch.empty((cache.B, g.H), dtype=torch.float32, device="cuda")
+        out, _ = lvq.kivi_decode_attn(g, prob.q, cache, max_len, prob.sm_scale, lse_out=lse, num_splits=ns)
+        torch.cuda.synchronize()
+        for (b, h) in rows:
+            q = prob.q[b, h].float().cpu().numpy().astype(np.float64)
+            o_ref, lse_ref = kv.attention(q, states[(b, h)], prob.sm_scale)
+            o = out[b, h].double().cpu().numpy()
+            err = np.abs(o - o_ref).max() / np.abs(o_ref).max()
+            worst = max(worst, err)
+            assert err <= REL_TOL, f"row ({b},{h}) splits {ns}: rel err {err:.3e}"
+            assert abs(float(lse[b, h]) - lse_ref) <= 2e-3
+    return worst
+
+
+def _states(prob, rows):
+    k = prob.k.cpu().numpy()
+    v = prob.v.cpu().numpy()
+    states = {}
+    for (b, h) in rows:
+        st = kv.KiviState(D=prob.g.D, group=prob.g.group, R=prob.g.R)
+        st.prefill(k[b, h], v[b, h])
+        states[(b, h)] = st
+    return states
+
+
+@pytest.mark.parametrize("L", [1, 100, 128, 160, 300, 700])
+def test_prefill_bit_exact_and_attention(L):
+    from tests import harness
+    cfg = kivi_config("kivi-b16-4k", B=3, H=2, L=L)
+    _say(f"[kivi prefill] L={L}")
+    prob = harness.build_kivi(cfg)
+    rows = [(b, h) for b in range(3) for h in range(2)]
+    states = _states(prob, rows)
+    for (b, h) in rows:
+        _compare_state(prob.cache, prob.g, b, h, states[(b, h)])
+    _check_attn(prob, rows, states)
+
+
+def test_decode_appends_bit_exact():
+    """Prefill, then 200 single-token appends (several key flushes, a value
+    overflow at every step), then attention."""
+    import decode_attention_loopvq_amd as lvq
+    import synth.kivi as synk
+    from tests import harness
+    cfg = kivi_config("kivi-b16-4k", B=2, H=2, L=300)
+    prob = harness.build_kivi(cfg)
+    rows = [(b, h) for b in range(2) for h in range(2)]
+    states = _states(prob, rows)
+    n = 200
+    kn, vn = synk.new_tokens(cfg, n, "cuda")          # [n][B][H][D]
+    kn_h, vn_h = kn.cpu().numpy(), vn.cpu().numpy()
+    for i in range(n):
+        lvq.kivi_append(prob.g, kn[i][:, :, None, :], vn[i][:, :, None, :], prob.cache, prefill=False)
+        for (b, h) in rows:
+            states[(b, h)].append(kn_h[i, b, h], vn_h[i, b, h])
+        if i in (0, 1, 27, 28, 29, 155, 199):
+            torch.cuda.synchronize()
+            for (b, h) in rows:
+                _compare_state(prob.cache, prob.g, b, h, states[(b, h)])
+    _check_attn(prob, rows, states)
+
+
+def test_full_b16_4k_sampled():
+    from tests import harness
+    cfg = kivi_config("kivi-b16-4k")
+    _say("[kivi full] B=16 H=32 L=4096")
+    prob = harness.build_kivi(cfg)
+    rows = [(0, 0), (7, 19), (15, 31)]
+    states = _states(prob, rows)
+    for (b, h) in rows:
+        _compare_state(prob.cache, prob.g, b, h, states[(b, h)])
+    worst = _check_attn(prob, rows, states)
+    _say(f"[kivi full] worst rel err {worst:.3e}")

@@ -1,0 +1,192 @@
+"""Parity of the HIP LoopVQ path with the fp64 oracle (GPU).
+
+Bars: indices and dequantised values bit-exact (a differing index passes only
+if its fp64 distance is within 1e-6 relative of the oracle's, lowest index
+on ties); attention outputs within max relative error 2e-3 per (request,
+head) row, ||o_gpu - o_ref||_inf / ||o_ref||_inf.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import loopvq as lv
+from synth.configs import loopvq_config
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 2e-3
+LSE_TOL = 2e-3
+TIE_BAND = 1e-6
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _geo(cfg):
+    return lv.Geometry(D=cfg.D, T=cfg.T, Tc=cfg.Tc, G=cfg.G, K=cfg.K, sink=cfg.sink, window=cfg.window,
+                       page=cfg.page)
+
+
+def _check_indices(p, b, h, geo):
+    """GPU indices of (b, h) against the oracle's encode; returns the oracle's indices."""
+    from tests import harness
+    L = p.lengths[b]
+    _, q_lo, q_hi = lv.cache_regions(L, geo)
+    out = {}
+    for kind in ("k", "v"):
+        E = harness.host_codebooks(p, h, kind)
+        ref = lv.encode_request(p.raw[(kind, b, h)], E, geo, L)
+        got = harness.gpu_indices(p, b, h, kind)
+        assert got.shape == ref.shape, (got.shape, ref.shape)
+        bad = np.argwhere(got != ref)
+        for beta, j, g in bad:
+            x = p.raw[(kind, b, h)][q_lo + j, beta * geo.Tc:(beta + 1) * geo.Tc, :]
+            z = lv.couple(x[:, None, :], geo.G)[0, g]
+            _, d = lv.nearest_codeword(z[None], E[beta, g])
+            assert d[0, got[beta, j, g]] <= d[0, ref[beta, j, g]] * (1 + TIE_BAND), \
+                f"index mismatch at block {beta} token {j} group {g}"
+        out[kind] = ref
+    return out
+
+
+def _check_row(p, t, b, h, geo, idx, out, lse):
+    L = p.lengths[b]
+    Ek, Ev = (lv_cb(p, h, "k"), lv_cb(p, h, "v"))
+    q = p.q[t, b, h].float().cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = lv.decode_step(q, t, p.raw[("k", b, h)], p.raw[("v", b, h)], idx["k"], idx["v"], Ek, Ev,
+                                    geo, L, p.sm_scale, p.cfg.rope_base)
+    o = out[b, h].double().cpu().numpy()
+    err = np.abs(o - o_ref).max() / np.abs(o_ref).max()
+    assert err <= REL_TOL, f"step {t} row ({b},{h}) L={L}: rel err {err:.3e}"
+    assert abs(float(lse[b, h]) - lse_ref) <= LSE_TOL, f"step {t} row ({b},{h}): lse {float(lse[b, h])} vs {lse_ref}"
+    return err
+
+
+def lv_cb(p, h, kind):
+    from tests import harness
+    return harness.host_codebooks(p, h, kind)
+
+
+def _run_parity(cfg, rows, steps, splits=(0,)):
+    from tests import harness
+    geo = _geo(cfg)
+    _say(f"[build] {cfg.name} B={cfg.B} H={cfg.H} L={cfg.L} T={cfg.T} Tc={cfg.Tc} G={cfg.G} rows={len(rows)}")
+    p = harness.build_loopvq(cfg, keep=rows)
+    idx = {}
+    for (b, h) in rows:
+        idx[(b, h)] = _check_indices(p, b, h, geo)
+    worst = 0.0
+    for ns in splits:
+        for t in steps:
+            lse = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device="cuda")
+            _say(f"[attn] {cfg.name} step {t} num_splits={ns}")
+            out, _ = harness.run_step(p, t, num_splits=ns, lse=lse)
+            torch.cuda.synchronize()
+            for (b, h) in rows:
+                worst = max(worst, _check_row(p, t, b, h, geo, idx[(b, h)], out, lse))
+    _say(f"[done] {cfg.name} worst rel err {worst:.3e}")
+    return p
+
+
+def test_rope_table_matches_fp64():
+    import decode_attention_loopvq_amd as lvq
+    cos, sin = lvq.lvq_rope_table(40000, 128, 10000.0)
+    phi = lv.rope_angles(np.arange(40000), 128, 10000.0)
+    # fp64 evaluation rounded once: within one fp32 rounding of the fp64 values
+    assert np.abs(cos.cpu().numpy() - np.cos(phi)).max() <= 6e-8
+    assert np.abs(sin.cpu().numpy() - np.sin(phi)).max() <= 6e-8
+
+
+@pytest.mark.parametrize("cb", ["bf16", "fp32"])
+@pytest.mark.parametrize("T,Tc,G", [(4, 2, 16), (4, 4, 32), (32, 4, 16)])
+def test_slices_bit_exact(cb, T, Tc, G):
+    import decode_attention_loopvq_amd as lvq
+    g = lvq.make_geom(T=T, Tc=Tc, G=G, H=3, cb_dtype=cb)
+    dt = torch.bfloat16 if cb == "bf16" else torch.float32
+    cbk = torch.randn((T // Tc, 3, 2, 128 * Tc // G, 256, G), device="cuda").to(dt)
+    sl = lvq.lvq_slice_codebooks(g, cbk)
+    host = cbk.float().cpu().numpy()
+    got = sl.float().cpu().numpy()
+    for t in range(T):
+        for h in range(3):
+            for kv in range(2):
+                np.testing.assert_array_equal(got[t, h, kv], lv.step_slice(host[t // Tc, h, kv], t % Tc, Tc, G))
+
+
+SMALL = [
+    # two requests per workgroup with an odd batch, several tiles and a ragged tail
+    loopvq_config("loopvq-b64-6k", B=5, H=2, L=700),
+    # fp32 codebooks, the 1K single-request workload as stated
+    loopvq_config("loopvq-b1-1k-fp32cb"),
+    # T_c = 4, G = 32, 256-token window
+    loopvq_config("loopvq-b8-32k", B=3, H=2, L=1500),
+    # 32 loop steps, c = 4, ragged lengths from 1 token up, random page order
+    loopvq_config("loopvq-deep-ragged", B=7, H=2, L=900, ragged=(1, 900)),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_decode_parity_small(cfg):
+    rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    steps = list(range(cfg.T)) if cfg.T <= 4 else [0, 3, 4, 17, 31]
+    _run_parity(cfg, rows, steps, splits=(0, 1, 3))
+
+
+def test_decode_edge_lengths(monkeypatch):
+    """Lengths shorter than the sinks, exactly sink + window, one page, and
+    pages beyond every split boundary; more splits than pages."""
+    from tests import harness
+    import synth.loopvq as syn
+    cfg = loopvq_config("loopvq-b64-6k", B=8, H=1, L=100)
+    lengths = [1, 5, 8, 72, 79, 80, 81, 100]
+    monkeypatch.setattr(syn, "lengths", lambda c: lengths)
+    if True:
+        geo = _geo(cfg)
+        rows = [(b, 0) for b in range(8)]
+        p = harness.build_loopvq(cfg, keep=rows)
+        idx = {(b, 0): _check_indices(p, b, 0, geo) for b in range(8)}
+        for ns in (0, 1, 2, 7, 50):
+            for t in range(cfg.T):
+                lse = torch.empty((8, 1), dtype=torch.float32, device="cuda")
+                out, _ = harness.run_step(p, t, num_splits=ns, lse=lse)
+                torch.cuda.synchronize()
+                for (b, h) in rows:
+                    _check_row(p, t, b, h, geo, idx[(b, h)], out, lse)
+
+
+def test_merge_parity():
+    import decode_attention_loopvq_amd as lvq
+    rng = np.random.default_rng(0)
+    n, S, D = 37, 6, 128
+    po = rng.standard_normal((n, S, D)).astype(np.float32)
+    pl = (rng.standard_normal((n, S)) * 5).astype(np.float32)
+    pl[3, :] = -np.inf
+    pl[5, [0, 2, 4]] = -np.inf
+    out, lse = lvq.splitk_lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for r in range(n):
+        o_ref, l_ref = lv.merge([(po[r, s].astype(np.float64), float(pl[r, s])) for s in range(S)])
+        if l_ref == -np.inf:
+            assert lse[r] == -np.inf and not out[r].any()
+            continue
+        assert np.abs(out[r] - o_ref).max() <= 1e-5 * max(1.0, np.abs(o_ref).max())
+        assert abs(lse[r] - l_ref) <= 1e-5 * max(1.0, abs(l_ref))
+
+
+def test_full_b64_6k_sampled():
+    """The serving-scale workload at full size in the benchmark's launch
+    configuration, checked on sampled rows."""
+    cfg = loopvq_config("loopvq-b64-6k")
+    rows = [(0, 0), (37, 9), (63, 15)]
+    _run_parity(cfg, rows, steps=range(cfg.T), splits=(0,))
+
+
+def test_full_b1_1k():
+    cfg = loopvq_config("loopvq-b1-1k-fp32cb")
+    _run_parity(cfg, [(0, 0)], steps=range(cfg.T), splits=(0,))
