@@ -177,12 +177,14 @@ def main():
     rows_tot = B * g.H * (S + 1)
     part_o = ws.view(torch.float32)[: rows_tot * g.D]
     part_lse = ws.view(torch.float32)[rows_tot * g.D: rows_tot * (g.D + 1)]
+    qws_bytes = lvq.lvq_quant_partial_workspace(g, B)
+    qws = torch.empty(qws_bytes, dtype=torch.uint8, device="cuda")
 
     def quant_args(t, l):
         return (gref, t, qs[t].data_ptr(), pools[l].data_ptr(), cache.page_table.data_ptr(),
                 int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, prob.slices.data_ptr(),
                 prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(), rope_len, C.c_float(prob.sm_scale),
-                part_o.data_ptr(), part_lse.data_ptr(), S, S + 1, B, sh)
+                part_o.data_ptr(), part_lse.data_ptr(), S, S + 1, qws.data_ptr(), qws_bytes, B, sh)
 
     qcalls = [quant_args(t, l) for t in range(cfg.T) for l in range(args.layers)]
 

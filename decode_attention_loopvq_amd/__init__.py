@@ -21,7 +21,7 @@ from . import layout  # noqa: F401
 __all__ = [
     "LvqError", "lvq_geom", "kivi_geom", "make_geom", "make_kivi_geom",
     "lvq_slice_codebooks", "lvq_rope_table", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn",
-    "lvq_decode_attn_splits", "lvq_quant_partial", "lvq_window_partial", "splitk_lse_merge", "kivi_append",
+    "lvq_decode_attn_splits", "lvq_quant_partial", "lvq_quant_partial_workspace", "lvq_window_partial", "splitk_lse_merge", "kivi_append",
     "kivi_decode_attn_workspace", "kivi_decode_attn", "KiviCache", "layout",
 ]
 
@@ -170,10 +170,14 @@ def lvq_decode_attn_splits(g: lvq_geom, B: int, max_len: int) -> int:
     return int(lib.lvq_decode_attn_splits(C.byref(g), int(B), int(max_len)))
 
 
+def lvq_quant_partial_workspace(g: lvq_geom, B: int) -> int:
+    return int(lib.lvq_quant_partial_workspace(C.byref(g), int(B)))
+
+
 def lvq_quant_partial(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor, page_table: torch.Tensor,
                       seq_len: torch.Tensor, max_len: int, slices: torch.Tensor, rope_cos: torch.Tensor,
                       rope_sin: torch.Tensor, sm_scale: float, part_o: torch.Tensor, part_lse: torch.Tensor,
-                      num_splits: int, stream=None):
+                      num_splits: int, ws: Optional[torch.Tensor] = None, stream=None):
     """Index-page partials into part_o [B*H][S_tot][D], part_lse [B*H][S_tot] (slots 0..num_splits-1)."""
     _need(q, "q", torch.bfloat16)
     _need(pool, "pool", torch.uint8)
@@ -183,11 +187,16 @@ def lvq_quant_partial(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tenso
     _need(part_o, "part_o", torch.float32)
     _need(part_lse, "part_lse", torch.float32)
     B = q.shape[0]
+    need = lvq_quant_partial_workspace(g, B)
+    if ws is None:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    _need(ws, "ws")
     check(lib.lvq_quant_partial(C.byref(g), int(step), q.data_ptr(), pool.data_ptr(), page_table.data_ptr(),
                                 int(page_table.shape[1]), seq_len.data_ptr(), int(max_len), slices.data_ptr(),
                                 rope_cos.data_ptr(), rope_sin.data_ptr(), int(rope_cos.shape[0]), float(sm_scale),
                                 part_o.data_ptr(), part_lse.data_ptr(), int(num_splits), int(part_lse.shape[1]),
-                                int(B), _stream(stream)), "lvq_quant_partial")
+                                ws.data_ptr(), ws.numel() * ws.element_size(), int(B), _stream(stream)),
+          "lvq_quant_partial")
 
 
 def lvq_window_partial(g: lvq_geom, step: int, q: torch.Tensor, seq_len: torch.Tensor, max_len: int,

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblvq.so")
 EXPORTS = (
     "lvq_last_error", "lvq_slice_codebooks", "lvq_rope_table", "lvq_encode",
     "lvq_decode_attn_workspace", "lvq_decode_attn_splits", "lvq_decode_attn", "lvq_quant_partial",
+    "lvq_quant_partial_workspace",
     "lvq_window_partial", "splitk_lse_merge",
     "kivi_append", "kivi_decode_attn_workspace", "kivi_decode_attn",
 )
@@ -62,7 +63,9 @@ def _load():
     lib.lvq_decode_attn_splits.restype = _I
     lib.lvq_decode_attn_splits.argtypes = [C.POINTER(lvq_geom), _I, _I]
     lib.lvq_quant_partial.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, _P, _I, _P, _I, _P, _P, _P, _I, C.c_float,
-                                      _P, _P, _I, _I, _I, _P]
+                                      _P, _P, _I, _I, _P, _S, _I, _P]
+    lib.lvq_quant_partial_workspace.restype = _S
+    lib.lvq_quant_partial_workspace.argtypes = [C.POINTER(lvq_geom), _I]
     lib.lvq_window_partial.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, _I, _P, _P, _P, _P, _I, C.c_float, _P, _P,
                                        _I, _I, _I, _P]
     lib.splitk_lse_merge.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]

@@ -193,7 +193,9 @@ LVQ_API int32_t lvq_decode_attn_splits(const lvq_geom* g, int32_t B, int32_t max
  * lvq_quant_partial: the index pages of each request are cut into
  *   num_splits ranges of ceil(max_pages / num_splits) pages and split s writes
  *   slot s; an empty range writes part_o = 0, part_lse = -inf.
- *   S_tot >= num_splits.  Two requests share one workgroup.
+ *   S_tot >= num_splits.  Two requests share one workgroup.  ws is device
+ *   scratch of at least lvq_quant_partial_workspace(g, B) bytes (the query
+ *   repacked into RoPE pairs).
  * lvq_window_partial: the sink and recent bf16 tokens of step `step`, written
  *   to slot `slot` (< S_tot).  Never empty for seq_len >= 1.
  * Other arguments as for lvq_decode_attn.
@@ -203,7 +205,8 @@ LVQ_API lvq_status lvq_quant_partial(const lvq_geom* g, int32_t step, const void
                                      const int32_t* seq_len, int32_t max_len, const void* slices,
                                      const float* rope_cos, const float* rope_sin, int32_t rope_len,
                                      float sm_scale, float* part_o, float* part_lse, int32_t num_splits,
-                                     int32_t S_tot, int32_t B, hipStream_t stream);
+                                     int32_t S_tot, void* ws, size_t ws_bytes, int32_t B, hipStream_t stream);
+LVQ_API size_t lvq_quant_partial_workspace(const lvq_geom* g, int32_t B);
 LVQ_API lvq_status lvq_window_partial(const lvq_geom* g, int32_t step, const void* q,
                                       const int32_t* seq_len, int32_t max_len,
                                       const void* win_k, const void* win_v,

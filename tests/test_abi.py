@@ -81,7 +81,8 @@ def test_decode_attn_empty_batch_is_a_no_op():
 def test_workspace_query():
     g = _geom()
     n = _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 3)
-    assert n == 64 * 2 * 4 * (128 + 1) * 4
+    assert n == 64 * 2 * 4 * (128 + 1) * 4 + 64 * 2 * 128 * 4     # partials + packed query pairs
+    assert _lib.lib.lvq_quant_partial_workspace(C.byref(g), 64) == 64 * 2 * 128 * 4
     assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 0) > 0
     assert _lib.lib.lvq_decode_attn_workspace(None, 64, 6144, 0) == 0
 
