@@ -163,7 +163,7 @@ def main():
         return (gref, t, qs[t].data_ptr(), pools[l].data_ptr(), cache.page_table.data_ptr(),
                 int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, wks[l].data_ptr(),
                 wvs[l].data_ptr(), prob.slices.data_ptr(), prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(),
-                rope_len, C.c_float(prob.sm_scale), outs[l].data_ptr(), None, ws.data_ptr(), ws_bytes, S, B, sh)
+                prob.rope16.data_ptr(), rope_len, C.c_float(prob.sm_scale), outs[l].data_ptr(), None, ws.data_ptr(), ws_bytes, S, B, sh)
 
     calls = [full_args(t, l) for t in range(cfg.T) for l in range(args.layers)]
 
@@ -177,13 +177,14 @@ def main():
     rows_tot = B * g.H * (S + 1)
     part_o = ws.view(torch.float32)[: rows_tot * g.D]
     part_lse = ws.view(torch.float32)[rows_tot * g.D: rows_tot * (g.D + 1)]
-    qws_bytes = lvq.lvq_quant_partial_workspace(g, B)
+    qws_bytes = lvq.lvq_quant_partial_workspace(g, B, cache.max_len)
     qws = torch.empty(qws_bytes, dtype=torch.uint8, device="cuda")
 
     def quant_args(t, l):
         return (gref, t, qs[t].data_ptr(), pools[l].data_ptr(), cache.page_table.data_ptr(),
                 int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, prob.slices.data_ptr(),
-                prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(), rope_len, C.c_float(prob.sm_scale),
+                prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(), prob.rope16.data_ptr(), rope_len,
+                C.c_float(prob.sm_scale),
                 part_o.data_ptr(), part_lse.data_ptr(), S, S + 1, qws.data_ptr(), qws_bytes, B, sh)
 
     qcalls = [quant_args(t, l) for t in range(cfg.T) for l in range(args.layers)]
@@ -249,7 +250,7 @@ def main():
             "workload": WORKLOAD, "B": cfg.B, "H": cfg.H, "L": cfg.L, "T": cfg.T, "Tc": cfg.Tc, "G": cfg.G,
             "K": cfg.K, "codebook": cfg.cb_dtype, "sink": cfg.sink, "window": cfg.window, "page": cfg.page,
             "layers_rotated": args.layers, "calls_per_step": len(calls), "num_splits": S,
-            "requests_per_workgroup": 2,
+            "requests_per_workgroup": 4,
         },
         "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
         "token_heads_per_s": round(token_heads * n_calls / sec, 1),

@@ -20,7 +20,7 @@ from . import layout  # noqa: F401
 
 __all__ = [
     "LvqError", "lvq_geom", "kivi_geom", "make_geom", "make_kivi_geom",
-    "lvq_slice_codebooks", "lvq_rope_table", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn",
+    "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn",
     "lvq_decode_attn_splits", "lvq_quant_partial", "lvq_quant_partial_workspace", "lvq_window_partial", "splitk_lse_merge", "kivi_append",
     "kivi_decode_attn_workspace", "kivi_decode_attn", "KiviCache", "layout",
 ]
@@ -85,6 +85,24 @@ def lvq_rope_table(length: int, D: int = 128, base: float = 10000.0, device="cud
     return cos, sin
 
 
+def lvq_rope_table_f16(length: int, D: int = 128, base: float = 10000.0, device="cuda",
+                       stream=None) -> torch.Tensor:
+    """Packed fp16 cos/sin [16][length][8] for the index-page pass (layout in include/lvq.h)."""
+    out = torch.empty((16, length, 8), dtype=torch.float16, device=device)
+    check(lib.lvq_rope_table_f16(int(length), int(D), float(base), out.data_ptr(), _stream(stream)),
+          "lvq_rope_table_f16")
+    return out
+
+
+def _rope_f16_ptr(rope_f16: Optional[torch.Tensor], rope_cos: torch.Tensor):
+    if rope_f16 is None:
+        return None
+    _need(rope_f16, "rope_f16", torch.float16)
+    if tuple(rope_f16.shape) != (16, rope_cos.shape[0], 8):
+        raise ValueError("rope_f16 must be [16][rope_len][8] with the rope_cos length")
+    return rope_f16.data_ptr()
+
+
 def lvq_encode(g: lvq_geom, block: int, x_k: Optional[torch.Tensor], x_v: Optional[torch.Tensor],
                codebooks: torch.Tensor, pool: torch.Tensor, page_table: torch.Tensor, first_page: torch.Tensor,
                n_pages: torch.Tensor, max_pages: int, x_tok0: Optional[torch.Tensor] = None, stream=None):
@@ -128,8 +146,10 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
                     slices: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor, sm_scale: float,
                     out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
                     ws: Optional[torch.Tensor] = None, num_splits: int = 0,
-                    stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Decode attention of loop step `step`; returns (out [B][H][D] fp32, lse [B][H] or None)."""
+                    stream=None, rope_f16: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Decode attention of loop step `step`; returns (out [B][H][D] fp32, lse [B][H] or None).
+    rope_f16 (lvq_rope_table_f16) is required with bf16 codebooks."""
     _need(q, "q", torch.bfloat16)
     B = q.shape[0]
     if tuple(q.shape) != (B, g.H, g.D):
@@ -158,7 +178,8 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
     check(lib.lvq_decode_attn(C.byref(g), int(step), q.data_ptr(), pool.data_ptr(), page_table.data_ptr(),
                               int(page_table.shape[1]), seq_len.data_ptr(), int(max_len), win_k.data_ptr(),
                               win_v.data_ptr(), slices.data_ptr(), rope_cos.data_ptr(), rope_sin.data_ptr(),
-                              int(rope_cos.shape[0]), float(sm_scale), out.data_ptr(),
+                              _rope_f16_ptr(rope_f16, rope_cos), int(rope_cos.shape[0]), float(sm_scale),
+                              out.data_ptr(),
                               lse_out.data_ptr() if lse_out is not None else None, ws.data_ptr(),
                               ws.numel() * ws.element_size(), int(num_splits), int(B), _stream(stream)),
           "lvq_decode_attn")
@@ -170,14 +191,15 @@ def lvq_decode_attn_splits(g: lvq_geom, B: int, max_len: int) -> int:
     return int(lib.lvq_decode_attn_splits(C.byref(g), int(B), int(max_len)))
 
 
-def lvq_quant_partial_workspace(g: lvq_geom, B: int) -> int:
-    return int(lib.lvq_quant_partial_workspace(C.byref(g), int(B)))
+def lvq_quant_partial_workspace(g: lvq_geom, B: int, max_len: int) -> int:
+    return int(lib.lvq_quant_partial_workspace(C.byref(g), int(B), int(max_len)))
 
 
 def lvq_quant_partial(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor, page_table: torch.Tensor,
                       seq_len: torch.Tensor, max_len: int, slices: torch.Tensor, rope_cos: torch.Tensor,
                       rope_sin: torch.Tensor, sm_scale: float, part_o: torch.Tensor, part_lse: torch.Tensor,
-                      num_splits: int, ws: Optional[torch.Tensor] = None, stream=None):
+                      num_splits: int, ws: Optional[torch.Tensor] = None, stream=None,
+                      rope_f16: Optional[torch.Tensor] = None):
     """Index-page partials into part_o [B*H][S_tot][D], part_lse [B*H][S_tot] (slots 0..num_splits-1)."""
     _need(q, "q", torch.bfloat16)
     _need(pool, "pool", torch.uint8)
@@ -187,14 +209,15 @@ def lvq_quant_partial(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tenso
     _need(part_o, "part_o", torch.float32)
     _need(part_lse, "part_lse", torch.float32)
     B = q.shape[0]
-    need = lvq_quant_partial_workspace(g, B)
+    need = lvq_quant_partial_workspace(g, B, max_len)
     if ws is None:
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
     _need(ws, "ws")
     check(lib.lvq_quant_partial(C.byref(g), int(step), q.data_ptr(), pool.data_ptr(), page_table.data_ptr(),
                                 int(page_table.shape[1]), seq_len.data_ptr(), int(max_len), slices.data_ptr(),
-                                rope_cos.data_ptr(), rope_sin.data_ptr(), int(rope_cos.shape[0]), float(sm_scale),
-                                part_o.data_ptr(), part_lse.data_ptr(), int(num_splits), int(part_lse.shape[1]),
+                                rope_cos.data_ptr(), rope_sin.data_ptr(), _rope_f16_ptr(rope_f16, rope_cos),
+                                int(rope_cos.shape[0]), float(sm_scale), part_o.data_ptr(), part_lse.data_ptr(),
+                                int(num_splits), int(part_lse.shape[1]),
                                 ws.data_ptr(), ws.numel() * ws.element_size(), int(B), _stream(stream)),
           "lvq_quant_partial")
 

@@ -10,6 +10,8 @@
 #include "common.h"
 
 #include <algorithm>
+#include <cmath>
+#include <type_traits>
 
 namespace lvq {
 namespace {
@@ -38,11 +40,16 @@ struct AttnArgs {
     int S_tot;                  // num_splits + 1 (the last slot is the window partial)
     int num_splits;
     int pps;                    // index pages per split
+    float* scores;              // [B*H][sc_stride] scores of the index tokens (log2 units)
+    long sc_stride;
+    float* cmax;                // [B*H][cm_stride] maximum per 64-token chunk
+    long cm_stride;
     int B;
     int max_len;                // device lengths are clamped to this
     int rope_len;
-    const uint32_t* qpack;      // [B*H][128]: (q_i, q_{i+64}) then (q_{i+64}, -q_i) as bf16 pairs
-    int fix_bits;               // fixed-point bits of the softmax weights in the V bins
+    const uint32_t* qpack;      // [B*H][64] packed fp16 query rows (pack_q_f16_kernel)
+    const uint4* rope16;        // [16][rope_len] packed fp16 cos/sin chunks (lvq_rope_table_f16)
+    int fix_bits;               // fixed-point fraction bits of the softmax weights in the V bins
 };
 
 __device__ __forceinline__ int clamp_len(const AttnArgs& a, int rb) {
@@ -195,7 +202,6 @@ __global__ void __launch_bounds__(256) quant_partial_kernel(AttnArgs a) {
             const uint8_t* krow = a.pool + phys * g.page_bytes + (long(a.beta) * g.H + h) * 2 * 8 * NG + (tok & 7) * NG;
             const uint8_t* vrow = krow + 8 * NG;
             const uint64_t ikA = load_idx<GPC>(krow, gA), ikB = load_idx<GPC>(krow, gB);
-            const uint64_t ivA = load_idx<GPC>(vrow, gA), ivB = load_idx<GPC>(vrow, gB);
             float kA[32], kB[32];
 #pragma unroll
             for (int q = 0; q < GPC; ++q) {
@@ -224,7 +230,7 @@ __global__ void __launch_bounds__(256) quant_partial_kernel(AttnArgs a) {
             float vA[32], vB[32];
 #pragma unroll
             for (int q = 0; q < GPC; ++q) {
-                const int ia = int((ivA >> (8 * q)) & 0xff), ib = int((ivB >> (8 * q)) & 0xff);
+                const int ia = vrow[(gA + q) ^ (tok & 15)], ib = vrow[(gB + q) ^ (tok & 15)];
                 load_cw<C>(cbv + ((gA + q) * K + ia) * C, vA + q * C);
                 load_cw<C>(cbv + ((gB + q) * K + ib) * C, vB + q * C);
             }
@@ -290,29 +296,41 @@ __global__ void __launch_bounds__(256) quant_partial_kernel(AttnArgs a) {
     }
 }
 
+
 // ---------------------------------------------------------------------------
-// Query pairs for the packed dot products: row r of qpack holds, for RoPE
-// pair i (channel i with channel i + 64), the bf16 pair (q_i, q_{i+64}) at
-// [i] and (q_{i+64}, -q_i) at [64 + i].  With k-pair (k_i, k_{i+64}):
-//   dot2(k, qpack[i])      = q_i k_i + q_{i+64} k_{i+64}        (= A_i)
-//   dot2(k, qpack[64 + i]) = q_{i+64} k_i - q_i k_{i+64}        (= B_i)
-// and q . RoPE_p(k) = sum_i cos(p th_i) A_i + sin(p th_i) B_i.
+// Index-page partial for bf16 codebooks.
+//
+// RoPE score without rotating keys: with the rotate-half pairing (channel i
+// with i + 64, angle p*th_i), q . R(p) k = k . psi(p) where
+//   psi_i      = cos(p th_i) q_i + sin(p th_i) q_{i+64}
+//   psi_{i+64} = cos(p th_i) q_{i+64} - sin(p th_i) q_i      (i < 64),
+// i.e. the query turned back by the key's angle.  psi is formed per
+// (request, position) in packed fp16 and dotted with the key rebuilt from
+// the step's K slice (fp16 in LDS) with fp32 accumulation.  The query is
+// pre-scaled by sm_scale * log2(e) so scores come out in log2 units.
+//
+// V is never rebuilt per token: the softmax weight of each token is added,
+// in fixed point, to one bin per (group, codeword) of its V indices, and the
+// partial output is sum_r bin[g][r] * B_t^V[g][r] at the end (exact up to
+// the weights' rounding).  Weights need the split's running maximum, so each
+// segment of tokens is scored first, the maximum taken, the bins rescaled if
+// it grew, and the weights then binned.
+//
+// Workgroup: R requests x one head x one split, 512 threads, one lane per
+// token position.  A position's cos/sin (packed fp16, 256 B) is loaded once
+// and serves all R requests; the K slice staged once serves all of them.
+//
+// LDS (bytes):  [0, 64K)    K slice as fp16 [NG][256][C]  (later: V slice)
+//               [64K, 128K) bins u32 [256 codewords][R*NG slots]
+//               then page ids of the segment and reduction scratch.
+// Bin slot of (request j, group g) is j*NG + g; row r holds slot s at
+// byte r*256 + 4*s.  The V index bytes of a token sit XOR-rotated by
+// (token & 15) in the pool (byte m holds group m ^ (token & 15)), so at
+// step m the 16 lanes of each LDS phase hit 16 distinct groups and thus 16
+// distinct banks.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void pack_q_row(const uint16_t* q, uint32_t* out, int i) {
-    const uint32_t lo = q[i], hi = q[i + 64];
-    out[i] = lo | (hi << 16);
-    out[64 + i] = hi | ((lo ^ 0x8000u) << 16);
-}
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
-__global__ void pack_q_kernel(const uint16_t* __restrict__ q, uint32_t* __restrict__ qpack) {
-    const long row = blockIdx.x;
-    pack_q_row(q + row * 128, qpack + row * 128, threadIdx.x);
-}
-
-typedef short bf16x2_t __attribute__((ext_vector_type(2)));
-
-// Read-only data that the kernel reads at wave-uniform addresses: through the
-// constant address space the compiler turns such reads into scalar loads.
 template <typename T>
 using const_ptr = const __attribute__((address_space(4))) T*;
 template <typename T>
@@ -320,379 +338,427 @@ __device__ __forceinline__ const_ptr<T> as_const(const T* p) {
     return reinterpret_cast<const_ptr<T>>(reinterpret_cast<uintptr_t>(p));
 }
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
-                                           false);
+__device__ __forceinline__ h2_t as_h2(uint32_t x) { return __builtin_bit_cast(h2_t, x); }
+
+__device__ __forceinline__ float dot2h(uint32_t a, h2_t b, float c) {
+    return __builtin_amdgcn_fdot2(as_h2(a), b, c, false);
 }
 
-// Two RoPE pairs of one token: acc += cos0 A0 + sin0 B0 + cos1 A1 + sin1 B1, with
-// (k_i, k_{i+64}) taken from the low (pair 0) and high (pair 1) bf16 halves of
-// kl / kh.  One block so that the packed dot products use the three-operand
-// form with a zero accumulator (no register to clear) and every dot result is
-// read at least three instructions after it is written, as gfx950 requires
-// after a DOT instruction.
-__device__ __forceinline__ float two_pairs(float acc, uint32_t kl, uint32_t kh, uint32_t q0a, uint32_t q0b,
-                                           uint32_t q1a, uint32_t q1b, float c0, float s0, float c1, float s1) {
-    uint32_t kp0, kp1;
-    float a0, b0, a1, b1;
-    asm("v_perm_b32 %[kp0], %[kh], %[kl], %[sl]\n\t"
-        "v_perm_b32 %[kp1], %[kh], %[kl], %[sh]\n\t"
-        "v_dot2_f32_bf16 %[a0], %[kp0], %[q0a], 0\n\t"
-        "v_dot2_f32_bf16 %[b0], %[kp0], %[q0b], 0\n\t"
-        "v_dot2_f32_bf16 %[a1], %[kp1], %[q1a], 0\n\t"
-        "v_dot2_f32_bf16 %[b1], %[kp1], %[q1b], 0\n\t"
-        "v_fmac_f32 %[acc], %[c0], %[a0]\n\t"
-        "v_fmac_f32 %[acc], %[s0], %[b0]\n\t"
-        "v_fmac_f32 %[acc], %[c1], %[a1]\n\t"
-        "v_fmac_f32 %[acc], %[s1], %[b1]"
-        : [acc] "+v"(acc), [kp0] "=&v"(kp0), [kp1] "=&v"(kp1), [a0] "=&v"(a0), [b0] "=&v"(b0), [a1] "=&v"(a1),
-          [b1] "=&v"(b1)
-        : [kl] "v"(kl), [kh] "v"(kh), [q0a] "s"(q0a), [q0b] "s"(q0b), [q1a] "s"(q1a), [q1b] "s"(q1b),
-          [c0] "v"(c0), [s0] "v"(s0), [c1] "v"(c1), [s1] "v"(s1), [sl] "s"(0x05040100u), [sh] "s"(0x07060302u));
-    return acc;
+// Two bf16 (one dword) to two fp16 (one dword), round to nearest even.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    const h2_t h = {(_Float16)bf16_lo(w), (_Float16)bf16_hi(w)};
+    return __builtin_bit_cast(uint32_t, h);
 }
 
-// (k_i, k_{i+64}) from the dwords holding k_i (group g) and k_{i+64} (group g + NG/2).
-__device__ __forceinline__ uint32_t kpair(uint32_t lo_dw, uint32_t hi_dw, int half) {
-    return __builtin_amdgcn_perm(hi_dw, lo_dw, half ? 0x07060302u : 0x05040100u);
+// Byte offset (r << SH) of the codeword r held in byte B of w (one SDWA shift).
+template <int SH, int B>
+__device__ __forceinline__ uint32_t byte_shl(uint32_t w) {
+    uint32_t d;
+    if constexpr (B == 0)
+        asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+            : "=v"(d) : "v"(w), "i"(SH));
+    else if constexpr (B == 1)
+        asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+            : "=v"(d) : "v"(w), "i"(SH));
+    else if constexpr (B == 2)
+        asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+            : "=v"(d) : "v"(w), "i"(SH));
+    else
+        asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+            : "=v"(d) : "v"(w), "i"(SH));
+    return d;
 }
 
-constexpr int kSeg = 2048;       // tokens per request per scoring segment
-constexpr int kThreadsV2 = 512;  // 8 waves: two per SIMD
-constexpr int kBinPad = 264;     // padded bin row (256 codewords) to spread LDS banks
-
-// Score contribution of pair chunk `ch` (pairs 8ch .. 8ch+7) for one request.
-template <int C>
-__device__ __forceinline__ float chunk_score(int ch, const uint32_t* ik, const uint16_t* cb,
-                                             const_ptr<uint32_t> qp, const float* cs, const float* sn,
-                                             float acc) {
-    constexpr int K = 256, NG = 128 / C, HALF = NG / 2;
-    uint32_t kl[4], kh[4];   // 8 bf16 of channels 8ch.. (kl) and 64+8ch.. (kh)
-    if constexpr (C == 8) {
-        const int al = (ik[ch >> 2] >> (8 * (ch & 3))) & 0xff;
-        const int ah = (ik[2 + (ch >> 2)] >> (8 * (ch & 3))) & 0xff;
-        const uint4 vl = *reinterpret_cast<const uint4*>(cb + (ch * K + al) * 8);
-        const uint4 vh = *reinterpret_cast<const uint4*>(cb + ((ch + HALF) * K + ah) * 8);
-        kl[0] = vl.x; kl[1] = vl.y; kl[2] = vl.z; kl[3] = vl.w;
-        kh[0] = vh.x; kh[1] = vh.y; kh[2] = vh.z; kh[3] = vh.w;
-    } else {
-        const uint32_t wl = ik[ch >> 1] >> (16 * (ch & 1));
-        const uint32_t wh = ik[4 + (ch >> 1)] >> (16 * (ch & 1));
-        const int g0 = 2 * ch;
-        const uint2 l0 = *reinterpret_cast<const uint2*>(cb + (g0 * K + (wl & 0xff)) * 4);
-        const uint2 l1 = *reinterpret_cast<const uint2*>(cb + ((g0 + 1) * K + ((wl >> 8) & 0xff)) * 4);
-        const uint2 h0 = *reinterpret_cast<const uint2*>(cb + ((g0 + HALF) * K + (wh & 0xff)) * 4);
-        const uint2 h1 = *reinterpret_cast<const uint2*>(cb + ((g0 + 1 + HALF) * K + ((wh >> 8) & 0xff)) * 4);
-        kl[0] = l0.x; kl[1] = l0.y; kl[2] = l1.x; kl[3] = l1.y;
-        kh[0] = h0.x; kh[1] = h0.y; kh[2] = h1.x; kh[3] = h1.y;
+template <int M, int N>
+struct StaticFor {
+    template <typename F>
+    __device__ __forceinline__ static void run(F&& f) {
+        if constexpr (M < N) {
+            f(std::integral_constant<int, M>{});
+            StaticFor<M + 1, N>::run(f);
+        }
     }
-#pragma unroll
-    for (int u = 0; u < 8; u += 2)
-        acc = two_pairs(acc, kl[u >> 1], kh[u >> 1], qp[8 * ch + u], qp[64 + 8 * ch + u], qp[8 * ch + u + 1],
-                        qp[64 + 8 * ch + u + 1], cs[u], sn[u], cs[u + 1], sn[u + 1]);
-    return acc;
-}
+};
 
-// ---------------------------------------------------------------------------
-// Index-page partial, bf16 codebooks.
-//
-// Grid (split, head, request pair); 256 threads; one workgroup per CU
-// (~150 KB of LDS).  B_t^K of head h is staged in LDS and serves both
-// requests.  Each split is scored in segments of up to 2048 tokens per
-// request:
-//   1. lane = position: a lane rebuilds the key of its position for both
-//      requests (16 codeword gathers each), forms the exact RoPE score
-//      sum_i cos A_i + sin B_i with packed bf16 dot products, and keeps it in
-//      LDS.  cos/sin(p th_i) is formed once per position for both requests as
-//      cos(P th)cos(l th) - sin(P th)sin(l th) from the table rows of the
-//      wave's base position P (uniform, scalar loads) and of the lane offset
-//      l (held in registers).
-//   2. block max per request; bins are rescaled if the max grew.
-//   3. each token adds its weight exp(s - max) in fixed point to one bin per
-//      (group, codeword) of its V indices (integer LDS atomics).
-// At the end B_t^V replaces B_t^K in LDS and o = sum_r bin[g][r] B_t^V[g][r]
-// gives the partial output; l is the bin total of any one group.
-// ---------------------------------------------------------------------------
-template <int C>
-__global__ void __launch_bounds__(kThreadsV2, 1) quant_v2_kernel(AttnArgs a) {
-    constexpr int D = 128, K = 256, NG = D / C, IW = NG / 4;
+constexpr int kSThreads = 256;                    // score / value passes: 4 waves, two workgroups per CU
+constexpr int kChunk = 64;                        // tokens per wave iteration (one per lane)
+constexpr int kBinBytes = 65536;                  // 256 rows x 64 slots x 4 B
+
+// Index-token range [lo, hi) of request slot j of a workgroup in split `split` (hi <= lo: empty).
+template <int R>
+__device__ __forceinline__ bool split_ranges(const AttnArgs& a, int split, int r0, int (&lo)[R], int (&hi)[R]) {
     const Geo& g = a.geo;
-    const int split = blockIdx.x, h = blockIdx.y;
-    const int r0 = 2 * blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    int lo[2], hi[2];
+    const int split_tok = a.pps * g.page;
     bool any = false;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        lo[j] = hi[j] = 0;
+    for (int j = 0; j < R; ++j) {
         const int rb = r0 + j;
-        if (rb < a.B) {
-            const int np = n_index_pages(clamp_len(a, rb), g);
-            lo[j] = min(np, split * a.pps) * g.page;
-            hi[j] = min(np, (split + 1) * a.pps) * g.page;
-            any |= hi[j] > lo[j];
-        }
+        const int np8 = rb < a.B ? n_index_pages(clamp_len(a, rb), g) * g.page : 0;
+        lo[j] = min(np8, split * split_tok);
+        hi[j] = min(np8, (split + 1) * split_tok);
+        any |= hi[j] > lo[j];
     }
-    if (!any) {
-        for (int j = 0; j < 2; ++j) {
-            const int rb = r0 + j;
-            if (rb >= a.B) continue;
-            const long row = (long(rb) * g.H + h) * a.S_tot + split;
-            if (tid < D) a.part_o[row * D + tid] = 0.f;
-            if (tid == 0) a.part_lse[row] = -INFINITY;
-        }
-        return;
-    }
+    return any;
+}
 
-    extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* cb = reinterpret_cast<uint16_t*>(smem);                           // 66 KB: B_t^K, later B_t^V
-    constexpr int kCbBytes = NG * (K * C + 8) * 2;                               // padded rows for the final pass
-    uint32_t* bins = reinterpret_cast<uint32_t*>(smem + kCbBytes);               // [2][NG][kBinPad]
-    float* sc = reinterpret_cast<float*>(bins + 2 * NG * kBinPad);              // [2][kSeg]
-    float* red = sc + 2 * kSeg;                                                  // [2][8] max + [2][8] sums
-    int32_t* spt = reinterpret_cast<int32_t*>(red + 32);                         // [2][kSeg/8] page ids
+// ---------------------------------------------------------------------------
+// Score pass.  Grid (split, head, request group of R); 256 threads.  The
+// step's K slice of head h is staged in LDS as fp16 (64 KB, two workgroups
+// per CU).  Each wave takes 64-token chunks; a lane scores its token for all
+// R requests (the position's cos/sin, loaded once, serve all of them) and
+// stores the score (log2 units) to `scores`; the maximum of each
+// (request, 64-token chunk) goes to `cmax`.
+// ---------------------------------------------------------------------------
+template <int C, int R>
+__global__ void __launch_bounds__(kSThreads, 2) score_kernel(AttnArgs a) {
+    constexpr int D = 128, K = 256, NG = D / C, HG = NG / 2;
+    constexpr int SH = (C == 8) ? 4 : 3;           // byte offset of codeword r in its group row: r << SH
+    constexpr int IW = NG / 4;                     // index dwords per token row
+    // Static LDS, the kernel's only LDS object: its base is 0 and folds into instruction offsets.
+    __shared__ __align__(16) unsigned char cb[NG * K * C * 2];
+    const Geo& g = a.geo;
+    const int split = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * R;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int lo[R], hi[R];
+    if (!split_ranges<R>(a, split, r0, lo, hi)) return;
 
-    {   // stage B_t^K (unpadded rows), clear the bins
+    {   // K slice of head h, bf16 -> fp16
         const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_k) +
                                                           h * a.slice_hstride);
         uint4* dst = reinterpret_cast<uint4*>(cb);
-        for (int e = tid; e < K * D * 2 / 16; e += kThreadsV2) dst[e] = src[e];
-        for (int e = tid; e < 2 * NG * kBinPad; e += kThreadsV2) bins[e] = 0u;
-    }
-
-    // cos/sin of the lane offset, all 64 pairs
-    float cl[64], sl[64];
-    {
-        const int row = min(lane, a.rope_len - 1);
-        const float4* c4 = reinterpret_cast<const float4*>(a.rc + long(row) * 64);
-        const float4* s4 = reinterpret_cast<const float4*>(a.rs + long(row) * 64);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float4 c = c4[i], s_ = s4[i];
-            cl[4 * i] = c.x; cl[4 * i + 1] = c.y; cl[4 * i + 2] = c.z; cl[4 * i + 3] = c.w;
-            sl[4 * i] = s_.x; sl[4 * i + 1] = s_.y; sl[4 * i + 2] = s_.z; sl[4 * i + 3] = s_.w;
+        for (int e = tid; e < NG * K * C * 2 / 16; e += kSThreads) {
+            const uint4 w = src[e];
+            dst[e] = make_uint4(bf16x2_to_f16x2(w.x), bf16x2_to_f16x2(w.y), bf16x2_to_f16x2(w.z),
+                                bf16x2_to_f16x2(w.w));
         }
     }
-    const_ptr<uint32_t> qp[2];
-    const int32_t* ptr[2];
+    const_ptr<uint32_t> qp[R];
+    const int32_t* ptr[R];
+    long srow[R];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < R; ++j) {
         const int rb = min(r0 + j, a.B - 1);
-        qp[j] = as_const(a.qpack + (long(rb) * g.H + h) * 128);
+        qp[j] = as_const(a.qpack + (long(rb) * g.H + h) * 64);
         ptr[j] = a.pt + long(rb) * a.pt_stride;
+        srow[j] = long(rb) * g.H + h;
     }
-    const long kv_off = (long(a.beta) * g.H + h) * 2 * 8 * NG;   // (block, head) slab inside a page
-    const float fix_scale = float(1u << a.fix_bits);
+    const uint32_t page_bytes = uint32_t(g.page_bytes);
+    const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG;   // (block, head) slab of page 0
+    int t_lo = 0x7fffffff, t_hi = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+        if (hi[j] > lo[j]) {
+            t_lo = min(t_lo, lo[j]);
+            t_hi = max(t_hi, hi[j]);
+        }
     __syncthreads();
 
-    float M[2] = {-INFINITY, -INFINITY};
-    uint32_t lsum[2] = {0u, 0u};
-    const int t_lo = min(hi[0] > lo[0] ? lo[0] : 0x7fffffff, hi[1] > lo[1] ? lo[1] : 0x7fffffff);
-    const int t_hi = max(hi[0] > lo[0] ? hi[0] : 0, hi[1] > lo[1] ? hi[1] : 0);
-
-    for (int s0 = t_lo; s0 < t_hi; s0 += kSeg) {
-        const int s1 = min(t_hi, s0 + kSeg);
-        float mloc[2] = {-INFINITY, -INFINITY};
-        // page ids of this segment's pages, both requests
-        for (int e = tid; e < 2 * (kSeg / 8); e += kThreadsV2) {
-            const int jj = e / (kSeg / 8), lp = (s0 >> 3) + e % (kSeg / 8);
-            spt[e] = (lp >= (lo[jj] >> 3) && lp < (hi[jj] >> 3)) ? ptr[jj][lp] : 0;
-        }
-        __syncthreads();
-        // ---- phase 1: scores ----
-        // Index rows of the next iteration are fetched while this one is scored.
-        uint32_t ik[2][IW], nk[2][IW];
-        auto fetch_k = [&](int base_, uint32_t (*dst)[IW]) {
-            // Branch-free: lanes outside a request's range read page 0 (always present); their
-            // scores are discarded.
-            const int tk = base_ + lane;
-            const int pi = min(max((tk - s0) >> 3, 0), kSeg / 8 - 1);
+    // Software pipeline over this wave's chunks c, c + NW, ...: page ids two chunks ahead, index rows
+    // and cos/sin one chunk ahead, in two alternating buffers.
+    constexpr int NW = kSThreads / 64;
+    auto in_req = [&](int j, int tau) { return tau >= lo[j] && tau < hi[j]; };
+    auto load_pid = [&](int c, uint32_t (&pid)[R]) {
+        const int tau = c * kChunk + lane;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const long phys = spt[j * (kSeg / 8) + pi];
-                const uint4* row = reinterpret_cast<const uint4*>(a.pool + phys * g.page_bytes + kv_off +
-                                                                  (tk & 7) * NG);
+        for (int j = 0; j < R; ++j)        // a valid column of the page table (unused out of range)
+            pid[j] = uint32_t(ptr[j][max(0, min(tau, hi[j] - 1)) >> 3]);
+    };
+    // Every lane issues the same loads (out-of-range lanes read a valid page through the clamped page id)
+    // and stores (into the pad chunk of the row), so that the loads in flight can be counted exactly
+    // across iterations.
+    auto load_rows = [&](int c, const uint32_t (&pid)[R], uint32_t (&ik)[R][IW], uint4 (&tr)[16]) {
+        const int tau = c * kChunk + lane;
 #pragma unroll
-                for (int w = 0; w < IW / 4; ++w) {
-                    const uint4 v = row[w];
-                    dst[j][4 * w] = v.x; dst[j][4 * w + 1] = v.y; dst[j][4 * w + 2] = v.z; dst[j][4 * w + 3] = v.w;
-                }
+        for (int j = 0; j < R; ++j) {
+            const uint4* row = reinterpret_cast<const uint4*>(slab + uint64_t(pid[j]) * page_bytes + (tau & 7) * NG);
+#pragma unroll
+            for (int w = 0; w < IW / 4; ++w) {
+                const uint4 kv = row[w];
+                ik[j][4 * w] = kv.x; ik[j][4 * w + 1] = kv.y; ik[j][4 * w + 2] = kv.z; ik[j][4 * w + 3] = kv.w;
             }
-        };
-        int base = s0 + wave * 64;
-        if (base < s1) fetch_k(base, ik);
-        for (; base < s1; base += kThreadsV2) {
-            const int tok = base + lane;
-            const int P = __builtin_amdgcn_readfirstlane(g.sink + base);   // position of lane 0 (wave-uniform)
-            if (base + kThreadsV2 < s1) fetch_k(base + kThreadsV2, nk);
-            bool in[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) in[j] = tok >= lo[j] && tok < hi[j] && tok < s1;
-            const_ptr<float> rcP = as_const(a.rc + long(P) * 64);
-            const_ptr<float> rsP = as_const(a.rs + long(P) * 64);
-            float acc[2] = {0.f, 0.f};
-#pragma unroll
-            for (int ch = 0; ch < 8; ++ch) {
-                float cs[8], sn[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float cp = rcP[8 * ch + u], sp = rsP[8 * ch + u];
-                    cs[u] = fmaf(cp, cl[8 * ch + u], -sp * sl[8 * ch + u]);
-                    sn[u] = fmaf(sp, cl[8 * ch + u], cp * sl[8 * ch + u]);
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    if (in[j]) acc[j] = chunk_score<C>(ch, ik[j], cb, qp[j], cs, sn, acc[j]);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (in[j]) {
-                    const float sv = acc[j] * a.scale_log2;
-                    sc[j * kSeg + (tok - s0)] = sv;
-                    mloc[j] = fmaxf(mloc[j], sv);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int w = 0; w < IW; ++w) ik[j][w] = nk[j][w];
         }
-        // ---- block max, rescale ----
+        const int p = min(g.sink + tau, a.rope_len - 1);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const float mw = wave_max(mloc[j]);
-            if (lane == 0) red[j * 8 + wave] = mw;
-        }
-        __syncthreads();
-        float Mn[2];
+        for (int m = 0; m < 16; ++m) tr[m] = a.rope16[long(m) * a.rope_len + p];
+    };
+    auto score_chunk = [&](int c, const uint32_t (&ik)[R][IW], const uint4 (&tr)[16]) {
+        const int tau = c * kChunk + lane;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            Mn[j] = red[j * 8];
-            for (int w = 1; w < kThreadsV2 / 64; ++w) Mn[j] = fmaxf(Mn[j], red[j * 8 + w]);
-            if (Mn[j] > M[j]) {
-                if (M[j] != -INFINITY) {
-                    const float f = exp2f(M[j] - Mn[j]);
-                    for (int e = tid; e < NG * kBinPad; e += kThreadsV2) {
-                        uint32_t* bp = bins + j * NG * kBinPad + e;
-                        *bp = uint32_t(float(*bp) * f + 0.5f);
+        for (int j = 0; j < R; ++j) {
+            const bool in = in_req(j, tau);
+            {
+                float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+                // two halves: frequencies 0..31 use groups [0, HG/2) and [HG, HG + HG/2), 32..63 the rest
+                StaticFor<0, 2>::run([&](auto hc) {
+                    constexpr int hf = decltype(hc)::value;
+                    uint32_t kw[HG][C / 2];     // [lo groups of this half | hi groups of this half]
+                    StaticFor<0, HG>::run([&](auto ic) {
+                        constexpr int i = decltype(ic)::value;
+                        constexpr int gi = (i < HG / 2) ? (hf * HG / 2 + i) : (HG + hf * HG / 2 + i - HG / 2);
+                        const uint32_t off = byte_shl<SH, gi & 3>(ik[j][gi >> 2]);
+                        const unsigned char* pcw = cb + gi * (K * C * 2) + off;
+                        if constexpr (C == 8) {
+                            const uint4 v = *reinterpret_cast<const uint4*>(pcw);
+                            kw[i][0] = v.x; kw[i][1] = v.y; kw[i][2] = v.z; kw[i][3] = v.w;
+                        } else {
+                            const uint2 v = *reinterpret_cast<const uint2*>(pcw);
+                            kw[i][0] = v.x; kw[i][1] = v.y;
+                        }
+                    });
+#pragma unroll
+                    for (int mm = 0; mm < 8; ++mm) {           // RoPE frequencies 4m .. 4m+3
+                        const int m = hf * 8 + mm;
+                        const h2_t c01 = as_h2(tr[m].x), c23 = as_h2(tr[m].y);
+                        const h2_t s01 = as_h2(tr[m].z), s23 = as_h2(tr[m].w);
+                        const h2_t l01 = as_h2(qp[j][4 * m]), l23 = as_h2(qp[j][4 * m + 1]);
+                        const h2_t u01 = as_h2(qp[j][4 * m + 2]), u23 = as_h2(qp[j][4 * m + 3]);
+                        const h2_t pl01 = __builtin_elementwise_fma(c01, l01, s01 * u01);
+                        const h2_t pl23 = __builtin_elementwise_fma(c23, l23, s23 * u23);
+                        const h2_t ph01 = __builtin_elementwise_fma(c01, u01, -(s01 * l01));
+                        const h2_t ph23 = __builtin_elementwise_fma(c23, u23, -(s23 * l23));
+                        uint32_t kl01, kl23, kh01, kh23;
+                        if constexpr (C == 8) {
+                            const int il = mm >> 1, d = (mm & 1) * 2;     // lo group hf*4 + il
+                            kl01 = kw[il][d]; kl23 = kw[il][d + 1];
+                            kh01 = kw[HG / 2 + il][d]; kh23 = kw[HG / 2 + il][d + 1];
+                        } else {
+                            kl01 = kw[mm][0]; kl23 = kw[mm][1];
+                            kh01 = kw[HG / 2 + mm][0]; kh23 = kw[HG / 2 + mm][1];
+                        }
+                        acc0 = dot2h(kl01, pl01, acc0);
+                        acc1 = dot2h(kl23, pl23, acc1);
+                        acc2 = dot2h(kh01, ph01, acc2);
+                        acc3 = dot2h(kh23, ph23, acc3);
                     }
-                    lsum[j] = uint32_t(float(lsum[j]) * f + 0.5f);
+                });
+                const float s_all = (acc0 + acc1) + (acc2 + acc3);
+                a.scores[srow[j] * a.sc_stride + (in ? tau : a.sc_stride - kChunk + lane)] = s_all;
+                // chunk maximum: chunks holding tokens of request j write their slot, others the pad slot
+                const float mw = wave_max_dpp(in ? s_all : -INFINITY);
+                const bool mine = c * kChunk < hi[j] && c * kChunk + kChunk > lo[j];
+                if (lane == 0) a.cmax[srow[j] * a.cm_stride + (mine ? c : a.cm_stride - 1)] = mw;
+            }
+        }
+    };
+    int c = t_lo / kChunk + wave;
+    uint32_t pidA[R], pidB[R];
+    uint32_t ikA[R][IW], ikB[R][IW];
+    uint4 trA[16], trB[16];
+    load_pid(c, pidA);
+    load_pid(c + NW, pidB);
+    load_rows(c, pidA, ikA, trA);
+    load_pid(c + 2 * NW, pidA);
+    while (c * kChunk < t_hi) {
+        load_rows(c + NW, pidB, ikB, trB);
+        load_pid(c + 3 * NW, pidB);
+        score_chunk(c, ikA, trA);
+        c += NW;
+        if (c * kChunk >= t_hi) break;
+        load_rows(c + NW, pidA, ikA, trA);
+        load_pid(c + 3 * NW, pidA);
+        score_chunk(c, ikB, trB);
+        c += NW;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Value pass.  Grid (split, head, request group of R); 256 threads.  The
+// split's maximum per request comes from the score pass's chunk maxima.
+// Each token adds its weight exp2(s - max), in fixed point with fix_bits
+// fraction bits, to one bin per (group, codeword) of its V indices (integer
+// LDS atomics; bins [256 codewords][R*NG slots], slot j*NG + g).  V index
+// bytes sit XOR-rotated by (token & 15) in the pool (byte m holds group
+// m ^ (token & 15)), so at step m the 16 lanes of each LDS phase hit 16
+// distinct groups, hence 16 distinct banks.  Then
+// o = sum_r bin[g][r] * B_t^V[g][r] / sum of weights, with the V slice read
+// from global memory, and the normalised partial and its logsumexp are written.
+// ---------------------------------------------------------------------------
+template <int C, int R>
+__global__ void __launch_bounds__(kSThreads, 2) value_kernel(AttnArgs a) {
+    constexpr int D = 128, K = 256, NG = D / C;
+    constexpr int IW = NG / 4;
+    constexpr int NW = kSThreads / 64;
+    static_assert(R * NG == 64, "one bin row holds R*NG = 64 slots");
+    __shared__ __align__(16) unsigned char smem[kBinBytes + NW * R * D * 4 + NW * R * 4];
+    uint32_t* bins = reinterpret_cast<uint32_t*>(smem);
+    float* wred = reinterpret_cast<float*>(smem + kBinBytes);                    // [waves][R*D]
+    uint32_t* lred = reinterpret_cast<uint32_t*>(wred + NW * R * D);            // [waves][R]
+    const Geo& g = a.geo;
+    const int split = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * R;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int lo[R], hi[R];
+    const bool any = split_ranges<R>(a, split, r0, lo, hi);
+    if (!any) {
+        for (int e = tid; e < R * D; e += kSThreads) {
+            const int j = e / D, d = e % D, rb = r0 + j;
+            if (rb >= a.B) continue;
+            const long row = (long(rb) * g.H + h) * a.S_tot + split;
+            a.part_o[row * D + d] = 0.f;
+            if (d == 0) a.part_lse[row] = -INFINITY;
+        }
+        return;
+    }
+    for (int e = tid; e < kBinBytes / 4; e += kSThreads) bins[e] = 0u;
+
+    const int32_t* ptr[R];
+    long srow[R];
+    float M[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int rb = min(r0 + j, a.B - 1);
+        ptr[j] = a.pt + long(rb) * a.pt_stride;
+        srow[j] = long(rb) * g.H + h;
+        // split maximum from the chunk maxima (at most 32 chunks of 64 tokens per split)
+        const int c0 = lo[j] / kChunk, c1 = (hi[j] + kChunk - 1) / kChunk;
+        const float m = (hi[j] > lo[j] && c0 + lane < c1) ? a.cmax[srow[j] * a.cm_stride + c0 + lane] : -INFINITY;
+        M[j] = wave_max_dpp(m);
+    }
+    const uint32_t page_bytes = uint32_t(g.page_bytes);
+    const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG + 8 * NG;   // value rows
+    const float fix_scale = float(1u << a.fix_bits);
+    int t_lo = 0x7fffffff, t_hi = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+        if (hi[j] > lo[j]) {
+            t_lo = min(t_lo, lo[j]);
+            t_hi = max(t_hi, hi[j]);
+        }
+    __syncthreads();
+
+    // Software pipeline as in the score pass: page ids two chunks ahead, value rows and scores one ahead.
+    auto in_req = [&](int j, int tau) { return tau >= lo[j] && tau < hi[j]; };
+    auto load_pid = [&](int c, uint32_t (&pid)[R]) {
+        const int tau = c * kChunk + lane;
+#pragma unroll
+        for (int j = 0; j < R; ++j) pid[j] = uint32_t(ptr[j][max(0, min(tau, hi[j] - 1)) >> 3]);
+    };
+    auto load_rows = [&](int c, const uint32_t (&pid)[R], uint32_t (&iv)[R][IW], float (&sc)[R]) {
+        const int tau = c * kChunk + lane;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const uint4* row = reinterpret_cast<const uint4*>(slab + uint64_t(pid[j]) * page_bytes + (tau & 7) * NG);
+#pragma unroll
+            for (int w = 0; w < IW / 4; ++w) {
+                const uint4 vv = row[w];
+                iv[j][4 * w] = vv.x; iv[j][4 * w + 1] = vv.y; iv[j][4 * w + 2] = vv.z; iv[j][4 * w + 3] = vv.w;
+            }
+            sc[j] = a.scores[srow[j] * a.sc_stride + (in_req(j, tau) ? tau : a.sc_stride - kChunk + lane)];
+        }
+    };
+    auto bin_chunk = [&](int c, const uint32_t (&iv)[R][IW], const float (&sc)[R]) {
+        const int tau = c * kChunk + lane;
+        const uint32_t rot = uint32_t(tau) & 15u;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            // lanes out of range add 0 (their index rows are valid memory, their bins any)
+            const uint32_t u = in_req(j, tau) ? uint32_t(fmaf(__builtin_amdgcn_exp2f(sc[j] - M[j]), fix_scale, 0.5f))
+                                              : 0u;
+            StaticFor<0, NG>::run([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                // bin byte address: [4 * group, codeword, 0, 0] with group = m ^ rot (one v_perm)
+                constexpr uint32_t sel = 0x0c0c0000u | (uint32_t(4 + (m & 3)) << 8);
+                const uint32_t addr = __builtin_amdgcn_perm(iv[j][m >> 2], 4u * (uint32_t(m) ^ rot), sel);
+                uint32_t* bin = static_cast<uint32_t*>(__builtin_assume_aligned(smem + addr + 4 * j * NG, 4));
+                __hip_atomic_fetch_add(bin, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            });
+        }
+    };
+    {
+        int c = t_lo / kChunk + wave;
+        uint32_t pidA[R], pidB[R];
+        uint32_t ivA[R][IW], ivB[R][IW];
+        float scA[R], scB[R];
+        load_pid(c, pidA);
+        load_pid(c + NW, pidB);
+        load_rows(c, pidA, ivA, scA);
+        load_pid(c + 2 * NW, pidA);
+        while (c * kChunk < t_hi) {
+            load_rows(c + NW, pidB, ivB, scB);
+            load_pid(c + 3 * NW, pidB);
+            bin_chunk(c, ivA, scA);
+            c += NW;
+            if (c * kChunk >= t_hi) break;
+            load_rows(c + NW, pidA, ivA, scA);
+            load_pid(c + 3 * NW, pidA);
+            bin_chunk(c, ivB, scB);
+            c += NW;
+        }
+    }
+    __syncthreads();
+
+    // ---- o = sum_r bin[g][r] * B_t^V[g][r]: wave w takes codewords [64w, 64w + 64), lane (j, g) ----
+    {
+        const int jj = lane / NG, gg = lane % NG;
+        const uint16_t* vsl = static_cast<const uint16_t*>(a.slice_v) + h * a.slice_hstride + gg * K * C;
+        float o[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) o[i] = 0.f;
+        uint32_t l0 = 0u;
+        const int rbeg = wave * (K / NW);
+        for (int rc = rbeg; rc < rbeg + K / NW; rc += 16) {
+            uint32_t vw[16][C / 2];
+            uint32_t bv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if constexpr (C == 8) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(vsl + (rc + u) * C);
+                    vw[u][0] = w.x; vw[u][1] = w.y; vw[u][2] = w.z; vw[u][3] = w.w;
+                } else {
+                    const uint2 w = *reinterpret_cast<const uint2*>(vsl + (rc + u) * C);
+                    vw[u][0] = w.x; vw[u][1] = w.y;
                 }
-                M[j] = Mn[j];
+                bv[u] = bins[(rc + u) * 64 + lane];
             }
-        }
-        __syncthreads();
-        // ---- phase 2: V bins ----
-        uint32_t iv[2][IW], nv[2][IW];
-        auto fetch_v = [&](int tk, uint32_t (*dst)[IW]) {
-            const int pi = min(max((tk - s0) >> 3, 0), kSeg / 8 - 1);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const long phys = spt[j * (kSeg / 8) + pi];
-                const uint4* row = reinterpret_cast<const uint4*>(a.pool + phys * g.page_bytes + kv_off + 8 * NG +
-                                                                  (tk & 7) * NG);
+            for (int u = 0; u < 16; ++u) {
+                l0 += gg == 0 ? bv[u] : 0u;
+                const float bw = float(bv[u]);
 #pragma unroll
-                for (int w = 0; w < IW / 4; ++w) {
-                    const uint4 v = row[w];
-                    dst[j][4 * w] = v.x; dst[j][4 * w + 1] = v.y; dst[j][4 * w + 2] = v.z; dst[j][4 * w + 3] = v.w;
+                for (int i = 0; i < C / 2; ++i) {
+                    o[2 * i] = fmaf(bw, bf16_lo(vw[u][i]), o[2 * i]);
+                    o[2 * i + 1] = fmaf(bw, bf16_hi(vw[u][i]), o[2 * i + 1]);
                 }
             }
-        };
-        int tok = s0 + tid;
-        if (tok < s1) fetch_v(tok, iv);
-        for (; tok < s1; tok += kThreadsV2) {
-            if (tok + kThreadsV2 < s1) fetch_v(tok + kThreadsV2, nv);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (tok >= lo[j] && tok < hi[j]) {
-                    const float w = exp2f(sc[j * kSeg + (tok - s0)] - M[j]);
-                    const uint32_t u = uint32_t(fmaf(w, fix_scale, 0.5f));
-                    lsum[j] += u;
-                    uint32_t* bj = bins + j * NG * kBinPad;
-#pragma unroll
-                    for (int grp = 0; grp < NG; ++grp)
-                        atomicAdd(bj + grp * kBinPad + ((iv[j][grp >> 2] >> (8 * (grp & 3))) & 0xff), u);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int w = 0; w < IW; ++w) iv[j][w] = nv[j][w];
-        }
-    }
-    // ---- totals ----
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        uint32_t t = lsum[j];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
-        if (lane == 0) reinterpret_cast<uint32_t*>(red)[16 + j * 8 + wave] = t;
-    }
-    __syncthreads();
-    {   // stage B_t^V over B_t^K with a 16-B pad per group row
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_v) +
-                                                          h * a.slice_hstride);
-        uint4* dst = reinterpret_cast<uint4*>(cb);
-        constexpr int row16 = K * C * 2 / 16;          // 16-B units per group row
-        for (int e = tid; e < NG * row16; e += kThreadsV2) dst[(e / row16) * (row16 + 1) + e % row16] = src[e];
-    }
-    __syncthreads();
-    // ---- o = sum_r bin[g][r] B_t^V[g][r] ----
-    constexpr int RCH = kThreadsV2 / (2 * NG);       // codeword chunks per (request, group): 16 (C=8), 8 (C=4)
-    constexpr int RPC = K / RCH;                     // codewords per chunk
-    const int j = tid / (kThreadsV2 / 2);
-    const int grp = (tid / RCH) & (NG - 1);
-    const int rc = tid & (RCH - 1);
-    float o[C];
-#pragma unroll
-    for (int i = 0; i < C; ++i) o[i] = 0.f;
-    const uint32_t* bj = bins + (j * NG + grp) * kBinPad;
-    const uint16_t* vrow = cb + grp * (K * C + 8);
-    for (int k = 0; k < RPC; ++k) {
-        const int r = rc + RCH * k;
-        const float bw = float(bj[r]);
-        float v[C];
-        if constexpr (C == 8) {
-            const uint4 w = *reinterpret_cast<const uint4*>(vrow + r * 8);
-            v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-            v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-        } else {
-            const uint2 w = *reinterpret_cast<const uint2*>(vrow + r * 4);
-            v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
         }
 #pragma unroll
-        for (int i = 0; i < C; ++i) o[i] = fmaf(bw, v[i], o[i]);
+        for (int i = 0; i < C; ++i) wred[wave * (R * D) + jj * D + gg * C + i] = o[i];
+        if (gg == 0) lred[wave * R + jj] = l0;
     }
-    // reduce over the RCH chunks (adjacent lanes)
-#pragma unroll
-    for (int i = 0; i < C; ++i)
-#pragma unroll
-        for (int off = 1; off < RCH; off <<= 1) o[i] += __shfl_xor(o[i], off, 64);
-    float* ored = reinterpret_cast<float*>(bins);    // bins are consumed above: reuse [2][128]
     __syncthreads();
-    if (rc == 0)
-#pragma unroll
-        for (int i = 0; i < C; ++i) ored[j * D + grp * C + i] = o[i];
-    __syncthreads();
-    if (tid < 256) {
-        const int jj = tid >> 7, d = tid & 127;
-        const int rb = r0 + jj;
-        if (rb < a.B) {
-            const long orow = (long(rb) * g.H + h) * a.S_tot + split;
-            if (hi[jj] > lo[jj]) {
-                const uint32_t* tr = reinterpret_cast<const uint32_t*>(red) + 16 + jj * 8;
-                float L = 0.f;                                                              // fixed point
-                for (int w = 0; w < kThreadsV2 / 64; ++w) L += float(tr[w]);
-                a.part_o[orow * D + d] = ored[jj * D + d] / L;
-                if (d == 0) a.part_lse[orow] = (M[jj] + log2f(L / fix_scale)) * kLn2;
-            } else {
-                a.part_o[orow * D + d] = 0.f;
-                if (d == 0) a.part_lse[orow] = -INFINITY;
-            }
+    for (int e = tid; e < R * D; e += kSThreads) {
+        const int j = e / D, d = e % D, rb = r0 + j;
+        if (rb >= a.B) continue;
+        const long orow = (long(rb) * g.H + h) * a.S_tot + split;
+        if (hi[j] <= lo[j]) {
+            a.part_o[orow * D + d] = 0.f;
+            if (d == 0) a.part_lse[orow] = -INFINITY;
+            continue;
         }
+        float acc = 0.f;
+        double L = 0.0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            acc += wred[w * (R * D) + e];
+            L += double(lred[w * R + j]);
+        }
+        a.part_o[orow * D + d] = float(double(acc) / L);
+        if (d == 0) a.part_lse[orow] = (M[j] + float(log2(L) - double(a.fix_bits))) * kLn2;
     }
+}
+
+// Query rows for score_kernel: 16 chunks of 4 dwords per (request, head),
+// chunk m = fp16 pairs (q_{4m}, q_{4m+1}), (q_{4m+2}, q_{4m+3}),
+// (q_{64+4m}, q_{65+4m}), (q_{66+4m}, q_{67+4m}), each value q * scale.
+__global__ void pack_q_f16_kernel(const uint16_t* __restrict__ q, float scale, uint32_t* __restrict__ qpack) {
+    const long row = blockIdx.x;
+    const int t = threadIdx.x;            // 64 threads: dword t
+    const int m = t >> 2, k = t & 3;
+    const int ch = (k < 2 ? 0 : 64) + 4 * m + 2 * (k & 1);
+    const uint16_t* qr = q + row * 128;
+    const h2_t v = {(_Float16)(bf16_to_f32(qr[ch]) * scale), (_Float16)(bf16_to_f32(qr[ch + 1]) * scale)};
+    qpack[row * 64 + t] = __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -780,14 +846,49 @@ __global__ void merge_kernel(const float* __restrict__ po, const float* __restri
     if (lse_out && threadIdx.x == 0) lse_out[n] = lse;
 }
 
+
+int max_index_pages(const Geo& g, int max_len) { return std::max(0, (max_len - g.sink - g.W) / g.page); }
+
+// Requests per workgroup of the bf16 index-page kernel (R * NG = 64 bin slots).
+int reqs_per_wg(const Geo& g) { return g.c == 8 ? 4 : 2; }
+
 int choose_splits(const Geo& g, int B, int max_len) {
-    const int max_pages = std::max(0, (max_len - g.sink - g.W) / g.page);
+    const int max_pages = max_index_pages(g, max_len);
     if (max_pages == 0) return 1;
-    const int wgs = ((B + 1) / 2) * g.H;
-    int s = ceil_div(512, std::max(1, wgs));
-    s = std::max(s, ceil_div(max_pages, 256));          // at most 256 pages (2048 tokens) per split
-    s = std::min(s, std::max(1, ceil_div(max_pages, 16)));
+    // Splits of at most 192 pages (1536 tokens): the fixed-point softmax weights keep 21 fraction bits.
+    int s = ceil_div(max_pages, 192);
+    // Enough (split, head, request group) workgroups for 256 CUs x 2, splits of >= 16 pages.
+    const int pairs = ceil_div(B, reqs_per_wg(g)) * g.H;
+    s = std::max(s, std::min(ceil_div(512, std::max(1, pairs)), ceil_div(max_pages, 16)));
     return std::max(1, std::min(s, 1024));
+}
+
+// Pages per split: a multiple of 8 (64 tokens), so that score chunks never straddle splits.
+int pages_per_split(int max_pages, int S) { return max_pages > 0 ? ceil_div(ceil_div(max_pages, S), 8) * 8 : 8; }
+
+// Scratch of the index-page pass inside a workspace: packed queries, scores of the index tokens
+// (rows of idx_stride, a multiple of 64) and the maximum of every 64-token chunk.
+struct QuantScratch {
+    size_t qpack, scores, cmax, bytes;
+    long sc_stride, cm_stride;
+};
+QuantScratch quant_scratch(const Geo& g, int B, int max_len) {
+    QuantScratch q{};
+    const long rows = long(B) * g.H;
+    // index tokens rounded up to 64, plus one pad chunk written by lanes past a request's range
+    q.sc_stride = long(ceil_div(long(max_index_pages(g, max_len)) * g.page, 64)) * 64 + 64;
+    q.cm_stride = q.sc_stride / 64;
+    q.qpack = 0;
+    q.scores = q.qpack + size_t(rows) * 64 * sizeof(uint32_t);
+    q.cmax = q.scores + size_t(rows) * q.sc_stride * sizeof(float);
+    q.bytes = q.cmax + size_t(rows) * q.cm_stride * sizeof(float);
+    return q;
+}
+
+int ceil_log2(long x) {
+    int r = 0;
+    while ((1L << r) < x) ++r;
+    return r;
 }
 
 }  // namespace
@@ -800,13 +901,13 @@ extern "C" size_t lvq_decode_attn_workspace(const lvq_geom* gp, int32_t B, int32
     if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 0 || num_splits < 0) return 0;
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
     const size_t rows = size_t(B) * g.H * (S + 1);
-    return rows * g.D * sizeof(float) + rows * sizeof(float) + size_t(B) * g.H * 128 * sizeof(uint32_t);
+    return rows * g.D * sizeof(float) + rows * sizeof(float) + quant_scratch(g, B, max_len).bytes;
 }
 
-extern "C" size_t lvq_quant_partial_workspace(const lvq_geom* gp, int32_t B) {
+extern "C" size_t lvq_quant_partial_workspace(const lvq_geom* gp, int32_t B, int32_t max_len) {
     Geo g;
-    if (validate_geom(gp, &g) != LVQ_OK || B < 0) return 0;
-    return size_t(B) * g.H * 128 * sizeof(uint32_t);
+    if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 0) return 0;
+    return quant_scratch(g, B, max_len).bytes;
 }
 
 namespace lvq {
@@ -815,8 +916,8 @@ namespace {
 // Checks shared by the attention entry points; fills the kernel arguments
 // except the partial buffers.
 lvq_status prepare(const char* fn, const lvq_geom* gp, int32_t step, const void* q, const int32_t* seq_len,
-                   int32_t max_len, const float* rope_cos, const float* rope_sin, int32_t rope_len, float sm_scale,
-                   int32_t B, AttnArgs* a) {
+                   int32_t max_len, const float* rope_cos, const float* rope_sin, const void* rope_f16,
+                   int32_t rope_len, float sm_scale, int32_t B, AttnArgs* a, bool need_f16 = true) {
     Geo& g = a->geo;
     lvq_status st = validate_geom(gp, &g);
     if (st != LVQ_OK) return st;
@@ -825,14 +926,17 @@ lvq_status prepare(const char* fn, const lvq_geom* gp, int32_t step, const void*
     LVQ_REQUIRE(max_len <= rope_len, LVQ_ERR_INVALID_ARG, "%s: max_len %d exceeds rope_len %d", fn, max_len,
                 rope_len);
     LVQ_REQUIRE(std::isfinite(sm_scale), LVQ_ERR_INVALID_ARG, "%s: sm_scale not finite", fn);
-    LVQ_REQUIRE(B <= 65535 * 2, LVQ_ERR_UNSUPPORTED, "%s: batch too large", fn);
+    LVQ_REQUIRE(B <= 65535, LVQ_ERR_UNSUPPORTED, "%s: batch too large", fn);
     LVQ_REQUIRE(B == 0 || (q && seq_len && rope_cos && rope_sin), LVQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    LVQ_REQUIRE(B == 0 || !need_f16 || g.cb != LVQ_BF16 || rope_f16, LVQ_ERR_INVALID_ARG,
+                "%s: bf16 codebooks need the packed fp16 RoPE table", fn);
     a->step = step;
     a->beta = step / g.Tc;
     a->q = static_cast<const uint16_t*>(q);
     a->seq_len = seq_len;
     a->rc = rope_cos;
     a->rs = rope_sin;
+    a->rope16 = static_cast<const uint4*>(rope_f16);
     a->scale_log2 = sm_scale * kLog2e;
     a->B = B;
     a->max_len = max_len;
@@ -840,35 +944,35 @@ lvq_status prepare(const char* fn, const lvq_geom* gp, int32_t step, const void*
     return LVQ_OK;
 }
 
-int max_index_pages(const Geo& g, int max_len) { return std::max(0, (max_len - g.sink - g.W) / g.page); }
-
-int ceil_log2(long x) {
-    int r = 0;
-    while ((1L << r) < x) ++r;
-    return r;
-}
-
-// Packs q into a.qpack (bf16 codebooks only) and launches the index-page partial.
-lvq_status launch_quant(AttnArgs& a, uint32_t* qpack, hipStream_t stream) {
+// Packs q (bf16 codebooks) and launches the index-page partial: the score pass, then the value pass.
+lvq_status launch_quant(AttnArgs& a, void* scratch, hipStream_t stream) {
     const Geo& g = a.geo;
-    const dim3 grid(a.num_splits, g.H, (a.B + 1) / 2);
     if (g.cb == LVQ_BF16) {
-        hipLaunchKernelGGL(pack_q_kernel, dim3(a.B * g.H), dim3(64), 0, stream, a.q, qpack);
+        const QuantScratch qs = quant_scratch(g, a.B, a.max_len);
+        unsigned char* base = static_cast<unsigned char*>(scratch);
+        a.qpack = reinterpret_cast<uint32_t*>(base + qs.qpack);
+        a.scores = reinterpret_cast<float*>(base + qs.scores);
+        a.cmax = reinterpret_cast<float*>(base + qs.cmax);
+        a.sc_stride = qs.sc_stride;
+        a.cm_stride = qs.cm_stride;
+        hipLaunchKernelGGL(pack_q_f16_kernel, dim3(a.B * g.H), dim3(64), 0, stream, a.q, a.scale_log2,
+                           const_cast<uint32_t*>(a.qpack));
         lvq_status st = check_launch("query packing");
         if (st != LVQ_OK) return st;
-        a.qpack = qpack;
-        a.fix_bits = std::max(8, std::min(20, 31 - ceil_log2(long(a.pps) * g.page)));
-        const size_t lds = size_t(g.NG) * (g.K * g.c + 8) * 2 + size_t(2) * g.NG * kBinPad * 4 +
-                           size_t(2) * kSeg * 4 + 32 * 4 + size_t(2) * (kSeg / 8) * 4;
-        auto kern = g.c == 8 ? quant_v2_kernel<8> : quant_v2_kernel<4>;
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                int(lds)) != hipSuccess) {
-            (void)hipGetLastError();
-            set_error("quantized partial: cannot reserve %zu bytes of LDS", lds);
-            return LVQ_ERR_HIP;
-        }
-        hipLaunchKernelGGL(kern, grid, dim3(kThreadsV2), lds, stream, a);
+        a.fix_bits = 32 - ceil_log2(long(a.pps) * g.page + 1);
+        const int R = reqs_per_wg(g);
+        const dim3 grid(a.num_splits, g.H, ceil_div(a.B, R));
+        if (g.c == 8)
+            hipLaunchKernelGGL((score_kernel<8, 4>), grid, dim3(kSThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((score_kernel<4, 2>), grid, dim3(kSThreads), 0, stream, a);
+        if ((st = check_launch("score pass")) != LVQ_OK) return st;
+        if (g.c == 8)
+            hipLaunchKernelGGL((value_kernel<8, 4>), grid, dim3(kSThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((value_kernel<4, 2>), grid, dim3(kSThreads), 0, stream, a);
     } else {
+        const dim3 grid(a.num_splits, g.H, (a.B + 1) / 2);
         const size_t red_bytes = 4 * (g.D + 2) * sizeof(float);
         if (g.c == 8)
             hipLaunchKernelGGL((quant_partial_kernel<8, float, false>), grid, dim3(256), red_bytes, stream, a);
@@ -899,12 +1003,13 @@ void set_slices(AttnArgs* a, const void* slices) {
 extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
                                         const int32_t* page_table, int32_t pt_stride, const int32_t* seq_len,
                                         int32_t max_len, const void* slices, const float* rope_cos,
-                                        const float* rope_sin, int32_t rope_len, float sm_scale, float* part_o,
+                                        const float* rope_sin, const void* rope_f16, int32_t rope_len,
+                                        float sm_scale, float* part_o,
                                         float* part_lse, int32_t num_splits, int32_t S_tot, void* ws,
                                         size_t ws_bytes, int32_t B, hipStream_t stream) {
     AttnArgs a{};
-    lvq_status st = prepare("lvq_quant_partial", gp, step, q, seq_len, max_len, rope_cos, rope_sin, rope_len,
-                            sm_scale, B, &a);
+    lvq_status st = prepare("lvq_quant_partial", gp, step, q, seq_len, max_len, rope_cos, rope_sin, rope_f16,
+                            rope_len, sm_scale, B, &a);
     if (st != LVQ_OK) return st;
     const Geo& g = a.geo;
     LVQ_REQUIRE(num_splits >= 1 && num_splits <= 1024 && S_tot >= num_splits, LVQ_ERR_INVALID_ARG,
@@ -912,8 +1017,9 @@ extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const 
     if (B == 0) return LVQ_OK;
     const int max_pages = max_index_pages(g, max_len);
     LVQ_REQUIRE(slices && part_o && part_lse && ws, LVQ_ERR_INVALID_ARG, "lvq_quant_partial: NULL pointer");
-    LVQ_REQUIRE(ws_bytes >= lvq_quant_partial_workspace(gp, B), LVQ_ERR_WORKSPACE,
-                "lvq_quant_partial: workspace %zu < %zu bytes", ws_bytes, lvq_quant_partial_workspace(gp, B));
+    LVQ_REQUIRE(ws_bytes >= lvq_quant_partial_workspace(gp, B, max_len), LVQ_ERR_WORKSPACE,
+                "lvq_quant_partial: workspace %zu < %zu bytes", ws_bytes,
+                lvq_quant_partial_workspace(gp, B, max_len));
     LVQ_REQUIRE(max_pages == 0 || (pool && page_table), LVQ_ERR_INVALID_ARG,
                 "lvq_quant_partial: NULL pool or page table");
     LVQ_REQUIRE(pt_stride >= max_pages, LVQ_ERR_INVALID_ARG, "lvq_quant_partial: pt_stride %d < %d pages",
@@ -926,8 +1032,8 @@ extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const 
     a.part_lse = part_lse;
     a.S_tot = S_tot;
     a.num_splits = num_splits;
-    a.pps = max_pages > 0 ? ceil_div(max_pages, num_splits) : 1;
-    return launch_quant(a, static_cast<uint32_t*>(ws), stream);
+    a.pps = pages_per_split(max_pages, num_splits);
+    return launch_quant(a, ws, stream);
 }
 
 extern "C" lvq_status lvq_window_partial(const lvq_geom* gp, int32_t step, const void* q, const int32_t* seq_len,
@@ -936,8 +1042,8 @@ extern "C" lvq_status lvq_window_partial(const lvq_geom* gp, int32_t step, const
                                          float sm_scale, float* part_o, float* part_lse, int32_t slot,
                                          int32_t S_tot, int32_t B, hipStream_t stream) {
     AttnArgs a{};
-    lvq_status st = prepare("lvq_window_partial", gp, step, q, seq_len, max_len, rope_cos, rope_sin, rope_len,
-                            sm_scale, B, &a);
+    lvq_status st = prepare("lvq_window_partial", gp, step, q, seq_len, max_len, rope_cos, rope_sin, nullptr,
+                            rope_len, sm_scale, B, &a, false);
     if (st != LVQ_OK) return st;
     LVQ_REQUIRE(slot >= 0 && slot < S_tot, LVQ_ERR_INVALID_ARG, "lvq_window_partial: slot %d of %d", slot, S_tot);
     if (B == 0) return LVQ_OK;
@@ -954,12 +1060,13 @@ extern "C" lvq_status lvq_window_partial(const lvq_geom* gp, int32_t step, const
 extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
                                       const int32_t* page_table, int32_t pt_stride, const int32_t* seq_len,
                                       int32_t max_len, const void* win_k, const void* win_v, const void* slices,
-                                      const float* rope_cos, const float* rope_sin, int32_t rope_len,
-                                      float sm_scale, float* out, float* lse_out, void* ws, size_t ws_bytes,
+                                      const float* rope_cos, const float* rope_sin, const void* rope_f16,
+                                      int32_t rope_len, float sm_scale, float* out, float* lse_out, void* ws,
+                                      size_t ws_bytes,
                                       int32_t num_splits, int32_t B, hipStream_t stream) {
     AttnArgs a{};
-    lvq_status st = prepare("lvq_decode_attn", gp, step, q, seq_len, max_len, rope_cos, rope_sin, rope_len,
-                            sm_scale, B, &a);
+    lvq_status st = prepare("lvq_decode_attn", gp, step, q, seq_len, max_len, rope_cos, rope_sin, rope_f16,
+                            rope_len, sm_scale, B, &a);
     if (st != LVQ_OK) return st;
     const Geo& g = a.geo;
     LVQ_REQUIRE(num_splits >= 0 && num_splits <= 1024, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: num_splits %d",
@@ -987,9 +1094,8 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
     a.part_lse = a.part_o + rows * g.D;
     a.S_tot = S + 1;
     a.num_splits = S;
-    a.pps = max_pages > 0 ? ceil_div(max_pages, S) : 1;
-    uint32_t* qpack = reinterpret_cast<uint32_t*>(a.part_lse + rows);
-    if ((st = launch_quant(a, qpack, stream)) != LVQ_OK) return st;
+    a.pps = pages_per_split(max_pages, S);
+    if ((st = launch_quant(a, a.part_lse + rows, stream)) != LVQ_OK) return st;
     if ((st = launch_window(a, stream)) != LVQ_OK) return st;
     hipLaunchKernelGGL(merge_kernel, dim3(B * g.H), dim3(128), 0, stream, a.part_o, a.part_lse, S + 1, g.D, out,
                        lse_out);

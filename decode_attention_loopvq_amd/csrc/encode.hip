@@ -50,6 +50,35 @@ __global__ void rope_table_kernel(int len, int D, double base, float* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Packed fp16 table for the index-page pass: chunk m (frequencies 4m..4m+3)
+// of position p at out[(m * len + p) * 8 ..]: cos x4 then sin x4.
+// ---------------------------------------------------------------------------
+// fp64 -> binary16 with one rounding (nearest even): round to fp32 with
+// round-to-odd first (fp32 keeps more than two extra bits), then RNE.
+__device__ __forceinline__ _Float16 f64_to_f16_rn(double x) {
+    float f = float(x);
+    if (double(f) != x) {
+        uint32_t u = __float_as_uint(f);
+        if (fabs(double(f)) > fabs(x)) --u;      // truncate toward zero
+        f = __uint_as_float(u | 1u);             // inexact: odd last bit
+    }
+    return (_Float16)f;
+}
+
+__global__ void rope_f16_kernel(int len, double base, _Float16* __restrict__ out) {
+    const long total = long(len) * 64;
+    for (long e = blockIdx.x * long(blockDim.x) + threadIdx.x; e < total; e += long(gridDim.x) * blockDim.x) {
+        const int p = int(e / 64), i = int(e % 64);
+        const double theta = pow(base, -2.0 * double(i) / 128.0);
+        const double ang = double(p) * theta;
+        const int m = i >> 2, k = i & 3;
+        _Float16* o = out + (long(m) * len + p) * 8;
+        o[k] = f64_to_f16_rn(cos(ang));
+        o[4 + k] = f64_to_f16_rn(sin(ang));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Encode: one workgroup per (page, head, K|V, request); one thread per
 // (token of the page, index group).  The nearest codeword is found by a
 // direct-difference scan in fp64 with each product and sum rounded
@@ -61,6 +90,9 @@ template <>
 __device__ __forceinline__ double cb_elem<uint16_t>(const uint16_t* p) { return double(bf16_to_f32(*p)); }
 template <>
 __device__ __forceinline__ double cb_elem<float>(const float* p) { return double(*p); }
+
+// Index-token number (from the first paged position) of token i of logical page lp.
+__device__ __forceinline__ int slot_token(int lp, int i, int page) { return lp * page + i; }
 
 template <typename CB>
 __global__ void encode_scan_kernel(Geo geo, int block, const uint16_t* __restrict__ xk,
@@ -107,7 +139,10 @@ __global__ void encode_scan_kernel(Geo geo, int block, const uint16_t* __restric
             best_r = r;
         }
     }
-    pool[phys * geo.page_bytes + ((long(block) * geo.H + h) * 2 + kv) * geo.page * NG + i_tok * NG + g] =
+    // Value rows are XOR-rotated by the index-token number (layout in lvq.h).
+    const int tau = slot_token(lp, i_tok, geo.page);
+    const int byte = kv == 0 ? g : (g ^ (tau & 15));
+    pool[phys * geo.page_bytes + ((long(block) * geo.H + h) * 2 + kv) * geo.page * NG + i_tok * NG + byte] =
         uint8_t(best_r);
 }
 
@@ -151,6 +186,16 @@ extern "C" lvq_status lvq_rope_table(int32_t len, int32_t D, double base, float*
     hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, len, D, base,
                        cos_out, sin_out);
     return check_launch("lvq_rope_table");
+}
+
+extern "C" lvq_status lvq_rope_table_f16(int32_t len, int32_t D, double base, void* out, hipStream_t stream) {
+    LVQ_REQUIRE(len > 0, LVQ_ERR_INVALID_ARG, "lvq_rope_table_f16: bad len=%d", len);
+    LVQ_REQUIRE(D == 128, LVQ_ERR_UNSUPPORTED, "lvq_rope_table_f16: D=%d (128 supported)", D);
+    LVQ_REQUIRE(base > 1.0, LVQ_ERR_INVALID_ARG, "lvq_rope_table_f16: base must exceed 1");
+    LVQ_REQUIRE(out, LVQ_ERR_INVALID_ARG, "lvq_rope_table_f16: NULL pointer");
+    hipLaunchKernelGGL(rope_f16_kernel, dim3(grid_for(long(len) * 64, 256)), dim3(256), 0, stream, len, base,
+                       static_cast<_Float16*>(out));
+    return check_launch("lvq_rope_table_f16");
 }
 
 extern "C" lvq_status lvq_encode(const lvq_geom* g, int32_t block, const void* x_k, const void* x_v,

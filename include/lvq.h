@@ -89,12 +89,20 @@ LVQ_API const char* lvq_last_error(void);
  *  slices     [T][H][2][NG][K][c]   slice[t][h][kv][g][r][i] =
  *             codebooks[t/Tc][h][kv][g][r][i*Tc + t%Tc]       cb_dtype
  *  pool       [P][NB][H][2][page][NG] uint8 index pages; one physical page
- *             holds 8 tokens of one request for every block and head
+ *             holds 8 tokens of one request for every block and head.  Key
+ *             rows are in group order; a value row of index-token tau
+ *             (counted from the first paged position) is XOR-rotated: byte m
+ *             holds the index of group m ^ (tau & 15).  Attention bins value
+ *             weights per (group, codeword) and the rotation lets the lanes
+ *             of one LDS phase update 16 distinct groups.
  *  page_table [B][pt_stride] int32, logical page -> physical page
  *  window     [B][T][H][Wcap][D] bf16, Wcap = sink + W + page; pre-RoPE
  *             K (and separately V) of every loop step; position p < sink sits
  *             in slot p, position p >= sink in slot sink + (p - sink) % (W + page)
  *  rope       cos, sin fp32 [rope_len][D/2]: cos/sin(p * base^(-2i/D))
+ *  rope_f16   packed fp16 copy for the index-page kernel (D = 128):
+ *             [16 chunks][rope_len][8 halves]; chunk m of position p holds
+ *             cos of frequencies 4m..4m+3, then sin of the same four
  */
 typedef struct {
     int32_t D, T, Tc, G, K, page, sink, window, H, cb_dtype;
@@ -116,6 +124,15 @@ LVQ_API lvq_status lvq_slice_codebooks(const lvq_geom* g, const void* codebooks,
  */
 LVQ_API lvq_status lvq_rope_table(int32_t len, int32_t D, double base, float* cos_out, float* sin_out,
                           hipStream_t stream);
+
+/*
+ * The packed fp16 RoPE table (layout rope_f16 above): each cos/sin is
+ * evaluated in fp64 and rounded once to binary16.  D must be 128.  out holds
+ * len * 256 bytes.  The index-page pass forms its scores from it in packed
+ * half precision (q turned back by the key's angle, dotted with the key in
+ * fp32 accumulation).
+ */
+LVQ_API lvq_status lvq_rope_table_f16(int32_t len, int32_t D, double base, void* out, hipStream_t stream);
 
 /*
  * Encode index pages of loop block `block` ("method steps", step 4; Figure 5):
@@ -160,12 +177,23 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  * positions come from the window buffers; keys are rotated at their absolute
  * position.  The index pages are attended in `num_splits` splits per request
  * (Flash-Decoding) and the bf16 window by a second kernel; a third merges all
- * partials exactly through logsumexp.  Two requests share one workgroup
- * (and with it the codebook slice and RoPE table loads).
+ * partials exactly through logsumexp.  With bf16 codebooks the index pages
+ * take two passes: one scores every index token (kept in the workspace), the
+ * next turns the scores into softmax weights and accumulates them per
+ * (group, codeword) of the value indices.  With bf16 codebooks four requests
+ * (two when c = 4) share one workgroup and with it the codebook slice and
+ * the RoPE table loads.
  *
  *  q          bf16 [B][H][D], already rotated at position seq_len[b] - 1.
  *  seq_len    device int32 [B], 1 <= seq_len[b] <= max_len <= rope_len.
  *  slices     slices of ALL steps (layout above); the call reads step `step`.
+ *             bf16 slice entries must lie within the binary16 range
+ *             (|x| <= 65504): the index-page pass converts the step's key
+ *             slice to fp16 (exact for |x| >= 2^-14, absolute error below
+ *             2^-25 under that).
+ *  rope_cos, rope_sin  fp32 tables (lvq_rope_table), rope_len rows each.
+ *  rope_f16   packed fp16 table (lvq_rope_table_f16) with the same rope_len;
+ *             required for bf16 codebooks, ignored (may be NULL) for fp32.
  *  out        fp32 [B][H][D];  lse_out fp32 [B][H] or NULL.
  *  ws         device workspace of at least lvq_decode_attn_workspace() bytes.
  *  num_splits 0 lets the library choose; otherwise 1..1024.
@@ -175,7 +203,7 @@ LVQ_API lvq_status lvq_decode_attn(const lvq_geom* g, int32_t step, const void* 
                            const int32_t* seq_len, int32_t max_len,
                            const void* win_k, const void* win_v,
                            const void* slices, const float* rope_cos, const float* rope_sin,
-                           int32_t rope_len, float sm_scale, float* out, float* lse_out,
+                           const void* rope_f16, int32_t rope_len, float sm_scale, float* out, float* lse_out,
                            void* ws, size_t ws_bytes, int32_t num_splits, int32_t B,
                            hipStream_t stream);
 
@@ -193,9 +221,12 @@ LVQ_API int32_t lvq_decode_attn_splits(const lvq_geom* g, int32_t B, int32_t max
  * lvq_quant_partial: the index pages of each request are cut into
  *   num_splits ranges of ceil(max_pages / num_splits) pages and split s writes
  *   slot s; an empty range writes part_o = 0, part_lse = -inf.
- *   S_tot >= num_splits.  Two requests share one workgroup.  ws is device
- *   scratch of at least lvq_quant_partial_workspace(g, B) bytes (the query
- *   repacked into RoPE pairs).
+ *   S_tot >= num_splits.  Splits cover ceil(ceil(max_pages / num_splits) / 8) * 8
+ *   pages each (later ones may be empty).  ws is device scratch of at least
+ *   lvq_quant_partial_workspace(g, B, max_len) bytes: the query repacked as
+ *   fp16 (pre-scaled by sm_scale * log2 e), the scores of every index token
+ *   and the maximum of every 64-token chunk (two passes: scores, then value
+ *   bins; see lvq_decode_attn).
  * lvq_window_partial: the sink and recent bf16 tokens of step `step`, written
  *   to slot `slot` (< S_tot).  Never empty for seq_len >= 1.
  * Other arguments as for lvq_decode_attn.
@@ -203,10 +234,11 @@ LVQ_API int32_t lvq_decode_attn_splits(const lvq_geom* g, int32_t B, int32_t max
 LVQ_API lvq_status lvq_quant_partial(const lvq_geom* g, int32_t step, const void* q,
                                      const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
                                      const int32_t* seq_len, int32_t max_len, const void* slices,
-                                     const float* rope_cos, const float* rope_sin, int32_t rope_len,
-                                     float sm_scale, float* part_o, float* part_lse, int32_t num_splits,
+                                     const float* rope_cos, const float* rope_sin, const void* rope_f16,
+                                     int32_t rope_len, float sm_scale, float* part_o, float* part_lse,
+                                     int32_t num_splits,
                                      int32_t S_tot, void* ws, size_t ws_bytes, int32_t B, hipStream_t stream);
-LVQ_API size_t lvq_quant_partial_workspace(const lvq_geom* g, int32_t B);
+LVQ_API size_t lvq_quant_partial_workspace(const lvq_geom* g, int32_t B, int32_t max_len);
 LVQ_API lvq_status lvq_window_partial(const lvq_geom* g, int32_t step, const void* q,
                                       const int32_t* seq_len, int32_t max_len,
                                       const void* win_k, const void* win_v,

@@ -31,6 +31,7 @@ class LoopVQProblem:
     slices: torch.Tensor
     rope_cos: torch.Tensor
     rope_sin: torch.Tensor
+    rope16: torch.Tensor                  # packed fp16 table for the index-page pass
     q: torch.Tensor                       # [T][B][H][D] bf16
     sm_scale: float
     raw: Dict[Tuple[str, int, int], np.ndarray] = field(default_factory=dict)   # (kind, b, h) -> [L][T][D] f64
@@ -53,6 +54,7 @@ def build_loopvq(cfg: LoopVQConfig, device="cuda", keep: Sequence[Tuple[int, int
     codebooks = syn.codebooks(cfg, device)
     slices = lvq.lvq_slice_codebooks(g, codebooks)
     rope_cos, rope_sin = lvq.lvq_rope_table(cache.max_len, cfg.D, cfg.rope_base, device=device)
+    rope16 = lvq.lvq_rope_table_f16(cache.max_len, cfg.D, cfg.rope_base, device=device)
     raw = {}
     keep = list(keep)
     for kind in ("k", "v"):
@@ -70,7 +72,7 @@ def build_loopvq(cfg: LoopVQConfig, device="cuda", keep: Sequence[Tuple[int, int
             raw[(kind, b, h)] = np.concatenate(host_steps[(b, h)], axis=1).astype(np.float64)
     q = syn.queries(cfg, device)
     torch.cuda.synchronize()
-    return LoopVQProblem(cfg, g, lengths, cache, codebooks, slices, rope_cos, rope_sin, q,
+    return LoopVQProblem(cfg, g, lengths, cache, codebooks, slices, rope_cos, rope_sin, rope16, q,
                          syn.softmax_scale(cfg), raw)
 
 
@@ -103,7 +105,13 @@ def gpu_indices(p: LoopVQProblem, b: int, h: int, kind: str) -> np.ndarray:
     sel = p.cache.pool[torch.as_tensor(pages, dtype=torch.long, device=p.cache.pool.device)]  # [n][NB][H][2][8][NG]
     sel = sel[:, :, h, kv]                                                                   # [n][NB][8][NG]
     NB, NG = sel.shape[1], sel.shape[3]
-    return sel.permute(1, 0, 2, 3).reshape(NB, n * g.page, NG).cpu().numpy()
+    rows = sel.permute(1, 0, 2, 3).reshape(NB, n * g.page, NG).cpu().numpy()
+    if kind == "v":
+        # value rows are XOR-rotated by the index-token number: byte m holds group m ^ (tau & 15)
+        tau = np.arange(n * g.page)[:, None]
+        m = np.arange(NG)[None, :]
+        rows = rows[:, tau, m ^ (tau & 15)]
+    return rows
 
 
 def host_codebooks(p: LoopVQProblem, h: int, kind: str) -> np.ndarray:
@@ -115,7 +123,7 @@ def host_codebooks(p: LoopVQProblem, h: int, kind: str) -> np.ndarray:
 def run_step(p: LoopVQProblem, t: int, num_splits: int = 0, out=None, lse=None, ws=None):
     return lvq.lvq_decode_attn(p.g, t, p.q[t].contiguous(), p.cache.pool, p.cache.page_table, p.cache.seq_len,
                                p.cache.max_len, p.cache.win_k, p.cache.win_v, p.slices, p.rope_cos, p.rope_sin,
-                               p.sm_scale, out=out, lse_out=lse, ws=ws, num_splits=num_splits)
+                               p.sm_scale, out=out, lse_out=lse, ws=ws, num_splits=num_splits, rope_f16=p.rope16)
 
 
 # ---------------------------------------------------------------------------

@@ -42,13 +42,15 @@ def _geom(**kw):
 
 def _attn(g, **over):
     args = dict(step=0, q=FAKE, pool=FAKE, pt=FAKE, pt_stride=1000, seq_len=FAKE, max_len=1024, wk=FAKE,
-                wv=FAKE, slices=FAKE, cos=FAKE, sin=FAKE, rope_len=2048, scale=0.1, out=FAKE, lse=None, ws=FAKE,
+                wv=FAKE, slices=FAKE, cos=FAKE, sin=FAKE, rope16=FAKE, rope_len=2048, scale=0.1, out=FAKE,
+                lse=None, ws=FAKE,
                 ws_bytes=1 << 30, splits=0, B=4)
     args.update(over)
     gp = C.byref(g) if g is not None else None
     return _lib.lib.lvq_decode_attn(gp, args["step"], args["q"], args["pool"], args["pt"], args["pt_stride"],
                                     args["seq_len"], args["max_len"], args["wk"], args["wv"], args["slices"],
-                                    args["cos"], args["sin"], args["rope_len"], args["scale"], args["out"],
+                                    args["cos"], args["sin"], args["rope16"], args["rope_len"], args["scale"],
+                                    args["out"],
                                     args["lse"], args["ws"], args["ws_bytes"], args["splits"], args["B"], None)
 
 
@@ -58,6 +60,7 @@ def _attn(g, **over):
     (dict(splits=2000), INVALID), (dict(q=None), INVALID), (dict(ws=None), INVALID),
     (dict(pool=None), INVALID), (dict(pt_stride=3), INVALID), (dict(scale=float("nan")), INVALID),
     (dict(ws_bytes=16), WORKSPACE),
+    (dict(rope16=None), INVALID),              # bf16 codebooks need the packed fp16 RoPE table
 ])
 def test_decode_attn_rejects(over, status):
     assert _attn(_geom(), **over) == status
@@ -81,8 +84,13 @@ def test_decode_attn_empty_batch_is_a_no_op():
 def test_workspace_query():
     g = _geom()
     n = _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 3)
-    assert n == 64 * 2 * 4 * (128 + 1) * 4 + 64 * 2 * 128 * 4     # partials + packed query pairs
-    assert _lib.lib.lvq_quant_partial_workspace(C.byref(g), 64) == 64 * 2 * 128 * 4
+    # partials + packed fp16 query rows + scores of the 6072 index tokens (rows of 6080 + a 64-token pad)
+    # + 96 chunk maxima
+    scratch = 64 * 2 * (64 + 6144 + 96) * 4
+    assert n == 64 * 2 * 4 * (128 + 1) * 4 + scratch
+    assert _lib.lib.lvq_quant_partial_workspace(C.byref(g), 64, 6144) == scratch
+    g32 = _geom(cb_dtype="fp32")
+    assert _attn(g32, rope16=None, B=0) == OK
     assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 0) > 0
     assert _lib.lib.lvq_decode_attn_workspace(None, 64, 6144, 0) == 0
 
@@ -103,6 +111,10 @@ def test_merge_and_tables_reject():
     assert _lib.lib.splitk_lse_merge(None, None, 0, 2, 128, None, None, None) == OK
     assert _lib.lib.lvq_rope_table(0, 128, 10000.0, FAKE, FAKE, None) == INVALID
     assert _lib.lib.lvq_rope_table(16, 127, 10000.0, FAKE, FAKE, None) == INVALID
+    assert _lib.lib.lvq_rope_table_f16(0, 128, 10000.0, FAKE, None) == INVALID
+    assert _lib.lib.lvq_rope_table_f16(16, 64, 10000.0, FAKE, None) == UNSUPPORTED
+    assert _lib.lib.lvq_rope_table_f16(16, 128, 1.0, FAKE, None) == INVALID
+    assert _lib.lib.lvq_rope_table_f16(16, 128, 10000.0, None, None) == INVALID
     g = _geom(D=64)
     assert _lib.lib.lvq_slice_codebooks(C.byref(g), FAKE, FAKE, None) == UNSUPPORTED
 

@@ -103,6 +103,18 @@ def test_rope_table_matches_fp64():
     assert np.abs(sin.cpu().numpy() - np.sin(phi)).max() <= 6e-8
 
 
+def test_rope_table_f16_layout_and_rounding():
+    """Packed fp16 table: chunk m of position p holds cos then sin of
+    frequencies 4m..4m+3, each the fp64 value rounded once to binary16."""
+    import decode_attention_loopvq_amd as lvq
+    n = 9000
+    t = lvq.lvq_rope_table_f16(n, 128, 10000.0).cpu().numpy()          # [16][n][8] fp16
+    phi = lv.rope_angles(np.arange(n), 128, 10000.0)                  # [n][64]
+    for m in range(16):
+        np.testing.assert_array_equal(t[m, :, :4], np.cos(phi[:, 4 * m:4 * m + 4]).astype(np.float16))
+        np.testing.assert_array_equal(t[m, :, 4:], np.sin(phi[:, 4 * m:4 * m + 4]).astype(np.float16))
+
+
 @pytest.mark.parametrize("cb", ["bf16", "fp32"])
 @pytest.mark.parametrize("T,Tc,G", [(4, 2, 16), (4, 4, 32), (32, 4, 16)])
 def test_slices_bit_exact(cb, T, Tc, G):
