@@ -40,14 +40,10 @@ struct AttnArgs {
     int S_tot;                  // num_splits + 1 (the last slot is the window partial)
     int num_splits;
     int pps;                    // index pages per split
-    float* scores;              // [B*H][sc_stride] scores of the index tokens (log2 units)
-    long sc_stride;
-    float* cmax;                // [B*H][cm_stride] maximum per 64-token chunk
-    long cm_stride;
     int B;
     int max_len;                // device lengths are clamped to this
     int rope_len;
-    const uint32_t* qpack;      // [B*H][64] packed fp16 query rows (pack_q_f16_kernel)
+    const uint32_t* qpack;      // [B*H][64] packed fp16 query rows (written and read by index_attn_kernel)
     const uint4* rope16;        // [16][rope_len] packed fp16 cos/sin chunks (lvq_rope_table_f16)
     int fix_bits;               // fixed-point fraction bits of the softmax weights in the V bins
 };
@@ -380,9 +376,10 @@ struct StaticFor {
     }
 };
 
-constexpr int kSThreads = 256;                    // score / value passes: 4 waves, two workgroups per CU
+constexpr int kIThreads = 256;                    // index-page partial: 4 waves, two workgroups per CU
 constexpr int kChunk = 64;                        // tokens per wave iteration (one per lane)
-constexpr int kBinBytes = 65536;                  // 256 rows x 64 slots x 4 B
+constexpr int kMaxSplitTok = 1536;                // index tokens per split at most (192 pages)
+constexpr int kChunksPerWave = kMaxSplitTok / kChunk / (kIThreads / 64);
 
 // Index-token range [lo, hi) of request slot j of a workgroup in split `split` (hi <= lo: empty).
 template <int R>
@@ -402,196 +399,79 @@ __device__ __forceinline__ bool split_ranges(const AttnArgs& a, int split, int r
 }
 
 // ---------------------------------------------------------------------------
-// Score pass.  Grid (split, head, request group of R); 256 threads.  The
-// step's K slice of head h is staged in LDS as fp16 (64 KB, two workgroups
-// per CU).  Each wave takes 64-token chunks; a lane scores its token for all
-// R requests (the position's cos/sin, loaded once, serve all of them) and
-// stores the score (log2 units) to `scores`; the maximum of each
-// (request, 64-token chunk) goes to `cmax`.
+// Index-page partial for bf16 codebooks: one workgroup per (split, head,
+// group of R requests), 256 threads (4 waves), two workgroups per CU.  A
+// split holds at most kMaxSplitTok index tokens, so a wave meets at most
+// kChunksPerWave chunks of 64 tokens and keeps their scores in registers.
+//
+// Setup.  The workgroup packs the query rows of its R requests as fp16
+// (pre-scaled by sm_scale * log2 e) into the workspace, from where the score
+// phase reads them with scalar loads, and stages the step's K slice of head
+// h in LDS as fp16 (64 KB).
+//
+// Scores.  The RoPE score needs no rotated key: with the rotate-half pairing
+// (channel i with i + 64, angle p * th_i), q . R(p) k = k . psi(p) with
+//   psi_i      = cos(p th_i) q_i + sin(p th_i) q_{i+64}
+//   psi_{i+64} = cos(p th_i) q_{i+64} - sin(p th_i) q_i      (i < 64),
+// the query turned back by the key's angle.  A lane scores its token for all
+// R requests: the position's cos/sin (packed fp16 table, 256 B) are loaded
+// once and serve all of them; psi is formed in packed fp16 and dotted with
+// the fp16 codewords gathered from LDS (fp32 accumulation).  A chunk is
+// worked in steps (frequency quarter qq, request j), quarters outermost:
+// step (qq, j) uses the codewords of the groups holding frequencies
+// 16qq .. 16qq+15, the 16 query dwords of that quarter (scalar registers)
+// and the quarter's cos/sin.  Each step first waits for its own LDS gathers
+// and query load, then issues the next step's, so the gathers of one step
+// are in flight while the previous one computes and the scalar loads never
+// hold up the LDS pipeline.  The cos/sin of a quarter are loaded one
+// quarter ahead.
+//
+// Weights.  The workgroup's maximum per request is taken; the K slice's LDS
+// becomes bins [256 codewords][64 slots] (slot g*R + j for group g of
+// request j), and every token adds exp2(s - max), in fixed point with
+// fix_bits fraction bits, to the bin of each (group, codeword) of its V
+// indices (integer LDS atomics).  V index bytes sit XOR-rotated by
+// (token & 15) in the pool (byte m holds group m ^ (token & 15)), so at step
+// m the 16 lanes of an LDS phase hit 16 distinct groups, hence 16 distinct
+// banks.
+//
+// Contraction.  o = sum_r bin[g][r] * B_t^V[g][r] / sum of weights: lane
+// (rb, g16) = (tid >> 4, tid & 15) owns codewords 16rb .. 16rb+15 of group g16
+// (and g16 + 16 when c = 4); its V rows are loaded when the weight phase
+// starts.  A 16-lane phase reads one bin row at 16 distinct slots.  Each
+// wave then overwrites its own bin rows with its lanes' partial sums, and
+// after a barrier every output sums 16 partials.  The weight total is exact:
+// every group's bins add up to the same integer.
 // ---------------------------------------------------------------------------
 template <int C, int R>
-__global__ void __launch_bounds__(kSThreads, 2) score_kernel(AttnArgs a) {
-    constexpr int D = 128, K = 256, NG = D / C, HG = NG / 2;
+__global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
+    constexpr int D = 128, K = 256, NG = D / C, NT = kIThreads, NW = NT / 64;
+    constexpr int CPW = kChunksPerWave;
     constexpr int SH = (C == 8) ? 4 : 3;           // byte offset of codeword r in its group row: r << SH
     constexpr int IW = NG / 4;                     // index dwords per token row
-    // Static LDS, the kernel's only LDS object: its base is 0 and folds into instruction offsets.
-    __shared__ __align__(16) unsigned char cb[NG * K * C * 2];
-    const Geo& g = a.geo;
-    const int split = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * R;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int lo[R], hi[R];
-    if (!split_ranges<R>(a, split, r0, lo, hi)) return;
-
-    {   // K slice of head h, bf16 -> fp16
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_k) +
-                                                          h * a.slice_hstride);
-        uint4* dst = reinterpret_cast<uint4*>(cb);
-        for (int e = tid; e < NG * K * C * 2 / 16; e += kSThreads) {
-            const uint4 w = src[e];
-            dst[e] = make_uint4(bf16x2_to_f16x2(w.x), bf16x2_to_f16x2(w.y), bf16x2_to_f16x2(w.z),
-                                bf16x2_to_f16x2(w.w));
-        }
-    }
-    const_ptr<uint32_t> qp[R];
-    const int32_t* ptr[R];
-    long srow[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        const int rb = min(r0 + j, a.B - 1);
-        qp[j] = as_const(a.qpack + (long(rb) * g.H + h) * 64);
-        ptr[j] = a.pt + long(rb) * a.pt_stride;
-        srow[j] = long(rb) * g.H + h;
-    }
-    const uint32_t page_bytes = uint32_t(g.page_bytes);
-    const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG;   // (block, head) slab of page 0
-    int t_lo = 0x7fffffff, t_hi = 0;
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-        if (hi[j] > lo[j]) {
-            t_lo = min(t_lo, lo[j]);
-            t_hi = max(t_hi, hi[j]);
-        }
-    __syncthreads();
-
-    // Software pipeline over this wave's chunks c, c + NW, ...: page ids two chunks ahead, index rows
-    // and cos/sin one chunk ahead, in two alternating buffers.
-    constexpr int NW = kSThreads / 64;
-    auto in_req = [&](int j, int tau) { return tau >= lo[j] && tau < hi[j]; };
-    auto load_pid = [&](int c, uint32_t (&pid)[R]) {
-        const int tau = c * kChunk + lane;
-#pragma unroll
-        for (int j = 0; j < R; ++j)        // a valid column of the page table (unused out of range)
-            pid[j] = uint32_t(ptr[j][max(0, min(tau, hi[j] - 1)) >> 3]);
-    };
-    // Every lane issues the same loads (out-of-range lanes read a valid page through the clamped page id)
-    // and stores (into the pad chunk of the row), so that the loads in flight can be counted exactly
-    // across iterations.
-    auto load_rows = [&](int c, const uint32_t (&pid)[R], uint32_t (&ik)[R][IW], uint4 (&tr)[16]) {
-        const int tau = c * kChunk + lane;
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            const uint4* row = reinterpret_cast<const uint4*>(slab + uint64_t(pid[j]) * page_bytes + (tau & 7) * NG);
-#pragma unroll
-            for (int w = 0; w < IW / 4; ++w) {
-                const uint4 kv = row[w];
-                ik[j][4 * w] = kv.x; ik[j][4 * w + 1] = kv.y; ik[j][4 * w + 2] = kv.z; ik[j][4 * w + 3] = kv.w;
-            }
-        }
-        const int p = min(g.sink + tau, a.rope_len - 1);
-#pragma unroll
-        for (int m = 0; m < 16; ++m) tr[m] = a.rope16[long(m) * a.rope_len + p];
-    };
-    auto score_chunk = [&](int c, const uint32_t (&ik)[R][IW], const uint4 (&tr)[16]) {
-        const int tau = c * kChunk + lane;
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            const bool in = in_req(j, tau);
-            {
-                float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-                // two halves: frequencies 0..31 use groups [0, HG/2) and [HG, HG + HG/2), 32..63 the rest
-                StaticFor<0, 2>::run([&](auto hc) {
-                    constexpr int hf = decltype(hc)::value;
-                    uint32_t kw[HG][C / 2];     // [lo groups of this half | hi groups of this half]
-                    StaticFor<0, HG>::run([&](auto ic) {
-                        constexpr int i = decltype(ic)::value;
-                        constexpr int gi = (i < HG / 2) ? (hf * HG / 2 + i) : (HG + hf * HG / 2 + i - HG / 2);
-                        const uint32_t off = byte_shl<SH, gi & 3>(ik[j][gi >> 2]);
-                        const unsigned char* pcw = cb + gi * (K * C * 2) + off;
-                        if constexpr (C == 8) {
-                            const uint4 v = *reinterpret_cast<const uint4*>(pcw);
-                            kw[i][0] = v.x; kw[i][1] = v.y; kw[i][2] = v.z; kw[i][3] = v.w;
-                        } else {
-                            const uint2 v = *reinterpret_cast<const uint2*>(pcw);
-                            kw[i][0] = v.x; kw[i][1] = v.y;
-                        }
-                    });
-#pragma unroll
-                    for (int mm = 0; mm < 8; ++mm) {           // RoPE frequencies 4m .. 4m+3
-                        const int m = hf * 8 + mm;
-                        const h2_t c01 = as_h2(tr[m].x), c23 = as_h2(tr[m].y);
-                        const h2_t s01 = as_h2(tr[m].z), s23 = as_h2(tr[m].w);
-                        const h2_t l01 = as_h2(qp[j][4 * m]), l23 = as_h2(qp[j][4 * m + 1]);
-                        const h2_t u01 = as_h2(qp[j][4 * m + 2]), u23 = as_h2(qp[j][4 * m + 3]);
-                        const h2_t pl01 = __builtin_elementwise_fma(c01, l01, s01 * u01);
-                        const h2_t pl23 = __builtin_elementwise_fma(c23, l23, s23 * u23);
-                        const h2_t ph01 = __builtin_elementwise_fma(c01, u01, -(s01 * l01));
-                        const h2_t ph23 = __builtin_elementwise_fma(c23, u23, -(s23 * l23));
-                        uint32_t kl01, kl23, kh01, kh23;
-                        if constexpr (C == 8) {
-                            const int il = mm >> 1, d = (mm & 1) * 2;     // lo group hf*4 + il
-                            kl01 = kw[il][d]; kl23 = kw[il][d + 1];
-                            kh01 = kw[HG / 2 + il][d]; kh23 = kw[HG / 2 + il][d + 1];
-                        } else {
-                            kl01 = kw[mm][0]; kl23 = kw[mm][1];
-                            kh01 = kw[HG / 2 + mm][0]; kh23 = kw[HG / 2 + mm][1];
-                        }
-                        acc0 = dot2h(kl01, pl01, acc0);
-                        acc1 = dot2h(kl23, pl23, acc1);
-                        acc2 = dot2h(kh01, ph01, acc2);
-                        acc3 = dot2h(kh23, ph23, acc3);
-                    }
-                });
-                const float s_all = (acc0 + acc1) + (acc2 + acc3);
-                a.scores[srow[j] * a.sc_stride + (in ? tau : a.sc_stride - kChunk + lane)] = s_all;
-                // chunk maximum: chunks holding tokens of request j write their slot, others the pad slot
-                const float mw = wave_max_dpp(in ? s_all : -INFINITY);
-                const bool mine = c * kChunk < hi[j] && c * kChunk + kChunk > lo[j];
-                if (lane == 0) a.cmax[srow[j] * a.cm_stride + (mine ? c : a.cm_stride - 1)] = mw;
-            }
-        }
-    };
-    int c = t_lo / kChunk + wave;
-    uint32_t pidA[R], pidB[R];
-    uint32_t ikA[R][IW], ikB[R][IW];
-    uint4 trA[16], trB[16];
-    load_pid(c, pidA);
-    load_pid(c + NW, pidB);
-    load_rows(c, pidA, ikA, trA);
-    load_pid(c + 2 * NW, pidA);
-    while (c * kChunk < t_hi) {
-        load_rows(c + NW, pidB, ikB, trB);
-        load_pid(c + 3 * NW, pidB);
-        score_chunk(c, ikA, trA);
-        c += NW;
-        if (c * kChunk >= t_hi) break;
-        load_rows(c + NW, pidA, ikA, trA);
-        load_pid(c + 3 * NW, pidA);
-        score_chunk(c, ikB, trB);
-        c += NW;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Value pass.  Grid (split, head, request group of R); 256 threads.  The
-// split's maximum per request comes from the score pass's chunk maxima.
-// Each token adds its weight exp2(s - max), in fixed point with fix_bits
-// fraction bits, to one bin per (group, codeword) of its V indices (integer
-// LDS atomics; bins [256 codewords][R*NG slots], slot j*NG + g).  V index
-// bytes sit XOR-rotated by (token & 15) in the pool (byte m holds group
-// m ^ (token & 15)), so at step m the 16 lanes of each LDS phase hit 16
-// distinct groups, hence 16 distinct banks.  Then
-// o = sum_r bin[g][r] * B_t^V[g][r] / sum of weights, with the V slice read
-// from global memory, and the normalised partial and its logsumexp are written.
-// ---------------------------------------------------------------------------
-template <int C, int R>
-__global__ void __launch_bounds__(kSThreads, 2) value_kernel(AttnArgs a) {
-    constexpr int D = 128, K = 256, NG = D / C;
-    constexpr int IW = NG / 4;
-    constexpr int NW = kSThreads / 64;
+    constexpr int GQ = (C == 8) ? 4 : 8;           // codewords gathered per score step
+    constexpr int GW = C / 2;                      // dwords per fp16 codeword
+    constexpr int NSTEP = 4 * R;                   // score steps per chunk (even: buffers alternate)
+    constexpr int CB16 = NG * K * C * 2 / 16;      // 16-byte words of the staged slice
+    constexpr int NSTAGE = CB16 / NT;
+    constexpr int GPL = NG / 16;                   // groups per contraction lane
+    constexpr int PL = R * C * GPL;                // partial sums per contraction lane
+    static_assert(NSTEP % 2 == 0, "step buffers alternate within a chunk");
     static_assert(R * NG == 64, "one bin row holds R*NG = 64 slots");
-    __shared__ __align__(16) unsigned char smem[kBinBytes + NW * R * D * 4 + NW * R * 4];
-    uint32_t* bins = reinterpret_cast<uint32_t*>(smem);
-    float* wred = reinterpret_cast<float*>(smem + kBinBytes);                    // [waves][R*D]
-    uint32_t* lred = reinterpret_cast<uint32_t*>(wred + NW * R * D);            // [waves][R]
+    static_assert(NT == 256 && CB16 % NT == 0, "contraction lanes: 16 codeword blocks x 16 groups");
+    static_assert(CPW * NW * kChunk == kMaxSplitTok, "a split fills the waves' score registers");
+    // Static LDS: the K slice (fp16), later the V bins [256][64] u32; both start at address 0, which
+    // folds into instruction offsets.
+    __shared__ __align__(16) unsigned char lds[NG * K * C * 2];
+    __shared__ float wmax[NW][R];
+    uint32_t* bins = reinterpret_cast<uint32_t*>(lds);
     const Geo& g = a.geo;
     const int split = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * R;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int lo[R], hi[R];
-    const bool any = split_ranges<R>(a, split, r0, lo, hi);
-    if (!any) {
-        for (int e = tid; e < R * D; e += kSThreads) {
+    if (!split_ranges<R>(a, split, r0, lo, hi)) {
+        for (int e = tid; e < R * D; e += NT) {
             const int j = e / D, d = e % D, rb = r0 + j;
             if (rb >= a.B) continue;
             const long row = (long(rb) * g.H + h) * a.S_tot + split;
@@ -600,134 +480,348 @@ __global__ void __launch_bounds__(kSThreads, 2) value_kernel(AttnArgs a) {
         }
         return;
     }
-    for (int e = tid; e < kBinBytes / 4; e += kSThreads) bins[e] = 0u;
-
-    const int32_t* ptr[R];
     long srow[R];
-    float M[R];
+    const int32_t* ptr[R];
+    int t_lo = 0x7fffffff, t_hi = 0;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int rb = min(r0 + j, a.B - 1);
         ptr[j] = a.pt + long(rb) * a.pt_stride;
         srow[j] = long(rb) * g.H + h;
-        // split maximum from the chunk maxima (at most 32 chunks of 64 tokens per split)
-        const int c0 = lo[j] / kChunk, c1 = (hi[j] + kChunk - 1) / kChunk;
-        const float m = (hi[j] > lo[j] && c0 + lane < c1) ? a.cmax[srow[j] * a.cm_stride + c0 + lane] : -INFINITY;
-        M[j] = wave_max_dpp(m);
-    }
-    const uint32_t page_bytes = uint32_t(g.page_bytes);
-    const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG + 8 * NG;   // value rows
-    const float fix_scale = float(1u << a.fix_bits);
-    int t_lo = 0x7fffffff, t_hi = 0;
-#pragma unroll
-    for (int j = 0; j < R; ++j)
         if (hi[j] > lo[j]) {
             t_lo = min(t_lo, lo[j]);
             t_hi = max(t_hi, hi[j]);
         }
-    __syncthreads();
+    }
 
-    // Software pipeline as in the score pass: page ids two chunks ahead, value rows and scores one ahead.
+    // ---- setup: packed query rows (dword t of row j: the fp16 pair of chunk t >> 2, see the score steps) ----
+    if (tid < R * 64) {
+        const int j = tid >> 6, t = tid & 63;
+        const int m = t >> 2, k = t & 3;
+        const int ch = (k < 2 ? 0 : 64) + 4 * m + 2 * (k & 1);
+        const uint16_t* qr = a.q + srow[j] * D;
+        const h2_t v = {(_Float16)(bf16_to_f32(qr[ch]) * a.scale_log2),
+                        (_Float16)(bf16_to_f32(qr[ch + 1]) * a.scale_log2)};
+        const_cast<uint32_t*>(a.qpack)[srow[j] * 64 + t] = __builtin_bit_cast(uint32_t, v);
+    }
+    {   // K slice of head h, bf16 -> fp16: every load issued before the first conversion
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_k) +
+                                                          h * a.slice_hstride);
+        uint4* dst = reinterpret_cast<uint4*>(lds);
+        uint4 w[NSTAGE];
+#pragma unroll
+        for (int i = 0; i < NSTAGE; ++i) w[i] = src[tid + i * NT];
+#pragma unroll
+        for (int i = 0; i < NSTAGE; ++i)
+            dst[tid + i * NT] = make_uint4(bf16x2_to_f16x2(w[i].x), bf16x2_to_f16x2(w[i].y),
+                                           bf16x2_to_f16x2(w[i].z), bf16x2_to_f16x2(w[i].w));
+    }
+    const uint32_t page_bytes = uint32_t(g.page_bytes);
+    const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG;   // (block, head) slab of page 0
+
+    // Page ids two chunks ahead, index rows one chunk ahead (two alternating buffers).  Every lane
+    // issues the same loads: lanes out of range read a valid page of the request through the clamped
+    // page id (a request with no index page reads physical page 0), so the loads in flight can be
+    // counted exactly across iterations.
     auto in_req = [&](int j, int tau) { return tau >= lo[j] && tau < hi[j]; };
     auto load_pid = [&](int c, uint32_t (&pid)[R]) {
         const int tau = c * kChunk + lane;
 #pragma unroll
-        for (int j = 0; j < R; ++j) pid[j] = uint32_t(ptr[j][max(0, min(tau, hi[j] - 1)) >> 3]);
+        for (int j = 0; j < R; ++j) {
+            const uint32_t e = uint32_t(ptr[j][max(0, min(tau, hi[j] - 1)) >> 3]);
+            pid[j] = hi[j] > 0 ? e : 0u;
+        }
     };
-    auto load_rows = [&](int c, const uint32_t (&pid)[R], uint32_t (&iv)[R][IW], float (&sc)[R]) {
+    // index row words of chunk c: kv = 0 for the key row, 1 for the value row
+    auto load_idx = [&](int c, int kv, const uint32_t (&pid)[R], uint32_t (&ix)[R][IW]) {
         const int tau = c * kChunk + lane;
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            const uint4* row = reinterpret_cast<const uint4*>(slab + uint64_t(pid[j]) * page_bytes + (tau & 7) * NG);
+            const uint4* row = reinterpret_cast<const uint4*>(slab + uint64_t(pid[j]) * page_bytes +
+                                                              (kv * 8 + (tau & 7)) * NG);
 #pragma unroll
             for (int w = 0; w < IW / 4; ++w) {
-                const uint4 vv = row[w];
-                iv[j][4 * w] = vv.x; iv[j][4 * w + 1] = vv.y; iv[j][4 * w + 2] = vv.z; iv[j][4 * w + 3] = vv.w;
+                const uint4 kv4 = row[w];
+                ix[j][4 * w] = kv4.x; ix[j][4 * w + 1] = kv4.y; ix[j][4 * w + 2] = kv4.z; ix[j][4 * w + 3] = kv4.w;
             }
-            sc[j] = a.scores[srow[j] * a.sc_stride + (in_req(j, tau) ? tau : a.sc_stride - kChunk + lane)];
         }
     };
-    auto bin_chunk = [&](int c, const uint32_t (&iv)[R][IW], const float (&sc)[R]) {
+
+    // ---- scores ----
+    uint4 tr[16];                                   // cos/sin of the lane's position, 4 frequencies each
+    auto load_tr = [&](int c, auto qc) {
+        constexpr int qq = decltype(qc)::value;
+        const int p = min(g.sink + c * kChunk + lane, a.rope_len - 1);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) tr[4 * qq + mm] = a.rope16[long(4 * qq + mm) * a.rope_len + p];
+    };
+    // Group of the i-th codeword gathered in quarter qq: lo groups first, then the hi groups holding
+    // channels 64 + (the same frequencies).
+    auto group_of = [](int qq, int i) constexpr {
+        return C == 8 ? (i < 2 ? 2 * qq + i : 8 + 2 * qq + (i - 2)) : (i < 4 ? 4 * qq + i : 16 + 4 * qq + (i - 4));
+    };
+    auto gather = [&](const uint32_t (&ik)[R][IW], auto qc, auto jc, uint32_t (&G)[GQ][GW]) {
+        constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
+        StaticFor<0, GQ>::run([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int gi = group_of(qq, i);
+            const uint32_t off = byte_shl<SH, gi & 3>(ik[j][gi >> 2]);
+            const unsigned char* pcw = lds + gi * (K * C * 2) + off;
+            if constexpr (C == 8) {
+                const uint4 v = *reinterpret_cast<const uint4*>(pcw);
+                G[i][0] = v.x; G[i][1] = v.y; G[i][2] = v.z; G[i][3] = v.w;
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(pcw);
+                G[i][0] = v.x; G[i][1] = v.y;
+            }
+        });
+    };
+    const_ptr<uint32_t> qrow[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) qrow[j] = as_const(a.qpack + srow[j] * 64);
+    auto load_q = [&](auto qc, auto jc, uint32_t (&qs)[16]) {
+        constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) qs[u] = qrow[j][16 * qq + u];
+    };
+    float acc[R][2];
+    float rmax[R];                                  // the lane's running maximum per request
+    float sreg[CPW][R];                             // scores of the wave's chunks, the latest in the last row
+    auto compute = [&](auto qc, auto jc, const uint32_t (&G)[GQ][GW], const uint32_t (&qs)[16]) {
+        constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {           // RoPE frequencies 4m .. 4m+3
+            const int m = 4 * qq + mm;
+            const h2_t c01 = as_h2(tr[m].x), c23 = as_h2(tr[m].y);
+            const h2_t s01 = as_h2(tr[m].z), s23 = as_h2(tr[m].w);
+            const h2_t l01 = as_h2(qs[4 * mm]), l23 = as_h2(qs[4 * mm + 1]);
+            const h2_t u01 = as_h2(qs[4 * mm + 2]), u23 = as_h2(qs[4 * mm + 3]);
+            const h2_t pl01 = __builtin_elementwise_fma(c01, l01, s01 * u01);
+            const h2_t pl23 = __builtin_elementwise_fma(c23, l23, s23 * u23);
+            const h2_t ph01 = __builtin_elementwise_fma(c01, u01, -(s01 * l01));
+            const h2_t ph23 = __builtin_elementwise_fma(c23, u23, -(s23 * l23));
+            uint32_t kl01, kl23, kh01, kh23;
+            if constexpr (C == 8) {
+                const int il = mm >> 1, d = (mm & 1) * 2;
+                kl01 = G[il][d]; kl23 = G[il][d + 1];
+                kh01 = G[2 + il][d]; kh23 = G[2 + il][d + 1];
+            } else {
+                kl01 = G[mm][0]; kl23 = G[mm][1];
+                kh01 = G[4 + mm][0]; kh23 = G[4 + mm][1];
+            }
+            acc[j][0] = dot2h(kl01, pl01, acc[j][0]);
+            acc[j][1] = dot2h(kl23, pl23, acc[j][1]);
+            acc[j][0] = dot2h(kh01, ph01, acc[j][0]);
+            acc[j][1] = dot2h(kh23, ph23, acc[j][1]);
+        }
+    };
+    auto finish = [&](int c, auto jc) {
+        constexpr int j = decltype(jc)::value;
+        const bool in = in_req(j, c * kChunk + lane);
+        const float s_all = acc[j][0] + acc[j][1];
+        acc[j][0] = 0.f;
+        acc[j][1] = 0.f;
+        sreg[CPW - 1][j] = s_all;
+        rmax[j] = fmaxf(rmax[j], in ? s_all : -INFINITY);
+    };
+    auto shift_scores = [&]() {
+#pragma unroll
+        for (int k = 0; k + 1 < CPW; ++k)
+#pragma unroll
+            for (int j = 0; j < R; ++j) sreg[k][j] = sreg[k + 1][j];
+    };
+    uint32_t G[2][GQ][GW];
+    uint32_t qs[2][16];
+    // One chunk: steps k = (qq, j); the last step issues the first gathers of the next chunk (ikn).
+    auto run_chunk = [&](int c, const uint32_t (&ikc)[R][IW], const uint32_t (&ikn)[R][IW]) {
+        shift_scores();
+        StaticFor<0, NSTEP>::run([&](auto kc) {
+            constexpr int k = decltype(kc)::value, qq = k / R, j = k % R, b = k & 1;
+            constexpr int k1 = (k + 1) % NSTEP;
+            using QN = std::integral_constant<int, k1 / R>;
+            using JN = std::integral_constant<int, k1 % R>;
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this step's gathers and query quarter
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (k + 1 < NSTEP) gather(ikc, QN{}, JN{}, G[b ^ 1]);
+            else gather(ikn, QN{}, JN{}, G[b ^ 1]);
+            load_q(QN{}, JN{}, qs[b ^ 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // at the start of a quarter, the cos/sin of the next quarter (of the wave's next chunk after the last)
+            if constexpr (j == 0) load_tr(qq < 3 ? c : c + NW, std::integral_constant<int, (qq + 1) % 4>{});
+            compute(std::integral_constant<int, qq>{}, std::integral_constant<int, j>{}, G[b], qs[b]);
+            if constexpr (qq == 3) finish(c, std::integral_constant<int, j>{});
+        });
+    };
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        acc[j][0] = acc[j][1] = 0.f;
+        rmax[j] = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) sreg[k][j] = 0.f;
+    }
+    const int c0 = t_lo / kChunk + wave;
+    int nch = 0;                                    // chunks of this wave
+    {
+        int c = c0;
+        uint32_t pidA[R], pidB[R];
+        uint32_t ikA[R][IW], ikB[R][IW];
+        load_pid(c, pidA);
+        load_pid(c + NW, pidB);
+        load_idx(c, 0, pidA, ikA);
+        load_pid(c + 2 * NW, pidA);
+        load_tr(c, std::integral_constant<int, 0>{});
+        __syncthreads();                            // K slice staged, query rows packed
+        gather(ikA, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, G[0]);
+        load_q(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, qs[0]);
+        while (c * kChunk < t_hi) {
+            load_idx(c + NW, 0, pidB, ikB);
+            load_pid(c + 3 * NW, pidB);
+            run_chunk(c, ikA, ikB);
+            c += NW;
+            ++nch;
+            if (c * kChunk >= t_hi) break;
+            load_idx(c + NW, 0, pidA, ikA);
+            load_pid(c + 3 * NW, pidA);
+            run_chunk(c, ikB, ikA);
+            c += NW;
+            ++nch;
+        }
+    }
+    // scores of this wave's chunk i now in sreg[CPW - nch + i]: move chunk 0 to the first row
+    for (int s = nch; s < CPW; ++s) shift_scores();
+
+    // ---- weights ----
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const float mw = wave_max_dpp(rmax[j]);
+        if (lane == 0) wmax[wave][j] = mw;
+    }
+    uint32_t pidA[R], pidB[R];
+    load_pid(c0, pidA);
+    load_pid(c0 + NW, pidB);
+    __syncthreads();                                // every wave is done with the K slice
+#pragma unroll
+    for (int i = 0; i < K * 64 / 4 / NT; ++i) reinterpret_cast<uint4*>(bins)[tid + i * NT] = make_uint4(0u, 0u, 0u, 0u);
+    // V rows of this lane's contraction block, needed once the bins are complete
+    const int cb_blk = tid >> 4, g16 = tid & 15;
+    uint4 vrow[16];
+    {
+        const uint16_t* vsl = static_cast<const uint16_t*>(a.slice_v) + h * a.slice_hstride;
+#pragma unroll
+        for (int k = 0; k < GPL; ++k) {
+            const uint4* src = reinterpret_cast<const uint4*>(vsl + (long(g16 + 16 * k) * K + 16 * cb_blk) * C);
+#pragma unroll
+            for (int i = 0; i < 16 / GPL; ++i) vrow[k * (16 / GPL) + i] = src[i];
+        }
+    }
+    uint32_t ivA[R][IW], ivB[R][IW];
+    load_idx(c0, 1, pidA, ivA);
+    load_pid(c0 + 2 * NW, pidA);
+    __syncthreads();                                // bins cleared, wave maxima visible
+    float M[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        M[j] = wmax[0][j];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M[j] = fmaxf(M[j], wmax[w][j]);
+    }
+    const float fix_scale = float(1u << a.fix_bits);
+    auto bin_chunk = [&](int c, const uint32_t (&iv)[R][IW]) {
         const int tau = c * kChunk + lane;
-        const uint32_t rot = uint32_t(tau) & 15u;
+        // byte k of base[w]: slot byte offset 4R * ((4w + k) ^ (tau & 15)) of the group held in V index byte 4w + k
+        const uint32_t rot = (uint32_t(tau) & 15u) * (4u * R) * 0x01010101u;
+        uint32_t base[IW];
+#pragma unroll
+        for (int w = 0; w < IW; ++w) base[w] = ((4u * R) * (0x03020100u + uint32_t(w) * 0x04040404u)) ^ rot;
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             // lanes out of range add 0 (their index rows are valid memory, their bins any)
-            const uint32_t u = in_req(j, tau) ? uint32_t(fmaf(__builtin_amdgcn_exp2f(sc[j] - M[j]), fix_scale, 0.5f))
-                                              : 0u;
+            const uint32_t u = in_req(j, tau)
+                                   ? uint32_t(fmaf(__builtin_amdgcn_exp2f(sreg[0][j] - M[j]), fix_scale, 0.5f))
+                                   : 0u;
             StaticFor<0, NG>::run([&](auto mc) {
                 constexpr int m = decltype(mc)::value;
-                // bin byte address: [4 * group, codeword, 0, 0] with group = m ^ rot (one v_perm)
-                constexpr uint32_t sel = 0x0c0c0000u | (uint32_t(4 + (m & 3)) << 8);
-                const uint32_t addr = __builtin_amdgcn_perm(iv[j][m >> 2], 4u * (uint32_t(m) ^ rot), sel);
-                uint32_t* bin = static_cast<uint32_t*>(__builtin_assume_aligned(smem + addr + 4 * j * NG, 4));
+                // bin byte address [slot offset, codeword, 0, 0] (one v_perm): row = codeword, 256 B per row
+                constexpr uint32_t sel = 0x0c0c0000u | (uint32_t(4 + (m & 3)) << 8) | uint32_t(m & 3);
+                const uint32_t addr = __builtin_amdgcn_perm(iv[j][m >> 2], base[m >> 2], sel);
+                uint32_t* bin = static_cast<uint32_t*>(__builtin_assume_aligned(lds + addr + 4 * j, 4));
                 __hip_atomic_fetch_add(bin, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             });
         }
+        shift_scores();
     };
     {
-        int c = t_lo / kChunk + wave;
-        uint32_t pidA[R], pidB[R];
-        uint32_t ivA[R][IW], ivB[R][IW];
-        float scA[R], scB[R];
-        load_pid(c, pidA);
-        load_pid(c + NW, pidB);
-        load_rows(c, pidA, ivA, scA);
-        load_pid(c + 2 * NW, pidA);
+        int c = c0;
         while (c * kChunk < t_hi) {
-            load_rows(c + NW, pidB, ivB, scB);
+            load_idx(c + NW, 1, pidB, ivB);
             load_pid(c + 3 * NW, pidB);
-            bin_chunk(c, ivA, scA);
+            bin_chunk(c, ivA);
             c += NW;
             if (c * kChunk >= t_hi) break;
-            load_rows(c + NW, pidA, ivA, scA);
+            load_idx(c + NW, 1, pidA, ivA);
             load_pid(c + 3 * NW, pidA);
-            bin_chunk(c, ivB, scB);
+            bin_chunk(c, ivB);
             c += NW;
         }
     }
     __syncthreads();
 
-    // ---- o = sum_r bin[g][r] * B_t^V[g][r]: wave w takes codewords [64w, 64w + 64), lane (j, g) ----
-    {
-        const int jj = lane / NG, gg = lane % NG;
-        const uint16_t* vsl = static_cast<const uint16_t*>(a.slice_v) + h * a.slice_hstride + gg * K * C;
-        float o[C];
+    // ---- contraction: lane (cb_blk, g16) over its 16 codewords ----
+    float o[PL];
 #pragma unroll
-        for (int i = 0; i < C; ++i) o[i] = 0.f;
-        uint32_t l0 = 0u;
-        const int rbeg = wave * (K / NW);
-        for (int rc = rbeg; rc < rbeg + K / NW; rc += 16) {
-            uint32_t vw[16][C / 2];
-            uint32_t bv[16];
+    for (int i = 0; i < PL; ++i) o[i] = 0.f;
+    uint32_t lsum[R];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                if constexpr (C == 8) {
-                    const uint4 w = *reinterpret_cast<const uint4*>(vsl + (rc + u) * C);
-                    vw[u][0] = w.x; vw[u][1] = w.y; vw[u][2] = w.z; vw[u][3] = w.w;
-                } else {
-                    const uint2 w = *reinterpret_cast<const uint2*>(vsl + (rc + u) * C);
-                    vw[u][0] = w.x; vw[u][1] = w.y;
-                }
-                bv[u] = bins[(rc + u) * 64 + lane];
+    for (int j = 0; j < R; ++j) lsum[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 16 * cb_blk + i;
+#pragma unroll
+        for (int k = 0; k < GPL; ++k) {
+            uint32_t bv[R];
+            if constexpr (R == 4) {
+                const uint4 b4 = *reinterpret_cast<const uint4*>(bins + r * 64 + (g16 + 16 * k) * R);
+                bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
+            } else {
+                const uint2 b2 = *reinterpret_cast<const uint2*>(bins + r * 64 + (g16 + 16 * k) * R);
+                bv[0] = b2.x; bv[1] = b2.y;
+            }
+            uint32_t vw[C / 2];                     // V row: C bf16 of codeword r, group g16 + 16k
+            if constexpr (C == 8) {
+                vw[0] = vrow[i].x; vw[1] = vrow[i].y; vw[2] = vrow[i].z; vw[3] = vrow[i].w;
+            } else {
+                const uint4 q = vrow[k * 8 + (i >> 1)];
+                vw[0] = (i & 1) ? q.z : q.x;
+                vw[1] = (i & 1) ? q.w : q.y;
             }
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                l0 += gg == 0 ? bv[u] : 0u;
-                const float bw = float(bv[u]);
+            for (int j = 0; j < R; ++j) {
+                if (k == 0) lsum[j] += bv[j];
+                const float bw = float(bv[j]);
 #pragma unroll
-                for (int i = 0; i < C / 2; ++i) {
-                    o[2 * i] = fmaf(bw, bf16_lo(vw[u][i]), o[2 * i]);
-                    o[2 * i + 1] = fmaf(bw, bf16_hi(vw[u][i]), o[2 * i + 1]);
+                for (int u = 0; u < C / 2; ++u) {
+                    o[j * C * GPL + k * C + 2 * u] = fmaf(bw, bf16_lo(vw[u]), o[j * C * GPL + k * C + 2 * u]);
+                    o[j * C * GPL + k * C + 2 * u + 1] = fmaf(bw, bf16_hi(vw[u]), o[j * C * GPL + k * C + 2 * u + 1]);
                 }
             }
         }
+    }
+    // Partials over this wave's own bin rows (64 rows of 256 B, read by no other wave): lane slot
+    // (cb_blk & 3) * 16 + g16 holds PL floats, then the weight totals of the g16 = 0 lanes.
+    float* part = reinterpret_cast<float*>(lds) + wave * 4096;
+    {
+        float4* dst = reinterpret_cast<float4*>(part + ((cb_blk & 3) * 16 + g16) * PL);
 #pragma unroll
-        for (int i = 0; i < C; ++i) wred[wave * (R * D) + jj * D + gg * C + i] = o[i];
-        if (gg == 0) lred[wave * R + jj] = l0;
+        for (int i = 0; i < PL / 4; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+        if (g16 == 0) {
+            uint32_t* ld = reinterpret_cast<uint32_t*>(part + 64 * PL) + (cb_blk & 3) * R;
+#pragma unroll
+            for (int j = 0; j < R; ++j) ld[j] = lsum[j];
+        }
     }
     __syncthreads();
-    for (int e = tid; e < R * D; e += kSThreads) {
+    for (int e = tid; e < R * D; e += NT) {
         const int j = e / D, d = e % D, rb = r0 + j;
         if (rb >= a.B) continue;
         const long orow = (long(rb) * g.H + h) * a.S_tot + split;
@@ -736,29 +830,21 @@ __global__ void __launch_bounds__(kSThreads, 2) value_kernel(AttnArgs a) {
             if (d == 0) a.part_lse[orow] = -INFINITY;
             continue;
         }
-        float acc = 0.f;
-        double L = 0.0;
+        const int gr = d / C, u = d % C;
+        const int p = j * C * GPL + (gr >> 4) * C + u;
+        const float* pbase = reinterpret_cast<const float*>(lds);
+        float accv = 0.f;
+        uint64_t L = 0;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            acc += wred[w * (R * D) + e];
-            L += double(lred[w * R + j]);
+        for (int b = 0; b < 16; ++b) {
+            const float* pw = pbase + (b >> 2) * 4096;
+            accv += pw[((b & 3) * 16 + (gr & 15)) * PL + p];
+            L += reinterpret_cast<const uint32_t*>(pw + 64 * PL)[(b & 3) * R + j];
         }
-        a.part_o[orow * D + d] = float(double(acc) / L);
-        if (d == 0) a.part_lse[orow] = (M[j] + float(log2(L) - double(a.fix_bits))) * kLn2;
+        const float Lf = float(L);
+        a.part_o[orow * D + d] = accv / Lf;
+        if (d == 0) a.part_lse[orow] = (M[j] + (log2f(Lf) - float(a.fix_bits))) * kLn2;
     }
-}
-
-// Query rows for score_kernel: 16 chunks of 4 dwords per (request, head),
-// chunk m = fp16 pairs (q_{4m}, q_{4m+1}), (q_{4m+2}, q_{4m+3}),
-// (q_{64+4m}, q_{65+4m}), (q_{66+4m}, q_{67+4m}), each value q * scale.
-__global__ void pack_q_f16_kernel(const uint16_t* __restrict__ q, float scale, uint32_t* __restrict__ qpack) {
-    const long row = blockIdx.x;
-    const int t = threadIdx.x;            // 64 threads: dword t
-    const int m = t >> 2, k = t & 3;
-    const int ch = (k < 2 ? 0 : 64) + 4 * m + 2 * (k & 1);
-    const uint16_t* qr = q + row * 128;
-    const h2_t v = {(_Float16)(bf16_to_f32(qr[ch]) * scale), (_Float16)(bf16_to_f32(qr[ch + 1]) * scale)};
-    qpack[row * 64 + t] = __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -855,8 +941,9 @@ int reqs_per_wg(const Geo& g) { return g.c == 8 ? 4 : 2; }
 int choose_splits(const Geo& g, int B, int max_len) {
     const int max_pages = max_index_pages(g, max_len);
     if (max_pages == 0) return 1;
-    // Splits of at most 192 pages (1536 tokens): the fixed-point softmax weights keep 21 fraction bits.
-    int s = ceil_div(max_pages, 192);
+    // Splits of at most 192 pages (1536 tokens): a wave's scores fit its registers and the fixed-point
+    // softmax weights keep 21 fraction bits.
+    int s = ceil_div(max_pages, kMaxSplitTok / g.page);
     // Enough (split, head, request group) workgroups for 256 CUs x 2, splits of >= 16 pages.
     const int pairs = ceil_div(B, reqs_per_wg(g)) * g.H;
     s = std::max(s, std::min(ceil_div(512, std::max(1, pairs)), ceil_div(max_pages, 16)));
@@ -866,23 +953,19 @@ int choose_splits(const Geo& g, int B, int max_len) {
 // Pages per split: a multiple of 8 (64 tokens), so that score chunks never straddle splits.
 int pages_per_split(int max_pages, int S) { return max_pages > 0 ? ceil_div(ceil_div(max_pages, S), 8) * 8 : 8; }
 
-// Scratch of the index-page pass inside a workspace: packed queries, scores of the index tokens
-// (rows of idx_stride, a multiple of 64) and the maximum of every 64-token chunk.
-struct QuantScratch {
-    size_t qpack, scores, cmax, bytes;
-    long sc_stride, cm_stride;
-};
-QuantScratch quant_scratch(const Geo& g, int B, int max_len) {
-    QuantScratch q{};
-    const long rows = long(B) * g.H;
-    // index tokens rounded up to 64, plus one pad chunk written by lanes past a request's range
-    q.sc_stride = long(ceil_div(long(max_index_pages(g, max_len)) * g.page, 64)) * 64 + 64;
-    q.cm_stride = q.sc_stride / 64;
-    q.qpack = 0;
-    q.scores = q.qpack + size_t(rows) * 64 * sizeof(uint32_t);
-    q.cmax = q.scores + size_t(rows) * q.sc_stride * sizeof(float);
-    q.bytes = q.cmax + size_t(rows) * q.cm_stride * sizeof(float);
-    return q;
+// Scratch of the index-page partial (bf16 codebooks): the packed query rows, 256 B per (request, head).
+size_t quant_scratch_bytes(const Geo& g, int B) { return size_t(B) * g.H * 64 * sizeof(uint32_t); }
+
+// Bytes of the partials (part_o, part_lse) of S_tot slots per row, rounded up to 256 so that the
+// scratch after them starts on a whole cache line.
+size_t partials_bytes(const Geo& g, int B, int S_tot) {
+    const size_t rows = size_t(B) * g.H * S_tot;
+    return (rows * (g.D + 1) * sizeof(float) + 255) / 256 * 256;
+}
+
+// A split count the bf16 index-page partial can run: splits of at most kMaxSplitTok tokens.
+bool splits_fit(const Geo& g, int max_pages, int S) {
+    return g.cb != LVQ_BF16 || max_pages == 0 || pages_per_split(max_pages, S) * g.page <= kMaxSplitTok;
 }
 
 int ceil_log2(long x) {
@@ -900,14 +983,13 @@ extern "C" size_t lvq_decode_attn_workspace(const lvq_geom* gp, int32_t B, int32
     Geo g;
     if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 0 || num_splits < 0) return 0;
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
-    const size_t rows = size_t(B) * g.H * (S + 1);
-    return rows * g.D * sizeof(float) + rows * sizeof(float) + quant_scratch(g, B, max_len).bytes;
+    return partials_bytes(g, B, S + 1) + quant_scratch_bytes(g, B);
 }
 
 extern "C" size_t lvq_quant_partial_workspace(const lvq_geom* gp, int32_t B, int32_t max_len) {
     Geo g;
     if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 0) return 0;
-    return quant_scratch(g, B, max_len).bytes;
+    return quant_scratch_bytes(g, B);
 }
 
 namespace lvq {
@@ -944,33 +1026,18 @@ lvq_status prepare(const char* fn, const lvq_geom* gp, int32_t step, const void*
     return LVQ_OK;
 }
 
-// Packs q (bf16 codebooks) and launches the index-page partial: the score pass, then the value pass.
+// Launches the index-page partial; `scratch` (256-byte aligned) holds the packed query rows.
 lvq_status launch_quant(AttnArgs& a, void* scratch, hipStream_t stream) {
     const Geo& g = a.geo;
     if (g.cb == LVQ_BF16) {
-        const QuantScratch qs = quant_scratch(g, a.B, a.max_len);
-        unsigned char* base = static_cast<unsigned char*>(scratch);
-        a.qpack = reinterpret_cast<uint32_t*>(base + qs.qpack);
-        a.scores = reinterpret_cast<float*>(base + qs.scores);
-        a.cmax = reinterpret_cast<float*>(base + qs.cmax);
-        a.sc_stride = qs.sc_stride;
-        a.cm_stride = qs.cm_stride;
-        hipLaunchKernelGGL(pack_q_f16_kernel, dim3(a.B * g.H), dim3(64), 0, stream, a.q, a.scale_log2,
-                           const_cast<uint32_t*>(a.qpack));
-        lvq_status st = check_launch("query packing");
-        if (st != LVQ_OK) return st;
+        a.qpack = static_cast<const uint32_t*>(scratch);
         a.fix_bits = 32 - ceil_log2(long(a.pps) * g.page + 1);
         const int R = reqs_per_wg(g);
         const dim3 grid(a.num_splits, g.H, ceil_div(a.B, R));
         if (g.c == 8)
-            hipLaunchKernelGGL((score_kernel<8, 4>), grid, dim3(kSThreads), 0, stream, a);
+            hipLaunchKernelGGL((index_attn_kernel<8, 4>), grid, dim3(kIThreads), 0, stream, a);
         else
-            hipLaunchKernelGGL((score_kernel<4, 2>), grid, dim3(kSThreads), 0, stream, a);
-        if ((st = check_launch("score pass")) != LVQ_OK) return st;
-        if (g.c == 8)
-            hipLaunchKernelGGL((value_kernel<8, 4>), grid, dim3(kSThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL((value_kernel<4, 2>), grid, dim3(kSThreads), 0, stream, a);
+            hipLaunchKernelGGL((index_attn_kernel<4, 2>), grid, dim3(kIThreads), 0, stream, a);
     } else {
         const dim3 grid(a.num_splits, g.H, (a.B + 1) / 2);
         const size_t red_bytes = 4 * (g.D + 2) * sizeof(float);
@@ -1024,6 +1091,11 @@ extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const 
                 "lvq_quant_partial: NULL pool or page table");
     LVQ_REQUIRE(pt_stride >= max_pages, LVQ_ERR_INVALID_ARG, "lvq_quant_partial: pt_stride %d < %d pages",
                 pt_stride, max_pages);
+    LVQ_REQUIRE(splits_fit(g, max_pages, num_splits), LVQ_ERR_INVALID_ARG,
+                "lvq_quant_partial: %d splits of %d index pages exceed %d tokens per split", num_splits, max_pages,
+                kMaxSplitTok);
+    LVQ_REQUIRE(reinterpret_cast<uintptr_t>(ws) % 256 == 0, LVQ_ERR_INVALID_ARG,
+                "lvq_quant_partial: workspace not 256-byte aligned");
     a.pool = pool;
     a.pt = page_table;
     a.pt_stride = pt_stride;
@@ -1080,8 +1152,12 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
     LVQ_REQUIRE(pt_stride >= max_pages, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: pt_stride %d < %d pages",
                 pt_stride, max_pages);
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
+    LVQ_REQUIRE(splits_fit(g, max_pages, S), LVQ_ERR_INVALID_ARG,
+                "lvq_decode_attn: %d splits of %d index pages exceed %d tokens per split", S, max_pages, kMaxSplitTok);
     const size_t need = lvq_decode_attn_workspace(gp, B, max_len, S);
     LVQ_REQUIRE(ws_bytes >= need, LVQ_ERR_WORKSPACE, "lvq_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
+    LVQ_REQUIRE(reinterpret_cast<uintptr_t>(ws) % 256 == 0, LVQ_ERR_INVALID_ARG,
+                "lvq_decode_attn: workspace not 256-byte aligned");
 
     a.pool = pool;
     a.pt = page_table;
@@ -1095,7 +1171,8 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
     a.S_tot = S + 1;
     a.num_splits = S;
     a.pps = pages_per_split(max_pages, S);
-    if ((st = launch_quant(a, a.part_lse + rows, stream)) != LVQ_OK) return st;
+    if ((st = launch_quant(a, static_cast<unsigned char*>(ws) + partials_bytes(g, B, S + 1), stream)) != LVQ_OK)
+        return st;
     if ((st = launch_window(a, stream)) != LVQ_OK) return st;
     hipLaunchKernelGGL(merge_kernel, dim3(B * g.H), dim3(128), 0, stream, a.part_o, a.part_lse, S + 1, g.D, out,
                        lse_out);

@@ -61,6 +61,8 @@ def _attn(g, **over):
     (dict(pool=None), INVALID), (dict(pt_stride=3), INVALID), (dict(scale=float("nan")), INVALID),
     (dict(ws_bytes=16), WORKSPACE),
     (dict(rope16=None), INVALID),              # bf16 codebooks need the packed fp16 RoPE table
+    (dict(max_len=2048, splits=1), INVALID),   # 247 index pages in one split: over 1536 tokens per split
+    (dict(ws=C.c_void_p(4096 + 16)), INVALID),  # workspace not 256-byte aligned
 ])
 def test_decode_attn_rejects(over, status):
     assert _attn(_geom(), **over) == status
@@ -84,10 +86,10 @@ def test_decode_attn_empty_batch_is_a_no_op():
 def test_workspace_query():
     g = _geom()
     n = _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 3)
-    # partials + packed fp16 query rows + scores of the 6072 index tokens (rows of 6080 + a 64-token pad)
-    # + 96 chunk maxima
-    scratch = 64 * 2 * (64 + 6144 + 96) * 4
+    # partials of 3 + 1 slots (rounded up to 256 B) + the packed fp16 query rows, 256 B per (request, head)
+    scratch = 64 * 2 * 64 * 4
     assert n == 64 * 2 * 4 * (128 + 1) * 4 + scratch
+    assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 3, 6144, 1) == (3 * 2 * 2 * 129 * 4 + 255) // 256 * 256 + 3 * 2 * 256
     assert _lib.lib.lvq_quant_partial_workspace(C.byref(g), 64, 6144) == scratch
     g32 = _geom(cb_dtype="fp32")
     assert _attn(g32, rope16=None, B=0) == OK
