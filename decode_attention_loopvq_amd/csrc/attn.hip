@@ -848,16 +848,42 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16-window partial: sinks [0, min(L, sink)) and recent tokens
-// [sink + 8*n_pages, L) of loop step t.  Grid (head, request); 256 threads;
-// each wave takes every fourth window token, lane l owns RoPE pair
-// (l, l + 64).  Writes partial slot num_splits.
+// bf16 window: sinks [0, min(L, sink)) and recent tokens [sink + 8*n_pages, L)
+// of loop step t.  Grid (head, request); 256 threads in 16 rows of 16 lanes;
+// row r takes window tokens r, r + 16, ...  Lane c of a row owns channels
+// 8c .. 8c+7 of its token (one 16-byte load of K and of V); lanes c and c ^ 8
+// hold the two halves of each RoPE pair (i, i + 64) and trade them through
+// DPP; a score is a 16-lane DPP sum.  Each row keeps its own online softmax
+// over kWinBatch tokens at a time (every load of the batch issued first);
+// the 16 rows are combined through LDS.  kMerge: the window partial is
+// merged at once with the row's index-page partials (slots
+// 0 .. num_splits-1) into the attention output (the exact logsumexp merge);
+// otherwise it is written to slot num_splits.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) window_partial_kernel(AttnArgs a) {
-    constexpr int D = 128;
+constexpr int kWinBatch = 5;
+constexpr int kWinPrefetch = 8;                   // index-page partials loaded at the start of the merge
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 16 lanes of a DPP row (every lane gets it).
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp<0x128>(x);     // row_ror:8
+    x += dpp<0x124>(x);     // row_ror:4
+    x += dpp<0x122>(x);     // row_ror:2
+    x += dpp<0x121>(x);     // row_ror:1
+    return x;
+}
+
+template <bool kMerge>
+__global__ void __launch_bounds__(256) window_kernel(AttnArgs a, float* __restrict__ out, float* __restrict__ lse_out) {
+    constexpr int D = 128, NR = 16;
     const Geo& g = a.geo;
     const int h = blockIdx.x, rb = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, c16 = tid & 15, trow = tid >> 4;
+    const bool hi_half = c16 >= 8;
+    const int f0 = 8 * (c16 & 7);                  // first RoPE frequency of the lane's channels
     const int L = clamp_len(a, rb);
     const int np = n_index_pages(L, g);
     const int q_hi = g.sink + g.page * np;
@@ -866,46 +892,132 @@ __global__ void __launch_bounds__(256) window_partial_kernel(AttnArgs a) {
     const int n_w = n_sink + n_recent;
     const int ring = g.W + g.page;
 
-    const uint16_t* qp = a.q + (long(rb) * g.H + h) * D;
-    const float q1 = bf16_to_f32(qp[lane]), q2 = bf16_to_f32(qp[lane + 64]);
-    const long wbase = ((long(rb) * g.T + a.step) * g.H + h) * long(g.Wcap) * D;
-    float m = -INFINITY, l = 0.f, o1 = 0.f, o2 = 0.f;
-    for (int w = wave; w < n_w; w += 4) {
-        const int p = w < n_sink ? w : q_hi + (w - n_sink);
-        const int slot = p < g.sink ? p : g.sink + (p - g.sink) % ring;
-        const uint16_t* kr = a.wk + wbase + long(slot) * D;
-        const uint16_t* vr = a.wv + wbase + long(slot) * D;
-        const float k1 = bf16_to_f32(kr[lane]), k2 = bf16_to_f32(kr[lane + 64]);
-        const float cs = a.rc[long(p) * (D / 2) + lane], sn = a.rs[long(p) * (D / 2) + lane];
-        const float r1 = k1 * cs - k2 * sn, r2 = k2 * cs + k1 * sn;
-        const float s = wave_sum(q1 * r1 + q2 * r2) * a.scale_log2;
-        const float m_new = fmaxf(m, s);
-        const float alpha = exp2f(m - m_new), wgt = exp2f(s - m_new);
-        l = l * alpha + wgt;
-        o1 = o1 * alpha + wgt * bf16_to_f32(vr[lane]);
-        o2 = o2 * alpha + wgt * bf16_to_f32(vr[lane + 64]);
-        m = m_new;
+    float qv[8];
+    {
+        const uint4 qw = *reinterpret_cast<const uint4*>(a.q + (long(rb) * g.H + h) * D + 8 * c16);
+        const uint32_t w4[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            qv[2 * u] = bf16_lo(w4[u]) * a.scale_log2;
+            qv[2 * u + 1] = bf16_hi(w4[u]) * a.scale_log2;
+        }
     }
-    __shared__ float red[4][D + 2];
-    red[wave][lane] = o1;
-    red[wave][lane + 64] = o2;
-    if (lane == 0) {
-        red[wave][D] = m;
-        red[wave][D + 1] = l;
+    const long row = long(rb) * g.H + h;
+    // merge inputs (the first kWinPrefetch index-page partials of the row), loaded with the window
+    float pre_l[kWinPrefetch], pre_o[kWinPrefetch];
+    if constexpr (kMerge) {
+#pragma unroll
+        for (int s2 = 0; s2 < kWinPrefetch; ++s2) {
+            const int sc = min(s2, max(a.num_splits - 1, 0));
+            pre_l[s2] = a.part_lse[row * a.S_tot + sc];
+            pre_o[s2] = a.part_o[(row * a.S_tot + sc) * D + (tid & (D - 1))];
+        }
+    }
+    const long wbase = ((long(rb) * g.T + a.step) * g.H + h) * long(g.Wcap) * D + 8 * c16;
+    float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = 0.f;
+    for (int w0 = trow; w0 < n_w; w0 += NR * kWinBatch) {
+        uint4 kw[kWinBatch], vw[kWinBatch];
+        float4 cs[kWinBatch][2], sn[kWinBatch][2];
+#pragma unroll
+        for (int i = 0; i < kWinBatch; ++i) {
+            const int w = min(w0 + NR * i, n_w - 1);      // a valid window token; extra ones are masked below
+            const int p = w < n_sink ? w : q_hi + (w - n_sink);
+            const int slot = p < g.sink ? p : g.sink + (p - g.sink) % ring;
+            kw[i] = *reinterpret_cast<const uint4*>(a.wk + wbase + long(slot) * D);
+            vw[i] = *reinterpret_cast<const uint4*>(a.wv + wbase + long(slot) * D);
+            const float4* cp = reinterpret_cast<const float4*>(a.rc + long(p) * (D / 2) + f0);
+            const float4* sp = reinterpret_cast<const float4*>(a.rs + long(p) * (D / 2) + f0);
+            cs[i][0] = cp[0]; cs[i][1] = cp[1];
+            sn[i][0] = sp[0]; sn[i][1] = sp[1];
+        }
+        float s[kWinBatch];
+        float mb = m;
+#pragma unroll
+        for (int i = 0; i < kWinBatch; ++i) {
+            const uint32_t k4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+            const float c8[8] = {cs[i][0].x, cs[i][0].y, cs[i][0].z, cs[i][0].w,
+                                 cs[i][1].x, cs[i][1].y, cs[i][1].z, cs[i][1].w};
+            const float s8[8] = {sn[i][0].x, sn[i][0].y, sn[i][0].z, sn[i][0].w,
+                                 sn[i][1].x, sn[i][1].y, sn[i][1].z, sn[i][1].w};
+            float part = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float k = (u & 1) ? bf16_hi(k4[u >> 1]) : bf16_lo(k4[u >> 1]);
+                const float kp = dpp<0x128>(k);           // the other half of the RoPE pair (lane c ^ 8)
+                // lo half: k_i cos - k_{i+64} sin;  hi half: k_{i+64} cos + k_i sin
+                const float r = fmaf(k, c8[u], (hi_half ? kp : -kp) * s8[u]);
+                part = fmaf(qv[u], r, part);
+            }
+            const float si = row_sum16(part);
+            s[i] = w0 + NR * i < n_w ? si : -INFINITY;
+            mb = fmaxf(mb, s[i]);
+        }
+        const float alpha = exp2f(m - mb);
+        l *= alpha;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] *= alpha;
+#pragma unroll
+        for (int i = 0; i < kWinBatch; ++i) {
+            const float wgt = exp2f(s[i] - mb);
+            l += wgt;
+            const uint32_t v4[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                o[2 * u] = fmaf(wgt, bf16_lo(v4[u]), o[2 * u]);
+                o[2 * u + 1] = fmaf(wgt, bf16_hi(v4[u]), o[2 * u + 1]);
+            }
+        }
+        m = mb;
+    }
+    __shared__ float red[NR][D + 2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) red[trow][8 * c16 + u] = o[u];
+    if (c16 == 0) {
+        red[trow][D] = m;
+        red[trow][D + 1] = l;
     }
     __syncthreads();
-    if (tid < D) {
-        float M = -INFINITY;
-        for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, red[w2][D]);
-        float Ls = 0.f, o = 0.f;
-        for (int w2 = 0; w2 < 4; ++w2) {
-            const float fw = red[w2][D] == -INFINITY ? 0.f : exp2f(red[w2][D] - M);
-            Ls += red[w2][D + 1] * fw;
-            o += red[w2][tid] * fw;
+    if (tid >= D) return;
+    float M = -INFINITY;
+    for (int r = 0; r < NR; ++r) M = fmaxf(M, red[r][D]);
+    float Ls = 0.f, ov = 0.f;
+    for (int r = 0; r < NR; ++r) {
+        const float fw = red[r][D] == -INFINITY ? 0.f : exp2f(red[r][D] - M);
+        Ls += red[r][D + 1] * fw;
+        ov += red[r][tid] * fw;
+    }
+    // an empty window (no sink, no recent token) contributes nothing
+    const float o_win = Ls > 0.f ? ov / Ls : 0.f;
+    const float lse_win = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+    if constexpr (!kMerge) {
+        const long orow = row * a.S_tot + a.num_splits;
+        a.part_o[orow * D + tid] = o_win;
+        if (tid == 0) a.part_lse[orow] = lse_win;
+    } else {
+        const int S = a.num_splits;
+        const float* pl = a.part_lse + row * a.S_tot;
+        auto lse_of = [&](int s2) { return s2 < kWinPrefetch ? pre_l[s2] : pl[s2]; };
+        float Mx = lse_win;
+#pragma unroll
+        for (int s2 = 0; s2 < kWinPrefetch; ++s2)
+            if (s2 < S) Mx = fmaxf(Mx, pre_l[s2]);
+        for (int s2 = kWinPrefetch; s2 < S; ++s2) Mx = fmaxf(Mx, pl[s2]);
+        float Lx = lse_win == -INFINITY ? 0.f : expf(lse_win - Mx);
+        for (int s2 = 0; s2 < S; ++s2) {
+            const float ls = lse_of(s2);
+            Lx += ls == -INFINITY ? 0.f : expf(ls - Mx);
         }
-        const long orow = (long(rb) * g.H + h) * a.S_tot + a.num_splits;
-        a.part_o[orow * D + tid] = o / Ls;
-        if (tid == 0) a.part_lse[orow] = (M + log2f(Ls)) * kLn2;
+        const float lse = Mx + logf(Lx);              // finite: a row holds at least one token
+        float acc = lse_win == -INFINITY ? 0.f : expf(lse_win - lse) * o_win;
+#pragma unroll
+        for (int s2 = 0; s2 < kWinPrefetch; ++s2)
+            if (s2 < S && pre_l[s2] != -INFINITY) acc += expf(pre_l[s2] - lse) * pre_o[s2];
+        for (int s2 = kWinPrefetch; s2 < S; ++s2)
+            if (pl[s2] != -INFINITY) acc += expf(pl[s2] - lse) * a.part_o[(row * a.S_tot + s2) * D + tid];
+        out[row * D + tid] = acc;
+        if (lse_out && tid == 0) lse_out[row] = lse;
     }
 }
 
@@ -1049,8 +1161,13 @@ lvq_status launch_quant(AttnArgs& a, void* scratch, hipStream_t stream) {
     return check_launch("quantized partial");
 }
 
-lvq_status launch_window(AttnArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(window_partial_kernel, dim3(a.geo.H, a.B), dim3(256), 0, stream, a);
+// The window partial into slot a.num_splits, or (out != NULL) merged with slots 0 .. a.num_splits-1 into
+// the attention output.
+lvq_status launch_window(AttnArgs& a, float* out, float* lse_out, hipStream_t stream) {
+    if (out)
+        hipLaunchKernelGGL(window_kernel<true>, dim3(a.geo.H, a.B), dim3(256), 0, stream, a, out, lse_out);
+    else
+        hipLaunchKernelGGL(window_kernel<false>, dim3(a.geo.H, a.B), dim3(256), 0, stream, a, nullptr, nullptr);
     return check_launch("window partial");
 }
 
@@ -1126,7 +1243,7 @@ extern "C" lvq_status lvq_window_partial(const lvq_geom* gp, int32_t step, const
     a.part_lse = part_lse;
     a.S_tot = S_tot;
     a.num_splits = slot;
-    return launch_window(a, stream);
+    return launch_window(a, nullptr, nullptr, stream);
 }
 
 extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
@@ -1173,10 +1290,7 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
     a.pps = pages_per_split(max_pages, S);
     if ((st = launch_quant(a, static_cast<unsigned char*>(ws) + partials_bytes(g, B, S + 1), stream)) != LVQ_OK)
         return st;
-    if ((st = launch_window(a, stream)) != LVQ_OK) return st;
-    hipLaunchKernelGGL(merge_kernel, dim3(B * g.H), dim3(128), 0, stream, a.part_o, a.part_lse, S + 1, g.D, out,
-                       lse_out);
-    return check_launch("lvq_decode_attn: merge");
+    return launch_window(a, out, lse_out, stream);
 }
 
 extern "C" int32_t lvq_decode_attn_splits(const lvq_geom* gp, int32_t B, int32_t max_len) {

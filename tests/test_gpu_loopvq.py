@@ -172,6 +172,33 @@ def test_decode_edge_lengths(monkeypatch):
                     _check_row(p, t, b, h, geo, idx[(b, h)], out, lse)
 
 
+def test_partial_entry_points_compose():
+    """lvq_quant_partial + lvq_window_partial + splitk_lse_merge give the attention of the oracle (the
+    standalone path that lvq_decode_attn fuses)."""
+    import decode_attention_loopvq_amd as lvq
+    from tests import harness
+    cfg = loopvq_config("loopvq-b64-6k", B=5, H=2, L=700)
+    geo = _geo(cfg)
+    rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    p = harness.build_loopvq(cfg, keep=rows)
+    idx = {r: _check_indices(p, r[0], r[1], geo) for r in rows}
+    c = p.cache
+    S = 2
+    for t in range(cfg.T):
+        _say(f"[partials] step {t} num_splits={S}")
+        po = torch.empty((cfg.B * cfg.H, S + 1, 128), dtype=torch.float32, device="cuda")
+        pl = torch.empty((cfg.B * cfg.H, S + 1), dtype=torch.float32, device="cuda")
+        q = p.q[t].contiguous()
+        lvq.lvq_quant_partial(p.g, t, q, c.pool, c.page_table, c.seq_len, c.max_len, p.slices, p.rope_cos,
+                              p.rope_sin, p.sm_scale, po, pl, S, rope_f16=p.rope16)
+        lvq.lvq_window_partial(p.g, t, q, c.seq_len, c.max_len, c.win_k, c.win_v, p.rope_cos, p.rope_sin,
+                               p.sm_scale, po, pl, slot=S)
+        out, lse = lvq.splitk_lse_merge(po, pl)
+        torch.cuda.synchronize()
+        for (b, h) in rows:
+            _check_row(p, t, b, h, geo, idx[(b, h)], out.view(cfg.B, cfg.H, 128), lse.view(cfg.B, cfg.H))
+
+
 def test_merge_parity():
     import decode_attention_loopvq_amd as lvq
     rng = np.random.default_rng(0)
