@@ -9,14 +9,21 @@ two-requests-per-block saving at this batch and context).
 
 One step is one decode step of a model with `--layers` attention layers that
 each own an independent copy of that cache: for each of the T loop steps,
-every layer runs lvq_decode_attn (index-page partial, bf16-window partial,
-logsumexp merge).  Rotating over the copies (3.4 GB) keeps the 256 MB
-Infinity Cache from serving repeated reads, as layers would in a real model.
+every layer runs lvq_decode_attn (the index-page partial kernel, then the
+bf16-window kernel that merges the partials through logsumexp).  Rotating
+over the copies (3.4 GB) keeps the 256 MB Infinity Cache from serving
+repeated reads, as layers would in a real model.
 
 Printed: one JSON line with the whole-call rate (algorithmic GB/s, fraction
 of the 8 TB/s HBM peak, token-heads/s), the roofline entry of the dominant
 kernel (the index-page partial, timed alone with HIP events on the stream it
-runs on), and the fp64 oracle timed on a bounded sample on the host.
+runs on; its HBM traffic from the committed counter runs when they match the
+kernel source), and the fp64 oracle timed on a bounded sample on the host.
+
+Counter runs (rocprofv3 --pmc, one counter per run): `--mode index-only`
+launches only the index-page partial, `--mode copy` a plain 256 MiB device
+copy for calibration, and `--pmc-summary` turns the four output directories
+into profiles/index_attn_b64_6k_traffic.json.
 """
 
 from __future__ import annotations
@@ -41,8 +48,21 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def call_bytes(g, lengths, max_len, cb_bytes):
-    """Algorithmic bytes of one lvq_decode_attn call, split by stream."""
+def _positions(g, lengths):
+    """(largest index-token count, set of window positions) over the requests."""
+    from decode_attention_loopvq_amd.layout import n_index_pages
+    max_q, win = 0, set()
+    for L in lengths:
+        nq = g.page * n_index_pages(L, g)
+        max_q = max(max_q, nq)
+        win.update(range(min(L, g.sink)))
+        win.update(range(g.sink + nq, L))
+    return max_q, win
+
+
+def call_bytes(g, lengths, cb_bytes):
+    """Algorithmic bytes of one lvq_decode_attn call, split by stream: every
+    input read once, the output written once."""
     from decode_attention_loopvq_amd.layout import index_groups, n_index_pages
     NG = index_groups(g)
     idx = win = pt = 0
@@ -53,25 +73,26 @@ def call_bytes(g, lengths, max_len, cb_bytes):
         win += g.H * (L - nq) * 2 * g.D * 2           # bf16 K and V of sinks + recent tokens
         pt += 4 * n                                   # page ids
     cb = g.H * 2 * g.K * g.D * cb_bytes               # the step's K and V slices
-    rope = max_len * g.D * 4                          # cos + sin fp32
+    max_q, wpos = _positions(g, lengths)
+    rope = max_q * g.D * 2 + len(wpos) * g.D * 4      # fp16 cos/sin of index positions, fp32 of window ones
     qo = len(lengths) * g.H * g.D * (2 + 4)           # bf16 q in, fp32 out
     return {"index": idx, "window": win, "page_table": pt, "codebook": cb, "rope": rope, "q_out": qo}
 
 
 def quant_kernel_bytes(g, lengths, cb_bytes, splits):
-    """Algorithmic bytes of one index-page partial launch: index rows, page ids,
-    codebook slices, cos/sin of the paged positions, q, and the partials written."""
+    """Algorithmic bytes of one index-page partial launch (index_attn_kernel):
+    index rows, page ids, codebook slices, fp16 cos/sin of the paged
+    positions, q, and the partials written."""
     from decode_attention_loopvq_amd.layout import index_groups, n_index_pages
     NG = index_groups(g)
     idx = pt = 0
-    max_q = 0
     for L in lengths:
         n = n_index_pages(L, g)
         idx += g.H * g.page * n * 2 * NG
         pt += 4 * n
-        max_q = max(max_q, g.page * n)
     cb = g.H * 2 * g.K * g.D * cb_bytes
-    rope = max_q * g.D * 4
+    max_q, _ = _positions(g, lengths)
+    rope = max_q * g.D * 2
     q = len(lengths) * g.H * g.D * 2
     parts = len(lengths) * g.H * splits * (g.D + 1) * 4
     return idx + pt + cb + rope + q + parts
@@ -112,6 +133,64 @@ def cpu_baseline(prob, rows, seconds):
     return n_rows, el
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_attn_b64_6k_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_loopvq_amd", "csrc", "attn.hip")
+COPY_BYTES = 256 << 20
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per index_attn_kernel launch from the committed counter runs, or None when the kernel
+    source has changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t["bytes_per_launch"] if t.get("attn_hip_sha256_16") == kernel_source_hash() else None
+
+
+def _pmc_values(d, counter, name_re):
+    """Per-dispatch values of `counter` for kernels whose name matches name_re, from a rocprofv3 csv dir."""
+    import csv
+    import glob
+    import re
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and re.search(name_re, r["Kernel_Name"]):
+                vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Traffic of index_attn_kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the
+    same counter reads for a plain copy of COPY_BYTES; writes TRAFFIC_FILE."""
+    import statistics
+    kf = _pmc_values(fetch_dir, "FETCH_SIZE", "index_attn_kernel")
+    kw = _pmc_values(write_dir, "WRITE_SIZE", "index_attn_kernel")
+    cf = [v for v in _pmc_values(copy_fetch_dir, "FETCH_SIZE", "copy|elementwise") if v * 1024 > COPY_BYTES / 8]
+    cw = [v for v in _pmc_values(copy_write_dir, "WRITE_SIZE", "copy|elementwise") if v * 1024 > COPY_BYTES / 8]
+    if not (kf and kw and cf and cw):
+        raise SystemExit(f"missing counter values: kernel fetch {len(kf)} write {len(kw)}, copy {len(cf)} {len(cw)}")
+    sf = COPY_BYTES / (statistics.median(cf) * 1024)
+    sw = COPY_BYTES / (statistics.median(cw) * 1024)
+    fetch = statistics.median(kf) * 1024 * sf
+    write = statistics.median(kw) * 1024 * sw
+    t = {"kernel": "index_attn_kernel<8, 4>", "workload": WORKLOAD, "attn_hip_sha256_16": kernel_source_hash(),
+         "fetch_bytes": round(fetch), "write_bytes": round(write), "bytes_per_launch": round(fetch + write),
+         "copy_scale_fetch": round(sf, 4), "copy_scale_write": round(sw, 4), "dispatches": [len(kf), len(kw)]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    print(json.dumps(t))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,8 +200,16 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("bench", "index-only", "copy"), default="bench",
+                    help="index-only: launch only the index-page partial (for counter runs); "
+                         "copy: a plain device copy of 256 MiB (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output dirs: write the measured traffic of the index-page kernel")
     args = ap.parse_args()
 
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the path "
@@ -138,11 +225,20 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.mode == "copy":
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {COPY_BYTES} bytes x {args.steps}", flush=True)
+        return
     cfg = loopvq_config(WORKLOAD)
     sample_rows = [(0, 0), (37, 9)]
+    want_cpu = args.mode == "bench" and not args.no_cpu_baseline
     log(f"[bench] building {WORKLOAD}: B={cfg.B} H={cfg.H} L={cfg.L} T={cfg.T} Tc={cfg.Tc} G={cfg.G}")
     t0 = time.perf_counter()
-    prob = harness.build_loopvq(cfg, keep=[] if args.no_cpu_baseline else sample_rows)
+    prob = harness.build_loopvq(cfg, keep=sample_rows if want_cpu else [])
     g, cache = prob.g, prob.cache
     log(f"[bench] built in {time.perf_counter() - t0:.1f}s; copying to {args.layers} layers")
     pools = [cache.pool] + [cache.pool.clone() for _ in range(args.layers - 1)]
@@ -163,7 +259,8 @@ def main():
         return (gref, t, qs[t].data_ptr(), pools[l].data_ptr(), cache.page_table.data_ptr(),
                 int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, wks[l].data_ptr(),
                 wvs[l].data_ptr(), prob.slices.data_ptr(), prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(),
-                prob.rope16.data_ptr(), rope_len, C.c_float(prob.sm_scale), outs[l].data_ptr(), None, ws.data_ptr(), ws_bytes, S, B, sh)
+                prob.rope16.data_ptr(), rope_len, C.c_float(prob.sm_scale), outs[l].data_ptr(), None,
+                ws.data_ptr(), ws_bytes, S, B, sh)
 
     calls = [full_args(t, l) for t in range(cfg.T) for l in range(args.layers)]
 
@@ -173,19 +270,18 @@ def main():
             if st != 0:
                 raise RuntimeError(lib.lvq_last_error().decode())
 
-    # Dominant kernel alone: the index-page partial into the same workspace.
-    rows_tot = B * g.H * (S + 1)
-    part_o = ws.view(torch.float32)[: rows_tot * g.D]
-    part_lse = ws.view(torch.float32)[rows_tot * g.D: rows_tot * (g.D + 1)]
+    # The dominant kernel alone: the index-page partial (one index_attn_kernel launch) into its own buffers.
+    part_o = torch.empty((B * g.H, S, g.D), dtype=torch.float32, device="cuda")
+    part_lse = torch.empty((B * g.H, S), dtype=torch.float32, device="cuda")
     qws_bytes = lvq.lvq_quant_partial_workspace(g, B, cache.max_len)
-    qws = torch.empty(qws_bytes, dtype=torch.uint8, device="cuda")
+    qws = torch.empty(max(qws_bytes, 256), dtype=torch.uint8, device="cuda")
 
     def quant_args(t, l):
         return (gref, t, qs[t].data_ptr(), pools[l].data_ptr(), cache.page_table.data_ptr(),
                 int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, prob.slices.data_ptr(),
                 prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(), prob.rope16.data_ptr(), rope_len,
-                C.c_float(prob.sm_scale),
-                part_o.data_ptr(), part_lse.data_ptr(), S, S + 1, qws.data_ptr(), qws_bytes, B, sh)
+                C.c_float(prob.sm_scale), part_o.data_ptr(), part_lse.data_ptr(), S, S, qws.data_ptr(),
+                qws.numel(), B, sh)
 
     qcalls = [quant_args(t, l) for t in range(cfg.T) for l in range(args.layers)]
 
@@ -194,6 +290,13 @@ def main():
             st = lib.lvq_quant_partial(*a)
             if st != 0:
                 raise RuntimeError(lib.lvq_last_error().decode())
+
+    if args.mode == "index-only":
+        for _ in range(args.warmup + args.steps):
+            quant_only()
+        torch.cuda.synchronize()
+        print(f"index-only: {(args.warmup + args.steps) * len(qcalls)} launches", flush=True)
+        return
 
     log(f"[bench] warmup {args.warmup} steps ({len(calls)} calls each, num_splits={S})")
     for _ in range(args.warmup):
@@ -210,7 +313,7 @@ def main():
     ms_total = e0.elapsed_time(e1)
     log(f"[bench] timed {args.steps} steps: {ms_total:.3f} ms")
 
-    # The dominant kernel alone, same rotation.
+    # The dominant kernel alone, same rotation, HIP events on the stream it is launched on.
     for _ in range(2):
         quant_only()
     torch.cuda.synchronize()
@@ -224,7 +327,7 @@ def main():
     log(f"[bench] index-page partial alone: {ms_quant * 1e3:.2f} us per launch")
 
     cb_bytes = 2 if cfg.cb_dtype == "bf16" else 4
-    parts = call_bytes(g, prob.lengths, cache.max_len, cb_bytes)
+    parts = call_bytes(g, prob.lengths, cb_bytes)
     per_call = sum(parts.values())
     n_calls = args.steps * len(calls)
     sec = ms_total / 1e3
@@ -232,6 +335,7 @@ def main():
     token_heads = sum(prob.lengths) * g.H
     qbytes = quant_kernel_bytes(g, prob.lengths, cb_bytes, S)
     q_gbps = qbytes / (ms_quant / 1e3) / 1e9
+    traffic = measured_traffic()
 
     result = {
         "metric": METRIC,
@@ -244,7 +348,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16/f32",
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD, "B": cfg.B, "H": cfg.H, "L": cfg.L, "T": cfg.T, "Tc": cfg.Tc, "G": cfg.G,
@@ -257,19 +361,19 @@ def main():
         "us_per_call": round(ms_total * 1e3 / n_calls, 2),
         "bytes_per_call": parts,
         "roofline": {
-            "kernel": "quant_partial_kernel (index-page partial)",
+            "kernel": "index_attn_kernel<8, 4> (index-page partial)",
             "bound": "hbm",
             "achieved": round(q_gbps, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "us_per_launch": round(ms_quant * 1e3, 2),
             "algorithmic_bytes_per_launch": qbytes,
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if want_cpu:
         log(f"[bench] cpu baseline: fp64 oracle on {len(sample_rows)} rows, about {args.cpu_seconds:.0f}s")
         n_rows, el = cpu_baseline(prob, sample_rows, args.cpu_seconds)
         share = per_call / (B * g.H)
