@@ -95,7 +95,9 @@ LVQ_API const char* lvq_last_error(void);
  *             holds the index of group m ^ (tau & 15).  Attention bins value
  *             weights per (group, codeword) and the rotation lets the lanes
  *             of one LDS phase update 16 distinct groups.
- *  page_table [B][pt_stride] int32, logical page -> physical page
+ *  page_table [B][pt_stride] int32, logical page -> physical page; attention
+ *             reads only the entries of a request's own index pages, which
+ *             must name pages of the pool (other entries may hold anything)
  *  window     [B][T][H][Wcap][D] bf16, Wcap = sink + W + page; pre-RoPE
  *             K (and separately V) of every loop step; position p < sink sits
  *             in slot p, position p >= sink in slot sink + (p - sink) % (W + page)
@@ -176,13 +178,13 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  * from their indices through the step's codebook slice, and sink/recent
  * positions come from the window buffers; keys are rotated at their absolute
  * position.  The index pages are attended in `num_splits` splits per request
- * (Flash-Decoding) and the bf16 window by a second kernel; a third merges all
- * partials exactly through logsumexp.  With bf16 codebooks the index pages
- * take two passes: one scores every index token (kept in the workspace), the
- * next turns the scores into softmax weights and accumulates them per
- * (group, codeword) of the value indices.  With bf16 codebooks four requests
- * (two when c = 4) share one workgroup and with it the codebook slice and
- * the RoPE table loads.
+ * (Flash-Decoding); a second kernel attends the bf16 window and merges its
+ * partial with the splits' exactly through logsumexp.  With bf16 codebooks
+ * one workgroup scores the tokens of a split for four requests (two when
+ * c = 4), sharing the codebook slice and the RoPE table loads, then turns the
+ * scores into softmax weights and accumulates them per (group, codeword) of
+ * the value indices; a split then holds at most 1536 index tokens (192
+ * pages).
  *
  *  q          bf16 [B][H][D], already rotated at position seq_len[b] - 1.
  *  seq_len    device int32 [B], 1 <= seq_len[b] <= max_len <= rope_len.
@@ -195,8 +197,13 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  *  rope_f16   packed fp16 table (lvq_rope_table_f16) with the same rope_len;
  *             required for bf16 codebooks, ignored (may be NULL) for fp32.
  *  out        fp32 [B][H][D];  lse_out fp32 [B][H] or NULL.
- *  ws         device workspace of at least lvq_decode_attn_workspace() bytes.
- *  num_splits 0 lets the library choose; otherwise 1..1024.
+ *  ws         device workspace of at least lvq_decode_attn_workspace() bytes,
+ *             256-byte aligned (LVQ_ERR_INVALID_ARG otherwise); contents
+ *             need no initialisation and are scratch after the call.
+ *  num_splits 0 lets the library choose; otherwise 1..1024, and with bf16
+ *             codebooks large enough that a split holds at most 192 index
+ *             pages: ceil(ceil(max_pages / num_splits) / 8) * 8 <= 192,
+ *             max_pages = (max_len - sink - window) / 8 (LVQ_ERR_INVALID_ARG).
  */
 LVQ_API lvq_status lvq_decode_attn(const lvq_geom* g, int32_t step, const void* q,
                            const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
@@ -222,11 +229,10 @@ LVQ_API int32_t lvq_decode_attn_splits(const lvq_geom* g, int32_t B, int32_t max
  *   num_splits ranges of ceil(max_pages / num_splits) pages and split s writes
  *   slot s; an empty range writes part_o = 0, part_lse = -inf.
  *   S_tot >= num_splits.  Splits cover ceil(ceil(max_pages / num_splits) / 8) * 8
- *   pages each (later ones may be empty).  ws is device scratch of at least
- *   lvq_quant_partial_workspace(g, B, max_len) bytes: the query repacked as
- *   fp16 (pre-scaled by sm_scale * log2 e), the scores of every index token
- *   and the maximum of every 64-token chunk (two passes: scores, then value
- *   bins; see lvq_decode_attn).
+ *   pages each (later ones may be empty; with bf16 codebooks at most 192, as
+ *   for lvq_decode_attn).  ws is 256-byte aligned device scratch of at least
+ *   lvq_quant_partial_workspace(g, B, max_len) bytes: the query rows repacked
+ *   as fp16 (pre-scaled by sm_scale * log2 e), 256 B per (request, head).
  * lvq_window_partial: the sink and recent bf16 tokens of step `step`, written
  *   to slot `slot` (< S_tot).  Never empty for seq_len >= 1.
  * Other arguments as for lvq_decode_attn.
