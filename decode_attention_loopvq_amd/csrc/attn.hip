@@ -466,9 +466,28 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
     __shared__ float wmax[NW][R];
     uint32_t* bins = reinterpret_cast<uint32_t*>(lds);
     const Geo& g = a.geo;
-    const int split = blockIdx.x, h = blockIdx.y, r0 = blockIdx.z * R;
+    // Head fastest in the grid: workgroup ids of one head are congruent modulo 8, so the head's slices
+    // stay in one XCD's L2.
+    const int h = blockIdx.x, split = blockIdx.y, r0 = blockIdx.z * R;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Loads that need no request length go first: the K slice of head h and the query elements this
+    // thread packs.
+    uint4 stage[NSTAGE];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_k) +
+                                                          h * a.slice_hstride);
+#pragma unroll
+        for (int i = 0; i < NSTAGE; ++i) stage[i] = src[tid + i * NT];
+    }
+    uint32_t qraw = 0;                              // two bf16 query elements (packed-query dword tid & 63)
+    const int qj = tid >> 6, qt = tid & 63;
+    const long qprow = long(min(r0 + min(qj, R - 1), a.B - 1)) * g.H + h;
+    if (tid < R * 64) {
+        const int m = qt >> 2, k = qt & 3;
+        const int ch = (k < 2 ? 0 : 64) + 4 * m + 2 * (k & 1);
+        qraw = *reinterpret_cast<const uint32_t*>(a.q + qprow * D + ch);
+    }
     int lo[R], hi[R];
     if (!split_ranges<R>(a, split, r0, lo, hi)) {
         for (int e = tid; e < R * D; e += NT) {
@@ -496,25 +515,15 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
 
     // ---- setup: packed query rows (dword t of row j: the fp16 pair of chunk t >> 2, see the score steps) ----
     if (tid < R * 64) {
-        const int j = tid >> 6, t = tid & 63;
-        const int m = t >> 2, k = t & 3;
-        const int ch = (k < 2 ? 0 : 64) + 4 * m + 2 * (k & 1);
-        const uint16_t* qr = a.q + srow[j] * D;
-        const h2_t v = {(_Float16)(bf16_to_f32(qr[ch]) * a.scale_log2),
-                        (_Float16)(bf16_to_f32(qr[ch + 1]) * a.scale_log2)};
-        const_cast<uint32_t*>(a.qpack)[srow[j] * 64 + t] = __builtin_bit_cast(uint32_t, v);
+        const h2_t v = {(_Float16)(bf16_lo(qraw) * a.scale_log2), (_Float16)(bf16_hi(qraw) * a.scale_log2)};
+        const_cast<uint32_t*>(a.qpack)[qprow * 64 + qt] = __builtin_bit_cast(uint32_t, v);
     }
-    {   // K slice of head h, bf16 -> fp16: every load issued before the first conversion
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_k) +
-                                                          h * a.slice_hstride);
+    {   // K slice of head h, bf16 -> fp16
         uint4* dst = reinterpret_cast<uint4*>(lds);
-        uint4 w[NSTAGE];
-#pragma unroll
-        for (int i = 0; i < NSTAGE; ++i) w[i] = src[tid + i * NT];
 #pragma unroll
         for (int i = 0; i < NSTAGE; ++i)
-            dst[tid + i * NT] = make_uint4(bf16x2_to_f16x2(w[i].x), bf16x2_to_f16x2(w[i].y),
-                                           bf16x2_to_f16x2(w[i].z), bf16x2_to_f16x2(w[i].w));
+            dst[tid + i * NT] = make_uint4(bf16x2_to_f16x2(stage[i].x), bf16x2_to_f16x2(stage[i].y),
+                                           bf16x2_to_f16x2(stage[i].z), bf16x2_to_f16x2(stage[i].w));
     }
     const uint32_t page_bytes = uint32_t(g.page_bytes);
     const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG;   // (block, head) slab of page 0
@@ -852,7 +861,8 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
 // of loop step t.  Grid (head, request); 256 threads in 16 rows of 16 lanes;
 // row r takes window tokens r, r + 16, ...  Lane c of a row owns channels
 // 8c .. 8c+7 of its token (one 16-byte load of K and of V); lanes c and c ^ 8
-// hold the two halves of each RoPE pair (i, i + 64) and trade them through
+// hold the two halves of each RoPE pair (i, i + 64) and trade them, and the
+// cos (loaded by c < 8) and sin (by c >= 8) of their frequencies, through
 // DPP; a score is a 16-lane DPP sum.  Each row keeps its own online softmax
 // over kWinBatch tokens at a time (every load of the batch issued first);
 // the 16 rows are combined through LDS.  kMerge: the window partial is
@@ -877,7 +887,7 @@ __device__ __forceinline__ float row_sum16(float x) {
 }
 
 template <bool kMerge>
-__global__ void __launch_bounds__(256) window_kernel(AttnArgs a, float* __restrict__ out, float* __restrict__ lse_out) {
+__global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __restrict__ out, float* __restrict__ lse_out) {
     constexpr int D = 128, NR = 16;
     const Geo& g = a.geo;
     const int h = blockIdx.x, rb = blockIdx.y;
@@ -919,7 +929,7 @@ __global__ void __launch_bounds__(256) window_kernel(AttnArgs a, float* __restri
     for (int u = 0; u < 8; ++u) o[u] = 0.f;
     for (int w0 = trow; w0 < n_w; w0 += NR * kWinBatch) {
         uint4 kw[kWinBatch], vw[kWinBatch];
-        float4 cs[kWinBatch][2], sn[kWinBatch][2];
+        float4 tg[kWinBatch][2];                    // cos (lanes c < 8) or sin (c >= 8) of the lane's frequencies
 #pragma unroll
         for (int i = 0; i < kWinBatch; ++i) {
             const int w = min(w0 + NR * i, n_w - 1);      // a valid window token; extra ones are masked below
@@ -927,27 +937,25 @@ __global__ void __launch_bounds__(256) window_kernel(AttnArgs a, float* __restri
             const int slot = p < g.sink ? p : g.sink + (p - g.sink) % ring;
             kw[i] = *reinterpret_cast<const uint4*>(a.wk + wbase + long(slot) * D);
             vw[i] = *reinterpret_cast<const uint4*>(a.wv + wbase + long(slot) * D);
-            const float4* cp = reinterpret_cast<const float4*>(a.rc + long(p) * (D / 2) + f0);
-            const float4* sp = reinterpret_cast<const float4*>(a.rs + long(p) * (D / 2) + f0);
-            cs[i][0] = cp[0]; cs[i][1] = cp[1];
-            sn[i][0] = sp[0]; sn[i][1] = sp[1];
+            const float4* tp = reinterpret_cast<const float4*>((hi_half ? a.rs : a.rc) + long(p) * (D / 2) + f0);
+            tg[i][0] = tp[0]; tg[i][1] = tp[1];
         }
         float s[kWinBatch];
         float mb = m;
 #pragma unroll
         for (int i = 0; i < kWinBatch; ++i) {
             const uint32_t k4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
-            const float c8[8] = {cs[i][0].x, cs[i][0].y, cs[i][0].z, cs[i][0].w,
-                                 cs[i][1].x, cs[i][1].y, cs[i][1].z, cs[i][1].w};
-            const float s8[8] = {sn[i][0].x, sn[i][0].y, sn[i][0].z, sn[i][0].w,
-                                 sn[i][1].x, sn[i][1].y, sn[i][1].z, sn[i][1].w};
+            const float t8[8] = {tg[i][0].x, tg[i][0].y, tg[i][0].z, tg[i][0].w,
+                                 tg[i][1].x, tg[i][1].y, tg[i][1].z, tg[i][1].w};
             float part = 0.f;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const float k = (u & 1) ? bf16_hi(k4[u >> 1]) : bf16_lo(k4[u >> 1]);
                 const float kp = dpp<0x128>(k);           // the other half of the RoPE pair (lane c ^ 8)
+                const float tp = dpp<0x128>(t8[u]);       // and the other of cos / sin
+                const float c = hi_half ? tp : t8[u], sgn_s = hi_half ? t8[u] : -tp;
                 // lo half: k_i cos - k_{i+64} sin;  hi half: k_{i+64} cos + k_i sin
-                const float r = fmaf(k, c8[u], (hi_half ? kp : -kp) * s8[u]);
+                const float r = fmaf(k, c, kp * sgn_s);
                 part = fmaf(qv[u], r, part);
             }
             const float si = row_sum16(part);
@@ -998,17 +1006,16 @@ __global__ void __launch_bounds__(256) window_kernel(AttnArgs a, float* __restri
     } else {
         const int S = a.num_splits;
         const float* pl = a.part_lse + row * a.S_tot;
-        auto lse_of = [&](int s2) { return s2 < kWinPrefetch ? pre_l[s2] : pl[s2]; };
         float Mx = lse_win;
 #pragma unroll
         for (int s2 = 0; s2 < kWinPrefetch; ++s2)
             if (s2 < S) Mx = fmaxf(Mx, pre_l[s2]);
         for (int s2 = kWinPrefetch; s2 < S; ++s2) Mx = fmaxf(Mx, pl[s2]);
         float Lx = lse_win == -INFINITY ? 0.f : expf(lse_win - Mx);
-        for (int s2 = 0; s2 < S; ++s2) {
-            const float ls = lse_of(s2);
-            Lx += ls == -INFINITY ? 0.f : expf(ls - Mx);
-        }
+#pragma unroll
+        for (int s2 = 0; s2 < kWinPrefetch; ++s2)
+            if (s2 < S && pre_l[s2] != -INFINITY) Lx += expf(pre_l[s2] - Mx);
+        for (int s2 = kWinPrefetch; s2 < S; ++s2) Lx += pl[s2] == -INFINITY ? 0.f : expf(pl[s2] - Mx);
         const float lse = Mx + logf(Lx);              // finite: a row holds at least one token
         float acc = lse_win == -INFINITY ? 0.f : expf(lse_win - lse) * o_win;
 #pragma unroll
@@ -1145,7 +1152,7 @@ lvq_status launch_quant(AttnArgs& a, void* scratch, hipStream_t stream) {
         a.qpack = static_cast<const uint32_t*>(scratch);
         a.fix_bits = 32 - ceil_log2(long(a.pps) * g.page + 1);
         const int R = reqs_per_wg(g);
-        const dim3 grid(a.num_splits, g.H, ceil_div(a.B, R));
+        const dim3 grid(g.H, a.num_splits, ceil_div(a.B, R));
         if (g.c == 8)
             hipLaunchKernelGGL((index_attn_kernel<8, 4>), grid, dim3(kIThreads), 0, stream, a);
         else
