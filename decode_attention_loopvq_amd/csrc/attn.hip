@@ -670,6 +670,10 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
         for (int k = 0; k < CPW; ++k) sreg[k][j] = 0.f;
     }
     const int c0 = t_lo / kChunk + wave;
+    // page ids of the weight phase's first two chunks, loaded now so that they wait in registers
+    uint32_t pidA[R], pidB[R];
+    load_pid(c0, pidA);
+    load_pid(c0 + NW, pidB);
     int nch = 0;                                    // chunks of this wave
     {
         int c = c0;
@@ -697,6 +701,10 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
             ++nch;
         }
     }
+    // value index rows of the weight phase's first chunk
+    uint32_t ivA[R][IW], ivB[R][IW];
+    load_idx(c0, 1, pidA, ivA);
+    load_pid(c0 + 2 * NW, pidA);
     // scores of this wave's chunk i now in sreg[CPW - nch + i]: move chunk 0 to the first row
     for (int s = nch; s < CPW; ++s) shift_scores();
 
@@ -706,9 +714,6 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
         const float mw = wave_max_dpp(rmax[j]);
         if (lane == 0) wmax[wave][j] = mw;
     }
-    uint32_t pidA[R], pidB[R];
-    load_pid(c0, pidA);
-    load_pid(c0 + NW, pidB);
     __syncthreads();                                // every wave is done with the K slice
 #pragma unroll
     for (int i = 0; i < K * 64 / 4 / NT; ++i) reinterpret_cast<uint4*>(bins)[tid + i * NT] = make_uint4(0u, 0u, 0u, 0u);
@@ -724,9 +729,6 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
             for (int i = 0; i < 16 / GPL; ++i) vrow[k * (16 / GPL) + i] = src[i];
         }
     }
-    uint32_t ivA[R][IW], ivB[R][IW];
-    load_idx(c0, 1, pidA, ivA);
-    load_pid(c0 + 2 * NW, pidA);
     __syncthreads();                                // bins cleared, wave maxima visible
     float M[R];
 #pragma unroll
