@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Per-step measurements of the quantized-KV decode path on one MI355X.
+
+bench.py measures the headline workload (LoopVQ B=64, 6K).  This script
+times every other step of the path on its own workload, each against the
+roofline that bounds it, and prints one JSON line per measurement:
+
+  encode-prefill   lvq_encode of every index page, K and V, 32K context
+                   (B=8, H=16, T_c=4, G=32): bf16 distance contraction,
+                   2*K*G flops per coupled vector; MFMA and HBM fractions
+  encode-page      lvq_encode of one page per request (the decode-time
+                   encode of the oldest window page), same workload
+  attn-32k         lvq_decode_attn, 32K context, 0.25 bit, all four steps
+  attn-deep        lvq_decode_attn, 32 loop steps, ragged lengths, random
+                   page order (B=128, H=8), steps 0, 15, 31
+  attn-1k          lvq_decode_attn, one request, 1K context, fp32 codebooks
+                   (latency)
+  kivi-prefill     kivi_append of a 4K prompt (B=16, H=32)
+  kivi-append      kivi_append of one decode token
+  kivi-attn        kivi_decode_attn after the 4K prefill
+
+Inputs are seeded and synthetic (synth/), timed with HIP events on the
+launch stream after warm-up.  Peaks: HBM 8 TB/s, dense bf16 MFMA
+2.5 PFLOP/s.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12
+PEAK_BF16 = 2.5e15
+
+
+def timed(fn, reps, warmup=2):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e-3        # seconds per call
+
+
+def emit(**kw):
+    print(json.dumps(kw), flush=True)
+
+
+def encode_rows(reps):
+    import torch
+    import decode_attention_loopvq_amd as lvq
+    from decode_attention_loopvq_amd.layout import LoopVQCache, index_groups
+    from synth import loopvq as syn
+    from synth.configs import loopvq_config
+    from tests.harness import geom_of
+
+    cfg = loopvq_config("loopvq-b8-32k")
+    g = geom_of(cfg)
+    lengths = syn.lengths(cfg)
+    cache = LoopVQCache(g, lengths, device="cuda")
+    cb = syn.codebooks(cfg, "cuda")
+    xs = {kind: x for kind in ("k", "v") for beta, x in syn.raw_blocks(cfg, kind, "cuda") if beta == 0}
+    NG = index_groups(g)
+    n_vec = sum(cache.n_pages) * g.page * g.H * NG * 2                   # coupled vectors, K and V
+    flops = 2.0 * g.K * g.G * n_vec
+    in_bytes = sum(cache.n_pages) * g.page * g.H * g.Tc * g.D * 2 * 2 + cb[0].numel() * 2
+    out_bytes = n_vec
+
+    def prefill():
+        lvq.lvq_encode(g, 0, xs["k"], xs["v"], cb, cache.pool, cache.page_table, cache.first_page,
+                       cache.n_pages_dev, cache.max_pages, x_tok0=cache.tok0)
+
+    t = timed(prefill, reps, warmup=1)
+    emit(row="encode-prefill", workload=cfg.name, B=cfg.B, H=cfg.H, tokens_per_request=cache.n_pages[0] * 8,
+         ms=round(t * 1e3, 3), tflops=round(flops / t / 1e12, 3), mfma_frac=round(flops / t / PEAK_BF16, 5),
+         hbm_gbps=round((in_bytes + out_bytes) / t / 1e9, 1),
+         hbm_frac=round((in_bytes + out_bytes) / t / PEAK_HBM, 5), flops=flops, bytes=in_bytes + out_bytes)
+
+    last = torch.tensor([n - 1 for n in cache.n_pages], dtype=torch.int32, device="cuda")
+    one = torch.ones_like(last)
+    tok0 = cache.tok0 + last.long() * g.page
+
+    def page():
+        lvq.lvq_encode(g, 0, xs["k"], xs["v"], cb, cache.pool, cache.page_table, last, one, 1, x_tok0=tok0)
+
+    t = timed(page, reps * 20)
+    cb_bytes = g.H * 2 * NG * g.K * g.G * 2                               # the block's codebooks, read once
+    emit(row="encode-page", workload=cfg.name, B=cfg.B, H=cfg.H, us=round(t * 1e6, 2),
+         codebook_gbps=round(cb_bytes / t / 1e9, 1), codebook_bytes=cb_bytes)
+    del xs
+
+
+def attn_row(name, cfg_name, steps, reps, **over):
+    import torch
+    import decode_attention_loopvq_amd as lvq
+    from synth.configs import loopvq_config
+    from tests import harness
+    from bench import call_bytes
+
+    cfg = loopvq_config(cfg_name, **over)
+    p = harness.build_loopvq(cfg)
+    cb_bytes = 2 if cfg.cb_dtype == "bf16" else 4
+    per_call = sum(call_bytes(p.g, p.lengths, cb_bytes).values())
+    out = torch.empty((cfg.B, cfg.H, cfg.D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lvq.lvq_decode_attn_workspace(p.g, cfg.B, p.cache.max_len), dtype=torch.uint8,
+                     device="cuda")
+    qs = [p.q[t].contiguous() for t in range(cfg.T)]
+
+    def run():
+        for t in steps:
+            lvq.lvq_decode_attn(p.g, t, qs[t], p.cache.pool, p.cache.page_table, p.cache.seq_len, p.cache.max_len,
+                                p.cache.win_k, p.cache.win_v, p.slices, p.rope_cos, p.rope_sin, p.sm_scale,
+                                out=out, ws=ws, rope_f16=p.rope16)
+
+    t = timed(run, reps) / len(steps)
+    emit(row=name, workload=cfg.name, B=cfg.B, H=cfg.H, L=cfg.L, steps=list(steps), us_per_call=round(t * 1e6, 2),
+         gbps=round(per_call / t / 1e9, 1), hbm_frac=round(per_call / t / PEAK_HBM, 4), bytes_per_call=per_call,
+         token_heads_per_s=round(sum(p.lengths) * cfg.H / t, 1))
+
+
+def kivi_rows(reps):
+    import torch
+    import decode_attention_loopvq_amd as lvq
+    from synth import kivi as synk
+    from synth.configs import kivi_config
+
+    cfg = kivi_config("kivi-b16-4k")
+    cap = ((cfg.L + 256 + cfg.group - 1) // cfg.group) * cfg.group
+    g = lvq.make_kivi_geom(D=cfg.D, H=cfg.H, bits=cfg.bits, group=cfg.group, R=cfg.R, cap=cap)
+    k, v = synk.raw_kv(cfg, "cuda")
+    cache = lvq.KiviCache(g, cfg.B, device="cuda")
+
+    def prefill():
+        cache.len.zero_()
+        cache.n_kq.zero_()
+        cache.n_vq.zero_()
+        lvq.kivi_append(g, k, v, cache, prefill=True)
+
+    t = timed(prefill, reps)
+    raw = k.numel() * 2 * 2
+    n_q = cfg.L - cfg.R
+    written = cfg.B * cfg.H * (n_q * cfg.D // 4 * 2 + (n_q // cfg.group) * cfg.D * 4 + n_q * (cfg.D // cfg.group) * 4
+                               + cfg.R * cfg.D * 2 * 2)
+    emit(row="kivi-prefill", workload=cfg.name, B=cfg.B, H=cfg.H, L=cfg.L, us=round(t * 1e6, 2),
+         gbps=round((raw + written) / t / 1e9, 1), hbm_frac=round((raw + written) / t / PEAK_HBM, 4),
+         bytes=raw + written)
+
+    prefill()
+    q = synk.queries(cfg, "cuda")[0].contiguous()
+    out = torch.empty((cfg.B, cfg.H, cfg.D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lvq.kivi_decode_attn_workspace(g, cfg.B, cap), dtype=torch.uint8, device="cuda")
+
+    def attn():
+        lvq.kivi_decode_attn(g, q, cache, cap, synk.softmax_scale(cfg), out=out, ws=ws)
+
+    t = timed(attn, reps * 10)
+    per_bh = n_q * cfg.D // 4 * 2 + (n_q // cfg.group) * cfg.D * 4 + n_q * (cfg.D // cfg.group) * 4 \
+        + cfg.R * cfg.D * 2 * 2
+    by = cfg.B * cfg.H * (per_bh + cfg.D * (2 + 4))
+    emit(row="kivi-attn", workload=cfg.name, B=cfg.B, H=cfg.H, L=cfg.L, us_per_call=round(t * 1e6, 2),
+         gbps=round(by / t / 1e9, 1), hbm_frac=round(by / t / PEAK_HBM, 4), bytes_per_call=by,
+         token_heads_per_s=round(cfg.B * cfg.H * cfg.L / t, 1))
+
+    k1 = k[:, :, :1].clone()
+    v1 = v[:, :, :1].clone()
+    n_app = 64
+
+    def appends():
+        for _ in range(n_app):
+            lvq.kivi_append(g, k1, v1, cache, prefill=False)
+
+    t = timed(appends, 2, warmup=0) / n_app
+    emit(row="kivi-append", workload=cfg.name, B=cfg.B, H=cfg.H, us_per_token=round(t * 1e6, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--only", nargs="*", default=None, help="encode attn-32k attn-deep attn-1k kivi")
+    args = ap.parse_args()
+    import torch
+    assert torch.cuda.is_available(), "bench_rows.py needs a GPU"
+    want = set(args.only) if args.only else {"encode", "attn-32k", "attn-deep", "attn-1k", "kivi"}
+    if "encode" in want:
+        encode_rows(args.reps)
+    if "attn-32k" in want:
+        attn_row("attn-32k", "loopvq-b8-32k", range(4), args.reps)
+    if "attn-deep" in want:
+        attn_row("attn-deep", "loopvq-deep-ragged", (0, 15, 31), args.reps)
+    if "attn-1k" in want:
+        attn_row("attn-1k", "loopvq-b1-1k-fp32cb", range(4), args.reps * 20)
+    if "kivi" in want:
+        kivi_rows(args.reps)
+
+
+if __name__ == "__main__":
+    main()
