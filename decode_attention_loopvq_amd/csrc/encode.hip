@@ -8,6 +8,7 @@
 #include "common.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace lvq {
 namespace {
@@ -146,6 +147,205 @@ __global__ void encode_scan_kernel(Geo geo, int block, const uint16_t* __restric
         uint8_t(best_r);
 }
 
+
+// ---------------------------------------------------------------------------
+// Encoder for bf16 codebooks on the matrix cores (G <= 32).
+//
+// argmin_r ||z - e_r||^2 = argmax_r (z . e_r - ||e_r||^2 / 2): a contraction
+// of the coupled vectors with the codebook, [tokens x G] x [G x 256], done
+// by v_mfma_f32_16x16x32_bf16 with the accumulator started at -||e_r||^2/2
+// (products of bf16 values are exact in fp32; sums round in fp32).
+//
+// Workgroup: 8 waves, one index group each (groups 8*octet .. 8*octet+7), a
+// block of kEncTile * kEncTilesPerWg tokens of one (request, head, K|V).
+// A wave keeps its group's codebook as 16 B-fragments (codewords 16t .. 16t+15)
+// in registers.  MFMA lane l holds row / column l & 15 and coordinates
+// k = 8*(l >> 4) .. +7 of its operands (the codebook's own coordinate order
+// i*T_c + m; coordinates past G are zero), and result rows 4*(l >> 4) .. +3
+// of column l & 15.  Per 16-token tile: 16 MFMAs, the best of the 16 tiles
+// per lane, then the best of the 16 lanes of each row through DPP; the
+// lowest index wins exact ties.  Picks differ from the exact minimum only
+// by fp32 rounding of the sums.
+// ---------------------------------------------------------------------------
+constexpr int kEncTile = 16;
+constexpr int kEncTilesPerWg = 32;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct EncArgs {
+    Geo geo;
+    int block;
+    const uint16_t* xk;
+    const uint16_t* xv;
+    long s0, s1, s2, s3;
+    const int64_t* tok0;
+    const uint16_t* cb;
+    uint8_t* pool;
+    const int32_t* pt;
+    int pt_stride;
+    const int32_t* first_page;
+    const int32_t* n_pages;
+    int noct;                   // group octets, NG / 8
+};
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+}
+
+template <int TC>
+__global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
+    constexpr int IPL = 8 / TC;                  // channels per lane and step
+    const Geo& g = a.geo;
+    const int G = g.G, c = g.c;
+    const int oct = blockIdx.y % a.noct;
+    const int kv = (blockIdx.y / a.noct) & 1;
+    const int h = blockIdx.y / (2 * a.noct);
+    const int b = blockIdx.z;
+    const int ntok = a.n_pages[b] * g.page;
+    const int tok_base = blockIdx.x * (kEncTile * kEncTilesPerWg);
+    if (tok_base >= ntok) return;
+    const uint16_t* x = kv == 0 ? a.xk : a.xv;
+    if (x == nullptr) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int grp = oct * 8 + (tid >> 6);
+    const int n = lane & 15, q = lane >> 4;
+    const bool kin = 8 * q < G;                  // this lane's coordinates exist
+
+    // codebook fragments and -||e||^2 / 2 per column
+    const uint16_t* e = a.cb + ((((long(a.block) * g.H + h) * 2 + kv) * g.NG + grp) * g.K) * long(G);
+    bf16x8_t bfr[16];
+    float cinit[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        uint4 w = *reinterpret_cast<const uint4*>(e + long(16 * t + n) * G + (kin ? 8 * q : 0));
+        w = make_uint4(w.x & (kin ? ~0u : 0u), w.y & (kin ? ~0u : 0u), w.z & (kin ? ~0u : 0u), w.w & (kin ? ~0u : 0u));
+        bfr[t] = __builtin_bit_cast(bf16x8_t, w);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        float s = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            s = fmaf(bf16_lo(ww[u]), bf16_lo(ww[u]), s);
+            s = fmaf(bf16_hi(ww[u]), bf16_hi(ww[u]), s);
+        }
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        cinit[t] = -0.5f * s;
+    }
+
+    // lanes past G read the group's first channels (a valid address) and zero them
+    const long xbase = long(b) * a.s0 + long(h) * a.s1 + long(grp) * c + (kin ? (8 * q) / TC : 0);
+    const uint32_t kmask = kin ? 0xffffffffu : 0u;
+    const long row0 = (a.tok0 ? a.tok0[b] : 0);
+    const int fp = a.first_page[b];
+    const long blk_off = ((long(a.block) * g.H + h) * 2 + kv) * g.page * g.NG;
+    // coupled-vector coordinates k = 8q .. 8q+7 of token j (row of this lane): the raw words are loaded one
+    // tile ahead and interleaved into coordinate order (element u = (i - i0) * TC + m) when used
+    struct RawA { uint32_t w[TC][(IPL + 1) / 2]; };
+    auto load_a = [&](int j) {
+        const long row = row0 + min(j, ntok - 1);
+        const uint16_t* xr = x + xbase + row * a.s2;
+        RawA r;
+#pragma unroll
+        for (int m = 0; m < TC; ++m) {
+            if constexpr (IPL == 8) {
+                const uint4 w = *reinterpret_cast<const uint4*>(xr + m * a.s3);
+                r.w[m][0] = w.x; r.w[m][1] = w.y; r.w[m][2] = w.z; r.w[m][3] = w.w;
+            } else if constexpr (IPL == 4) {
+                const uint2 w = *reinterpret_cast<const uint2*>(xr + m * a.s3);
+                r.w[m][0] = w.x; r.w[m][1] = w.y;
+            } else if constexpr (IPL == 2) {
+                r.w[m][0] = *reinterpret_cast<const uint32_t*>(xr + m * a.s3);
+            } else {
+                r.w[m][0] = xr[m * a.s3];
+            }
+        }
+        return r;
+    };
+    auto build_a = [&](const RawA& r) {
+        auto elem = [&](int u) -> uint32_t {         // bf16 bits of coordinate 8q + u
+            const int m = u % TC, il = u / TC;
+            return (r.w[m][il >> 1] >> (16 * (il & 1))) & 0xffffu;
+        };
+        uint32_t d[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) d[w] = (elem(2 * w) | (elem(2 * w + 1) << 16)) & kmask;
+        return __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
+    };
+
+    // indices of the block's tokens for the 8 groups of this octet, written out at the end
+    __shared__ __align__(16) uint8_t idx[kEncTile * kEncTilesPerWg][8];
+    auto tile_fn = [&](int t0, const RawA& raw) {
+        const bf16x8_t Acur = build_a(raw);
+        int rsel = 0;
+        f32x4_t acc[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const f32x4_t ci = {cinit[t], cinit[t], cinit[t], cinit[t]};
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur, bfr[t], ci, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float best = acc[0][i];
+            int bt = 0;
+#pragma unroll
+            for (int t = 1; t < 16; ++t) {
+                const bool gt = acc[t][i] > best;
+                best = gt ? acc[t][i] : best;
+                bt = gt ? t : bt;
+            }
+            int r = 16 * bt + n;
+            // best over the 16 lanes of the row (DPP row rotations); lower index on equal values
+            auto step = [&](auto ctl) {
+                constexpr int C = decltype(ctl)::value;
+                const float ob = __int_as_float(dpp_i<C>(__float_as_int(best)));
+                const int orr = dpp_i<C>(r);
+                const bool take = ob > best || (ob == best && orr < r);
+                best = take ? ob : best;
+                r = take ? orr : r;
+            };
+            step(std::integral_constant<int, 0x128>{});
+            step(std::integral_constant<int, 0x124>{});
+            step(std::integral_constant<int, 0x122>{});
+            step(std::integral_constant<int, 0x121>{});
+            rsel = n == i ? r : rsel;
+        }
+        // row 4q + n (n < 4) of the tile into the workgroup's index block
+        if (n < 4) idx[(t0 - tok_base) + 4 * q + n][grp & 7] = uint8_t(rsel);
+    };
+    // two alternating buffers: the loads of tile k+1 are in flight while tile k computes
+    RawA rawA = load_a(tok_base + n), rawB;
+    const int t_end = min(ntok, tok_base + kEncTile * kEncTilesPerWg);
+    for (int t0 = tok_base; t0 < t_end; t0 += 2 * kEncTile) {
+        rawB = load_a(t0 + kEncTile + n);              // (clamped to the last token at the end)
+        tile_fn(t0, rawA);
+        if (t0 + kEncTile >= t_end) break;
+        rawA = load_a(t0 + 2 * kEncTile + n);
+        tile_fn(t0 + kEncTile, rawB);
+    }
+    __syncthreads();
+    // one thread per token: the octet's 8 index bytes, one 8-byte store (value rows: the octet's bytes sit
+    // in the half row (octet ^ (tau >> 3 & 1)) XOR-permuted by tau & 7)
+    const int j = tok_base + tid;
+    if (tid < kEncTile * kEncTilesPerWg && j < t_end) {
+        const int lp = fp + j / g.page, ri = j % g.page;
+        const long phys = a.pt[long(b) * a.pt_stride + lp];
+        const int tau = lp * g.page + ri;
+        uint8_t* row = a.pool + phys * g.page_bytes + blk_off + ri * g.NG;
+        if (kv == 0) {
+            *reinterpret_cast<uint2*>(row + 8 * oct) = *reinterpret_cast<const uint2*>(idx[tid]);
+        } else {
+            // group 8*oct + u goes to byte (8*oct + u) ^ (tau & 15)
+            const int rot = tau & 15;
+            uint8_t v8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v8[u ^ (rot & 7)] = idx[tid][u];
+            *reinterpret_cast<uint2*>(row + 8 * (oct ^ (rot >> 3))) = *reinterpret_cast<const uint2*>(v8);
+        }
+    }
+}
+
 int grid_for(long total, int threads) {
     long b = (total + threads - 1) / threads;
     if (b > 65536) b = 65536;
@@ -215,6 +415,24 @@ extern "C" lvq_status lvq_encode(const lvq_geom* g, int32_t block, const void* x
     LVQ_REQUIRE(B <= 65535, LVQ_ERR_UNSUPPORTED, "lvq_encode: batch %d above 65535", B);
     if (B == 0 || max_pages == 0) return LVQ_OK;
     LVQ_REQUIRE(max_pages <= 0x7fffffff, LVQ_ERR_UNSUPPORTED, "lvq_encode: too many pages");
+    if (geo.cb == LVQ_BF16 && geo.G <= 32 && geo.NG % 8 == 0) {
+        EncArgs ea{geo, block, static_cast<const uint16_t*>(x_k), static_cast<const uint16_t*>(x_v),
+                   long(x_strides[0]), long(x_strides[1]), long(x_strides[2]), long(x_strides[3]), x_tok0,
+                   static_cast<const uint16_t*>(codebooks), pool, page_table, pt_stride, first_page, n_pages,
+                   geo.NG / 8};
+        // token blocks fastest and a multiple of 8: the octets of one block share an XCD's L2
+        const long tokens = long(max_pages) * geo.page;
+        const long nblk = (tokens + kEncTile * kEncTilesPerWg - 1) / (kEncTile * kEncTilesPerWg);
+        LVQ_REQUIRE(nblk <= 0x7ffffff8L, LVQ_ERR_UNSUPPORTED, "lvq_encode: too many pages");
+        const dim3 grid(unsigned((nblk + 7) / 8 * 8), geo.H * 2 * (geo.NG / 8), B);
+        switch (geo.Tc) {
+            case 1: hipLaunchKernelGGL(encode_mfma_kernel<1>, grid, dim3(512), 0, stream, ea); break;
+            case 2: hipLaunchKernelGGL(encode_mfma_kernel<2>, grid, dim3(512), 0, stream, ea); break;
+            case 4: hipLaunchKernelGGL(encode_mfma_kernel<4>, grid, dim3(512), 0, stream, ea); break;
+            default: hipLaunchKernelGGL(encode_mfma_kernel<8>, grid, dim3(512), 0, stream, ea); break;
+        }
+        return check_launch("lvq_encode");
+    }
     const dim3 grid(max_pages, geo.H * 2, B);
     const dim3 threads(geo.page * geo.NG);
     if (geo.cb == LVQ_BF16)

@@ -141,9 +141,13 @@ LVQ_API lvq_status lvq_rope_table_f16(int32_t len, int32_t D, double base, void*
  * for each request b and each logical page lp in
  * [first_page[b], first_page[b] + n_pages[b]), the 8 tokens of the page are
  * coupled across the block's T_c loop steps and each coupled sub-vector is
- * replaced by the index of its nearest codeword, argmin_r ||z - e_r||^2
- * (ties and distances within rounding resolve to the lowest index), and
+ * replaced by the index of its nearest codeword, argmin_r ||z - e_r||^2, and
  * written to pool page page_table[b*pt_stride + lp] at [block][h][kv].
+ * bf16 codebooks (G <= 32): the distances come from a bf16 matrix-core
+ * contraction with fp32 sums, argmax_r (z . e_r - ||e_r||^2 / 2); equal
+ * values resolve to the lowest index, and a pick can differ from the exact
+ * minimum only by the fp32 rounding of the sums.  fp32 codebooks: an exact
+ * fp64 scan, lowest index on ties.
  * The same call serves prefill (many pages) and decode (the oldest window
  * page, every 8 generated tokens).
  *
