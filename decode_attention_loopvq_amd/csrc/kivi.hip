@@ -191,84 +191,209 @@ __global__ void decode_counters_kernel(KArgs a, int B) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode attention partial: grid (split, H, B), 256 threads (4 waves).  Each
-// wave takes every fourth token of the split; lane l owns channels 2l, 2l+1.
+// Decode attention partial: grid (split, H, B), 256 threads in 32 lane groups
+// of 8; lane c of a group owns channels 16c .. 16c+15 (one dword of 2-bit
+// codes per token).  A split is a multiple of 32 tokens.  Fast path: lane
+// group j takes the j-th whole 32-token key group of the split inside the
+// fully quantized range [0, min(n_kq, n_vq)); it loads the group's key
+// scale/zero once and the codes and value parameters of its 32 tokens at
+// once, scores them (q_d s_d folded into one weight per channel, the zero
+// point into one bias), then adds their values (a lane group with more key
+// groups takes them in turn, rescaling its running softmax):
+//   o_d += p_t s_t (c_td - z_t)  =  sum_t (p_t s_t) c_td - sum_t p_t s_t z_t,
+// the second sum kept once per lane.  Tokens past the quantized range (the
+// fp16 residual, a partial group) take a generic path, one token per lane
+// group at a time.  Each lane group keeps its own softmax state; the 32 are
+// combined through LDS.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) kivi_attn_partial_kernel(KArgs a, const uint16_t* __restrict__ q,
-                                                                float scale_log2, int tps, int S_tot, int max_len,
-                                                                float* __restrict__ po, float* __restrict__ pl) {
+constexpr int kKiviLaneGroups = 32;
+
+template <int CTRL>
+__device__ __forceinline__ float kdpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// sum over the 8 lanes of a lane group (every lane gets it)
+__device__ __forceinline__ float sum8(float x) {
+    x += kdpp<0xb1>(x);      // quad_perm [1,0,3,2]
+    x += kdpp<0x4e>(x);      // quad_perm [2,3,0,1]
+    x += kdpp<0x141>(x);     // row_half_mirror
+    return x;
+}
+// the 16 two-bit codes of a dword as floats, channel j at bits 2j
+__device__ __forceinline__ void codes16(uint32_t w, float (&c)[16]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t x = (w >> (2 * k)) & 0x03030303u;    // bytes: channels k, 4+k, 8+k, 12+k
+        c[k] = float(x & 0xffu);                             // v_cvt_f32_ubyte0 .. 3
+        c[4 + k] = float((x >> 8) & 0xffu);
+        c[8 + k] = float((x >> 16) & 0xffu);
+        c[12 + k] = float(x >> 24);
+    }
+}
+__device__ __forceinline__ void half8(uint4 w, float* out) {
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        out[2 * u] = f16_to_f32(uint16_t(ww[u]));
+        out[2 * u + 1] = f16_to_f32(uint16_t(ww[u] >> 16));
+    }
+}
+
+__global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, const uint16_t* __restrict__ q,
+                                                                   float scale_log2, int tps, int S_tot,
+                                                                   int max_len, float* __restrict__ po,
+                                                                   float* __restrict__ pl) {
+    constexpr int D = 128, NLG = kKiviLaneGroups;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int D = a.D;
+    const int tid = threadIdx.x, c8 = tid & 7, lg = tid >> 3;
     const int L = min(max(a.c.len[b], 0), max_len);
     const int nk = min(a.c.n_kq[b], L), nv = min(a.c.n_vq[b], L);
     const int t_lo = min(L, split * tps), t_hi = min(L, (split + 1) * tps);
-    const long orow = bh(a, b, h) * S_tot + split;
-    const int d0 = 2 * lane;
-    const uint16_t* qp = q + bh(a, b, h) * D;
-    const float q0 = f16_to_f32(qp[d0]), q1 = f16_to_f32(qp[d0 + 1]);
-    const long cb = bh(a, b, h) * a.cap;
-    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int tok = t_lo + wave; tok < t_hi; tok += 4) {
-        float k0, k1, v0, v1;
+    const long row = bh(a, b, h);
+    const int ch0 = 16 * c8, vg = c8 >> 1;          // channels and their value group
+    float qv[16];
+    {
+        const uint4* qp = reinterpret_cast<const uint4*>(q + row * D + ch0);
+        half8(qp[0], qv);
+        half8(qp[1], qv + 8);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qv[j] *= scale_log2;
+    }
+    float m = -INFINITY, l = 0.f, o[16], ob = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[j] = 0.f;
+    const long cb = row * a.cap;
+
+    // ---- fast path: whole key groups inside [0, min(nk, nv)) ----
+    const int q_end = min(nk, nv) & ~31;
+    const int f_hi = min(t_hi, q_end);
+    for (int t0 = t_lo + 32 * lg; t0 + 32 <= f_hi; t0 += 32 * NLG) {
+        uint32_t kc[32], vc[32], vs[32], vz[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const long tok = cb + t0 + k;
+            kc[k] = reinterpret_cast<const uint32_t*>(a.c.k_codes + tok * (D / 4))[c8];
+            vc[k] = reinterpret_cast<const uint32_t*>(a.c.v_codes + tok * (D / 4))[c8];
+            vs[k] = reinterpret_cast<const uint32_t*>(U16(a.c.v_scale) + tok * (D / 32))[vg >> 1];
+            vz[k] = reinterpret_cast<const uint32_t*>(U16(a.c.v_zero) + tok * (D / 32))[vg >> 1];
+        }
+        float w[16], bk = 0.f;
+        {
+            const long pidx = (row * (a.cap / 32) + t0 / 32) * D + ch0;
+            const uint4* sp = reinterpret_cast<const uint4*>(U16(a.c.k_scale) + pidx);
+            const uint4* zp = reinterpret_cast<const uint4*>(U16(a.c.k_zero) + pidx);
+            float s16[16], z16[16];
+            half8(sp[0], s16); half8(sp[1], s16 + 8);
+            half8(zp[0], z16); half8(zp[1], z16 + 8);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                w[j] = qv[j] * s16[j];
+                bk = fmaf(w[j], z16[j], bk);
+            }
+        }
+        float sc[32];
+        float mb = m;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            float c[16];
+            codes16(kc[k], c);
+            float part = -bk;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) part = fmaf(w[j], c[j], part);
+            sc[k] = sum8(part);
+            mb = fmaxf(mb, sc[k]);
+        }
+        // the batch joins the lane group's running softmax
+        {
+            const float alpha = exp2f(m - mb);
+            l *= alpha;
+            ob *= alpha;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[j] *= alpha;
+        }
+        const int hsel = 16 * (vg & 1);              // which half of the dword holds this lane's group
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const float p = exp2f(sc[k] - mb);
+            l += p;
+            const float av = p * f16_to_f32(uint16_t(vs[k] >> hsel));
+            ob = fmaf(av, f16_to_f32(uint16_t(vz[k] >> hsel)), ob);
+            float c[16];
+            codes16(vc[k], c);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[j] = fmaf(av, c[j], o[j]);
+        }
+        m = mb;
+    }
+
+    // ---- generic path: the rest of the split, one token per lane group at a time ----
+    const int g_lo = max(t_lo, f_hi);
+    for (int tok = g_lo + lg; tok < t_hi; tok += NLG) {
+        float kf[16], vf[16];
         if (tok < nk) {
-            const uint32_t byte = a.c.k_codes[(cb + tok) * (D / 4) + d0 / 4];
-            const int sh = 2 * (d0 & 3);
-            const long pidx = (bh(a, b, h) * (a.cap / a.G) + tok / a.G) * D + d0;
-            const float s0 = f16_to_f32(U16(a.c.k_scale)[pidx]), s1 = f16_to_f32(U16(a.c.k_scale)[pidx + 1]);
-            const float z0 = f16_to_f32(U16(a.c.k_zero)[pidx]), z1 = f16_to_f32(U16(a.c.k_zero)[pidx + 1]);
-            k0 = s0 * (float((byte >> sh) & 3) - z0);
-            k1 = s1 * (float((byte >> (sh + 2)) & 3) - z1);
+            float c[16], s16[16], z16[16];
+            codes16(reinterpret_cast<const uint32_t*>(a.c.k_codes + (cb + tok) * (D / 4))[c8], c);
+            const long pidx = (row * (a.cap / 32) + tok / 32) * D + ch0;
+            const uint4* sp = reinterpret_cast<const uint4*>(U16(a.c.k_scale) + pidx);
+            const uint4* zp = reinterpret_cast<const uint4*>(U16(a.c.k_zero) + pidx);
+            half8(sp[0], s16); half8(sp[1], s16 + 8);
+            half8(zp[0], z16); half8(zp[1], z16 + 8);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) kf[j] = s16[j] * (c[j] - z16[j]);
         } else {
-            const uint16_t* r = U16(a.c.k_res) + (bh(a, b, h) * a.ring + tok % a.ring) * D;
-            k0 = f16_to_f32(r[d0]);
-            k1 = f16_to_f32(r[d0 + 1]);
+            const uint4* r = reinterpret_cast<const uint4*>(U16(a.c.k_res) + (row * a.ring + tok % a.ring) * D + ch0);
+            half8(r[0], kf); half8(r[1], kf + 8);
         }
-        const float s = wave_sum(q0 * k0 + q1 * k1) * scale_log2;
         if (tok < nv) {
-            const uint32_t byte = a.c.v_codes[(cb + tok) * (D / 4) + d0 / 4];
-            const int sh = 2 * (d0 & 3);
-            const long pidx = (cb + tok) * (D / a.G) + d0 / a.G;
-            const float sv = f16_to_f32(U16(a.c.v_scale)[pidx]), zv = f16_to_f32(U16(a.c.v_zero)[pidx]);
-            v0 = sv * (float((byte >> sh) & 3) - zv);
-            v1 = sv * (float((byte >> (sh + 2)) & 3) - zv);
+            float c[16];
+            codes16(reinterpret_cast<const uint32_t*>(a.c.v_codes + (cb + tok) * (D / 4))[c8], c);
+            const float s1 = f16_to_f32(U16(a.c.v_scale)[(cb + tok) * (D / 32) + vg]);
+            const float z1 = f16_to_f32(U16(a.c.v_zero)[(cb + tok) * (D / 32) + vg]);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) vf[j] = s1 * (c[j] - z1);
         } else {
-            const uint16_t* r = U16(a.c.v_res) + (bh(a, b, h) * a.ring + tok % a.ring) * D;
-            v0 = f16_to_f32(r[d0]);
-            v1 = f16_to_f32(r[d0 + 1]);
+            const uint4* r = reinterpret_cast<const uint4*>(U16(a.c.v_res) + (row * a.ring + tok % a.ring) * D + ch0);
+            half8(r[0], vf); half8(r[1], vf + 8);
         }
+        float part = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) part = fmaf(qv[j], kf[j], part);
+        const float s = sum8(part);
         const float m_new = fmaxf(m, s);
-        const float alpha = exp2f(m - m_new), w = exp2f(s - m_new);
-        l = l * alpha + w;
-        o0 = o0 * alpha + w * v0;
-        o1 = o1 * alpha + w * v1;
+        const float alpha = exp2f(m - m_new), p = exp2f(s - m_new);
+        l = l * alpha + p;
+        ob *= alpha;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[j] = fmaf(p, vf[j], o[j] * alpha);
         m = m_new;
     }
-    __shared__ float red[4][130];
-    red[wave][d0] = o0;
-    red[wave][d0 + 1] = o1;
-    if (lane == 0) {
-        red[wave][128] = m;
-        red[wave][129] = l;
+
+    // ---- combine the 32 lane groups ----
+    __shared__ float red[NLG][D + 2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) red[lg][ch0 + j] = o[j] - ob;
+    if (c8 == 0) {
+        red[lg][D] = m;
+        red[lg][D + 1] = l;
     }
     __syncthreads();
-    if (tid < D) {
-        float M = -INFINITY;
-        for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, red[w2][128]);
-        if (M == -INFINITY) {
-            po[orow * D + tid] = 0.f;
-            if (tid == 0) pl[orow] = -INFINITY;
-            return;
-        }
-        float Ls = 0.f, o = 0.f;
-        for (int w2 = 0; w2 < 4; ++w2) {
-            const float fw = red[w2][128] == -INFINITY ? 0.f : exp2f(red[w2][128] - M);
-            Ls += red[w2][129] * fw;
-            o += red[w2][tid] * fw;
-        }
-        po[orow * D + tid] = o / Ls;
-        if (tid == 0) pl[orow] = (M + log2f(Ls)) * kLn2;
+    if (tid >= D) return;
+    const long orow = row * S_tot + split;
+    float M = -INFINITY;
+    for (int g2 = 0; g2 < NLG; ++g2) M = fmaxf(M, red[g2][D]);
+    if (M == -INFINITY) {
+        po[orow * D + tid] = 0.f;
+        if (tid == 0) pl[orow] = -INFINITY;
+        return;
     }
+    float Ls = 0.f, ov = 0.f;
+    for (int g2 = 0; g2 < NLG; ++g2) {
+        const float fw = red[g2][D] == -INFINITY ? 0.f : exp2f(red[g2][D] - M);
+        Ls += red[g2][D + 1] * fw;
+        ov += red[g2][tid] * fw;
+    }
+    po[orow * D + tid] = ov / Ls;
+    if (tid == 0) pl[orow] = (M + log2f(Ls)) * kLn2;
 }
 
 __global__ void kivi_merge_kernel(const float* __restrict__ po, const float* __restrict__ pl, int S, int D,
@@ -316,7 +441,7 @@ KArgs make_args(const kivi_geom* g, const kivi_cache* c) {
 int choose_kivi_splits(const kivi_geom* g, int B, int max_len) {
     const int wgs = B * g->H;
     int s = ceil_div(1024, std::max(1, wgs));
-    s = std::max(s, ceil_div(max_len, 2048));
+    s = std::max(s, ceil_div(max_len, 1024));          // at most 1024 tokens (32 key groups) per split
     s = std::min(s, std::max(1, ceil_div(max_len, 64)));
     return std::max(1, std::min(s, 1024));
 }
@@ -394,7 +519,7 @@ extern "C" lvq_status kivi_decode_attn(const kivi_geom* g, const void* q, const 
     const size_t rows = size_t(B) * g->H * S;
     float* po = static_cast<float*>(ws);
     float* pl = po + rows * g->D;
-    const int tps = ceil_div(max_len, S);
+    const int tps = ceil_div(ceil_div(max_len, S), 32) * 32;     // whole key groups per split
     hipLaunchKernelGGL(kivi_attn_partial_kernel, dim3(S, g->H, B), dim3(256), 0, stream, a,
                        static_cast<const uint16_t*>(q), sm_scale * kLog2e, tps, S, max_len, po, pl);
     if ((st = check_launch("kivi_decode_attn: partial")) != LVQ_OK) return st;
