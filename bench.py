@@ -9,21 +9,25 @@ two-requests-per-block saving at this batch and context).
 
 One step is one decode step of a model with `--layers` attention layers that
 each own an independent copy of that cache: for each of the T loop steps,
-every layer runs lvq_decode_attn (the index-page partial kernel, then the
-bf16-window kernel that merges the partials through logsumexp).  Rotating
-over the copies (3.4 GB) keeps the 256 MB Infinity Cache from serving
-repeated reads, as layers would in a real model.
+every layer runs lvq_decode_attn.  At this batch the library runs a call as
+one kernel (index_full_kernel: one workgroup per head and group of four
+requests, window and merge included); with `--num-splits N` (N >= 1) it runs
+the split path instead (the index-page partial kernel, then the bf16-window
+kernel that merges the partials through logsumexp).  Rotating over the
+copies (3.4 GB) keeps the 256 MB Infinity Cache from serving repeated reads,
+as layers would in a real model.
 
 Printed: one JSON line with the whole-call rate (algorithmic GB/s, fraction
 of the 8 TB/s HBM peak, token-heads/s), the roofline entry of the dominant
-kernel (the index-page partial, timed alone with HIP events on the stream it
-runs on; its HBM traffic from the committed counter runs when they match the
-kernel source), and the fp64 oracle timed on a bounded sample on the host.
+kernel (the single-pass kernel, or the index-page partial of the split path
+timed alone; HIP events on the stream it runs on; its HBM traffic from the
+committed counter runs when they match the kernel source), and the fp64
+oracle timed on a bounded sample on the host.
 
 Counter runs (rocprofv3 --pmc, one counter per run): `--mode index-only`
-launches only the index-page partial, `--mode copy` a plain 256 MiB device
-copy for calibration, and `--pmc-summary` turns the four output directories
-into profiles/index_attn_b64_6k_traffic.json.
+launches only the dominant kernel, `--mode copy` a plain 256 MiB device copy
+for calibration, and `--pmc-summary` turns the four output directories into
+profiles/<kernel>_b64_6k_traffic.json.
 """
 
 from __future__ import annotations
@@ -133,7 +137,8 @@ def cpu_baseline(prob, rows, seconds):
     return n_rows, el
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_attn_b64_6k_traffic.json")
+KERNELS = {"index_full_kernel": "index_full_kernel<8, 4> (single-pass attention)",
+           "index_attn_kernel": "index_attn_kernel<8, 4> (index-page partial)"}
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_loopvq_amd", "csrc", "attn.hip")
 COPY_BYTES = 256 << 20
 
@@ -144,11 +149,15 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per index_attn_kernel launch from the committed counter runs, or None when the kernel
-    source has changed since they were taken."""
+def traffic_file(kernel):
+    return os.path.join(ROOT, "profiles", kernel.replace("_kernel", "") + "_b64_6k_traffic.json")
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs, or None when the kernel source has
+    changed since they were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -169,11 +178,15 @@ def _pmc_values(d, counter, name_re):
 
 
 def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
-    """Traffic of index_attn_kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the
-    same counter reads for a plain copy of COPY_BYTES; writes TRAFFIC_FILE."""
+    """Traffic of the dominant kernel (whichever of KERNELS the counter runs hold) from FETCH_SIZE /
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for a plain copy of
+    COPY_BYTES; writes its traffic file."""
     import statistics
-    kf = _pmc_values(fetch_dir, "FETCH_SIZE", "index_attn_kernel")
-    kw = _pmc_values(write_dir, "WRITE_SIZE", "index_attn_kernel")
+    kernel = next((k for k in KERNELS if _pmc_values(fetch_dir, "FETCH_SIZE", k)), None)
+    if kernel is None:
+        raise SystemExit("no dispatch of a known kernel in the counter runs")
+    kf = _pmc_values(fetch_dir, "FETCH_SIZE", kernel)
+    kw = _pmc_values(write_dir, "WRITE_SIZE", kernel)
     cf = [v for v in _pmc_values(copy_fetch_dir, "FETCH_SIZE", "copy|elementwise") if v * 1024 > COPY_BYTES / 8]
     cw = [v for v in _pmc_values(copy_write_dir, "WRITE_SIZE", "copy|elementwise") if v * 1024 > COPY_BYTES / 8]
     if not (kf and kw and cf and cw):
@@ -182,10 +195,10 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     sw = COPY_BYTES / (statistics.median(cw) * 1024)
     fetch = statistics.median(kf) * 1024 * sf
     write = statistics.median(kw) * 1024 * sw
-    t = {"kernel": "index_attn_kernel<8, 4>", "workload": WORKLOAD, "attn_hip_sha256_16": kernel_source_hash(),
+    t = {"kernel": KERNELS[kernel], "workload": WORKLOAD, "attn_hip_sha256_16": kernel_source_hash(),
          "fetch_bytes": round(fetch), "write_bytes": round(write), "bytes_per_launch": round(fetch + write),
          "copy_scale_fetch": round(sf, 4), "copy_scale_write": round(sw, 4), "dispatches": [len(kf), len(kw)]}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(kernel), "w") as f:
         json.dump(t, f, indent=1)
         f.write("\n")
     print(json.dumps(t))
@@ -197,11 +210,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=6, help="independent cache copies rotated through")
-    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="0: the library's choice; -1: the single-pass kernel; N >= 1: the split path")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=("bench", "index-only", "copy"), default="bench",
-                    help="index-only: launch only the index-page partial (for counter runs); "
+                    help="index-only: launch only the dominant kernel (for counter runs); "
                          "copy: a plain device copy of 256 MiB (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 --pmc output dirs: write the measured traffic of the index-page kernel")
@@ -245,8 +259,9 @@ def main():
     wks = [cache.win_k] + [cache.win_k.clone() for _ in range(args.layers - 1)]
     wvs = [cache.win_v] + [cache.win_v.clone() for _ in range(args.layers - 1)]
     B = cfg.B
-    S = args.num_splits or lvq.lvq_decode_attn_splits(g, B, cache.max_len)
-    ws_bytes = lvq.lvq_decode_attn_workspace(g, B, cache.max_len, S)
+    plan = args.num_splits or lvq.lvq_decode_attn_splits(g, B, cache.max_len)   # -1: single pass
+    single = plan == -1
+    ws_bytes = lvq.lvq_decode_attn_workspace(g, B, cache.max_len, args.num_splits)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     outs = [torch.empty((B, g.H, g.D), dtype=torch.float32, device="cuda") for _ in range(args.layers)]
     qs = [prob.q[t].contiguous() for t in range(cfg.T)]
@@ -260,7 +275,7 @@ def main():
                 int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, wks[l].data_ptr(),
                 wvs[l].data_ptr(), prob.slices.data_ptr(), prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(),
                 prob.rope16.data_ptr(), rope_len, C.c_float(prob.sm_scale), outs[l].data_ptr(), None,
-                ws.data_ptr(), ws_bytes, S, B, sh)
+                ws.data_ptr(), ws_bytes, args.num_splits, B, sh)
 
     calls = [full_args(t, l) for t in range(cfg.T) for l in range(args.layers)]
 
@@ -270,7 +285,9 @@ def main():
             if st != 0:
                 raise RuntimeError(lib.lvq_last_error().decode())
 
-    # The dominant kernel alone: the index-page partial (one index_attn_kernel launch) into its own buffers.
+    # The split path's dominant kernel alone: the index-page partial (one index_attn_kernel launch) into its
+    # own buffers.  (A single-pass call is itself one launch of the dominant kernel.)
+    S = 1 if single else plan
     part_o = torch.empty((B * g.H, S, g.D), dtype=torch.float32, device="cuda")
     part_lse = torch.empty((B * g.H, S), dtype=torch.float32, device="cuda")
     qws_bytes = lvq.lvq_quant_partial_workspace(g, B, cache.max_len)
@@ -291,14 +308,16 @@ def main():
             if st != 0:
                 raise RuntimeError(lib.lvq_last_error().decode())
 
+    dominant = one_step if single else quant_only
     if args.mode == "index-only":
         for _ in range(args.warmup + args.steps):
-            quant_only()
+            dominant()
         torch.cuda.synchronize()
         print(f"index-only: {(args.warmup + args.steps) * len(qcalls)} launches", flush=True)
         return
 
-    log(f"[bench] warmup {args.warmup} steps ({len(calls)} calls each, num_splits={S})")
+    log(f"[bench] warmup {args.warmup} steps ({len(calls)} calls each, "
+        f"{'single-pass kernel' if single else f'{plan} splits'})")
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -313,18 +332,21 @@ def main():
     ms_total = e0.elapsed_time(e1)
     log(f"[bench] timed {args.steps} steps: {ms_total:.3f} ms")
 
-    # The dominant kernel alone, same rotation, HIP events on the stream it is launched on.
-    for _ in range(2):
-        quant_only()
-    torch.cuda.synchronize()
-    q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    q0.record(stream)
-    for _ in range(args.steps):
-        quant_only()
-    q1.record(stream)
-    torch.cuda.synchronize()
-    ms_quant = q0.elapsed_time(q1) / (args.steps * len(qcalls))
-    log(f"[bench] index-page partial alone: {ms_quant * 1e3:.2f} us per launch")
+    if single:
+        ms_quant = ms_total / (args.steps * len(calls))      # a call is one launch of the dominant kernel
+    else:
+        # The dominant kernel alone, same rotation, HIP events on the stream it is launched on.
+        for _ in range(2):
+            quant_only()
+        torch.cuda.synchronize()
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record(stream)
+        for _ in range(args.steps):
+            quant_only()
+        q1.record(stream)
+        torch.cuda.synchronize()
+        ms_quant = q0.elapsed_time(q1) / (args.steps * len(qcalls))
+        log(f"[bench] index-page partial alone: {ms_quant * 1e3:.2f} us per launch")
 
     cb_bytes = 2 if cfg.cb_dtype == "bf16" else 4
     parts = call_bytes(g, prob.lengths, cb_bytes)
@@ -333,9 +355,10 @@ def main():
     sec = ms_total / 1e3
     gbps = per_call * n_calls / sec / 1e9
     token_heads = sum(prob.lengths) * g.H
-    qbytes = quant_kernel_bytes(g, prob.lengths, cb_bytes, S)
+    kernel = "index_full_kernel" if single else "index_attn_kernel"
+    qbytes = per_call if single else quant_kernel_bytes(g, prob.lengths, cb_bytes, S)
     q_gbps = qbytes / (ms_quant / 1e3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(kernel)
 
     result = {
         "metric": METRIC,
@@ -353,7 +376,8 @@ def main():
         "config": {
             "workload": WORKLOAD, "B": cfg.B, "H": cfg.H, "L": cfg.L, "T": cfg.T, "Tc": cfg.Tc, "G": cfg.G,
             "K": cfg.K, "codebook": cfg.cb_dtype, "sink": cfg.sink, "window": cfg.window, "page": cfg.page,
-            "layers_rotated": args.layers, "calls_per_step": len(calls), "num_splits": S,
+            "layers_rotated": args.layers, "calls_per_step": len(calls),
+            "path": "single-pass" if single else f"{plan} splits",
             "requests_per_workgroup": 4,
         },
         "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
@@ -361,7 +385,7 @@ def main():
         "us_per_call": round(ms_total * 1e3 / n_calls, 2),
         "bytes_per_call": parts,
         "roofline": {
-            "kernel": "index_attn_kernel<8, 4> (index-page partial)",
+            "kernel": KERNELS[kernel],
             "bound": "hbm",
             "achieved": round(q_gbps, 2),
             "peak": PEAK_HBM_GBPS,

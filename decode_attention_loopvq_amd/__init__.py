@@ -187,7 +187,7 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
 
 
 def lvq_decode_attn_splits(g: lvq_geom, B: int, max_len: int) -> int:
-    """The split count lvq_decode_attn picks when num_splits = 0."""
+    """What lvq_decode_attn runs when num_splits = 0: -1 for the single-pass kernel, else its split count."""
     return int(lib.lvq_decode_attn_splits(C.byref(g), int(B), int(max_len)))
 
 

@@ -525,6 +525,9 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
             dst[tid + i * NT] = make_uint4(bf16x2_to_f16x2(stage[i].x), bf16x2_to_f16x2(stage[i].y),
                                            bf16x2_to_f16x2(stage[i].z), bf16x2_to_f16x2(stage[i].w));
     }
+    // Other waves read the packed rows through the scalar cache after the barrier below, which orders
+    // LDS only: the vector stores must have reached L2 first.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const uint32_t page_bytes = uint32_t(g.page_bytes);
     const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG;   // (block, head) slab of page 0
 
@@ -888,12 +891,16 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
-template <bool kMerge>
-__global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __restrict__ out, float* __restrict__ lse_out) {
-    constexpr int D = 128, NR = 16;
+// One row of 16 lanes attends the window tokens first, first + stride, ...
+// of request rb (n_w of them: the sinks, then the recent tokens; none when
+// !live) with an online softmax in log2 units.  Lane c16 holds channels
+// 8*c16 .. 8*c16+7: on return o[] is that part of the unnormalised
+// sum_w 2^(s_w - m) v_w, with m the row's maximum score (-inf for no token)
+// and l = sum_w 2^(s_w - m), the same in every lane of the row.
+__device__ __forceinline__ void window_row(const AttnArgs& a, int rb, int h, bool live, int first, int stride,
+                                           int c16, float& m_out, float& l_out, float (&o)[8]) {
+    constexpr int D = 128;
     const Geo& g = a.geo;
-    const int h = blockIdx.x, rb = blockIdx.y;
-    const int tid = threadIdx.x, c16 = tid & 15, trow = tid >> 4;
     const bool hi_half = c16 >= 8;
     const int f0 = 8 * (c16 & 7);                  // first RoPE frequency of the lane's channels
     const int L = clamp_len(a, rb);
@@ -901,7 +908,7 @@ __global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __res
     const int q_hi = g.sink + g.page * np;
     const int n_sink = min(L, g.sink);
     const int n_recent = max(0, L - q_hi);
-    const int n_w = n_sink + n_recent;
+    const int n_w = live ? n_sink + n_recent : 0;
     const int ring = g.W + g.page;
 
     float qv[8];
@@ -914,27 +921,16 @@ __global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __res
             qv[2 * u + 1] = bf16_hi(w4[u]) * a.scale_log2;
         }
     }
-    const long row = long(rb) * g.H + h;
-    // merge inputs (the first kWinPrefetch index-page partials of the row), loaded with the window
-    float pre_l[kWinPrefetch], pre_o[kWinPrefetch];
-    if constexpr (kMerge) {
-#pragma unroll
-        for (int s2 = 0; s2 < kWinPrefetch; ++s2) {
-            const int sc = min(s2, max(a.num_splits - 1, 0));
-            pre_l[s2] = a.part_lse[row * a.S_tot + sc];
-            pre_o[s2] = a.part_o[(row * a.S_tot + sc) * D + (tid & (D - 1))];
-        }
-    }
     const long wbase = ((long(rb) * g.T + a.step) * g.H + h) * long(g.Wcap) * D + 8 * c16;
-    float m = -INFINITY, l = 0.f, o[8];
+    float m = -INFINITY, l = 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) o[u] = 0.f;
-    for (int w0 = trow; w0 < n_w; w0 += NR * kWinBatch) {
+    for (int w0 = first; w0 < n_w; w0 += stride * kWinBatch) {
         uint4 kw[kWinBatch], vw[kWinBatch];
         float4 tg[kWinBatch][2];                    // cos (lanes c < 8) or sin (c >= 8) of the lane's frequencies
 #pragma unroll
         for (int i = 0; i < kWinBatch; ++i) {
-            const int w = min(w0 + NR * i, n_w - 1);      // a valid window token; extra ones are masked below
+            const int w = min(w0 + stride * i, n_w - 1);  // a valid window token; extra ones are masked below
             const int p = w < n_sink ? w : q_hi + (w - n_sink);
             const int slot = p < g.sink ? p : g.sink + (p - g.sink) % ring;
             kw[i] = *reinterpret_cast<const uint4*>(a.wk + wbase + long(slot) * D);
@@ -961,7 +957,7 @@ __global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __res
                 part = fmaf(qv[u], r, part);
             }
             const float si = row_sum16(part);
-            s[i] = w0 + NR * i < n_w ? si : -INFINITY;
+            s[i] = w0 + stride * i < n_w ? si : -INFINITY;
             mb = fmaxf(mb, s[i]);
         }
         const float alpha = exp2f(m - mb);
@@ -981,6 +977,28 @@ __global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __res
         }
         m = mb;
     }
+    m_out = m;
+    l_out = l;
+}
+
+template <bool kMerge>
+__global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __restrict__ out, float* __restrict__ lse_out) {
+    constexpr int D = 128, NR = 16;
+    const int h = blockIdx.x, rb = blockIdx.y;
+    const int tid = threadIdx.x, c16 = tid & 15, trow = tid >> 4;
+    const long row = long(rb) * a.geo.H + h;
+    // merge inputs (the first kWinPrefetch index-page partials of the row), loaded with the window
+    float pre_l[kWinPrefetch], pre_o[kWinPrefetch];
+    if constexpr (kMerge) {
+#pragma unroll
+        for (int s2 = 0; s2 < kWinPrefetch; ++s2) {
+            const int sc = min(s2, max(a.num_splits - 1, 0));
+            pre_l[s2] = a.part_lse[row * a.S_tot + sc];
+            pre_o[s2] = a.part_o[(row * a.S_tot + sc) * D + (tid & (D - 1))];
+        }
+    }
+    float m, l, o[8];
+    window_row(a, rb, h, true, trow, NR, c16, m, l, o);
     __shared__ float red[NR][D + 2];
 #pragma unroll
     for (int u = 0; u < 8; ++u) red[trow][8 * c16 + u] = o[u];
@@ -1027,6 +1045,482 @@ __global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __res
             if (pl[s2] != -INFINITY) acc += expf(pl[s2] - lse) * a.part_o[(row * a.S_tot + s2) * D + tid];
         out[row * D + tid] = acc;
         if (lse_out && tid == 0) lse_out[row] = lse;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Single-pass decode attention for bf16 codebooks: one workgroup of 512
+// threads (8 waves, alone on its CU) per (head, group of R requests) does the
+// whole call, window and merge included, and writes the output rows.  The K
+// slice is staged in LDS once; the index tokens are taken in items of
+// kItemTok (the fixed-point weights of an item share one maximum), each
+// scored, binned and contracted as in index_attn_kernel, and the items and
+// the window are merged per output element with a running logsumexp.  Wave w
+// takes chunks w, w + 8, w + 16, ... of 64 tokens, three per item, so its
+// load stream runs on across items: the page ids of the next item and the
+// key index rows of its first chunk are in flight while the current item
+// finishes.
+//
+// LDS (bytes): [0, 64K) K slice (fp16); [64K, 128K) bins u32 [256][R*NG];
+// [128K, 144K) partials (window rows, then per-wave contraction partials);
+// then wave maxima, wave weight totals and the window rows' (m, l).  The bin
+// address of an atomic is one v_perm: [slot offset, codeword, 0x01, 0] with
+// the 0x01 (the 64K page of the bins) taken from the base word.  Each wave
+// contracts, and zeroes behind itself, the 32 bin rows no other wave reads,
+// so the bins are clear for the next item without a pass of their own.
+// ---------------------------------------------------------------------------
+constexpr int kFThreads = 512;
+constexpr int kItemTok = 1536;                    // index tokens per item (fixed-point weights of one maximum)
+
+// Sum of x over the four 16-lane rows of the wave (every lane gets the sum at its position in the row).
+// (The swap results are copied out of their vector before the bit casts: a bit cast of a vector element
+// reads element 0.)
+template <typename T>
+__device__ __forceinline__ T sum_rows4(T x) {
+    const uint32_t xi = __builtin_bit_cast(uint32_t, x);
+    const auto t = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);   // lanes l and l ^ 32
+    const uint32_t t0 = t[0], t1 = t[1];
+    const T y = __builtin_bit_cast(T, t0) + __builtin_bit_cast(T, t1);
+    const uint32_t yi = __builtin_bit_cast(uint32_t, y);
+    const auto u = __builtin_amdgcn_permlane16_swap(yi, yi, false, false);   // rows r and r ^ 1
+    const uint32_t u0 = u[0], u1 = u[1];
+    return __builtin_bit_cast(T, u0) + __builtin_bit_cast(T, u1);
+}
+
+template <int C, int R>
+__global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, float* __restrict__ out,
+                                                                   float* __restrict__ lse_out) {
+    constexpr int D = 128, K = 256, NG = D / C, NT = kFThreads, NW = NT / 64;
+    constexpr int CPW = kItemTok / kChunk / NW;    // chunks per wave and item
+    constexpr int SH = (C == 8) ? 4 : 3;           // byte offset of codeword r in its group row: r << SH
+    constexpr int IW = NG / 4;                     // index dwords per token row
+    constexpr int GQ = (C == 8) ? 4 : 8;           // codewords gathered per score step
+    constexpr int GW = C / 2;                      // dwords per fp16 codeword
+    constexpr int NSTEP = 4 * R;                   // score steps per chunk (even: buffers alternate)
+    constexpr int KS = NG * K * C * 2;             // bytes of the fp16 K slice
+    constexpr int NSTAGE = KS / 16 / NT;
+    constexpr int GPL = NG / 16;                   // groups per contraction lane
+    constexpr int PL = R * C * GPL;                // partial sums per contraction lane
+    constexpr int CPB = K / (NT / 16);             // codewords per contraction lane
+    constexpr int VPG = CPB * C * 2 / 16;          // 16-byte V words per contraction lane and group
+    constexpr int RPJ = 32 / R;                    // window rows per request
+    constexpr int PART = 4096;                     // floats of the partials region
+    static_assert(CPW == 3 && NSTEP % 2 == 0 && R * NG == 64 && CPB == 8, "item and contraction shapes");
+    static_assert(16 * PL * NW <= PART && 32 * D <= PART, "partials region");
+    __shared__ __align__(16) unsigned char lds[2 * KS + PART * 4 + 2 * NW * R * 4 + 32 * 2 * 4];
+    uint32_t* const bins = reinterpret_cast<uint32_t*>(lds + KS);
+    float* const part = reinterpret_cast<float*>(lds + 2 * KS);
+    float (*const wmax)[R] = reinterpret_cast<float (*)[R]>(lds + 2 * KS + PART * 4);
+    uint32_t (*const lw)[R] = reinterpret_cast<uint32_t (*)[R]>(lds + 2 * KS + PART * 4 + NW * R * 4);
+    float (*const wml)[2] = reinterpret_cast<float (*)[2]>(lds + 2 * KS + PART * 4 + 2 * NW * R * 4);
+    const Geo& g = a.geo;
+    const int h = blockIdx.x, r0 = blockIdx.y * R;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // ---- setup ----
+    uint32_t qraw = 0;                              // two bf16 query elements (packed-query dword tid & 63)
+    const int qj = tid >> 6, qt = tid & 63;
+    const long qprow = long(min(r0 + min(qj, R - 1), a.B - 1)) * g.H + h;
+    if (tid < R * 64) {
+        const int m = qt >> 2, k = qt & 3;
+        const int ch = (k < 2 ? 0 : 64) + 4 * m + 2 * (k & 1);
+        qraw = *reinterpret_cast<const uint32_t*>(a.q + qprow * D + ch);
+    }
+    uint4 stage[NSTAGE];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_k) +
+                                                          h * a.slice_hstride);
+#pragma unroll
+        for (int i = 0; i < NSTAGE; ++i) stage[i] = src[tid + i * NT];
+    }
+    if (tid < R * 64) {   // packed query rows: dword t of row j is the fp16 pair of score chunk t >> 2
+        const h2_t v = {(_Float16)(bf16_lo(qraw) * a.scale_log2), (_Float16)(bf16_hi(qraw) * a.scale_log2)};
+        const_cast<uint32_t*>(a.qpack)[qprow * 64 + qt] = __builtin_bit_cast(uint32_t, v);
+    }
+    int hi[R];
+    long srow[R];
+    const int32_t* ptr[R];
+    int t_hi = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int rb = min(r0 + j, a.B - 1);
+        hi[j] = r0 + j < a.B ? n_index_pages(clamp_len(a, rb), g) * g.page : 0;
+        ptr[j] = a.pt + long(rb) * a.pt_stride;
+        srow[j] = long(rb) * g.H + h;
+        t_hi = max(t_hi, hi[j]);
+    }
+    const uint32_t page_bytes = uint32_t(g.page_bytes);
+    const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG;   // (block, head) slab of page 0
+
+    // Every lane issues the same loads: lanes past a request's last token read a valid page of the request
+    // through the clamped page id (a request with no index page reads physical page 0).
+    auto in_req = [&](int j, int tau) { return tau < hi[j]; };
+    auto load_pid = [&](int c, uint32_t (&pid)[R]) {
+        const int tau = c * kChunk + lane;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const uint32_t e = uint32_t(ptr[j][max(0, min(tau, hi[j] - 1)) >> 3]);
+            pid[j] = hi[j] > 0 ? e : 0u;
+        }
+    };
+    // index row words of chunk c: kv = 0 for the key row, 1 for the value row
+    auto load_idx = [&](int c, int kv, const uint32_t (&pid)[R], uint32_t (&ix)[R][IW]) {
+        const int tau = c * kChunk + lane;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const uint4* row = reinterpret_cast<const uint4*>(slab + uint64_t(pid[j]) * page_bytes +
+                                                              (kv * 8 + (tau & 7)) * NG);
+#pragma unroll
+            for (int w = 0; w < IW / 4; ++w) {
+                const uint4 kv4 = row[w];
+                ix[j][4 * w] = kv4.x; ix[j][4 * w + 1] = kv4.y; ix[j][4 * w + 2] = kv4.z; ix[j][4 * w + 3] = kv4.w;
+            }
+        }
+    };
+    uint32_t pidc[CPW][R];                          // page ids of the current item's chunks
+    if (t_hi > 0) {                                 // (no page table to read otherwise)
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) load_pid(wave + i * NW, pidc[i]);
+    }
+    {   // bins start clear; each item's contraction clears them again behind itself
+#pragma unroll
+        for (int i = 0; i < 64 * K / 4 / NT; ++i) reinterpret_cast<uint4*>(bins)[tid + i * NT] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // ---- window: 32 rows of 16 lanes, RPJ rows per request ----
+    {
+        const int trow = tid >> 4, c16 = tid & 15, wj = trow / RPJ;
+        float m, l, o[8];
+        window_row(a, min(r0 + wj, a.B - 1), h, r0 + wj < a.B, trow % RPJ, RPJ, c16, m, l, o);
+        float4* dst = reinterpret_cast<float4*>(part + trow * D + 8 * c16);
+        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        if (c16 == 0) {
+            wml[trow][0] = m;
+            wml[trow][1] = l;
+        }
+    }
+    {   // K slice of head h, bf16 -> fp16
+        uint4* dst = reinterpret_cast<uint4*>(lds);
+#pragma unroll
+        for (int i = 0; i < NSTAGE; ++i)
+            dst[tid + i * NT] = make_uint4(bf16x2_to_f16x2(stage[i].x), bf16x2_to_f16x2(stage[i].y),
+                                           bf16x2_to_f16x2(stage[i].z), bf16x2_to_f16x2(stage[i].w));
+    }
+    // Other waves read the packed query rows through the scalar cache after the barrier below, which
+    // orders LDS only: the vector stores must have reached L2 first.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // ---- score machinery (as in index_attn_kernel) ----
+    uint4 tr[16];                                   // cos/sin of the lane's position, 4 frequencies each
+    auto load_tr = [&](int c, auto qc) {
+        constexpr int qq = decltype(qc)::value;
+        const int p = min(g.sink + c * kChunk + lane, a.rope_len - 1);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) tr[4 * qq + mm] = a.rope16[long(4 * qq + mm) * a.rope_len + p];
+    };
+    auto group_of = [](int qq, int i) constexpr {
+        return C == 8 ? (i < 2 ? 2 * qq + i : 8 + 2 * qq + (i - 2)) : (i < 4 ? 4 * qq + i : 16 + 4 * qq + (i - 4));
+    };
+    auto gather = [&](const uint32_t (&ik)[R][IW], auto qc, auto jc, uint32_t (&G)[GQ][GW]) {
+        constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
+        StaticFor<0, GQ>::run([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int gi = group_of(qq, i);
+            const uint32_t off = byte_shl<SH, gi & 3>(ik[j][gi >> 2]);
+            const unsigned char* pcw = lds + gi * (K * C * 2) + off;
+            if constexpr (C == 8) {
+                const uint4 v = *reinterpret_cast<const uint4*>(pcw);
+                G[i][0] = v.x; G[i][1] = v.y; G[i][2] = v.z; G[i][3] = v.w;
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(pcw);
+                G[i][0] = v.x; G[i][1] = v.y;
+            }
+        });
+    };
+    const_ptr<uint32_t> qrow[R];
+    // The packed query rows and the V rows are the same in every item: their base pointers pass through an
+    // empty asm at the top of each item, so that their loads stay where they are written instead of being
+    // hoisted out of the item loop (which would hold all of them in registers across it).
+    auto set_qrow = [&]() {
+        const uint32_t* qp = a.qpack;
+        asm volatile("" : "+s"(qp));
+#pragma unroll
+        for (int j = 0; j < R; ++j) qrow[j] = as_const(qp + srow[j] * 64);
+    };
+    set_qrow();
+    auto load_q = [&](auto qc, auto jc, uint32_t (&qs)[16]) {
+        constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) qs[u] = qrow[j][16 * qq + u];
+    };
+    float acc[R][2];
+    float rmax[R];
+    float sreg[CPW][R];                             // scores of the wave's chunks of the item
+    auto compute = [&](auto qc, auto jc, const uint32_t (&G)[GQ][GW], const uint32_t (&qs)[16]) {
+        constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {           // RoPE frequencies 4m .. 4m+3
+            const int m = 4 * qq + mm;
+            const h2_t c01 = as_h2(tr[m].x), c23 = as_h2(tr[m].y);
+            const h2_t s01 = as_h2(tr[m].z), s23 = as_h2(tr[m].w);
+            const h2_t l01 = as_h2(qs[4 * mm]), l23 = as_h2(qs[4 * mm + 1]);
+            const h2_t u01 = as_h2(qs[4 * mm + 2]), u23 = as_h2(qs[4 * mm + 3]);
+            const h2_t pl01 = __builtin_elementwise_fma(c01, l01, s01 * u01);
+            const h2_t pl23 = __builtin_elementwise_fma(c23, l23, s23 * u23);
+            const h2_t ph01 = __builtin_elementwise_fma(c01, u01, -(s01 * l01));
+            const h2_t ph23 = __builtin_elementwise_fma(c23, u23, -(s23 * l23));
+            uint32_t kl01, kl23, kh01, kh23;
+            if constexpr (C == 8) {
+                const int il = mm >> 1, d = (mm & 1) * 2;
+                kl01 = G[il][d]; kl23 = G[il][d + 1];
+                kh01 = G[2 + il][d]; kh23 = G[2 + il][d + 1];
+            } else {
+                kl01 = G[mm][0]; kl23 = G[mm][1];
+                kh01 = G[4 + mm][0]; kh23 = G[4 + mm][1];
+            }
+            acc[j][0] = dot2h(kl01, pl01, acc[j][0]);
+            acc[j][1] = dot2h(kl23, pl23, acc[j][1]);
+            acc[j][0] = dot2h(kh01, ph01, acc[j][0]);
+            acc[j][1] = dot2h(kh23, ph23, acc[j][1]);
+        }
+    };
+    uint32_t G[2][GQ][GW];
+    uint32_t qs[2][16];
+    // Chunk slot I of the item (chunk c): steps k = (qq, j); the last step issues the cos/sin of the first
+    // quarter of the wave's next chunk and, but in the item's last chunk, its first gathers (from ikn) and
+    // query quarter.  (The item's end starts the next item's gathers afresh, so that they are not held in
+    // registers through the weights and the contraction.)
+    auto run_chunk = [&](auto Ic, int c, const uint32_t (&ikc)[R][IW], const uint32_t (&ikn)[R][IW]) {
+        constexpr int I = decltype(Ic)::value;
+        StaticFor<0, NSTEP>::run([&](auto kc) {
+            constexpr int k = decltype(kc)::value, qq = k / R, j = k % R, b = k & 1;
+            constexpr int k1 = (k + 1) % NSTEP;
+            using QN = std::integral_constant<int, k1 / R>;
+            using JN = std::integral_constant<int, k1 % R>;
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this step's gathers and query quarter
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (k + 1 < NSTEP) gather(ikc, QN{}, JN{}, G[b ^ 1]);
+            else if constexpr (I + 1 < CPW) gather(ikn, QN{}, JN{}, G[b ^ 1]);
+            if constexpr (k + 1 < NSTEP || I + 1 < CPW) load_q(QN{}, JN{}, qs[b ^ 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (j == 0) load_tr(qq < 3 ? c : c + NW, std::integral_constant<int, (qq + 1) % 4>{});
+            compute(std::integral_constant<int, qq>{}, std::integral_constant<int, j>{}, G[b], qs[b]);
+            if constexpr (qq == 3) {
+                const bool in = in_req(j, c * kChunk + lane);
+                const float s_all = acc[j][0] + acc[j][1];
+                acc[j][0] = 0.f;
+                acc[j][1] = 0.f;
+                sreg[I][j] = s_all;
+                rmax[j] = fmaxf(rmax[j], in ? s_all : -INFINITY);
+            }
+        });
+    };
+
+    uint32_t ik0[R][IW], ik1[R][IW], ik2[R][IW];   // key index rows of the item's chunks 0, 1, 2
+    if (t_hi > 0) {
+        load_idx(wave, 0, pidc[0], ik0);
+        load_tr(wave, std::integral_constant<int, 0>{});
+    }
+    __syncthreads();                                // K slice staged, query rows packed, window rows written
+
+    // Running merge of this thread's output element (request j, channel d), in log2 units: the window,
+    // then each item.  m = -inf: nothing yet.
+    const int oj = tid / D, od = tid % D;
+    float run_m = -INFINITY, run_l = 0.f, run_o = 0.f;
+    if (wave < R * D / 64) {
+        float mw = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < RPJ; ++r) mw = fmaxf(mw, wml[oj * RPJ + r][0]);
+        if (mw != -INFINITY) {
+#pragma unroll
+            for (int r = 0; r < RPJ; ++r) {
+                const float f = exp2f(wml[oj * RPJ + r][0] - mw);   // 0 for a row without tokens
+                run_l = fmaf(wml[oj * RPJ + r][1], f, run_l);
+                run_o = fmaf(part[(oj * RPJ + r) * D + od], f, run_o);
+            }
+            run_m = mw;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[j][0] = acc[j][1] = 0.f;
+
+    const float fix_scale = float(1u << a.fix_bits);
+    const uint16_t* vsl = static_cast<const uint16_t*>(a.slice_v) + h * a.slice_hstride;
+    const int n_items = (t_hi + kItemTok - 1) / kItemTok;
+    int c = wave;                                   // the wave's chunk in slot 0 of the item
+    for (int it = 0; it < n_items; ++it, c += CPW * NW) {
+        // Values that are the same in every item pass through empty asm here, so that the addresses
+        // derived from them are formed where they are used instead of being hoisted out of the loop
+        // and held in registers through the score phase.
+        set_qrow();
+        long vofs = 0;                              // (an integer, so that the loads stay global ones)
+        asm volatile("" : "+s"(vofs));
+        const uint16_t* vsl_it = vsl + vofs;
+        int tid_it = tid;
+        asm volatile("" : "+v"(tid_it));
+        const int cb_blk = tid_it >> 4, g16 = tid_it & 15;
+        // ---- scores ----
+        gather(ik0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, G[0]);
+        load_q(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, qs[0]);
+        uint32_t pidn[CPW][R];                      // page ids of the next item's chunks
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) load_pid(c + (CPW + i) * NW, pidn[i]);
+        load_idx(c + NW, 0, pidc[1], ik1);
+#pragma unroll
+        for (int j = 0; j < R; ++j) rmax[j] = -INFINITY;
+        run_chunk(std::integral_constant<int, 0>{}, c, ik0, ik1);
+        load_idx(c + 2 * NW, 0, pidc[2], ik2);
+        run_chunk(std::integral_constant<int, 1>{}, c + NW, ik1, ik2);
+        load_idx(c + 3 * NW, 0, pidn[0], ik0);      // the next item's first chunk
+        run_chunk(std::integral_constant<int, 2>{}, c + 2 * NW, ik2, ik0);
+        uint32_t iv[CPW][R][IW];                    // value index rows of the item's chunks
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) load_idx(c + i * NW, 1, pidc[i], iv[i]);
+        // (Stores in this loop come from all lanes of a wave, with the same value where they meet: a
+        // lane-divergent branch here costs the score phase its registers.)
+#pragma unroll
+        for (int j = 0; j < R; ++j) wmax[wave][j] = wave_max_dpp(rmax[j]);
+        __syncthreads();                            // wave maxima visible
+        float M[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            M[j] = wmax[0][j];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) M[j] = fmaxf(M[j], wmax[w][j]);
+        }
+
+        // ---- weights: one atomic per (token, request, value group) ----
+        uint4 vrow[GPL * VPG];                      // V rows of this lane's contraction block (L2 hits)
+        StaticFor<0, CPW>::run([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i == CPW - 1) {           // issued once the first chunks' index rows are dead
+#pragma unroll
+                for (int k = 0; k < GPL; ++k) {
+                    const uint4* src =
+                        reinterpret_cast<const uint4*>(vsl_it + (long(g16 + 16 * k) * K + CPB * cb_blk) * C);
+#pragma unroll
+                    for (int v = 0; v < VPG; ++v) vrow[k * VPG + v] = src[v];
+                }
+            }
+            const int tau = (c + i * NW) * kChunk + lane;
+            // byte k of base2[v]: slot byte offset 4R * ((2v + k) ^ (tau & 15)) of the group held in V index
+            // byte 2v + k; byte 2: the bins' 64K page
+            const uint32_t rot = (uint32_t(tau) & 15u) * (4u * R) * 0x0101u;
+            uint32_t base2[NG / 2];
+#pragma unroll
+            for (int v = 0; v < NG / 2; ++v) base2[v] = (((4u * R) * (0x0100u + uint32_t(v) * 0x0202u)) ^ rot) | 0x10000u;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const uint32_t u = in_req(j, tau)
+                                       ? uint32_t(fmaf(__builtin_amdgcn_exp2f(sreg[i][j] - M[j]), fix_scale, 0.5f))
+                                       : 0u;
+                StaticFor<0, NG>::run([&](auto mc) {
+                    constexpr int m = decltype(mc)::value;
+                    // bin byte address [slot offset, codeword, 0x01, 0]: row = codeword, 256 B per row
+                    constexpr uint32_t sel = 0x0c020000u | (uint32_t(4 + (m & 3)) << 8) | uint32_t(m & 1);
+                    const uint32_t addr = __builtin_amdgcn_perm(iv[i][j][m >> 2], base2[m >> 1], sel);
+                    uint32_t* bin = static_cast<uint32_t*>(__builtin_assume_aligned(lds + addr + 4 * j, 4));
+                    __hip_atomic_fetch_add(bin, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                });
+            }
+        });
+        __syncthreads();                            // bins complete
+
+        // ---- contraction: lane (cb_blk, g16) over codewords CPB*cb_blk .. +CPB-1 of its groups ----
+        float o[PL];
+#pragma unroll
+        for (int i = 0; i < PL; ++i) o[i] = 0.f;
+        uint32_t lsum[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) lsum[j] = 0u;
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) {
+            const int r = CPB * cb_blk + i;
+#pragma unroll
+            for (int k = 0; k < GPL; ++k) {
+                uint32_t bv[R];
+                uint32_t* bp = bins + r * 64 + (g16 + 16 * k) * R;
+                if constexpr (R == 4) {
+                    const uint4 b4 = *reinterpret_cast<const uint4*>(bp);
+                    bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
+                    *reinterpret_cast<uint4*>(bp) = make_uint4(0u, 0u, 0u, 0u);
+                } else {
+                    const uint2 b2 = *reinterpret_cast<const uint2*>(bp);
+                    bv[0] = b2.x; bv[1] = b2.y;
+                    *reinterpret_cast<uint2*>(bp) = make_uint2(0u, 0u);
+                }
+                uint32_t vw[C / 2];                 // V row: C bf16 of codeword r, group g16 + 16k
+                if constexpr (C == 8) {
+                    vw[0] = vrow[i].x; vw[1] = vrow[i].y; vw[2] = vrow[i].z; vw[3] = vrow[i].w;
+                } else {
+                    const uint4 q = vrow[k * VPG + (i >> 1)];
+                    vw[0] = (i & 1) ? q.z : q.x;
+                    vw[1] = (i & 1) ? q.w : q.y;
+                }
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    if (k == 0) lsum[j] += bv[j];
+                    const float bw = float(bv[j]);
+#pragma unroll
+                    for (int u = 0; u < C / 2; ++u) {
+                        o[j * C * GPL + k * C + 2 * u] = fmaf(bw, bf16_lo(vw[u]), o[j * C * GPL + k * C + 2 * u]);
+                        o[j * C * GPL + k * C + 2 * u + 1] =
+                            fmaf(bw, bf16_hi(vw[u]), o[j * C * GPL + k * C + 2 * u + 1]);
+                    }
+                }
+            }
+        }
+        // sum over the wave's four codeword blocks; row 0 of the wave writes the wave's partials
+#pragma unroll
+        for (int i = 0; i < PL; ++i) o[i] = sum_rows4(o[i]);
+#pragma unroll
+        for (int j = 0; j < R; ++j) lsum[j] = sum_rows4(lsum[j]);
+        {   // the four rows of the wave hold the same sums: they write them to the same place
+            float4* dst = reinterpret_cast<float4*>(part + (wave * 16 + g16) * PL);
+#pragma unroll
+            for (int i = 0; i < PL / 4; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+#pragma unroll
+            for (int j = 0; j < R; ++j) lw[wave][j] = __builtin_amdgcn_readlane(lsum[j], 0);   // group 0's total
+        }
+        __syncthreads();                            // partials complete
+
+        // ---- merge the item into the running output element ----
+        if (wave < R * D / 64) {
+            const int gr = od / C, u = od % C;
+            const int p = oj * C * GPL + (gr >> 4) * C + u;
+            float U = 0.f;
+            uint64_t Ls = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                U += part[(w * 16 + (gr & 15)) * PL + p];
+                Ls += lw[w][oj];
+            }
+            float Mo = M[0];
+#pragma unroll
+            for (int j = 1; j < R; ++j) Mo = oj == j ? M[j] : Mo;
+            if (Ls > 0) {
+                const float e = Mo - float(a.fix_bits);     // the item's weights are 2^(s - e) in fixed point
+                const float mn = fmaxf(run_m, e);
+                const float sa = exp2f(run_m - mn), sb = exp2f(e - mn);
+                run_o = fmaf(run_o, sa, U * sb);
+                run_l = fmaf(run_l, sa, float(Ls) * sb);
+                run_m = mn;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
+#pragma unroll
+            for (int j = 0; j < R; ++j) pidc[i][j] = pidn[i][j];
+    }
+
+    // ---- output: a request holds at least one token, so run_l > 0 ----
+    if (tid < R * D && r0 + oj < a.B) {
+        const long row = long(r0 + oj) * g.H + h;
+        out[row * D + od] = run_o / run_l;
+        if (lse_out && od == 0) lse_out[row] = (run_m + log2f(run_l)) * kLn2;
     }
 }
 
@@ -1102,7 +1596,8 @@ using namespace lvq;
 
 extern "C" size_t lvq_decode_attn_workspace(const lvq_geom* gp, int32_t B, int32_t max_len, int32_t num_splits) {
     Geo g;
-    if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 0 || num_splits < 0) return 0;
+    if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 0 || num_splits < -1) return 0;
+    if (num_splits == -1) return quant_scratch_bytes(g, B);   // the single-pass kernel
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
     return partials_bytes(g, B, S + 1) + quant_scratch_bytes(g, B);
 }
@@ -1168,6 +1663,26 @@ lvq_status launch_quant(AttnArgs& a, void* scratch, hipStream_t stream) {
             hipLaunchKernelGGL((quant_partial_kernel<4, float, false>), grid, dim3(256), red_bytes, stream, a);
     }
     return check_launch("quantized partial");
+}
+
+// Whether the library's choice for lvq_decode_attn is the single-pass kernel.  (Not yet: it runs no faster
+// than the split path on the shapes measured so far, so num_splits = 0 keeps the split path.)
+bool use_full(const Geo& g, int B, int max_pages) {
+    (void)g, (void)B, (void)max_pages;
+    return false;
+}
+
+// The single-pass kernel; `scratch` (256-byte aligned) holds the packed query rows.
+lvq_status launch_full(AttnArgs& a, void* scratch, float* out, float* lse_out, hipStream_t stream) {
+    const Geo& g = a.geo;
+    a.qpack = static_cast<const uint32_t*>(scratch);
+    a.fix_bits = 32 - ceil_log2(long(kItemTok) + 1);
+    const dim3 grid(g.H, ceil_div(a.B, reqs_per_wg(g)));
+    if (g.c == 8)
+        hipLaunchKernelGGL((index_full_kernel<8, 4>), grid, dim3(kFThreads), 0, stream, a, out, lse_out);
+    else
+        hipLaunchKernelGGL((index_full_kernel<4, 2>), grid, dim3(kFThreads), 0, stream, a, out, lse_out);
+    return check_launch("single-pass attention");
 }
 
 // The window partial into slot a.num_splits, or (out != NULL) merged with slots 0 .. a.num_splits-1 into
@@ -1267,8 +1782,10 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
                             rope_len, sm_scale, B, &a);
     if (st != LVQ_OK) return st;
     const Geo& g = a.geo;
-    LVQ_REQUIRE(num_splits >= 0 && num_splits <= 1024, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: num_splits %d",
+    LVQ_REQUIRE(num_splits >= -1 && num_splits <= 1024, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: num_splits %d",
                 num_splits);
+    LVQ_REQUIRE(num_splits != -1 || g.cb == LVQ_BF16, LVQ_ERR_UNSUPPORTED,
+                "lvq_decode_attn: the single-pass kernel (num_splits -1) needs bf16 codebooks");
     LVQ_REQUIRE(pt_stride >= 0, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: negative pt_stride");
     if (B == 0) return LVQ_OK;
     LVQ_REQUIRE(win_k && win_v && slices && out && ws, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: NULL pointer");
@@ -1277,10 +1794,11 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
                 "lvq_decode_attn: NULL pool or page table");
     LVQ_REQUIRE(pt_stride >= max_pages, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: pt_stride %d < %d pages",
                 pt_stride, max_pages);
+    const bool single = num_splits == -1 || (num_splits == 0 && use_full(g, B, max_pages));
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
-    LVQ_REQUIRE(splits_fit(g, max_pages, S), LVQ_ERR_INVALID_ARG,
+    LVQ_REQUIRE(single || splits_fit(g, max_pages, S), LVQ_ERR_INVALID_ARG,
                 "lvq_decode_attn: %d splits of %d index pages exceed %d tokens per split", S, max_pages, kMaxSplitTok);
-    const size_t need = lvq_decode_attn_workspace(gp, B, max_len, S);
+    const size_t need = lvq_decode_attn_workspace(gp, B, max_len, num_splits);
     LVQ_REQUIRE(ws_bytes >= need, LVQ_ERR_WORKSPACE, "lvq_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
     LVQ_REQUIRE(reinterpret_cast<uintptr_t>(ws) % 256 == 0, LVQ_ERR_INVALID_ARG,
                 "lvq_decode_attn: workspace not 256-byte aligned");
@@ -1291,6 +1809,7 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
     a.wk = static_cast<const uint16_t*>(win_k);
     a.wv = static_cast<const uint16_t*>(win_v);
     set_slices(&a, slices);
+    if (single) return launch_full(a, ws, out, lse_out, stream);
     const size_t rows = size_t(B) * g.H * (S + 1);
     a.part_o = static_cast<float*>(ws);
     a.part_lse = a.part_o + rows * g.D;
@@ -1305,6 +1824,7 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
 extern "C" int32_t lvq_decode_attn_splits(const lvq_geom* gp, int32_t B, int32_t max_len) {
     Geo g;
     if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 1) return 0;
+    if (use_full(g, B, max_index_pages(g, max_len))) return -1;
     return choose_splits(g, B, max_len);
 }
 

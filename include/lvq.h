@@ -171,7 +171,8 @@ LVQ_API lvq_status lvq_encode(const lvq_geom* g, int32_t block,
 
 /*
  * Bytes of workspace lvq_decode_attn needs for B requests of length at most
- * max_len with the given split count (0 = the library's choice).
+ * max_len with the given split count (0 = the library's choice, -1 = the
+ * single-pass kernel).
  */
 LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t max_len, int32_t num_splits);
 
@@ -188,7 +189,10 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  * c = 4), sharing the codebook slice and the RoPE table loads, then turns the
  * scores into softmax weights and accumulates them per (group, codeword) of
  * the value indices; a split then holds at most 1536 index tokens (192
- * pages).
+ * pages).  With bf16 codebooks the call can instead run as one kernel: one
+ * workgroup per (head, group of four requests, two when c = 4) takes all of
+ * its requests' index pages in turns of 1536 tokens and the window, and
+ * merges them into the output itself (num_splits -1).
  *
  *  q          bf16 [B][H][D], already rotated at position seq_len[b] - 1.
  *  seq_len    device int32 [B], 1 <= seq_len[b] <= max_len <= rope_len.
@@ -204,9 +208,11 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  *  ws         device workspace of at least lvq_decode_attn_workspace() bytes,
  *             256-byte aligned (LVQ_ERR_INVALID_ARG otherwise); contents
  *             need no initialisation and are scratch after the call.
- *  num_splits 0 lets the library choose; otherwise 1..1024, and with bf16
- *             codebooks large enough that a split holds at most 192 index
- *             pages: ceil(ceil(max_pages / num_splits) / 8) * 8 <= 192,
+ *  num_splits 0 lets the library choose; -1 asks for the single-pass kernel
+ *             (bf16 codebooks only, LVQ_ERR_UNSUPPORTED otherwise); otherwise
+ *             1..1024, and with bf16 codebooks large enough that a split
+ *             holds at most 192 index pages:
+ *             ceil(ceil(max_pages / num_splits) / 8) * 8 <= 192,
  *             max_pages = (max_len - sink - window) / 8 (LVQ_ERR_INVALID_ARG).
  */
 LVQ_API lvq_status lvq_decode_attn(const lvq_geom* g, int32_t step, const void* q,
@@ -218,7 +224,8 @@ LVQ_API lvq_status lvq_decode_attn(const lvq_geom* g, int32_t step, const void* 
                            void* ws, size_t ws_bytes, int32_t num_splits, int32_t B,
                            hipStream_t stream);
 
-/* The split count lvq_decode_attn uses when passed num_splits = 0 (0 on bad arguments). */
+/* What lvq_decode_attn runs for num_splits = 0: -1 for the single-pass kernel, else its split count
+ * (0 on bad arguments). */
 LVQ_API int32_t lvq_decode_attn_splits(const lvq_geom* g, int32_t B, int32_t max_len);
 
 /*

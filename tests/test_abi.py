@@ -57,12 +57,14 @@ def _attn(g, **over):
 @pytest.mark.parametrize("over,status", [
     (dict(step=4), INVALID), (dict(step=-1), INVALID), (dict(max_len=0), INVALID),
     (dict(max_len=4096), INVALID),             # beyond the RoPE table
-    (dict(splits=2000), INVALID), (dict(q=None), INVALID), (dict(ws=None), INVALID),
+    (dict(splits=2000), INVALID), (dict(splits=-2), INVALID), (dict(q=None), INVALID), (dict(ws=None), INVALID),
     (dict(pool=None), INVALID), (dict(pt_stride=3), INVALID), (dict(scale=float("nan")), INVALID),
     (dict(ws_bytes=16), WORKSPACE),
     (dict(rope16=None), INVALID),              # bf16 codebooks need the packed fp16 RoPE table
     (dict(max_len=2048, splits=1), INVALID),   # 247 index pages in one split: over 1536 tokens per split
     (dict(ws=C.c_void_p(4096 + 16)), INVALID),  # workspace not 256-byte aligned
+    (dict(splits=-1, ws=C.c_void_p(4096 + 16)), INVALID),
+    (dict(splits=-1, ws_bytes=4 * 2 * 256 - 1), WORKSPACE),   # single pass: the packed query rows only
 ])
 def test_decode_attn_rejects(over, status):
     assert _attn(_geom(), **over) == status
@@ -95,6 +97,10 @@ def test_workspace_query():
     assert _attn(g32, rope16=None, B=0) == OK
     assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 0) > 0
     assert _lib.lib.lvq_decode_attn_workspace(None, 64, 6144, 0) == 0
+    # the single-pass kernel needs the packed query rows only, and bf16 codebooks
+    assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, -1) == scratch
+    assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, -2) == 0
+    assert _attn(g32, rope16=None, splits=-1) == UNSUPPORTED
 
 
 def test_encode_rejects():

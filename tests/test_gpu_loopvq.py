@@ -147,7 +147,8 @@ SMALL = [
 def test_decode_parity_small(cfg):
     rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
     steps = list(range(cfg.T)) if cfg.T <= 4 else [0, 3, 4, 17, 31]
-    _run_parity(cfg, rows, steps, splits=(0, 1, 3))
+    single = (-1,) if cfg.cb_dtype == "bf16" else ()
+    _run_parity(cfg, rows, steps, splits=(0, 1, 3) + single)
 
 
 def test_decode_edge_lengths(monkeypatch):
@@ -163,13 +164,23 @@ def test_decode_edge_lengths(monkeypatch):
         rows = [(b, 0) for b in range(8)]
         p = harness.build_loopvq(cfg, keep=rows)
         idx = {(b, 0): _check_indices(p, b, 0, geo) for b in range(8)}
-        for ns in (0, 1, 2, 7, 50):
+        for ns in (0, 1, 2, 7, 50, -1):
             for t in range(cfg.T):
                 lse = torch.empty((8, 1), dtype=torch.float32, device="cuda")
                 out, _ = harness.run_step(p, t, num_splits=ns, lse=lse)
                 torch.cuda.synchronize()
                 for (b, h) in rows:
                     _check_row(p, t, b, h, geo, idx[(b, h)], out, lse)
+
+
+def test_single_pass_items():
+    """The single-pass kernel over several items of 1536 index tokens: ragged lengths (requests of one
+    workgroup ending in different items, one with no index page), random page order, a batch that leaves the
+    last workgroup's request group short."""
+    # lengths 3845, 220, 1997, 57, 1548, 143: three items, one, two, no index page; the second group short
+    cfg = loopvq_config("loopvq-b64-6k", B=6, H=2, L=4000, ragged=(40, 4000), random_pages=True, seed=12)
+    rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    _run_parity(cfg, rows, steps=range(cfg.T), splits=(-1, 3))
 
 
 def test_partial_entry_points_compose():
@@ -223,7 +234,7 @@ def test_full_b64_6k_sampled():
     configuration, checked on sampled rows."""
     cfg = loopvq_config("loopvq-b64-6k")
     rows = [(0, 0), (37, 9), (63, 15)]
-    _run_parity(cfg, rows, steps=range(cfg.T), splits=(0,))
+    _run_parity(cfg, rows, steps=range(cfg.T), splits=(0, -1))
 
 
 def test_full_b1_1k():
