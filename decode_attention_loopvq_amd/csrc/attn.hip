@@ -891,92 +891,108 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
-// One row of 16 lanes attends the window tokens first, first + stride, ...
-// of request rb (n_w of them: the sinks, then the recent tokens; none when
-// !live) with an online softmax in log2 units.  Lane c16 holds channels
-// 8*c16 .. 8*c16+7: on return o[] is that part of the unnormalised
-// sum_w 2^(s_w - m) v_w, with m the row's maximum score (-inf for no token)
-// and l = sum_w 2^(s_w - m), the same in every lane of the row.
-__device__ __forceinline__ void window_row(const AttnArgs& a, int rb, int h, bool live, int first, int stride,
-                                           int c16, float& m_out, float& l_out, float (&o)[8]) {
+// Window tokens of one request as seen by one row of 16 lanes (lane c16 holds
+// channels 8*c16 .. 8*c16+7): the sinks [0, min(L, sink)), then the recent
+// tokens [sink + 8*n_pages, L); n_w of them (none when !live).
+struct WinRow {
+    int n_sink, q_hi, n_w, ring;
+    long wbase;                                    // element offset of the row's (request, step, head) buffer
+    const float* trig;                             // cos (lanes c < 8) or sin (c >= 8) table
+    float qv[8];                                   // the lane's query channels, times sm_scale * log2 e
+};
+
+__device__ __forceinline__ WinRow window_setup(const AttnArgs& a, int rb, int h, bool live, int c16) {
+    constexpr int D = 128;
+    const Geo& g = a.geo;
+    WinRow w;
+    const int L = clamp_len(a, rb);
+    w.q_hi = g.sink + g.page * n_index_pages(L, g);
+    w.n_sink = min(L, g.sink);
+    w.n_w = live ? w.n_sink + max(0, L - w.q_hi) : 0;
+    w.ring = g.W + g.page;
+    w.wbase = ((long(rb) * g.T + a.step) * g.H + h) * long(g.Wcap) * D + 8 * c16;
+    w.trig = (c16 >= 8 ? a.rs : a.rc) + 8 * (c16 & 7);
+    const uint4 qw = *reinterpret_cast<const uint4*>(a.q + (long(rb) * g.H + h) * D + 8 * c16);
+    const uint32_t w4[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        w.qv[2 * u] = bf16_lo(w4[u]) * a.scale_log2;
+        w.qv[2 * u + 1] = bf16_hi(w4[u]) * a.scale_log2;
+    }
+    return w;
+}
+
+// Online softmax step over the window tokens w0, w0 + stride, ... (NB of them, those >= n_w masked; needs
+// n_w >= 1), in log2 units: o[] is the lane's part of the unnormalised sum_w 2^(s_w - m) v_w, with m the
+// row's running maximum (-inf before the first token) and l = sum_w 2^(s_w - m), the same in every lane.
+template <int NB = kWinBatch>
+__device__ __forceinline__ void window_batch(const AttnArgs& a, const WinRow& w, int w0, int stride, int c16,
+                                             float& m, float& l, float (&o)[8]) {
     constexpr int D = 128;
     const Geo& g = a.geo;
     const bool hi_half = c16 >= 8;
-    const int f0 = 8 * (c16 & 7);                  // first RoPE frequency of the lane's channels
-    const int L = clamp_len(a, rb);
-    const int np = n_index_pages(L, g);
-    const int q_hi = g.sink + g.page * np;
-    const int n_sink = min(L, g.sink);
-    const int n_recent = max(0, L - q_hi);
-    const int n_w = live ? n_sink + n_recent : 0;
-    const int ring = g.W + g.page;
-
-    float qv[8];
-    {
-        const uint4 qw = *reinterpret_cast<const uint4*>(a.q + (long(rb) * g.H + h) * D + 8 * c16);
-        const uint32_t w4[4] = {qw.x, qw.y, qw.z, qw.w};
+    uint4 kw[NB], vw[NB];
+    float4 tg[NB][2];                        // cos (lanes c < 8) or sin (c >= 8) of the lane's frequencies
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int t = min(w0 + stride * i, w.n_w - 1);    // a valid window token; extra ones are masked below
+        const int p = t < w.n_sink ? t : w.q_hi + (t - w.n_sink);
+        const int slot = p < g.sink ? p : g.sink + (p - g.sink) % w.ring;
+        kw[i] = *reinterpret_cast<const uint4*>(a.wk + w.wbase + long(slot) * D);
+        vw[i] = *reinterpret_cast<const uint4*>(a.wv + w.wbase + long(slot) * D);
+        const float4* tp = reinterpret_cast<const float4*>(w.trig + long(p) * (D / 2));
+        tg[i][0] = tp[0]; tg[i][1] = tp[1];
+    }
+    float s[NB];
+    float mb = m;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const uint32_t k4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+        const float t8[8] = {tg[i][0].x, tg[i][0].y, tg[i][0].z, tg[i][0].w,
+                             tg[i][1].x, tg[i][1].y, tg[i][1].z, tg[i][1].w};
+        float part = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float k = (u & 1) ? bf16_hi(k4[u >> 1]) : bf16_lo(k4[u >> 1]);
+            const float kp = dpp<0x128>(k);           // the other half of the RoPE pair (lane c ^ 8)
+            const float tp = dpp<0x128>(t8[u]);       // and the other of cos / sin
+            const float c = hi_half ? tp : t8[u], sgn_s = hi_half ? t8[u] : -tp;
+            // lo half: k_i cos - k_{i+64} sin;  hi half: k_{i+64} cos + k_i sin
+            const float r = fmaf(k, c, kp * sgn_s);
+            part = fmaf(w.qv[u], r, part);
+        }
+        const float si = row_sum16(part);
+        s[i] = w0 + stride * i < w.n_w ? si : -INFINITY;
+        mb = fmaxf(mb, s[i]);
+    }
+    const float mref = mb == -INFINITY ? 0.f : mb;  // a row with no token yet and none in this batch adds 0
+    const float alpha = exp2f(m - mref);
+    l *= alpha;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const float wgt = exp2f(s[i] - mref);
+        l += wgt;
+        const uint32_t v4[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            qv[2 * u] = bf16_lo(w4[u]) * a.scale_log2;
-            qv[2 * u + 1] = bf16_hi(w4[u]) * a.scale_log2;
+            o[2 * u] = fmaf(wgt, bf16_lo(v4[u]), o[2 * u]);
+            o[2 * u + 1] = fmaf(wgt, bf16_hi(v4[u]), o[2 * u + 1]);
         }
     }
-    const long wbase = ((long(rb) * g.T + a.step) * g.H + h) * long(g.Wcap) * D + 8 * c16;
+    m = mb;
+}
+
+// One row of 16 lanes attends all window tokens first, first + stride, ... of request rb; on return (m, l,
+// o[]) as left by window_batch (m = -inf, l = 0, o = 0 when the row has no token).
+__device__ __forceinline__ void window_row(const AttnArgs& a, int rb, int h, bool live, int first, int stride,
+                                           int c16, float& m_out, float& l_out, float (&o)[8]) {
+    const WinRow w = window_setup(a, rb, h, live, c16);
     float m = -INFINITY, l = 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) o[u] = 0.f;
-    for (int w0 = first; w0 < n_w; w0 += stride * kWinBatch) {
-        uint4 kw[kWinBatch], vw[kWinBatch];
-        float4 tg[kWinBatch][2];                    // cos (lanes c < 8) or sin (c >= 8) of the lane's frequencies
-#pragma unroll
-        for (int i = 0; i < kWinBatch; ++i) {
-            const int w = min(w0 + stride * i, n_w - 1);  // a valid window token; extra ones are masked below
-            const int p = w < n_sink ? w : q_hi + (w - n_sink);
-            const int slot = p < g.sink ? p : g.sink + (p - g.sink) % ring;
-            kw[i] = *reinterpret_cast<const uint4*>(a.wk + wbase + long(slot) * D);
-            vw[i] = *reinterpret_cast<const uint4*>(a.wv + wbase + long(slot) * D);
-            const float4* tp = reinterpret_cast<const float4*>((hi_half ? a.rs : a.rc) + long(p) * (D / 2) + f0);
-            tg[i][0] = tp[0]; tg[i][1] = tp[1];
-        }
-        float s[kWinBatch];
-        float mb = m;
-#pragma unroll
-        for (int i = 0; i < kWinBatch; ++i) {
-            const uint32_t k4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
-            const float t8[8] = {tg[i][0].x, tg[i][0].y, tg[i][0].z, tg[i][0].w,
-                                 tg[i][1].x, tg[i][1].y, tg[i][1].z, tg[i][1].w};
-            float part = 0.f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float k = (u & 1) ? bf16_hi(k4[u >> 1]) : bf16_lo(k4[u >> 1]);
-                const float kp = dpp<0x128>(k);           // the other half of the RoPE pair (lane c ^ 8)
-                const float tp = dpp<0x128>(t8[u]);       // and the other of cos / sin
-                const float c = hi_half ? tp : t8[u], sgn_s = hi_half ? t8[u] : -tp;
-                // lo half: k_i cos - k_{i+64} sin;  hi half: k_{i+64} cos + k_i sin
-                const float r = fmaf(k, c, kp * sgn_s);
-                part = fmaf(qv[u], r, part);
-            }
-            const float si = row_sum16(part);
-            s[i] = w0 + stride * i < n_w ? si : -INFINITY;
-            mb = fmaxf(mb, s[i]);
-        }
-        const float alpha = exp2f(m - mb);
-        l *= alpha;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o[u] *= alpha;
-#pragma unroll
-        for (int i = 0; i < kWinBatch; ++i) {
-            const float wgt = exp2f(s[i] - mb);
-            l += wgt;
-            const uint32_t v4[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                o[2 * u] = fmaf(wgt, bf16_lo(v4[u]), o[2 * u]);
-                o[2 * u + 1] = fmaf(wgt, bf16_hi(v4[u]), o[2 * u + 1]);
-            }
-        }
-        m = mb;
-    }
+    for (int w0 = first; w0 < w.n_w; w0 += stride * kWinBatch) window_batch(a, w, w0, stride, c16, m, l, o);
     m_out = m;
     l_out = l;
 }
@@ -1091,7 +1107,9 @@ template <int C, int R>
 __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, float* __restrict__ out,
                                                                    float* __restrict__ lse_out) {
     constexpr int D = 128, K = 256, NG = D / C, NT = kFThreads, NW = NT / 64;
-    constexpr int CPW = kItemTok / kChunk / NW;    // chunks per wave and item
+    constexpr int CPI = kItemTok / kChunk;         // chunks per item
+    constexpr int NFAST = NW / 2;                  // the first waves of the workgroup
+    constexpr int FCH = 3, SCH = 3;                // chunks per item of the first waves, of the others
     constexpr int SH = (C == 8) ? 4 : 3;           // byte offset of codeword r in its group row: r << SH
     constexpr int IW = NG / 4;                     // index dwords per token row
     constexpr int GQ = (C == 8) ? 4 : 8;           // codewords gathered per score step
@@ -1103,16 +1121,19 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
     constexpr int PL = R * C * GPL;                // partial sums per contraction lane
     constexpr int CPB = K / (NT / 16);             // codewords per contraction lane
     constexpr int VPG = CPB * C * 2 / 16;          // 16-byte V words per contraction lane and group
-    constexpr int RPJ = 32 / R;                    // window rows per request
+    constexpr int NWW = NFAST;                     // waves that attend the window: the first ones
+    constexpr int RPJ = NWW * 4 / R;               // window rows (of 16 lanes) per request
     constexpr int PART = 4096;                     // floats of the partials region
-    static_assert(CPW == 3 && NSTEP % 2 == 0 && R * NG == 64 && CPB == 8, "item and contraction shapes");
-    static_assert(16 * PL * NW <= PART && 32 * D <= PART, "partials region");
+    static_assert(NFAST * FCH + (NW - NFAST) * SCH == CPI && NSTEP % 2 == 0 && R * NG == 64 && CPB == 8,
+                  "item and contraction shapes");
+    static_assert(16 * PL * NW <= PART && NWW * 4 * D <= PART, "partials region");
+    static_assert(RPJ % 4 == 0, "a wave's window rows belong to one request");
     __shared__ __align__(16) unsigned char lds[2 * KS + PART * 4 + 2 * NW * R * 4 + 32 * 2 * 4];
     uint32_t* const bins = reinterpret_cast<uint32_t*>(lds + KS);
     float* const part = reinterpret_cast<float*>(lds + 2 * KS);
     float (*const wmax)[R] = reinterpret_cast<float (*)[R]>(lds + 2 * KS + PART * 4);
     uint32_t (*const lw)[R] = reinterpret_cast<uint32_t (*)[R]>(lds + 2 * KS + PART * 4 + NW * R * 4);
-    float (*const wml)[2] = reinterpret_cast<float (*)[2]>(lds + 2 * KS + PART * 4 + 2 * NW * R * 4);
+    float (*const wml)[2] = reinterpret_cast<float (*)[2]>(lds + 2 * KS + PART * 4 + 2 * NW * R * 4);   // [16]
     const Geo& g = a.geo;
     const int h = blockIdx.x, r0 = blockIdx.y * R;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1178,29 +1199,22 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
             }
         }
     };
-    uint32_t pidc[CPW][R];                          // page ids of the current item's chunks
+    // Chunks of an item (CPI of them): waves w < NFAST take w + 4i (i < FCH), the others
+    // 4 FCH + (w - NFAST) + 4i (i < SCH); a SIMD holds wave w and wave w + NFAST.
+    const bool fast = wave < NFAST;
+    const int cbase = fast ? wave : 4 * FCH + wave - NFAST;   // chunk of slot 0 in item 0
+    constexpr int MCH = FCH > SCH ? FCH : SCH;
+    uint32_t pidc[MCH][R];                          // page ids of the current item's chunks (slots)
     if (t_hi > 0) {                                 // (no page table to read otherwise)
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) load_pid(wave + i * NW, pidc[i]);
+        for (int i = 0; i < MCH; ++i)
+            if (i < (fast ? FCH : SCH)) load_pid(cbase + 4 * i, pidc[i]);
     }
     {   // bins start clear; each item's contraction clears them again behind itself
 #pragma unroll
         for (int i = 0; i < 64 * K / 4 / NT; ++i) reinterpret_cast<uint4*>(bins)[tid + i * NT] = make_uint4(0u, 0u, 0u, 0u);
     }
 
-    // ---- window: 32 rows of 16 lanes, RPJ rows per request ----
-    {
-        const int trow = tid >> 4, c16 = tid & 15, wj = trow / RPJ;
-        float m, l, o[8];
-        window_row(a, min(r0 + wj, a.B - 1), h, r0 + wj < a.B, trow % RPJ, RPJ, c16, m, l, o);
-        float4* dst = reinterpret_cast<float4*>(part + trow * D + 8 * c16);
-        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-        if (c16 == 0) {
-            wml[trow][0] = m;
-            wml[trow][1] = l;
-        }
-    }
     {   // K slice of head h, bf16 -> fp16
         uint4* dst = reinterpret_cast<uint4*>(lds);
 #pragma unroll
@@ -1257,7 +1271,7 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
     };
     float acc[R][2];
     float rmax[R];
-    float sreg[CPW][R];                             // scores of the wave's chunks of the item
+    float sreg[MCH][R];                             // scores of the wave's chunks of the item
     auto compute = [&](auto qc, auto jc, const uint32_t (&G)[GQ][GW], const uint32_t (&qs)[16]) {
         constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
 #pragma unroll
@@ -1288,12 +1302,13 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
     };
     uint32_t G[2][GQ][GW];
     uint32_t qs[2][16];
-    // Chunk slot I of the item (chunk c): steps k = (qq, j); the last step issues the cos/sin of the first
-    // quarter of the wave's next chunk and, but in the item's last chunk, its first gathers (from ikn) and
-    // query quarter.  (The item's end starts the next item's gathers afresh, so that they are not held in
-    // registers through the weights and the contraction.)
-    auto run_chunk = [&](auto Ic, int c, const uint32_t (&ikc)[R][IW], const uint32_t (&ikn)[R][IW]) {
-        constexpr int I = decltype(Ic)::value;
+    // Chunk slot I of N in the item (chunk c): steps k = (qq, j); the last step issues the cos/sin of the
+    // first quarter of the wave's next chunk cn and, but in the item's last slot, its first gathers (from
+    // ikn) and query quarter.  (The item's end starts the next item's gathers afresh, so that they are not
+    // held in registers through the weights and the contraction.)
+    auto run_chunk = [&](auto Ic, auto Nc, int c, int cn, const uint32_t (&ikc)[R][IW],
+                         const uint32_t (&ikn)[R][IW]) {
+        constexpr int I = decltype(Ic)::value, N = decltype(Nc)::value;
         StaticFor<0, NSTEP>::run([&](auto kc) {
             constexpr int k = decltype(kc)::value, qq = k / R, j = k % R, b = k & 1;
             constexpr int k1 = (k + 1) % NSTEP;
@@ -1303,10 +1318,10 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
             __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this step's gathers and query quarter
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (k + 1 < NSTEP) gather(ikc, QN{}, JN{}, G[b ^ 1]);
-            else if constexpr (I + 1 < CPW) gather(ikn, QN{}, JN{}, G[b ^ 1]);
-            if constexpr (k + 1 < NSTEP || I + 1 < CPW) load_q(QN{}, JN{}, qs[b ^ 1]);
+            else if constexpr (I + 1 < N) gather(ikn, QN{}, JN{}, G[b ^ 1]);
+            if constexpr (k + 1 < NSTEP || I + 1 < N) load_q(QN{}, JN{}, qs[b ^ 1]);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (j == 0) load_tr(qq < 3 ? c : c + NW, std::integral_constant<int, (qq + 1) % 4>{});
+            if constexpr (j == 0) load_tr(qq < 3 ? c : cn, std::integral_constant<int, (qq + 1) % 4>{});
             compute(std::integral_constant<int, qq>{}, std::integral_constant<int, j>{}, G[b], qs[b]);
             if constexpr (qq == 3) {
                 const bool in = in_req(j, c * kChunk + lane);
@@ -1319,39 +1334,41 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
         });
     };
 
-    uint32_t ik0[R][IW], ik1[R][IW], ik2[R][IW];   // key index rows of the item's chunks 0, 1, 2
+    uint32_t ik[3][R][IW];                          // key index rows of slot I in ik[I % (N even ? 2 : 3)]
     if (t_hi > 0) {
-        load_idx(wave, 0, pidc[0], ik0);
-        load_tr(wave, std::integral_constant<int, 0>{});
+        load_idx(cbase, 0, pidc[0], ik[0]);
+        load_tr(cbase, std::integral_constant<int, 0>{});
     }
-    __syncthreads();                                // K slice staged, query rows packed, window rows written
+    __syncthreads();                                // K slice staged, query rows packed
 
-    // Running merge of this thread's output element (request j, channel d), in log2 units: the window,
-    // then each item.  m = -inf: nothing yet.
+    // ---- window: the first NWW waves attend it while the others start on the first item (the first waves
+    // of a workgroup get the issue slots first when both of a SIMD's waves are ready, and run their score
+    // loop about twice as fast).  Window row wr = tid >> 4 of 16 lanes takes tokens of request wj spaced
+    // RPJ apart; every row of a wave serves the same request.  The rows' results wait in registers until
+    // after the last item.
+    const int c16 = tid & 15, wr = tid >> 4;
+    float wm = -INFINITY, wl = 0.f, wo[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) wo[u] = 0.f;
+    if (wave < NWW) {
+        const int wj = wave * 4 / RPJ;
+        window_row(a, min(r0 + wj, a.B - 1), h, r0 + wj < a.B, wr % RPJ, RPJ, c16, wm, wl, wo);
+    }
+
+    // Running merge of this thread's output element (request j, channel d), in log2 units: each item, then
+    // the window.  m = -inf: nothing yet.
     const int oj = tid / D, od = tid % D;
     float run_m = -INFINITY, run_l = 0.f, run_o = 0.f;
-    if (wave < R * D / 64) {
-        float mw = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < RPJ; ++r) mw = fmaxf(mw, wml[oj * RPJ + r][0]);
-        if (mw != -INFINITY) {
-#pragma unroll
-            for (int r = 0; r < RPJ; ++r) {
-                const float f = exp2f(wml[oj * RPJ + r][0] - mw);   // 0 for a row without tokens
-                run_l = fmaf(wml[oj * RPJ + r][1], f, run_l);
-                run_o = fmaf(part[(oj * RPJ + r) * D + od], f, run_o);
-            }
-            run_m = mw;
-        }
-    }
 #pragma unroll
     for (int j = 0; j < R; ++j) acc[j][0] = acc[j][1] = 0.f;
 
     const float fix_scale = float(1u << a.fix_bits);
     const uint16_t* vsl = static_cast<const uint16_t*>(a.slice_v) + h * a.slice_hstride;
     const int n_items = (t_hi + kItemTok - 1) / kItemTok;
-    int c = wave;                                   // the wave's chunk in slot 0 of the item
-    for (int it = 0; it < n_items; ++it, c += CPW * NW) {
+    auto item_loop = [&](auto Nc) {
+      constexpr int N = decltype(Nc)::value;        // chunk slots of this wave
+      int c = cbase;                                // the wave's chunk in slot 0 of the item
+      for (int it = 0; it < n_items; ++it, c += CPI) {
         // Values that are the same in every item pass through empty asm here, so that the addresses
         // derived from them are formed where they are used instead of being hoisted out of the loop
         // and held in registers through the score phase.
@@ -1363,22 +1380,24 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
         asm volatile("" : "+v"(tid_it));
         const int cb_blk = tid_it >> 4, g16 = tid_it & 15;
         // ---- scores ----
-        gather(ik0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, G[0]);
+        gather(ik[0], std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, G[0]);
         load_q(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, qs[0]);
-        uint32_t pidn[CPW][R];                      // page ids of the next item's chunks
+        uint32_t pidn[N][R];                        // page ids of the next item's chunks
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) load_pid(c + (CPW + i) * NW, pidn[i]);
-        load_idx(c + NW, 0, pidc[1], ik1);
+        for (int i = 0; i < N; ++i) load_pid(c + CPI + 4 * i, pidn[i]);
 #pragma unroll
         for (int j = 0; j < R; ++j) rmax[j] = -INFINITY;
-        run_chunk(std::integral_constant<int, 0>{}, c, ik0, ik1);
-        load_idx(c + 2 * NW, 0, pidc[2], ik2);
-        run_chunk(std::integral_constant<int, 1>{}, c + NW, ik1, ik2);
-        load_idx(c + 3 * NW, 0, pidn[0], ik0);      // the next item's first chunk
-        run_chunk(std::integral_constant<int, 2>{}, c + 2 * NW, ik2, ik0);
-        uint32_t iv[CPW][R][IW];                    // value index rows of the item's chunks
+        StaticFor<0, N>::run([&](auto Ic) {
+            constexpr int I = decltype(Ic)::value, NB = N % 2 == 0 ? 2 : 3;
+            auto& cur = ik[I % NB];
+            auto& nxt = ik[(I + 1) % NB];           // (after the last slot: ik[0], the next item's first)
+            if constexpr (I + 1 < N) load_idx(c + 4 * (I + 1), 0, pidc[I + 1], nxt);
+            else load_idx(c + CPI, 0, pidn[0], nxt);
+            run_chunk(Ic, Nc, c + 4 * I, I + 1 < N ? c + 4 * (I + 1) : c + CPI, cur, nxt);
+        });
+        uint32_t iv[N][R][IW];                      // value index rows of the item's chunks
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) load_idx(c + i * NW, 1, pidc[i], iv[i]);
+        for (int i = 0; i < N; ++i) load_idx(c + 4 * i, 1, pidc[i], iv[i]);
         // (Stores in this loop come from all lanes of a wave, with the same value where they meet: a
         // lane-divergent branch here costs the score phase its registers.)
 #pragma unroll
@@ -1394,9 +1413,9 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
 
         // ---- weights: one atomic per (token, request, value group) ----
         uint4 vrow[GPL * VPG];                      // V rows of this lane's contraction block (L2 hits)
-        StaticFor<0, CPW>::run([&](auto ic) {
+        StaticFor<0, N>::run([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            if constexpr (i == CPW - 1) {           // issued once the first chunks' index rows are dead
+            if constexpr (i == N - 1) {             // issued once the first chunks' index rows are dead
 #pragma unroll
                 for (int k = 0; k < GPL; ++k) {
                     const uint4* src =
@@ -1405,7 +1424,7 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
                     for (int v = 0; v < VPG; ++v) vrow[k * VPG + v] = src[v];
                 }
             }
-            const int tau = (c + i * NW) * kChunk + lane;
+            const int tau = (c + 4 * i) * kChunk + lane;
             // byte k of base2[v]: slot byte offset 4R * ((2v + k) ^ (tau & 15)) of the group held in V index
             // byte 2v + k; byte 2: the bins' 64K page
             const uint32_t rot = (uint32_t(tau) & 15u) * (4u * R) * 0x0101u;
@@ -1511,9 +1530,43 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
             }
         }
 #pragma unroll
-        for (int i = 0; i < CPW; ++i)
+        for (int i = 0; i < N; ++i)
 #pragma unroll
             for (int j = 0; j < R; ++j) pidc[i][j] = pidn[i][j];
+      }
+    };
+    if constexpr (FCH == SCH) item_loop(std::integral_constant<int, FCH>{});
+    else if (fast) item_loop(std::integral_constant<int, FCH>{});
+    else item_loop(std::integral_constant<int, SCH>{});
+
+    // ---- the window rows, merged like an item ----
+    __syncthreads();                                // the last item's partials are read
+    if (wave < NWW) {
+        float4* dst = reinterpret_cast<float4*>(part + wr * D + 8 * c16);
+        dst[0] = make_float4(wo[0], wo[1], wo[2], wo[3]);
+        dst[1] = make_float4(wo[4], wo[5], wo[6], wo[7]);
+        wml[wr][0] = wm;                            // (the row's 16 lanes hold the same m and l)
+        wml[wr][1] = wl;
+    }
+    __syncthreads();
+    if (wave < R * D / 64) {
+        float mw = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < RPJ; ++r) mw = fmaxf(mw, wml[oj * RPJ + r][0]);
+        if (mw != -INFINITY) {
+            float lw_ = 0.f, ow = 0.f;
+#pragma unroll
+            for (int r = 0; r < RPJ; ++r) {
+                const float f = exp2f(wml[oj * RPJ + r][0] - mw);   // 0 for a row without tokens
+                lw_ = fmaf(wml[oj * RPJ + r][1], f, lw_);
+                ow = fmaf(part[(oj * RPJ + r) * D + od], f, ow);
+            }
+            const float mn = fmaxf(run_m, mw);
+            const float sa = exp2f(run_m - mn), sb = exp2f(mw - mn);
+            run_o = fmaf(run_o, sa, ow * sb);
+            run_l = fmaf(run_l, sa, lw_ * sb);
+            run_m = mn;
+        }
     }
 
     // ---- output: a request holds at least one token, so run_l > 0 ----
