@@ -47,6 +47,20 @@ __device__ __forceinline__ uint32_t code_of(float x, float s, float z) {
     return uint32_t(u);
 }
 
+// The same code with the quotient fl32(x / s) from r = v_rcp_f32(s) and one Newton step on the quotient
+// (Markstein): q0 = x r, e = x - q0 s (exact in one FMA), q = q0 + e r rounded once.  For fp16 x and s
+// this is the correctly rounded quotient: x / s = M / N 2^k with N < 2^11, so unless it is exact it lies
+// at least 2^-12 ulp from every rounding midpoint, while q0 + e r is within 2^-20 ulp of x / s
+// (|e| <= 2 ulp(q0) s and |r - 1/s| <= 1 ulp(1/s)).
+__device__ __forceinline__ uint32_t code_of_r(float x, float s, float r, float z) {
+    const float q0 = x * r;
+    const float e = fmaf(-q0, s, x);
+    float u = __fadd_rn(fmaf(e, r, q0), z);
+    u = rintf(u);
+    u = fminf(fmaxf(u, 0.f), 3.f);
+    return uint32_t(u);
+}
+
 __device__ __forceinline__ long bh(const KArgs& a, int b, int h) { return long(b) * a.H + h; }
 
 // Key groups: one thread per (group of 32 tokens, 4 channels).  Tokens come
@@ -142,6 +156,145 @@ __global__ void prefill_counters_kernel(KArgs a, int B, int L, int n_kq, int n_v
     a.c.len[b] = L;
     a.c.n_kq[b] = n_kq;
     a.c.n_vq[b] = n_vq;
+}
+
+// ---------------------------------------------------------------------------
+// Prefill in one pass (D = 128, group 32, 16-byte aligned rows): grid
+// (ceil(L / 128), H, B), 256 threads.  Wave w takes tokens t0 .. t0+31,
+// t0 = 128 bx + 32 w (one key group); lane l holds channels 8(l & 15) .. +7
+// of tokens t0 + 8(l >> 4) .. +7, K and V each loaded once (16 bytes per lane
+// and token, V after K is done).  Keys of a whole quantized group: per-channel minimum and
+// maximum over the lane's 8 tokens, then over the 4 lanes l ^ 16k (permlane
+// swaps).  Values of quantized tokens: per-token minimum and maximum over the
+// lane's 8 channels, then over the 4 lanes of the 32-channel group (DPP).
+// Codes go out 2 bytes per lane and token; the rows past the quantized
+// ranges go to the fp16 rings; block (0, 0, b) sets request b's counters.
+// ---------------------------------------------------------------------------
+template <typename F>
+__device__ __forceinline__ float rows4_reduce(float x, F op) {   // over lanes l, l ^ 16, l ^ 32, l ^ 48
+    const uint32_t xi = __float_as_uint(x);
+    const auto t = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    const uint32_t t0 = t[0], t1 = t[1];
+    const float y = op(__uint_as_float(t0), __uint_as_float(t1));
+    const uint32_t yi = __float_as_uint(y);
+    const auto u = __builtin_amdgcn_permlane16_swap(yi, yi, false, false);
+    const uint32_t u0 = u[0], u1 = u[1];
+    return op(__uint_as_float(u0), __uint_as_float(u1));
+}
+template <int CTRL>
+__device__ __forceinline__ float kdpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// the 8 fp16 of a 16-byte word as floats
+__device__ __forceinline__ void half8_f(const uint4& w, float (&f)[8]) {
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        f[2 * u] = f16_to_f32(uint16_t(d[u] & 0xffffu));
+        f[2 * u + 1] = f16_to_f32(uint16_t(d[u] >> 16));
+    }
+}
+
+__global__ void __launch_bounds__(256, 4) prefill_kv_kernel(KArgs a, NewSrc k, NewSrc v, int L, int n_kq, int n_vq) {
+    constexpr int D = 128, G = 32;
+    const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, lane = tid & 63;
+    const int t0 = blockIdx.x * 128 + (tid >> 6) * 32;
+    const int co = lane & 15, tq = lane >> 4;
+    const long bhi = bh(a, b, h);
+    if (blockIdx.x == 0 && h == 0 && tid == 0) {
+        a.c.len[b] = L;
+        a.c.n_kq[b] = n_kq;
+        a.c.n_vq[b] = n_vq;
+    }
+    if (t0 >= L) return;                            // (whole wave)
+    uint4 kx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = min(t0 + 8 * tq + i, L - 1);  // rows past L load a valid row and are not stored
+        kx[i] = *reinterpret_cast<const uint4*>(k.row(b, h, t) + 8 * co);
+    }
+    // ---- keys: one group of 32 tokens per wave ----
+    if (t0 + G <= n_kq) {
+        float mn[8], mx[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { mn[u] = INFINITY; mx[u] = -INFINITY; }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float f[8];
+            half8_f(kx[i], f);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) { mn[u] = fminf(mn[u], f[u]); mx[u] = fmaxf(mx[u], f[u]); }
+        }
+        GroupParams gp[8];
+        float rs[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            mn[u] = rows4_reduce(mn[u], [](float p, float q) { return fminf(p, q); });
+            mx[u] = rows4_reduce(mx[u], [](float p, float q) { return fmaxf(p, q); });
+            gp[u] = group_params(mn[u], mx[u]);
+            rs[u] = __builtin_amdgcn_rcpf(gp[u].s);
+        }
+        if (tq == 0) {
+            const long pofs = (bhi * (a.cap / G) + t0 / G) * D + 8 * co;
+            uint32_t sw[4], zw[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                sw[u] = uint32_t(gp[2 * u].s16) | uint32_t(gp[2 * u + 1].s16) << 16;
+                zw[u] = uint32_t(gp[2 * u].z16) | uint32_t(gp[2 * u + 1].z16) << 16;
+            }
+            *reinterpret_cast<uint4*>(U16(a.c.k_scale) + pofs) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+            *reinterpret_cast<uint4*>(U16(a.c.k_zero) + pofs) = make_uint4(zw[0], zw[1], zw[2], zw[3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float f[8];
+            half8_f(kx[i], f);
+            uint32_t c2 = 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c2 |= code_of_r(f[u], gp[u].s, rs[u], gp[u].z) << (2 * u);
+            const int t = t0 + 8 * tq + i;
+            *reinterpret_cast<uint16_t*>(a.c.k_codes + (bhi * a.cap + t) * (D / 4) + 2 * co) = uint16_t(c2);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {                   // key rows past the quantized groups: fp16 ring
+        const int t = t0 + 8 * tq + i;
+        if (t < L && t >= n_kq) *reinterpret_cast<uint4*>(U16(a.c.k_res) + (bhi * a.ring + t % a.ring) * D + 8 * co) = kx[i];
+    }
+    // ---- values: per token, groups of 32 channels (lanes 4g .. 4g+3 of a row) ----
+    uint4 vx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vx[i] = *reinterpret_cast<const uint4*>(v.row(b, h, min(t0 + 8 * tq + i, L - 1)) + 8 * co);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = t0 + 8 * tq + i;
+        float f[8];
+        half8_f(vx[i], f);
+        float mn = f[0], mx = f[0];
+#pragma unroll
+        for (int u = 1; u < 8; ++u) { mn = fminf(mn, f[u]); mx = fmaxf(mx, f[u]); }
+        mn = fminf(mn, kdpp_f<0xb1>(mn));           // quad_perm [1,0,3,2]
+        mx = fmaxf(mx, kdpp_f<0xb1>(mx));
+        mn = fminf(mn, kdpp_f<0x4e>(mn));           // quad_perm [2,3,0,1]
+        mx = fmaxf(mx, kdpp_f<0x4e>(mx));
+        if (t < n_vq) {
+            const GroupParams gp = group_params(mn, mx);
+            const float r = __builtin_amdgcn_rcpf(gp.s);
+            uint32_t c2 = 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c2 |= code_of_r(f[u], gp.s, r, gp.z) << (2 * u);
+            *reinterpret_cast<uint16_t*>(a.c.v_codes + (bhi * a.cap + t) * (D / 4) + 2 * co) = uint16_t(c2);
+            if ((co & 3) == 0) {
+                U16(a.c.v_scale)[(bhi * a.cap + t) * (D / G) + (co >> 2)] = gp.s16;
+                U16(a.c.v_zero)[(bhi * a.cap + t) * (D / G) + (co >> 2)] = gp.z16;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {                   // value rows past the quantized tokens: fp16 ring
+        const int t = t0 + 8 * tq + i;
+        if (t < L && t >= n_vq) *reinterpret_cast<uint4*>(U16(a.c.v_res) + (bhi * a.ring + t % a.ring) * D + 8 * co) = vx[i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -468,6 +621,15 @@ extern "C" lvq_status kivi_append(const kivi_geom* g, const void* k_new, const v
     if (prefill) {
         const int n_kq = g->group * std::max(0, (n_new - g->R) / g->group);
         const int n_vq = std::max(0, n_new - g->R);
+        // One pass when every row starts on a 16-byte boundary (the usual contiguous layouts).
+        const bool aligned = reinterpret_cast<uintptr_t>(k_new) % 16 == 0 &&
+                             reinterpret_cast<uintptr_t>(v_new) % 16 == 0 && new_strides[0] % 8 == 0 &&
+                             new_strides[1] % 8 == 0 && new_strides[2] % 8 == 0;
+        if (aligned) {
+            hipLaunchKernelGGL(prefill_kv_kernel, dim3(ceil_div(n_new, 128), g->H, B), dim3(256), 0, stream, a, ks,
+                               vs, n_new, n_kq, n_vq);
+            return check_launch("kivi_append: prefill");
+        }
         if (n_kq > 0) {
             hipLaunchKernelGGL(prefill_keys_kernel, dim3(n_kq / g->group, g->H, B), dim3(g->D / 4), 0, stream, a, ks,
                                n_kq);
