@@ -166,6 +166,11 @@ __global__ void encode_scan_kernel(Geo geo, int block, const uint16_t* __restric
 // per lane, then the best of the 16 lanes of each row through DPP; the
 // lowest index wins exact ties.  Picks differ from the exact minimum only
 // by fp32 rounding of the sums.
+//
+// XREQ (few pages per request, as in the decode-time encode of one page):
+// a workgroup takes token slots u = b * tpr + j of all requests (tpr =
+// 8 * max_pages, j < 8 * n_pages[b] valid), so that each head's codebooks are
+// loaded once for the whole batch instead of once per request.
 // ---------------------------------------------------------------------------
 constexpr int kEncTile = 16;
 constexpr int kEncTilesPerWg = 32;
@@ -187,6 +192,8 @@ struct EncArgs {
     const int32_t* first_page;
     const int32_t* n_pages;
     int noct;                   // group octets, NG / 8
+    int B;
+    int tpr;                    // XREQ: token slots per request (8 * max_pages)
 };
 
 template <int CTRL>
@@ -194,7 +201,7 @@ __device__ __forceinline__ int dpp_i(int x) {
     return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
 }
 
-template <int TC>
+template <int TC, bool XREQ>
 __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
     constexpr int IPL = 8 / TC;                  // channels per lane and step
     const Geo& g = a.geo;
@@ -202,8 +209,8 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
     const int oct = blockIdx.y % a.noct;
     const int kv = (blockIdx.y / a.noct) & 1;
     const int h = blockIdx.y / (2 * a.noct);
-    const int b = blockIdx.z;
-    const int ntok = a.n_pages[b] * g.page;
+    const int b = XREQ ? 0 : blockIdx.z;        // (XREQ: per token slot, below)
+    const int ntok = XREQ ? a.B * a.tpr : a.n_pages[b] * g.page;   // XREQ: token slots
     const int tok_base = blockIdx.x * (kEncTile * kEncTilesPerWg);
     if (tok_base >= ntok) return;
     const uint16_t* x = kv == 0 ? a.xk : a.xv;
@@ -240,13 +247,31 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
     const long row0 = (a.tok0 ? a.tok0[b] : 0);
     const int fp = a.first_page[b];
     const long blk_off = ((long(a.block) * g.H + h) * 2 + kv) * g.page * g.NG;
+    // XREQ: token slot u -> (request, token of the request, whether the slot holds a token)
+    auto slot = [&](int u, int& bu, int& ju) {
+        bu = min(u / a.tpr, a.B - 1);
+        ju = u - bu * a.tpr;
+        return ju < a.n_pages[bu] * g.page;
+    };
     // coupled-vector coordinates k = 8q .. 8q+7 of token j (row of this lane): the raw words are loaded one
     // tile ahead and interleaved into coordinate order (element u = (i - i0) * TC + m) when used
     struct RawA { uint32_t w[TC][(IPL + 1) / 2]; };
     auto load_a = [&](int j) {
-        const long row = row0 + min(j, ntok - 1);
-        const uint16_t* xr = x + xbase + row * a.s2;
         RawA r;
+        const uint16_t* xr;
+        if constexpr (XREQ) {                    // a slot without a token loads nothing (zeros)
+            int bu, ju;
+            if (!slot(min(j, ntok - 1), bu, ju)) {
+#pragma unroll
+                for (int m = 0; m < TC; ++m)
+#pragma unroll
+                    for (int w = 0; w < (IPL + 1) / 2; ++w) r.w[m][w] = 0u;
+                return r;
+            }
+            xr = x + xbase + long(bu) * a.s0 + ((a.tok0 ? a.tok0[bu] : 0) + ju) * a.s2;
+        } else {
+            xr = x + xbase + (row0 + min(j, ntok - 1)) * a.s2;
+        }
 #pragma unroll
         for (int m = 0; m < TC; ++m) {
             if constexpr (IPL == 8) {
@@ -327,10 +352,19 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
     __syncthreads();
     // one thread per token: the octet's 8 index bytes, one 8-byte store (value rows: the octet's bytes sit
     // in the half row (octet ^ (tau >> 3 & 1)) XOR-permuted by tau & 7)
-    const int j = tok_base + tid;
-    if (tid < kEncTile * kEncTilesPerWg && j < t_end) {
-        const int lp = fp + j / g.page, ri = j % g.page;
-        const long phys = a.pt[long(b) * a.pt_stride + lp];
+    int j = tok_base + tid, bj = b, fpj = fp;
+    bool has = tid < kEncTile * kEncTilesPerWg && j < t_end;
+    if constexpr (XREQ) {
+        if (has) {
+            int ju;
+            has = slot(j, bj, ju);
+            j = ju;
+            fpj = a.first_page[bj];
+        }
+    }
+    if (has) {
+        const int lp = fpj + j / g.page, ri = j % g.page;
+        const long phys = a.pt[long(bj) * a.pt_stride + lp];
         const int tau = lp * g.page + ri;
         uint8_t* row = a.pool + phys * g.page_bytes + blk_off + ri * g.NG;
         if (kv == 0) {
@@ -419,17 +453,32 @@ extern "C" lvq_status lvq_encode(const lvq_geom* g, int32_t block, const void* x
         EncArgs ea{geo, block, static_cast<const uint16_t*>(x_k), static_cast<const uint16_t*>(x_v),
                    long(x_strides[0]), long(x_strides[1]), long(x_strides[2]), long(x_strides[3]), x_tok0,
                    static_cast<const uint16_t*>(codebooks), pool, page_table, pt_stride, first_page, n_pages,
-                   geo.NG / 8};
-        // token blocks fastest and a multiple of 8: the octets of one block share an XCD's L2
+                   geo.NG / 8, B, 0};
         const long tokens = long(max_pages) * geo.page;
-        const long nblk = (tokens + kEncTile * kEncTilesPerWg - 1) / (kEncTile * kEncTilesPerWg);
+        constexpr long kBlk = kEncTile * kEncTilesPerWg;
+        if (tokens <= 64 && long(B) * tokens <= 0x7fff0000L) {
+            // few pages per request: token slots of all requests per workgroup, codebooks loaded once per
+            // head for the whole batch
+            ea.B = B;
+            ea.tpr = int(tokens);
+            const dim3 grid(unsigned((long(B) * tokens + kBlk - 1) / kBlk), geo.H * 2 * (geo.NG / 8), 1);
+            switch (geo.Tc) {
+                case 1: hipLaunchKernelGGL((encode_mfma_kernel<1, true>), grid, dim3(512), 0, stream, ea); break;
+                case 2: hipLaunchKernelGGL((encode_mfma_kernel<2, true>), grid, dim3(512), 0, stream, ea); break;
+                case 4: hipLaunchKernelGGL((encode_mfma_kernel<4, true>), grid, dim3(512), 0, stream, ea); break;
+                default: hipLaunchKernelGGL((encode_mfma_kernel<8, true>), grid, dim3(512), 0, stream, ea); break;
+            }
+            return check_launch("lvq_encode");
+        }
+        // token blocks fastest and a multiple of 8: the octets of one block share an XCD's L2
+        const long nblk = (tokens + kBlk - 1) / kBlk;
         LVQ_REQUIRE(nblk <= 0x7ffffff8L, LVQ_ERR_UNSUPPORTED, "lvq_encode: too many pages");
         const dim3 grid(unsigned((nblk + 7) / 8 * 8), geo.H * 2 * (geo.NG / 8), B);
         switch (geo.Tc) {
-            case 1: hipLaunchKernelGGL(encode_mfma_kernel<1>, grid, dim3(512), 0, stream, ea); break;
-            case 2: hipLaunchKernelGGL(encode_mfma_kernel<2>, grid, dim3(512), 0, stream, ea); break;
-            case 4: hipLaunchKernelGGL(encode_mfma_kernel<4>, grid, dim3(512), 0, stream, ea); break;
-            default: hipLaunchKernelGGL(encode_mfma_kernel<8>, grid, dim3(512), 0, stream, ea); break;
+            case 1: hipLaunchKernelGGL((encode_mfma_kernel<1, false>), grid, dim3(512), 0, stream, ea); break;
+            case 2: hipLaunchKernelGGL((encode_mfma_kernel<2, false>), grid, dim3(512), 0, stream, ea); break;
+            case 4: hipLaunchKernelGGL((encode_mfma_kernel<4, false>), grid, dim3(512), 0, stream, ea); break;
+            default: hipLaunchKernelGGL((encode_mfma_kernel<8, false>), grid, dim3(512), 0, stream, ea); break;
         }
         return check_launch("lvq_encode");
     }

@@ -183,6 +183,43 @@ def test_single_pass_items():
     _run_parity(cfg, rows, steps=range(cfg.T), splits=(-1, 3))
 
 
+def test_encode_decode_page():
+    """The decode-time encode: one page per request (its last index page, as after every 8 generated
+    tokens), written into a cleared pool, equals byte for byte the prefill encode of the same tokens (whose
+    indices the parity tests check against the oracle), for every loop block, K and V; a request without
+    an index page writes nothing.  Lengths 683, 115, 454, 49, 388, 88, random page order."""
+    import decode_attention_loopvq_amd as lvq
+    import synth.loopvq as syn
+    from tests import harness
+    cfg = loopvq_config("loopvq-b64-6k", B=6, H=2, L=700, ragged=(40, 700), random_pages=True, seed=12)
+    geo = _geo(cfg)
+    p = harness.build_loopvq(cfg, keep=[(0, 1), (5, 0)])
+    for (b, h) in [(0, 1), (5, 0)]:
+        _check_indices(p, b, h, geo)
+    c = p.cache
+    n = torch.tensor(c.n_pages, dtype=torch.int32, device="cuda")
+    last = (n - 1).clamp(min=0)
+    one = (n > 0).to(torch.int32)
+    tok0 = c.tok0 + last.long() * p.g.page
+    pool2 = torch.zeros_like(c.pool)
+    _say("[encode page] one page per request, every block, K and V")
+    for kind in ("k", "v"):
+        for beta, x in syn.raw_blocks(cfg, kind, "cuda"):
+            lvq.lvq_encode(p.g, beta, x if kind == "k" else None, x if kind == "v" else None, p.codebooks, pool2,
+                           c.page_table, last, one, 1, x_tok0=tok0)
+    torch.cuda.synchronize()
+    written = []
+    for b in range(cfg.B):
+        if c.n_pages[b] == 0:
+            continue
+        phys = int(c.page_table_host[b, c.n_pages[b] - 1])
+        written.append(phys)
+        assert torch.equal(pool2[phys], c.pool[phys]), f"request {b}: page {phys} differs"
+    rest = torch.ones(pool2.shape[0], dtype=torch.bool, device="cuda")
+    rest[torch.tensor(written, device="cuda")] = False
+    assert not pool2[rest].any(), "bytes written outside the encoded pages"
+
+
 def test_partial_entry_points_compose():
     """lvq_quant_partial + lvq_window_partial + splitk_lse_merge give the attention of the oracle (the
     standalone path that lvq_decode_attn fuses)."""
