@@ -158,10 +158,11 @@ def kivi_rows(reps):
     prefill()
     q = synk.queries(cfg, "cuda")[0].contiguous()
     out = torch.empty((cfg.B, cfg.H, cfg.D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(lvq.kivi_decode_attn_workspace(g, cfg.B, cap), dtype=torch.uint8, device="cuda")
+    # max_len: the longest request after the prefill (what a server knows on the host), not the capacity
+    ws = torch.empty(lvq.kivi_decode_attn_workspace(g, cfg.B, cfg.L), dtype=torch.uint8, device="cuda")
 
     def attn():
-        lvq.kivi_decode_attn(g, q, cache, cap, synk.softmax_scale(cfg), out=out, ws=ws)
+        lvq.kivi_decode_attn(g, q, cache, cfg.L, synk.softmax_scale(cfg), out=out, ws=ws)
 
     t = timed(attn, reps * 10)
     per_bh = n_q * cfg.D // 4 * 2 + (n_q // cfg.group) * cfg.D * 4 + n_q * (cfg.D // cfg.group) * 4 \
