@@ -158,14 +158,16 @@ __global__ void encode_scan_kernel(Geo geo, int block, const uint16_t* __restric
 //
 // Workgroup: 8 waves, one index group each (groups 8*octet .. 8*octet+7), a
 // block of kEncTile * kEncTilesPerWg tokens of one (request, head, K|V).
-// A wave keeps its group's codebook as 16 B-fragments (codewords 16t .. 16t+15)
-// in registers.  MFMA lane l holds row / column l & 15 and coordinates
-// k = 8*(l >> 4) .. +7 of its operands (the codebook's own coordinate order
-// i*T_c + m; coordinates past G are zero), and result rows 4*(l >> 4) .. +3
-// of column l & 15.  Per 16-token tile: 16 MFMAs, the best of the 16 tiles
-// per lane, then the best of the 16 lanes of each row through DPP; the
-// lowest index wins exact ties.  Picks differ from the exact minimum only
-// by fp32 rounding of the sums.
+// A wave keeps its group's codebook as 16 operand fragments (codewords
+// 16t .. 16t+15) in registers and -||e||^2/2 of its 256 codewords in LDS.
+// MFMA lane l holds row / column l & 15 and coordinates k = 8*(l >> 4) .. +7
+// of its operands (the codebook's own coordinate order i*T_c + m;
+// coordinates past G are zero), and result rows 4*(l >> 4) .. +3 of column
+// l & 15.  Per 16-token tile: 16 MFMAs with the codewords as rows and the
+// tokens as columns, so lane (q, n) holds 64 scores of token n (codewords
+// 16t + 4q + i); its best, then the best of the 4 lanes of the column
+// through two lane swaps; the lowest index wins exact ties.  Picks differ
+// from the exact minimum only by fp32 rounding of the sums.
 //
 // XREQ (few pages per request, as in the decode-time encode of one page):
 // a workgroup takes token slots u = b * tpr + j of all requests (tpr =
@@ -301,43 +303,58 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
 
     // indices of the block's tokens for the 8 groups of this octet, written out at the end
     __shared__ __align__(16) uint8_t idx[kEncTile * kEncTilesPerWg][8];
+    // -||e_r||^2 / 2 of the wave's group in codeword order (each wave writes and reads only its own row)
+    __shared__ __align__(16) float cnorm[8][256];
+    {
+        const int w8 = tid >> 6;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) cnorm[w8][16 * t + n] = cinit[t];   // (the 4 lanes of a column agree)
+    }
+    // Tile of 16 tokens with the codewords as rows: lane (q, n) gets the scores of token t0 + n for
+    // codewords 16t + 4q + i (t < 16, i < 4), keeps its best (scanning in increasing codeword order with a
+    // strict >, so the lowest index wins equal values), then the best of the 4 lanes n, n + 16, n + 32,
+    // n + 48 through two lane swaps.
+    auto merge = [](float& best, int& r, float ob, int orr) {
+        const bool take = ob > best || (ob == best && orr < r);
+        best = take ? ob : best;
+        r = take ? orr : r;
+    };
     auto tile_fn = [&](int t0, const RawA& raw) {
-        const bf16x8_t Acur = build_a(raw);
-        int rsel = 0;
+        const bf16x8_t Bcur = build_a(raw);
+        const float* cn = &cnorm[tid >> 6][4 * q];
         f32x4_t acc[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const f32x4_t ci = {cinit[t], cinit[t], cinit[t], cinit[t]};
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur, bfr[t], ci, 0, 0, 0);
+            const f32x4_t ci = *reinterpret_cast<const f32x4_t*>(cn + 16 * t);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[t], Bcur, ci, 0, 0, 0);
         }
+        float best = acc[0][0];
+        int r = 4 * q;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float best = acc[0][i];
-            int bt = 0;
+        for (int t = 0; t < 16; ++t)
 #pragma unroll
-            for (int t = 1; t < 16; ++t) {
+            for (int i = (t == 0 ? 1 : 0); i < 4; ++i) {
                 const bool gt = acc[t][i] > best;
                 best = gt ? acc[t][i] : best;
-                bt = gt ? t : bt;
+                r = gt ? 16 * t + 4 * q + i : r;
             }
-            int r = 16 * bt + n;
-            // best over the 16 lanes of the row (DPP row rotations); lower index on equal values
-            auto step = [&](auto ctl) {
-                constexpr int C = decltype(ctl)::value;
-                const float ob = __int_as_float(dpp_i<C>(__float_as_int(best)));
-                const int orr = dpp_i<C>(r);
-                const bool take = ob > best || (ob == best && orr < r);
-                best = take ? ob : best;
-                r = take ? orr : r;
-            };
-            step(std::integral_constant<int, 0x128>{});
-            step(std::integral_constant<int, 0x124>{});
-            step(std::integral_constant<int, 0x122>{});
-            step(std::integral_constant<int, 0x121>{});
-            rsel = n == i ? r : rsel;
+        {   // lanes l and l ^ 32, then l and l ^ 16 (the combine is symmetric, so both lanes of a pair agree)
+            const auto bv = __builtin_amdgcn_permlane32_swap(__float_as_uint(best), __float_as_uint(best), false, false);
+            const auto rv = __builtin_amdgcn_permlane32_swap(uint32_t(r), uint32_t(r), false, false);
+            const uint32_t b0 = bv[0], b1 = bv[1], r0v = rv[0], r1v = rv[1];
+            best = __uint_as_float(b0);
+            r = int(r0v);
+            merge(best, r, __uint_as_float(b1), int(r1v));
         }
-        // row 4q + n (n < 4) of the tile into the workgroup's index block
-        if (n < 4) idx[(t0 - tok_base) + 4 * q + n][grp & 7] = uint8_t(rsel);
+        {
+            const auto bv = __builtin_amdgcn_permlane16_swap(__float_as_uint(best), __float_as_uint(best), false, false);
+            const auto rv = __builtin_amdgcn_permlane16_swap(uint32_t(r), uint32_t(r), false, false);
+            const uint32_t b0 = bv[0], b1 = bv[1], r0v = rv[0], r1v = rv[1];
+            best = __uint_as_float(b0);
+            r = int(r0v);
+            merge(best, r, __uint_as_float(b1), int(r1v));
+        }
+        if (q == 0) idx[(t0 - tok_base) + n][grp & 7] = uint8_t(r);
     };
     // two alternating buffers: the loads of tile k+1 are in flight while tile k computes
     RawA rawA = load_a(tok_base + n), rawB;
