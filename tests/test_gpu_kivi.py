@@ -135,3 +135,44 @@ def test_full_b16_4k_sampled():
         _compare_state(prob.cache, prob.g, b, h, states[(b, h)])
     worst = _check_attn(prob, rows, states)
     _say(f"[kivi full] worst rel err {worst:.3e}")
+
+
+def _layout(x: torch.Tensor, layout: str) -> torch.Tensor:
+    """The same [B][H][L][D] values in another memory layout (a strided view)."""
+    B, H, L, D = x.shape
+    if layout == "bhld":
+        return x
+    if layout == "blhd":                      # token-major, as a model's projections write it
+        return x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    if layout == "padded":                    # row stride D + 1: rows off the 16-byte grid
+        buf = torch.zeros((B, H, L, D + 1), dtype=x.dtype, device=x.device)
+        buf[..., :D] = x
+        return buf[..., :D]
+    if layout == "offset":                    # contiguous, base one element past an aligned address
+        buf = torch.zeros(x.numel() + 8, dtype=x.dtype, device=x.device)
+        buf[1:1 + x.numel()] = x.reshape(-1)
+        return buf[1:1 + x.numel()].view(B, H, L, D)
+    raise ValueError(layout)
+
+
+@pytest.mark.parametrize("layout", ["blhd", "padded", "offset"])
+def test_prefill_strided_inputs(layout):
+    """Prefill from views that are not contiguous [B][H][L][D]: token-major rows go through the one-pass
+    kernel; rows off the 16-byte grid go through the per-stage kernels.  Both bit-exact."""
+    import decode_attention_loopvq_amd as lvq
+    import synth.kivi as synk
+    cfg = kivi_config("kivi-b16-4k", B=2, H=3, L=333)
+    _say(f"[kivi prefill strided] layout={layout}")
+    g = lvq.make_kivi_geom(D=cfg.D, H=cfg.H, bits=cfg.bits, group=cfg.group, R=cfg.R, cap=((cfg.L + 256 + cfg.group - 1) // cfg.group) * cfg.group)
+    cache = lvq.KiviCache(g, cfg.B, device="cuda")
+    k, v = synk.raw_kv(cfg, "cuda")
+    kl, vl = _layout(k, layout), _layout(v, layout)
+    assert torch.equal(kl, k) and torch.equal(vl, v)
+    lvq.kivi_append(g, kl, vl, cache, prefill=True)
+    torch.cuda.synchronize()
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            st = kv.KiviState(D=g.D, group=g.group, R=g.R)
+            st.prefill(kh[b, h], vh[b, h])
+            _compare_state(cache, g, b, h, st)
