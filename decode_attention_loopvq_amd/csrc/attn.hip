@@ -891,14 +891,17 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
-// Window tokens of one request as seen by one row of 16 lanes (lane c16 holds
-// channels 8*c16 .. 8*c16+7): the sinks [0, min(L, sink)), then the recent
-// tokens [sink + 8*n_pages, L); n_w of them (none when !live).
+// Window tokens of one request as seen by one row of 16 lanes: lane c16 holds the RoPE pairs of frequencies
+// 4*c16 .. 4*c16+3, i.e. channels 4*c16 .. 4*c16+3 and 64 + the same (window_channel); the sinks
+// [0, min(L, sink)), then the recent tokens [sink + 8*n_pages, L); n_w of them (none when !live).
+__device__ __forceinline__ int window_channel(int c16, int u) { return (u < 4 ? 0 : 64) + 4 * c16 + (u & 3); }
+
 struct WinRow {
     int n_sink, q_hi, n_w, ring;
     long wbase;                                    // element offset of the row's (request, step, head) buffer
-    const float* trig;                             // cos (lanes c < 8) or sin (c >= 8) table
-    float qv[8];                                   // the lane's query channels, times sm_scale * log2 e
+    const float* rc;                               // cos and sin of the lane's frequencies at position 0
+    const float* rs;
+    float ql[4], qh[4];                            // the lane's query channels (i, then i + 64), times sm_scale * log2 e
 };
 
 __device__ __forceinline__ WinRow window_setup(const AttnArgs& a, int rb, int h, bool live, int c16) {
@@ -910,71 +913,74 @@ __device__ __forceinline__ WinRow window_setup(const AttnArgs& a, int rb, int h,
     w.n_sink = min(L, g.sink);
     w.n_w = live ? w.n_sink + max(0, L - w.q_hi) : 0;
     w.ring = g.W + g.page;
-    w.wbase = ((long(rb) * g.T + a.step) * g.H + h) * long(g.Wcap) * D + 8 * c16;
-    w.trig = (c16 >= 8 ? a.rs : a.rc) + 8 * (c16 & 7);
-    const uint4 qw = *reinterpret_cast<const uint4*>(a.q + (long(rb) * g.H + h) * D + 8 * c16);
-    const uint32_t w4[4] = {qw.x, qw.y, qw.z, qw.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        w.qv[2 * u] = bf16_lo(w4[u]) * a.scale_log2;
-        w.qv[2 * u + 1] = bf16_hi(w4[u]) * a.scale_log2;
-    }
+    w.wbase = ((long(rb) * g.T + a.step) * g.H + h) * long(g.Wcap) * D + 4 * c16;
+    w.rc = a.rc + 4 * c16;
+    w.rs = a.rs + 4 * c16;
+    const uint16_t* qp = a.q + (long(rb) * g.H + h) * D + 4 * c16;
+    const uint2 lo = *reinterpret_cast<const uint2*>(qp), hi = *reinterpret_cast<const uint2*>(qp + 64);
+    w.ql[0] = bf16_lo(lo.x) * a.scale_log2; w.ql[1] = bf16_hi(lo.x) * a.scale_log2;
+    w.ql[2] = bf16_lo(lo.y) * a.scale_log2; w.ql[3] = bf16_hi(lo.y) * a.scale_log2;
+    w.qh[0] = bf16_lo(hi.x) * a.scale_log2; w.qh[1] = bf16_hi(hi.x) * a.scale_log2;
+    w.qh[2] = bf16_lo(hi.y) * a.scale_log2; w.qh[3] = bf16_hi(hi.y) * a.scale_log2;
     return w;
 }
 
 // Online softmax step over the window tokens w0, w0 + stride, ... (NB of them, those >= n_w masked; needs
-// n_w >= 1), in log2 units: o[] is the lane's part of the unnormalised sum_w 2^(s_w - m) v_w, with m the
-// row's running maximum (-inf before the first token) and l = sum_w 2^(s_w - m), the same in every lane.
+// n_w >= 1), in log2 units: o[] is the lane's part (channels window_channel(c16, u)) of the unnormalised
+// sum_w 2^(s_w - m) v_w, with m the row's running maximum (-inf before the first token) and
+// l = sum_w 2^(s_w - m), the same in every lane.  The score needs no rotated key: per pair (i, i + 64),
+// q . R(p) k = k_i (q_i cos + q_{i+64} sin) + k_{i+64} (q_{i+64} cos - q_i sin).
 template <int NB = kWinBatch>
 __device__ __forceinline__ void window_batch(const AttnArgs& a, const WinRow& w, int w0, int stride, int c16,
                                              float& m, float& l, float (&o)[8]) {
     constexpr int D = 128;
     const Geo& g = a.geo;
-    const bool hi_half = c16 >= 8;
-    uint4 kw[NB], vw[NB];
-    float4 tg[NB][2];                        // cos (lanes c < 8) or sin (c >= 8) of the lane's frequencies
+    uint2 kl[NB], kh[NB], vl[NB], vh[NB];
+    float4 cs[NB], sn[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         const int t = min(w0 + stride * i, w.n_w - 1);    // a valid window token; extra ones are masked below
         const int p = t < w.n_sink ? t : w.q_hi + (t - w.n_sink);
         const int slot = p < g.sink ? p : g.sink + (p - g.sink) % w.ring;
-        kw[i] = *reinterpret_cast<const uint4*>(a.wk + w.wbase + long(slot) * D);
-        vw[i] = *reinterpret_cast<const uint4*>(a.wv + w.wbase + long(slot) * D);
-        const float4* tp = reinterpret_cast<const float4*>(w.trig + long(p) * (D / 2));
-        tg[i][0] = tp[0]; tg[i][1] = tp[1];
+        const uint16_t* kr = a.wk + w.wbase + long(slot) * D;
+        const uint16_t* vr = a.wv + w.wbase + long(slot) * D;
+        kl[i] = *reinterpret_cast<const uint2*>(kr);
+        kh[i] = *reinterpret_cast<const uint2*>(kr + 64);
+        vl[i] = *reinterpret_cast<const uint2*>(vr);
+        vh[i] = *reinterpret_cast<const uint2*>(vr + 64);
+        cs[i] = *reinterpret_cast<const float4*>(w.rc + long(p) * (D / 2));
+        sn[i] = *reinterpret_cast<const float4*>(w.rs + long(p) * (D / 2));
     }
     float s[NB];
     float mb = m;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        const uint32_t k4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
-        const float t8[8] = {tg[i][0].x, tg[i][0].y, tg[i][0].z, tg[i][0].w,
-                             tg[i][1].x, tg[i][1].y, tg[i][1].z, tg[i][1].w};
+        const float c4[4] = {cs[i].x, cs[i].y, cs[i].z, cs[i].w};
+        const float s4[4] = {sn[i].x, sn[i].y, sn[i].z, sn[i].w};
+        const float k_lo[4] = {bf16_lo(kl[i].x), bf16_hi(kl[i].x), bf16_lo(kl[i].y), bf16_hi(kl[i].y)};
+        const float k_hi[4] = {bf16_lo(kh[i].x), bf16_hi(kh[i].x), bf16_lo(kh[i].y), bf16_hi(kh[i].y)};
         float part = 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float k = (u & 1) ? bf16_hi(k4[u >> 1]) : bf16_lo(k4[u >> 1]);
-            const float kp = dpp<0x128>(k);           // the other half of the RoPE pair (lane c ^ 8)
-            const float tp = dpp<0x128>(t8[u]);       // and the other of cos / sin
-            const float c = hi_half ? tp : t8[u], sgn_s = hi_half ? t8[u] : -tp;
-            // lo half: k_i cos - k_{i+64} sin;  hi half: k_{i+64} cos + k_i sin
-            const float r = fmaf(k, c, kp * sgn_s);
-            part = fmaf(w.qv[u], r, part);
+        for (int u = 0; u < 4; ++u) {
+            const float psl = fmaf(w.ql[u], c4[u], w.qh[u] * s4[u]);
+            const float psh = fmaf(w.qh[u], c4[u], -(w.ql[u] * s4[u]));
+            part = fmaf(k_lo[u], psl, part);
+            part = fmaf(k_hi[u], psh, part);
         }
         const float si = row_sum16(part);
         s[i] = w0 + stride * i < w.n_w ? si : -INFINITY;
         mb = fmaxf(mb, s[i]);
     }
     const float mref = mb == -INFINITY ? 0.f : mb;  // a row with no token yet and none in this batch adds 0
-    const float alpha = exp2f(m - mref);
+    const float alpha = __builtin_amdgcn_exp2f(m - mref);
     l *= alpha;
 #pragma unroll
     for (int u = 0; u < 8; ++u) o[u] *= alpha;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        const float wgt = exp2f(s[i] - mref);
+        const float wgt = __builtin_amdgcn_exp2f(s[i] - mref);
         l += wgt;
-        const uint32_t v4[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
+        const uint32_t v4[4] = {vl[i].x, vl[i].y, vh[i].x, vh[i].y};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             o[2 * u] = fmaf(wgt, bf16_lo(v4[u]), o[2 * u]);
@@ -1017,7 +1023,7 @@ __global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __res
     window_row(a, rb, h, true, trow, NR, c16, m, l, o);
     __shared__ float red[NR][D + 2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) red[trow][8 * c16 + u] = o[u];
+    for (int u = 0; u < 8; ++u) red[trow][window_channel(c16, u)] = o[u];
     if (c16 == 0) {
         red[trow][D] = m;
         red[trow][D + 1] = l;
@@ -1028,7 +1034,7 @@ __global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __res
     for (int r = 0; r < NR; ++r) M = fmaxf(M, red[r][D]);
     float Ls = 0.f, ov = 0.f;
     for (int r = 0; r < NR; ++r) {
-        const float fw = red[r][D] == -INFINITY ? 0.f : exp2f(red[r][D] - M);
+        const float fw = red[r][D] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red[r][D] - M);
         Ls += red[r][D + 1] * fw;
         ov += red[r][tid] * fw;
     }
@@ -1047,18 +1053,18 @@ __global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __res
         for (int s2 = 0; s2 < kWinPrefetch; ++s2)
             if (s2 < S) Mx = fmaxf(Mx, pre_l[s2]);
         for (int s2 = kWinPrefetch; s2 < S; ++s2) Mx = fmaxf(Mx, pl[s2]);
-        float Lx = lse_win == -INFINITY ? 0.f : expf(lse_win - Mx);
+        float Lx = lse_win == -INFINITY ? 0.f : __expf(lse_win - Mx);
 #pragma unroll
         for (int s2 = 0; s2 < kWinPrefetch; ++s2)
-            if (s2 < S && pre_l[s2] != -INFINITY) Lx += expf(pre_l[s2] - Mx);
-        for (int s2 = kWinPrefetch; s2 < S; ++s2) Lx += pl[s2] == -INFINITY ? 0.f : expf(pl[s2] - Mx);
-        const float lse = Mx + logf(Lx);              // finite: a row holds at least one token
-        float acc = lse_win == -INFINITY ? 0.f : expf(lse_win - lse) * o_win;
+            if (s2 < S && pre_l[s2] != -INFINITY) Lx += __expf(pre_l[s2] - Mx);
+        for (int s2 = kWinPrefetch; s2 < S; ++s2) Lx += pl[s2] == -INFINITY ? 0.f : __expf(pl[s2] - Mx);
+        const float lse = Mx + __logf(Lx);              // finite: a row holds at least one token
+        float acc = lse_win == -INFINITY ? 0.f : __expf(lse_win - lse) * o_win;
 #pragma unroll
         for (int s2 = 0; s2 < kWinPrefetch; ++s2)
-            if (s2 < S && pre_l[s2] != -INFINITY) acc += expf(pre_l[s2] - lse) * pre_o[s2];
+            if (s2 < S && pre_l[s2] != -INFINITY) acc += __expf(pre_l[s2] - lse) * pre_o[s2];
         for (int s2 = kWinPrefetch; s2 < S; ++s2)
-            if (pl[s2] != -INFINITY) acc += expf(pl[s2] - lse) * a.part_o[(row * a.S_tot + s2) * D + tid];
+            if (pl[s2] != -INFINITY) acc += __expf(pl[s2] - lse) * a.part_o[(row * a.S_tot + s2) * D + tid];
         out[row * D + tid] = acc;
         if (lse_out && tid == 0) lse_out[row] = lse;
     }
@@ -1542,9 +1548,8 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
     // ---- the window rows, merged like an item ----
     __syncthreads();                                // the last item's partials are read
     if (wave < NWW) {
-        float4* dst = reinterpret_cast<float4*>(part + wr * D + 8 * c16);
-        dst[0] = make_float4(wo[0], wo[1], wo[2], wo[3]);
-        dst[1] = make_float4(wo[4], wo[5], wo[6], wo[7]);
+        *reinterpret_cast<float4*>(part + wr * D + window_channel(c16, 0)) = make_float4(wo[0], wo[1], wo[2], wo[3]);
+        *reinterpret_cast<float4*>(part + wr * D + window_channel(c16, 4)) = make_float4(wo[4], wo[5], wo[6], wo[7]);
         wml[wr][0] = wm;                            // (the row's 16 lanes hold the same m and l)
         wml[wr][1] = wl;
     }
