@@ -115,17 +115,23 @@ def attn_row(name, cfg_name, steps, reps, **over):
     ws = torch.empty(lvq.lvq_decode_attn_workspace(p.g, cfg.B, p.cache.max_len), dtype=torch.uint8,
                      device="cuda")
     qs = [p.q[t].contiguous() for t in range(cfg.T)]
+    # Ragged batches: the requests grouped by length (one order per decode step, shared by its calls).
+    order = lvq.lvq_request_order(p.cache.seq_len, p.cache.max_len) if cfg.ragged else None
+    extra = {}
+    if order is not None:
+        t_ord = timed(lambda: lvq.lvq_request_order(p.cache.seq_len, p.cache.max_len, out=order), reps * 10)
+        extra = dict(order="by length (lvq_request_order, once per decode step)", order_us=round(t_ord * 1e6, 2))
 
     def run():
         for t in steps:
             lvq.lvq_decode_attn(p.g, t, qs[t], p.cache.pool, p.cache.page_table, p.cache.seq_len, p.cache.max_len,
                                 p.cache.win_k, p.cache.win_v, p.slices, p.rope_cos, p.rope_sin, p.sm_scale,
-                                out=out, ws=ws, rope_f16=p.rope16)
+                                out=out, ws=ws, rope_f16=p.rope16, order=order)
 
     t = timed(run, reps) / len(steps)
     emit(row=name, workload=cfg.name, B=cfg.B, H=cfg.H, L=cfg.L, steps=list(steps), us_per_call=round(t * 1e6, 2),
          gbps=round(per_call / t / 1e9, 1), hbm_frac=round(per_call / t / PEAK_HBM, 4), bytes_per_call=per_call,
-         token_heads_per_s=round(sum(p.lengths) * cfg.H / t, 1))
+         token_heads_per_s=round(sum(p.lengths) * cfg.H / t, 1), **extra)
 
 
 def kivi_rows(reps):

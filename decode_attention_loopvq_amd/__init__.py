@@ -20,7 +20,7 @@ from . import layout  # noqa: F401
 
 __all__ = [
     "LvqError", "lvq_geom", "kivi_geom", "make_geom", "make_kivi_geom",
-    "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn",
+    "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_request_order",
     "lvq_decode_attn_splits", "lvq_quant_partial", "lvq_quant_partial_workspace", "lvq_window_partial", "splitk_lse_merge", "kivi_append",
     "kivi_decode_attn_workspace", "kivi_decode_attn", "KiviCache", "layout",
 ]
@@ -146,10 +146,11 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
                     slices: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor, sm_scale: float,
                     out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
                     ws: Optional[torch.Tensor] = None, num_splits: int = 0,
-                    stream=None, rope_f16: Optional[torch.Tensor] = None
+                    stream=None, rope_f16: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Decode attention of loop step `step`; returns (out [B][H][D] fp32, lse [B][H] or None).
-    rope_f16 (lvq_rope_table_f16) is required with bf16 codebooks."""
+    rope_f16 (lvq_rope_table_f16) is required with bf16 codebooks; order (int32 [B], e.g. from
+    lvq_request_order) groups the requests into workgroups (None: in batch order)."""
     _need(q, "q", torch.bfloat16)
     B = q.shape[0]
     if tuple(q.shape) != (B, g.H, g.D):
@@ -166,6 +167,7 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
     _need(rope_sin, "rope_sin", torch.float32)
     if seq_len.numel() != B or page_table.dim() != 2 or page_table.shape[0] != B:
         raise ValueError("seq_len / page_table batch does not match q")
+    _need_order(order, B)
     if out is None:
         out = torch.empty((B, g.H, g.D), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32)
@@ -176,7 +178,8 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
     _need(ws, "ws")
     check(lib.lvq_decode_attn(C.byref(g), int(step), q.data_ptr(), pool.data_ptr(), page_table.data_ptr(),
-                              int(page_table.shape[1]), seq_len.data_ptr(), int(max_len), win_k.data_ptr(),
+                              int(page_table.shape[1]), seq_len.data_ptr(), int(max_len),
+                              order.data_ptr() if order is not None else None, win_k.data_ptr(),
                               win_v.data_ptr(), slices.data_ptr(), rope_cos.data_ptr(), rope_sin.data_ptr(),
                               _rope_f16_ptr(rope_f16, rope_cos), int(rope_cos.shape[0]), float(sm_scale),
                               out.data_ptr(),
@@ -184,6 +187,26 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
                               ws.numel() * ws.element_size(), int(num_splits), int(B), _stream(stream)),
           "lvq_decode_attn")
     return out, lse_out
+
+
+def _need_order(order: Optional[torch.Tensor], B: int):
+    if order is not None:
+        _need(order, "order", torch.int32)
+        if order.numel() != B:
+            raise ValueError("order must hold one entry per request")
+
+
+def lvq_request_order(seq_len: torch.Tensor, max_len: int, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """The batch ranked by length, longest first (ties by index): int32 [B] for the `order` argument."""
+    _need(seq_len, "seq_len", torch.int32)
+    B = seq_len.numel()
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=seq_len.device)
+    _need_order(out, B)
+    check(lib.lvq_request_order(seq_len.data_ptr(), int(B), int(max_len), out.data_ptr(), _stream(stream)),
+          "lvq_request_order")
+    return out
 
 
 def lvq_decode_attn_splits(g: lvq_geom, B: int, max_len: int) -> int:
@@ -199,7 +222,7 @@ def lvq_quant_partial(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tenso
                       seq_len: torch.Tensor, max_len: int, slices: torch.Tensor, rope_cos: torch.Tensor,
                       rope_sin: torch.Tensor, sm_scale: float, part_o: torch.Tensor, part_lse: torch.Tensor,
                       num_splits: int, ws: Optional[torch.Tensor] = None, stream=None,
-                      rope_f16: Optional[torch.Tensor] = None):
+                      rope_f16: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None):
     """Index-page partials into part_o [B*H][S_tot][D], part_lse [B*H][S_tot] (slots 0..num_splits-1)."""
     _need(q, "q", torch.bfloat16)
     _need(pool, "pool", torch.uint8)
@@ -209,12 +232,14 @@ def lvq_quant_partial(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tenso
     _need(part_o, "part_o", torch.float32)
     _need(part_lse, "part_lse", torch.float32)
     B = q.shape[0]
+    _need_order(order, B)
     need = lvq_quant_partial_workspace(g, B, max_len)
     if ws is None:
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
     _need(ws, "ws")
     check(lib.lvq_quant_partial(C.byref(g), int(step), q.data_ptr(), pool.data_ptr(), page_table.data_ptr(),
-                                int(page_table.shape[1]), seq_len.data_ptr(), int(max_len), slices.data_ptr(),
+                                int(page_table.shape[1]), seq_len.data_ptr(), int(max_len),
+                                order.data_ptr() if order is not None else None, slices.data_ptr(),
                                 rope_cos.data_ptr(), rope_sin.data_ptr(), _rope_f16_ptr(rope_f16, rope_cos),
                                 int(rope_cos.shape[0]), float(sm_scale), part_o.data_ptr(), part_lse.data_ptr(),
                                 int(num_splits), int(part_lse.shape[1]),

@@ -42,6 +42,7 @@ struct AttnArgs {
     int pps;                    // index pages per split
     int B;
     int max_len;                // device lengths are clamped to this
+    const int32_t* order;       // [B] request of each workgroup slot (NULL: request i in slot i)
     int rope_len;
     const uint32_t* qpack;      // [B*H][64] packed fp16 query rows (written and read by index_attn_kernel)
     const uint4* rope16;        // [16][rope_len] packed fp16 cos/sin chunks (lvq_rope_table_f16)
@@ -51,6 +52,15 @@ struct AttnArgs {
 __device__ __forceinline__ int clamp_len(const AttnArgs& a, int rb) {
     const int L = a.seq_len[rb];
     return L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+}
+
+// The request in slot i of the batch's grouping (workgroups take consecutive slots): order[i] when an
+// order is given, else i; B (no request) for slots past the batch and for entries outside [0, B).
+__device__ __forceinline__ int group_request(const AttnArgs& a, int i) {
+    if (i >= a.B) return a.B;
+    if (!a.order) return i;
+    const int r = a.order[i];
+    return r >= 0 && r < a.B ? r : a.B;
 }
 
 __device__ __forceinline__ int n_index_pages(int L, const Geo& g) {
@@ -117,8 +127,9 @@ __global__ void __launch_bounds__(256) quant_partial_kernel(AttnArgs a) {
     // Page ranges of the two requests; leave early when both are empty.
     int plo[2], phi[2];
     bool any = false;
+    int rq[2];
     for (int j = 0; j < 2; ++j) {
-        const int rb = r0 + j;
+        const int rb = rq[j] = group_request(a, r0 + j);
         plo[j] = phi[j] = 0;
         if (rb < a.B) {
             const int np = n_index_pages(clamp_len(a, rb), g);
@@ -129,7 +140,7 @@ __global__ void __launch_bounds__(256) quant_partial_kernel(AttnArgs a) {
     }
     if (!any) {
         for (int j = 0; j < 2; ++j) {
-            const int rb = r0 + j;
+            const int rb = rq[j];
             if (rb >= a.B) continue;
             const long row = (long(rb) * g.H + h) * a.S_tot + split;
             if (tid < D) a.part_o[row * D + tid] = 0.f;
@@ -170,8 +181,8 @@ __global__ void __launch_bounds__(256) quant_partial_kernel(AttnArgs a) {
     const int gA = chA / C, gB = chB / C;                // first group of each chunk
 
     for (int j = 0; j < 2; ++j) {
-        const int rb = r0 + j;
-        if (rb >= a.B) break;
+        const int rb = rq[j];
+        if (rb >= a.B) continue;
         const long orow = (long(rb) * g.H + h) * a.S_tot + split;
         if (phi[j] <= plo[j]) {
             if (tid < D) a.part_o[orow * D + tid] = 0.f;
@@ -381,15 +392,17 @@ constexpr int kChunk = 64;                        // tokens per wave iteration (
 constexpr int kMaxSplitTok = 1536;                // index tokens per split at most (192 pages)
 constexpr int kChunksPerWave = kMaxSplitTok / kChunk / (kIThreads / 64);
 
-// Index-token range [lo, hi) of request slot j of a workgroup in split `split` (hi <= lo: empty).
+// Index-token range [lo, hi) of request slot j (request rq[j], none when >= B) of a workgroup in split
+// `split` (hi <= lo: empty).
 template <int R>
-__device__ __forceinline__ bool split_ranges(const AttnArgs& a, int split, int r0, int (&lo)[R], int (&hi)[R]) {
+__device__ __forceinline__ bool split_ranges(const AttnArgs& a, int split, const int (&rq)[R], int (&lo)[R],
+                                             int (&hi)[R]) {
     const Geo& g = a.geo;
     const int split_tok = a.pps * g.page;
     bool any = false;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        const int rb = r0 + j;
+        const int rb = rq[j];
         const int np8 = rb < a.B ? n_index_pages(clamp_len(a, rb), g) * g.page : 0;
         lo[j] = min(np8, split * split_tok);
         hi[j] = min(np8, (split + 1) * split_tok);
@@ -471,6 +484,9 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
     const int h = blockIdx.x, split = blockIdx.y, r0 = blockIdx.z * R;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int rq[R];                                      // the requests of the workgroup's slots (>= B: none)
+#pragma unroll
+    for (int j = 0; j < R; ++j) rq[j] = group_request(a, r0 + j);
     // Loads that need no request length go first: the K slice of head h and the query elements this
     // thread packs.
     uint4 stage[NSTAGE];
@@ -482,16 +498,16 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
     }
     uint32_t qraw = 0;                              // two bf16 query elements (packed-query dword tid & 63)
     const int qj = tid >> 6, qt = tid & 63;
-    const long qprow = long(min(r0 + min(qj, R - 1), a.B - 1)) * g.H + h;
+    const long qprow = long(min(rq[min(qj, R - 1)], a.B - 1)) * g.H + h;
     if (tid < R * 64) {
         const int m = qt >> 2, k = qt & 3;
         const int ch = (k < 2 ? 0 : 64) + 4 * m + 2 * (k & 1);
         qraw = *reinterpret_cast<const uint32_t*>(a.q + qprow * D + ch);
     }
     int lo[R], hi[R];
-    if (!split_ranges<R>(a, split, r0, lo, hi)) {
+    if (!split_ranges<R>(a, split, rq, lo, hi)) {
         for (int e = tid; e < R * D; e += NT) {
-            const int j = e / D, d = e % D, rb = r0 + j;
+            const int j = e / D, d = e % D, rb = rq[j];
             if (rb >= a.B) continue;
             const long row = (long(rb) * g.H + h) * a.S_tot + split;
             a.part_o[row * D + d] = 0.f;
@@ -504,7 +520,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
     int t_lo = 0x7fffffff, t_hi = 0;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        const int rb = min(r0 + j, a.B - 1);
+        const int rb = min(rq[j], a.B - 1);
         ptr[j] = a.pt + long(rb) * a.pt_stride;
         srow[j] = long(rb) * g.H + h;
         if (hi[j] > lo[j]) {
@@ -836,7 +852,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
     }
     __syncthreads();
     for (int e = tid; e < R * D; e += NT) {
-        const int j = e / D, d = e % D, rb = r0 + j;
+        const int j = e / D, d = e % D, rb = rq[j];
         if (rb >= a.B) continue;
         const long orow = (long(rb) * g.H + h) * a.S_tot + split;
         if (hi[j] <= lo[j]) {
@@ -1142,13 +1158,16 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
     float (*const wml)[2] = reinterpret_cast<float (*)[2]>(lds + 2 * KS + PART * 4 + 2 * NW * R * 4);   // [16]
     const Geo& g = a.geo;
     const int h = blockIdx.x, r0 = blockIdx.y * R;
+    int rq[R];                                      // the requests of the workgroup's slots (>= B: none)
+#pragma unroll
+    for (int j = 0; j < R; ++j) rq[j] = group_request(a, r0 + j);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     // ---- setup ----
     uint32_t qraw = 0;                              // two bf16 query elements (packed-query dword tid & 63)
     const int qj = tid >> 6, qt = tid & 63;
-    const long qprow = long(min(r0 + min(qj, R - 1), a.B - 1)) * g.H + h;
+    const long qprow = long(min(rq[min(qj, R - 1)], a.B - 1)) * g.H + h;
     if (tid < R * 64) {
         const int m = qt >> 2, k = qt & 3;
         const int ch = (k < 2 ? 0 : 64) + 4 * m + 2 * (k & 1);
@@ -1171,8 +1190,8 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
     int t_hi = 0;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-        const int rb = min(r0 + j, a.B - 1);
-        hi[j] = r0 + j < a.B ? n_index_pages(clamp_len(a, rb), g) * g.page : 0;
+        const int rb = min(rq[j], a.B - 1);
+        hi[j] = rq[j] < a.B ? n_index_pages(clamp_len(a, rb), g) * g.page : 0;
         ptr[j] = a.pt + long(rb) * a.pt_stride;
         srow[j] = long(rb) * g.H + h;
         t_hi = max(t_hi, hi[j]);
@@ -1358,7 +1377,8 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
     for (int u = 0; u < 8; ++u) wo[u] = 0.f;
     if (wave < NWW) {
         const int wj = wave * 4 / RPJ;
-        window_row(a, min(r0 + wj, a.B - 1), h, r0 + wj < a.B, wr % RPJ, RPJ, c16, wm, wl, wo);
+        const int wrb = group_request(a, r0 + wj);
+        window_row(a, min(wrb, a.B - 1), h, wrb < a.B, wr % RPJ, RPJ, c16, wm, wl, wo);
     }
 
     // Running merge of this thread's output element (request j, channel d), in log2 units: each item, then
@@ -1575,8 +1595,9 @@ __global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, fl
     }
 
     // ---- output: a request holds at least one token, so run_l > 0 ----
-    if (tid < R * D && r0 + oj < a.B) {
-        const long row = long(r0 + oj) * g.H + h;
+    const int orb = group_request(a, r0 + min(oj, R - 1));
+    if (tid < R * D && orb < a.B) {
+        const long row = long(orb) * g.H + h;
         out[row * D + od] = run_o / run_l;
         if (lse_out && od == 0) lse_out[row] = (run_m + log2f(run_l)) * kLn2;
     }
@@ -1768,7 +1789,8 @@ void set_slices(AttnArgs* a, const void* slices) {
 
 extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
                                         const int32_t* page_table, int32_t pt_stride, const int32_t* seq_len,
-                                        int32_t max_len, const void* slices, const float* rope_cos,
+                                        int32_t max_len, const int32_t* order, const void* slices,
+                                        const float* rope_cos,
                                         const float* rope_sin, const void* rope_f16, int32_t rope_len,
                                         float sm_scale, float* part_o,
                                         float* part_lse, int32_t num_splits, int32_t S_tot, void* ws,
@@ -1777,6 +1799,7 @@ extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const 
     lvq_status st = prepare("lvq_quant_partial", gp, step, q, seq_len, max_len, rope_cos, rope_sin, rope_f16,
                             rope_len, sm_scale, B, &a);
     if (st != LVQ_OK) return st;
+    a.order = order;
     const Geo& g = a.geo;
     LVQ_REQUIRE(num_splits >= 1 && num_splits <= 1024 && S_tot >= num_splits, LVQ_ERR_INVALID_ARG,
                 "lvq_quant_partial: num_splits %d, S_tot %d", num_splits, S_tot);
@@ -1830,7 +1853,8 @@ extern "C" lvq_status lvq_window_partial(const lvq_geom* gp, int32_t step, const
 
 extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
                                       const int32_t* page_table, int32_t pt_stride, const int32_t* seq_len,
-                                      int32_t max_len, const void* win_k, const void* win_v, const void* slices,
+                                      int32_t max_len, const int32_t* order, const void* win_k,
+                                      const void* win_v, const void* slices,
                                       const float* rope_cos, const float* rope_sin, const void* rope_f16,
                                       int32_t rope_len, float sm_scale, float* out, float* lse_out, void* ws,
                                       size_t ws_bytes,
@@ -1839,6 +1863,7 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
     lvq_status st = prepare("lvq_decode_attn", gp, step, q, seq_len, max_len, rope_cos, rope_sin, rope_f16,
                             rope_len, sm_scale, B, &a);
     if (st != LVQ_OK) return st;
+    a.order = order;
     const Geo& g = a.geo;
     LVQ_REQUIRE(num_splits >= -1 && num_splits <= 1024, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: num_splits %d",
                 num_splits);
@@ -1896,4 +1921,54 @@ extern "C" lvq_status splitk_lse_merge(const float* part_o, const float* part_ls
     hipLaunchKernelGGL(merge_kernel, dim3(n), dim3(D < 256 ? ((D + 63) / 64) * 64 : 256), 0, stream, part_o,
                        part_lse, S, D, out, lse_out);
     return check_launch("splitk_lse_merge");
+}
+
+// ---------------------------------------------------------------------------
+// Request order for ragged batches: the batch ranked by length, longest first (ties by index), so that
+// the requests a workgroup takes together have similar lengths.  Request i's key
+// (clamped length << 12) | (4095 - i) is distinct and orders by length, then by index; its rank is the
+// number of larger keys.  One workgroup; batches over kOrderMaxB or lengths from 2^20 get the identity.
+// ---------------------------------------------------------------------------
+namespace lvq {
+namespace {
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderMaxB = 4096;
+
+__global__ void __launch_bounds__(kOrderThreads) request_order_kernel(const int32_t* __restrict__ seq_len, int B,
+                                                                       int max_len, int32_t* __restrict__ order) {
+    __shared__ __align__(16) uint32_t key[kOrderMaxB];
+    const int B4 = (B + 3) & ~3;
+    for (int i = threadIdx.x; i < B4; i += kOrderThreads) {
+        const int L = i < B ? min(max(seq_len[i], 0), max_len) : 0;
+        key[i] = i < B ? (uint32_t(L) << 12) | uint32_t(4095 - i) : 0u;   // padding ranks no request
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < B; i += kOrderThreads) {
+        const uint32_t ki = key[i];
+        int rank = 0;
+        for (int k = 0; k < B4; k += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(key + k);
+            rank += int(v.x > ki) + int(v.y > ki) + int(v.z > ki) + int(v.w > ki);
+        }
+        order[rank] = i;
+    }
+}
+
+__global__ void identity_order_kernel(int B, int32_t* __restrict__ order) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < B) order[i] = i;
+}
+}  // namespace
+}  // namespace lvq
+
+extern "C" lvq_status lvq_request_order(const int32_t* seq_len, int32_t B, int32_t max_len, int32_t* order,
+                                        hipStream_t stream) {
+    LVQ_REQUIRE(B >= 0 && max_len >= 1, LVQ_ERR_INVALID_ARG, "lvq_request_order: B=%d max_len=%d", B, max_len);
+    if (B == 0) return LVQ_OK;
+    LVQ_REQUIRE(seq_len && order, LVQ_ERR_INVALID_ARG, "lvq_request_order: NULL pointer");
+    if (B <= kOrderMaxB && max_len < (1 << 20))
+        hipLaunchKernelGGL(request_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, seq_len, B, max_len, order);
+    else
+        hipLaunchKernelGGL(identity_order_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, B, order);
+    return check_launch("lvq_request_order");
 }

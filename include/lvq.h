@@ -196,6 +196,15 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  *
  *  q          bf16 [B][H][D], already rotated at position seq_len[b] - 1.
  *  seq_len    device int32 [B], 1 <= seq_len[b] <= max_len <= rope_len.
+ *  order      device int32 [B] or NULL: the grouping of requests into
+ *             workgroups, which take consecutive entries (four at a time,
+ *             two when c = 4); NULL means order[i] = i.  It must hold each
+ *             request once (lvq_request_order below writes one sorted by
+ *             length, which keeps a workgroup's requests of similar length
+ *             and so saves work on ragged batches); an entry outside [0, B)
+ *             leaves its slot empty and that request unattended (its output
+ *             is then undefined), never an out-of-bounds access.  The output
+ *             does not depend on the grouping.
  *  slices     slices of ALL steps (layout above); the call reads step `step`.
  *             bf16 slice entries must lie within the binary16 range
  *             (|x| <= 65504): the index-page pass converts the step's key
@@ -217,7 +226,7 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  */
 LVQ_API lvq_status lvq_decode_attn(const lvq_geom* g, int32_t step, const void* q,
                            const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
-                           const int32_t* seq_len, int32_t max_len,
+                           const int32_t* seq_len, int32_t max_len, const int32_t* order,
                            const void* win_k, const void* win_v,
                            const void* slices, const float* rope_cos, const float* rope_sin,
                            const void* rope_f16, int32_t rope_len, float sm_scale, float* out, float* lse_out,
@@ -227,6 +236,19 @@ LVQ_API lvq_status lvq_decode_attn(const lvq_geom* g, int32_t step, const void* 
 /* What lvq_decode_attn runs for num_splits = 0: -1 for the single-pass kernel, else its split count
  * (0 on bad arguments). */
 LVQ_API int32_t lvq_decode_attn_splits(const lvq_geom* g, int32_t B, int32_t max_len);
+
+/*
+ * A request order for ragged batches: order[k] = the request of rank k when
+ * the batch is sorted by length min(max(seq_len[b], 0), max_len), longest
+ * first, equal lengths by index (a permutation of 0 .. B-1; equal lengths
+ * give the identity).  Batches of more than 4096 requests, or max_len of
+ * 2^20 or more, get the identity.  One kernel launch; within a decode step
+ * every layer and loop step can use the same order.
+ *  seq_len  device int32 [B];  order  device int32 [B], written.
+ * Errors: LVQ_ERR_INVALID_ARG for B < 0, max_len < 1 or NULL pointers.
+ */
+LVQ_API lvq_status lvq_request_order(const int32_t* seq_len, int32_t B, int32_t max_len, int32_t* order,
+                                     hipStream_t stream);
 
 /*
  * The two partial passes lvq_decode_attn is made of, callable on their own
@@ -250,7 +272,8 @@ LVQ_API int32_t lvq_decode_attn_splits(const lvq_geom* g, int32_t B, int32_t max
  */
 LVQ_API lvq_status lvq_quant_partial(const lvq_geom* g, int32_t step, const void* q,
                                      const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
-                                     const int32_t* seq_len, int32_t max_len, const void* slices,
+                                     const int32_t* seq_len, int32_t max_len, const int32_t* order,
+                                     const void* slices,
                                      const float* rope_cos, const float* rope_sin, const void* rope_f16,
                                      int32_t rope_len, float sm_scale, float* part_o, float* part_lse,
                                      int32_t num_splits,

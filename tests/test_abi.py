@@ -48,7 +48,7 @@ def _attn(g, **over):
     args.update(over)
     gp = C.byref(g) if g is not None else None
     return _lib.lib.lvq_decode_attn(gp, args["step"], args["q"], args["pool"], args["pt"], args["pt_stride"],
-                                    args["seq_len"], args["max_len"], args["wk"], args["wv"], args["slices"],
+                                    args["seq_len"], args["max_len"], None, args["wk"], args["wv"], args["slices"],
                                     args["cos"], args["sin"], args["rope16"], args["rope_len"], args["scale"],
                                     args["out"],
                                     args["lse"], args["ws"], args["ws_bytes"], args["splits"], args["B"], None)
@@ -157,3 +157,13 @@ def test_python_binding_refuses_host_tensors():
     g = _geom()
     with pytest.raises(ValueError):
         lvq.lvq_slice_codebooks(g, torch.zeros((2, 2, 2, 16, 256, 16), dtype=torch.bfloat16))
+
+
+def test_request_order_rejects():
+    """Argument checks of lvq_request_order (all fail before any launch); B = 0 is a no-op."""
+    f = _lib.lib.lvq_request_order
+    assert f(FAKE, -1, 100, FAKE, None) == INVALID
+    assert f(FAKE, 4, 0, FAKE, None) == INVALID
+    assert f(None, 4, 100, FAKE, None) == INVALID
+    assert f(FAKE, 4, 100, None, None) == INVALID
+    assert f(None, 0, 100, None, None) == OK

@@ -277,3 +277,48 @@ def test_full_b64_6k_sampled():
 def test_full_b1_1k():
     cfg = loopvq_config("loopvq-b1-1k-fp32cb")
     _run_parity(cfg, [(0, 0)], steps=range(cfg.T), splits=(0,))
+
+
+def test_request_order_sorts_by_length():
+    """lvq_request_order against a stable host sort of the clamped lengths (longest first, ties by index)."""
+    import decode_attention_loopvq_amd as lvq
+    rng = np.random.default_rng(21)
+    for B, max_len in ((1, 100), (7, 900), (64, 6144), (255, 5000), (1000, 70000)):
+        lens = rng.integers(-3, max_len + 50, size=B).astype(np.int32)
+        lens[: B // 3] = lens[0]                       # runs of equal lengths
+        _say(f"[order] B={B} max_len={max_len}")
+        order = lvq.lvq_request_order(torch.from_numpy(lens).cuda(), max_len).cpu().numpy()
+        clamped = np.clip(lens, 0, max_len)
+        expect = np.lexsort((np.arange(B), -clamped))  # primary key: length descending; then index
+        np.testing.assert_array_equal(order, expect)
+    lens = np.full(37, 300, dtype=np.int32)
+    order = lvq.lvq_request_order(torch.from_numpy(lens).cuda(), 300).cpu().numpy()
+    np.testing.assert_array_equal(order, np.arange(37))
+
+
+@pytest.mark.parametrize("name,over,splits", [
+    ("loopvq-b64-6k", dict(B=9, H=2, L=3000, ragged=(40, 3000), random_pages=True, seed=31), (0, 3, -1)),
+    ("loopvq-deep-ragged", dict(B=7, H=2, L=900, ragged=(1, 900)), (0, 2, -1)),
+    ("loopvq-b1-1k-fp32cb", dict(B=5, H=2, L=1024, ragged=(30, 1024)), (0, 2)),
+], ids=["bf16-c8", "bf16-c4", "fp32"])
+def test_order_does_not_change_the_output(name, over, splits):
+    """The grouping of requests into workgroups changes no bit of the output: no order, the length order and
+    a random permutation (every path: the split kernels for bf16 and fp32 codebooks, the single pass)."""
+    import decode_attention_loopvq_amd as lvq
+    from tests import harness
+    cfg = loopvq_config(name, **over)
+    _say(f"[build] {cfg.name} B={cfg.B} ragged order invariance")
+    p = harness.build_loopvq(cfg, keep=[])
+    c = p.cache
+    by_len = lvq.lvq_request_order(c.seq_len, c.max_len)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(cfg.B).astype(np.int32)).cuda()
+    for ns in splits:
+        for t in (0, cfg.T - 1):
+            _say(f"[order] {cfg.name} step {t} num_splits={ns}")
+            ref, lse_ref = harness.run_step(p, t, num_splits=ns,
+                                            lse=torch.empty((cfg.B, cfg.H), dtype=torch.float32, device="cuda"))
+            for order in (by_len, perm):
+                out, lse = harness.run_step(p, t, num_splits=ns, order=order,
+                                            lse=torch.empty((cfg.B, cfg.H), dtype=torch.float32, device="cuda"))
+                torch.cuda.synchronize()
+                assert torch.equal(out, ref) and torch.equal(lse, lse_ref), f"step {t} splits {ns}"
