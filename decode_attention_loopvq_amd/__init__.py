@@ -20,7 +20,7 @@ from . import layout  # noqa: F401
 
 __all__ = [
     "LvqError", "lvq_geom", "kivi_geom", "make_geom", "make_kivi_geom",
-    "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_request_order",
+    "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_request_order", "lvq_window_append",
     "lvq_decode_attn_splits", "lvq_quant_partial", "lvq_quant_partial_workspace", "lvq_window_partial", "splitk_lse_merge", "kivi_append",
     "kivi_decode_attn_workspace", "kivi_decode_attn", "KiviCache", "layout",
 ]
@@ -207,6 +207,22 @@ def lvq_request_order(seq_len: torch.Tensor, max_len: int, out: Optional[torch.T
     check(lib.lvq_request_order(seq_len.data_ptr(), int(B), int(max_len), out.data_ptr(), _stream(stream)),
           "lvq_request_order")
     return out
+
+
+def lvq_window_append(g: lvq_geom, step: int, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
+                      cache, max_len: int, stream=None):
+    """One generated token (bf16 [B][H][D] pre-RoPE K and/or V of loop step `step`) into the window
+    of `cache` (a layout.LoopVQCache) at position seq_len[b] - 1."""
+    B = cache.B
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        if x is not None:
+            _need(x, name, torch.bfloat16)
+            if tuple(x.shape) != (B, g.H, g.D):
+                raise ValueError(f"{name} must be [B][H][D]")
+    check(lib.lvq_window_append(C.byref(g), int(step), k_new.data_ptr() if k_new is not None else None,
+                                v_new.data_ptr() if v_new is not None else None, cache.win_k.data_ptr(),
+                                cache.win_v.data_ptr(), cache.seq_len.data_ptr(), int(max_len), int(B),
+                                _stream(stream)), "lvq_window_append")
 
 
 def lvq_decode_attn_splits(g: lvq_geom, B: int, max_len: int) -> int:

@@ -1972,3 +1972,51 @@ extern "C" lvq_status lvq_request_order(const int32_t* seq_len, int32_t B, int32
         hipLaunchKernelGGL(identity_order_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, B, order);
     return check_launch("lvq_request_order");
 }
+
+// ---------------------------------------------------------------------------
+// Window append (LoopVQ page, Figure 5: each generated token's bf16 K and V of a loop step go into the
+// recent window; the oldest page leaves it for the index pool every 8 tokens).  Position
+// p = seq_len[b] - 1 (the caller has counted the new token) goes to window slot p for p < sink, else
+// sink + (p - sink) mod (W + page); one 16-byte chunk per thread.
+// ---------------------------------------------------------------------------
+namespace lvq {
+namespace {
+__global__ void window_append_kernel(Geo g, int step, const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+                                     uint4* __restrict__ win_k, uint4* __restrict__ win_v,
+                                     const int32_t* __restrict__ seq_len, int B, int max_len) {
+    constexpr int D = 128, CH = D / 8;              // 16-byte chunks per row
+    const long e = long(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (e >= long(B) * g.H * CH) return;
+    const int ch = int(e % CH), h = int((e / CH) % g.H), b = int(e / (long(CH) * g.H));
+    const int p = min(seq_len[b], max_len) - 1;
+    if (p < 0) return;
+    const int slot = p < g.sink ? p : g.sink + (p - g.sink) % (g.W + g.page);
+    const long dst = (((long(b) * g.T + step) * g.H + h) * g.Wcap + slot) * CH + ch;
+    const long src = (long(b) * g.H + h) * CH + ch;
+    if (k_new) win_k[dst] = k_new[src];
+    if (v_new) win_v[dst] = v_new[src];
+}
+}  // namespace
+}  // namespace lvq
+
+extern "C" lvq_status lvq_window_append(const lvq_geom* gp, int32_t step, const void* k_new, const void* v_new,
+                                        void* win_k, void* win_v, const int32_t* seq_len, int32_t max_len,
+                                        int32_t B, hipStream_t stream) {
+    Geo g;
+    lvq_status st = validate_geom(gp, &g);
+    if (st != LVQ_OK) return st;
+    LVQ_REQUIRE(step >= 0 && step < g.T, LVQ_ERR_INVALID_ARG, "lvq_window_append: step %d out of [0,%d)", step, g.T);
+    LVQ_REQUIRE(B >= 0 && max_len >= 1, LVQ_ERR_INVALID_ARG, "lvq_window_append: B=%d max_len=%d", B, max_len);
+    if (B == 0) return LVQ_OK;
+    LVQ_REQUIRE(k_new || v_new, LVQ_ERR_INVALID_ARG, "lvq_window_append: k_new and v_new both NULL");
+    LVQ_REQUIRE((!k_new || win_k) && (!v_new || win_v) && seq_len, LVQ_ERR_INVALID_ARG,
+                "lvq_window_append: NULL window or seq_len");
+    const bool aligned = (reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+                          reinterpret_cast<uintptr_t>(win_k) | reinterpret_cast<uintptr_t>(win_v)) % 16 == 0;
+    LVQ_REQUIRE(aligned, LVQ_ERR_INVALID_ARG, "lvq_window_append: buffers must be 16-byte aligned");
+    const long n = long(B) * g.H * (g.D / 8);
+    hipLaunchKernelGGL(window_append_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, g, step,
+                       static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), static_cast<uint4*>(win_k),
+                       static_cast<uint4*>(win_v), seq_len, int(B), int(max_len));
+    return check_launch("lvq_window_append");
+}

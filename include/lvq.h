@@ -233,6 +233,20 @@ LVQ_API lvq_status lvq_decode_attn(const lvq_geom* g, int32_t step, const void* 
                            void* ws, size_t ws_bytes, int32_t num_splits, int32_t B,
                            hipStream_t stream);
 
+/*
+ * Append one generated token to the bf16 window of loop step `step` (the LoopVQ page, Figure 5: each new
+ * token's pre-RoPE K and V of every loop step enter the recent window; after every 8 generated tokens
+ * the window's oldest page is encoded into the pool with lvq_encode, reading the window through its
+ * strides, and leaves it).  For each request b the token is position p = min(seq_len[b], max_len) - 1,
+ * i.e. seq_len already counts it (nothing is written when p < 0); it goes to window slot p for
+ * p < sink, else sink + (p - sink) mod (window + page) of win_k / win_v [B][T][H][sink+window+page][D].
+ *  k_new, v_new  bf16 [B][H][D] pre-RoPE (either may be NULL to skip), 16-byte aligned.
+ * Errors: LVQ_ERR_INVALID_ARG for a bad step, B < 0, max_len < 1, NULL or misaligned buffers.
+ */
+LVQ_API lvq_status lvq_window_append(const lvq_geom* g, int32_t step, const void* k_new, const void* v_new,
+                                     void* win_k, void* win_v, const int32_t* seq_len, int32_t max_len,
+                                     int32_t B, hipStream_t stream);
+
 /* What lvq_decode_attn runs for num_splits = 0: -1 for the single-pass kernel, else its split count
  * (0 on bad arguments). */
 LVQ_API int32_t lvq_decode_attn_splits(const lvq_geom* g, int32_t B, int32_t max_len);

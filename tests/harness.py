@@ -76,12 +76,12 @@ def build_loopvq(cfg: LoopVQConfig, device="cuda", keep: Sequence[Tuple[int, int
                          syn.softmax_scale(cfg), raw)
 
 
-def _fill_window(cache: LoopVQCache, beta: int, x: torch.Tensor, kind: str):
+def _fill_window(cache: LoopVQCache, beta: int, x: torch.Tensor, kind: str, lengths=None):
     g = cache.g
     win = cache.win_k if kind == "k" else cache.win_v
     from decode_attention_loopvq_amd.layout import window_positions, window_slot
     groups: Dict[int, List[int]] = {}
-    for b, L in enumerate(cache.lengths):
+    for b, L in enumerate(cache.lengths if lengths is None else lengths):
         groups.setdefault(L, []).append(b)
     for L, bs in groups.items():
         pos = window_positions(L, g)

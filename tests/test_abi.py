@@ -167,3 +167,17 @@ def test_request_order_rejects():
     assert f(None, 4, 100, FAKE, None) == INVALID
     assert f(FAKE, 4, 100, None, None) == INVALID
     assert f(None, 0, 100, None, None) == OK
+
+
+def test_window_append_rejects():
+    """Argument checks of lvq_window_append (all fail before any launch); B = 0 is a no-op."""
+    g = _geom(T=4, Tc=2)
+    f = _lib.lib.lvq_window_append
+    gp = C.byref(g)
+    assert f(gp, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 2, None) == INVALID      # step out of range
+    assert f(gp, 0, None, None, FAKE, FAKE, FAKE, 100, 2, None) == INVALID      # nothing to append
+    assert f(gp, 0, FAKE, FAKE, None, FAKE, FAKE, 100, 2, None) == INVALID      # no window
+    assert f(gp, 0, FAKE, FAKE, FAKE, FAKE, None, 100, 2, None) == INVALID      # no lengths
+    assert f(gp, 0, C.c_void_p(4098), None, FAKE, None, FAKE, 100, 2, None) == INVALID   # misaligned
+    assert f(gp, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, None) == INVALID        # max_len < 1
+    assert f(gp, 0, None, None, None, None, None, 100, 0, None) == OK
