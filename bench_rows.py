@@ -18,6 +18,7 @@ roofline that bounds it, and prints one JSON line per measurement:
   kivi-prefill     kivi_append of a 4K prompt (B=16, H=32)
   kivi-append      kivi_append of one decode token
   kivi-attn        kivi_decode_attn after the 4K prefill
+  kmeans-step      one Fisher-weighted k-means step (lvq_encode + lvq_codebook_update), 16 x 2048 tokens
 
 Inputs are seeded and synthetic (synth/), timed with HIP events on the
 launch stream after warm-up.  Peaks: HBM 8 TB/s, dense bf16 MFMA
@@ -98,6 +99,45 @@ def encode_rows(reps):
     emit(row="encode-page", workload=cfg.name, B=cfg.B, H=cfg.H, us=round(t * 1e6, 2),
          codebook_gbps=round(cb_bytes / t / 1e9, 1), codebook_bytes=cb_bytes)
     del xs
+
+
+def kmeans_row(reps):
+    """One Fisher-weighted k-means step (assignment by lvq_encode, weighted means by
+    lvq_codebook_update), every loop block, K and V, on a calibration set of the page's size: 16
+    sequences of 2048 tokens (the 6K workload's geometry), log-normal stand-in weights."""
+    import torch
+    import decode_attention_loopvq_amd as lvq
+    import synth.loopvq as syn
+    from synth.configs import loopvq_config
+    from tests import harness
+
+    cfg = loopvq_config("loopvq-b64-6k", B=16, L=2048)
+    p = harness.build_loopvq(cfg)
+    g, c = p.g, p.cache
+    xs = {kind: dict(syn.raw_blocks(cfg, kind, "cuda")) for kind in ("k", "v")}
+    NG = g.D // (g.G // g.Tc)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    w = {kind: torch.exp(torch.randn((cfg.B, cfg.H, cfg.L, NG), generator=gen, device="cuda")) for kind in "kv"}
+    cb = p.codebooks.clone()
+
+    def step():
+        for beta in range(g.T // g.Tc):
+            lvq.lvq_encode(g, beta, xs["k"][beta], xs["v"][beta], cb, c.pool, c.page_table, c.first_page,
+                           c.n_pages_dev, c.max_pages, x_tok0=c.tok0)
+            lvq.lvq_codebook_update(g, beta, xs["k"][beta], xs["v"][beta], w["k"], w["v"], cb, c.pool,
+                                    c.page_table, c.first_page, c.n_pages_dev, c.max_pages, x_tok0=c.tok0)
+
+    def update_only():
+        for beta in range(g.T // g.Tc):
+            lvq.lvq_codebook_update(g, beta, xs["k"][beta], xs["v"][beta], w["k"], w["v"], cb, c.pool,
+                                    c.page_table, c.first_page, c.n_pages_dev, c.max_pages, x_tok0=c.tok0)
+
+    t = timed(step, reps)
+    t_upd = timed(update_only, reps)
+    n_vec = sum(c.n_pages) * g.page * g.H * NG * 2 * (g.T // g.Tc)
+    emit(row="kmeans-step", workload="loopvq-b64-6k geometry, 16 x 2048-token calibration set", B=cfg.B,
+         H=cfg.H, L=cfg.L, us=round(t * 1e6, 2), update_us=round(t_upd * 1e6, 2), coupled_vectors=n_vec,
+         vectors_per_s=round(n_vec / t, 1), assign_flops=2.0 * g.K * g.G * n_vec)
 
 
 def attn_row(name, cfg_name, steps, reps, **over):
@@ -193,11 +233,11 @@ def kivi_rows(reps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--reps", type=int, default=5)
-    ap.add_argument("--only", nargs="*", default=None, help="encode attn-32k attn-deep attn-1k kivi")
+    ap.add_argument("--only", nargs="*", default=None, help="encode attn-32k attn-deep attn-1k kivi kmeans")
     args = ap.parse_args()
     import torch
     assert torch.cuda.is_available(), "bench_rows.py needs a GPU"
-    want = set(args.only) if args.only else {"encode", "attn-32k", "attn-deep", "attn-1k", "kivi"}
+    want = set(args.only) if args.only else {"encode", "attn-32k", "attn-deep", "attn-1k", "kivi", "kmeans"}
     if "encode" in want:
         encode_rows(args.reps)
     if "attn-32k" in want:
@@ -208,6 +248,8 @@ def main():
         attn_row("attn-1k", "loopvq-b1-1k-fp32cb", range(4), args.reps * 20)
     if "kivi" in want:
         kivi_rows(args.reps)
+    if "kmeans" in want:
+        kmeans_row(args.reps)
 
 
 if __name__ == "__main__":

@@ -21,6 +21,7 @@ from . import layout  # noqa: F401
 __all__ = [
     "LvqError", "lvq_geom", "kivi_geom", "make_geom", "make_kivi_geom",
     "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_request_order", "lvq_window_append",
+    "lvq_codebook_update",
     "lvq_decode_attn_splits", "lvq_quant_partial", "lvq_quant_partial_workspace", "lvq_window_partial", "splitk_lse_merge", "kivi_append",
     "kivi_decode_attn_workspace", "kivi_decode_attn", "KiviCache", "layout",
 ]
@@ -135,6 +136,48 @@ def lvq_encode(g: lvq_geom, block: int, x_k: Optional[torch.Tensor], x_v: Option
                          pool.data_ptr(), page_table.data_ptr(), int(page_table.shape[-1]),
                          first_page.data_ptr(), n_pages.data_ptr(), int(B), int(max_pages), _stream(stream)),
           "lvq_encode")
+
+
+def lvq_codebook_update(g: lvq_geom, block: int, x_k: Optional[torch.Tensor], x_v: Optional[torch.Tensor],
+                        w_k: Optional[torch.Tensor], w_v: Optional[torch.Tensor], codebooks: torch.Tensor,
+                        pool: torch.Tensor, page_table: torch.Tensor, first_page: torch.Tensor,
+                        n_pages: torch.Tensor, max_pages: int, x_tok0: Optional[torch.Tensor] = None,
+                        stream=None):
+    """One weighted k-means step for loop block `block` (after lvq_encode of the same pages).
+
+    x_k / x_v: bf16 [B][H][N][Tc][D] views as for lvq_encode; w_k / w_v: fp32 [B][H][N][NG] views
+    (unit stride on the group) holding the weight of each coupled vector; codebooks updated in place."""
+    xs = [x for x in (x_k, x_v) if x is not None]
+    if not xs:
+        raise ValueError("x_k and x_v are both None")
+    ws_list = []
+    for name, x, wname, w in (("x_k", x_k, "w_k", w_k), ("x_v", x_v, "w_v", w_v)):
+        if x is None:
+            continue
+        _need(x, name, torch.bfloat16, contiguous=False)
+        if x.dim() != 5 or x.shape[-1] != g.D or x.stride(-1) != 1:
+            raise ValueError(f"{name} must be [B][H][N][Tc][D] with unit stride on D")
+        if w is None:
+            raise ValueError(f"{wname} is required with {name}")
+        _need(w, wname, torch.float32, contiguous=False)
+        if w.dim() != 4 or tuple(w.shape[:3]) != tuple(x.shape[:3]) or w.stride(-1) != 1:
+            raise ValueError(f"{wname} must be [B][H][N][NG] matching {name}, unit stride on the group")
+        ws_list.append(w)
+    if x_k is not None and x_v is not None and (x_k.stride() != x_v.stride() or w_k.stride() != w_v.stride()):
+        raise ValueError("K and V inputs must share strides")
+    xstr = (C.c_int64 * 4)(*xs[0].stride()[:4])
+    wstr = (C.c_int64 * 3)(*ws_list[0].stride()[:3])
+    _need(codebooks, "codebooks", _cb_torch_dtype(g))
+    B = first_page.numel()
+    check(lib.lvq_codebook_update(C.byref(g), int(block), x_k.data_ptr() if x_k is not None else None,
+                                  x_v.data_ptr() if x_v is not None else None, xstr,
+                                  x_tok0.data_ptr() if x_tok0 is not None else None,
+                                  w_k.data_ptr() if w_k is not None else None,
+                                  w_v.data_ptr() if w_v is not None else None, wstr, codebooks.data_ptr(),
+                                  pool.data_ptr(), page_table.data_ptr(), int(page_table.shape[-1]),
+                                  first_page.data_ptr(), n_pages.data_ptr(), int(B), int(max_pages),
+                                  _stream(stream)),
+          "lvq_codebook_update")
 
 
 def lvq_decode_attn_workspace(g: lvq_geom, B: int, max_len: int, num_splits: int = 0) -> int:

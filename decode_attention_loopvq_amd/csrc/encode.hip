@@ -515,3 +515,299 @@ extern "C" lvq_status lvq_encode(const lvq_geom* g, int32_t block, const void* x
                            first_page, n_pages);
     return check_launch("lvq_encode");
 }
+
+// ---------------------------------------------------------------------------
+// Weighted codebook update: one Lloyd step of Fisher-weighted k-means (LoopVQ page: background
+// "Fisher-weighted k-means" and "method steps" step 2).  The assignment is the encoder's (a scalar
+// weight scales all of a sample's distances alike, so the nearest codeword does not depend on it): run
+// lvq_encode on the calibration pages first.  Then every coupled vector z of those pages, with weight w,
+// adds w*z and w to the sums of the codeword its page holds, and each codeword of loop block `block`
+// becomes sum(w z) / sum(w), rounded once to the codebook dtype, or keeps its value when its cluster's
+// weight sum is not positive.
+//
+// The sums are exact fixed-point integers, not float atomics (on this chip an fp32 add to LDS runs at
+// about 1/40 of the rate of an integer one).  A workgroup first scans its samples for a = max |w z_k|
+// and m = max |w| and counts them (N); then w*z (exact in fp64: a 24-bit times an 8-bit significand) is
+// scaled by 2^e with N * a * 2^e < 2^51, rounded to the nearest integer and added into a 64-bit LDS
+// sum, likewise w with its own 2^ew.  No sum can reach 2^52, each addend is off by at most 2^-e / 2
+// (relative 2^-52 of the largest term times N), and integer adds commute, so the result does not
+// depend on the order of the adds.  A NaN or infinite weight or coordinate makes the whole group's
+// codebook NaN.
+// ---------------------------------------------------------------------------
+namespace lvq {
+namespace {
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;          // NaN stays NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+// Round a double once to bf16 (nearest, ties to even).  The fp32 step rounds to nearest too; where it
+// lands exactly halfway between two bf16 values without d being there, nudge it one fp32 step towards
+// d so that the second rounding goes the way d does.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
+    const float f = float(d);
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0xffffu) == 0x8000u && double(f) != d) u = fabs(d) > fabs(double(f)) ? u + 1 : u - 1;
+    return f32_to_bf16_rne(__uint_as_float(u));
+}
+
+// x * 2^e rounded to the nearest integer (ties to even), for |x| < 2^51: adding 1.5 * 2^52 leaves the
+// integer in the low significand bits.
+__device__ __forceinline__ long long round_to_int(double x) {
+    constexpr double kMagic = 6755399441055744.0;                     // 1.5 * 2^52
+    return __double_as_longlong(x + kMagic) - __double_as_longlong(kMagic);
+}
+
+// Scale exponent for N terms of magnitude at most `amax`: the largest e with N * amax * 2^e < 2^51.
+__device__ __forceinline__ int sum_exponent(double amax, long n) {
+    if (!(amax > 0.0)) return 0;
+    int ex;
+    frexp(amax * double(n) * (1.0 + 0x1p-20), &ex);                   // amax * n < 2^ex
+    return 51 - ex;
+}
+
+// One workgroup per (head, K|V, group): its threads take the sampled tokens of all requests in turn
+// (request b, page slot, token of the page) and, after a barrier, turn the 256 sums into codewords.  No
+// other workgroup touches them.
+//
+// A group's channels are 2c bytes of each 256-byte step row, so the NG workgroups of one (head, K|V)
+// read the same cache lines.  Workgroups go to the 8 XCDs round-robin by linear id; with XCD_MAP the id
+// is split as (slot s = id / 8, XCD x = id % 8) and the (head, K|V) pair x + 8 * (s / NG) takes group
+// s % NG, so that all groups of one pair run on one XCD and share its L2 (needs 2H % 8 == 0).
+// VEC: a group's c channels of one step are read as one 2c-byte load (x 2c-byte aligned, strides
+// multiples of c).
+constexpr int kKmThreads = 1024;
+
+template <int C>
+struct VecOf;
+template <>
+struct VecOf<4> { using type = uint2; };
+template <>
+struct VecOf<8> { using type = uint4; };
+
+// The G coordinates of one token's coupled vector as floats in slots z[0 .. G-1] (fixed slots, so that
+// z stays in registers).  VEC_C > 0: slot m*c + i holds step m, channel g*c + i (one vector load per
+// step); otherwise slot k holds coordinate k.  km_coord gives the coordinate of a slot: coordinate
+// i*Tc + m <- step m, channel g*c + i.
+template <int VEC_C>
+__device__ __forceinline__ void load_coupled(const uint16_t* xb, long s3, int Tc, int G, float (&z)[32]) {
+    if constexpr (VEC_C > 0) {
+        using V = typename VecOf<VEC_C>::type;
+        constexpr int kMaxTc = 32 / VEC_C;
+#pragma unroll
+        for (int m = 0; m < kMaxTc; ++m) {
+            if (m < Tc) {
+                const V v = *reinterpret_cast<const V*>(xb + long(m) * s3);
+                const uint32_t* u = reinterpret_cast<const uint32_t*>(&v);
+#pragma unroll
+                for (int i = 0; i < VEC_C; ++i)
+                    z[m * VEC_C + i] = bf16_to_f32(uint16_t(i & 1 ? u[i >> 1] >> 16 : u[i >> 1] & 0xffffu));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+            if (k < G) z[k] = bf16_to_f32(xb[long(k % Tc) * s3 + k / Tc]);
+    }
+}
+
+template <int VEC_C>
+__device__ __forceinline__ int km_coord(int k, int Tc) {
+    if constexpr (VEC_C > 0) return (k % VEC_C) * Tc + k / VEC_C;
+    else return k;
+}
+
+template <typename CB, bool XCD_MAP, int VEC_C>
+__global__ void __launch_bounds__(kKmThreads) kmeans_update_kernel(
+        Geo geo, int block, const uint16_t* __restrict__ xk, const uint16_t* __restrict__ xv, long s0, long s1,
+        long s2, long s3, const int64_t* __restrict__ tok0, const float* __restrict__ wk,
+        const float* __restrict__ wv, long w0, long w1, long w2, const uint8_t* __restrict__ pool,
+        const int32_t* __restrict__ pt, int pt_stride, const int32_t* __restrict__ first_page,
+        const int32_t* __restrict__ n_pages, int B, int max_pages, CB* __restrict__ cb) {
+    __shared__ unsigned long long sums[256 * 33];   // [K][G + 1]: sum of w z (G) and of w, fixed point
+    __shared__ unsigned long long bound[2];         // max |w z_k|, max |w| (non-negative doubles as bits)
+    __shared__ uint32_t nonfinite;
+    const int NG = geo.NG, c = geo.c, Tc = geo.Tc, G = geo.G, K = geo.K;
+    int g, pair;
+    if constexpr (XCD_MAP) {
+        const int id = blockIdx.x, slot = id >> 3;
+        g = slot % NG;
+        pair = (id & 7) + 8 * (slot / NG);
+    } else {
+        g = blockIdx.x % NG;
+        pair = blockIdx.x / NG;
+    }
+    const int h = pair >> 1, kv = pair & 1;
+    const uint16_t* x = kv == 0 ? xk : xv;
+    const float* wt = kv == 0 ? wk : wv;
+    if (x == nullptr) return;
+    for (int e = threadIdx.x; e < K * (G + 1); e += kKmThreads) sums[e] = 0ull;
+    if (threadIdx.x == 0) {
+        bound[0] = bound[1] = 0ull;
+        nonfinite = 0u;
+    }
+    __syncthreads();
+
+    // pass 1: bounds and sample count
+    long n_tok = 0;
+    double amax = 0.0, wmax = 0.0;
+    bool bad = false;
+    for (int b = 0; b < B; ++b) {
+        const int np = min(n_pages[b], max_pages);
+        const long row0 = tok0 ? tok0[b] : 0;
+        n_tok += long(np) * geo.page;
+        for (int j = threadIdx.x; j < np * geo.page; j += kKmThreads) {
+            const long row = row0 + j;
+            const float w = wt[long(b) * w0 + long(h) * w1 + row * w2 + g];
+            float z[32];
+            load_coupled<VEC_C>(x + long(b) * s0 + long(h) * s1 + row * s2 + g * c, s3, Tc, G, z);
+            float zmax = 0.f;
+            bool zbad = false;
+#pragma unroll
+            for (int k = 0; k < 32; ++k)
+                if (k < G) {
+                    zmax = fmaxf(zmax, fabsf(z[k]));
+                    zbad |= !(fabsf(z[k]) <= 3.4028235e38f);
+                }
+            bad |= zbad || !(fabsf(w) <= 3.4028235e38f);
+            amax = fmax(amax, double(fabsf(w)) * double(zmax));
+            wmax = fmax(wmax, double(fabsf(w)));
+        }
+    }
+    if (bad) atomicOr(&nonfinite, 1u);
+    for (int off = 32; off > 0; off >>= 1) {
+        amax = fmax(amax, __shfl_xor(amax, off));
+        wmax = fmax(wmax, __shfl_xor(wmax, off));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        atomicMax(&bound[0], static_cast<unsigned long long>(__double_as_longlong(amax)));
+        atomicMax(&bound[1], static_cast<unsigned long long>(__double_as_longlong(wmax)));
+    }
+    __syncthreads();
+    const int ez = sum_exponent(__longlong_as_double(static_cast<long long>(bound[0])), n_tok);
+    const int ew = sum_exponent(__longlong_as_double(static_cast<long long>(bound[1])), n_tok);
+    const double scale_z = ldexp(1.0, ez), scale_w = ldexp(1.0, ew);
+
+    // pass 2: fixed-point sums per codeword
+    if (nonfinite == 0u) {
+        const long blk_off = ((long(block) * geo.H + h) * 2 + kv) * geo.page * NG;
+        for (int b = 0; b < B; ++b) {
+            const int np = min(n_pages[b], max_pages), fp = first_page[b];
+            const long row0 = tok0 ? tok0[b] : 0;
+            for (int j = threadIdx.x; j < np * geo.page; j += kKmThreads) {
+                const int slot = j / geo.page, i_tok = j % geo.page;
+                const int lp = fp + slot;
+                const long row = row0 + j;
+                // the page id, the token's data and its weight are loaded together; only the index byte waits
+                const long phys = pt[long(b) * pt_stride + lp];
+                const float w = wt[long(b) * w0 + long(h) * w1 + row * w2 + g];
+                float z[32];
+                load_coupled<VEC_C>(x + long(b) * s0 + long(h) * s1 + row * s2 + g * c, s3, Tc, G, z);
+                const int tau = slot_token(lp, i_tok, geo.page);
+                const int byte = kv == 0 ? g : (g ^ (tau & 15));     // value rows XOR-rotated (lvq.h)
+                const int r = pool[phys * geo.page_bytes + blk_off + i_tok * NG + byte];
+                unsigned long long* acc = sums + r * (G + 1);
+                const double wz = double(w) * scale_z;                // exact: a power-of-two scale
+#pragma unroll
+                for (int k = 0; k < 32; ++k)
+                    if (k < G)
+                        atomicAdd(acc + km_coord<VEC_C>(k, Tc),
+                                  static_cast<unsigned long long>(round_to_int(wz * double(z[k]))));
+                atomicAdd(acc + G, static_cast<unsigned long long>(round_to_int(double(w) * scale_w)));
+            }
+        }
+    }
+    __syncthreads();
+    CB* out = cb + ((((long(block) * geo.H + h) * 2 + kv) * NG + g) * K) * G;
+    const bool all_nan = nonfinite != 0u;
+    for (int e = threadIdx.x; e < K * G; e += kKmThreads) {
+        const int r = e / G, k = e % G;
+        double v;
+        if (all_nan) {
+            v = __longlong_as_double(0x7ff8000000000000LL);
+        } else {
+            const long long den = static_cast<long long>(sums[r * (G + 1) + G]);
+            if (den <= 0) continue;                                   // empty cluster: the codeword stays
+            v = ldexp(double(static_cast<long long>(sums[r * (G + 1) + k])) / double(den), ew - ez);
+        }
+        if constexpr (std::is_same<CB, uint16_t>::value) out[e] = f64_to_bf16_rne(v);
+        else out[e] = float(v);
+    }
+}
+
+struct KmArgs {
+    Geo geo;
+    int block;
+    const uint16_t *xk, *xv;
+    long s0, s1, s2, s3;
+    const int64_t* tok0;
+    const float *wk, *wv;
+    long w0, w1, w2;
+    const uint8_t* pool;
+    const int32_t* pt;
+    int pt_stride;
+    const int32_t *first_page, *n_pages;
+    int B, max_pages;
+};
+
+template <typename CB, bool XCD_MAP, int VEC_C>
+void launch_kmeans(const KmArgs& a, void* cb, hipStream_t stream) {
+    const dim3 grid(unsigned(a.geo.NG * 2 * a.geo.H));
+    hipLaunchKernelGGL((kmeans_update_kernel<CB, XCD_MAP, VEC_C>), grid, dim3(kKmThreads), 0, stream, a.geo,
+                       a.block, a.xk, a.xv, a.s0, a.s1, a.s2, a.s3, a.tok0, a.wk, a.wv, a.w0, a.w1, a.w2, a.pool,
+                       a.pt, a.pt_stride, a.first_page, a.n_pages, a.B, a.max_pages, static_cast<CB*>(cb));
+}
+
+template <typename CB, bool XCD_MAP>
+void launch_kmeans_vec(const KmArgs& a, int vec_c, void* cb, hipStream_t stream) {
+    if (vec_c == 8) launch_kmeans<CB, XCD_MAP, 8>(a, cb, stream);
+    else if (vec_c == 4) launch_kmeans<CB, XCD_MAP, 4>(a, cb, stream);
+    else launch_kmeans<CB, XCD_MAP, 0>(a, cb, stream);
+}
+
+template <typename CB>
+void launch_kmeans_map(const KmArgs& a, int vec_c, void* cb, hipStream_t stream) {
+    if ((2 * a.geo.H) % 8 == 0) launch_kmeans_vec<CB, true>(a, vec_c, cb, stream);
+    else launch_kmeans_vec<CB, false>(a, vec_c, cb, stream);
+}
+
+}  // namespace
+}  // namespace lvq
+
+extern "C" lvq_status lvq_codebook_update(const lvq_geom* g, int32_t block, const void* x_k, const void* x_v,
+                                          const int64_t x_strides[4], const int64_t* x_tok0, const float* w_k,
+                                          const float* w_v, const int64_t w_strides[3], void* codebooks,
+                                          const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
+                                          const int32_t* first_page, const int32_t* n_pages, int32_t B,
+                                          int32_t max_pages, hipStream_t stream) {
+    Geo geo;
+    lvq_status st = validate_geom(g, &geo);
+    if (st != LVQ_OK) return st;
+    LVQ_REQUIRE(block >= 0 && block < geo.NB, LVQ_ERR_INVALID_ARG, "lvq_codebook_update: block %d out of [0,%d)",
+                block, geo.NB);
+    LVQ_REQUIRE(x_k || x_v, LVQ_ERR_INVALID_ARG, "lvq_codebook_update: both x_k and x_v are NULL");
+    LVQ_REQUIRE((!x_k || w_k) && (!x_v || w_v), LVQ_ERR_INVALID_ARG, "lvq_codebook_update: missing weights");
+    LVQ_REQUIRE(x_strides && w_strides && codebooks && pool && page_table && first_page && n_pages,
+                LVQ_ERR_INVALID_ARG, "lvq_codebook_update: NULL pointer");
+    LVQ_REQUIRE(B >= 0 && max_pages >= 0 && pt_stride >= 0, LVQ_ERR_INVALID_ARG,
+                "lvq_codebook_update: negative size");
+    LVQ_REQUIRE(geo.G <= 32, LVQ_ERR_UNSUPPORTED, "lvq_codebook_update: G=%d (at most 32)", geo.G);
+    LVQ_REQUIRE(long(max_pages) * geo.page <= 0x7fffffffL, LVQ_ERR_UNSUPPORTED, "lvq_codebook_update: too many pages");
+    if (B == 0 || max_pages == 0) return LVQ_OK;
+    KmArgs a{geo, int(block), static_cast<const uint16_t*>(x_k), static_cast<const uint16_t*>(x_v),
+             long(x_strides[0]), long(x_strides[1]), long(x_strides[2]), long(x_strides[3]), x_tok0, w_k, w_v,
+             long(w_strides[0]), long(w_strides[1]), long(w_strides[2]), pool, page_table, int(pt_stride),
+             first_page, n_pages, int(B), int(max_pages)};
+    // one vector load per (token, step) when every row start of every given tensor is 2c-byte aligned
+    int vec_c = (geo.c == 4 || geo.c == 8) ? geo.c : 0;
+    for (const void* p : {x_k, x_v})
+        if (p && reinterpret_cast<uintptr_t>(p) % (2 * geo.c) != 0) vec_c = 0;
+    for (int i = 0; i < 4; ++i)
+        if (vec_c && x_strides[i] % geo.c != 0) vec_c = 0;
+    if (geo.cb == LVQ_BF16) launch_kmeans_map<uint16_t>(a, vec_c, codebooks, stream);
+    else launch_kmeans_map<float>(a, vec_c, codebooks, stream);
+    return check_launch("lvq_codebook_update");
+}

@@ -170,6 +170,36 @@ LVQ_API lvq_status lvq_encode(const lvq_geom* g, int32_t block,
                       int32_t B, int32_t max_pages, hipStream_t stream);
 
 /*
+ * One Lloyd step of Fisher-weighted k-means for the codebooks of loop block `block` (the LoopVQ page:
+ * background "Fisher-weighted k-means" and "method steps" step 2, the codebook initialisation of Eq. 3).
+ * The assignment is the encoder's: call lvq_encode on the calibration pages with the current codebooks
+ * first (a scalar weight per sub-vector scales all of its distances alike, so the nearest codeword does
+ * not depend on it).  Then each coupled vector z of those pages, weight w, adds w*z and w to the sums of
+ * the codeword its page holds, and every codeword of block `block` becomes sum(w z) / sum(w), rounded
+ * once to the codebook dtype (nearest-even); a codeword whose weight sum is not positive keeps its value.
+ * The sums are exact fixed-point integers per (head, K|V, group): each product w*z is rounded to a
+ * multiple of 2^-e with N * max|w z| * 2^e < 2^51 (N the samples of the call), likewise w, so the result
+ * does not depend on the order of the adds and is reproducible bit for bit.  A weight below about
+ * 2^-52 * N times the largest one can round to zero.  A NaN or infinite weight or coordinate turns the
+ * whole codebook of its (head, K|V, group) into NaN.  No workspace.  Requires G <= 32.
+ *
+ *  x_k, x_v, x_strides, x_tok0, page_table, pt_stride, first_page, n_pages, B, max_pages: as for
+ *            lvq_encode (the same pages it encoded); either of x_k / x_v may be NULL to skip K or V.
+ *  w_k, w_v  fp32 weights (>= 0) of the key / value sub-vectors: the weight of group g of token row
+ *            `row` (x_tok0[b] + j, as for x) of request b, head h is
+ *            w[b*w_strides[0] + h*w_strides[1] + row*w_strides[2] + g] (strides in elements); required
+ *            with the matching x.
+ *  codebooks the full codebooks (layout above), updated in place for block `block` only.
+ * Errors: LVQ_ERR_INVALID_ARG for a bad block, sizes or NULL pointers, LVQ_ERR_UNSUPPORTED for G > 32.
+ */
+LVQ_API lvq_status lvq_codebook_update(const lvq_geom* g, int32_t block, const void* x_k, const void* x_v,
+                                       const int64_t x_strides[4], const int64_t* x_tok0, const float* w_k,
+                                       const float* w_v, const int64_t w_strides[3], void* codebooks,
+                                       const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
+                                       const int32_t* first_page, const int32_t* n_pages, int32_t B,
+                                       int32_t max_pages, hipStream_t stream);
+
+/*
  * Bytes of workspace lvq_decode_attn needs for B requests of length at most
  * max_len with the given split count (0 = the library's choice, -1 = the
  * single-pass kernel).

@@ -181,3 +181,28 @@ def test_window_append_rejects():
     assert f(gp, 0, C.c_void_p(4098), None, FAKE, None, FAKE, 100, 2, None) == INVALID   # misaligned
     assert f(gp, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, None) == INVALID        # max_len < 1
     assert f(gp, 0, None, None, None, None, None, 100, 0, None) == OK
+
+
+def test_codebook_update_rejects():
+    """Argument checks of lvq_codebook_update (all fail before any launch)."""
+    g = _geom(T=4, Tc=2)
+    gp = C.byref(g)
+    f = _lib.lib.lvq_codebook_update
+    xs = (C.c_int64 * 4)(1, 1, 1, 1)
+    wst = (C.c_int64 * 3)(1, 1, 1)
+
+    def call(**o):
+        a = dict(block=0, xk=FAKE, xv=FAKE, xs=xs, tok0=None, wk=FAKE, wv=FAKE, wst=wst, cb=FAKE, pool=FAKE,
+                 pt=FAKE, pts=10, first=FAKE, n=FAKE, B=2, maxp=3)
+        a.update(o)
+        return f(gp, a["block"], a["xk"], a["xv"], a["xs"], a["tok0"], a["wk"], a["wv"], a["wst"], a["cb"],
+                 a["pool"], a["pt"], a["pts"], a["first"], a["n"], a["B"], a["maxp"], None)
+
+    assert call(block=2) == INVALID
+    assert call(xk=None, xv=None) == INVALID
+    assert call(wk=None) == INVALID
+    assert call(cb=None) == INVALID
+    assert call(B=-1) == INVALID
+    assert call(maxp=-1) == INVALID
+    assert call(B=0) == OK
+    assert call(maxp=0) == OK
