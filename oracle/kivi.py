@@ -148,7 +148,8 @@ class KiviState:
     D: int = 128
     group: int = 32
     R: int = 128
-    bits: int = 2
+    bits: int = 2                 # key code width
+    v_bits: int = 0               # value code width (0: the same as the keys')
     k_codes: List[np.ndarray] = field(default_factory=list)   # blocks of [group][D]
     k_s: List[np.ndarray] = field(default_factory=list)       # blocks of [D]
     k_z: List[np.ndarray] = field(default_factory=list)
@@ -181,7 +182,7 @@ class KiviState:
 
     def _flush_values(self, n_rows: int):
         block = np.stack(self.v_res[:n_rows]).astype(F16)
-        codes, s, z = quantize_values(block, self.group, self.bits)
+        codes, s, z = quantize_values(block, self.group, self.v_bits or self.bits)
         for j in range(n_rows):
             self.v_codes.append(codes[j])
             self.v_s.append(s[j])

@@ -48,14 +48,15 @@ def _groups(seed, n=2000, size=32, scale=1.0):
     return (rng.standard_normal((n, size)) * scale).astype(np.float16)
 
 
+@pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("scale", [1.0, 20.0, 1e-3])
-def test_codes_in_range_and_error_bound(scale):
-    """Every code lies in [0, 3]; |x - x_hat| <= s/2 + s|z - z_exact| + a few
+def test_codes_in_range_and_error_bound(scale, bits):
+    """Every code lies in [0, 2^b - 1]; |x - x_hat| <= s/2 + s|z - z_exact| + a few
     ulps, where z_exact = -min/s before fp16 rounding."""
     for x in _groups(1, scale=scale):
-        s, z = kv.group_params(x)
-        q = kv.quantize(x, s, z)
-        assert q.min() >= 0 and q.max() <= 3
+        s, z = kv.group_params(x, bits)
+        q = kv.quantize(x, s, z, bits)
+        assert q.min() >= 0 and q.max() <= 2 ** bits - 1
         xh = kv.dequantize(q, s, z).astype(np.float64)
         xf = x.astype(np.float64)
         z_exact = -xf.min() / float(s)
@@ -63,35 +64,72 @@ def test_codes_in_range_and_error_bound(scale):
         assert np.abs(xf - xh).max() <= bound
 
 
-def test_end_points_map_to_extreme_codes():
-    """min -> 0 and max -> 3 unless fp16 rounding of z moves the value across a
+@pytest.mark.parametrize("bits", [2, 4])
+def test_end_points_map_to_extreme_codes(bits):
+    """min -> 0 and max -> 2^b - 1 unless fp16 rounding of z moves the value across a
     rounding boundary (checked by recomputing with the exact z)."""
-    n_checked = 0
+    top = 2 ** bits - 1
+    n_checked = n_top = 0
     for x in _groups(2):
-        s, z = kv.group_params(x)
-        q = kv.quantize(x, s, z)
+        s, z = kv.group_params(x, bits)
+        q = kv.quantize(x, s, z, bits)
         xf = x.astype(np.float32)
         u_min = np.float32(np.float32(xf.min()) / np.float32(s)) + np.float32(z)
         u_max = np.float32(np.float32(xf.max()) / np.float32(s)) + np.float32(z)
         if abs(u_min) < 0.49:
             assert q[np.argmin(xf)] == 0
             n_checked += 1
-        if abs(u_max - 3) < 0.49:
-            assert q[np.argmax(xf)] == 3
-    assert n_checked > 1500
+        if abs(u_max - top) < 0.49:
+            assert q[np.argmax(xf)] == top
+            n_top += 1
+    assert n_checked > 1500 and n_top > 1500
 
 
-def test_exactly_representable_group_is_lossless():
+@pytest.mark.parametrize("bits", [2, 4])
+def test_exactly_representable_group_is_lossless(bits):
     rng = np.random.default_rng(3)
+    top = 2 ** bits - 1
     for _ in range(200):
         s = float(2.0 ** rng.integers(-4, 4))
         a = float(rng.integers(-8, 8)) * s     # min on the grid so z = -a/s is an integer
-        levels = np.array([0, 1, 2, 3])
+        levels = np.arange(top + 1)
         x = (a + s * rng.choice(levels, size=32)).astype(np.float16)
-        x[0], x[1] = a, a + 3 * s            # make min and max exact
-        s16, z16 = kv.group_params(x)
-        q = kv.quantize(x, s16, z16)
+        x[0], x[1] = a, a + top * s          # make min and max exact
+        s16, z16 = kv.group_params(x, bits)
+        q = kv.quantize(x, s16, z16, bits)
         np.testing.assert_array_equal(kv.dequantize(q, s16, z16), x.astype(np.float32))
+
+
+def test_four_bit_hand_case():
+    """Worked by hand: x = 0, 1, ..., 15 (fp16) over a 16-value group: max - min = 15, so
+    s = 15 / 15 = 1, z = -0 / 1 = 0 and each value is its own code; x = -1.5 and 6 give
+    s = 7.5 / 15 = 0.5, z = 1.5 / 0.5 = 3, and x = 0 -> 0 / 0.5 + 3 = 3."""
+    x = np.arange(16, dtype=np.float16)
+    s, z = kv.group_params(x, 4)
+    assert float(s) == 1.0 and float(z) == 0.0
+    assert kv.quantize(x, s, z, 4).tolist() == list(range(16))
+    y = np.array([-1.5, 6.0, 0.0, 2.25], dtype=np.float16)
+    s, z = kv.group_params(y, 4)
+    assert float(s) == 0.5 and float(z) == 3.0
+    # 2.25 / 0.5 + 3 = 7.5 -> 8 (ties to even)
+    assert kv.quantize(y, s, z, 4).tolist() == [0, 15, 3, 8]
+
+
+def test_mixed_widths_quantize_each_side_with_its_own():
+    """A state with 4-bit keys and 2-bit values: key codes reach 15, value codes stay in [0, 3],
+    and each side equals a quantizer call with its own width."""
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((300, 32)).astype(np.float16)
+    v = rng.standard_normal((300, 32)).astype(np.float16)
+    st = kv.KiviState(D=32, bits=4, v_bits=2)
+    st.prefill(k, v)
+    kc = np.concatenate(st.k_codes)
+    vc = np.stack(st.v_codes)
+    assert kc.max() == 15 and vc.max() == 3
+    codes, _, _ = kv.quantize_keys(k[:st.n_kq], 32, 4)
+    np.testing.assert_array_equal(kc, codes)
+    codes, _, _ = kv.quantize_values(v[:st.n_vq], 32, 2)
+    np.testing.assert_array_equal(vc, codes)
 
 
 def test_round_half_to_even():
