@@ -23,7 +23,7 @@ __all__ = [
     "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_request_order", "lvq_window_append",
     "lvq_codebook_update",
     "lvq_decode_attn_splits", "lvq_quant_partial", "lvq_quant_partial_workspace", "lvq_window_partial", "splitk_lse_merge", "kivi_append",
-    "kivi_decode_attn_workspace", "kivi_decode_attn", "KiviCache", "layout",
+    "kivi_decode_attn_workspace", "kivi_decode_attn", "KiviCache", "kivi_widths", "layout",
 ]
 
 
@@ -48,8 +48,14 @@ def make_geom(D=128, T=4, Tc=2, G=16, K=256, page=8, sink=8, window=64, H=1, cb_
     return lvq_geom(D, T, Tc, G, K, page, sink, window, H, cb)
 
 
-def make_kivi_geom(D=128, H=1, bits=2, group=32, R=128, cap=4096) -> kivi_geom:
-    return kivi_geom(D, H, bits, group, R, cap)
+def make_kivi_geom(D=128, H=1, bits=2, group=32, R=128, cap=4096, v_bits=0, Hq=0) -> kivi_geom:
+    """bits: key code width (2 or 4); v_bits: value code width (0 = as keys); Hq: query heads (0 = H)."""
+    return kivi_geom(D, H, bits, group, R, cap, v_bits, Hq)
+
+
+def kivi_widths(g: kivi_geom):
+    """(key bits, value bits, query heads) of a geometry."""
+    return g.bits, (g.v_bits or g.bits), (g.Hq or g.H)
 
 
 def _cb_torch_dtype(g: lvq_geom):
@@ -352,11 +358,12 @@ class KiviCache:
     def __init__(self, g: kivi_geom, B: int, device="cuda"):
         self.g, self.B = g, B
         D, H, G, cap, ring = g.D, g.H, g.group, g.cap, g.R + g.group
+        kb, vb, _ = kivi_widths(g)
         u8, f16 = torch.uint8, torch.float16
-        self.k_codes = torch.zeros((B, H, cap, D // 4), dtype=u8, device=device)
+        self.k_codes = torch.zeros((B, H, cap, D * kb // 8), dtype=u8, device=device)
         self.k_scale = torch.zeros((B, H, cap // G, D), dtype=f16, device=device)
         self.k_zero = torch.zeros((B, H, cap // G, D), dtype=f16, device=device)
-        self.v_codes = torch.zeros((B, H, cap, D // 4), dtype=u8, device=device)
+        self.v_codes = torch.zeros((B, H, cap, D * vb // 8), dtype=u8, device=device)
         self.v_scale = torch.zeros((B, H, cap, D // G), dtype=f16, device=device)
         self.v_zero = torch.zeros((B, H, cap, D // G), dtype=f16, device=device)
         self.k_res = torch.zeros((B, H, ring, D), dtype=f16, device=device)
@@ -392,10 +399,11 @@ def kivi_decode_attn(g: kivi_geom, q: torch.Tensor, cache: KiviCache, max_len: i
                      ws: Optional[torch.Tensor] = None, num_splits: int = 0, stream=None):
     _need(q, "q", torch.float16)
     B = cache.B
-    if tuple(q.shape) != (B, g.H, g.D):
-        raise ValueError("q must be [B][H][D]")
+    Hq = kivi_widths(g)[2]
+    if tuple(q.shape) != (B, Hq, g.D):
+        raise ValueError("q must be [B][Hq][D]")
     if out is None:
-        out = torch.empty((B, g.H, g.D), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, Hq, g.D), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32)
     if lse_out is not None:
         _need(lse_out, "lse_out", torch.float32)

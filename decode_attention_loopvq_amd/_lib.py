@@ -35,7 +35,7 @@ class lvq_geom(C.Structure):
 
 
 class kivi_geom(C.Structure):
-    _fields_ = [(n, C.c_int32) for n in ("D", "H", "bits", "group", "R", "cap")]
+    _fields_ = [(n, C.c_int32) for n in ("D", "H", "bits", "group", "R", "cap", "v_bits", "Hq")]
 
 
 class kivi_cache(C.Structure):

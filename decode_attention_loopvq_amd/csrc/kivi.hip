@@ -1,5 +1,7 @@
-// KIVI-style 2-bit asymmetric KV cache: append (prefill / decode) and decode
-// attention over the quantized and fp16 segments with one softmax.
+// KIVI-style asymmetric KV cache with 2- or 4-bit codes (key and value widths
+// chosen apart): append (prefill / decode) and decode attention over the
+// quantized and fp16 segments with one softmax, for Hq query heads sharing
+// each of the H KV heads (grouped-query attention).
 //
 // KIVI page ("KIVI 完全拆解：非对称 2-bit KV Cache 量化"): "definitions"
 // (q = clamp(round(x/s + z), 0, 2^b - 1), x_hat = s (q - z), [min, max]
@@ -19,6 +21,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 struct KArgs {
     int D, H, G, R, cap, ring;
+    int kb, vb;           // key and value code widths (2 or 4 bits)
+    int nrep;             // query heads per KV head
     kivi_cache c;
 };
 
@@ -30,9 +34,10 @@ struct GroupParams {
     float s, z;
 };
 
-__device__ __forceinline__ GroupParams group_params(float mn, float mx) {
+// levels = 2^b - 1
+__device__ __forceinline__ GroupParams group_params(float mn, float mx, float levels) {
     GroupParams p;
-    p.s16 = f32_to_f16_rne(__fdiv_rn(__fsub_rn(mx, mn), 3.0f));
+    p.s16 = f32_to_f16_rne(__fdiv_rn(__fsub_rn(mx, mn), levels));
     if ((p.s16 & 0x7fff) == 0) p.s16 = 0x3c00;       // s == 0 (constant group) -> 1
     p.s = f16_to_f32(p.s16);
     p.z16 = f32_to_f16_rne(__fdiv_rn(-mn, p.s));
@@ -40,10 +45,10 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx) {
     return p;
 }
 
-__device__ __forceinline__ uint32_t code_of(float x, float s, float z) {
+__device__ __forceinline__ uint32_t code_of(float x, float s, float z, float levels) {
     float u = __fadd_rn(__fdiv_rn(x, s), z);
     u = rintf(u);
-    u = fminf(fmaxf(u, 0.f), 3.f);
+    u = fminf(fmaxf(u, 0.f), levels);
     return uint32_t(u);
 }
 
@@ -52,12 +57,12 @@ __device__ __forceinline__ uint32_t code_of(float x, float s, float z) {
 // this is the correctly rounded quotient: x / s = M / N 2^k with N < 2^11, so unless it is exact it lies
 // at least 2^-12 ulp from every rounding midpoint, while q0 + e r is within 2^-20 ulp of x / s
 // (|e| <= 2 ulp(q0) s and |r - 1/s| <= 1 ulp(1/s)).
-__device__ __forceinline__ uint32_t code_of_r(float x, float s, float r, float z) {
+__device__ __forceinline__ uint32_t code_of_r(float x, float s, float r, float z, float levels) {
     const float q0 = x * r;
     const float e = fmaf(-q0, s, x);
     float u = __fadd_rn(fmaf(e, r, q0), z);
     u = rintf(u);
-    u = fminf(fmaxf(u, 0.f), 3.f);
+    u = fminf(fmaxf(u, 0.f), levels);
     return uint32_t(u);
 }
 
@@ -78,18 +83,22 @@ __device__ void quantize_key_group(const KArgs& a, int b, int h, int gi, int qua
             mx[u] = fmaxf(mx[u], x);
         }
     }
+    const int kb = a.kb;
+    const float levels = float((1 << kb) - 1);
     GroupParams gp[4];
     for (int u = 0; u < 4; ++u) {
-        gp[u] = group_params(mn[u], mx[u]);
+        gp[u] = group_params(mn[u], mx[u], levels);
         U16(a.c.k_scale)[(bh(a, b, h) * (a.cap / a.G) + gi) * D + quad * 4 + u] = gp[u].s16;
         U16(a.c.k_zero)[(bh(a, b, h) * (a.cap / a.G) + gi) * D + quad * 4 + u] = gp[u].z16;
     }
     for (int j = 0; j < a.G; ++j) {
         const int tok = gi * a.G + j;
         const uint16_t* row = src(tok);
-        uint32_t byte = 0;
-        for (int u = 0; u < 4; ++u) byte |= code_of(f16_to_f32(row[quad * 4 + u]), gp[u].s, gp[u].z) << (2 * u);
-        a.c.k_codes[(bh(a, b, h) * a.cap + tok) * (D / 4) + quad] = uint8_t(byte);
+        uint32_t word = 0;             // 4 channels: kb / 2 bytes
+        for (int u = 0; u < 4; ++u)
+            word |= code_of(f16_to_f32(row[quad * 4 + u]), gp[u].s, gp[u].z, levels) << (kb * u);
+        uint8_t* dst = a.c.k_codes + (bh(a, b, h) * a.cap + tok) * (D * kb / 8) + quad * (kb / 2);
+        for (int i = 0; i < kb / 2; ++i) dst[i] = uint8_t(word >> (8 * i));
     }
 }
 
@@ -102,15 +111,17 @@ __device__ void quantize_value_group(const KArgs& a, int b, int h, int tok, int 
         mn = fminf(mn, x);
         mx = fmaxf(mx, x);
     }
-    const GroupParams gp = group_params(mn, mx);
+    const int vb = a.vb;
+    const float levels = float((1 << vb) - 1);
+    const GroupParams gp = group_params(mn, mx, levels);
     U16(a.c.v_scale)[(bh(a, b, h) * a.cap + tok) * (D / a.G) + gi] = gp.s16;
     U16(a.c.v_zero)[(bh(a, b, h) * a.cap + tok) * (D / a.G) + gi] = gp.z16;
-    uint8_t* out = a.c.v_codes + (bh(a, b, h) * a.cap + tok) * (D / 4) + gi * a.G / 4;
+    uint8_t* out = a.c.v_codes + (bh(a, b, h) * a.cap + tok) * (D * vb / 8) + gi * a.G * vb / 8;
     for (int e = 0; e < a.G; e += 4) {
-        uint32_t byte = 0;
+        uint32_t word = 0;             // 4 channels: vb / 2 bytes
         for (int u = 0; u < 4; ++u)
-            byte |= code_of(f16_to_f32(row[gi * a.G + e + u]), gp.s, gp.z) << (2 * u);
-        out[e / 4] = uint8_t(byte);
+            word |= code_of(f16_to_f32(row[gi * a.G + e + u]), gp.s, gp.z, levels) << (vb * u);
+        for (int i = 0; i < vb / 2; ++i) out[(e / 4) * (vb / 2) + i] = uint8_t(word >> (8 * i));
     }
 }
 
@@ -167,7 +178,7 @@ __global__ void prefill_counters_kernel(KArgs a, int B, int L, int n_kq, int n_v
 // maximum over the lane's 8 tokens, then over the 4 lanes l ^ 16k (permlane
 // swaps).  Values of quantized tokens: per-token minimum and maximum over the
 // lane's 8 channels, then over the 4 lanes of the 32-channel group (DPP).
-// Codes go out 2 bytes per lane and token; the rows past the quantized
+// Codes go out 8 * bits / 8 bytes per lane and token; the rows past the quantized
 // ranges go to the fp16 rings; block (0, 0, b) sets request b's counters.
 // ---------------------------------------------------------------------------
 template <typename F>
@@ -195,8 +206,17 @@ __device__ __forceinline__ void half8_f(const uint4& w, float (&f)[8]) {
     }
 }
 
+// the codes of a lane's 8 channels (8 * BITS bits) into their place in a token's code row
+template <int BITS>
+__device__ __forceinline__ void store_codes8(uint8_t* row, int co, uint32_t word) {
+    if constexpr (BITS == 2) *reinterpret_cast<uint16_t*>(row + 2 * co) = uint16_t(word);
+    else *reinterpret_cast<uint32_t*>(row + 4 * co) = word;
+}
+
+template <int KB, int VB>
 __global__ void __launch_bounds__(256, 4) prefill_kv_kernel(KArgs a, NewSrc k, NewSrc v, int L, int n_kq, int n_vq) {
     constexpr int D = 128, G = 32;
+    constexpr float kLevels = float((1 << KB) - 1), vLevels = float((1 << VB) - 1);
     const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, lane = tid & 63;
     const int t0 = blockIdx.x * 128 + (tid >> 6) * 32;
     const int co = lane & 15, tq = lane >> 4;
@@ -231,7 +251,7 @@ __global__ void __launch_bounds__(256, 4) prefill_kv_kernel(KArgs a, NewSrc k, N
         for (int u = 0; u < 8; ++u) {
             mn[u] = rows4_reduce(mn[u], [](float p, float q) { return fminf(p, q); });
             mx[u] = rows4_reduce(mx[u], [](float p, float q) { return fmaxf(p, q); });
-            gp[u] = group_params(mn[u], mx[u]);
+            gp[u] = group_params(mn[u], mx[u], kLevels);
             rs[u] = __builtin_amdgcn_rcpf(gp[u].s);
         }
         if (tq == 0) {
@@ -251,9 +271,9 @@ __global__ void __launch_bounds__(256, 4) prefill_kv_kernel(KArgs a, NewSrc k, N
             half8_f(kx[i], f);
             uint32_t c2 = 0;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) c2 |= code_of_r(f[u], gp[u].s, rs[u], gp[u].z) << (2 * u);
+            for (int u = 0; u < 8; ++u) c2 |= code_of_r(f[u], gp[u].s, rs[u], gp[u].z, kLevels) << (KB * u);
             const int t = t0 + 8 * tq + i;
-            *reinterpret_cast<uint16_t*>(a.c.k_codes + (bhi * a.cap + t) * (D / 4) + 2 * co) = uint16_t(c2);
+            store_codes8<KB>(a.c.k_codes + (bhi * a.cap + t) * (D * KB / 8), co, c2);
         }
     }
 #pragma unroll
@@ -278,12 +298,12 @@ __global__ void __launch_bounds__(256, 4) prefill_kv_kernel(KArgs a, NewSrc k, N
         mn = fminf(mn, kdpp_f<0x4e>(mn));           // quad_perm [2,3,0,1]
         mx = fmaxf(mx, kdpp_f<0x4e>(mx));
         if (t < n_vq) {
-            const GroupParams gp = group_params(mn, mx);
+            const GroupParams gp = group_params(mn, mx, vLevels);
             const float r = __builtin_amdgcn_rcpf(gp.s);
             uint32_t c2 = 0;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) c2 |= code_of_r(f[u], gp.s, r, gp.z) << (2 * u);
-            *reinterpret_cast<uint16_t*>(a.c.v_codes + (bhi * a.cap + t) * (D / 4) + 2 * co) = uint16_t(c2);
+            for (int u = 0; u < 8; ++u) c2 |= code_of_r(f[u], gp.s, r, gp.z, vLevels) << (VB * u);
+            store_codes8<VB>(a.c.v_codes + (bhi * a.cap + t) * (D * VB / 8), co, c2);
             if ((co & 3) == 0) {
                 U16(a.c.v_scale)[(bhi * a.cap + t) * (D / G) + (co >> 2)] = gp.s16;
                 U16(a.c.v_zero)[(bhi * a.cap + t) * (D / G) + (co >> 2)] = gp.z16;
@@ -344,20 +364,24 @@ __global__ void decode_counters_kernel(KArgs a, int B) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode attention partial: grid (split, H, B), 256 threads in 32 lane groups
-// of 8; lane c of a group owns channels 16c .. 16c+15 (one dword of 2-bit
-// codes per token).  A split is a multiple of 32 tokens.  Fast path: lane
-// group j takes the j-th whole 32-token key group of the split inside the
-// fully quantized range [0, min(n_kq, n_vq)); it loads the group's key
-// scale/zero once and the codes and value parameters of its 32 tokens at
-// once, scores them (q_d s_d folded into one weight per channel, the zero
-// point into one bias), then adds their values (a lane group with more key
-// groups takes them in turn, rescaling its running softmax):
+// Decode attention partial: grid (split, KV head h, B), 256 threads in 32 lane
+// groups of 8; lane c of a group owns channels 16c .. 16c+15 (16 * bits bits
+// of codes per token: one dword at 2 bits, two at 4).  The nrep query heads of
+// KV head h share the workgroup: lane group lg serves query head
+// h * nrep + lg % nrep and takes every (32 / nrep)-th token range, so the
+// lane groups of the nrep heads in one wave read the same code words in the
+// same instruction.  A split is a multiple of 32 tokens.  Fast path: a lane
+// group takes whole 32-token key groups inside the fully quantized range
+// [0, min(n_kq, n_vq)); it loads the group's key scale/zero once and the
+// codes and value parameters of TB tokens at once (all 32 at 2 bits, 16 at a
+// time when a side has 4-bit codes), scores them (q_d s_d folded into one
+// weight per channel, the zero point into one bias), then adds their values
+// (rescaling its running softmax per batch):
 //   o_d += p_t s_t (c_td - z_t)  =  sum_t (p_t s_t) c_td - sum_t p_t s_t z_t,
 // the second sum kept once per lane.  Tokens past the quantized range (the
 // fp16 residual, a partial group) take a generic path, one token per lane
-// group at a time.  Each lane group keeps its own softmax state; the 32 are
-// combined through LDS.
+// group at a time.  Each lane group keeps its own softmax state; those of one
+// query head are combined through LDS.
 // ---------------------------------------------------------------------------
 constexpr int kKiviLaneGroups = 32;
 
@@ -372,15 +396,47 @@ __device__ __forceinline__ float sum8(float x) {
     x += kdpp<0x141>(x);     // row_half_mirror
     return x;
 }
-// the 16 two-bit codes of a dword as floats, channel j at bits 2j
-__device__ __forceinline__ void codes16(uint32_t w, float (&c)[16]) {
+
+// The code words of one lane's 16 channels: channel j at bits BITS * j.
+template <int BITS>
+struct Codes16 {
+    uint32_t w[BITS / 2];
+};
+template <int BITS>
+__device__ __forceinline__ Codes16<BITS> load_codes16(const uint8_t* row, int c8) {
+    Codes16<BITS> c;
+    if constexpr (BITS == 2) {
+        c.w[0] = reinterpret_cast<const uint32_t*>(row)[c8];
+    } else {
+        const uint2 v = reinterpret_cast<const uint2*>(row)[c8];
+        c.w[0] = v.x;
+        c.w[1] = v.y;
+    }
+    return c;
+}
+// the 16 codes as floats
+template <int BITS>
+__device__ __forceinline__ void codes16(const Codes16<BITS>& cw, float (&c)[16]) {
+    if constexpr (BITS == 2) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t x = (w >> (2 * k)) & 0x03030303u;    // bytes: channels k, 4+k, 8+k, 12+k
-        c[k] = float(x & 0xffu);                             // v_cvt_f32_ubyte0 .. 3
-        c[4 + k] = float((x >> 8) & 0xffu);
-        c[8 + k] = float((x >> 16) & 0xffu);
-        c[12 + k] = float(x >> 24);
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t x = (cw.w[0] >> (2 * k)) & 0x03030303u;    // bytes: channels k, 4+k, 8+k, 12+k
+            c[k] = float(x & 0xffu);                                 // v_cvt_f32_ubyte0 .. 3
+            c[4 + k] = float((x >> 8) & 0xffu);
+            c[8 + k] = float((x >> 16) & 0xffu);
+            c[12 + k] = float(x >> 24);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t x = (cw.w[i] >> (4 * k)) & 0x0f0f0f0fu;   // bytes: channels 8i + k, +2, +4, +6
+                c[8 * i + k] = float(x & 0xffu);
+                c[8 * i + 2 + k] = float((x >> 8) & 0xffu);
+                c[8 * i + 4 + k] = float((x >> 16) & 0xffu);
+                c[8 * i + 6 + k] = float(x >> 24);
+            }
     }
 }
 __device__ __forceinline__ void half8(uint4 w, float* out) {
@@ -392,21 +448,26 @@ __device__ __forceinline__ void half8(uint4 w, float* out) {
     }
 }
 
+template <int KB, int VB>
 __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, const uint16_t* __restrict__ q,
                                                                    float scale_log2, int tps, int S_tot,
                                                                    int max_len, float* __restrict__ po,
                                                                    float* __restrict__ pl) {
     constexpr int D = 128, NLG = kKiviLaneGroups;
+    constexpr int TB = (KB == 4 || VB == 4) ? 16 : 32;   // tokens whose codes are held at once
+    constexpr int KROW = D * KB / 8, VROW = D * VB / 8;  // code bytes per token
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, c8 = tid & 7, lg = tid >> 3;
+    const int nrep = a.nrep, head = lg % nrep, tl = lg / nrep, NT = NLG / nrep;
     const int L = min(max(a.c.len[b], 0), max_len);
     const int nk = min(a.c.n_kq[b], L), nv = min(a.c.n_vq[b], L);
     const int t_lo = min(L, split * tps), t_hi = min(L, (split + 1) * tps);
-    const long row = bh(a, b, h);
+    const long row = bh(a, b, h);                    // KV row
+    const long qrow = row * nrep + head;             // query row: b * Hq + h * nrep + head
     const int ch0 = 16 * c8, vg = c8 >> 1;          // channels and their value group
     float qv[16];
     {
-        const uint4* qp = reinterpret_cast<const uint4*>(q + row * D + ch0);
+        const uint4* qp = reinterpret_cast<const uint4*>(q + qrow * D + ch0);
         half8(qp[0], qv);
         half8(qp[1], qv + 8);
 #pragma unroll
@@ -420,16 +481,7 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
     // ---- fast path: whole key groups inside [0, min(nk, nv)) ----
     const int q_end = min(nk, nv) & ~31;
     const int f_hi = min(t_hi, q_end);
-    for (int t0 = t_lo + 32 * lg; t0 + 32 <= f_hi; t0 += 32 * NLG) {
-        uint32_t kc[32], vc[32], vs[32], vz[32];
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            const long tok = cb + t0 + k;
-            kc[k] = reinterpret_cast<const uint32_t*>(a.c.k_codes + tok * (D / 4))[c8];
-            vc[k] = reinterpret_cast<const uint32_t*>(a.c.v_codes + tok * (D / 4))[c8];
-            vs[k] = reinterpret_cast<const uint32_t*>(U16(a.c.v_scale) + tok * (D / 32))[vg >> 1];
-            vz[k] = reinterpret_cast<const uint32_t*>(U16(a.c.v_zero) + tok * (D / 32))[vg >> 1];
-        }
+    for (int t0 = t_lo + 32 * tl; t0 + 32 <= f_hi; t0 += 32 * NT) {
         float w[16], bk = 0.f;
         {
             const long pidx = (row * (a.cap / 32) + t0 / 32) * D + ch0;
@@ -444,48 +496,62 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
                 bk = fmaf(w[j], z16[j], bk);
             }
         }
-        float sc[32];
-        float mb = m;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            float c[16];
-            codes16(kc[k], c);
-            float part = -bk;
+        for (int tb = 0; tb < 32; tb += TB) {
+            Codes16<KB> kc[TB];
+            Codes16<VB> vc[TB];
+            uint32_t vs[TB], vz[TB];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) part = fmaf(w[j], c[j], part);
-            sc[k] = sum8(part);
-            mb = fmaxf(mb, sc[k]);
+            for (int k = 0; k < TB; ++k) {
+                const long tok = cb + t0 + tb + k;
+                kc[k] = load_codes16<KB>(a.c.k_codes + tok * KROW, c8);
+                vc[k] = load_codes16<VB>(a.c.v_codes + tok * VROW, c8);
+                vs[k] = reinterpret_cast<const uint32_t*>(U16(a.c.v_scale) + tok * (D / 32))[vg >> 1];
+                vz[k] = reinterpret_cast<const uint32_t*>(U16(a.c.v_zero) + tok * (D / 32))[vg >> 1];
+            }
+            float sc[TB];
+            float mb = m;
+#pragma unroll
+            for (int k = 0; k < TB; ++k) {
+                float c[16];
+                codes16<KB>(kc[k], c);
+                float part = -bk;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) part = fmaf(w[j], c[j], part);
+                sc[k] = sum8(part);
+                mb = fmaxf(mb, sc[k]);
+            }
+            // the batch joins the lane group's running softmax
+            {
+                const float alpha = exp2f(m - mb);
+                l *= alpha;
+                ob *= alpha;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[j] *= alpha;
+            }
+            const int hsel = 16 * (vg & 1);          // which half of the dword holds this lane's group
+#pragma unroll
+            for (int k = 0; k < TB; ++k) {
+                const float p = exp2f(sc[k] - mb);
+                l += p;
+                const float av = p * f16_to_f32(uint16_t(vs[k] >> hsel));
+                ob = fmaf(av, f16_to_f32(uint16_t(vz[k] >> hsel)), ob);
+                float c[16];
+                codes16<VB>(vc[k], c);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[j] = fmaf(av, c[j], o[j]);
+            }
+            m = mb;
         }
-        // the batch joins the lane group's running softmax
-        {
-            const float alpha = exp2f(m - mb);
-            l *= alpha;
-            ob *= alpha;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) o[j] *= alpha;
-        }
-        const int hsel = 16 * (vg & 1);              // which half of the dword holds this lane's group
-#pragma unroll
-        for (int k = 0; k < 32; ++k) {
-            const float p = exp2f(sc[k] - mb);
-            l += p;
-            const float av = p * f16_to_f32(uint16_t(vs[k] >> hsel));
-            ob = fmaf(av, f16_to_f32(uint16_t(vz[k] >> hsel)), ob);
-            float c[16];
-            codes16(vc[k], c);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) o[j] = fmaf(av, c[j], o[j]);
-        }
-        m = mb;
     }
 
     // ---- generic path: the rest of the split, one token per lane group at a time ----
     const int g_lo = max(t_lo, f_hi);
-    for (int tok = g_lo + lg; tok < t_hi; tok += NLG) {
+    for (int tok = g_lo + tl; tok < t_hi; tok += NT) {
         float kf[16], vf[16];
         if (tok < nk) {
             float c[16], s16[16], z16[16];
-            codes16(reinterpret_cast<const uint32_t*>(a.c.k_codes + (cb + tok) * (D / 4))[c8], c);
+            codes16<KB>(load_codes16<KB>(a.c.k_codes + (cb + tok) * KROW, c8), c);
             const long pidx = (row * (a.cap / 32) + tok / 32) * D + ch0;
             const uint4* sp = reinterpret_cast<const uint4*>(U16(a.c.k_scale) + pidx);
             const uint4* zp = reinterpret_cast<const uint4*>(U16(a.c.k_zero) + pidx);
@@ -499,7 +565,7 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
         }
         if (tok < nv) {
             float c[16];
-            codes16(reinterpret_cast<const uint32_t*>(a.c.v_codes + (cb + tok) * (D / 4))[c8], c);
+            codes16<VB>(load_codes16<VB>(a.c.v_codes + (cb + tok) * VROW, c8), c);
             const float s1 = f16_to_f32(U16(a.c.v_scale)[(cb + tok) * (D / 32) + vg]);
             const float z1 = f16_to_f32(U16(a.c.v_zero)[(cb + tok) * (D / 32) + vg]);
 #pragma unroll
@@ -521,7 +587,7 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
         m = m_new;
     }
 
-    // ---- combine the 32 lane groups ----
+    // ---- combine the lane groups of each query head ----
     __shared__ float red[NLG][D + 2];
 #pragma unroll
     for (int j = 0; j < 16; ++j) red[lg][ch0 + j] = o[j] - ob;
@@ -530,23 +596,25 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
         red[lg][D + 1] = l;
     }
     __syncthreads();
-    if (tid >= D) return;
-    const long orow = row * S_tot + split;
-    float M = -INFINITY;
-    for (int g2 = 0; g2 < NLG; ++g2) M = fmaxf(M, red[g2][D]);
-    if (M == -INFINITY) {
-        po[orow * D + tid] = 0.f;
-        if (tid == 0) pl[orow] = -INFINITY;
-        return;
+    for (int e = tid; e < nrep * D; e += 256) {
+        const int hr = e / D, d = e % D;
+        const long orow = (row * nrep + hr) * S_tot + split;
+        float M = -INFINITY;
+        for (int g2 = hr; g2 < NLG; g2 += nrep) M = fmaxf(M, red[g2][D]);
+        if (M == -INFINITY) {
+            po[orow * D + d] = 0.f;
+            if (d == 0) pl[orow] = -INFINITY;
+            continue;
+        }
+        float Ls = 0.f, ov = 0.f;
+        for (int g2 = hr; g2 < NLG; g2 += nrep) {
+            const float fw = red[g2][D] == -INFINITY ? 0.f : exp2f(red[g2][D] - M);
+            Ls += red[g2][D + 1] * fw;
+            ov += red[g2][d] * fw;
+        }
+        po[orow * D + d] = ov / Ls;
+        if (d == 0) pl[orow] = (M + log2f(Ls)) * kLn2;
     }
-    float Ls = 0.f, ov = 0.f;
-    for (int g2 = 0; g2 < NLG; ++g2) {
-        const float fw = red[g2][D] == -INFINITY ? 0.f : exp2f(red[g2][D] - M);
-        Ls += red[g2][D + 1] * fw;
-        ov += red[g2][tid] * fw;
-    }
-    po[orow * D + tid] = ov / Ls;
-    if (tid == 0) pl[orow] = (M + log2f(Ls)) * kLn2;
 }
 
 __global__ void kivi_merge_kernel(const float* __restrict__ po, const float* __restrict__ pl, int S, int D,
@@ -572,10 +640,16 @@ __global__ void kivi_merge_kernel(const float* __restrict__ po, const float* __r
 lvq_status validate_kivi(const kivi_geom* g, const kivi_cache* c) {
     LVQ_REQUIRE(g && c, LVQ_ERR_INVALID_ARG, "kivi: NULL geometry or cache");
     LVQ_REQUIRE(g->D == 128, LVQ_ERR_UNSUPPORTED, "kivi: head dimension %d unsupported (128)", g->D);
-    LVQ_REQUIRE(g->bits == 2, LVQ_ERR_UNSUPPORTED, "kivi: %d-bit codes unsupported (2)", g->bits);
+    LVQ_REQUIRE(g->bits == 2 || g->bits == 4, LVQ_ERR_UNSUPPORTED, "kivi: %d-bit key codes unsupported (2, 4)",
+                g->bits);
+    LVQ_REQUIRE(g->v_bits == 0 || g->v_bits == 2 || g->v_bits == 4, LVQ_ERR_UNSUPPORTED,
+                "kivi: %d-bit value codes unsupported (0 = as keys, 2, 4)", g->v_bits);
     LVQ_REQUIRE(g->group == 32, LVQ_ERR_UNSUPPORTED, "kivi: group %d unsupported (32)", g->group);
     LVQ_REQUIRE(g->H > 0 && g->R > 0 && g->R % g->group == 0, LVQ_ERR_INVALID_ARG,
                 "kivi: R=%d must be a positive multiple of the group", g->R);
+    LVQ_REQUIRE(g->Hq >= 0 && (g->Hq == 0 || (g->Hq % g->H == 0 && kKiviLaneGroups % (g->Hq / g->H) == 0)),
+                LVQ_ERR_UNSUPPORTED, "kivi: %d query heads over %d KV heads (a multiple, at most 32 per KV head, "
+                "dividing 32)", g->Hq, g->H);
     LVQ_REQUIRE(g->cap > 0 && g->cap % g->group == 0, LVQ_ERR_INVALID_ARG,
                 "kivi: capacity %d must be a positive multiple of the group", g->cap);
     LVQ_REQUIRE(c->k_codes && c->k_scale && c->k_zero && c->v_codes && c->v_scale && c->v_zero && c->k_res &&
@@ -587,6 +661,9 @@ lvq_status validate_kivi(const kivi_geom* g, const kivi_cache* c) {
 KArgs make_args(const kivi_geom* g, const kivi_cache* c) {
     KArgs a;
     a.D = g->D; a.H = g->H; a.G = g->group; a.R = g->R; a.cap = g->cap; a.ring = g->R + g->group;
+    a.kb = g->bits;
+    a.vb = g->v_bits ? g->v_bits : g->bits;
+    a.nrep = g->Hq ? g->Hq / g->H : 1;
     a.c = *c;
     return a;
 }
@@ -628,8 +705,15 @@ extern "C" lvq_status kivi_append(const kivi_geom* g, const void* k_new, const v
                              reinterpret_cast<uintptr_t>(v_new) % 16 == 0 && new_strides[0] % 8 == 0 &&
                              new_strides[1] % 8 == 0 && new_strides[2] % 8 == 0;
         if (aligned) {
-            hipLaunchKernelGGL(prefill_kv_kernel, dim3(ceil_div(n_new, 128), g->H, B), dim3(256), 0, stream, a, ks,
-                               vs, n_new, n_kq, n_vq);
+            const dim3 grid(ceil_div(n_new, 128), g->H, B);
+            if (a.kb == 2 && a.vb == 2)
+                hipLaunchKernelGGL((prefill_kv_kernel<2, 2>), grid, dim3(256), 0, stream, a, ks, vs, n_new, n_kq, n_vq);
+            else if (a.kb == 2)
+                hipLaunchKernelGGL((prefill_kv_kernel<2, 4>), grid, dim3(256), 0, stream, a, ks, vs, n_new, n_kq, n_vq);
+            else if (a.vb == 2)
+                hipLaunchKernelGGL((prefill_kv_kernel<4, 2>), grid, dim3(256), 0, stream, a, ks, vs, n_new, n_kq, n_vq);
+            else
+                hipLaunchKernelGGL((prefill_kv_kernel<4, 4>), grid, dim3(256), 0, stream, a, ks, vs, n_new, n_kq, n_vq);
             return check_launch("kivi_append: prefill");
         }
         if (n_kq > 0) {
@@ -659,8 +743,9 @@ extern "C" lvq_status kivi_append(const kivi_geom* g, const void* k_new, const v
 
 extern "C" size_t kivi_decode_attn_workspace(const kivi_geom* g, int32_t B, int32_t max_len, int32_t num_splits) {
     if (!g || B < 0 || max_len < 0 || num_splits < 0 || g->H <= 0 || g->D <= 0) return 0;
+    if (g->Hq < 0 || (g->Hq && g->Hq % g->H)) return 0;
     const int S = num_splits > 0 ? num_splits : choose_kivi_splits(g, B, max_len);
-    const size_t rows = size_t(B) * g->H * S;
+    const size_t rows = size_t(B) * (g->Hq ? g->Hq : g->H) * S;     // (request, query head, split)
     return rows * g->D * sizeof(float) + rows * sizeof(float);
 }
 
@@ -680,13 +765,23 @@ extern "C" lvq_status kivi_decode_attn(const kivi_geom* g, const void* q, const 
     const size_t need = kivi_decode_attn_workspace(g, B, max_len, S);
     LVQ_REQUIRE(ws_bytes >= need, LVQ_ERR_WORKSPACE, "kivi_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
     KArgs a = make_args(g, c);
-    const size_t rows = size_t(B) * g->H * S;
+    const int Hq = g->H * a.nrep;
+    const size_t rows = size_t(B) * Hq * S;
     float* po = static_cast<float*>(ws);
     float* pl = po + rows * g->D;
     const int tps = ceil_div(ceil_div(max_len, S), 32) * 32;     // whole key groups per split
-    hipLaunchKernelGGL(kivi_attn_partial_kernel, dim3(S, g->H, B), dim3(256), 0, stream, a,
-                       static_cast<const uint16_t*>(q), sm_scale * kLog2e, tps, S, max_len, po, pl);
+    const dim3 grid(S, g->H, B);
+    const auto* qp = static_cast<const uint16_t*>(q);
+    const float sl2 = sm_scale * kLog2e;
+    if (a.kb == 2 && a.vb == 2)
+        hipLaunchKernelGGL((kivi_attn_partial_kernel<2, 2>), grid, dim3(256), 0, stream, a, qp, sl2, tps, S, max_len, po, pl);
+    else if (a.kb == 2)
+        hipLaunchKernelGGL((kivi_attn_partial_kernel<2, 4>), grid, dim3(256), 0, stream, a, qp, sl2, tps, S, max_len, po, pl);
+    else if (a.vb == 2)
+        hipLaunchKernelGGL((kivi_attn_partial_kernel<4, 2>), grid, dim3(256), 0, stream, a, qp, sl2, tps, S, max_len, po, pl);
+    else
+        hipLaunchKernelGGL((kivi_attn_partial_kernel<4, 4>), grid, dim3(256), 0, stream, a, qp, sl2, tps, S, max_len, po, pl);
     if ((st = check_launch("kivi_decode_attn: partial")) != LVQ_OK) return st;
-    hipLaunchKernelGGL(kivi_merge_kernel, dim3(B * g->H), dim3(128), 0, stream, po, pl, S, g->D, out, lse_out);
+    hipLaunchKernelGGL(kivi_merge_kernel, dim3(B * Hq), dim3(128), 0, stream, po, pl, S, g->D, out, lse_out);
     return check_launch("kivi_decode_attn: merge");
 }

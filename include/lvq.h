@@ -347,20 +347,28 @@ LVQ_API lvq_status splitk_lse_merge(const float* part_o, const float* part_lse, 
 
 /*
  * D      head dimension (128 supported)     H      KV heads
- * bits   2                                   group  32 (tokens per key group, channels per value group)
+ * bits   key code width: 2 or 4 (KIVI page, "definitions": 2^b - 1 levels;
+ *        4 bits is its KIVI-4 variant)
+ * group  32 (tokens per key group, channels per value group)
  * R      residual length (a multiple of group)
  * cap    token capacity per request (a multiple of group)
+ * v_bits value code width: 2 or 4, or 0 for the keys' width (mixed widths)
+ * Hq     query heads (grouped-query attention: Hq / H query heads share each
+ *        KV head, query head j uses KV head j / (Hq / H)); 0 means H.  Hq / H
+ *        must divide 32.
  */
 typedef struct {
-    int32_t D, H, bits, group, R, cap;
+    int32_t D, H, bits, group, R, cap, v_bits, Hq;
 } kivi_geom;
 
 /*
- * Cache of B requests, all device pointers:
- *  k_codes  uint8 [B][H][cap][D/4]   key codes, token-major; channel d of a
- *                                    token sits in byte d/4 at bits 2*(d%4)
+ * Cache of B requests, all device pointers (b = the side's code width, kb for
+ * keys, vb for values):
+ *  k_codes  uint8 [B][H][cap][D*kb/8] key codes, token-major; channel d of a
+ *                                    token sits in byte d*kb/8 at bits
+ *                                    kb*(d % (8/kb))
  *  k_scale, k_zero  fp16 [B][H][cap/group][D]   per (32-token group, channel)
- *  v_codes  uint8 [B][H][cap][D/4]   value codes, same packing
+ *  v_codes  uint8 [B][H][cap][D*vb/8] value codes, same packing
  *  v_scale, v_zero  fp16 [B][H][cap][D/group]   per (token, 32-channel group)
  *  k_res, v_res     fp16 [B][H][R+group][D]     residual rings: position p in slot p % (R+group)
  *  len, n_kq, n_vq  int32 [B]        tokens held; keys [0, n_kq) and values
@@ -382,10 +390,10 @@ typedef struct {
  *    then, if the key residual holds R or more rows, its oldest R rows are
  *    quantized (R/group whole groups) and dropped; if the value residual holds
  *    more than R rows, the rows beyond the newest R are quantized.
- * Codes, s and z follow q = clamp(rint(fl32(fl32(x/s) + z)), 0, 3) with
- * s = fp16(fl32(fl32(max - min)/3)) (1 if that is 0) and z = fp16(fl32(-min/s)),
+ * Codes, s and z follow q = clamp(rint(fl32(fl32(x/s) + z)), 0, 2^b - 1) with
+ * s = fp16(fl32(fl32(max - min)/(2^b - 1))) (1 if that is 0) and z = fp16(fl32(-min/s)),
  * each step IEEE binary32 round-to-nearest-even.
- *  k_new, v_new  fp16; element (b, h, j, d) at b*new_strides[0] + h*new_strides[1]
+ *  k_new, v_new  fp16 (H KV heads); element (b, h, j, d) at b*new_strides[0] + h*new_strides[1]
  *                + j*new_strides[2] + d   (strides in elements, host array).
  *  prefill       host flag: 1 = prefill, 0 = decode.
  */
@@ -399,7 +407,9 @@ LVQ_API size_t kivi_decode_attn_workspace(const kivi_geom* g, int32_t B, int32_t
  * Decode attention over the quantized and fp16 segments with ONE softmax over
  * all logits ("core design", segment attention; "engineering": the segments
  * must share the normaliser).  Keys are used as stored (post-RoPE in KIVI).
- *  q  fp16 [B][H][D];  out fp32 [B][H][D];  lse_out fp32 [B][H] or NULL.
+ *  q  fp16 [B][Hq][D];  out fp32 [B][Hq][D];  lse_out fp32 [B][Hq] or NULL
+ *  (Hq = H when the geometry's Hq is 0).  Query head j attends over KV head
+ *  j / (Hq / H).
  *  max_len (host) bounds len[b]; num_splits 0 = the library's choice.
  */
 LVQ_API lvq_status kivi_decode_attn(const kivi_geom* g, const void* q, const kivi_cache* c, int32_t max_len,

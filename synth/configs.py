@@ -43,7 +43,9 @@ class KiviConfig:
     H: int
     L: int
     D: int = 128
-    bits: int = 2
+    bits: int = 2               # key code width
+    v_bits: int = 0             # value code width (0: as the keys)
+    Hq: int = 0                 # query heads (0: one per KV head; a multiple of H for grouped-query attention)
     group: int = 32             # tokens per key group (per-channel) and channels per value group (per-token)
     R: int = 128                # residual length kept in fp16
     n_outlier: int = 4          # fixed outlier key channels per head
@@ -71,6 +73,9 @@ LOOPVQ_CONFIGS = {
 
 KIVI_CONFIGS = {
     "kivi-b16-4k": KiviConfig(name="kivi-b16-4k", B=16, H=32, L=4096, seed=1002),
+    # the page's variants: 4-bit codes (KIVI-4), and grouped-query attention (32 query heads over 8 KV heads)
+    "kivi4-b16-4k": KiviConfig(name="kivi4-b16-4k", B=16, H=32, L=4096, bits=4, seed=1004),
+    "kivi-gqa-b16-4k": KiviConfig(name="kivi-gqa-b16-4k", B=16, H=8, Hq=32, L=4096, seed=1005),
 }
 
 

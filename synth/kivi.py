@@ -52,8 +52,8 @@ def new_tokens(cfg: KiviConfig, n: int, device="cpu") -> Tuple[torch.Tensor, tor
 
 
 def queries(cfg: KiviConfig, device="cpu", n: int = 1) -> torch.Tensor:
-    """Queries [n][B][H][D] fp16, N(0,1)."""
-    q = torch.randn((n, cfg.B, cfg.H, cfg.D), generator=_gen(cfg, device, 5), device=device)
+    """Queries [n][B][Hq][D] fp16, N(0,1) (Hq = H unless the workload groups query heads)."""
+    q = torch.randn((n, cfg.B, cfg.Hq or cfg.H, cfg.D), generator=_gen(cfg, device, 5), device=device)
     return q.to(torch.float16)
 
 

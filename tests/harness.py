@@ -138,13 +138,14 @@ class KiviProblem:
     cache: "lvq.KiviCache"
     k: torch.Tensor          # [B][H][L][D] fp16 prefill data
     v: torch.Tensor
-    q: torch.Tensor          # [B][H][D] fp16
+    q: torch.Tensor          # [B][Hq][D] fp16
     sm_scale: float
 
 
 def build_kivi(cfg: KiviConfig, device="cuda", cap: int = 0) -> KiviProblem:
     cap = cap or ((cfg.L + 256 + cfg.group - 1) // cfg.group) * cfg.group
-    g = lvq.make_kivi_geom(D=cfg.D, H=cfg.H, bits=cfg.bits, group=cfg.group, R=cfg.R, cap=cap)
+    g = lvq.make_kivi_geom(D=cfg.D, H=cfg.H, bits=cfg.bits, group=cfg.group, R=cfg.R, cap=cap, v_bits=cfg.v_bits,
+                           Hq=cfg.Hq)
     cache = lvq.KiviCache(g, cfg.B, device=device)
     k, v = synk.raw_kv(cfg, device)
     lvq.kivi_append(g, k, v, cache, prefill=True)

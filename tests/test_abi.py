@@ -139,8 +139,12 @@ def test_kivi_rejects():
     assert f(C.byref(g), FAKE, FAKE, strides, 2, 0, C.byref(c), 4, None) == UNSUPPORTED   # decode of 2 tokens
     assert f(C.byref(g), FAKE, FAKE, strides, 0, 1, C.byref(c), 4, None) == INVALID
     assert f(C.byref(g), FAKE, FAKE, strides, 5000, 1, C.byref(c), 4, None) == INVALID   # over capacity
-    bad = lvq.make_kivi_geom(H=2, bits=4)
-    assert f(C.byref(bad), FAKE, FAKE, strides, 1, 0, C.byref(c), 4, None) == UNSUPPORTED
+    for kw in (dict(bits=3), dict(bits=8), dict(v_bits=3), dict(v_bits=1), dict(Hq=3), dict(Hq=2 * 64),
+               dict(Hq=2 * 3), dict(Hq=-2)):
+        bad = lvq.make_kivi_geom(H=2, **kw)
+        assert f(C.byref(bad), FAKE, FAKE, strides, 1, 0, C.byref(c), 4, None) == UNSUPPORTED, kw
+    assert _lib.lib.kivi_decode_attn_workspace(C.byref(lvq.make_kivi_geom(H=2, Hq=8)), 4, 4096, 2) == \
+        4 * 8 * 2 * (128 + 1) * 4
     bad = lvq.make_kivi_geom(H=2, R=100)
     assert f(C.byref(bad), FAKE, FAKE, strides, 1, 0, C.byref(c), 4, None) == INVALID
     c.len = None

@@ -23,12 +23,13 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _unpack(codes: np.ndarray) -> np.ndarray:
-    """[n][D/4] bytes -> [n][D] codes, channel d at bits 2*(d%4) of byte d/4."""
+def _unpack(codes: np.ndarray, bits: int = 2) -> np.ndarray:
+    """[n][D*b/8] bytes -> [n][D] codes, channel d at bits b*(d % (8/b)) of byte d*b/8."""
     n, nb = codes.shape
-    out = np.empty((n, nb * 4), dtype=np.uint8)
-    for u in range(4):
-        out[:, u::4] = (codes >> (2 * u)) & 3
+    per = 8 // bits
+    out = np.empty((n, nb * per), dtype=np.uint8)
+    for u in range(per):
+        out[:, u::per] = (codes >> (bits * u)) & ((1 << bits) - 1)
     return out
 
 
@@ -37,15 +38,17 @@ def _u16(x):
 
 
 def _compare_state(cache, g, b, h, st: kv.KiviState):
+    import decode_attention_loopvq_amd as lvq
+    kb, vb, _ = lvq.kivi_widths(g)
     ring = g.R + g.group
     L, nk, nv = int(cache.len[b]), int(cache.n_kq[b]), int(cache.n_vq[b])
     assert (L, nk, nv) == (st.length, st.n_kq, st.n_vq), ((L, nk, nv), (st.length, st.n_kq, st.n_vq))
     if nk:
-        np.testing.assert_array_equal(_unpack(cache.k_codes[b, h, :nk].cpu().numpy()), np.concatenate(st.k_codes))
+        np.testing.assert_array_equal(_unpack(cache.k_codes[b, h, :nk].cpu().numpy(), kb), np.concatenate(st.k_codes))
         np.testing.assert_array_equal(_u16(cache.k_scale[b, h, :nk // g.group].cpu().numpy()), _u16(np.stack(st.k_s)))
         np.testing.assert_array_equal(_u16(cache.k_zero[b, h, :nk // g.group].cpu().numpy()), _u16(np.stack(st.k_z)))
     if nv:
-        np.testing.assert_array_equal(_unpack(cache.v_codes[b, h, :nv].cpu().numpy()), np.stack(st.v_codes))
+        np.testing.assert_array_equal(_unpack(cache.v_codes[b, h, :nv].cpu().numpy(), vb), np.stack(st.v_codes))
         np.testing.assert_array_equal(_u16(cache.v_scale[b, h, :nv].cpu().numpy()), _u16(np.stack(st.v_s)))
         np.testing.assert_array_equal(_u16(cache.v_zero[b, h, :nv].cpu().numpy()), _u16(np.stack(st.v_z)))
     kres = cache.k_res[b, h].cpu().numpy()
@@ -57,22 +60,26 @@ def _compare_state(cache, g, b, h, st: kv.KiviState):
 
 
 def _check_attn(prob, rows, states):
+    """rows: (request, KV head); every query head of those KV heads is checked."""
     import decode_attention_loopvq_amd as lvq
     g, cache = prob.g, prob.cache
+    Hq = lvq.kivi_widths(g)[2]
+    nrep = Hq // g.H
     max_len = int(cache.len.max())
     worst = 0.0
     for ns in (0, 1, 5):
-        lse = torch.empty((cache.B, g.H), dtype=torch.float32, device="cuda")
+        lse = torch.empty((cache.B, Hq), dtype=torch.float32, device="cuda")
         out, _ = lvq.kivi_decode_attn(g, prob.q, cache, max_len, prob.sm_scale, lse_out=lse, num_splits=ns)
         torch.cuda.synchronize()
         for (b, h) in rows:
-            q = prob.q[b, h].float().cpu().numpy().astype(np.float64)
-            o_ref, lse_ref = kv.attention(q, states[(b, h)], prob.sm_scale)
-            o = out[b, h].double().cpu().numpy()
-            err = np.abs(o - o_ref).max() / np.abs(o_ref).max()
-            worst = max(worst, err)
-            assert err <= REL_TOL, f"row ({b},{h}) splits {ns}: rel err {err:.3e}"
-            assert abs(float(lse[b, h]) - lse_ref) <= 2e-3
+            for hq in range(h * nrep, (h + 1) * nrep):
+                q = prob.q[b, hq].float().cpu().numpy().astype(np.float64)
+                o_ref, lse_ref = kv.attention(q, states[(b, h)], prob.sm_scale)
+                o = out[b, hq].double().cpu().numpy()
+                err = np.abs(o - o_ref).max() / np.abs(o_ref).max()
+                worst = max(worst, err)
+                assert err <= REL_TOL, f"row ({b},{hq}) over KV head {h}, splits {ns}: rel err {err:.3e}"
+                assert abs(float(lse[b, hq]) - lse_ref) <= 2e-3
     return worst
 
 
@@ -81,7 +88,7 @@ def _states(prob, rows):
     v = prob.v.cpu().numpy()
     states = {}
     for (b, h) in rows:
-        st = kv.KiviState(D=prob.g.D, group=prob.g.group, R=prob.g.R)
+        st = kv.KiviState(D=prob.g.D, group=prob.g.group, R=prob.g.R, bits=prob.g.bits, v_bits=prob.g.v_bits)
         st.prefill(k[b, h], v[b, h])
         states[(b, h)] = st
     return states
@@ -176,3 +183,48 @@ def test_prefill_strided_inputs(layout):
             st = kv.KiviState(D=g.D, group=g.group, R=g.R)
             st.prefill(kh[b, h], vh[b, h])
             _compare_state(cache, g, b, h, st)
+
+
+# KIVI-4, mixed key/value widths and grouped-query attention ("core design" with b = 4; the page's note
+# on GQA support): prefill of a length with a partial key group and a long value overflow, then 40
+# single-token appends (a key flush among them); state bit-exact, every query head's output against
+# the oracle over its KV head.
+@pytest.mark.parametrize("bits,v_bits,H,Hq", [
+    (4, 0, 2, 0), (4, 2, 2, 0), (2, 4, 2, 0), (2, 0, 2, 8), (4, 4, 1, 32),
+], ids=["k4v4", "k4v2", "k2v4", "k2v2-gqa4", "k4v4-gqa32"])
+def test_widths_and_grouped_queries(bits, v_bits, H, Hq):
+    import decode_attention_loopvq_amd as lvq
+    import synth.kivi as synk
+    from tests import harness
+    cfg = kivi_config("kivi-b16-4k", B=2, H=H, L=700, bits=bits, v_bits=v_bits, Hq=Hq)
+    _say(f"[kivi widths] k{bits} v{v_bits or bits} H={H} Hq={Hq or H}")
+    prob = harness.build_kivi(cfg)
+    rows = [(b, h) for b in range(2) for h in range(H)]
+    states = _states(prob, rows)
+    for (b, h) in rows:
+        _compare_state(prob.cache, prob.g, b, h, states[(b, h)])
+    kn, vn = synk.new_tokens(cfg, 40, "cuda")
+    kn_h, vn_h = kn.cpu().numpy(), vn.cpu().numpy()
+    for i in range(40):
+        lvq.kivi_append(prob.g, kn[i][:, :, None, :], vn[i][:, :, None, :], prob.cache, prefill=False)
+        for (b, h) in rows:
+            states[(b, h)].append(kn_h[i, b, h], vn_h[i, b, h])
+    torch.cuda.synchronize()
+    for (b, h) in rows:
+        _compare_state(prob.cache, prob.g, b, h, states[(b, h)])
+    worst = _check_attn(prob, rows, states)
+    _say(f"[kivi widths] worst rel err {worst:.3e}")
+
+
+@pytest.mark.parametrize("name", ["kivi4-b16-4k", "kivi-gqa-b16-4k"])
+def test_variant_workloads_full_size_sampled(name):
+    from tests import harness
+    cfg = kivi_config(name)
+    _say(f"[kivi full] {name}")
+    prob = harness.build_kivi(cfg)
+    rows = [(0, 0), (9, cfg.H // 2), (15, cfg.H - 1)]
+    states = _states(prob, rows)
+    for (b, h) in rows:
+        _compare_state(prob.cache, prob.g, b, h, states[(b, h)])
+    worst = _check_attn(prob, rows, states)
+    _say(f"[kivi full] {name} worst rel err {worst:.3e}")
