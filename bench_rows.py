@@ -19,6 +19,8 @@ roofline that bounds it, and prints one JSON line per measurement:
   kivi-append      kivi_append of one decode token
   kivi-attn        kivi_decode_attn after the 4K prefill
   kmeans-step      one Fisher-weighted k-means step (lvq_encode + lvq_codebook_update), 16 x 2048 tokens
+  kivi4-attn       kivi_decode_attn with 4-bit keys and values (KIVI-4), B=16, H=32, 4K
+  kivi-gqa-attn    kivi_decode_attn, 2-bit, 32 query heads over 8 KV heads, B=16, 4K
 
 Inputs are seeded and synthetic (synth/), timed with HIP events on the
 launch stream after warm-up.  Peaks: HBM 8 TB/s, dense bf16 MFMA
@@ -230,14 +232,45 @@ def kivi_rows(reps):
     emit(row="kivi-append", workload=cfg.name, B=cfg.B, H=cfg.H, us_per_token=round(t * 1e6, 2))
 
 
+def kivi_variant_row(row, name, reps):
+    """Prefill then time decode attention on a KIVI variant workload; algorithmic bytes per call are
+    each KV head's codes at their widths, its scales and zero-points and fp16 residual, plus every
+    query head's fp16 query and fp32 output."""
+    import torch
+    import decode_attention_loopvq_amd as lvq
+    from synth import kivi as synk
+    from synth.configs import kivi_config
+    from tests import harness
+
+    cfg = kivi_config(name)
+    p = harness.build_kivi(cfg)
+    g = p.g
+    kb, vb, Hq = lvq.kivi_widths(g)
+    out = torch.empty((cfg.B, Hq, cfg.D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lvq.kivi_decode_attn_workspace(g, cfg.B, cfg.L), dtype=torch.uint8, device="cuda")
+
+    def attn():
+        lvq.kivi_decode_attn(g, p.q, p.cache, cfg.L, p.sm_scale, out=out, ws=ws)
+
+    t = timed(attn, reps * 10)
+    n_q = cfg.L - cfg.R
+    per_kv = (n_q * cfg.D * kb // 8 + (n_q // cfg.group) * cfg.D * 4 + n_q * cfg.D * vb // 8
+              + n_q * (cfg.D // cfg.group) * 4 + cfg.R * cfg.D * 2 * 2)
+    by = cfg.B * cfg.H * per_kv + cfg.B * Hq * cfg.D * (2 + 4)
+    emit(row=row, workload=cfg.name, B=cfg.B, H=cfg.H, Hq=Hq, key_bits=kb, value_bits=vb, L=cfg.L,
+         us_per_call=round(t * 1e6, 2), gbps=round(by / t / 1e9, 1), hbm_frac=round(by / t / PEAK_HBM, 4),
+         bytes_per_call=by, token_heads_per_s=round(cfg.B * Hq * cfg.L / t, 1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--reps", type=int, default=5)
-    ap.add_argument("--only", nargs="*", default=None, help="encode attn-32k attn-deep attn-1k kivi kmeans")
+    ap.add_argument("--only", nargs="*", default=None, help="encode attn-32k attn-deep attn-1k kivi kivi4 kivi-gqa kmeans")
     args = ap.parse_args()
     import torch
     assert torch.cuda.is_available(), "bench_rows.py needs a GPU"
-    want = set(args.only) if args.only else {"encode", "attn-32k", "attn-deep", "attn-1k", "kivi", "kmeans"}
+    want = set(args.only) if args.only else {"encode", "attn-32k", "attn-deep", "attn-1k", "kivi", "kivi4", "kivi-gqa",
+                                                         "kmeans"}
     if "encode" in want:
         encode_rows(args.reps)
     if "attn-32k" in want:
@@ -250,6 +283,10 @@ def main():
         kivi_rows(args.reps)
     if "kmeans" in want:
         kmeans_row(args.reps)
+    if "kivi4" in want:
+        kivi_variant_row("kivi4-attn", "kivi4-b16-4k", args.reps)
+    if "kivi-gqa" in want:
+        kivi_variant_row("kivi-gqa-attn", "kivi-gqa-b16-4k", args.reps)
 
 
 if __name__ == "__main__":
