@@ -30,6 +30,12 @@ are counted from 0 here; RoPE is the rotate-half form pairing channel i with
 i + D/2, theta_i = base^(-2i/D), angles at the absolute token position
 counted from 0; the query is supplied already rotated; the attention output
 is rounded to fp32 only by the caller of the oracle.
+
+Key scale stream (TaSQ+LoopVQ, the page's limitations note: the keys carry an
+extra fp16 scale of about 0.008 bit per element): read as one fp16 scale per
+paged key token and loop step, shared by the heads (16 bits over H*D = 2048
+elements at 16 heads of 128 channels), multiplying the reconstructed key; the
+transform that produces the scales is not on the page, so they are inputs.
 """
 
 from __future__ import annotations
@@ -204,16 +210,20 @@ def encode_request(raw: np.ndarray, E: np.ndarray, geo: Geometry, L: int) -> np.
     return out
 
 
-def assemble_step(t: int, raw: np.ndarray, idx: np.ndarray, E: np.ndarray, geo: Geometry, L: int) -> np.ndarray:
+def assemble_step(t: int, raw: np.ndarray, idx: np.ndarray, E: np.ndarray, geo: Geometry, L: int,
+                  scales: np.ndarray = None) -> np.ndarray:
     """Pre-RoPE keys (or values) that loop step t attends over: [L][D] float64.
 
     Sinks and recent tokens come from the bf16 values of step t; paged tokens
-    from their indices through B_t."""
+    from their indices through B_t, each multiplied by its scale when `scales`
+    ([n_tok] for step t, the key scale stream) is given."""
     _, q_lo, q_hi = cache_regions(L, geo)
     beta, m = block_of_step(t, geo.Tc)
     out = np.asarray(raw[:L, t, :], dtype=np.float64).copy()
     if q_hi > q_lo:
         out[q_lo:q_hi] = dequant_step(idx[beta], E[beta], m, geo.Tc, geo.G)
+        if scales is not None:
+            out[q_lo:q_hi] *= np.asarray(scales[:q_hi - q_lo], dtype=np.float64)[:, None]
     return out
 
 
@@ -278,13 +288,15 @@ def merge(parts: Sequence[Tuple[np.ndarray, float]]) -> Tuple[np.ndarray, float]
 
 def decode_step(q: np.ndarray, t: int, raw_k: np.ndarray, raw_v: np.ndarray,
                 idx_k: np.ndarray, idx_v: np.ndarray, E_k: np.ndarray, E_v: np.ndarray,
-                geo: Geometry, L: int, sm_scale: float, base: float = 10000.0) -> Tuple[np.ndarray, float]:
+                geo: Geometry, L: int, sm_scale: float, base: float = 10000.0,
+                k_scales: np.ndarray = None) -> Tuple[np.ndarray, float]:
     """Decode attention of the post-RoPE query q at loop step t over the whole cache.
 
     raw_k/raw_v: [>=L][T][D] bf16 values (sinks and recent tokens are read from
     them); idx_k/idx_v: [NB][n_tok][NG] indices of the paged tokens; E_k/E_v:
-    [NB][NG][K][G] codebooks.  Keys are rotated at positions 0..L-1."""
-    k = assemble_step(t, raw_k, idx_k, E_k, geo, L)
+    [NB][NG][K][G] codebooks; k_scales: optional [n_tok][T] key scale stream of
+    the paged tokens.  Keys are rotated at positions 0..L-1."""
+    k = assemble_step(t, raw_k, idx_k, E_k, geo, L, None if k_scales is None else np.asarray(k_scales)[:, t])
     v = assemble_step(t, raw_v, idx_v, E_v, geo, L)
     k = apply_rope(k, np.arange(L), base)
     return attention(q, k, v, sm_scale)

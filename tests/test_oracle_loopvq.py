@@ -391,3 +391,58 @@ def test_lossless_cache_equals_textbook_attention():
         w = np.exp(s - s.max())
         np.testing.assert_allclose(o, (w @ raw_v[:, t]) / w.sum(), atol=1e-12)
         assert abs(lse - logsumexp(s)) < 1e-12
+
+
+
+# ---------------------------------------------------------------------------
+# Key scale stream (TaSQ+LoopVQ plumbing)
+# ---------------------------------------------------------------------------
+
+def _scale_case(seed=21, L=150):
+    geo = lv.Geometry(D=16, T=4, Tc=2, G=8, K=16, sink=8, window=16, page=8)
+    rng = np.random.default_rng(seed)
+    raw_k = rng.standard_normal((L, geo.T, geo.D))
+    raw_v = rng.standard_normal((L, geo.T, geo.D))
+    E_k = rng.standard_normal((geo.NB, geo.NG, geo.K, geo.G))
+    E_v = rng.standard_normal((geo.NB, geo.NG, geo.K, geo.G))
+    idx_k = lv.encode_request(raw_k, E_k, geo, L)
+    idx_v = lv.encode_request(raw_v, E_v, geo, L)
+    q = rng.standard_normal(geo.D)
+    return geo, rng, raw_k, raw_v, E_k, E_v, idx_k, idx_v, q
+
+
+def test_uniform_key_scale_equals_scaled_codebook():
+    """A scale alpha on every paged key token equals multiplying the key codebooks by alpha
+    (reconstruction is linear in the codeword), for every loop step."""
+    geo, rng, raw_k, raw_v, E_k, E_v, idx_k, idx_v, q = _scale_case()
+    L = raw_k.shape[0]
+    n_tok = idx_k.shape[1]
+    for alpha in (0.37, 2.5):
+        sc = np.full((n_tok, geo.T), alpha)
+        for t in range(geo.T):
+            o1, l1 = lv.decode_step(q, t, raw_k, raw_v, idx_k, idx_v, E_k, E_v, geo, L, 0.3, k_scales=sc)
+            o2, l2 = lv.decode_step(q, t, raw_k, raw_v, idx_k, idx_v, alpha * E_k, E_v, geo, L, 0.3)
+            np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+            assert abs(l1 - l2) < 1e-12
+
+
+def test_zero_key_scales_give_uniform_paged_logits():
+    """Zero scales make every paged logit 0: the output is the closed form
+    (sum_paged v + sum_bf16 e^{s_j} v_j) / (n_paged + sum_bf16 e^{s_j})."""
+    geo, rng, raw_k, raw_v, E_k, E_v, idx_k, idx_v, q = _scale_case(seed=5, L=131)
+    L = raw_k.shape[0]
+    _, q_lo, q_hi = lv.cache_regions(L, geo)
+    sc = np.zeros((idx_k.shape[1], geo.T))
+    t = 3
+    o, lse = lv.decode_step(q, t, raw_k, raw_v, idx_k, idx_v, E_k, E_v, geo, L, 0.5, k_scales=sc)
+    v = lv.assemble_step(t, raw_v, idx_v, E_v, geo, L)
+    bf = np.r_[0:q_lo, q_hi:L]
+    ang = lv.rope_angles(bf, geo.D)
+    kb = raw_k[bf, t, :]
+    half = geo.D // 2
+    rot = np.concatenate([kb[:, :half] * np.cos(ang) - kb[:, half:] * np.sin(ang),
+                          kb[:, half:] * np.cos(ang) + kb[:, :half] * np.sin(ang)], axis=1)
+    e = np.exp(0.5 * rot @ q)
+    want = (v[q_lo:q_hi].sum(axis=0) + e @ v[bf]) / ((q_hi - q_lo) + e.sum())
+    np.testing.assert_allclose(o, want, rtol=1e-10, atol=1e-12)
+    assert abs(lse - np.log((q_hi - q_lo) + e.sum())) < 1e-10
