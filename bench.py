@@ -272,7 +272,7 @@ def main():
 
     def full_args(t, l):
         return (gref, t, qs[t].data_ptr(), pools[l].data_ptr(), cache.page_table.data_ptr(),
-                int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, None, wks[l].data_ptr(),
+                int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, None, None, wks[l].data_ptr(),
                 wvs[l].data_ptr(), prob.slices.data_ptr(), prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(),
                 prob.rope16.data_ptr(), rope_len, C.c_float(prob.sm_scale), outs[l].data_ptr(), None,
                 ws.data_ptr(), ws_bytes, args.num_splits, B, sh)
@@ -295,7 +295,8 @@ def main():
 
     def quant_args(t, l):
         return (gref, t, qs[t].data_ptr(), pools[l].data_ptr(), cache.page_table.data_ptr(),
-                int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, None, prob.slices.data_ptr(),
+                int(cache.page_table.shape[1]), cache.seq_len.data_ptr(), cache.max_len, None, None,
+                prob.slices.data_ptr(),
                 prob.rope_cos.data_ptr(), prob.rope_sin.data_ptr(), prob.rope16.data_ptr(), rope_len,
                 C.c_float(prob.sm_scale), part_o.data_ptr(), part_lse.data_ptr(), S, S, qws.data_ptr(),
                 qws.numel(), B, sh)

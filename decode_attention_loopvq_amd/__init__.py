@@ -195,11 +195,12 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
                     slices: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor, sm_scale: float,
                     out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
                     ws: Optional[torch.Tensor] = None, num_splits: int = 0,
-                    stream=None, rope_f16: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None
-                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                    stream=None, rope_f16: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None,
+                    k_scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Decode attention of loop step `step`; returns (out [B][H][D] fp32, lse [B][H] or None).
     rope_f16 (lvq_rope_table_f16) is required with bf16 codebooks; order (int32 [B], e.g. from
-    lvq_request_order) groups the requests into workgroups (None: in batch order)."""
+    lvq_request_order) groups the requests into workgroups (None: in batch order); k_scales (fp16
+    [physical pages][T][8]) is the key scale stream of the index tokens (None: no scales)."""
     _need(q, "q", torch.bfloat16)
     B = q.shape[0]
     if tuple(q.shape) != (B, g.H, g.D):
@@ -217,6 +218,7 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
     if seq_len.numel() != B or page_table.dim() != 2 or page_table.shape[0] != B:
         raise ValueError("seq_len / page_table batch does not match q")
     _need_order(order, B)
+    _need_kscales(k_scales, g, pool)
     if out is None:
         out = torch.empty((B, g.H, g.D), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32)
@@ -228,7 +230,8 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
     _need(ws, "ws")
     check(lib.lvq_decode_attn(C.byref(g), int(step), q.data_ptr(), pool.data_ptr(), page_table.data_ptr(),
                               int(page_table.shape[1]), seq_len.data_ptr(), int(max_len),
-                              order.data_ptr() if order is not None else None, win_k.data_ptr(),
+                              order.data_ptr() if order is not None else None,
+                              k_scales.data_ptr() if k_scales is not None else None, win_k.data_ptr(),
                               win_v.data_ptr(), slices.data_ptr(), rope_cos.data_ptr(), rope_sin.data_ptr(),
                               _rope_f16_ptr(rope_f16, rope_cos), int(rope_cos.shape[0]), float(sm_scale),
                               out.data_ptr(),
@@ -236,6 +239,13 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
                               ws.numel() * ws.element_size(), int(num_splits), int(B), _stream(stream)),
           "lvq_decode_attn")
     return out, lse_out
+
+
+def _need_kscales(k_scales: Optional[torch.Tensor], g: lvq_geom, pool: torch.Tensor):
+    if k_scales is not None:
+        _need(k_scales, "k_scales", torch.float16)
+        if tuple(k_scales.shape) != (pool.shape[0], g.T, 8):
+            raise ValueError("k_scales must be [physical pages][T][8], one page per pool page")
 
 
 def _need_order(order: Optional[torch.Tensor], B: int):
@@ -287,7 +297,8 @@ def lvq_quant_partial(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tenso
                       seq_len: torch.Tensor, max_len: int, slices: torch.Tensor, rope_cos: torch.Tensor,
                       rope_sin: torch.Tensor, sm_scale: float, part_o: torch.Tensor, part_lse: torch.Tensor,
                       num_splits: int, ws: Optional[torch.Tensor] = None, stream=None,
-                      rope_f16: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None):
+                      rope_f16: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None,
+                      k_scales: Optional[torch.Tensor] = None):
     """Index-page partials into part_o [B*H][S_tot][D], part_lse [B*H][S_tot] (slots 0..num_splits-1)."""
     _need(q, "q", torch.bfloat16)
     _need(pool, "pool", torch.uint8)
@@ -298,13 +309,15 @@ def lvq_quant_partial(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tenso
     _need(part_lse, "part_lse", torch.float32)
     B = q.shape[0]
     _need_order(order, B)
+    _need_kscales(k_scales, g, pool)
     need = lvq_quant_partial_workspace(g, B, max_len)
     if ws is None:
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
     _need(ws, "ws")
     check(lib.lvq_quant_partial(C.byref(g), int(step), q.data_ptr(), pool.data_ptr(), page_table.data_ptr(),
                                 int(page_table.shape[1]), seq_len.data_ptr(), int(max_len),
-                                order.data_ptr() if order is not None else None, slices.data_ptr(),
+                                order.data_ptr() if order is not None else None,
+                                k_scales.data_ptr() if k_scales is not None else None, slices.data_ptr(),
                                 rope_cos.data_ptr(), rope_sin.data_ptr(), _rope_f16_ptr(rope_f16, rope_cos),
                                 int(rope_cos.shape[0]), float(sm_scale), part_o.data_ptr(), part_lse.data_ptr(),
                                 int(num_splits), int(part_lse.shape[1]),

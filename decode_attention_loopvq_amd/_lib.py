@@ -61,7 +61,7 @@ def _load():
                                _P, _P, _I, _I, _P]
     lib.lvq_decode_attn_workspace.restype = _S
     lib.lvq_decode_attn_workspace.argtypes = [C.POINTER(lvq_geom), _I, _I, _I]
-    lib.lvq_decode_attn.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P, _P,
+    lib.lvq_decode_attn.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _I, C.c_float, _P, _P, _P, _S, _I, _I, _P]
     lib.lvq_request_order.argtypes = [_P, _I, _I, _P, _P]
     lib.lvq_window_append.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, _P, _P, _P, _I, _I, _P]
@@ -69,8 +69,8 @@ def _load():
                                         C.POINTER(C.c_int64), _P, _P, _P, _I, _P, _P, _I, _I, _P]
     lib.lvq_decode_attn_splits.restype = _I
     lib.lvq_decode_attn_splits.argtypes = [C.POINTER(lvq_geom), _I, _I]
-    lib.lvq_quant_partial.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P, _I,
-                                      C.c_float, _P, _P, _I, _I, _P, _S, _I, _P]
+    lib.lvq_quant_partial.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P, _P,
+                                      _I, C.c_float, _P, _P, _I, _I, _P, _S, _I, _P]
     lib.lvq_quant_partial_workspace.restype = _S
     lib.lvq_quant_partial_workspace.argtypes = [C.POINTER(lvq_geom), _I, _I]
     lib.lvq_window_partial.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, _I, _P, _P, _P, _P, _I, C.c_float, _P, _P,

@@ -43,6 +43,7 @@ struct AttnArgs {
     int B;
     int max_len;                // device lengths are clamped to this
     const int32_t* order;       // [B] request of each workgroup slot (NULL: request i in slot i)
+    const uint16_t* kscale;     // key scale stream fp16 [physical page][T][8] (NULL: none)
     int rope_len;
     const uint32_t* qpack;      // [B*H][64] packed fp16 query rows (written and read by index_attn_kernel)
     const uint4* rope16;        // [16][rope_len] packed fp16 cos/sin chunks (lvq_rope_table_f16)
@@ -233,7 +234,8 @@ __global__ void __launch_bounds__(256) quant_partial_kernel(AttnArgs a) {
                     part += qA[i + u] * r1 + qB[i + u] * r2;
                 }
             }
-            const float s = (part + __shfl_xor(part, 32, 64)) * a.scale_log2;
+            float s = (part + __shfl_xor(part, 32, 64)) * a.scale_log2;
+            if (a.kscale) s *= f16_to_f32(a.kscale[(phys * g.T + a.step) * 8 + (tok & 7)]);
             float vA[32], vB[32];
 #pragma unroll
             for (int q = 0; q < GPC; ++q) {
@@ -456,7 +458,7 @@ __device__ __forceinline__ bool split_ranges(const AttnArgs& a, int split, const
 // after a barrier every output sums 16 partials.  The weight total is exact:
 // every group's bins add up to the same integer.
 // ---------------------------------------------------------------------------
-template <int C, int R>
+template <int C, int R, bool KS>
 __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
     constexpr int D = 128, K = 256, NG = D / C, NT = kIThreads, NW = NT / 64;
     constexpr int CPW = kChunksPerWave;
@@ -575,6 +577,16 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
         }
     };
 
+    // key scales of chunk c (KS): token tau of request j at (page, step, tau & 7) of the scale stream
+    auto load_ks = [&](int c, const uint32_t (&pid)[R], float (&ks)[R]) {
+        if constexpr (KS) {
+            const int tau = c * kChunk + lane;
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                ks[j] = f16_to_f32(a.kscale[(uint64_t(pid[j]) * g.T + a.step) * 8 + (tau & 7)]);
+        }
+    };
+
     // ---- scores ----
     uint4 tr[16];                                   // cos/sin of the lane's position, 4 frequencies each
     auto load_tr = [&](int c, auto qc) {
@@ -643,10 +655,11 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
             acc[j][1] = dot2h(kh23, ph23, acc[j][1]);
         }
     };
-    auto finish = [&](int c, auto jc) {
+    auto finish = [&](int c, auto jc, const float (&ks)[R]) {
         constexpr int j = decltype(jc)::value;
         const bool in = in_req(j, c * kChunk + lane);
-        const float s_all = acc[j][0] + acc[j][1];
+        float s_all = acc[j][0] + acc[j][1];
+        if constexpr (KS) s_all *= ks[j];
         acc[j][0] = 0.f;
         acc[j][1] = 0.f;
         sreg[CPW - 1][j] = s_all;
@@ -661,7 +674,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
     uint32_t G[2][GQ][GW];
     uint32_t qs[2][16];
     // One chunk: steps k = (qq, j); the last step issues the first gathers of the next chunk (ikn).
-    auto run_chunk = [&](int c, const uint32_t (&ikc)[R][IW], const uint32_t (&ikn)[R][IW]) {
+    auto run_chunk = [&](int c, const uint32_t (&ikc)[R][IW], const uint32_t (&ikn)[R][IW], const float (&ks)[R]) {
         shift_scores();
         StaticFor<0, NSTEP>::run([&](auto kc) {
             constexpr int k = decltype(kc)::value, qq = k / R, j = k % R, b = k & 1;
@@ -678,7 +691,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
             // at the start of a quarter, the cos/sin of the next quarter (of the wave's next chunk after the last)
             if constexpr (j == 0) load_tr(qq < 3 ? c : c + NW, std::integral_constant<int, (qq + 1) % 4>{});
             compute(std::integral_constant<int, qq>{}, std::integral_constant<int, j>{}, G[b], qs[b]);
-            if constexpr (qq == 3) finish(c, std::integral_constant<int, j>{});
+            if constexpr (qq == 3) finish(c, std::integral_constant<int, j>{}, ks);
         });
     };
 #pragma unroll
@@ -698,9 +711,11 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
         int c = c0;
         uint32_t pidA[R], pidB[R];
         uint32_t ikA[R][IW], ikB[R][IW];
+        float ksA[R], ksB[R];
         load_pid(c, pidA);
         load_pid(c + NW, pidB);
         load_idx(c, 0, pidA, ikA);
+        load_ks(c, pidA, ksA);
         load_pid(c + 2 * NW, pidA);
         load_tr(c, std::integral_constant<int, 0>{});
         __syncthreads();                            // K slice staged, query rows packed
@@ -708,14 +723,16 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
         load_q(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, qs[0]);
         while (c * kChunk < t_hi) {
             load_idx(c + NW, 0, pidB, ikB);
+            load_ks(c + NW, pidB, ksB);
             load_pid(c + 3 * NW, pidB);
-            run_chunk(c, ikA, ikB);
+            run_chunk(c, ikA, ikB, ksA);
             c += NW;
             ++nch;
             if (c * kChunk >= t_hi) break;
             load_idx(c + NW, 0, pidA, ikA);
+            load_ks(c + NW, pidA, ksA);
             load_pid(c + 3 * NW, pidA);
-            run_chunk(c, ikB, ikA);
+            run_chunk(c, ikB, ikA, ksB);
             c += NW;
             ++nch;
         }
@@ -1729,10 +1746,13 @@ lvq_status launch_quant(AttnArgs& a, void* scratch, hipStream_t stream) {
         a.fix_bits = 32 - ceil_log2(long(a.pps) * g.page + 1);
         const int R = reqs_per_wg(g);
         const dim3 grid(g.H, a.num_splits, ceil_div(a.B, R));
-        if (g.c == 8)
-            hipLaunchKernelGGL((index_attn_kernel<8, 4>), grid, dim3(kIThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL((index_attn_kernel<4, 2>), grid, dim3(kIThreads), 0, stream, a);
+        if (g.c == 8) {
+            if (a.kscale) hipLaunchKernelGGL((index_attn_kernel<8, 4, true>), grid, dim3(kIThreads), 0, stream, a);
+            else hipLaunchKernelGGL((index_attn_kernel<8, 4, false>), grid, dim3(kIThreads), 0, stream, a);
+        } else {
+            if (a.kscale) hipLaunchKernelGGL((index_attn_kernel<4, 2, true>), grid, dim3(kIThreads), 0, stream, a);
+            else hipLaunchKernelGGL((index_attn_kernel<4, 2, false>), grid, dim3(kIThreads), 0, stream, a);
+        }
     } else {
         const dim3 grid(a.num_splits, g.H, (a.B + 1) / 2);
         const size_t red_bytes = 4 * (g.D + 2) * sizeof(float);
@@ -1789,8 +1809,8 @@ void set_slices(AttnArgs* a, const void* slices) {
 
 extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
                                         const int32_t* page_table, int32_t pt_stride, const int32_t* seq_len,
-                                        int32_t max_len, const int32_t* order, const void* slices,
-                                        const float* rope_cos,
+                                        int32_t max_len, const int32_t* order, const void* k_scales,
+                                        const void* slices, const float* rope_cos,
                                         const float* rope_sin, const void* rope_f16, int32_t rope_len,
                                         float sm_scale, float* part_o,
                                         float* part_lse, int32_t num_splits, int32_t S_tot, void* ws,
@@ -1800,6 +1820,7 @@ extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const 
                             rope_len, sm_scale, B, &a);
     if (st != LVQ_OK) return st;
     a.order = order;
+    a.kscale = static_cast<const uint16_t*>(k_scales);
     const Geo& g = a.geo;
     LVQ_REQUIRE(num_splits >= 1 && num_splits <= 1024 && S_tot >= num_splits, LVQ_ERR_INVALID_ARG,
                 "lvq_quant_partial: num_splits %d, S_tot %d", num_splits, S_tot);
@@ -1853,8 +1874,8 @@ extern "C" lvq_status lvq_window_partial(const lvq_geom* gp, int32_t step, const
 
 extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
                                       const int32_t* page_table, int32_t pt_stride, const int32_t* seq_len,
-                                      int32_t max_len, const int32_t* order, const void* win_k,
-                                      const void* win_v, const void* slices,
+                                      int32_t max_len, const int32_t* order, const void* k_scales,
+                                      const void* win_k, const void* win_v, const void* slices,
                                       const float* rope_cos, const float* rope_sin, const void* rope_f16,
                                       int32_t rope_len, float sm_scale, float* out, float* lse_out, void* ws,
                                       size_t ws_bytes,
@@ -1864,9 +1885,12 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
                             rope_len, sm_scale, B, &a);
     if (st != LVQ_OK) return st;
     a.order = order;
+    a.kscale = static_cast<const uint16_t*>(k_scales);
     const Geo& g = a.geo;
     LVQ_REQUIRE(num_splits >= -1 && num_splits <= 1024, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: num_splits %d",
                 num_splits);
+    LVQ_REQUIRE(num_splits != -1 || !k_scales, LVQ_ERR_UNSUPPORTED,
+                "lvq_decode_attn: the single-pass kernel (num_splits -1) takes no key scale stream");
     LVQ_REQUIRE(num_splits != -1 || g.cb == LVQ_BF16, LVQ_ERR_UNSUPPORTED,
                 "lvq_decode_attn: the single-pass kernel (num_splits -1) needs bf16 codebooks");
     LVQ_REQUIRE(pt_stride >= 0, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: negative pt_stride");
@@ -1877,7 +1901,7 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
                 "lvq_decode_attn: NULL pool or page table");
     LVQ_REQUIRE(pt_stride >= max_pages, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: pt_stride %d < %d pages",
                 pt_stride, max_pages);
-    const bool single = num_splits == -1 || (num_splits == 0 && use_full(g, B, max_pages));
+    const bool single = num_splits == -1 || (num_splits == 0 && !k_scales && use_full(g, B, max_pages));
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
     LVQ_REQUIRE(single || splits_fit(g, max_pages, S), LVQ_ERR_INVALID_ARG,
                 "lvq_decode_attn: %d splits of %d index pages exceed %d tokens per split", S, max_pages, kMaxSplitTok);

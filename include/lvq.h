@@ -235,6 +235,16 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  *             leaves its slot empty and that request unattended (its output
  *             is then undefined), never an out-of-bounds access.  The output
  *             does not depend on the grouping.
+ *  k_scales   device fp16 [physical page][T][8] or NULL: the key scale stream
+ *             of TaSQ+LoopVQ (LoopVQ page, limitations note: an extra fp16
+ *             key scale of about 0.008 bit per element, read as one per index
+ *             token and loop step, shared by the heads).  Index token i of
+ *             physical page p is scored with its reconstructed key times
+ *             k_scales[(p*T + step)*8 + i]; bf16 window tokens are not scaled.
+ *             One page of scales per pool page.  Not taken by the single-pass
+ *             kernel (num_splits -1: LVQ_ERR_UNSUPPORTED).  The transform that
+ *             produces the scales is not part of this library: lvq_encode
+ *             takes keys already divided by their scale.
  *  slices     slices of ALL steps (layout above); the call reads step `step`.
  *             bf16 slice entries must lie within the binary16 range
  *             (|x| <= 65504): the index-page pass converts the step's key
@@ -257,7 +267,7 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
 LVQ_API lvq_status lvq_decode_attn(const lvq_geom* g, int32_t step, const void* q,
                            const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
                            const int32_t* seq_len, int32_t max_len, const int32_t* order,
-                           const void* win_k, const void* win_v,
+                           const void* k_scales, const void* win_k, const void* win_v,
                            const void* slices, const float* rope_cos, const float* rope_sin,
                            const void* rope_f16, int32_t rope_len, float sm_scale, float* out, float* lse_out,
                            void* ws, size_t ws_bytes, int32_t num_splits, int32_t B,
@@ -317,7 +327,7 @@ LVQ_API lvq_status lvq_request_order(const int32_t* seq_len, int32_t B, int32_t 
 LVQ_API lvq_status lvq_quant_partial(const lvq_geom* g, int32_t step, const void* q,
                                      const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
                                      const int32_t* seq_len, int32_t max_len, const int32_t* order,
-                                     const void* slices,
+                                     const void* k_scales, const void* slices,
                                      const float* rope_cos, const float* rope_sin, const void* rope_f16,
                                      int32_t rope_len, float sm_scale, float* part_o, float* part_lse,
                                      int32_t num_splits,

@@ -120,11 +120,12 @@ def host_codebooks(p: LoopVQProblem, h: int, kind: str) -> np.ndarray:
     return p.codebooks[:, h, kv].float().cpu().numpy().astype(np.float64)
 
 
-def run_step(p: LoopVQProblem, t: int, num_splits: int = 0, out=None, lse=None, ws=None, order=None):
+def run_step(p: LoopVQProblem, t: int, num_splits: int = 0, out=None, lse=None, ws=None, order=None,
+             k_scales=None):
     return lvq.lvq_decode_attn(p.g, t, p.q[t].contiguous(), p.cache.pool, p.cache.page_table, p.cache.seq_len,
                                p.cache.max_len, p.cache.win_k, p.cache.win_v, p.slices, p.rope_cos, p.rope_sin,
                                p.sm_scale, out=out, lse_out=lse, ws=ws, num_splits=num_splits, rope_f16=p.rope16,
-                               order=order)
+                               order=order, k_scales=k_scales)
 
 
 # ---------------------------------------------------------------------------

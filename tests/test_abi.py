@@ -48,7 +48,8 @@ def _attn(g, **over):
     args.update(over)
     gp = C.byref(g) if g is not None else None
     return _lib.lib.lvq_decode_attn(gp, args["step"], args["q"], args["pool"], args["pt"], args["pt_stride"],
-                                    args["seq_len"], args["max_len"], None, args["wk"], args["wv"], args["slices"],
+                                    args["seq_len"], args["max_len"], None, args.get("kscale"), args["wk"], args["wv"],
+                                    args["slices"],
                                     args["cos"], args["sin"], args["rope16"], args["rope_len"], args["scale"],
                                     args["out"],
                                     args["lse"], args["ws"], args["ws_bytes"], args["splits"], args["B"], None)
@@ -210,3 +211,9 @@ def test_codebook_update_rejects():
     assert call(maxp=-1) == INVALID
     assert call(B=0) == OK
     assert call(maxp=0) == OK
+
+
+def test_key_scales_rejected_by_single_pass():
+    """A key scale stream with the single-pass kernel (num_splits -1) is refused before any launch."""
+    g = _geom()
+    assert _attn(g, kscale=FAKE, splits=-1) == UNSUPPORTED
