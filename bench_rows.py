@@ -19,6 +19,8 @@ roofline that bounds it, and prints one JSON line per measurement:
   kivi-append      kivi_append of one decode token
   kivi-attn        kivi_decode_attn after the 4K prefill
   kmeans-step      one Fisher-weighted k-means step (lvq_encode + lvq_codebook_update), 16 x 2048 tokens
+  attn-6k-kscale   lvq_decode_attn on the 6K batch-64 workload with a key scale stream (TaSQ+LoopVQ),
+                   against the same calls without it
   kivi4-attn       kivi_decode_attn with 4-bit keys and values (KIVI-4), B=16, H=32, 4K
   kivi-gqa-attn    kivi_decode_attn, 2-bit, 32 query heads over 8 KV heads, B=16, 4K
 
@@ -142,7 +144,7 @@ def kmeans_row(reps):
          vectors_per_s=round(n_vec / t, 1), assign_flops=2.0 * g.K * g.G * n_vec)
 
 
-def attn_row(name, cfg_name, steps, reps, **over):
+def attn_row(name, cfg_name, steps, reps, kscale=False, **over):
     import torch
     import decode_attention_loopvq_amd as lvq
     from synth.configs import loopvq_config
@@ -164,11 +166,24 @@ def attn_row(name, cfg_name, steps, reps, **over):
         t_ord = timed(lambda: lvq.lvq_request_order(p.cache.seq_len, p.cache.max_len, out=order), reps * 10)
         extra = dict(order="by length (lvq_request_order, once per decode step)", order_us=round(t_ord * 1e6, 2))
 
+    # key scale stream (TaSQ+LoopVQ): fp16 per index token and loop step, 2 bytes per index token per call
+    sc = None
+    if kscale:
+        gen = torch.Generator(device="cuda").manual_seed(3)
+        sc = torch.exp(0.25 * torch.randn((p.cache.pool.shape[0], cfg.T, 8), generator=gen, device="cuda"))
+        sc = sc.to(torch.float16)
+        t0 = timed(lambda: [lvq.lvq_decode_attn(p.g, t, qs[t], p.cache.pool, p.cache.page_table, p.cache.seq_len,
+                                                p.cache.max_len, p.cache.win_k, p.cache.win_v, p.slices, p.rope_cos,
+                                                p.rope_sin, p.sm_scale, out=out, ws=ws, rope_f16=p.rope16,
+                                                order=order) for t in steps], reps) / len(steps)
+        per_call += sum(p.cache.n_pages) * 8 * 2
+        extra["unscaled_us_per_call"] = round(t0 * 1e6, 2)
+
     def run():
         for t in steps:
             lvq.lvq_decode_attn(p.g, t, qs[t], p.cache.pool, p.cache.page_table, p.cache.seq_len, p.cache.max_len,
                                 p.cache.win_k, p.cache.win_v, p.slices, p.rope_cos, p.rope_sin, p.sm_scale,
-                                out=out, ws=ws, rope_f16=p.rope16, order=order)
+                                out=out, ws=ws, rope_f16=p.rope16, order=order, k_scales=sc)
 
     t = timed(run, reps) / len(steps)
     emit(row=name, workload=cfg.name, B=cfg.B, H=cfg.H, L=cfg.L, steps=list(steps), us_per_call=round(t * 1e6, 2),
@@ -265,12 +280,12 @@ def kivi_variant_row(row, name, reps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--reps", type=int, default=5)
-    ap.add_argument("--only", nargs="*", default=None, help="encode attn-32k attn-deep attn-1k kivi kivi4 kivi-gqa kmeans")
+    ap.add_argument("--only", nargs="*", default=None, help="encode attn-32k attn-deep attn-1k attn-6k-kscale kivi kivi4 kivi-gqa kmeans")
     args = ap.parse_args()
     import torch
     assert torch.cuda.is_available(), "bench_rows.py needs a GPU"
-    want = set(args.only) if args.only else {"encode", "attn-32k", "attn-deep", "attn-1k", "kivi", "kivi4", "kivi-gqa",
-                                                         "kmeans"}
+    want = set(args.only) if args.only else {"encode", "attn-32k", "attn-deep", "attn-1k", "attn-6k-kscale", "kivi",
+                                                         "kivi4", "kivi-gqa", "kmeans"}
     if "encode" in want:
         encode_rows(args.reps)
     if "attn-32k" in want:
@@ -279,6 +294,8 @@ def main():
         attn_row("attn-deep", "loopvq-deep-ragged", (0, 15, 31), args.reps)
     if "attn-1k" in want:
         attn_row("attn-1k", "loopvq-b1-1k-fp32cb", range(4), args.reps * 20)
+    if "attn-6k-kscale" in want:
+        attn_row("attn-6k-kscale", "loopvq-b64-6k", range(4), args.reps, kscale=True)
     if "kivi" in want:
         kivi_rows(args.reps)
     if "kmeans" in want:
