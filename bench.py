@@ -138,7 +138,7 @@ def cpu_baseline(prob, rows, seconds):
 
 
 KERNELS = {"index_full_kernel": "index_full_kernel<8, 4> (single-pass attention)",
-           "index_attn_kernel": "index_attn_kernel<8, 4> (index-page partial)"}
+           "index_attn_kernel": "index_attn_kernel<8, 4, false> (index-page partial)"}
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_loopvq_amd", "csrc", "attn.hip")
 COPY_BYTES = 256 << 20
 
