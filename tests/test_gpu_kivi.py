@@ -162,15 +162,18 @@ def _layout(x: torch.Tensor, layout: str) -> torch.Tensor:
     raise ValueError(layout)
 
 
+@pytest.mark.parametrize("bits,v_bits", [(2, 0), (4, 2), (2, 4)], ids=["k2v2", "k4v2", "k2v4"])
 @pytest.mark.parametrize("layout", ["blhd", "padded", "offset"])
-def test_prefill_strided_inputs(layout):
+def test_prefill_strided_inputs(layout, bits, v_bits):
     """Prefill from views that are not contiguous [B][H][L][D]: token-major rows go through the one-pass
-    kernel; rows off the 16-byte grid go through the per-stage kernels.  Both bit-exact."""
+    kernel; rows off the 16-byte grid go through the per-stage kernels.  Both bit-exact, at each code
+    width."""
     import decode_attention_loopvq_amd as lvq
     import synth.kivi as synk
-    cfg = kivi_config("kivi-b16-4k", B=2, H=3, L=333)
-    _say(f"[kivi prefill strided] layout={layout}")
-    g = lvq.make_kivi_geom(D=cfg.D, H=cfg.H, bits=cfg.bits, group=cfg.group, R=cfg.R, cap=((cfg.L + 256 + cfg.group - 1) // cfg.group) * cfg.group)
+    cfg = kivi_config("kivi-b16-4k", B=2, H=3, L=333, bits=bits, v_bits=v_bits)
+    _say(f"[kivi prefill strided] layout={layout} k{bits} v{v_bits or bits}")
+    g = lvq.make_kivi_geom(D=cfg.D, H=cfg.H, bits=cfg.bits, group=cfg.group, R=cfg.R,
+                           cap=((cfg.L + 256 + cfg.group - 1) // cfg.group) * cfg.group, v_bits=cfg.v_bits)
     cache = lvq.KiviCache(g, cfg.B, device="cuda")
     k, v = synk.raw_kv(cfg, "cuda")
     kl, vl = _layout(k, layout), _layout(v, layout)
@@ -180,7 +183,7 @@ def test_prefill_strided_inputs(layout):
     kh, vh = k.cpu().numpy(), v.cpu().numpy()
     for b in range(cfg.B):
         for h in range(cfg.H):
-            st = kv.KiviState(D=g.D, group=g.group, R=g.R)
+            st = kv.KiviState(D=g.D, group=g.group, R=g.R, bits=g.bits, v_bits=g.v_bits)
             st.prefill(kh[b, h], vh[b, h])
             _compare_state(cache, g, b, h, st)
 

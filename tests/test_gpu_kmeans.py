@@ -86,7 +86,9 @@ def _update(p, xs, w, cb, beta, shift=False):
     ("loopvq-deep-ragged", dict(B=2, H=1, L=500, T=8, ragged=(300, 500)), False),
     ("loopvq-deep-ragged", dict(B=2, H=4, L=400, T=8, ragged=(200, 400)), True),
     ("loopvq-b1-1k-fp32cb", dict(B=2, H=2, L=700), False),
-], ids=["bf16-c8", "bf16-c8-unaligned", "bf16-c4", "bf16-c4-unaligned-xcd", "fp32"])
+    # lengths 81, 79, 204, 55: one request with a single index page, two with none
+    ("loopvq-b64-6k", dict(B=4, H=2, L=600, ragged=(10, 600)), False),
+], ids=["bf16-c8", "bf16-c8-unaligned", "bf16-c4", "bf16-c4-unaligned-xcd", "fp32", "bf16-c8-short"])
 def test_update_matches_oracle(name, over, shift):
     cfg, p, xs, w, NG = _setup(name, over)
     g = p.g
