@@ -23,6 +23,7 @@ struct KArgs {
     int D, H, G, R, cap, ring;
     int kb, vb;           // key and value code widths (2 or 4 bits)
     int nrep;             // query heads per KV head
+    bool res_slot;        // attention: the last split slot holds only the rows past the quantized key groups
     kivi_cache c;
 };
 
@@ -367,10 +368,11 @@ __global__ void decode_counters_kernel(KArgs a, int B) {
 // Decode attention partial: grid (split, KV head h, B), 256 threads in 32 lane
 // groups of 8; lane c of a group owns channels 16c .. 16c+15 (16 * bits bits
 // of codes per token: one dword at 2 bits, two at 4).  The nrep query heads of
-// KV head h share the workgroup: lane group lg serves query head
-// h * nrep + lg % nrep and takes every (32 / nrep)-th token range, so the
-// lane groups of the nrep heads in one wave read the same code words in the
-// same instruction.  A split is a multiple of 32 tokens.  Fast path: a lane
+// KV head h share the workgroup in sets of HPL (2 when nrep is even, else 1): lane group lg
+// serves set lg % (nrep / HPL) and takes every (32 / (nrep / HPL))-th token
+// range; it dequantises each token once and scores it for the HPL heads of
+// its set, and the lane groups of different sets in one wave read the same
+// code words in the same instruction.  A split is a multiple of 32 tokens.  Fast path: a lane
 // group takes whole 32-token key groups inside the fully quantized range
 // [0, min(n_kq, n_vq)); it loads the group's key scale/zero once and the
 // codes and value parameters of TB tokens at once (all 32 at 2 bits, 16 at a
@@ -448,41 +450,70 @@ __device__ __forceinline__ void half8(uint4 w, float* out) {
     }
 }
 
-template <int KB, int VB>
+template <int KB, int VB, int HPL>
 __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, const uint16_t* __restrict__ q,
-                                                                   float scale_log2, int tps, int S_tot,
+                                                                   float scale_log2, int S_tot,
                                                                    int max_len, float* __restrict__ po,
                                                                    float* __restrict__ pl) {
     constexpr int D = 128, NLG = kKiviLaneGroups;
-    constexpr int TB = (KB == 4 || VB == 4) ? 16 : 32;   // tokens whose codes are held at once
+    // tokens whose codes are held at once: fewer with 4-bit codes or several heads per lane group
+    static_assert(HPL == 1 || HPL == 2, "one or two heads per lane group (four spill registers)");
+    constexpr int TB = HPL == 2 ? 8 : (KB == 4 || VB == 4) ? 16 : 32;
     constexpr int KROW = D * KB / 8, VROW = D * VB / 8;  // code bytes per token
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, c8 = tid & 7, lg = tid >> 3;
-    const int nrep = a.nrep, head = lg % nrep, tl = lg / nrep, NT = NLG / nrep;
+    // The nrep query heads of KV head h form nset = nrep / HPL sets of HPL heads; lane group lg serves
+    // set lg % nset (heads h*nrep + set*HPL + u) and takes every (32 / nset)-th token range.
+    const int nset = a.nrep / HPL, hset = lg % nset, tl = lg / nset, NT = NLG / nset;
     const int L = min(max(a.c.len[b], 0), max_len);
     const int nk = min(a.c.n_kq[b], L), nv = min(a.c.n_vq[b], L);
-    const int t_lo = min(L, split * tps), t_hi = min(L, (split + 1) * tps);
+    // With grouped queries (a.res_slot) splits 0 .. S_tot-2 share the whole key groups of [0, q_end) (both
+    // sides quantized) evenly and the last slot takes the rest (fp16 residual rows, a partial group), so
+    // that it runs beside the quantized splits instead of after one of them (a lane group walks those
+    // rows one at a time for all its heads).  Otherwise the S_tot splits share [0, L) in whole key
+    // groups and the last one also takes the rest.
+    const int q_end = min(nk, nv) & ~31;
+    const int nq = a.res_slot ? S_tot - 1 : S_tot;
+    int t_lo, t_hi;
+    if (!a.res_slot) {
+        const int tq = ((L + S_tot - 1) / S_tot + 31) & ~31;
+        t_lo = min(L, split * tq);
+        t_hi = min(L, (split + 1) * tq);
+    } else if (split < nq) {
+        const int tq = ((q_end + nq - 1) / nq + 31) & ~31;   // whole key groups per split
+        t_lo = min(q_end, split * tq);
+        t_hi = min(q_end, (split + 1) * tq);
+    } else {
+        t_lo = q_end;
+        t_hi = L;
+    }
     const long row = bh(a, b, h);                    // KV row
-    const long qrow = row * nrep + head;             // query row: b * Hq + h * nrep + head
+    const long qrow0 = row * a.nrep + hset * HPL;    // first query row: b * Hq + h * nrep + set * HPL
     const int ch0 = 16 * c8, vg = c8 >> 1;          // channels and their value group
-    float qv[16];
-    {
-        const uint4* qp = reinterpret_cast<const uint4*>(q + qrow * D + ch0);
+    // the lane's 16 query channels of head u of its set, times sm_scale * log2 e (read again where
+    // needed rather than held: with several heads per lane group the registers go to the accumulators)
+    auto load_q = [&](int u, float (&qv)[16]) {
+        const uint4* qp = reinterpret_cast<const uint4*>(q + (qrow0 + u) * D + ch0);
         half8(qp[0], qv);
         half8(qp[1], qv + 8);
 #pragma unroll
         for (int j = 0; j < 16; ++j) qv[j] *= scale_log2;
-    }
-    float m = -INFINITY, l = 0.f, o[16], ob = 0.f;
+    };
+    float m[HPL], l[HPL], o[HPL][16], ob[HPL];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[j] = 0.f;
+    for (int u = 0; u < HPL; ++u) {
+        m[u] = -INFINITY;
+        l[u] = 0.f;
+        ob[u] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[u][j] = 0.f;
+    }
     const long cb = row * a.cap;
 
     // ---- fast path: whole key groups inside [0, min(nk, nv)) ----
-    const int q_end = min(nk, nv) & ~31;
     const int f_hi = min(t_hi, q_end);
     for (int t0 = t_lo + 32 * tl; t0 + 32 <= f_hi; t0 += 32 * NT) {
-        float w[16], bk = 0.f;
+        float w[HPL][16], bk[HPL];
         {
             const long pidx = (row * (a.cap / 32) + t0 / 32) * D + ch0;
             const uint4* sp = reinterpret_cast<const uint4*>(U16(a.c.k_scale) + pidx);
@@ -491,13 +522,19 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
             half8(sp[0], s16); half8(sp[1], s16 + 8);
             half8(zp[0], z16); half8(zp[1], z16 + 8);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                w[j] = qv[j] * s16[j];
-                bk = fmaf(w[j], z16[j], bk);
+            for (int u = 0; u < HPL; ++u) {
+                float qv[16];
+                load_q(u, qv);
+                bk[u] = 0.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    w[u][j] = qv[j] * s16[j];
+                    bk[u] = fmaf(w[u][j], z16[j], bk[u]);
+                }
             }
         }
-#pragma unroll
-        for (int tb = 0; tb < 32; tb += TB) {
+#pragma unroll 1
+        for (int tb = 0; tb < 32; tb += TB) {           // rolled: each batch's loads stay in its iteration
             Codes16<KB> kc[TB];
             Codes16<VB> vc[TB];
             uint32_t vs[TB], vz[TB];
@@ -509,39 +546,49 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
                 vs[k] = reinterpret_cast<const uint32_t*>(U16(a.c.v_scale) + tok * (D / 32))[vg >> 1];
                 vz[k] = reinterpret_cast<const uint32_t*>(U16(a.c.v_zero) + tok * (D / 32))[vg >> 1];
             }
-            float sc[TB];
-            float mb = m;
+            float sc[TB][HPL];
+            float mb[HPL];
+#pragma unroll
+            for (int u = 0; u < HPL; ++u) mb[u] = m[u];
 #pragma unroll
             for (int k = 0; k < TB; ++k) {
                 float c[16];
-                codes16<KB>(kc[k], c);
-                float part = -bk;
+                codes16<KB>(kc[k], c);                // dequantised once for every head of the set
 #pragma unroll
-                for (int j = 0; j < 16; ++j) part = fmaf(w[j], c[j], part);
-                sc[k] = sum8(part);
-                mb = fmaxf(mb, sc[k]);
+                for (int u = 0; u < HPL; ++u) {
+                    float part = -bk[u];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) part = fmaf(w[u][j], c[j], part);
+                    sc[k][u] = sum8(part);
+                    mb[u] = fmaxf(mb[u], sc[k][u]);
+                }
             }
-            // the batch joins the lane group's running softmax
-            {
-                const float alpha = exp2f(m - mb);
-                l *= alpha;
-                ob *= alpha;
+            // the batch joins each head's running softmax
 #pragma unroll
-                for (int j = 0; j < 16; ++j) o[j] *= alpha;
+            for (int u = 0; u < HPL; ++u) {
+                const float alpha = __builtin_amdgcn_exp2f(m[u] - mb[u]);
+                l[u] *= alpha;
+                ob[u] *= alpha;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[u][j] *= alpha;
+                m[u] = mb[u];
             }
             const int hsel = 16 * (vg & 1);          // which half of the dword holds this lane's group
 #pragma unroll
             for (int k = 0; k < TB; ++k) {
-                const float p = exp2f(sc[k] - mb);
-                l += p;
-                const float av = p * f16_to_f32(uint16_t(vs[k] >> hsel));
-                ob = fmaf(av, f16_to_f32(uint16_t(vz[k] >> hsel)), ob);
                 float c[16];
                 codes16<VB>(vc[k], c);
+                const float vsf = f16_to_f32(uint16_t(vs[k] >> hsel)), vzf = f16_to_f32(uint16_t(vz[k] >> hsel));
 #pragma unroll
-                for (int j = 0; j < 16; ++j) o[j] = fmaf(av, c[j], o[j]);
+                for (int u = 0; u < HPL; ++u) {
+                    const float p = __builtin_amdgcn_exp2f(sc[k][u] - m[u]);
+                    l[u] += p;
+                    const float av = p * vsf;
+                    ob[u] = fmaf(av, vzf, ob[u]);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) o[u][j] = fmaf(av, c[j], o[u][j]);
+                }
             }
-            m = mb;
         }
     }
 
@@ -574,46 +621,55 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
             const uint4* r = reinterpret_cast<const uint4*>(U16(a.c.v_res) + (row * a.ring + tok % a.ring) * D + ch0);
             half8(r[0], vf); half8(r[1], vf + 8);
         }
-        float part = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) part = fmaf(qv[j], kf[j], part);
-        const float s = sum8(part);
-        const float m_new = fmaxf(m, s);
-        const float alpha = exp2f(m - m_new), p = exp2f(s - m_new);
-        l = l * alpha + p;
-        ob *= alpha;
+        for (int u = 0; u < HPL; ++u) {
+            float qv[16];
+            load_q(u, qv);
+            float part = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[j] = fmaf(p, vf[j], o[j] * alpha);
-        m = m_new;
+            for (int j = 0; j < 16; ++j) part = fmaf(qv[j], kf[j], part);
+            const float s = sum8(part);
+            const float m_new = fmaxf(m[u], s);
+            const float alpha = __builtin_amdgcn_exp2f(m[u] - m_new), p = __builtin_amdgcn_exp2f(s - m_new);
+            l[u] = l[u] * alpha + p;
+            ob[u] *= alpha;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[u][j] = fmaf(p, vf[j], o[u][j] * alpha);
+            m[u] = m_new;
+        }
     }
 
-    // ---- combine the lane groups of each query head ----
+    // ---- combine the lane groups of each query head, one head of every set per round ----
     __shared__ float red[NLG][D + 2];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) red[lg][ch0 + j] = o[j] - ob;
-    if (c8 == 0) {
-        red[lg][D] = m;
-        red[lg][D + 1] = l;
-    }
-    __syncthreads();
-    for (int e = tid; e < nrep * D; e += 256) {
-        const int hr = e / D, d = e % D;
-        const long orow = (row * nrep + hr) * S_tot + split;
-        float M = -INFINITY;
-        for (int g2 = hr; g2 < NLG; g2 += nrep) M = fmaxf(M, red[g2][D]);
-        if (M == -INFINITY) {
-            po[orow * D + d] = 0.f;
-            if (d == 0) pl[orow] = -INFINITY;
-            continue;
+    for (int u = 0; u < HPL; ++u) {
+        if (u > 0) __syncthreads();                  // the previous round has read red
+#pragma unroll
+        for (int j = 0; j < 16; ++j) red[lg][ch0 + j] = o[u][j] - ob[u];
+        if (c8 == 0) {
+            red[lg][D] = m[u];
+            red[lg][D + 1] = l[u];
         }
-        float Ls = 0.f, ov = 0.f;
-        for (int g2 = hr; g2 < NLG; g2 += nrep) {
-            const float fw = red[g2][D] == -INFINITY ? 0.f : exp2f(red[g2][D] - M);
-            Ls += red[g2][D + 1] * fw;
-            ov += red[g2][d] * fw;
+        __syncthreads();
+        for (int e = tid; e < nset * D; e += 256) {
+            const int hs = e / D, d = e % D;
+            const long orow = (row * a.nrep + hs * HPL + u) * S_tot + split;
+            float M = -INFINITY;
+            for (int g2 = hs; g2 < NLG; g2 += nset) M = fmaxf(M, red[g2][D]);
+            if (M == -INFINITY) {
+                po[orow * D + d] = 0.f;
+                if (d == 0) pl[orow] = -INFINITY;
+                continue;
+            }
+            float Ls = 0.f, ov = 0.f;
+            for (int g2 = hs; g2 < NLG; g2 += nset) {
+                const float fw = red[g2][D] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red[g2][D] - M);
+                Ls += red[g2][D + 1] * fw;
+                ov += red[g2][d] * fw;
+            }
+            po[orow * D + d] = ov / Ls;
+            if (d == 0) pl[orow] = (M + log2f(Ls)) * kLn2;
         }
-        po[orow * D + d] = ov / Ls;
-        if (d == 0) pl[orow] = (M + log2f(Ls)) * kLn2;
     }
 }
 
@@ -664,8 +720,18 @@ KArgs make_args(const kivi_geom* g, const kivi_cache* c) {
     a.kb = g->bits;
     a.vb = g->v_bits ? g->v_bits : g->bits;
     a.nrep = g->Hq ? g->Hq / g->H : 1;
+    a.res_slot = a.nrep > 1;
     a.c = *c;
     return a;
+}
+
+template <int KB, int VB>
+void launch_kivi_attn(int hpl, dim3 grid, hipStream_t stream, const KArgs& a, const uint16_t* q, float sl2,
+                      int S_tot, int max_len, float* po, float* pl) {
+    if (hpl == 2)
+        hipLaunchKernelGGL((kivi_attn_partial_kernel<KB, VB, 2>), grid, dim3(256), 0, stream, a, q, sl2, S_tot, max_len, po, pl);
+    else
+        hipLaunchKernelGGL((kivi_attn_partial_kernel<KB, VB, 1>), grid, dim3(256), 0, stream, a, q, sl2, S_tot, max_len, po, pl);
 }
 
 int choose_kivi_splits(const kivi_geom* g, int B, int max_len) {
@@ -744,7 +810,8 @@ extern "C" lvq_status kivi_append(const kivi_geom* g, const void* k_new, const v
 extern "C" size_t kivi_decode_attn_workspace(const kivi_geom* g, int32_t B, int32_t max_len, int32_t num_splits) {
     if (!g || B < 0 || max_len < 0 || num_splits < 0 || g->H <= 0 || g->D <= 0) return 0;
     if (g->Hq < 0 || (g->Hq && g->Hq % g->H)) return 0;
-    const int S = num_splits > 0 ? num_splits : choose_kivi_splits(g, B, max_len);
+    const bool res_slot = g->Hq > g->H;              // grouped queries: a slot of its own for the residual rows
+    const int S = (num_splits > 0 ? num_splits : choose_kivi_splits(g, B, max_len)) + (res_slot ? 1 : 0);
     const size_t rows = size_t(B) * (g->Hq ? g->Hq : g->H) * S;     // (request, query head, split)
     return rows * g->D * sizeof(float) + rows * sizeof(float);
 }
@@ -766,22 +833,19 @@ extern "C" lvq_status kivi_decode_attn(const kivi_geom* g, const void* q, const 
     LVQ_REQUIRE(ws_bytes >= need, LVQ_ERR_WORKSPACE, "kivi_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
     KArgs a = make_args(g, c);
     const int Hq = g->H * a.nrep;
-    const size_t rows = size_t(B) * Hq * S;
+    const int S_tot = S + (a.res_slot ? 1 : 0);                   // with grouped queries: + the residual slot
+    const size_t rows = size_t(B) * Hq * S_tot;
     float* po = static_cast<float*>(ws);
     float* pl = po + rows * g->D;
-    const int tps = ceil_div(ceil_div(max_len, S), 32) * 32;     // whole key groups per split
-    const dim3 grid(S, g->H, B);
+    const dim3 grid(S_tot, g->H, B);
     const auto* qp = static_cast<const uint16_t*>(q);
     const float sl2 = sm_scale * kLog2e;
-    if (a.kb == 2 && a.vb == 2)
-        hipLaunchKernelGGL((kivi_attn_partial_kernel<2, 2>), grid, dim3(256), 0, stream, a, qp, sl2, tps, S, max_len, po, pl);
-    else if (a.kb == 2)
-        hipLaunchKernelGGL((kivi_attn_partial_kernel<2, 4>), grid, dim3(256), 0, stream, a, qp, sl2, tps, S, max_len, po, pl);
-    else if (a.vb == 2)
-        hipLaunchKernelGGL((kivi_attn_partial_kernel<4, 2>), grid, dim3(256), 0, stream, a, qp, sl2, tps, S, max_len, po, pl);
-    else
-        hipLaunchKernelGGL((kivi_attn_partial_kernel<4, 4>), grid, dim3(256), 0, stream, a, qp, sl2, tps, S, max_len, po, pl);
+    const int hpl = a.nrep % 2 == 0 ? 2 : 1;       // heads per lane group
+    if (a.kb == 2 && a.vb == 2) launch_kivi_attn<2, 2>(hpl, grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
+    else if (a.kb == 2) launch_kivi_attn<2, 4>(hpl, grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
+    else if (a.vb == 2) launch_kivi_attn<4, 2>(hpl, grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
+    else launch_kivi_attn<4, 4>(hpl, grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
     if ((st = check_launch("kivi_decode_attn: partial")) != LVQ_OK) return st;
-    hipLaunchKernelGGL(kivi_merge_kernel, dim3(B * Hq), dim3(128), 0, stream, po, pl, S, g->D, out, lse_out);
+    hipLaunchKernelGGL(kivi_merge_kernel, dim3(B * Hq), dim3(128), 0, stream, po, pl, S_tot, g->D, out, lse_out);
     return check_launch("kivi_decode_attn: merge");
 }
