@@ -17,7 +17,7 @@ namespace {
 // B_t slices: slices[t][h][kv][g][r][i] = codebooks[t/Tc][h][kv][g][r][i*Tc + t%Tc]
 // ---------------------------------------------------------------------------
 template <typename E>
-__global__ void slice_kernel(const E* __restrict__ cb, E* __restrict__ out, int T, int Tc, int H,
+__global__ void slice_kernel(const E* __restrict__ cb, E* __restrict__ out, int Tc, int H,
                              int NG, int K, int G, long total) {
     const int c = G / Tc;
     for (long e = blockIdx.x * long(blockDim.x) + threadIdx.x; e < total; e += long(gridDim.x) * blockDim.x) {
@@ -419,11 +419,11 @@ extern "C" lvq_status lvq_slice_codebooks(const lvq_geom* g, const void* codeboo
     const int threads = 256;
     if (geo.cb == LVQ_BF16)
         hipLaunchKernelGGL(slice_kernel<uint16_t>, dim3(grid_for(total, threads)), dim3(threads), 0, stream,
-                           static_cast<const uint16_t*>(codebooks), static_cast<uint16_t*>(slices), geo.T,
-                           geo.Tc, geo.H, geo.NG, geo.K, geo.G, total);
+                           static_cast<const uint16_t*>(codebooks), static_cast<uint16_t*>(slices), geo.Tc,
+                           geo.H, geo.NG, geo.K, geo.G, total);
     else
         hipLaunchKernelGGL(slice_kernel<float>, dim3(grid_for(total, threads)), dim3(threads), 0, stream,
-                           static_cast<const float*>(codebooks), static_cast<float*>(slices), geo.T, geo.Tc,
+                           static_cast<const float*>(codebooks), static_cast<float*>(slices), geo.Tc,
                            geo.H, geo.NG, geo.K, geo.G, total);
     return check_launch("lvq_slice_codebooks");
 }
