@@ -88,7 +88,8 @@ def _update(p, xs, w, cb, beta, shift=False):
     ("loopvq-b1-1k-fp32cb", dict(B=2, H=2, L=700), False),
     # lengths 81, 79, 204, 55: one request with a single index page, two with none
     ("loopvq-b64-6k", dict(B=4, H=2, L=600, ragged=(10, 600)), False),
-], ids=["bf16-c8", "bf16-c8-unaligned", "bf16-c4", "bf16-c4-unaligned-xcd", "fp32", "bf16-c8-short"])
+    ("loopvq-deep-ragged", dict(B=2, H=4, L=450, T=8, ragged=(200, 450), cb_dtype="fp32"), False),
+], ids=["bf16-c8", "bf16-c8-unaligned", "bf16-c4", "bf16-c4-unaligned-xcd", "fp32", "bf16-c8-short", "fp32-c4-xcd"])
 def test_update_matches_oracle(name, over, shift):
     cfg, p, xs, w, NG = _setup(name, over)
     g = p.g

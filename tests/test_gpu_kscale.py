@@ -72,10 +72,12 @@ def test_key_scales_match_oracle(name, over):
     sc = _scales(p, 31)
     sc_host = sc.float().cpu().numpy().astype(np.float64)
     worst = 0.0
-    for ns in (0, 3):
+    # ragged batches also with their requests grouped by length: scales follow the physical pages
+    order = lvq.lvq_request_order(p.cache.seq_len, p.cache.max_len) if cfg.ragged else None
+    for ns, od in ((0, None), (3, None)) + (((0, order),) if order is not None else ()):
         for t in range(cfg.T):
             lse = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device="cuda")
-            out, _ = harness.run_step(p, t, num_splits=ns, lse=lse, k_scales=sc)
+            out, _ = harness.run_step(p, t, num_splits=ns, lse=lse, k_scales=sc, order=od)
             torch.cuda.synchronize()
             worst = max(worst, _check(p, t, rows, geo, idx, sc_host, out, lse))
     # the standalone partial entry point takes the same stream
