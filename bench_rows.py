@@ -172,20 +172,36 @@ def attn_row(name, cfg_name, steps, reps, kscale=False, **over):
         gen = torch.Generator(device="cuda").manual_seed(3)
         sc = torch.exp(0.25 * torch.randn((p.cache.pool.shape[0], cfg.T, 8), generator=gen, device="cuda"))
         sc = sc.to(torch.float16)
-        t0 = timed(lambda: [lvq.lvq_decode_attn(p.g, t, qs[t], p.cache.pool, p.cache.page_table, p.cache.seq_len,
-                                                p.cache.max_len, p.cache.win_k, p.cache.win_v, p.slices, p.rope_cos,
-                                                p.rope_sin, p.sm_scale, out=out, ws=ws, rope_f16=p.rope16,
-                                                order=order) for t in steps], reps) / len(steps)
+    # The calls are prebuilt ctypes argument tuples (as in bench.py): the Python binding's argument checks
+    # would add host time comparable to a call's GPU time.
+    import ctypes as C
+    from decode_attention_loopvq_amd._lib import lib
+    gref = C.byref(p.g)
+    sh = torch.cuda.current_stream().cuda_stream
+    ws_bytes = ws.numel()
+
+    def call_args(t, ks):
+        c = p.cache
+        return (gref, t, qs[t].data_ptr(), c.pool.data_ptr(), c.page_table.data_ptr(), int(c.page_table.shape[1]),
+                c.seq_len.data_ptr(), c.max_len, order.data_ptr() if order is not None else None,
+                ks.data_ptr() if ks is not None else None, c.win_k.data_ptr(), c.win_v.data_ptr(),
+                p.slices.data_ptr(), p.rope_cos.data_ptr(), p.rope_sin.data_ptr(), p.rope16.data_ptr(),
+                int(p.rope_cos.shape[0]), C.c_float(p.sm_scale), out.data_ptr(), None, ws.data_ptr(), ws_bytes, 0,
+                cfg.B, sh)
+
+    def runner(calls):
+        def run():
+            for a in calls:
+                if lib.lvq_decode_attn(*a) != 0:
+                    raise RuntimeError(lib.lvq_last_error().decode())
+        return run
+
+    if kscale:
+        t0 = timed(runner([call_args(t, None) for t in steps]), reps) / len(steps)
         per_call += sum(p.cache.n_pages) * 8 * 2
         extra["unscaled_us_per_call"] = round(t0 * 1e6, 2)
 
-    def run():
-        for t in steps:
-            lvq.lvq_decode_attn(p.g, t, qs[t], p.cache.pool, p.cache.page_table, p.cache.seq_len, p.cache.max_len,
-                                p.cache.win_k, p.cache.win_v, p.slices, p.rope_cos, p.rope_sin, p.sm_scale,
-                                out=out, ws=ws, rope_f16=p.rope16, order=order, k_scales=sc)
-
-    t = timed(run, reps) / len(steps)
+    t = timed(runner([call_args(t, sc) for t in steps]), reps) / len(steps)
     emit(row=name, workload=cfg.name, B=cfg.B, H=cfg.H, L=cfg.L, steps=list(steps), us_per_call=round(t * 1e6, 2),
          gbps=round(per_call / t / 1e9, 1), hbm_frac=round(per_call / t / PEAK_HBM, 4), bytes_per_call=per_call,
          token_heads_per_s=round(sum(p.lengths) * cfg.H / t, 1), **extra)
