@@ -466,7 +466,10 @@ extern "C" lvq_status lvq_encode(const lvq_geom* g, int32_t block, const void* x
     LVQ_REQUIRE(B <= 65535, LVQ_ERR_UNSUPPORTED, "lvq_encode: batch %d above 65535", B);
     if (B == 0 || max_pages == 0) return LVQ_OK;
     LVQ_REQUIRE(max_pages <= 0x7fffffff, LVQ_ERR_UNSUPPORTED, "lvq_encode: too many pages");
-    if (geo.cb == LVQ_BF16 && geo.G <= 32 && geo.NG % 8 == 0) {
+    // The matrix-core encoder takes whole 8-coordinate operand fragments and interleaves T_c in {1, 2, 4, 8}
+    // loop steps per fragment; other shapes take the exact scan.
+    const bool mfma_shape = geo.G % 8 == 0 && (geo.Tc == 1 || geo.Tc == 2 || geo.Tc == 4 || geo.Tc == 8);
+    if (geo.cb == LVQ_BF16 && mfma_shape && geo.NG % 8 == 0) {
         EncArgs ea{geo, block, static_cast<const uint16_t*>(x_k), static_cast<const uint16_t*>(x_v),
                    long(x_strides[0]), long(x_strides[1]), long(x_strides[2]), long(x_strides[3]), x_tok0,
                    static_cast<const uint16_t*>(codebooks), pool, page_table, pt_stride, first_page, n_pages,
@@ -483,7 +486,8 @@ extern "C" lvq_status lvq_encode(const lvq_geom* g, int32_t block, const void* x
                 case 1: hipLaunchKernelGGL((encode_mfma_kernel<1, true>), grid, dim3(512), 0, stream, ea); break;
                 case 2: hipLaunchKernelGGL((encode_mfma_kernel<2, true>), grid, dim3(512), 0, stream, ea); break;
                 case 4: hipLaunchKernelGGL((encode_mfma_kernel<4, true>), grid, dim3(512), 0, stream, ea); break;
-                default: hipLaunchKernelGGL((encode_mfma_kernel<8, true>), grid, dim3(512), 0, stream, ea); break;
+                case 8: hipLaunchKernelGGL((encode_mfma_kernel<8, true>), grid, dim3(512), 0, stream, ea); break;
+                default: break;
             }
             return check_launch("lvq_encode");
         }
@@ -495,7 +499,8 @@ extern "C" lvq_status lvq_encode(const lvq_geom* g, int32_t block, const void* x
             case 1: hipLaunchKernelGGL((encode_mfma_kernel<1, false>), grid, dim3(512), 0, stream, ea); break;
             case 2: hipLaunchKernelGGL((encode_mfma_kernel<2, false>), grid, dim3(512), 0, stream, ea); break;
             case 4: hipLaunchKernelGGL((encode_mfma_kernel<4, false>), grid, dim3(512), 0, stream, ea); break;
-            default: hipLaunchKernelGGL((encode_mfma_kernel<8, false>), grid, dim3(512), 0, stream, ea); break;
+            case 8: hipLaunchKernelGGL((encode_mfma_kernel<8, false>), grid, dim3(512), 0, stream, ea); break;
+            default: break;
         }
         return check_launch("lvq_encode");
     }

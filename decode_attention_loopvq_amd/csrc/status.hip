@@ -43,6 +43,7 @@ lvq_status validate_geom(const lvq_geom* g, Geo* o) {
     LVQ_REQUIRE(g->page == 8, LVQ_ERR_UNSUPPORTED, "page of %d tokens unsupported (8)", g->page);
     const int c = g->G / g->Tc;
     LVQ_REQUIRE(c == 4 || c == 8, LVQ_ERR_UNSUPPORTED, "c = G/T_c = %d unsupported (4 or 8)", c);
+    LVQ_REQUIRE(g->G <= 32, LVQ_ERR_UNSUPPORTED, "codeword dimension G=%d unsupported (at most 32)", g->G);
     LVQ_REQUIRE(g->window % g->page == 0, LVQ_ERR_UNSUPPORTED,
                 "window %d must be a multiple of the page size", g->window);
     LVQ_REQUIRE(g->cb_dtype == LVQ_BF16 || g->cb_dtype == LVQ_FP32, LVQ_ERR_UNSUPPORTED,

@@ -72,8 +72,9 @@ LVQ_API const char* lvq_last_error(void);
  * D       head dimension (128 supported)
  * T       loop steps; T_c must divide T and G ("method steps", step 1)
  * Tc      loop steps that share one index row
- * G       codeword dimension; c = G/Tc channels per codeword per step
- *         (c = 4 or 8 supported); NG = D/c index groups per token and step
+ * G       codeword dimension (at most 32); c = G/Tc channels per codeword
+ *         per step (c = 4 or 8 supported); NG = D/c index groups per token
+ *         and step
  * K       codewords per codebook (256: 8-bit indices)
  * page    tokens per index page (8)
  * sink    leading tokens kept bf16 (8)
@@ -143,11 +144,12 @@ LVQ_API lvq_status lvq_rope_table_f16(int32_t len, int32_t D, double base, void*
  * coupled across the block's T_c loop steps and each coupled sub-vector is
  * replaced by the index of its nearest codeword, argmin_r ||z - e_r||^2, and
  * written to pool page page_table[b*pt_stride + lp] at [block][h][kv].
- * bf16 codebooks (G <= 32): the distances come from a bf16 matrix-core
+ * bf16 codebooks with G a multiple of 8 and T_c in {1, 2, 4, 8}: the
+ * distances come from a bf16 matrix-core
  * contraction with fp32 sums, argmax_r (z . e_r - ||e_r||^2 / 2); equal
  * values resolve to the lowest index, and a pick can differ from the exact
- * minimum only by the fp32 rounding of the sums.  fp32 codebooks: an exact
- * fp64 scan, lowest index on ties.
+ * minimum only by the fp32 rounding of the sums.  fp32 codebooks and the
+ * other bf16 shapes: an exact fp64 scan, lowest index on ties.
  * The same call serves prefill (many pages) and decode (the oldest window
  * page, every 8 generated tokens).
  *

@@ -76,6 +76,7 @@ def test_decode_attn_rejects(over, status):
     (dict(D=64), UNSUPPORTED), (dict(K=128), UNSUPPORTED), (dict(page=16), UNSUPPORTED),
     (dict(T=4, Tc=3), INVALID), (dict(G=12, Tc=2), UNSUPPORTED), (dict(G=64, Tc=2), UNSUPPORTED),
     (dict(window=60), UNSUPPORTED), (dict(T=0), INVALID),
+    (dict(T=8, Tc=8, G=64), UNSUPPORTED),    # c = 8, but codewords longer than 32 coordinates
 ])
 def test_geometry_rejects(kw, status):
     assert _attn(_geom(**kw)) == status
@@ -112,6 +113,8 @@ def test_encode_rejects():
     assert f(C.byref(g), 0, None, None, strides, None, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 4, 8, None) == INVALID
     assert f(C.byref(g), 0, FAKE, None, strides, None, FAKE, None, FAKE, 8, FAKE, FAKE, 4, 8, None) == INVALID
     assert f(C.byref(g), 0, FAKE, None, strides, None, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 0, 8, None) == OK
+    g64 = _geom(T=8, Tc=8, G=64)
+    assert f(C.byref(g64), 0, FAKE, None, strides, None, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 4, 8, None) == UNSUPPORTED
 
 
 def test_merge_and_tables_reject():

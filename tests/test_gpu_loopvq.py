@@ -151,6 +151,16 @@ def test_decode_parity_small(cfg):
     _run_parity(cfg, rows, steps, splits=(0, 1, 3) + single)
 
 
+@pytest.mark.parametrize("T,Tc,G", [(4, 1, 4), (6, 3, 24)], ids=["tc1-g4", "tc3-g24"])
+def test_encode_shapes_off_the_matrix_core_path(T, Tc, G):
+    """Geometries the matrix-core encoder does not take (a codeword shorter than one 8-coordinate operand
+    fragment; three loop steps per index row) go to the exact scan: every index against the oracle, and
+    attention at every loop step."""
+    cfg = loopvq_config("loopvq-b64-6k", B=3, H=2, L=500, T=T, Tc=Tc, G=G)
+    rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    _run_parity(cfg, rows, steps=range(cfg.T), splits=(0,))
+
+
 def test_decode_edge_lengths(monkeypatch):
     """Lengths shorter than the sinks, exactly sink + window, one page, and
     pages beyond every split boundary; more splits than pages."""

@@ -219,3 +219,56 @@ def test_joint_softmax_equals_merged_segments_and_differs_from_separate():
     assert abs(lse - lse2) < 1e-12
     bad = kv.attention_per_segment_softmax(q, st, 1 / math.sqrt(128))
     assert np.abs(bad - o).max() > 1e-2
+
+
+def _lossless_grid_cache(L, D=128, group=32, bits=2, seed=11):
+    """Keys and values whose every quantizer group is an exactly representable grid
+    {a, a+s, ..., a+(2^b-1)s} holding both end points, with a scale and an offset of its
+    own per group: key groups are (32-token block, channel), aligned at token 0 as the
+    flush rule keeps them; value groups are (token, 32-channel block)."""
+    rng = np.random.default_rng(seed)
+    top = 2 ** bits - 1
+
+    def grid(n):
+        s = float(2.0 ** rng.integers(-5, 3))
+        a = -float(rng.integers(0, top + 1)) * s       # z = -a/s is an integer
+        x = a + s * rng.integers(0, top + 1, size=n)
+        i_lo, i_hi = rng.choice(n, size=2, replace=False)
+        x[i_lo], x[i_hi] = a, a + top * s
+        return x
+
+    k = np.empty((L, D))
+    for g0 in range(0, L, group):
+        for d in range(D):
+            n = min(group, L - g0)
+            k[g0:g0 + n, d] = grid(group)[:n]
+    v = np.empty((L, D))
+    for j in range(L):
+        for c0 in range(0, D, group):
+            v[j, c0:c0 + group] = grid(group)
+    return k.astype(np.float16), v.astype(np.float16)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_state_keys_and_values_reproduce_lossless_inputs(bits):
+    """keys() / values() put each dequantized row back at its own position with its own
+    group's (s, z): on lossless grids (scale and offset differing from group to group, so a
+    misplaced broadcast of s or z, or a row out of order, changes values) the whole cache,
+    quantized and fp16 parts, equals the fp16 input exactly, after prefill and after decode
+    appends that flush keys and values several times (KIVI page, core design: attention runs
+    over the dequantized groups followed by the fp16 residual)."""
+    L0, n_app = 300, 150
+    k, v = _lossless_grid_cache(L0 + n_app, bits=bits)
+    st = kv.KiviState(D=128, R=128, group=32, bits=bits)
+    st.prefill(k[:L0], v[:L0])
+    assert st.n_kq == 160 and st.n_vq == 172
+    np.testing.assert_array_equal(st.keys(), k[:L0].astype(np.float64))
+    np.testing.assert_array_equal(st.values(), v[:L0].astype(np.float64))
+    for j in range(L0, L0 + n_app):
+        st.append(k[j], v[j])
+    assert st.n_kq == 416 and st.n_vq == L0 + n_app - 128
+    np.testing.assert_array_equal(st.keys(), k.astype(np.float64))
+    np.testing.assert_array_equal(st.values(), v.astype(np.float64))
+    # the groups really do carry distinct parameters (so the check above can see a wrong broadcast)
+    assert len({float(x) for x in np.stack(st.k_s)[:, 0]}) > 1
+    assert len({float(x) for x in np.stack(st.v_s)[0]}) > 1

@@ -141,6 +141,23 @@ def test_nearest_codeword_brute_force(K, G):
         assert d[j, idx[j]] == min(sum((a - b) ** 2 for a, b in zip(z[j], e)) for e in E)
 
 
+@pytest.mark.parametrize("N,chunk", [(4096 + 1000, 4096), (9000, 4096), (50, 7)])
+def test_nearest_codeword_across_row_chunks(N, chunk):
+    """Rows are scanned in chunks of `chunk`; every row of every chunk, the partial last one
+    included, gets its own brute-force nearest codeword and its full distance row."""
+    rng = np.random.default_rng(N)
+    G, K = 3, 12
+    z = rng.integers(-3, 4, size=(N, G)).astype(np.float64)
+    E = rng.integers(-3, 4, size=(K, G)).astype(np.float64)
+    idx, d = lv.nearest_codeword(z, E, chunk=chunk)
+    E_list = [list(e) for e in E]
+    for j in range(N):
+        zj = list(z[j])
+        assert idx[j] == _brute_nearest(zj, E_list)
+        for r in range(K):
+            assert d[j, r] == sum((a - b) ** 2 for a, b in zip(zj, E_list[r]))
+
+
 def test_duplicate_codewords_pick_lowest_index():
     E = np.array([[1.0, 1.0], [0.0, 0.0], [0.0, 0.0], [5.0, 5.0]])
     idx, _ = lv.nearest_codeword(np.array([[0.1, -0.1], [0.0, 0.0]]), E)
