@@ -20,7 +20,7 @@ from . import layout  # noqa: F401
 
 __all__ = [
     "LvqError", "lvq_geom", "kivi_geom", "make_geom", "make_kivi_geom",
-    "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_request_order", "lvq_window_append",
+    "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_decode_attn_noalloc", "lvq_request_order", "lvq_window_append",
     "lvq_codebook_update",
     "lvq_decode_attn_splits", "lvq_quant_partial", "lvq_quant_partial_workspace", "lvq_window_partial", "splitk_lse_merge", "kivi_append",
     "kivi_decode_attn_workspace", "kivi_decode_attn", "KiviCache", "kivi_widths", "layout",
@@ -238,6 +238,50 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
                               lse_out.data_ptr() if lse_out is not None else None, ws.data_ptr(),
                               ws.numel() * ws.element_size(), int(num_splits), int(B), _stream(stream)),
           "lvq_decode_attn")
+    return out, lse_out
+
+
+def lvq_decode_attn_noalloc(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor, page_table: torch.Tensor,
+                            seq_len: torch.Tensor, max_len: int, win_k: torch.Tensor, win_v: torch.Tensor,
+                            slices: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor, sm_scale: float,
+                            out: torch.Tensor, lse_out: Optional[torch.Tensor] = None, num_splits: int = 0,
+                            stream=None, rope_f16: Optional[torch.Tensor] = None,
+                            order: Optional[torch.Tensor] = None,
+                            k_scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """lvq_decode_attn with the library's own per-GPU workspace: the caller passes `out` (and `lse_out`) and
+    nothing is allocated, here or in the library."""
+    _need(q, "q", torch.bfloat16)
+    B = q.shape[0]
+    if tuple(q.shape) != (B, g.H, g.D):
+        raise ValueError("q must be [B][H][D]")
+    _need(pool, "pool", torch.uint8)
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_len, "seq_len", torch.int32)
+    for name, w in (("win_k", win_k), ("win_v", win_v)):
+        _need(w, name, torch.bfloat16)
+        if tuple(w.shape) != (B, g.T, g.H, g.sink + g.window + g.page, g.D):
+            raise ValueError(f"{name} must be [B][T][H][sink+window+page][D]")
+    _need(slices, "slices", _cb_torch_dtype(g))
+    _need(rope_cos, "rope_cos", torch.float32)
+    _need(rope_sin, "rope_sin", torch.float32)
+    if seq_len.numel() != B or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("seq_len / page_table batch does not match q")
+    _need_order(order, B)
+    _need_kscales(k_scales, g, pool)
+    _need(out, "out", torch.float32)
+    if tuple(out.shape) != (B, g.H, g.D):
+        raise ValueError("out must be [B][H][D]")
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32)
+    check(lib.lvq_decode_attn_noalloc(C.byref(g), int(step), q.data_ptr(), pool.data_ptr(), page_table.data_ptr(),
+                                      int(page_table.shape[1]), seq_len.data_ptr(), int(max_len),
+                                      order.data_ptr() if order is not None else None,
+                                      k_scales.data_ptr() if k_scales is not None else None, win_k.data_ptr(),
+                                      win_v.data_ptr(), slices.data_ptr(), rope_cos.data_ptr(), rope_sin.data_ptr(),
+                                      _rope_f16_ptr(rope_f16, rope_cos), int(rope_cos.shape[0]), float(sm_scale),
+                                      out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None,
+                                      int(num_splits), int(B), _stream(stream)),
+          "lvq_decode_attn_noalloc")
     return out, lse_out
 
 

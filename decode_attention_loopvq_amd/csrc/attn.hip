@@ -1872,43 +1872,41 @@ extern "C" lvq_status lvq_window_partial(const lvq_geom* gp, int32_t step, const
     return launch_window(a, nullptr, nullptr, stream);
 }
 
-extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
-                                      const int32_t* page_table, int32_t pt_stride, const int32_t* seq_len,
-                                      int32_t max_len, const int32_t* order, const void* k_scales,
-                                      const void* win_k, const void* win_v, const void* slices,
-                                      const float* rope_cos, const float* rope_sin, const void* rope_f16,
-                                      int32_t rope_len, float sm_scale, float* out, float* lse_out, void* ws,
-                                      size_t ws_bytes,
-                                      int32_t num_splits, int32_t B, hipStream_t stream) {
+namespace lvq {
+
+lvq_status decode_attn_impl(const char* fn, const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
+                            const int32_t* page_table, int32_t pt_stride, const int32_t* seq_len, int32_t max_len,
+                            const int32_t* order, const void* k_scales, const void* win_k, const void* win_v,
+                            const void* slices, const float* rope_cos, const float* rope_sin, const void* rope_f16,
+                            int32_t rope_len, float sm_scale, float* out, float* lse_out, void* ws, size_t ws_bytes,
+                            WorkspaceProvider provider, int32_t num_splits, int32_t B, hipStream_t stream) {
     AttnArgs a{};
-    lvq_status st = prepare("lvq_decode_attn", gp, step, q, seq_len, max_len, rope_cos, rope_sin, rope_f16,
-                            rope_len, sm_scale, B, &a);
+    lvq_status st = prepare(fn, gp, step, q, seq_len, max_len, rope_cos, rope_sin, rope_f16, rope_len, sm_scale, B, &a);
     if (st != LVQ_OK) return st;
     a.order = order;
     a.kscale = static_cast<const uint16_t*>(k_scales);
     const Geo& g = a.geo;
-    LVQ_REQUIRE(num_splits >= -1 && num_splits <= 1024, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: num_splits %d",
-                num_splits);
+    LVQ_REQUIRE(num_splits >= -1 && num_splits <= 1024, LVQ_ERR_INVALID_ARG, "%s: num_splits %d", fn, num_splits);
     LVQ_REQUIRE(num_splits != -1 || !k_scales, LVQ_ERR_UNSUPPORTED,
-                "lvq_decode_attn: the single-pass kernel (num_splits -1) takes no key scale stream");
+                "%s: the single-pass kernel (num_splits -1) takes no key scale stream", fn);
     LVQ_REQUIRE(num_splits != -1 || g.cb == LVQ_BF16, LVQ_ERR_UNSUPPORTED,
-                "lvq_decode_attn: the single-pass kernel (num_splits -1) needs bf16 codebooks");
-    LVQ_REQUIRE(pt_stride >= 0, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: negative pt_stride");
+                "%s: the single-pass kernel (num_splits -1) needs bf16 codebooks", fn);
+    LVQ_REQUIRE(pt_stride >= 0, LVQ_ERR_INVALID_ARG, "%s: negative pt_stride", fn);
     if (B == 0) return LVQ_OK;
-    LVQ_REQUIRE(win_k && win_v && slices && out && ws, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: NULL pointer");
+    LVQ_REQUIRE(win_k && win_v && slices && out, LVQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     const int max_pages = max_index_pages(g, max_len);
-    LVQ_REQUIRE(max_pages == 0 || (pool && page_table), LVQ_ERR_INVALID_ARG,
-                "lvq_decode_attn: NULL pool or page table");
-    LVQ_REQUIRE(pt_stride >= max_pages, LVQ_ERR_INVALID_ARG, "lvq_decode_attn: pt_stride %d < %d pages",
-                pt_stride, max_pages);
+    LVQ_REQUIRE(max_pages == 0 || (pool && page_table), LVQ_ERR_INVALID_ARG, "%s: NULL pool or page table", fn);
+    LVQ_REQUIRE(pt_stride >= max_pages, LVQ_ERR_INVALID_ARG, "%s: pt_stride %d < %d pages", fn, pt_stride, max_pages);
     const bool single = num_splits == -1 || (num_splits == 0 && !k_scales && use_full(g, B, max_pages));
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
     LVQ_REQUIRE(single || splits_fit(g, max_pages, S), LVQ_ERR_INVALID_ARG,
-                "lvq_decode_attn: %d splits of %d index pages exceed %d tokens per split", S, max_pages, kMaxSplitTok);
+                "%s: %d splits of %d index pages exceed %d tokens per split", fn, S, max_pages, kMaxSplitTok);
     const size_t need = lvq_decode_attn_workspace(gp, B, max_len, num_splits);
-    LVQ_REQUIRE(ws_bytes >= need, LVQ_ERR_WORKSPACE, "lvq_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
-    LVQ_REQUIRE(reinterpret_cast<uintptr_t>(ws) % 256 == 0, LVQ_ERR_INVALID_ARG,
-                "lvq_decode_attn: workspace not 256-byte aligned");
+    if (provider && (st = provider(need, &ws, &ws_bytes)) != LVQ_OK) return st;
+    LVQ_REQUIRE(ws, LVQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    LVQ_REQUIRE(ws_bytes >= need, LVQ_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+    LVQ_REQUIRE(reinterpret_cast<uintptr_t>(ws) % 256 == 0, LVQ_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned",
+                fn);
 
     a.pool = pool;
     a.pt = page_table;
@@ -1926,6 +1924,21 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
     if ((st = launch_quant(a, static_cast<unsigned char*>(ws) + partials_bytes(g, B, S + 1), stream)) != LVQ_OK)
         return st;
     return launch_window(a, out, lse_out, stream);
+}
+
+}  // namespace lvq
+
+extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
+                                      const int32_t* page_table, int32_t pt_stride, const int32_t* seq_len,
+                                      int32_t max_len, const int32_t* order, const void* k_scales,
+                                      const void* win_k, const void* win_v, const void* slices,
+                                      const float* rope_cos, const float* rope_sin, const void* rope_f16,
+                                      int32_t rope_len, float sm_scale, float* out, float* lse_out, void* ws,
+                                      size_t ws_bytes,
+                                      int32_t num_splits, int32_t B, hipStream_t stream) {
+    return decode_attn_impl("lvq_decode_attn", gp, step, q, pool, page_table, pt_stride, seq_len, max_len, order,
+                            k_scales, win_k, win_v, slices, rope_cos, rope_sin, rope_f16, rope_len, sm_scale, out,
+                            lse_out, ws, ws_bytes, nullptr, num_splits, B, stream);
 }
 
 extern "C" int32_t lvq_decode_attn_splits(const lvq_geom* gp, int32_t B, int32_t max_len) {

@@ -97,4 +97,17 @@ struct Geo {
 // Validate a caller's geometry; fills `out` on success.
 lvq_status validate_geom(const lvq_geom* g, Geo* out);
 
+// Supplies the workspace of a decode-attention call once its arguments are valid: given the bytes the call
+// needs, sets *ws and *ws_bytes or returns an error.
+using WorkspaceProvider = lvq_status (*)(size_t need, void** ws, size_t* ws_bytes);
+
+// lvq_decode_attn with error messages naming `fn`; with a provider, the workspace comes from it (after every
+// other argument has been checked) instead of from ws / ws_bytes.
+lvq_status decode_attn_impl(const char* fn, const lvq_geom* gp, int32_t step, const void* q, const uint8_t* pool,
+                            const int32_t* page_table, int32_t pt_stride, const int32_t* seq_len, int32_t max_len,
+                            const int32_t* order, const void* k_scales, const void* win_k, const void* win_v,
+                            const void* slices, const float* rope_cos, const float* rope_sin, const void* rope_f16,
+                            int32_t rope_len, float sm_scale, float* out, float* lse_out, void* ws, size_t ws_bytes,
+                            WorkspaceProvider provider, int32_t num_splits, int32_t B, hipStream_t stream);
+
 }  // namespace lvq

@@ -276,6 +276,29 @@ LVQ_API lvq_status lvq_decode_attn(const lvq_geom* g, int32_t step, const void* 
                            hipStream_t stream);
 
 /*
+ * lvq_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and result as lvq_decode_attn, without ws / ws_bytes: the
+ * workspace is a device array the library holds, LVQ_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) per GPU, kept until the process ends.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); its first call on a
+ * device looks up that device's copy of the array.
+ * Errors: those of lvq_decode_attn, and LVQ_ERR_WORKSPACE when
+ * lvq_decode_attn_workspace(g, B, max_len, num_splits) exceeds
+ * LVQ_NOALLOC_SCRATCH_BYTES (nothing is launched).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (several streams or host threads at once) race and must not be issued.
+ */
+#define LVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+LVQ_API lvq_status lvq_decode_attn_noalloc(const lvq_geom* g, int32_t step, const void* q,
+                                           const uint8_t* pool, const int32_t* page_table, int32_t pt_stride,
+                                           const int32_t* seq_len, int32_t max_len, const int32_t* order,
+                                           const void* k_scales, const void* win_k, const void* win_v,
+                                           const void* slices, const float* rope_cos, const float* rope_sin,
+                                           const void* rope_f16, int32_t rope_len, float sm_scale, float* out,
+                                           float* lse_out, int32_t num_splits, int32_t B, hipStream_t stream);
+
+/*
  * Append one generated token to the bf16 window of loop step `step` (the LoopVQ page, Figure 5: each new
  * token's pre-RoPE K and V of every loop step enter the recent window; after every 8 generated tokens
  * the window's oldest page is encoded into the pool with lvq_encode, reading the window through its

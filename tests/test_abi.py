@@ -221,3 +221,21 @@ def test_key_scales_rejected_by_single_pass():
     """A key scale stream with the single-pass kernel (num_splits -1) is refused before any launch."""
     g = _geom()
     assert _attn(g, kscale=FAKE, splits=-1) == UNSUPPORTED
+
+
+def test_noalloc_rejects_before_touching_the_device():
+    """lvq_decode_attn_noalloc refuses a call whose workspace would exceed the scratch it holds per GPU, and
+    passes argument errors through from lvq_decode_attn, all before any device call."""
+    g = _geom()
+    f = _lib.lib.lvq_decode_attn_noalloc
+    def call(**over):
+        a = dict(step=0, max_len=1024, splits=0, B=4, rope_len=2048, scale=0.1, rope16=FAKE)
+        a.update(over)
+        return f(C.byref(g), a["step"], FAKE, FAKE, FAKE, 1 << 20, FAKE, a["max_len"], None, None, FAKE, FAKE, FAKE,
+                 FAKE, FAKE, a["rope16"], a["rope_len"], a["scale"], FAKE, None, a["splits"], a["B"], None)
+    need = _lib.lib.lvq_decode_attn_workspace(C.byref(g), 60000, 1024, 0)
+    assert need > 16 << 20
+    assert call(B=60000) == WORKSPACE
+    assert "16777216" in _lib.lib.lvq_last_error().decode()
+    assert call(step=9) == INVALID
+    assert call(B=0) == OK
