@@ -9,18 +9,16 @@ two-requests-per-block saving at this batch and context).
 
 One step is one decode step of a model with `--layers` attention layers that
 each own an independent copy of that cache: for each of the T loop steps,
-every layer runs lvq_decode_attn.  At this batch the library runs a call as
-one kernel (index_full_kernel: one workgroup per head and group of four
-requests, window and merge included); with `--num-splits N` (N >= 1) it runs
-the split path instead (the index-page partial kernel, then the bf16-window
-kernel that merges the partials through logsumexp).  Rotating over the
+every layer runs lvq_decode_attn: the index-page partial kernel
+(index_mfma_kernel), then the bf16-window kernel that merges the partials
+through logsumexp; `--num-splits N` fixes the split count (0: the library's
+choice).  Rotating over the
 copies (3.4 GB) keeps the 256 MB Infinity Cache from serving repeated reads,
 as layers would in a real model.
 
 Printed: one JSON line with the whole-call rate (algorithmic GB/s, fraction
 of the 8 TB/s HBM peak, token-heads/s), the roofline entry of the dominant
-kernel (the single-pass kernel, or the index-page partial of the split path
-timed alone; HIP events on the stream it runs on; its HBM traffic from the
+kernel (the index-page partial timed alone; HIP events on the stream it runs on; its HBM traffic from the
 committed counter runs when they match the kernel source), and the fp64
 oracle timed on a bounded sample on the host.
 
@@ -84,7 +82,7 @@ def call_bytes(g, lengths, cb_bytes):
 
 
 def quant_kernel_bytes(g, lengths, cb_bytes, splits):
-    """Algorithmic bytes of one index-page partial launch (index_attn_kernel):
+    """Algorithmic bytes of one index-page partial launch (index_mfma_kernel):
     index rows, page ids, codebook slices, fp16 cos/sin of the paged
     positions, q, and the partials written."""
     from decode_attention_loopvq_amd.layout import index_groups, n_index_pages
@@ -137,8 +135,7 @@ def cpu_baseline(prob, rows, seconds):
     return n_rows, el
 
 
-KERNELS = {"index_full_kernel": "index_full_kernel<8, 4> (single-pass attention)",
-           "index_attn_kernel": "index_attn_kernel<8, 4, false> (index-page partial)"}
+KERNELS = {"index_mfma_kernel": "index_mfma_kernel<false> (index-page partial, c = 8)"}
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_loopvq_amd", "csrc", "attn.hip")
 COPY_BYTES = 256 << 20
 
@@ -211,7 +208,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=6, help="independent cache copies rotated through")
     ap.add_argument("--num-splits", type=int, default=0,
-                    help="0: the library's choice; -1: the single-pass kernel; N >= 1: the split path")
+                    help="0: the library's choice; N >= 1: that many splits")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=("bench", "index-only", "copy"), default="bench",
@@ -259,8 +256,7 @@ def main():
     wks = [cache.win_k] + [cache.win_k.clone() for _ in range(args.layers - 1)]
     wvs = [cache.win_v] + [cache.win_v.clone() for _ in range(args.layers - 1)]
     B = cfg.B
-    plan = args.num_splits or lvq.lvq_decode_attn_splits(g, B, cache.max_len)   # -1: single pass
-    single = plan == -1
+    plan = args.num_splits or lvq.lvq_decode_attn_splits(g, B, cache.max_len)
     ws_bytes = lvq.lvq_decode_attn_workspace(g, B, cache.max_len, args.num_splits)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     outs = [torch.empty((B, g.H, g.D), dtype=torch.float32, device="cuda") for _ in range(args.layers)]
@@ -285,9 +281,8 @@ def main():
             if st != 0:
                 raise RuntimeError(lib.lvq_last_error().decode())
 
-    # The split path's dominant kernel alone: the index-page partial (one index_attn_kernel launch) into its
-    # own buffers.  (A single-pass call is itself one launch of the dominant kernel.)
-    S = 1 if single else plan
+    # The dominant kernel alone: the index-page partial (one index_mfma_kernel launch) into its own buffers.
+    S = plan
     part_o = torch.empty((B * g.H, S, g.D), dtype=torch.float32, device="cuda")
     part_lse = torch.empty((B * g.H, S), dtype=torch.float32, device="cuda")
     qws_bytes = lvq.lvq_quant_partial_workspace(g, B, cache.max_len)
@@ -309,7 +304,7 @@ def main():
             if st != 0:
                 raise RuntimeError(lib.lvq_last_error().decode())
 
-    dominant = one_step if single else quant_only
+    dominant = quant_only
     if args.mode == "index-only":
         for _ in range(args.warmup + args.steps):
             dominant()
@@ -318,7 +313,7 @@ def main():
         return
 
     log(f"[bench] warmup {args.warmup} steps ({len(calls)} calls each, "
-        f"{'single-pass kernel' if single else f'{plan} splits'})")
+        f"{plan} splits)")
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -333,21 +328,18 @@ def main():
     ms_total = e0.elapsed_time(e1)
     log(f"[bench] timed {args.steps} steps: {ms_total:.3f} ms")
 
-    if single:
-        ms_quant = ms_total / (args.steps * len(calls))      # a call is one launch of the dominant kernel
-    else:
-        # The dominant kernel alone, same rotation, HIP events on the stream it is launched on.
-        for _ in range(2):
-            quant_only()
-        torch.cuda.synchronize()
-        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        q0.record(stream)
-        for _ in range(args.steps):
-            quant_only()
-        q1.record(stream)
-        torch.cuda.synchronize()
-        ms_quant = q0.elapsed_time(q1) / (args.steps * len(qcalls))
-        log(f"[bench] index-page partial alone: {ms_quant * 1e3:.2f} us per launch")
+    # The dominant kernel alone, same rotation, HIP events on the stream it is launched on.
+    for _ in range(2):
+        quant_only()
+    torch.cuda.synchronize()
+    q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    q0.record(stream)
+    for _ in range(args.steps):
+        quant_only()
+    q1.record(stream)
+    torch.cuda.synchronize()
+    ms_quant = q0.elapsed_time(q1) / (args.steps * len(qcalls))
+    log(f"[bench] index-page partial alone: {ms_quant * 1e3:.2f} us per launch")
 
     cb_bytes = 2 if cfg.cb_dtype == "bf16" else 4
     parts = call_bytes(g, prob.lengths, cb_bytes)
@@ -356,8 +348,8 @@ def main():
     sec = ms_total / 1e3
     gbps = per_call * n_calls / sec / 1e9
     token_heads = sum(prob.lengths) * g.H
-    kernel = "index_full_kernel" if single else "index_attn_kernel"
-    qbytes = per_call if single else quant_kernel_bytes(g, prob.lengths, cb_bytes, S)
+    kernel = "index_mfma_kernel"
+    qbytes = quant_kernel_bytes(g, prob.lengths, cb_bytes, S)
     q_gbps = qbytes / (ms_quant / 1e3) / 1e9
     traffic = measured_traffic(kernel)
 
@@ -378,7 +370,7 @@ def main():
             "workload": WORKLOAD, "B": cfg.B, "H": cfg.H, "L": cfg.L, "T": cfg.T, "Tc": cfg.Tc, "G": cfg.G,
             "K": cfg.K, "codebook": cfg.cb_dtype, "sink": cfg.sink, "window": cfg.window, "page": cfg.page,
             "layers_rotated": args.layers, "calls_per_step": len(calls),
-            "path": "single-pass" if single else f"{plan} splits",
+            "path": f"{plan} splits",
             "requests_per_workgroup": 4,
         },
         "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),

@@ -94,8 +94,8 @@ def lvq_rope_table(length: int, D: int = 128, base: float = 10000.0, device="cud
 
 def lvq_rope_table_f16(length: int, D: int = 128, base: float = 10000.0, device="cuda",
                        stream=None) -> torch.Tensor:
-    """Packed fp16 cos/sin [16][length][8] for the index-page pass (layout in include/lvq.h)."""
-    out = torch.empty((16, length, 8), dtype=torch.float16, device=device)
+    """Packed fp16 cos/sin [length][32][8] for the index-page pass (layout in include/lvq.h)."""
+    out = torch.empty((length, 32, 8), dtype=torch.float16, device=device)
     check(lib.lvq_rope_table_f16(int(length), int(D), float(base), out.data_ptr(), _stream(stream)),
           "lvq_rope_table_f16")
     return out
@@ -105,8 +105,8 @@ def _rope_f16_ptr(rope_f16: Optional[torch.Tensor], rope_cos: torch.Tensor):
     if rope_f16 is None:
         return None
     _need(rope_f16, "rope_f16", torch.float16)
-    if tuple(rope_f16.shape) != (16, rope_cos.shape[0], 8):
-        raise ValueError("rope_f16 must be [16][rope_len][8] with the rope_cos length")
+    if tuple(rope_f16.shape) != (rope_cos.shape[0], 32, 8):
+        raise ValueError("rope_f16 must be [rope_len][32][8] with the rope_cos length")
     return rope_f16.data_ptr()
 
 
@@ -329,7 +329,7 @@ def lvq_window_append(g: lvq_geom, step: int, k_new: Optional[torch.Tensor], v_n
 
 
 def lvq_decode_attn_splits(g: lvq_geom, B: int, max_len: int) -> int:
-    """What lvq_decode_attn runs when num_splits = 0: -1 for the single-pass kernel, else its split count."""
+    """The split count lvq_decode_attn runs when num_splits = 0."""
     return int(lib.lvq_decode_attn_splits(C.byref(g), int(B), int(max_len)))
 
 

@@ -209,11 +209,10 @@ __global__ void __launch_bounds__(256) quant_partial_kernel(AttnArgs a) {
             const long phys = ptr[tok >> 3];
             const uint8_t* krow = a.pool + phys * g.page_bytes + (long(a.beta) * g.H + h) * 2 * 8 * NG + (tok & 7) * NG;
             const uint8_t* vrow = krow + 8 * NG;
-            const uint64_t ikA = load_idx<GPC>(krow, gA), ikB = load_idx<GPC>(krow, gB);
             float kA[32], kB[32];
 #pragma unroll
             for (int q = 0; q < GPC; ++q) {
-                const int ia = int((ikA >> (8 * q)) & 0xff), ib = int((ikB >> (8 * q)) & 0xff);
+                const int ia = krow[index_byte(0, NG, gA + q, tok)], ib = krow[index_byte(0, NG, gB + q, tok)];
                 load_cw<C>(cbk + ((gA + q) * K + ia) * C, kA + q * C);
                 load_cw<C>(cbk + ((gB + q) * K + ib) * C, kB + q * C);
             }
@@ -239,7 +238,7 @@ __global__ void __launch_bounds__(256) quant_partial_kernel(AttnArgs a) {
             float vA[32], vB[32];
 #pragma unroll
             for (int q = 0; q < GPC; ++q) {
-                const int ia = vrow[(gA + q) ^ (tok & 15)], ib = vrow[(gB + q) ^ (tok & 15)];
+                const int ia = vrow[index_byte(1, NG, gA + q, tok)], ib = vrow[index_byte(1, NG, gB + q, tok)];
                 load_cw<C>(cbv + ((gA + q) * K + ia) * C, vA + q * C);
                 load_cw<C>(cbv + ((gB + q) * K + ib) * C, vB + q * C);
             }
@@ -392,6 +391,7 @@ struct StaticFor {
 constexpr int kIThreads = 256;                    // index-page partial: 4 waves, two workgroups per CU
 constexpr int kChunk = 64;                        // tokens per wave iteration (one per lane)
 constexpr int kMaxSplitTok = 1536;                // index tokens per split at most (192 pages)
+constexpr int kMaxSplits = 1024;                  // splits per request at most
 constexpr int kChunksPerWave = kMaxSplitTok / kChunk / (kIThreads / 64);
 
 // Index-token range [lo, hi) of request slot j (request rq[j], none when >= B) of a workgroup in split
@@ -593,7 +593,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
         constexpr int qq = decltype(qc)::value;
         const int p = min(g.sink + c * kChunk + lane, a.rope_len - 1);
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) tr[4 * qq + mm] = a.rope16[long(4 * qq + mm) * a.rope_len + p];
+        for (int mm = 0; mm < 4; ++mm) tr[4 * qq + mm] = a.rope16[long(p) * 32 + 4 * qq + mm];
     };
     // Group of the i-th codeword gathered in quarter qq: lo groups first, then the hi groups holding
     // channels 64 + (the same frequencies).
@@ -895,6 +895,464 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Index-page partial for bf16 codebooks with c = 8 (16 index groups per token): the scores on the matrix
+// cores.  One workgroup per (head, split, group of R = 4 requests), 256 threads (4 waves), two workgroups
+// per CU.  Wave w takes the 16-token blocks w, w + 4, ... of the split for all four requests.
+//
+// Score of index token t of request r: with psi(p) the query turned back by the key's angle (rotate-half
+// pairing, channel i with i + 64, angle p * th_i),
+//   psi_i = cos(p th_i) q_i + sin(p th_i) q_{i+64},   psi_{i+64} = cos(p th_i) q_{i+64} - sin(p th_i) q_i,
+// q . R(p) k = k . psi(p), and k is the concatenation of the 16 codewords its indices name.  Per block of 16
+// tokens and request, four v_mfma_f32_16x16x32_f16 with the gathered codewords as the rows of A (8 channels
+// = one group per lane and k-block) and psi as the columns of B give C[row][col] = codeword(row) .
+// psi(col) summed over the 32 k-slots of each MFMA; the diagonal entries, where the row holds the column's
+// token, are the scores.  MFMA lane l = (n, kb) = (l & 15, l >> 4) holds row / column n and k-block kb;
+// k-slot (kb, m) of token t holds group P(4 kb + m) ^ t (the key-row byte layout, lvq.h), so that
+//  - lanes n = 0..15 of one k-block gather 16 distinct groups: with the step's K slice in LDS as fp16,
+//    codeword-major (row r of 256 bytes holds the 16 groups' codewords r), a 16-lane LDS phase reads 16
+//    distinct 16-byte columns, conflict-free;
+//  - lane (n, kb) holds for every m the 4 index bytes of dword kb of its token's key row;
+//  - slots m and m + 2 hold RoPE partner groups (x and x ^ 8) of one block of 8 frequencies, so a lane
+//    forms psi of both from one set of cos/sin: slot 0 is the lo group for n < 8 and the hi group for
+//    n >= 8, and the latter lanes read the packed table's copy with negated sines (qa, qb swapped):
+//    psi_m = qa cos + qb sin',  psi_{m+2} = qb cos - qa sin'.
+// psi depends only on the position and the request's query, so the lane's query (two blocks of 8
+// frequencies, lo and hi halves, as fp16 pairs pre-scaled by sm_scale * log2 e) stays in registers and the
+// position's cos/sin (one 64-byte load per lane and block) serve the four requests.  Request j's A rows are
+// its tokens permuted (row n holds token n ^ 4j), so that token n's diagonal entry lands in lane
+// (n, (n >> 2) ^ j), register n & 3: each lane ends with exactly one score per block, of request
+// kb ^ (n >> 2), taken by 15 selects.
+//
+// Weights: the workgroup's maximum per request; the K slice's LDS becomes bins [256 codewords][64 slots]
+// (slot 4 g + r); each lane adds exp2(s - max), in fixed point with fix_bits fraction bits, to the 16 bins of
+// its (request, token)'s value indices.  Value row byte i holds group i ^ (t & 15), so the 64 lanes of one
+// atomic hit 64 distinct (request, group) slots, i.e. 64 distinct banks.  Each bin address is one v_perm of
+// the index dword with a lane constant.
+//
+// Contraction: o = sum_r bin[g][r] * B_t^V[g][r] / sum of weights, as in the c = 4 kernel.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMBlk = 16;                                      // tokens per MFMA block
+constexpr int kMBlocksPerWave = kMaxSplitTok / kMBlk / 4 + 3;  // score registers per lane (whole rounds of 4)
+
+__device__ __forceinline__ uint32_t pack_q2(uint32_t w, float sc) {
+    const h2_t v = {(_Float16)(bf16_lo(w) * sc), (_Float16)(bf16_hi(w) * sc)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+template <bool KS>
+__global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
+    constexpr int D = 128, K = 256, NG = 16, C = 8, R = 4, NT = kIThreads, NW = NT / 64;
+    constexpr int NB = kMBlocksPerWave;
+    constexpr int PL = R * C;                       // partial sums per contraction lane
+    __shared__ __align__(16) unsigned char lds[K * 256];
+    __shared__ float wmax[NW][R];
+    __shared__ uint32_t pid_lds[R][kMaxSplitTok / 8];  // page ids of the split's pages, per request
+    uint32_t* bins = reinterpret_cast<uint32_t*>(lds);
+    const Geo& g = a.geo;
+    const int h = blockIdx.x, split = blockIdx.y, r0 = blockIdx.z * R;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, kb = lane >> 4;
+    int rq[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) rq[j] = group_request(a, r0 + j);
+
+    // K slice of head h: 16-byte chunk e = tid + NT * i is codeword e >> 4 of group e & 15 (global layout
+    // [group][codeword][8]); it goes to LDS byte 16 e = 256 * codeword + 16 * group.
+    uint4 stage[16];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_k) +
+                                                          h * a.slice_hstride);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = tid + NT * i;
+            stage[i] = src[(e & 15) * K + (e >> 4)];
+        }
+    }
+    int lo[R], hi[R];
+    if (!split_ranges<R>(a, split, rq, lo, hi)) {
+        for (int e = tid; e < R * D; e += NT) {
+            const int j = e / D, d = e % D, rb = rq[j];
+            if (rb >= a.B) continue;
+            const long row = (long(rb) * g.H + h) * a.S_tot + split;
+            a.part_o[row * D + d] = 0.f;
+            if (d == 0) a.part_lse[row] = -INFINITY;
+        }
+        return;
+    }
+    const int32_t* ptr[R];
+    int t_lo = 0x7fffffff, t_hi = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        ptr[j] = a.pt + long(min(rq[j], a.B - 1)) * a.pt_stride;
+        if (hi[j] > lo[j]) {
+            t_lo = min(t_lo, lo[j]);
+            t_hi = max(t_hi, hi[j]);
+        }
+    }
+    // The lane's query: blocks f1 = ((2 kb) ^ n) & 7 and f2 = f1 ^ 1 of 8 frequencies, qa = the half of
+    // slot 0's group, qb the partner half, as fp16 pairs times sm_scale * log2 e.
+    const int hl = (n >> 3) & 1;
+    const int f1 = ((2 * kb) ^ n) & 7;
+    uint32_t qa[R][2][4], qb[R][2][4];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const uint16_t* qp = a.q + (long(min(rq[j], a.B - 1)) * g.H + h) * D;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int f = f1 ^ s;
+            const uint4 wa = *reinterpret_cast<const uint4*>(qp + 64 * hl + 8 * f);
+            const uint4 wb = *reinterpret_cast<const uint4*>(qp + 64 * (hl ^ 1) + 8 * f);
+            qa[j][s][0] = pack_q2(wa.x, a.scale_log2); qa[j][s][1] = pack_q2(wa.y, a.scale_log2);
+            qa[j][s][2] = pack_q2(wa.z, a.scale_log2); qa[j][s][3] = pack_q2(wa.w, a.scale_log2);
+            qb[j][s][0] = pack_q2(wb.x, a.scale_log2); qb[j][s][1] = pack_q2(wb.y, a.scale_log2);
+            qb[j][s][2] = pack_q2(wb.z, a.scale_log2); qb[j][s][3] = pack_q2(wb.w, a.scale_log2);
+        }
+    }
+    // Gather address constants: byte j of ck[m] is 16 * (group of key-row byte 4 kb + m of token n ^ 4 j).
+    uint32_t ck[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int j = 0; j < R; ++j) v |= uint32_t(16 * key_group_of_byte(4 * kb + m, n ^ (4 * j))) << (8 * j);
+        ck[m] = v;
+    }
+    // The lane's own (request, token) of every block: request ro = kb ^ (n >> 2), token tau0 + n.
+    const int ro = kb ^ (n >> 2);
+    // bits 0, 1 of ro and of n for the score selects, hidden from the optimiser so that the selects stay a
+    // tree of 15 rather than becoming a dynamic register index
+    auto opaque_bit = [](int x, int bit) { asm volatile("" : "+v"(x)); return (x & bit) != 0; };
+    const bool br0 = opaque_bit(ro, 1), br1 = opaque_bit(ro, 2), bn0 = opaque_bit(n, 1), bn1 = opaque_bit(n, 2);
+    int lo_o = lo[0], hi_o = hi[0];
+    const int32_t* ptr_o = ptr[0];
+#pragma unroll
+    for (int j = 1; j < R; ++j)
+        if (ro == j) { lo_o = lo[j]; hi_o = hi[j]; ptr_o = ptr[j]; }
+
+    const uint32_t page_bytes = uint32_t(g.page_bytes);
+    const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG;   // (block, head) K rows of page 0
+    const uint4* rope = a.rope16;
+    const int nblk = (t_hi - t_lo + kMBlk - 1) / kMBlk;   // blocks of the workgroup
+    const int nk = wave < nblk ? (nblk - wave + NW - 1) / NW : 0;   // blocks of this wave: wave + NW k, k < nk
+    // Page ids of the split's pages (index-token page (tau - t_lo) / 8), per request: a page past a request's
+    // range holds its last index page, a request without index pages physical page 0, so that every load below
+    // reads valid memory.  Loads never branch: a block past the end is clamped to the last one.
+    for (int e = tid; e < R * (kMaxSplitTok / 8); e += NT) {
+        const int j = e / (kMaxSplitTok / 8), pp = e % (kMaxSplitTok / 8);
+        const int tau = min(t_lo + 8 * pp, hi[j] - 1);
+        pid_lds[j][pp] = hi[j] > 0 ? uint32_t(ptr[j][max(tau, 0) >> 3]) : 0u;
+    }
+    auto tau0_of = [&](int k) { return t_lo + kMBlk * min(wave + NW * k, nblk - 1); };
+    // Per-lane parts of the load addresses (blocks start at multiples of 16 tokens, so token n ^ 4 j of a
+    // block sits in page (tau0 - t_lo) / 8 + ((n ^ 4 j) >> 3) at row (n ^ 4 j) & 7).
+    const uint32_t* pid_flat = &pid_lds[0][0];
+    const unsigned char* kbase[R];                  // dword kb of that row in page 0's (block, head) K rows
+    int pidx[R];                                    // its page-table entry, relative to the block's first page
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        kbase[j] = slab + ((n ^ (4 * j)) & 7) * NG + 4 * kb;
+        pidx[j] = j * (kMaxSplitTok / 8) + ((n ^ (4 * j)) >> 3);
+    }
+    const uint4* rope_l1 = rope + 16 * hl + 2 * f1;          // the lane's cos/sin chunks at position 0
+    const uint4* rope_l2 = rope + 16 * hl + 2 * (f1 ^ 1);
+    // key-row dwords of the wave's k-th block: dword kb of token n ^ 4 j of request j
+    auto load_ik = [&](int k, uint32_t (&ik)[R]) {
+        const int pp = (tau0_of(k) - t_lo) >> 3;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const uint32_t pid = pid_flat[pidx[j] + pp];
+            ik[j] = *reinterpret_cast<const uint32_t*>(kbase[j] + uint64_t(pid) * page_bytes);
+        }
+    };
+    // cos/sin chunks of the lane's token (block f1: 2, block f2: 2) and its key scale (KS)
+    struct CsBuf { uint4 cs[4]; float ks; };
+    auto load_cs = [&](int k, CsBuf& b) {
+        const int tau0 = tau0_of(k);
+        const uint32_t p = uint32_t(min(g.sink + tau0 + n, a.rope_len - 1));
+        const uint4* r1 = rope_l1 + uint64_t(p) * 32;
+        const uint4* r2 = rope_l2 + uint64_t(p) * 32;
+        b.cs[0] = r1[0];
+        b.cs[1] = r1[1];
+        b.cs[2] = r2[0];
+        b.cs[3] = r2[1];
+        if constexpr (KS) {
+            const uint32_t pid = pid_lds[ro][(tau0 + n - t_lo) >> 3];
+            b.ks = f16_to_f32(a.kscale[(uint64_t(pid) * g.T + a.step) * 8 + ((tau0 + n) & 7)]);
+        }
+    };
+    float sreg[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) sreg[i] = -INFINITY;
+    float rmax = -INFINITY;
+    // The wave's k-th block: the scores of the four requests, the lane's own kept.
+    // Codeword gathers of request j of a block from its key-row dwords (one v_perm and one 16-byte LDS read
+    // per MFMA slot).
+    auto gather = [&](auto jc, uint32_t ikj, uint4 (&G)[4]) {
+        constexpr int j = decltype(jc)::value;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t sel = 0x0c0c0000u | (uint32_t(4 + m) << 8) | uint32_t(j);
+            G[m] = *reinterpret_cast<const uint4*>(lds + __builtin_amdgcn_perm(ikj, ck[m], sel));
+        }
+    };
+    // psi of request j times its gathered codewords: the four MFMAs of one accumulator
+    auto request_mfma = [&](auto jc, const uint4 (&G)[4], const uint32_t (&c)[2][4], const uint32_t (&s)[2][4]) {
+        constexpr int j = decltype(jc)::value;
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int u = m & 1;
+            uint32_t psi[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const h2_t cc = as_h2(c[u][q]), ss = as_h2(s[u][q]);
+                const h2_t x = as_h2(qa[j][u][q]), y = as_h2(qb[j][u][q]);
+                const h2_t v = m < 2 ? __builtin_elementwise_fma(x, cc, y * ss)
+                                     : __builtin_elementwise_fma(y, cc, -(x * ss));
+                psi[q] = __builtin_bit_cast(uint32_t, v);
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(f16x8_t, G[m]),
+                __builtin_bit_cast(f16x8_t, make_uint4(psi[0], psi[1], psi[2], psi[3])), acc, 0, 0, 0);
+        }
+        return acc;
+    };
+    using J0 = std::integral_constant<int, 0>;
+    using J1 = std::integral_constant<int, 1>;
+    using J2 = std::integral_constant<int, 2>;
+    using J3 = std::integral_constant<int, 3>;
+    // The wave's k-th block: the scores of the four requests, the lane's own kept.  The gathers of request 0
+    // arrive in G0 (issued during the block before); each request's gathers are issued one request ahead,
+    // and the next block's request 0 into G0 (ikn: its key-row dwords).
+    auto score_blk = [&](int k, const uint32_t (&ik)[R], const CsBuf& b, uint4 (&G0)[4], const uint32_t (&ikn)[R]) {
+        uint32_t c[2][4], s[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            c[u][0] = b.cs[2 * u].x; c[u][1] = b.cs[2 * u].y; c[u][2] = b.cs[2 * u + 1].x; c[u][3] = b.cs[2 * u + 1].y;
+            s[u][0] = b.cs[2 * u].z; s[u][1] = b.cs[2 * u].w; s[u][2] = b.cs[2 * u + 1].z; s[u][3] = b.cs[2 * u + 1].w;
+        }
+        f32x4_t acc[R];
+        uint4 G1[4], G2[4], G3[4];
+        gather(J1{}, ik[1], G1);
+        acc[0] = request_mfma(J0{}, G0, c, s);
+        gather(J2{}, ik[2], G2);
+        acc[1] = request_mfma(J1{}, G1, c, s);
+        gather(J3{}, ik[3], G3);
+        acc[2] = request_mfma(J2{}, G2, c, s);
+        gather(J0{}, ikn[0], G0);
+        acc[3] = request_mfma(J3{}, G3, c, s);
+        // the lane's own score: request ro, register n & 3 of its accumulator (15 selects on the lane bits)
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x01 = br0 ? acc[1][i] : acc[0][i];
+            const float x23 = br0 ? acc[3][i] : acc[2][i];
+            e[i] = br1 ? x23 : x01;
+        }
+        const float e01 = bn0 ? e[1] : e[0];
+        const float e23 = bn0 ? e[3] : e[2];
+        float sc = bn1 ? e23 : e01;
+        if constexpr (KS) sc *= b.ks;
+        const int tau = t_lo + kMBlk * (wave + NW * k) + n;
+        sc = (k < nk && tau >= lo_o && tau < hi_o) ? sc : -INFINITY;
+        rmax = fmaxf(rmax, sc);
+        sreg[k] = sc;
+    };
+    __syncthreads();                                      // page ids in LDS
+    // key-row dwords four blocks ahead (set k % 4), cos/sin two blocks ahead (set k % 2); each set is reloaded
+    // right after its block is scored.  The first loads are issued before the K slice is stored to LDS.
+    uint32_t IK0[R], IK1[R], IK2[R], IK3[R];
+    CsBuf C0, C1;
+    if (nk > 0) {
+        load_ik(0, IK0);
+        load_ik(1, IK1);
+        load_ik(2, IK2);
+        load_ik(3, IK3);
+        load_cs(0, C0);
+        load_cs(1, C1);
+    }
+    {   // K slice, bf16 -> fp16
+        uint4* dst = reinterpret_cast<uint4*>(lds);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            dst[tid + NT * i] = make_uint4(bf16x2_to_f16x2(stage[i].x), bf16x2_to_f16x2(stage[i].y),
+                                           bf16x2_to_f16x2(stage[i].z), bf16x2_to_f16x2(stage[i].w));
+    }
+    __syncthreads();                                      // K slice staged
+    if (nk > 0) {
+        uint4 G0[4];
+        gather(J0{}, IK0[0], G0);
+        // whole rounds of four blocks: a round's blocks past the wave's last one rescore that block with their
+        // scores discarded (the loop has one exit, so the loads in flight are counted across iterations)
+        for (int k = 0; k < nk; k += 4) {
+            score_blk(k, IK0, C0, G0, IK1);
+            load_ik(k + 4, IK0);
+            load_cs(k + 2, C0);
+            score_blk(k + 1, IK1, C1, G0, IK2);
+            load_ik(k + 5, IK1);
+            load_cs(k + 3, C1);
+            score_blk(k + 2, IK2, C0, G0, IK3);
+            load_ik(k + 6, IK2);
+            load_cs(k + 4, C0);
+            score_blk(k + 3, IK3, C1, G0, IK0);
+            load_ik(k + 7, IK3);
+            load_cs(k + 5, C1);
+        }
+    }
+    // value rows of the lane's own (request, token) of the wave's k-th block, the first four loaded now
+    const unsigned char* vbase = slab + (8 + (n & 7)) * NG;   // the lane's value row in page 0
+    const int vidx = ro * (kMaxSplitTok / 8) + (n >> 3);
+    auto load_vr = [&](int k) -> uint4 {
+        const uint32_t pid = pid_flat[vidx + ((tau0_of(k) - t_lo) >> 3)];
+        return *reinterpret_cast<const uint4*>(vbase + uint64_t(pid) * page_bytes);
+    };
+    uint4 VR0 = make_uint4(0u, 0u, 0u, 0u), VR1 = VR0, VR2 = VR0, VR3 = VR0;
+    if (nk > 0) {
+        VR0 = load_vr(0);
+        VR1 = load_vr(1);
+        VR2 = load_vr(2);
+        VR3 = load_vr(3);
+    }
+
+    // ---- weights ----
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const float mw = wave_max_dpp(ro == j ? rmax : -INFINITY);
+        if (lane == 0) wmax[wave][j] = mw;
+    }
+    __syncthreads();                                // every wave is done with the K slice
+#pragma unroll
+    for (int i = 0; i < K * 64 / 4 / NT; ++i) reinterpret_cast<uint4*>(bins)[tid + i * NT] = make_uint4(0u, 0u, 0u, 0u);
+    // V rows of this lane's contraction block, needed once the bins are complete
+    const int cb_blk = tid >> 4, g16 = tid & 15;
+    uint4 vrow[16];
+    {
+        const uint16_t* vsl = static_cast<const uint16_t*>(a.slice_v) + h * a.slice_hstride;
+        const uint4* src = reinterpret_cast<const uint4*>(vsl + (long(g16) * K + 16 * cb_blk) * C);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vrow[i] = src[i];
+    }
+    __syncthreads();                                // bins cleared, wave maxima visible
+    float M[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        M[j] = wmax[0][j];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M[j] = fmaxf(M[j], wmax[w][j]);
+    }
+    float Mo = M[0];
+#pragma unroll
+    for (int j = 1; j < R; ++j) if (ro == j) Mo = M[j];
+    // bin byte offsets of the lane's value-row bytes: byte i of cv[w] = 4 * (4 * ((4 w + i) ^ n) + ro)
+    uint32_t cv[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v |= uint32_t(4 * (4 * ((4 * w + i) ^ n) + ro)) << (8 * i);
+        cv[w] = v;
+    }
+    const float fix_scale = float(1u << a.fix_bits);
+    auto bin_blk = [&](float sc, const uint4& v4) {
+        // out-of-range tokens hold -inf: weight 0 (their rows are valid memory, their bins any)
+        const uint32_t wgt = sc == -INFINITY ? 0u : uint32_t(fmaf(__builtin_amdgcn_exp2f(sc - Mo), fix_scale, 0.5f));
+        const uint32_t vw[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const uint32_t sel = 0x0c0c0000u | (uint32_t(4 + (m & 3)) << 8) | uint32_t(m & 3);
+            const uint32_t addr = __builtin_amdgcn_perm(vw[m >> 2], cv[m >> 2], sel);
+            uint32_t* bin = static_cast<uint32_t*>(__builtin_assume_aligned(lds + addr, 4));
+            __hip_atomic_fetch_add(bin, wgt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    };
+    // value rows four blocks ahead (set k % 4); whole rounds of four blocks as above (discarded scores are
+    // -inf: weight 0).  A round's scores are read from the (dynamically indexed) score registers at the start
+    // of the round before, when the only loads in flight are the value rows that round needs at once.
+    float S0 = sreg[0], S1 = sreg[1], S2 = sreg[2], S3 = sreg[3];
+    for (int k = 0; k < nk; k += 4) {
+        const float N0 = sreg[min(k + 4, NB - 1)], N1 = sreg[min(k + 5, NB - 1)];
+        const float N2 = sreg[min(k + 6, NB - 1)], N3 = sreg[min(k + 7, NB - 1)];
+        bin_blk(S0, VR0);
+        VR0 = load_vr(k + 4);
+        bin_blk(S1, VR1);
+        VR1 = load_vr(k + 5);
+        bin_blk(S2, VR2);
+        VR2 = load_vr(k + 6);
+        bin_blk(S3, VR3);
+        VR3 = load_vr(k + 7);
+        S0 = N0; S1 = N1; S2 = N2; S3 = N3;
+    }
+    __syncthreads();
+
+    // ---- contraction: lane (cb_blk, g16) over its 16 codewords ----
+    float o[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) o[i] = 0.f;
+    uint32_t lsum[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) lsum[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 16 * cb_blk + i;
+        const uint4 b4 = *reinterpret_cast<const uint4*>(bins + r * 64 + g16 * R);
+        const uint32_t bv[R] = {b4.x, b4.y, b4.z, b4.w};
+        const uint32_t vw[4] = {vrow[i].x, vrow[i].y, vrow[i].z, vrow[i].w};
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            lsum[j] += bv[j];
+            const float bw = float(bv[j]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                o[j * C + 2 * u] = fmaf(bw, bf16_lo(vw[u]), o[j * C + 2 * u]);
+                o[j * C + 2 * u + 1] = fmaf(bw, bf16_hi(vw[u]), o[j * C + 2 * u + 1]);
+            }
+        }
+    }
+    // Partials over this wave's own bin rows (64 rows of 256 B, read by no other wave): lane slot
+    // (cb_blk & 3) * 16 + g16 holds PL floats, then the weight totals of the g16 = 0 lanes.
+    float* part = reinterpret_cast<float*>(lds) + wave * 4096;
+    {
+        float4* dst = reinterpret_cast<float4*>(part + ((cb_blk & 3) * 16 + g16) * PL);
+#pragma unroll
+        for (int i = 0; i < PL / 4; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+        if (g16 == 0) {
+            uint32_t* ld = reinterpret_cast<uint32_t*>(part + 64 * PL) + (cb_blk & 3) * R;
+#pragma unroll
+            for (int j = 0; j < R; ++j) ld[j] = lsum[j];
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < R * D; e += NT) {
+        const int j = e / D, d = e % D, rb = rq[j];
+        if (rb >= a.B) continue;
+        const long orow = (long(rb) * g.H + h) * a.S_tot + split;
+        if (hi[j] <= lo[j]) {
+            a.part_o[orow * D + d] = 0.f;
+            if (d == 0) a.part_lse[orow] = -INFINITY;
+            continue;
+        }
+        const int gr = d / C, u = d % C;
+        const int p = j * C + u;
+        const float* pbase = reinterpret_cast<const float*>(lds);
+        float accv = 0.f;
+        uint64_t L = 0;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+            const float* pw = pbase + (b >> 2) * 4096;
+            accv += pw[((b & 3) * 16 + gr) * PL + p];
+            L += reinterpret_cast<const uint32_t*>(pw + 64 * PL)[(b & 3) * R + j];
+        }
+        const float Lf = float(L);
+        a.part_o[orow * D + d] = accv / Lf;
+        if (d == 0) a.part_lse[orow] = (M[j] + (log2f(Lf) - float(a.fix_bits))) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // bf16 window: sinks [0, min(L, sink)) and recent tokens [sink + 8*n_pages, L)
 // of loop step t.  Grid (head, request); 256 threads in 16 rows of 16 lanes;
 // row r takes window tokens r, r + 16, ...  Lane c of a row owns channels
@@ -1104,523 +1562,6 @@ __global__ void __launch_bounds__(256, 4) window_kernel(AttnArgs a, float* __res
 }
 
 // ---------------------------------------------------------------------------
-// Single-pass decode attention for bf16 codebooks: one workgroup of 512
-// threads (8 waves, alone on its CU) per (head, group of R requests) does the
-// whole call, window and merge included, and writes the output rows.  The K
-// slice is staged in LDS once; the index tokens are taken in items of
-// kItemTok (the fixed-point weights of an item share one maximum), each
-// scored, binned and contracted as in index_attn_kernel, and the items and
-// the window are merged per output element with a running logsumexp.  Wave w
-// takes chunks w, w + 8, w + 16, ... of 64 tokens, three per item, so its
-// load stream runs on across items: the page ids of the next item and the
-// key index rows of its first chunk are in flight while the current item
-// finishes.
-//
-// LDS (bytes): [0, 64K) K slice (fp16); [64K, 128K) bins u32 [256][R*NG];
-// [128K, 144K) partials (window rows, then per-wave contraction partials);
-// then wave maxima, wave weight totals and the window rows' (m, l).  The bin
-// address of an atomic is one v_perm: [slot offset, codeword, 0x01, 0] with
-// the 0x01 (the 64K page of the bins) taken from the base word.  Each wave
-// contracts, and zeroes behind itself, the 32 bin rows no other wave reads,
-// so the bins are clear for the next item without a pass of their own.
-// ---------------------------------------------------------------------------
-constexpr int kFThreads = 512;
-constexpr int kItemTok = 1536;                    // index tokens per item (fixed-point weights of one maximum)
-
-// Sum of x over the four 16-lane rows of the wave (every lane gets the sum at its position in the row).
-// (The swap results are copied out of their vector before the bit casts: a bit cast of a vector element
-// reads element 0.)
-template <typename T>
-__device__ __forceinline__ T sum_rows4(T x) {
-    const uint32_t xi = __builtin_bit_cast(uint32_t, x);
-    const auto t = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);   // lanes l and l ^ 32
-    const uint32_t t0 = t[0], t1 = t[1];
-    const T y = __builtin_bit_cast(T, t0) + __builtin_bit_cast(T, t1);
-    const uint32_t yi = __builtin_bit_cast(uint32_t, y);
-    const auto u = __builtin_amdgcn_permlane16_swap(yi, yi, false, false);   // rows r and r ^ 1
-    const uint32_t u0 = u[0], u1 = u[1];
-    return __builtin_bit_cast(T, u0) + __builtin_bit_cast(T, u1);
-}
-
-template <int C, int R>
-__global__ void __launch_bounds__(kFThreads, 1) index_full_kernel(AttnArgs a, float* __restrict__ out,
-                                                                   float* __restrict__ lse_out) {
-    constexpr int D = 128, K = 256, NG = D / C, NT = kFThreads, NW = NT / 64;
-    constexpr int CPI = kItemTok / kChunk;         // chunks per item
-    constexpr int NFAST = NW / 2;                  // the first waves of the workgroup
-    constexpr int FCH = 3, SCH = 3;                // chunks per item of the first waves, of the others
-    constexpr int SH = (C == 8) ? 4 : 3;           // byte offset of codeword r in its group row: r << SH
-    constexpr int IW = NG / 4;                     // index dwords per token row
-    constexpr int GQ = (C == 8) ? 4 : 8;           // codewords gathered per score step
-    constexpr int GW = C / 2;                      // dwords per fp16 codeword
-    constexpr int NSTEP = 4 * R;                   // score steps per chunk (even: buffers alternate)
-    constexpr int KS = NG * K * C * 2;             // bytes of the fp16 K slice
-    constexpr int NSTAGE = KS / 16 / NT;
-    constexpr int GPL = NG / 16;                   // groups per contraction lane
-    constexpr int PL = R * C * GPL;                // partial sums per contraction lane
-    constexpr int CPB = K / (NT / 16);             // codewords per contraction lane
-    constexpr int VPG = CPB * C * 2 / 16;          // 16-byte V words per contraction lane and group
-    constexpr int NWW = NFAST;                     // waves that attend the window: the first ones
-    constexpr int RPJ = NWW * 4 / R;               // window rows (of 16 lanes) per request
-    constexpr int PART = 4096;                     // floats of the partials region
-    static_assert(NFAST * FCH + (NW - NFAST) * SCH == CPI && NSTEP % 2 == 0 && R * NG == 64 && CPB == 8,
-                  "item and contraction shapes");
-    static_assert(16 * PL * NW <= PART && NWW * 4 * D <= PART, "partials region");
-    static_assert(RPJ % 4 == 0, "a wave's window rows belong to one request");
-    __shared__ __align__(16) unsigned char lds[2 * KS + PART * 4 + 2 * NW * R * 4 + 32 * 2 * 4];
-    uint32_t* const bins = reinterpret_cast<uint32_t*>(lds + KS);
-    float* const part = reinterpret_cast<float*>(lds + 2 * KS);
-    float (*const wmax)[R] = reinterpret_cast<float (*)[R]>(lds + 2 * KS + PART * 4);
-    uint32_t (*const lw)[R] = reinterpret_cast<uint32_t (*)[R]>(lds + 2 * KS + PART * 4 + NW * R * 4);
-    float (*const wml)[2] = reinterpret_cast<float (*)[2]>(lds + 2 * KS + PART * 4 + 2 * NW * R * 4);   // [16]
-    const Geo& g = a.geo;
-    const int h = blockIdx.x, r0 = blockIdx.y * R;
-    int rq[R];                                      // the requests of the workgroup's slots (>= B: none)
-#pragma unroll
-    for (int j = 0; j < R; ++j) rq[j] = group_request(a, r0 + j);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    // ---- setup ----
-    uint32_t qraw = 0;                              // two bf16 query elements (packed-query dword tid & 63)
-    const int qj = tid >> 6, qt = tid & 63;
-    const long qprow = long(min(rq[min(qj, R - 1)], a.B - 1)) * g.H + h;
-    if (tid < R * 64) {
-        const int m = qt >> 2, k = qt & 3;
-        const int ch = (k < 2 ? 0 : 64) + 4 * m + 2 * (k & 1);
-        qraw = *reinterpret_cast<const uint32_t*>(a.q + qprow * D + ch);
-    }
-    uint4 stage[NSTAGE];
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_k) +
-                                                          h * a.slice_hstride);
-#pragma unroll
-        for (int i = 0; i < NSTAGE; ++i) stage[i] = src[tid + i * NT];
-    }
-    if (tid < R * 64) {   // packed query rows: dword t of row j is the fp16 pair of score chunk t >> 2
-        const h2_t v = {(_Float16)(bf16_lo(qraw) * a.scale_log2), (_Float16)(bf16_hi(qraw) * a.scale_log2)};
-        const_cast<uint32_t*>(a.qpack)[qprow * 64 + qt] = __builtin_bit_cast(uint32_t, v);
-    }
-    int hi[R];
-    long srow[R];
-    const int32_t* ptr[R];
-    int t_hi = 0;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        const int rb = min(rq[j], a.B - 1);
-        hi[j] = rq[j] < a.B ? n_index_pages(clamp_len(a, rb), g) * g.page : 0;
-        ptr[j] = a.pt + long(rb) * a.pt_stride;
-        srow[j] = long(rb) * g.H + h;
-        t_hi = max(t_hi, hi[j]);
-    }
-    const uint32_t page_bytes = uint32_t(g.page_bytes);
-    const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG;   // (block, head) slab of page 0
-
-    // Every lane issues the same loads: lanes past a request's last token read a valid page of the request
-    // through the clamped page id (a request with no index page reads physical page 0).
-    auto in_req = [&](int j, int tau) { return tau < hi[j]; };
-    auto load_pid = [&](int c, uint32_t (&pid)[R]) {
-        const int tau = c * kChunk + lane;
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            const uint32_t e = uint32_t(ptr[j][max(0, min(tau, hi[j] - 1)) >> 3]);
-            pid[j] = hi[j] > 0 ? e : 0u;
-        }
-    };
-    // index row words of chunk c: kv = 0 for the key row, 1 for the value row
-    auto load_idx = [&](int c, int kv, const uint32_t (&pid)[R], uint32_t (&ix)[R][IW]) {
-        const int tau = c * kChunk + lane;
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            const uint4* row = reinterpret_cast<const uint4*>(slab + uint64_t(pid[j]) * page_bytes +
-                                                              (kv * 8 + (tau & 7)) * NG);
-#pragma unroll
-            for (int w = 0; w < IW / 4; ++w) {
-                const uint4 kv4 = row[w];
-                ix[j][4 * w] = kv4.x; ix[j][4 * w + 1] = kv4.y; ix[j][4 * w + 2] = kv4.z; ix[j][4 * w + 3] = kv4.w;
-            }
-        }
-    };
-    // Chunks of an item (CPI of them): waves w < NFAST take w + 4i (i < FCH), the others
-    // 4 FCH + (w - NFAST) + 4i (i < SCH); a SIMD holds wave w and wave w + NFAST.
-    const bool fast = wave < NFAST;
-    const int cbase = fast ? wave : 4 * FCH + wave - NFAST;   // chunk of slot 0 in item 0
-    constexpr int MCH = FCH > SCH ? FCH : SCH;
-    uint32_t pidc[MCH][R];                          // page ids of the current item's chunks (slots)
-    if (t_hi > 0) {                                 // (no page table to read otherwise)
-#pragma unroll
-        for (int i = 0; i < MCH; ++i)
-            if (i < (fast ? FCH : SCH)) load_pid(cbase + 4 * i, pidc[i]);
-    }
-    {   // bins start clear; each item's contraction clears them again behind itself
-#pragma unroll
-        for (int i = 0; i < 64 * K / 4 / NT; ++i) reinterpret_cast<uint4*>(bins)[tid + i * NT] = make_uint4(0u, 0u, 0u, 0u);
-    }
-
-    {   // K slice of head h, bf16 -> fp16
-        uint4* dst = reinterpret_cast<uint4*>(lds);
-#pragma unroll
-        for (int i = 0; i < NSTAGE; ++i)
-            dst[tid + i * NT] = make_uint4(bf16x2_to_f16x2(stage[i].x), bf16x2_to_f16x2(stage[i].y),
-                                           bf16x2_to_f16x2(stage[i].z), bf16x2_to_f16x2(stage[i].w));
-    }
-    // Other waves read the packed query rows through the scalar cache after the barrier below, which
-    // orders LDS only: the vector stores must have reached L2 first.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-    // ---- score machinery (as in index_attn_kernel) ----
-    uint4 tr[16];                                   // cos/sin of the lane's position, 4 frequencies each
-    auto load_tr = [&](int c, auto qc) {
-        constexpr int qq = decltype(qc)::value;
-        const int p = min(g.sink + c * kChunk + lane, a.rope_len - 1);
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm) tr[4 * qq + mm] = a.rope16[long(4 * qq + mm) * a.rope_len + p];
-    };
-    auto group_of = [](int qq, int i) constexpr {
-        return C == 8 ? (i < 2 ? 2 * qq + i : 8 + 2 * qq + (i - 2)) : (i < 4 ? 4 * qq + i : 16 + 4 * qq + (i - 4));
-    };
-    auto gather = [&](const uint32_t (&ik)[R][IW], auto qc, auto jc, uint32_t (&G)[GQ][GW]) {
-        constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
-        StaticFor<0, GQ>::run([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            constexpr int gi = group_of(qq, i);
-            const uint32_t off = byte_shl<SH, gi & 3>(ik[j][gi >> 2]);
-            const unsigned char* pcw = lds + gi * (K * C * 2) + off;
-            if constexpr (C == 8) {
-                const uint4 v = *reinterpret_cast<const uint4*>(pcw);
-                G[i][0] = v.x; G[i][1] = v.y; G[i][2] = v.z; G[i][3] = v.w;
-            } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(pcw);
-                G[i][0] = v.x; G[i][1] = v.y;
-            }
-        });
-    };
-    const_ptr<uint32_t> qrow[R];
-    // The packed query rows and the V rows are the same in every item: their base pointers pass through an
-    // empty asm at the top of each item, so that their loads stay where they are written instead of being
-    // hoisted out of the item loop (which would hold all of them in registers across it).
-    auto set_qrow = [&]() {
-        const uint32_t* qp = a.qpack;
-        asm volatile("" : "+s"(qp));
-#pragma unroll
-        for (int j = 0; j < R; ++j) qrow[j] = as_const(qp + srow[j] * 64);
-    };
-    set_qrow();
-    auto load_q = [&](auto qc, auto jc, uint32_t (&qs)[16]) {
-        constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) qs[u] = qrow[j][16 * qq + u];
-    };
-    float acc[R][2];
-    float rmax[R];
-    float sreg[MCH][R];                             // scores of the wave's chunks of the item
-    auto compute = [&](auto qc, auto jc, const uint32_t (&G)[GQ][GW], const uint32_t (&qs)[16]) {
-        constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {           // RoPE frequencies 4m .. 4m+3
-            const int m = 4 * qq + mm;
-            const h2_t c01 = as_h2(tr[m].x), c23 = as_h2(tr[m].y);
-            const h2_t s01 = as_h2(tr[m].z), s23 = as_h2(tr[m].w);
-            const h2_t l01 = as_h2(qs[4 * mm]), l23 = as_h2(qs[4 * mm + 1]);
-            const h2_t u01 = as_h2(qs[4 * mm + 2]), u23 = as_h2(qs[4 * mm + 3]);
-            const h2_t pl01 = __builtin_elementwise_fma(c01, l01, s01 * u01);
-            const h2_t pl23 = __builtin_elementwise_fma(c23, l23, s23 * u23);
-            const h2_t ph01 = __builtin_elementwise_fma(c01, u01, -(s01 * l01));
-            const h2_t ph23 = __builtin_elementwise_fma(c23, u23, -(s23 * l23));
-            uint32_t kl01, kl23, kh01, kh23;
-            if constexpr (C == 8) {
-                const int il = mm >> 1, d = (mm & 1) * 2;
-                kl01 = G[il][d]; kl23 = G[il][d + 1];
-                kh01 = G[2 + il][d]; kh23 = G[2 + il][d + 1];
-            } else {
-                kl01 = G[mm][0]; kl23 = G[mm][1];
-                kh01 = G[4 + mm][0]; kh23 = G[4 + mm][1];
-            }
-            acc[j][0] = dot2h(kl01, pl01, acc[j][0]);
-            acc[j][1] = dot2h(kl23, pl23, acc[j][1]);
-            acc[j][0] = dot2h(kh01, ph01, acc[j][0]);
-            acc[j][1] = dot2h(kh23, ph23, acc[j][1]);
-        }
-    };
-    uint32_t G[2][GQ][GW];
-    uint32_t qs[2][16];
-    // Chunk slot I of N in the item (chunk c): steps k = (qq, j); the last step issues the cos/sin of the
-    // first quarter of the wave's next chunk cn and, but in the item's last slot, its first gathers (from
-    // ikn) and query quarter.  (The item's end starts the next item's gathers afresh, so that they are not
-    // held in registers through the weights and the contraction.)
-    auto run_chunk = [&](auto Ic, auto Nc, int c, int cn, const uint32_t (&ikc)[R][IW],
-                         const uint32_t (&ikn)[R][IW]) {
-        constexpr int I = decltype(Ic)::value, N = decltype(Nc)::value;
-        StaticFor<0, NSTEP>::run([&](auto kc) {
-            constexpr int k = decltype(kc)::value, qq = k / R, j = k % R, b = k & 1;
-            constexpr int k1 = (k + 1) % NSTEP;
-            using QN = std::integral_constant<int, k1 / R>;
-            using JN = std::integral_constant<int, k1 % R>;
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this step's gathers and query quarter
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (k + 1 < NSTEP) gather(ikc, QN{}, JN{}, G[b ^ 1]);
-            else if constexpr (I + 1 < N) gather(ikn, QN{}, JN{}, G[b ^ 1]);
-            if constexpr (k + 1 < NSTEP || I + 1 < N) load_q(QN{}, JN{}, qs[b ^ 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (j == 0) load_tr(qq < 3 ? c : cn, std::integral_constant<int, (qq + 1) % 4>{});
-            compute(std::integral_constant<int, qq>{}, std::integral_constant<int, j>{}, G[b], qs[b]);
-            if constexpr (qq == 3) {
-                const bool in = in_req(j, c * kChunk + lane);
-                const float s_all = acc[j][0] + acc[j][1];
-                acc[j][0] = 0.f;
-                acc[j][1] = 0.f;
-                sreg[I][j] = s_all;
-                rmax[j] = fmaxf(rmax[j], in ? s_all : -INFINITY);
-            }
-        });
-    };
-
-    uint32_t ik[3][R][IW];                          // key index rows of slot I in ik[I % (N even ? 2 : 3)]
-    if (t_hi > 0) {
-        load_idx(cbase, 0, pidc[0], ik[0]);
-        load_tr(cbase, std::integral_constant<int, 0>{});
-    }
-    __syncthreads();                                // K slice staged, query rows packed
-
-    // ---- window: the first NWW waves attend it while the others start on the first item (the first waves
-    // of a workgroup get the issue slots first when both of a SIMD's waves are ready, and run their score
-    // loop about twice as fast).  Window row wr = tid >> 4 of 16 lanes takes tokens of request wj spaced
-    // RPJ apart; every row of a wave serves the same request.  The rows' results wait in registers until
-    // after the last item.
-    const int c16 = tid & 15, wr = tid >> 4;
-    float wm = -INFINITY, wl = 0.f, wo[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) wo[u] = 0.f;
-    if (wave < NWW) {
-        const int wj = wave * 4 / RPJ;
-        const int wrb = group_request(a, r0 + wj);
-        window_row(a, min(wrb, a.B - 1), h, wrb < a.B, wr % RPJ, RPJ, c16, wm, wl, wo);
-    }
-
-    // Running merge of this thread's output element (request j, channel d), in log2 units: each item, then
-    // the window.  m = -inf: nothing yet.
-    const int oj = tid / D, od = tid % D;
-    float run_m = -INFINITY, run_l = 0.f, run_o = 0.f;
-#pragma unroll
-    for (int j = 0; j < R; ++j) acc[j][0] = acc[j][1] = 0.f;
-
-    const float fix_scale = float(1u << a.fix_bits);
-    const uint16_t* vsl = static_cast<const uint16_t*>(a.slice_v) + h * a.slice_hstride;
-    const int n_items = (t_hi + kItemTok - 1) / kItemTok;
-    auto item_loop = [&](auto Nc) {
-      constexpr int N = decltype(Nc)::value;        // chunk slots of this wave
-      int c = cbase;                                // the wave's chunk in slot 0 of the item
-      for (int it = 0; it < n_items; ++it, c += CPI) {
-        // Values that are the same in every item pass through empty asm here, so that the addresses
-        // derived from them are formed where they are used instead of being hoisted out of the loop
-        // and held in registers through the score phase.
-        set_qrow();
-        long vofs = 0;                              // (an integer, so that the loads stay global ones)
-        asm volatile("" : "+s"(vofs));
-        const uint16_t* vsl_it = vsl + vofs;
-        int tid_it = tid;
-        asm volatile("" : "+v"(tid_it));
-        const int cb_blk = tid_it >> 4, g16 = tid_it & 15;
-        // ---- scores ----
-        gather(ik[0], std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, G[0]);
-        load_q(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, qs[0]);
-        uint32_t pidn[N][R];                        // page ids of the next item's chunks
-#pragma unroll
-        for (int i = 0; i < N; ++i) load_pid(c + CPI + 4 * i, pidn[i]);
-#pragma unroll
-        for (int j = 0; j < R; ++j) rmax[j] = -INFINITY;
-        StaticFor<0, N>::run([&](auto Ic) {
-            constexpr int I = decltype(Ic)::value, NB = N % 2 == 0 ? 2 : 3;
-            auto& cur = ik[I % NB];
-            auto& nxt = ik[(I + 1) % NB];           // (after the last slot: ik[0], the next item's first)
-            if constexpr (I + 1 < N) load_idx(c + 4 * (I + 1), 0, pidc[I + 1], nxt);
-            else load_idx(c + CPI, 0, pidn[0], nxt);
-            run_chunk(Ic, Nc, c + 4 * I, I + 1 < N ? c + 4 * (I + 1) : c + CPI, cur, nxt);
-        });
-        uint32_t iv[N][R][IW];                      // value index rows of the item's chunks
-#pragma unroll
-        for (int i = 0; i < N; ++i) load_idx(c + 4 * i, 1, pidc[i], iv[i]);
-        // (Stores in this loop come from all lanes of a wave, with the same value where they meet: a
-        // lane-divergent branch here costs the score phase its registers.)
-#pragma unroll
-        for (int j = 0; j < R; ++j) wmax[wave][j] = wave_max_dpp(rmax[j]);
-        __syncthreads();                            // wave maxima visible
-        float M[R];
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            M[j] = wmax[0][j];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) M[j] = fmaxf(M[j], wmax[w][j]);
-        }
-
-        // ---- weights: one atomic per (token, request, value group) ----
-        uint4 vrow[GPL * VPG];                      // V rows of this lane's contraction block (L2 hits)
-        StaticFor<0, N>::run([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            if constexpr (i == N - 1) {             // issued once the first chunks' index rows are dead
-#pragma unroll
-                for (int k = 0; k < GPL; ++k) {
-                    const uint4* src =
-                        reinterpret_cast<const uint4*>(vsl_it + (long(g16 + 16 * k) * K + CPB * cb_blk) * C);
-#pragma unroll
-                    for (int v = 0; v < VPG; ++v) vrow[k * VPG + v] = src[v];
-                }
-            }
-            const int tau = (c + 4 * i) * kChunk + lane;
-            // byte k of base2[v]: slot byte offset 4R * ((2v + k) ^ (tau & 15)) of the group held in V index
-            // byte 2v + k; byte 2: the bins' 64K page
-            const uint32_t rot = (uint32_t(tau) & 15u) * (4u * R) * 0x0101u;
-            uint32_t base2[NG / 2];
-#pragma unroll
-            for (int v = 0; v < NG / 2; ++v) base2[v] = (((4u * R) * (0x0100u + uint32_t(v) * 0x0202u)) ^ rot) | 0x10000u;
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const uint32_t u = in_req(j, tau)
-                                       ? uint32_t(fmaf(__builtin_amdgcn_exp2f(sreg[i][j] - M[j]), fix_scale, 0.5f))
-                                       : 0u;
-                StaticFor<0, NG>::run([&](auto mc) {
-                    constexpr int m = decltype(mc)::value;
-                    // bin byte address [slot offset, codeword, 0x01, 0]: row = codeword, 256 B per row
-                    constexpr uint32_t sel = 0x0c020000u | (uint32_t(4 + (m & 3)) << 8) | uint32_t(m & 1);
-                    const uint32_t addr = __builtin_amdgcn_perm(iv[i][j][m >> 2], base2[m >> 1], sel);
-                    uint32_t* bin = static_cast<uint32_t*>(__builtin_assume_aligned(lds + addr + 4 * j, 4));
-                    __hip_atomic_fetch_add(bin, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                });
-            }
-        });
-        __syncthreads();                            // bins complete
-
-        // ---- contraction: lane (cb_blk, g16) over codewords CPB*cb_blk .. +CPB-1 of its groups ----
-        float o[PL];
-#pragma unroll
-        for (int i = 0; i < PL; ++i) o[i] = 0.f;
-        uint32_t lsum[R];
-#pragma unroll
-        for (int j = 0; j < R; ++j) lsum[j] = 0u;
-#pragma unroll
-        for (int i = 0; i < CPB; ++i) {
-            const int r = CPB * cb_blk + i;
-#pragma unroll
-            for (int k = 0; k < GPL; ++k) {
-                uint32_t bv[R];
-                uint32_t* bp = bins + r * 64 + (g16 + 16 * k) * R;
-                if constexpr (R == 4) {
-                    const uint4 b4 = *reinterpret_cast<const uint4*>(bp);
-                    bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
-                    *reinterpret_cast<uint4*>(bp) = make_uint4(0u, 0u, 0u, 0u);
-                } else {
-                    const uint2 b2 = *reinterpret_cast<const uint2*>(bp);
-                    bv[0] = b2.x; bv[1] = b2.y;
-                    *reinterpret_cast<uint2*>(bp) = make_uint2(0u, 0u);
-                }
-                uint32_t vw[C / 2];                 // V row: C bf16 of codeword r, group g16 + 16k
-                if constexpr (C == 8) {
-                    vw[0] = vrow[i].x; vw[1] = vrow[i].y; vw[2] = vrow[i].z; vw[3] = vrow[i].w;
-                } else {
-                    const uint4 q = vrow[k * VPG + (i >> 1)];
-                    vw[0] = (i & 1) ? q.z : q.x;
-                    vw[1] = (i & 1) ? q.w : q.y;
-                }
-#pragma unroll
-                for (int j = 0; j < R; ++j) {
-                    if (k == 0) lsum[j] += bv[j];
-                    const float bw = float(bv[j]);
-#pragma unroll
-                    for (int u = 0; u < C / 2; ++u) {
-                        o[j * C * GPL + k * C + 2 * u] = fmaf(bw, bf16_lo(vw[u]), o[j * C * GPL + k * C + 2 * u]);
-                        o[j * C * GPL + k * C + 2 * u + 1] =
-                            fmaf(bw, bf16_hi(vw[u]), o[j * C * GPL + k * C + 2 * u + 1]);
-                    }
-                }
-            }
-        }
-        // sum over the wave's four codeword blocks; row 0 of the wave writes the wave's partials
-#pragma unroll
-        for (int i = 0; i < PL; ++i) o[i] = sum_rows4(o[i]);
-#pragma unroll
-        for (int j = 0; j < R; ++j) lsum[j] = sum_rows4(lsum[j]);
-        {   // the four rows of the wave hold the same sums: they write them to the same place
-            float4* dst = reinterpret_cast<float4*>(part + (wave * 16 + g16) * PL);
-#pragma unroll
-            for (int i = 0; i < PL / 4; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-#pragma unroll
-            for (int j = 0; j < R; ++j) lw[wave][j] = __builtin_amdgcn_readlane(lsum[j], 0);   // group 0's total
-        }
-        __syncthreads();                            // partials complete
-
-        // ---- merge the item into the running output element ----
-        if (wave < R * D / 64) {
-            const int gr = od / C, u = od % C;
-            const int p = oj * C * GPL + (gr >> 4) * C + u;
-            float U = 0.f;
-            uint64_t Ls = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                U += part[(w * 16 + (gr & 15)) * PL + p];
-                Ls += lw[w][oj];
-            }
-            float Mo = M[0];
-#pragma unroll
-            for (int j = 1; j < R; ++j) Mo = oj == j ? M[j] : Mo;
-            if (Ls > 0) {
-                const float e = Mo - float(a.fix_bits);     // the item's weights are 2^(s - e) in fixed point
-                const float mn = fmaxf(run_m, e);
-                const float sa = exp2f(run_m - mn), sb = exp2f(e - mn);
-                run_o = fmaf(run_o, sa, U * sb);
-                run_l = fmaf(run_l, sa, float(Ls) * sb);
-                run_m = mn;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-#pragma unroll
-            for (int j = 0; j < R; ++j) pidc[i][j] = pidn[i][j];
-      }
-    };
-    if constexpr (FCH == SCH) item_loop(std::integral_constant<int, FCH>{});
-    else if (fast) item_loop(std::integral_constant<int, FCH>{});
-    else item_loop(std::integral_constant<int, SCH>{});
-
-    // ---- the window rows, merged like an item ----
-    __syncthreads();                                // the last item's partials are read
-    if (wave < NWW) {
-        *reinterpret_cast<float4*>(part + wr * D + window_channel(c16, 0)) = make_float4(wo[0], wo[1], wo[2], wo[3]);
-        *reinterpret_cast<float4*>(part + wr * D + window_channel(c16, 4)) = make_float4(wo[4], wo[5], wo[6], wo[7]);
-        wml[wr][0] = wm;                            // (the row's 16 lanes hold the same m and l)
-        wml[wr][1] = wl;
-    }
-    __syncthreads();
-    if (wave < R * D / 64) {
-        float mw = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < RPJ; ++r) mw = fmaxf(mw, wml[oj * RPJ + r][0]);
-        if (mw != -INFINITY) {
-            float lw_ = 0.f, ow = 0.f;
-#pragma unroll
-            for (int r = 0; r < RPJ; ++r) {
-                const float f = exp2f(wml[oj * RPJ + r][0] - mw);   // 0 for a row without tokens
-                lw_ = fmaf(wml[oj * RPJ + r][1], f, lw_);
-                ow = fmaf(part[(oj * RPJ + r) * D + od], f, ow);
-            }
-            const float mn = fmaxf(run_m, mw);
-            const float sa = exp2f(run_m - mn), sb = exp2f(mw - mn);
-            run_o = fmaf(run_o, sa, ow * sb);
-            run_l = fmaf(run_l, sa, lw_ * sb);
-            run_m = mn;
-        }
-    }
-
-    // ---- output: a request holds at least one token, so run_l > 0 ----
-    const int orb = group_request(a, r0 + min(oj, R - 1));
-    if (tid < R * D && orb < a.B) {
-        const long row = long(orb) * g.H + h;
-        out[row * D + od] = run_o / run_l;
-        if (lse_out && od == 0) lse_out[row] = (run_m + log2f(run_l)) * kLn2;
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Exact merge of S partials per row.
 // ---------------------------------------------------------------------------
 __global__ void merge_kernel(const float* __restrict__ po, const float* __restrict__ pl, int S, int D,
@@ -1658,7 +1599,7 @@ int choose_splits(const Geo& g, int B, int max_len) {
     // Enough (split, head, request group) workgroups for 256 CUs x 2, splits of >= 16 pages.
     const int pairs = ceil_div(B, reqs_per_wg(g)) * g.H;
     s = std::max(s, std::min(ceil_div(512, std::max(1, pairs)), ceil_div(max_pages, 16)));
-    return std::max(1, std::min(s, 1024));
+    return std::max(1, std::min(s, kMaxSplits));
 }
 
 // Pages per split: a multiple of 8 (64 tokens), so that score chunks never straddle splits.
@@ -1692,8 +1633,7 @@ using namespace lvq;
 
 extern "C" size_t lvq_decode_attn_workspace(const lvq_geom* gp, int32_t B, int32_t max_len, int32_t num_splits) {
     Geo g;
-    if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 0 || num_splits < -1) return 0;
-    if (num_splits == -1) return quant_scratch_bytes(g, B);   // the single-pass kernel
+    if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 0 || num_splits < 0) return 0;
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
     return partials_bytes(g, B, S + 1) + quant_scratch_bytes(g, B);
 }
@@ -1747,8 +1687,8 @@ lvq_status launch_quant(AttnArgs& a, void* scratch, hipStream_t stream) {
         const int R = reqs_per_wg(g);
         const dim3 grid(g.H, a.num_splits, ceil_div(a.B, R));
         if (g.c == 8) {
-            if (a.kscale) hipLaunchKernelGGL((index_attn_kernel<8, 4, true>), grid, dim3(kIThreads), 0, stream, a);
-            else hipLaunchKernelGGL((index_attn_kernel<8, 4, false>), grid, dim3(kIThreads), 0, stream, a);
+            if (a.kscale) hipLaunchKernelGGL((index_mfma_kernel<true>), grid, dim3(kIThreads), 0, stream, a);
+            else hipLaunchKernelGGL((index_mfma_kernel<false>), grid, dim3(kIThreads), 0, stream, a);
         } else {
             if (a.kscale) hipLaunchKernelGGL((index_attn_kernel<4, 2, true>), grid, dim3(kIThreads), 0, stream, a);
             else hipLaunchKernelGGL((index_attn_kernel<4, 2, false>), grid, dim3(kIThreads), 0, stream, a);
@@ -1762,26 +1702,6 @@ lvq_status launch_quant(AttnArgs& a, void* scratch, hipStream_t stream) {
             hipLaunchKernelGGL((quant_partial_kernel<4, float, false>), grid, dim3(256), red_bytes, stream, a);
     }
     return check_launch("quantized partial");
-}
-
-// Whether the library's choice for lvq_decode_attn is the single-pass kernel.  (Not yet: it runs no faster
-// than the split path on the shapes measured so far, so num_splits = 0 keeps the split path.)
-bool use_full(const Geo& g, int B, int max_pages) {
-    (void)g, (void)B, (void)max_pages;
-    return false;
-}
-
-// The single-pass kernel; `scratch` (256-byte aligned) holds the packed query rows.
-lvq_status launch_full(AttnArgs& a, void* scratch, float* out, float* lse_out, hipStream_t stream) {
-    const Geo& g = a.geo;
-    a.qpack = static_cast<const uint32_t*>(scratch);
-    a.fix_bits = 32 - ceil_log2(long(kItemTok) + 1);
-    const dim3 grid(g.H, ceil_div(a.B, reqs_per_wg(g)));
-    if (g.c == 8)
-        hipLaunchKernelGGL((index_full_kernel<8, 4>), grid, dim3(kFThreads), 0, stream, a, out, lse_out);
-    else
-        hipLaunchKernelGGL((index_full_kernel<4, 2>), grid, dim3(kFThreads), 0, stream, a, out, lse_out);
-    return check_launch("single-pass attention");
 }
 
 // The window partial into slot a.num_splits, or (out != NULL) merged with slots 0 .. a.num_splits-1 into
@@ -1822,7 +1742,7 @@ extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const 
     a.order = order;
     a.kscale = static_cast<const uint16_t*>(k_scales);
     const Geo& g = a.geo;
-    LVQ_REQUIRE(num_splits >= 1 && num_splits <= 1024 && S_tot >= num_splits, LVQ_ERR_INVALID_ARG,
+    LVQ_REQUIRE(num_splits >= 1 && num_splits <= kMaxSplits && S_tot >= num_splits, LVQ_ERR_INVALID_ARG,
                 "lvq_quant_partial: num_splits %d, S_tot %d", num_splits, S_tot);
     if (B == 0) return LVQ_OK;
     const int max_pages = max_index_pages(g, max_len);
@@ -1886,20 +1806,19 @@ lvq_status decode_attn_impl(const char* fn, const lvq_geom* gp, int32_t step, co
     a.order = order;
     a.kscale = static_cast<const uint16_t*>(k_scales);
     const Geo& g = a.geo;
-    LVQ_REQUIRE(num_splits >= -1 && num_splits <= 1024, LVQ_ERR_INVALID_ARG, "%s: num_splits %d", fn, num_splits);
-    LVQ_REQUIRE(num_splits != -1 || !k_scales, LVQ_ERR_UNSUPPORTED,
-                "%s: the single-pass kernel (num_splits -1) takes no key scale stream", fn);
-    LVQ_REQUIRE(num_splits != -1 || g.cb == LVQ_BF16, LVQ_ERR_UNSUPPORTED,
-                "%s: the single-pass kernel (num_splits -1) needs bf16 codebooks", fn);
+    LVQ_REQUIRE(num_splits >= 0 && num_splits <= kMaxSplits, LVQ_ERR_INVALID_ARG, "%s: num_splits %d", fn,
+                num_splits);
     LVQ_REQUIRE(pt_stride >= 0, LVQ_ERR_INVALID_ARG, "%s: negative pt_stride", fn);
     if (B == 0) return LVQ_OK;
     LVQ_REQUIRE(win_k && win_v && slices && out, LVQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     const int max_pages = max_index_pages(g, max_len);
     LVQ_REQUIRE(max_pages == 0 || (pool && page_table), LVQ_ERR_INVALID_ARG, "%s: NULL pool or page table", fn);
     LVQ_REQUIRE(pt_stride >= max_pages, LVQ_ERR_INVALID_ARG, "%s: pt_stride %d < %d pages", fn, pt_stride, max_pages);
-    const bool single = num_splits == -1 || (num_splits == 0 && !k_scales && use_full(g, B, max_pages));
+    LVQ_REQUIRE(g.cb != LVQ_BF16 || max_pages <= kMaxSplits * (kMaxSplitTok / g.page), LVQ_ERR_UNSUPPORTED,
+                "%s: a context of %d index pages exceeds the %d (%d splits of %d pages) the bf16 kernels take", fn,
+                max_pages, kMaxSplits * (kMaxSplitTok / g.page), kMaxSplits, kMaxSplitTok / g.page);
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
-    LVQ_REQUIRE(single || splits_fit(g, max_pages, S), LVQ_ERR_INVALID_ARG,
+    LVQ_REQUIRE(splits_fit(g, max_pages, S), LVQ_ERR_INVALID_ARG,
                 "%s: %d splits of %d index pages exceed %d tokens per split", fn, S, max_pages, kMaxSplitTok);
     const size_t need = lvq_decode_attn_workspace(gp, B, max_len, num_splits);
     if (provider && (st = provider(need, &ws, &ws_bytes)) != LVQ_OK) return st;
@@ -1914,7 +1833,6 @@ lvq_status decode_attn_impl(const char* fn, const lvq_geom* gp, int32_t step, co
     a.wk = static_cast<const uint16_t*>(win_k);
     a.wv = static_cast<const uint16_t*>(win_v);
     set_slices(&a, slices);
-    if (single) return launch_full(a, ws, out, lse_out, stream);
     const size_t rows = size_t(B) * g.H * (S + 1);
     a.part_o = static_cast<float*>(ws);
     a.part_lse = a.part_o + rows * g.D;
@@ -1944,7 +1862,6 @@ extern "C" lvq_status lvq_decode_attn(const lvq_geom* gp, int32_t step, const vo
 extern "C" int32_t lvq_decode_attn_splits(const lvq_geom* gp, int32_t B, int32_t max_len) {
     Geo g;
     if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 1) return 0;
-    if (use_full(g, B, max_index_pages(g, max_len))) return -1;
     return choose_splits(g, B, max_len);
 }
 

@@ -97,6 +97,23 @@ struct Geo {
 // Validate a caller's geometry; fills `out` on success.
 lvq_status validate_geom(const lvq_geom* g, Geo* out);
 
+// Byte position of group g in the index row of index-token tau (counted from the first paged position);
+// layout in lvq.h.  Value rows: g ^ (tau & 15).  Key rows with 16 groups: the byte j with
+// P(j) ^ (tau & 15) = g, P the fixed bit permutation (j3 j2 j1 j0) -> (j1 j3 j2 j0), so that the dword k of a
+// key row holds groups {2k, 2k+1, 2k+8, 2k+9} ^ (tau & 15): two RoPE-paired group pairs.  Key rows with 32
+// groups: g.
+__host__ __device__ inline int index_byte(int kv, int NG, int g, int tau) {
+    if (kv != 0) return g ^ (tau & 15);
+    if (NG != 16) return g;
+    const int b = g ^ (tau & 15);
+    return (b & 1) | (((b >> 3) & 1) << 1) | (((b >> 1) & 1) << 2) | (((b >> 2) & 1) << 3);
+}
+// The group held by byte j of a key row with 16 groups (the inverse of index_byte for kv = 0).
+__host__ __device__ inline int key_group_of_byte(int j, int tau) {
+    const int p = (j & 1) | (((j >> 2) & 1) << 1) | (((j >> 3) & 1) << 2) | (((j >> 1) & 1) << 3);
+    return p ^ (tau & 15);
+}
+
 // Supplies the workspace of a decode-attention call once its arguments are valid: given the bytes the call
 // needs, sets *ws and *ws_bytes or returns an error.
 using WorkspaceProvider = lvq_status (*)(size_t need, void** ws, size_t* ws_bytes);

@@ -51,8 +51,10 @@ __global__ void rope_table_kernel(int len, int D, double base, float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Packed fp16 table for the index-page pass: chunk m (frequencies 4m..4m+3)
-// of position p at out[(m * len + p) * 8 ..]: cos x4 then sin x4.
+// Packed fp16 table for the index-page pass (layout rope_f16 in lvq.h): 32
+// chunks of 8 halves per position p; chunk m < 16 (frequencies 4m..4m+3) at
+// out[(p * 32 + m) * 8 ..] holds cos x4 then sin x4, chunk 16 + m the same
+// with the sines negated.
 // ---------------------------------------------------------------------------
 // fp64 -> binary16 with one rounding (nearest even): round to fp32 with
 // round-to-odd first (fp32 keeps more than two extra bits), then RNE.
@@ -73,9 +75,12 @@ __global__ void rope_f16_kernel(int len, double base, _Float16* __restrict__ out
         const double theta = pow(base, -2.0 * double(i) / 128.0);
         const double ang = double(p) * theta;
         const int m = i >> 2, k = i & 3;
-        _Float16* o = out + (long(m) * len + p) * 8;
-        o[k] = f64_to_f16_rn(cos(ang));
-        o[4 + k] = f64_to_f16_rn(sin(ang));
+        _Float16* o = out + (long(p) * 32 + m) * 8;
+        const _Float16 c = f64_to_f16_rn(cos(ang)), sn = f64_to_f16_rn(sin(ang));
+        o[k] = c;
+        o[4 + k] = sn;
+        o[16 * 8 + k] = c;
+        o[16 * 8 + 4 + k] = -sn;
     }
 }
 
@@ -140,9 +145,9 @@ __global__ void encode_scan_kernel(Geo geo, int block, const uint16_t* __restric
             best_r = r;
         }
     }
-    // Value rows are XOR-rotated by the index-token number (layout in lvq.h).
+    // Index rows are permuted by the index-token number (layout in lvq.h).
     const int tau = slot_token(lp, i_tok, geo.page);
-    const int byte = kv == 0 ? g : (g ^ (tau & 15));
+    const int byte = index_byte(kv, NG, g, tau);
     pool[phys * geo.page_bytes + ((long(block) * geo.H + h) * 2 + kv) * geo.page * NG + i_tok * NG + byte] =
         uint8_t(best_r);
 }
@@ -384,7 +389,17 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
         const long phys = a.pt[long(bj) * a.pt_stride + lp];
         const int tau = lp * g.page + ri;
         uint8_t* row = a.pool + phys * g.page_bytes + blk_off + ri * g.NG;
-        if (kv == 0) {
+        if (kv == 0 && g.NG == 16) {
+            // key rows of 16 groups (layout in lvq.h): the octet's groups 8*oct + u sit in the bytes j with
+            // bit 1 of j equal to oct ^ bit 3 of tau, two adjacent bytes at a time
+            const int hb = (oct ^ (tau >> 3)) & 1;
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+                const int j = 4 * pr + 2 * hb;
+                const int u0 = key_group_of_byte(j, tau) - 8 * oct, u1 = key_group_of_byte(j + 1, tau) - 8 * oct;
+                *reinterpret_cast<uint16_t*>(row + j) = uint16_t(idx[tid][u0] | (uint32_t(idx[tid][u1]) << 8));
+            }
+        } else if (kv == 0) {
             *reinterpret_cast<uint2*>(row + 8 * oct) = *reinterpret_cast<const uint2*>(idx[tid]);
         } else {
             // group 8*oct + u goes to byte (8*oct + u) ^ (tau & 15)
@@ -712,7 +727,7 @@ __global__ void __launch_bounds__(kKmThreads) kmeans_update_kernel(
                 float z[32];
                 load_coupled<VEC_C>(x + long(b) * s0 + long(h) * s1 + row * s2 + g * c, s3, Tc, G, z);
                 const int tau = slot_token(lp, i_tok, geo.page);
-                const int byte = kv == 0 ? g : (g ^ (tau & 15));     // value rows XOR-rotated (lvq.h)
+                const int byte = index_byte(kv, NG, g, tau);         // index rows permuted (lvq.h)
                 const int r = pool[phys * geo.page_bytes + blk_off + i_tok * NG + byte];
                 unsigned long long* acc = sums + r * (G + 1);
                 const double wz = double(w) * scale_z;                // exact: a power-of-two scale

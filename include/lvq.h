@@ -90,12 +90,18 @@ LVQ_API const char* lvq_last_error(void);
  *  slices     [T][H][2][NG][K][c]   slice[t][h][kv][g][r][i] =
  *             codebooks[t/Tc][h][kv][g][r][i*Tc + t%Tc]       cb_dtype
  *  pool       [P][NB][H][2][page][NG] uint8 index pages; one physical page
- *             holds 8 tokens of one request for every block and head.  Key
- *             rows are in group order; a value row of index-token tau
- *             (counted from the first paged position) is XOR-rotated: byte m
- *             holds the index of group m ^ (tau & 15).  Attention bins value
- *             weights per (group, codeword) and the rotation lets the lanes
- *             of one LDS phase update 16 distinct groups.
+ *             holds 8 tokens of one request for every block and head.  Rows
+ *             are permuted by the index-token number tau (counted from the
+ *             first paged position), t = tau & 15:
+ *             - a value row is XOR-rotated: byte m holds group m ^ t;
+ *             - a key row of 16 groups (c = 8): byte j holds group P(j) ^ t,
+ *               P the bit permutation (j3 j2 j1 j0) -> (j1 j3 j2 j0), so
+ *               dword k holds groups {2k, 2k+1, 2k+8, 2k+9} ^ t: two pairs of
+ *               RoPE-partner groups (channels i and i + 64);
+ *             - a key row of 32 groups (c = 4) is in group order.
+ *             The permutations let the 16 lanes of one LDS phase of the
+ *             attention kernels read or update 16 distinct groups (hence
+ *             16 distinct banks) while each lane keeps whole index dwords.
  *  page_table [B][pt_stride] int32, logical page -> physical page; attention
  *             reads only the entries of a request's own index pages, which
  *             must name pages of the pool (other entries may hold anything)
@@ -103,9 +109,10 @@ LVQ_API const char* lvq_last_error(void);
  *             K (and separately V) of every loop step; position p < sink sits
  *             in slot p, position p >= sink in slot sink + (p - sink) % (W + page)
  *  rope       cos, sin fp32 [rope_len][D/2]: cos/sin(p * base^(-2i/D))
- *  rope_f16   packed fp16 copy for the index-page kernel (D = 128):
- *             [16 chunks][rope_len][8 halves]; chunk m of position p holds
- *             cos of frequencies 4m..4m+3, then sin of the same four
+ *  rope_f16   packed fp16 copy for the index-page kernels (D = 128):
+ *             [rope_len][32 chunks][8 halves]; chunk m < 16 of position p
+ *             holds cos of frequencies 4m..4m+3, then sin of the same four;
+ *             chunk 16 + m the same with the sines negated
  */
 typedef struct {
     int32_t D, T, Tc, G, K, page, sink, window, H, cb_dtype;
@@ -203,8 +210,8 @@ LVQ_API lvq_status lvq_codebook_update(const lvq_geom* g, int32_t block, const v
 
 /*
  * Bytes of workspace lvq_decode_attn needs for B requests of length at most
- * max_len with the given split count (0 = the library's choice, -1 = the
- * single-pass kernel).
+ * max_len with the given split count (0 = the library's choice); 0 for
+ * invalid arguments.
  */
 LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t max_len, int32_t num_splits);
 
@@ -221,10 +228,8 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  * c = 4), sharing the codebook slice and the RoPE table loads, then turns the
  * scores into softmax weights and accumulates them per (group, codeword) of
  * the value indices; a split then holds at most 1536 index tokens (192
- * pages).  With bf16 codebooks the call can instead run as one kernel: one
- * workgroup per (head, group of four requests, two when c = 4) takes all of
- * its requests' index pages in turns of 1536 tokens and the window, and
- * merges them into the output itself (num_splits -1).
+ * pages), so a request holds at most 1024 * 192 index pages (longer
+ * contexts: LVQ_ERR_UNSUPPORTED).
  *
  *  q          bf16 [B][H][D], already rotated at position seq_len[b] - 1.
  *  seq_len    device int32 [B], 1 <= seq_len[b] <= max_len <= rope_len.
@@ -243,8 +248,7 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  *             token and loop step, shared by the heads).  Index token i of
  *             physical page p is scored with its reconstructed key times
  *             k_scales[(p*T + step)*8 + i]; bf16 window tokens are not scaled.
- *             One page of scales per pool page.  Not taken by the single-pass
- *             kernel (num_splits -1: LVQ_ERR_UNSUPPORTED).  The transform that
+ *             One page of scales per pool page.  The transform that
  *             produces the scales is not part of this library: lvq_encode
  *             takes keys already divided by their scale.
  *  slices     slices of ALL steps (layout above); the call reads step `step`.
@@ -259,8 +263,7 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  *  ws         device workspace of at least lvq_decode_attn_workspace() bytes,
  *             256-byte aligned (LVQ_ERR_INVALID_ARG otherwise); contents
  *             need no initialisation and are scratch after the call.
- *  num_splits 0 lets the library choose; -1 asks for the single-pass kernel
- *             (bf16 codebooks only, LVQ_ERR_UNSUPPORTED otherwise); otherwise
+ *  num_splits 0 lets the library choose; otherwise
  *             1..1024, and with bf16 codebooks large enough that a split
  *             holds at most 192 index pages:
  *             ceil(ceil(max_pages / num_splits) / 8) * 8 <= 192,
@@ -312,8 +315,7 @@ LVQ_API lvq_status lvq_window_append(const lvq_geom* g, int32_t step, const void
                                      void* win_k, void* win_v, const int32_t* seq_len, int32_t max_len,
                                      int32_t B, hipStream_t stream);
 
-/* What lvq_decode_attn runs for num_splits = 0: -1 for the single-pass kernel, else its split count
- * (0 on bad arguments). */
+/* The split count lvq_decode_attn runs for num_splits = 0 (0 on bad arguments). */
 LVQ_API int32_t lvq_decode_attn_splits(const lvq_geom* g, int32_t B, int32_t max_len);
 
 /*

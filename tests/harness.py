@@ -106,12 +106,23 @@ def gpu_indices(p: LoopVQProblem, b: int, h: int, kind: str) -> np.ndarray:
     sel = sel[:, :, h, kv]                                                                   # [n][NB][8][NG]
     NB, NG = sel.shape[1], sel.shape[3]
     rows = sel.permute(1, 0, 2, 3).reshape(NB, n * g.page, NG).cpu().numpy()
+    tau = np.arange(n * g.page)[:, None]
+    grp = np.arange(NG)[None, :]
+    return rows[:, tau, index_byte(kind, NG, grp, tau)]
+
+
+def index_byte(kind: str, NG: int, grp, tau):
+    """Byte position of group `grp` in the index row of index-token `tau` (the pool layout of lvq.h): value
+    rows are XOR-rotated, byte grp ^ (tau & 15); key rows of 16 groups hold group P(j) ^ (tau & 15) in byte j,
+    P the bit permutation (j3 j2 j1 j0) -> (j1 j3 j2 j0); key rows of 32 groups are in group order."""
+    grp = np.asarray(grp)
+    tau = np.asarray(tau)
     if kind == "v":
-        # value rows are XOR-rotated by the index-token number: byte m holds group m ^ (tau & 15)
-        tau = np.arange(n * g.page)[:, None]
-        m = np.arange(NG)[None, :]
-        rows = rows[:, tau, m ^ (tau & 15)]
-    return rows
+        return grp ^ (tau & 15)
+    if NG != 16:
+        return grp + 0 * tau
+    b = grp ^ (tau & 15)
+    return (b & 1) | (((b >> 3) & 1) << 1) | (((b >> 1) & 1) << 2) | (((b >> 2) & 1) << 3)
 
 
 def host_codebooks(p: LoopVQProblem, h: int, kind: str) -> np.ndarray:

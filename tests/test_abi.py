@@ -64,8 +64,7 @@ def _attn(g, **over):
     (dict(rope16=None), INVALID),              # bf16 codebooks need the packed fp16 RoPE table
     (dict(max_len=2048, splits=1), INVALID),   # 247 index pages in one split: over 1536 tokens per split
     (dict(ws=C.c_void_p(4096 + 16)), INVALID),  # workspace not 256-byte aligned
-    (dict(splits=-1, ws=C.c_void_p(4096 + 16)), INVALID),
-    (dict(splits=-1, ws_bytes=4 * 2 * 256 - 1), WORKSPACE),   # single pass: the packed query rows only
+    (dict(splits=-1), INVALID),                # no single-pass kernel
 ])
 def test_decode_attn_rejects(over, status):
     assert _attn(_geom(), **over) == status
@@ -99,10 +98,7 @@ def test_workspace_query():
     assert _attn(g32, rope16=None, B=0) == OK
     assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 0) > 0
     assert _lib.lib.lvq_decode_attn_workspace(None, 64, 6144, 0) == 0
-    # the single-pass kernel needs the packed query rows only, and bf16 codebooks
-    assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, -1) == scratch
-    assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, -2) == 0
-    assert _attn(g32, rope16=None, splits=-1) == UNSUPPORTED
+    assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, -1) == 0
 
 
 def test_encode_rejects():
@@ -217,10 +213,14 @@ def test_codebook_update_rejects():
     assert call(maxp=0) == OK
 
 
-def test_key_scales_rejected_by_single_pass():
-    """A key scale stream with the single-pass kernel (num_splits -1) is refused before any launch."""
+def test_context_beyond_the_split_limit_is_unsupported():
+    """bf16 codebooks take at most 1024 splits of 192 index pages: a longer context is refused as unsupported,
+    naming the context, whatever the split count asked for."""
     g = _geom()
-    assert _attn(g, kscale=FAKE, splits=-1) == UNSUPPORTED
+    max_len = 8 + 64 + 8 * 1024 * 192 + 8
+    for splits in (0, 1024):
+        assert _attn(g, max_len=max_len, rope_len=max_len, pt_stride=1 << 20, splits=splits) == UNSUPPORTED
+        assert "index pages" in _lib.lib.lvq_last_error().decode()
 
 
 def test_noalloc_rejects_before_touching_the_device():

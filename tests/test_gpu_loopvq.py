@@ -104,15 +104,19 @@ def test_rope_table_matches_fp64():
 
 
 def test_rope_table_f16_layout_and_rounding():
-    """Packed fp16 table: chunk m of position p holds cos then sin of
-    frequencies 4m..4m+3, each the fp64 value rounded once to binary16."""
+    """Packed fp16 table: chunk m < 16 of position p holds cos then sin of frequencies 4m..4m+3, chunk 16 + m
+    the same with the sines negated, each the fp64 value rounded once to binary16."""
     import decode_attention_loopvq_amd as lvq
     n = 9000
-    t = lvq.lvq_rope_table_f16(n, 128, 10000.0).cpu().numpy()          # [16][n][8] fp16
+    t = lvq.lvq_rope_table_f16(n, 128, 10000.0).cpu().numpy()          # [n][32][8] fp16
     phi = lv.rope_angles(np.arange(n), 128, 10000.0)                  # [n][64]
     for m in range(16):
-        np.testing.assert_array_equal(t[m, :, :4], np.cos(phi[:, 4 * m:4 * m + 4]).astype(np.float16))
-        np.testing.assert_array_equal(t[m, :, 4:], np.sin(phi[:, 4 * m:4 * m + 4]).astype(np.float16))
+        c16 = np.cos(phi[:, 4 * m:4 * m + 4]).astype(np.float16)
+        s16 = np.sin(phi[:, 4 * m:4 * m + 4]).astype(np.float16)
+        np.testing.assert_array_equal(t[:, m, :4], c16)
+        np.testing.assert_array_equal(t[:, m, 4:], s16)
+        np.testing.assert_array_equal(t[:, 16 + m, :4], c16)
+        np.testing.assert_array_equal(t[:, 16 + m, 4:], -s16)
 
 
 @pytest.mark.parametrize("cb", ["bf16", "fp32"])
@@ -147,8 +151,7 @@ SMALL = [
 def test_decode_parity_small(cfg):
     rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
     steps = list(range(cfg.T)) if cfg.T <= 4 else [0, 3, 4, 17, 31]
-    single = (-1,) if cfg.cb_dtype == "bf16" else ()
-    _run_parity(cfg, rows, steps, splits=(0, 1, 3) + single)
+    _run_parity(cfg, rows, steps, splits=(0, 1, 3))
 
 
 @pytest.mark.parametrize("T,Tc,G", [(4, 1, 4), (6, 3, 24)], ids=["tc1-g4", "tc3-g24"])
@@ -174,7 +177,7 @@ def test_decode_edge_lengths(monkeypatch):
         rows = [(b, 0) for b in range(8)]
         p = harness.build_loopvq(cfg, keep=rows)
         idx = {(b, 0): _check_indices(p, b, 0, geo) for b in range(8)}
-        for ns in (0, 1, 2, 7, 50, -1):
+        for ns in (0, 1, 2, 7, 50):
             for t in range(cfg.T):
                 lse = torch.empty((8, 1), dtype=torch.float32, device="cuda")
                 out, _ = harness.run_step(p, t, num_splits=ns, lse=lse)
@@ -183,14 +186,13 @@ def test_decode_edge_lengths(monkeypatch):
                     _check_row(p, t, b, h, geo, idx[(b, h)], out, lse)
 
 
-def test_single_pass_items():
-    """The single-pass kernel over several items of 1536 index tokens: ragged lengths (requests of one
-    workgroup ending in different items, one with no index page), random page order, a batch that leaves the
-    last workgroup's request group short."""
-    # lengths 3845, 220, 1997, 57, 1548, 143: three items, one, two, no index page; the second group short
+def test_ragged_splits_and_pages():
+    """Ragged lengths (requests of one workgroup ending in different splits, one with no index page), random
+    page order, a batch that leaves the last workgroup's request group short; split counts 0, 3 and 5."""
+    # lengths 3845, 220, 1997, 57, 1548, 143
     cfg = loopvq_config("loopvq-b64-6k", B=6, H=2, L=4000, ragged=(40, 4000), random_pages=True, seed=12)
     rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
-    _run_parity(cfg, rows, steps=range(cfg.T), splits=(-1, 3))
+    _run_parity(cfg, rows, steps=range(cfg.T), splits=(0, 3, 5))
 
 
 def test_encode_decode_page():
@@ -281,7 +283,7 @@ def test_full_b64_6k_sampled():
     configuration, checked on sampled rows."""
     cfg = loopvq_config("loopvq-b64-6k")
     rows = [(0, 0), (37, 9), (63, 15)]
-    _run_parity(cfg, rows, steps=range(cfg.T), splits=(0, -1))
+    _run_parity(cfg, rows, steps=range(cfg.T), splits=(0,))
 
 
 def test_full_b1_1k():
@@ -307,13 +309,13 @@ def test_request_order_sorts_by_length():
 
 
 @pytest.mark.parametrize("name,over,splits", [
-    ("loopvq-b64-6k", dict(B=9, H=2, L=3000, ragged=(40, 3000), random_pages=True, seed=31), (0, 3, -1)),
-    ("loopvq-deep-ragged", dict(B=7, H=2, L=900, ragged=(1, 900)), (0, 2, -1)),
+    ("loopvq-b64-6k", dict(B=9, H=2, L=3000, ragged=(40, 3000), random_pages=True, seed=31), (0, 3)),
+    ("loopvq-deep-ragged", dict(B=7, H=2, L=900, ragged=(1, 900)), (0, 2)),
     ("loopvq-b1-1k-fp32cb", dict(B=5, H=2, L=1024, ragged=(30, 1024)), (0, 2)),
 ], ids=["bf16-c8", "bf16-c4", "fp32"])
 def test_order_does_not_change_the_output(name, over, splits):
     """The grouping of requests into workgroups changes no bit of the output: no order, the length order and
-    a random permutation (every path: the split kernels for bf16 and fp32 codebooks, the single pass)."""
+    a random permutation (every path: the split kernels for bf16 codebooks with c = 8 and c = 4, and fp32)."""
     import decode_attention_loopvq_amd as lvq
     from tests import harness
     cfg = loopvq_config(name, **over)
