@@ -63,6 +63,20 @@ __device__ __forceinline__ int group_request(const AttnArgs& a, int i) {
     const int r = a.order[i];
     return r >= 0 && r < a.B ? r : a.B;
 }
+// group_request for the R consecutive slots from i0, with the order entries read together (one uniform branch).
+template <int R>
+__device__ __forceinline__ void group_requests(const AttnArgs& a, int i0, int (&rq)[R]) {
+    int r[R];
+    if (a.order) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) r[j] = a.order[min(i0 + j, a.B - 1)];
+    } else {
+#pragma unroll
+        for (int j = 0; j < R; ++j) r[j] = i0 + j;
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) rq[j] = i0 + j < a.B && r[j] >= 0 && r[j] < a.B ? r[j] : a.B;
+}
 
 __device__ __forceinline__ int n_index_pages(int L, const Geo& g) {
     const int r = L - g.sink - g.W;
@@ -405,7 +419,8 @@ __device__ __forceinline__ bool split_ranges(const AttnArgs& a, int split, const
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int rb = rq[j];
-        const int np8 = rb < a.B ? n_index_pages(clamp_len(a, rb), g) * g.page : 0;
+        const int L = clamp_len(a, min(rb, a.B - 1));   // read for every slot, so that the loads issue together
+        const int np8 = rb < a.B ? n_index_pages(L, g) * g.page : 0;
         lo[j] = min(np8, split * split_tok);
         hi[j] = min(np8, (split + 1) * split_tok);
         any |= hi[j] > lo[j];
@@ -949,7 +964,12 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     constexpr int PL = R * C;                       // partial sums per contraction lane
     __shared__ __align__(16) unsigned char lds[K * 256];
     __shared__ float wmax[NW][R];
-    __shared__ uint32_t pid_lds[R][kMaxSplitTok / 8];  // page ids of the split's pages, per request
+    __shared__ __align__(16) float cpart[NW][64][2 * R];   // contraction partials per wave (lane, channel pair)
+    __shared__ uint32_t lpart[NW][R];                      // weight totals per wave
+    // Page ids of the split's pages, grouped by page pair (one 16-token block): entry (P, h, j) holds request
+    // j's page 2 P + (h ^ (j >> 1)), so that lane (n, kb), whose row of request j holds token n ^ 4 j (page
+    // half (n >> 3) ^ (j >> 1)), finds its four page ids of a block in one 16-byte read at (P, n >> 3).
+    __shared__ __align__(16) uint32_t pid_lds[kMaxSplitTok / 16][2][R];
     uint32_t* bins = reinterpret_cast<uint32_t*>(lds);
     const Geo& g = a.geo;
     const int h = blockIdx.x, split = blockIdx.y, r0 = blockIdx.z * R;
@@ -957,9 +977,79 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, kb = lane >> 4;
     int rq[R];
+    group_requests<R>(a, r0, rq);
+    // index-token ranges of the requests in this split (8-token pages; every length read, without branches,
+    // so that the loads issue together)
+    int lo[R], hi[R];
+    bool any = false;
+    {
+        int len[R];
 #pragma unroll
-    for (int j = 0; j < R; ++j) rq[j] = group_request(a, r0 + j);
-
+        for (int j = 0; j < R; ++j) len[j] = a.seq_len[min(rq[j], a.B - 1)];
+        const int split_tok = a.pps * 8;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int L = min(max(len[j], 0), a.max_len);
+            const int np8 = rq[j] < a.B ? max(L - g.sink - g.W, 0) & ~7 : 0;
+            lo[j] = min(np8, split * split_tok);
+            hi[j] = min(np8, (split + 1) * split_tok);
+            any |= hi[j] > lo[j];
+        }
+    }
+    if (!any) {
+        for (int e = tid; e < R * D; e += NT) {
+            const int j = e / D, d = e % D, rb = rq[j];
+            if (rb >= a.B) continue;
+            const long row = (long(rb) * g.H + h) * a.S_tot + split;
+            a.part_o[row * D + d] = 0.f;
+            if (d == 0) a.part_lse[row] = -INFINITY;
+        }
+        return;
+    }
+    int t_lo = 0x7fffffff, t_hi = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (hi[j] > lo[j]) {
+            t_lo = min(t_lo, lo[j]);
+            t_hi = max(t_hi, hi[j]);
+        }
+    }
+    // Setup loads, in the order they are needed (the vector loads complete in order): the split's page-table
+    // entries (page ids, per request: a page past a request's range holds its last index page, a request
+    // without index pages physical page 0, so that every load below reads valid memory), the query rows, then
+    // the step's K slice of head h.
+    constexpr int kPt = R * (kMaxSplitTok / 8) / NT;   // page-table entries per thread
+    static_assert(R * (kMaxSplitTok / 8) % NT == 0, "page-table fill");
+    uint32_t ptv[kPt];
+#pragma unroll
+    for (int i = 0; i < kPt; ++i) {
+        // one unconditional load from the table's base (page 0 of its row when the request has no index
+        // pages: in bounds, as some request of the workgroup has index pages, so rows hold >= 1 entry)
+        const int e = tid + NT * i;
+        const int j = e / (kMaxSplitTok / 8), pp = e % (kMaxSplitTok / 8);
+        int row = min(rq[0], a.B - 1), hij = hi[0];
+#pragma unroll
+        for (int jj = 1; jj < R; ++jj)
+            if (j == jj) { row = min(rq[jj], a.B - 1); hij = hi[jj]; }
+        const int page = hij > 0 ? max(min(t_lo + 8 * pp, hij - 1), 0) >> 3 : 0;
+        const uint32_t v = uint32_t(a.pt[long(row) * a.pt_stride + page]);
+        ptv[i] = hij > 0 ? v : 0u;
+    }
+    // The lane's query: blocks f1 = ((2 kb) ^ n) & 7 and f2 = f1 ^ 1 of 8 frequencies, qa = the half of
+    // slot 0's group, qb the partner half (raw bf16 here, packed below).
+    const int hl = (n >> 3) & 1;
+    const int f1 = ((2 * kb) ^ n) & 7;
+    uint4 qra[R][2], qrb[R][2];
+    uint32_t qa[R][2][4], qb[R][2][4];                // packed once the first score loads are issued
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const uint16_t* qp = a.q + (long(min(rq[j], a.B - 1)) * g.H + h) * D;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            qra[j][s] = *reinterpret_cast<const uint4*>(qp + 64 * hl + 8 * (f1 ^ s));
+            qrb[j][s] = *reinterpret_cast<const uint4*>(qp + 64 * (hl ^ 1) + 8 * (f1 ^ s));
+        }
+    }
     // K slice of head h: 16-byte chunk e = tid + NT * i is codeword e >> 4 of group e & 15 (global layout
     // [group][codeword][8]); it goes to LDS byte 16 e = 256 * codeword + 16 * group.
     uint4 stage[16];
@@ -972,45 +1062,11 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
             stage[i] = src[(e & 15) * K + (e >> 4)];
         }
     }
-    int lo[R], hi[R];
-    if (!split_ranges<R>(a, split, rq, lo, hi)) {
-        for (int e = tid; e < R * D; e += NT) {
-            const int j = e / D, d = e % D, rb = rq[j];
-            if (rb >= a.B) continue;
-            const long row = (long(rb) * g.H + h) * a.S_tot + split;
-            a.part_o[row * D + d] = 0.f;
-            if (d == 0) a.part_lse[row] = -INFINITY;
-        }
-        return;
-    }
-    const int32_t* ptr[R];
-    int t_lo = 0x7fffffff, t_hi = 0;
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-        ptr[j] = a.pt + long(min(rq[j], a.B - 1)) * a.pt_stride;
-        if (hi[j] > lo[j]) {
-            t_lo = min(t_lo, lo[j]);
-            t_hi = max(t_hi, hi[j]);
-        }
-    }
-    // The lane's query: blocks f1 = ((2 kb) ^ n) & 7 and f2 = f1 ^ 1 of 8 frequencies, qa = the half of
-    // slot 0's group, qb the partner half, as fp16 pairs times sm_scale * log2 e.
-    const int hl = (n >> 3) & 1;
-    const int f1 = ((2 * kb) ^ n) & 7;
-    uint32_t qa[R][2][4], qb[R][2][4];
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        const uint16_t* qp = a.q + (long(min(rq[j], a.B - 1)) * g.H + h) * D;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int f = f1 ^ s;
-            const uint4 wa = *reinterpret_cast<const uint4*>(qp + 64 * hl + 8 * f);
-            const uint4 wb = *reinterpret_cast<const uint4*>(qp + 64 * (hl ^ 1) + 8 * f);
-            qa[j][s][0] = pack_q2(wa.x, a.scale_log2); qa[j][s][1] = pack_q2(wa.y, a.scale_log2);
-            qa[j][s][2] = pack_q2(wa.z, a.scale_log2); qa[j][s][3] = pack_q2(wa.w, a.scale_log2);
-            qb[j][s][0] = pack_q2(wb.x, a.scale_log2); qb[j][s][1] = pack_q2(wb.y, a.scale_log2);
-            qb[j][s][2] = pack_q2(wb.z, a.scale_log2); qb[j][s][3] = pack_q2(wb.w, a.scale_log2);
-        }
+    for (int i = 0; i < kPt; ++i) {
+        const int e = tid + NT * i;
+        const int j = e / (kMaxSplitTok / 8), pp = e % (kMaxSplitTok / 8);
+        pid_lds[pp >> 1][(pp & 1) ^ (j >> 1)][j] = ptv[i];
     }
     // Gather address constants: byte j of ck[m] is 16 * (group of key-row byte 4 kb + m of token n ^ 4 j).
     uint32_t ck[4];
@@ -1028,46 +1084,38 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     auto opaque_bit = [](int x, int bit) { asm volatile("" : "+v"(x)); return (x & bit) != 0; };
     const bool br0 = opaque_bit(ro, 1), br1 = opaque_bit(ro, 2), bn0 = opaque_bit(n, 1), bn1 = opaque_bit(n, 2);
     int lo_o = lo[0], hi_o = hi[0];
-    const int32_t* ptr_o = ptr[0];
 #pragma unroll
     for (int j = 1; j < R; ++j)
-        if (ro == j) { lo_o = lo[j]; hi_o = hi[j]; ptr_o = ptr[j]; }
+        if (ro == j) { lo_o = lo[j]; hi_o = hi[j]; }
 
     const uint32_t page_bytes = uint32_t(g.page_bytes);
     const unsigned char* slab = a.pool + (long(a.beta) * g.H + h) * 2 * 8 * NG;   // (block, head) K rows of page 0
     const uint4* rope = a.rope16;
     const int nblk = (t_hi - t_lo + kMBlk - 1) / kMBlk;   // blocks of the workgroup
     const int nk = wave < nblk ? (nblk - wave + NW - 1) / NW : 0;   // blocks of this wave: wave + NW k, k < nk
-    // Page ids of the split's pages (index-token page (tau - t_lo) / 8), per request: a page past a request's
-    // range holds its last index page, a request without index pages physical page 0, so that every load below
-    // reads valid memory.  Loads never branch: a block past the end is clamped to the last one.
-    for (int e = tid; e < R * (kMaxSplitTok / 8); e += NT) {
-        const int j = e / (kMaxSplitTok / 8), pp = e % (kMaxSplitTok / 8);
-        const int tau = min(t_lo + 8 * pp, hi[j] - 1);
-        pid_lds[j][pp] = hi[j] > 0 ? uint32_t(ptr[j][max(tau, 0) >> 3]) : 0u;
-    }
+    // Loads never branch: a block past the end is clamped to the last one.
     auto tau0_of = [&](int k) { return t_lo + kMBlk * min(wave + NW * k, nblk - 1); };
     // Per-lane parts of the load addresses (blocks start at multiples of 16 tokens, so token n ^ 4 j of a
     // block sits in page (tau0 - t_lo) / 8 + ((n ^ 4 j) >> 3) at row (n ^ 4 j) & 7).
-    const uint32_t* pid_flat = &pid_lds[0][0];
+    // page id of request j's page `page` (relative to the split's first)
+    auto pid_of = [&](int j, int page) { return pid_lds[page >> 1][(page & 1) ^ (j >> 1)][j]; };
     const unsigned char* kbase[R];                  // dword kb of that row in page 0's (block, head) K rows
-    int pidx[R];                                    // its page-table entry, relative to the block's first page
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-        kbase[j] = slab + ((n ^ (4 * j)) & 7) * NG + 4 * kb;
-        pidx[j] = j * (kMaxSplitTok / 8) + ((n ^ (4 * j)) >> 3);
-    }
+    for (int j = 0; j < R; ++j) kbase[j] = slab + ((n ^ (4 * j)) & 7) * NG + 4 * kb;
     const uint4* rope_l1 = rope + 16 * hl + 2 * f1;          // the lane's cos/sin chunks at position 0
     const uint4* rope_l2 = rope + 16 * hl + 2 * (f1 ^ 1);
-    // key-row dwords of the wave's k-th block: dword kb of token n ^ 4 j of request j
-    auto load_ik = [&](int k, uint32_t (&ik)[R]) {
-        const int pp = (tau0_of(k) - t_lo) >> 3;
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            const uint32_t pid = pid_flat[pidx[j] + pp];
-            ik[j] = *reinterpret_cast<const uint32_t*>(kbase[j] + uint64_t(pid) * page_bytes);
-        }
+    // the lane's four page ids of the wave's k-th block (request j's in component j)
+    auto read_pids = [&](int k) {
+        return *reinterpret_cast<const uint4*>(&pid_lds[(tau0_of(k) - t_lo) >> 4][n >> 3][0]);
     };
+    // key-row dwords of a block from its page ids: dword kb of token n ^ 4 j of request j
+    auto issue_ik = [&](const uint4& pd, uint32_t (&ik)[R]) {
+        const uint32_t pid[R] = {pd.x, pd.y, pd.z, pd.w};
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            ik[j] = *reinterpret_cast<const uint32_t*>(kbase[j] + uint64_t(pid[j]) * page_bytes);
+    };
+    auto load_ik = [&](int k, uint32_t (&ik)[R]) { issue_ik(read_pids(k), ik); };
     // cos/sin chunks of the lane's token (block f1: 2, block f2: 2) and its key scale (KS)
     struct CsBuf { uint4 cs[4]; float ks; };
     auto load_cs = [&](int k, CsBuf& b) {
@@ -1080,7 +1128,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         b.cs[2] = r2[0];
         b.cs[3] = r2[1];
         if constexpr (KS) {
-            const uint32_t pid = pid_lds[ro][(tau0 + n - t_lo) >> 3];
+            const uint32_t pid = pid_of(ro, (tau0 + n - t_lo) >> 3);
             b.ks = f16_to_f32(a.kscale[(uint64_t(pid) * g.T + a.step) * 8 + ((tau0 + n) & 7)]);
         }
     };
@@ -1128,23 +1176,30 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     // The wave's k-th block: the scores of the four requests, the lane's own kept.  The gathers of request 0
     // arrive in G0 (issued during the block before); each request's gathers are issued one request ahead,
     // and the next block's request 0 into G0 (ikn: its key-row dwords).
-    auto score_blk = [&](int k, const uint32_t (&ik)[R], const CsBuf& b, uint4 (&G0)[4], const uint32_t (&ikn)[R]) {
+    // The loads for later blocks are issued inside: the page ids of block k + 4 before the gathers of request
+    // 2 (so that waiting for them never waits for gathers issued after them), block k + 4's key-row dwords into
+    // ik once its last gathers are issued, block k + 2's cos/sin into b once psi is formed.
+    auto score_blk = [&](int k, uint32_t (&ik)[R], CsBuf& b, uint4 (&G0)[4], const uint32_t (&ikn)[R]) {
         uint32_t c[2][4], s[2][4];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             c[u][0] = b.cs[2 * u].x; c[u][1] = b.cs[2 * u].y; c[u][2] = b.cs[2 * u + 1].x; c[u][3] = b.cs[2 * u + 1].y;
             s[u][0] = b.cs[2 * u].z; s[u][1] = b.cs[2 * u].w; s[u][2] = b.cs[2 * u + 1].z; s[u][3] = b.cs[2 * u + 1].w;
         }
+        const float ks = KS ? b.ks : 1.f;
         f32x4_t acc[R];
         uint4 G1[4], G2[4], G3[4];
         gather(J1{}, ik[1], G1);
+        const uint4 pd = read_pids(k + 4);
         acc[0] = request_mfma(J0{}, G0, c, s);
         gather(J2{}, ik[2], G2);
         acc[1] = request_mfma(J1{}, G1, c, s);
         gather(J3{}, ik[3], G3);
+        issue_ik(pd, ik);
         acc[2] = request_mfma(J2{}, G2, c, s);
         gather(J0{}, ikn[0], G0);
         acc[3] = request_mfma(J3{}, G3, c, s);
+        load_cs(k + 2, b);
         // the lane's own score: request ro, register n & 3 of its accumulator (15 selects on the lane bits)
         float e[4];
 #pragma unroll
@@ -1156,7 +1211,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         const float e01 = bn0 ? e[1] : e[0];
         const float e23 = bn0 ? e[3] : e[2];
         float sc = bn1 ? e23 : e01;
-        if constexpr (KS) sc *= b.ks;
+        if constexpr (KS) sc *= ks;
         const int tau = t_lo + kMBlk * (wave + NW * k) + n;
         sc = (k < nk && tau >= lo_o && tau < hi_o) ? sc : -INFINITY;
         rmax = fmaxf(rmax, sc);
@@ -1164,7 +1219,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     };
     __syncthreads();                                      // page ids in LDS
     // key-row dwords four blocks ahead (set k % 4), cos/sin two blocks ahead (set k % 2); each set is reloaded
-    // right after its block is scored.  The first loads are issued before the K slice is stored to LDS.
+    // while its block is scored.  The first loads are issued before the K slice is stored to LDS.
     uint32_t IK0[R], IK1[R], IK2[R], IK3[R];
     CsBuf C0, C1;
     if (nk > 0) {
@@ -1174,6 +1229,18 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         load_ik(3, IK3);
         load_cs(0, C0);
         load_cs(1, C1);
+    }
+    // the query as fp16 pairs times sm_scale * log2 e
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint4 wa = qra[j][s], wb = qrb[j][s];
+            qa[j][s][0] = pack_q2(wa.x, a.scale_log2); qa[j][s][1] = pack_q2(wa.y, a.scale_log2);
+            qa[j][s][2] = pack_q2(wa.z, a.scale_log2); qa[j][s][3] = pack_q2(wa.w, a.scale_log2);
+            qb[j][s][0] = pack_q2(wb.x, a.scale_log2); qb[j][s][1] = pack_q2(wb.y, a.scale_log2);
+            qb[j][s][2] = pack_q2(wb.z, a.scale_log2); qb[j][s][3] = pack_q2(wb.w, a.scale_log2);
+        }
     }
     {   // K slice, bf16 -> fp16
         uint4* dst = reinterpret_cast<uint4*>(lds);
@@ -1190,24 +1257,15 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         // scores discarded (the loop has one exit, so the loads in flight are counted across iterations)
         for (int k = 0; k < nk; k += 4) {
             score_blk(k, IK0, C0, G0, IK1);
-            load_ik(k + 4, IK0);
-            load_cs(k + 2, C0);
             score_blk(k + 1, IK1, C1, G0, IK2);
-            load_ik(k + 5, IK1);
-            load_cs(k + 3, C1);
             score_blk(k + 2, IK2, C0, G0, IK3);
-            load_ik(k + 6, IK2);
-            load_cs(k + 4, C0);
             score_blk(k + 3, IK3, C1, G0, IK0);
-            load_ik(k + 7, IK3);
-            load_cs(k + 5, C1);
         }
     }
     // value rows of the lane's own (request, token) of the wave's k-th block, the first four loaded now
     const unsigned char* vbase = slab + (8 + (n & 7)) * NG;   // the lane's value row in page 0
-    const int vidx = ro * (kMaxSplitTok / 8) + (n >> 3);
     auto load_vr = [&](int k) -> uint4 {
-        const uint32_t pid = pid_flat[vidx + ((tau0_of(k) - t_lo) >> 3)];
+        const uint32_t pid = pid_of(ro, ((tau0_of(k) - t_lo) >> 3) + (n >> 3));
         return *reinterpret_cast<const uint4*>(vbase + uint64_t(pid) * page_bytes);
     };
     uint4 VR0 = make_uint4(0u, 0u, 0u, 0u), VR1 = VR0, VR2 = VR0, VR3 = VR0;
@@ -1227,14 +1285,16 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     __syncthreads();                                // every wave is done with the K slice
 #pragma unroll
     for (int i = 0; i < K * 64 / 4 / NT; ++i) reinterpret_cast<uint4*>(bins)[tid + i * NT] = make_uint4(0u, 0u, 0u, 0u);
-    // V rows of this lane's contraction block, needed once the bins are complete
-    const int cb_blk = tid >> 4, g16 = tid & 15;
-    uint4 vrow[16];
+    // V slice dwords of this lane's contraction part, needed once the bins are complete: wave w takes
+    // codewords 64 w .. 64 w + 63; lane l = 4 g + q takes dword q (channels 2 q, 2 q + 1) of group g's rows.
+    constexpr int kCw = K / NW;
+    uint32_t vd[kCw];
     {
-        const uint16_t* vsl = static_cast<const uint16_t*>(a.slice_v) + h * a.slice_hstride;
-        const uint4* src = reinterpret_cast<const uint4*>(vsl + (long(g16) * K + 16 * cb_blk) * C);
+        const uint32_t* vsl = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.slice_v) +
+                                                                h * a.slice_hstride);
+        const uint32_t* src = vsl + ((lane >> 2) * K + kCw * wave) * (C / 2) + (lane & 3);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) vrow[i] = src[i];
+        for (int t = 0; t < kCw; ++t) vd[t] = src[t * (C / 2)];
     }
     __syncthreads();                                // bins cleared, wave maxima visible
     float M[R];
@@ -1288,67 +1348,62 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     }
     __syncthreads();
 
-    // ---- contraction: lane (cb_blk, g16) over its 16 codewords ----
-    float o[PL];
-#pragma unroll
-    for (int i = 0; i < PL; ++i) o[i] = 0.f;
-    uint32_t lsum[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) lsum[j] = 0u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = 16 * cb_blk + i;
-        const uint4 b4 = *reinterpret_cast<const uint4*>(bins + r * 64 + g16 * R);
-        const uint32_t bv[R] = {b4.x, b4.y, b4.z, b4.w};
-        const uint32_t vw[4] = {vrow[i].x, vrow[i].y, vrow[i].z, vrow[i].w};
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            lsum[j] += bv[j];
-            const float bw = float(bv[j]);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                o[j * C + 2 * u] = fmaf(bw, bf16_lo(vw[u]), o[j * C + 2 * u]);
-                o[j * C + 2 * u + 1] = fmaf(bw, bf16_hi(vw[u]), o[j * C + 2 * u + 1]);
-            }
-        }
-    }
-    // Partials over this wave's own bin rows (64 rows of 256 B, read by no other wave): lane slot
-    // (cb_blk & 3) * 16 + g16 holds PL floats, then the weight totals of the g16 = 0 lanes.
-    float* part = reinterpret_cast<float*>(lds) + wave * 4096;
+    // ---- contraction on the matrix cores ----
+    // o[r][8 g + c] = sum over codewords w of bin[w][4 g + r] * V_g[w][c]: per group a 4 x 4 block product per
+    // channel set, the 16 groups as the 16 blocks of v_mfma_f32_4x4x1_16b_f32 (lane 4 g + i supplies row i of
+    // block g's A = the bin of request i, lane 4 g + j column j of its B = channel 2 j (set 0) or 2 j + 1
+    // (set 1) of the codeword; register i of lane 4 g + j receives (request i, channel 2 j + set)).  fp32
+    // throughout (a bin converts with relative rounding 2^-24).  Lanes 0..3 (group 0) also total the bins of
+    // their request in integers: the sum of its weights.
     {
-        float4* dst = reinterpret_cast<float4*>(part + ((cb_blk & 3) * 16 + g16) * PL);
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0;
+        uint32_t lsum = 0u;
+        const uint32_t* brow = bins + kCw * wave * 64 + lane;
 #pragma unroll
-        for (int i = 0; i < PL / 4; ++i) dst[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-        if (g16 == 0) {
-            uint32_t* ld = reinterpret_cast<uint32_t*>(part + 64 * PL) + (cb_blk & 3) * R;
-#pragma unroll
-            for (int j = 0; j < R; ++j) ld[j] = lsum[j];
+        for (int t = 0; t < kCw; t += 2) {
+            const uint32_t u0 = brow[t * 64], u1 = brow[(t + 1) * 64];
+            lsum += u0 + u1;
+            const float a0 = float(u0), a1 = float(u1);
+            acc0 = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, bf16_lo(vd[t]), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, bf16_hi(vd[t]), acc1, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, bf16_lo(vd[t + 1]), acc2, 0, 0, 0);
+            acc3 = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, bf16_hi(vd[t + 1]), acc3, 0, 0, 0);
         }
+        float4* dst = reinterpret_cast<float4*>(&cpart[wave][lane][0]);
+        dst[0] = make_float4(acc0[0] + acc2[0], acc0[1] + acc2[1], acc0[2] + acc2[2], acc0[3] + acc2[3]);
+        dst[1] = make_float4(acc1[0] + acc3[0], acc1[1] + acc3[1], acc1[2] + acc3[2], acc1[3] + acc3[3]);
+        if (lane < R) lpart[wave][lane] = lsum;
     }
     __syncthreads();
-    for (int e = tid; e < R * D; e += NT) {
-        const int j = e / D, d = e % D, rb = rq[j];
-        if (rb >= a.B) continue;
-        const long orow = (long(rb) * g.H + h) * a.S_tot + split;
-        if (hi[j] <= lo[j]) {
-            a.part_o[orow * D + d] = 0.f;
-            if (d == 0) a.part_lse[orow] = -INFINITY;
-            continue;
-        }
-        const int gr = d / C, u = d % C;
-        const int p = j * C + u;
-        const float* pbase = reinterpret_cast<const float*>(lds);
-        float accv = 0.f;
-        uint64_t L = 0;
+    {
+        // thread (l, i): request i, channels 8 (l >> 2) + 2 (l & 3) + {0, 1}
+        const int l = tid >> 2, i = tid & 3, rb = rq[i];
+        int lo_i = lo[0], hi_i = hi[0];
+        float Mi = M[0];
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            const float* pw = pbase + (b >> 2) * 4096;
-            accv += pw[((b & 3) * 16 + gr) * PL + p];
-            L += reinterpret_cast<const uint32_t*>(pw + 64 * PL)[(b & 3) * R + j];
+        for (int j = 1; j < R; ++j)
+            if (i == j) { lo_i = lo[j]; hi_i = hi[j]; Mi = M[j]; }
+        if (rb < a.B) {
+            const long orow = (long(rb) * g.H + h) * a.S_tot + split;
+            const int d = 8 * (l >> 2) + 2 * (l & 3);
+            float2* po = reinterpret_cast<float2*>(a.part_o + orow * D + d);
+            if (hi_i <= lo_i) {
+                *po = make_float2(0.f, 0.f);
+                if (d == 0) a.part_lse[orow] = -INFINITY;
+            } else {
+                float o0 = 0.f, o1 = 0.f;
+                uint32_t L = 0u;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    o0 += cpart[w][l][i];
+                    o1 += cpart[w][l][R + i];
+                    L += lpart[w][i];
+                }
+                const float Lf = float(L);
+                *po = make_float2(o0 / Lf, o1 / Lf);
+                if (d == 0) a.part_lse[orow] = (Mi + (log2f(Lf) - float(a.fix_bits))) * kLn2;
+            }
         }
-        const float Lf = float(L);
-        a.part_o[orow * D + d] = accv / Lf;
-        if (d == 0) a.part_lse[orow] = (M[j] + (log2f(Lf) - float(a.fix_bits))) * kLn2;
     }
 }
 
