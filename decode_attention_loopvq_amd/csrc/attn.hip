@@ -966,6 +966,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     __shared__ float wmax[NW][R];
     __shared__ __align__(16) float cpart[NW][64][2 * R];   // contraction partials per wave (lane, channel pair)
     __shared__ uint32_t lpart[NW][R];                      // weight totals per wave
+    __shared__ __align__(16) uint32_t qf16[R][D / 2];      // query rows as fp16 pairs times sm_scale * log2 e
     // Page ids of the split's pages, grouped by page pair (one 16-token block): entry (P, h, j) holds request
     // j's page 2 P + (h ^ (j >> 1)), so that lane (n, kb), whose row of request j holds token n ^ 4 j (page
     // half (n >> 3) ^ (j >> 1)), finds its four page ids of a block in one 16-byte read at (P, n >> 3).
@@ -1035,21 +1036,18 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         const uint32_t v = uint32_t(a.pt[long(row) * a.pt_stride + page]);
         ptv[i] = hij > 0 ? v : 0u;
     }
+    // The query rows: wave w converts request w's row, one dword (two channels) per lane, into qf16.
+    static_assert(R * D / 2 == NT, "one query dword per thread");
+    int qrow = rq[0];
+#pragma unroll
+    for (int j = 1; j < R; ++j)
+        if (wave == j) qrow = rq[j];
+    const uint32_t qraw = reinterpret_cast<const uint32_t*>(a.q + (long(min(qrow, a.B - 1)) * g.H + h) * D)[lane];
     // The lane's query: blocks f1 = ((2 kb) ^ n) & 7 and f2 = f1 ^ 1 of 8 frequencies, qa = the half of
-    // slot 0's group, qb the partner half (raw bf16 here, packed below).
+    // slot 0's group, qb the partner half (read from qf16 once the first score loads are issued).
     const int hl = (n >> 3) & 1;
     const int f1 = ((2 * kb) ^ n) & 7;
-    uint4 qra[R][2], qrb[R][2];
-    uint32_t qa[R][2][4], qb[R][2][4];                // packed once the first score loads are issued
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        const uint16_t* qp = a.q + (long(min(rq[j], a.B - 1)) * g.H + h) * D;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            qra[j][s] = *reinterpret_cast<const uint4*>(qp + 64 * hl + 8 * (f1 ^ s));
-            qrb[j][s] = *reinterpret_cast<const uint4*>(qp + 64 * (hl ^ 1) + 8 * (f1 ^ s));
-        }
-    }
+    uint32_t qa[R][2][4], qb[R][2][4];
     // K slice of head h: 16-byte chunk e = tid + NT * i is codeword e >> 4 of group e & 15 (global layout
     // [group][codeword][8]); it goes to LDS byte 16 e = 256 * codeword + 16 * group.
     uint4 stage[16];
@@ -1068,14 +1066,15 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         const int j = e / (kMaxSplitTok / 8), pp = e % (kMaxSplitTok / 8);
         pid_lds[pp >> 1][(pp & 1) ^ (j >> 1)][j] = ptv[i];
     }
-    // Gather address constants: byte j of ck[m] is 16 * (group of key-row byte 4 kb + m of token n ^ 4 j).
+    qf16[wave][lane] = pack_q2(qraw, a.scale_log2);
+    // Gather address constants: byte j of ck[m] is 16 * (group of key-row byte 4 kb + m of token n ^ 4 j),
+    // i.e. 16 * (P(4 kb + m) ^ n ^ 4 j) with P(4 kb + m) = (m & 1) | 2 kb | 8 (m >> 1) (the key-row byte
+    // permutation, see index_byte).
     uint32_t ck[4];
+    {
+        const uint32_t c0 = (uint32_t(16 * ((2 * kb) ^ n)) * 0x01010101u) ^ 0xC0804000u;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int j = 0; j < R; ++j) v |= uint32_t(16 * key_group_of_byte(4 * kb + m, n ^ (4 * j))) << (8 * j);
-        ck[m] = v;
+        for (int m = 0; m < 4; ++m) ck[m] = c0 ^ (uint32_t(16 * ((m & 1) | ((m >> 1) << 3))) * 0x01010101u);
     }
     // The lane's own (request, token) of every block: request ro = kb ^ (n >> 2), token tau0 + n.
     const int ro = kb ^ (n >> 2);
@@ -1230,16 +1229,14 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         load_cs(0, C0);
         load_cs(1, C1);
     }
-    // the query as fp16 pairs times sm_scale * log2 e
 #pragma unroll
     for (int j = 0; j < R; ++j) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const uint4 wa = qra[j][s], wb = qrb[j][s];
-            qa[j][s][0] = pack_q2(wa.x, a.scale_log2); qa[j][s][1] = pack_q2(wa.y, a.scale_log2);
-            qa[j][s][2] = pack_q2(wa.z, a.scale_log2); qa[j][s][3] = pack_q2(wa.w, a.scale_log2);
-            qb[j][s][0] = pack_q2(wb.x, a.scale_log2); qb[j][s][1] = pack_q2(wb.y, a.scale_log2);
-            qb[j][s][2] = pack_q2(wb.z, a.scale_log2); qb[j][s][3] = pack_q2(wb.w, a.scale_log2);
+            const uint4 wa = *reinterpret_cast<const uint4*>(&qf16[j][32 * hl + 4 * (f1 ^ s)]);
+            const uint4 wb = *reinterpret_cast<const uint4*>(&qf16[j][32 * (hl ^ 1) + 4 * (f1 ^ s)]);
+            qa[j][s][0] = wa.x; qa[j][s][1] = wa.y; qa[j][s][2] = wa.z; qa[j][s][3] = wa.w;
+            qb[j][s][0] = wb.x; qb[j][s][1] = wb.y; qb[j][s][2] = wb.z; qb[j][s][3] = wb.w;
         }
     }
     {   // K slice, bf16 -> fp16
