@@ -170,9 +170,12 @@ __global__ void encode_scan_kernel(Geo geo, int block, const uint16_t* __restric
 // coordinates past G are zero), and result rows 4*(l >> 4) .. +3 of column
 // l & 15.  Per 16-token tile: 16 MFMAs with the codewords as rows and the
 // tokens as columns, so lane (q, n) holds 64 scores of token n (codewords
-// 16t + 4q + i); its best, then the best of the 4 lanes of the column
-// through two lane swaps; the lowest index wins exact ties.  Picks differ
-// from the exact minimum only by fp32 rounding of the sums.
+// 16t + 4q + i); its best two, then the best two of the 4 lanes of the
+// column through two lane swaps; the lowest index wins exact ties.  Where the
+// best two scores lie within twice the fp32 error bound of a score, the
+// token's nearest codeword is taken again from fp64 direct differences over
+// all 256 codewords, so that every pick is the exact nearest codeword (the
+// first one among equal distances).
 //
 // XREQ (few pages per request, as in the decode-time encode of one page):
 // a workgroup takes token slots u = b * tpr + j of all requests (tpr =
@@ -308,6 +311,8 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
 
     // indices of the block's tokens for the 8 groups of this octet, written out at the end
     __shared__ __align__(16) uint8_t idx[kEncTile * kEncTilesPerWg][8];
+    // per wave and tile, the tokens whose best two scores lie within the error bound (bit n: token t0 + n)
+    __shared__ uint16_t near_tok[8][kEncTilesPerWg];
     // -||e_r||^2 / 2 of the wave's group in codeword order (each wave writes and reads only its own row)
     __shared__ __align__(16) float cnorm[8][256];
     {
@@ -315,51 +320,91 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) cnorm[w8][16 * t + n] = cinit[t];   // (the 4 lanes of a column agree)
     }
+    // Error bound of a score (sums in fp32; products of bf16 values exact): |s^ - s| <= eps =
+    // kScoreErr * (||z|| E + E^2), E the largest codeword norm of the group.  kScoreErr is twice the fp32
+    // bound gamma_32 = 32 * 2^-24 / (1 - 32 * 2^-24) of a 33-term sum, which also covers an accumulation that
+    // does not round to nearest.  Where the best and second-best scores of a token differ by more than 2 eps,
+    // the best is the exact nearest codeword.
+    constexpr float kScoreErr = 4.0e-6f;
+    float e2max = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) e2max = fmaxf(e2max, -2.f * cinit[t]);
+    e2max = __builtin_amdgcn_readfirstlane(wave_max(e2max));
+    const float emax = __builtin_amdgcn_readfirstlane(sqrtf(e2max));
     // Tile of 16 tokens with the codewords as rows: lane (q, n) gets the scores of token t0 + n for
     // codewords 16t + 4q + i (t < 16, i < 4), keeps its best (scanning in increasing codeword order with a
-    // strict >, so the lowest index wins equal values), then the best of the 4 lanes n, n + 16, n + 32,
-    // n + 48 through two lane swaps.
-    auto merge = [](float& best, int& r, float ob, int orr) {
+    // strict >, so the lowest index wins equal values) and its second best (a median of three), then the best
+    // two of the 4 lanes n, n + 16, n + 32, n + 48 through two lane swaps.  Tokens whose best two lie within
+    // 2 eps are decided again by exact distances (recheck).
+    auto merge = [](float& best, float& second, int& r, float ob, float os, int orr) {
         const bool take = ob > best || (ob == best && orr < r);
+        second = __builtin_amdgcn_fmed3f(best, ob, fmaxf(second, os));   // max(min(best, ob), second, os)
         best = take ? ob : best;
         r = take ? orr : r;
     };
     auto tile_fn = [&](int t0, const RawA& raw) {
         const bf16x8_t Bcur = build_a(raw);
         const float* cn = &cnorm[tid >> 6][4 * q];
+        // each tile of scores is scanned four MFMAs after it is issued, so that few accumulators are live
+        constexpr int kLag = 4;
         f32x4_t acc[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const f32x4_t ci = *reinterpret_cast<const f32x4_t*>(cn + 16 * t);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[t], Bcur, ci, 0, 0, 0);
-        }
-        float best = acc[0][0];
+        float best = -INFINITY, second = -INFINITY;
         int r = 4 * q;
+        auto scan = [&](int t) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t)
-#pragma unroll
-            for (int i = (t == 0 ? 1 : 0); i < 4; ++i) {
-                const bool gt = acc[t][i] > best;
-                best = gt ? acc[t][i] : best;
+            for (int i = 0; i < 4; ++i) {
+                const float v = acc[t][i];
+                const bool gt = v > best;
+                second = __builtin_amdgcn_fmed3f(best, second, v);
                 r = gt ? 16 * t + 4 * q + i : r;
+                best = gt ? v : best;
             }
+        };
+#pragma unroll
+        for (int t = 0; t < 16 + kLag; ++t) {
+            if (t < 16) {
+                const f32x4_t ci = *reinterpret_cast<const f32x4_t*>(cn + 16 * t);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[t], Bcur, ci, 0, 0, 0);
+            }
+            if (t >= kLag) scan(t - kLag);
+        }
         {   // lanes l and l ^ 32, then l and l ^ 16 (the combine is symmetric, so both lanes of a pair agree)
             const auto bv = __builtin_amdgcn_permlane32_swap(__float_as_uint(best), __float_as_uint(best), false, false);
+            const auto sv = __builtin_amdgcn_permlane32_swap(__float_as_uint(second), __float_as_uint(second), false, false);
             const auto rv = __builtin_amdgcn_permlane32_swap(uint32_t(r), uint32_t(r), false, false);
-            const uint32_t b0 = bv[0], b1 = bv[1], r0v = rv[0], r1v = rv[1];
+            const uint32_t b0 = bv[0], b1 = bv[1], s0v = sv[0], s1v = sv[1], r0v = rv[0], r1v = rv[1];
             best = __uint_as_float(b0);
+            second = __uint_as_float(s0v);
             r = int(r0v);
-            merge(best, r, __uint_as_float(b1), int(r1v));
+            merge(best, second, r, __uint_as_float(b1), __uint_as_float(s1v), int(r1v));
         }
         {
             const auto bv = __builtin_amdgcn_permlane16_swap(__float_as_uint(best), __float_as_uint(best), false, false);
+            const auto sv = __builtin_amdgcn_permlane16_swap(__float_as_uint(second), __float_as_uint(second), false, false);
             const auto rv = __builtin_amdgcn_permlane16_swap(uint32_t(r), uint32_t(r), false, false);
-            const uint32_t b0 = bv[0], b1 = bv[1], r0v = rv[0], r1v = rv[1];
+            const uint32_t b0 = bv[0], b1 = bv[1], s0v = sv[0], s1v = sv[1], r0v = rv[0], r1v = rv[1];
             best = __uint_as_float(b0);
+            second = __uint_as_float(s0v);
             r = int(r0v);
-            merge(best, r, __uint_as_float(b1), int(r1v));
+            merge(best, second, r, __uint_as_float(b1), __uint_as_float(s1v), int(r1v));
         }
+        // ||z||^2 of the column's token (the 4 lanes of the column hold 8 coordinates each)
+        const uint4 bw = __builtin_bit_cast(uint4, Bcur);
+        float zsq = 0.f;
+        {
+            const uint32_t w4[4] = {bw.x, bw.y, bw.z, bw.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                zsq = fmaf(bf16_lo(w4[u]), bf16_lo(w4[u]), zsq);
+                zsq = fmaf(bf16_hi(w4[u]), bf16_hi(w4[u]), zsq);
+            }
+            zsq += __shfl_xor(zsq, 16, 64);
+            zsq += __shfl_xor(zsq, 32, 64);
+        }
+        const float eps = kScoreErr * (sqrtf(zsq) * emax + e2max);
+        const uint64_t near = __builtin_amdgcn_ballot_w64(q == 0 && best - second <= 2.f * eps);
         if (q == 0) idx[(t0 - tok_base) + n][grp & 7] = uint8_t(r);
+        if (lane == 0) near_tok[tid >> 6][(t0 - tok_base) / kEncTile] = uint16_t(near);
     };
     // two alternating buffers: the loads of tile k+1 are in flight while tile k computes
     RawA rawA = load_a(tok_base + n), rawB;
@@ -370,6 +415,55 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
         if (t0 + kEncTile >= t_end) break;
         rawA = load_a(t0 + 2 * kEncTile + n);
         tile_fn(t0 + kEncTile, rawB);
+    }
+    // The tokens marked near a tie: the nearest codeword again, by direct differences in fp64 summed in
+    // coordinate order (as the definition writes it) over all 256 codewords; lane k < G loads coordinate k of
+    // the coupled vector, each lane takes codewords lane + 64 i, then the wave's minimum, the lowest index
+    // among equal distances.
+    for (int tt = 0; tt * kEncTile < t_end - tok_base; ++tt) {
+        uint32_t near = near_tok[tid >> 6][tt];
+        while (near != 0) {
+            const int nf = __builtin_ctz(near);
+            near &= near - 1;
+            const int j = tok_base + tt * kEncTile + nf;
+            const uint16_t* xr = nullptr;
+            if constexpr (XREQ) {
+                int bu, ju;
+                if (!slot(j, bu, ju)) continue;             // a slot without a token: nothing to decide
+                xr = x + xbase + long(bu) * a.s0 + ((a.tok0 ? a.tok0[bu] : 0) + ju) * a.s2;
+            } else {
+                xr = x + xbase + (row0 + j) * a.s2;
+            }
+            // xbase points at this lane's first coordinate (8 q / TC channels in); step back to the group's
+            const uint16_t* xg = xr - (kin ? (8 * q) / TC : 0);
+            const int kl = lane < G ? lane : 0;
+            const float zl = bf16_to_f32(xg[long(kl % TC) * a.s3 + kl / TC]);
+            const uint16_t* eg = a.cb + ((((long(a.block) * g.H + h) * 2 + kv) * g.NG + grp) * g.K) * long(G);
+            double bd = 0.0;
+            int br = -1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = lane + 64 * i;
+                const uint16_t* er = eg + long(rr) * G;
+                double d = 0.0;
+#pragma unroll
+                for (int k = 0; k < 32; ++k) {
+                    if (k < G) {
+                        const float zk = __shfl(zl, k, 64);
+                        const double diff = double(zk) - double(bf16_to_f32(er[k]));
+                        d = fma(diff, diff, d);
+                    }
+                }
+                if (br < 0 || d < bd) { bd = d; br = rr; }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const double od = __shfl_xor(bd, off, 64);
+                const int orr = __shfl_xor(br, off, 64);
+                if (od < bd || (od == bd && orr < br)) { bd = od; br = orr; }
+            }
+            if (lane == 0) idx[j - tok_base][grp & 7] = uint8_t(br);
+        }
     }
     __syncthreads();
     // one thread per token: the octet's 8 index bytes, one 8-byte store (value rows: the octet's bytes sit

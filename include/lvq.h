@@ -152,11 +152,13 @@ LVQ_API lvq_status lvq_rope_table_f16(int32_t len, int32_t D, double base, void*
  * replaced by the index of its nearest codeword, argmin_r ||z - e_r||^2, and
  * written to pool page page_table[b*pt_stride + lp] at [block][h][kv].
  * bf16 codebooks with G a multiple of 8 and T_c in {1, 2, 4, 8}: the
- * distances come from a bf16 matrix-core
- * contraction with fp32 sums, argmax_r (z . e_r - ||e_r||^2 / 2); equal
- * values resolve to the lowest index, and a pick can differ from the exact
- * minimum only by the fp32 rounding of the sums.  fp32 codebooks and the
- * other bf16 shapes: an exact fp64 scan, lowest index on ties.
+ * scores come from a bf16 matrix-core contraction with fp32 sums,
+ * argmax_r (z . e_r - ||e_r||^2 / 2); where a token's best two scores lie
+ * within twice the fp32 error bound of a score, its nearest codeword is
+ * taken again from fp64 direct differences over all codewords, so every
+ * pick is the exact nearest codeword, the lowest index among equal
+ * distances.  fp32 codebooks and the other bf16 shapes: an exact fp64 scan,
+ * lowest index on ties.
  * The same call serves prefill (many pages) and decode (the oldest window
  * page, every 8 generated tokens).
  *
