@@ -33,17 +33,46 @@ def _geo(cfg):
                        page=cfg.page)
 
 
-def _check_indices(p, b, h, geo):
-    """GPU indices of (b, h) against the oracle's encode; returns the oracle's indices."""
+def _oracle_indices(raw, E, geo, L, blocks=None):
+    """The oracle's encode of one (request, head) (encode_request's steps: the coupled vectors of each loop
+    block, then each group's nearest codeword), for the loop blocks `blocks` only (all when None; the others
+    stay zero), with the (block, group) problems spread over host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    _, q_lo, q_hi = lv.cache_regions(L, geo)
+    out = np.zeros((geo.NB, q_hi - q_lo, geo.NG), dtype=np.uint8)
+    if q_hi == q_lo:
+        return out
+    blocks = range(geo.NB) if blocks is None else blocks
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        jobs = []
+        for beta in blocks:
+            x_block = np.transpose(np.asarray(raw[q_lo:q_hi, beta * geo.Tc:(beta + 1) * geo.Tc, :], np.float64),
+                                   (1, 0, 2))
+            z = lv.couple(x_block, geo.G)
+            for grp in range(geo.NG):
+                jobs.append((beta, grp, ex.submit(lv.nearest_codeword, np.ascontiguousarray(z[:, grp]),
+                                                  np.asarray(E[beta, grp], np.float64))))
+        for beta, grp, job in jobs:
+            out[beta, :, grp] = job.result()[0]
+    return out
+
+
+def _check_indices(p, b, h, geo, blocks=None):
+    """GPU indices of (b, h) against the oracle's encode (loop blocks `blocks`, all when None); returns the
+    oracle's indices."""
     from tests import harness
     L = p.lengths[b]
     _, q_lo, q_hi = lv.cache_regions(L, geo)
     out = {}
     for kind in ("k", "v"):
         E = harness.host_codebooks(p, h, kind)
-        ref = lv.encode_request(p.raw[(kind, b, h)], E, geo, L)
+        ref = _oracle_indices(p.raw[(kind, b, h)], E, geo, L, blocks)
         got = harness.gpu_indices(p, b, h, kind)
         assert got.shape == ref.shape, (got.shape, ref.shape)
+        if blocks is not None:
+            keep = np.zeros(geo.NB, dtype=bool)
+            keep[list(blocks)] = True
+            got = np.where(keep[:, None, None], got, ref)
         bad = np.argwhere(got != ref)
         for beta, j, g in bad:
             x = p.raw[(kind, b, h)][q_lo + j, beta * geo.Tc:(beta + 1) * geo.Tc, :]
@@ -73,14 +102,18 @@ def lv_cb(p, h, kind):
     return harness.host_codebooks(p, h, kind)
 
 
-def _run_parity(cfg, rows, steps, splits=(0,)):
+def _run_parity(cfg, rows, steps, splits=(0,), only_needed_blocks=False):
+    """Indices and attention of `rows` against the oracle at loop steps `steps`.  only_needed_blocks: the
+    indices of the loop blocks those steps read only (long contexts)."""
     from tests import harness
     geo = _geo(cfg)
     _say(f"[build] {cfg.name} B={cfg.B} H={cfg.H} L={cfg.L} T={cfg.T} Tc={cfg.Tc} G={cfg.G} rows={len(rows)}")
     p = harness.build_loopvq(cfg, keep=rows)
+    blocks = sorted({t // cfg.Tc for t in steps}) if only_needed_blocks else None
     idx = {}
     for (b, h) in rows:
-        idx[(b, h)] = _check_indices(p, b, h, geo)
+        _say(f"[indices] {cfg.name} row ({b},{h}) L={p.lengths[b]}")
+        idx[(b, h)] = _check_indices(p, b, h, geo, blocks)
     worst = 0.0
     for ns in splits:
         for t in steps:
@@ -197,17 +230,17 @@ def test_ragged_splits_and_pages():
 
 def test_encode_decode_page():
     """The decode-time encode: one page per request (its last index page, as after every 8 generated
-    tokens), written into a cleared pool, equals byte for byte the prefill encode of the same tokens (whose
-    indices the parity tests check against the oracle), for every loop block, K and V; a request without
-    an index page writes nothing.  Lengths 683, 115, 454, 49, 388, 88, random page order."""
+    tokens), written into a cleared pool, equals byte for byte the prefill encode of the same tokens and the
+    oracle's indices of those tokens, for every request, head, loop block, K and V; a request without an
+    index page writes nothing.  Lengths 683, 115, 454, 49, 388, 88, random page order."""
     import decode_attention_loopvq_amd as lvq
     import synth.loopvq as syn
     from tests import harness
     cfg = loopvq_config("loopvq-b64-6k", B=6, H=2, L=700, ragged=(40, 700), random_pages=True, seed=12)
     geo = _geo(cfg)
-    p = harness.build_loopvq(cfg, keep=[(0, 1), (5, 0)])
-    for (b, h) in [(0, 1), (5, 0)]:
-        _check_indices(p, b, h, geo)
+    rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    p = harness.build_loopvq(cfg, keep=rows)
+    ref = {(b, h): _check_indices(p, b, h, geo) for (b, h) in rows}
     c = p.cache
     n = torch.tensor(c.n_pages, dtype=torch.int32, device="cuda")
     last = (n - 1).clamp(min=0)
@@ -221,12 +254,23 @@ def test_encode_decode_page():
                            c.page_table, last, one, 1, x_tok0=tok0)
     torch.cuda.synchronize()
     written = []
+    NG = geo.NG
     for b in range(cfg.B):
         if c.n_pages[b] == 0:
             continue
         phys = int(c.page_table_host[b, c.n_pages[b] - 1])
         written.append(phys)
         assert torch.equal(pool2[phys], c.pool[phys]), f"request {b}: page {phys} differs"
+        # the written page against the oracle's indices of the request's last 8 index tokens
+        page = pool2[phys].cpu().numpy()                                  # [NB][H][2][8][NG]
+        tau = 8 * (c.n_pages[b] - 1) + np.arange(8)[:, None]
+        grp = np.arange(NG)[None, :]
+        for h in range(cfg.H):
+            for kv, kind in enumerate(("k", "v")):
+                for beta in range(geo.NB):
+                    got = page[beta, h, kv][np.arange(8)[:, None], harness.index_byte(kind, NG, grp, tau)]
+                    np.testing.assert_array_equal(got, ref[(b, h)][kind][beta, -8:],
+                                                  err_msg=f"request {b} head {h} {kind} block {beta}")
     rest = torch.ones(pool2.shape[0], dtype=torch.bool, device="cuda")
     rest[torch.tensor(written, device="cuda")] = False
     assert not pool2[rest].any(), "bytes written outside the encoded pages"
@@ -289,6 +333,24 @@ def test_full_b64_6k_sampled():
 def test_full_b1_1k():
     cfg = loopvq_config("loopvq-b1-1k-fp32cb")
     _run_parity(cfg, [(0, 0)], steps=range(cfg.T), splits=(0,))
+
+
+def test_full_b8_32k_sampled():
+    """The 0.25-bit long-context workload at full size (batch 8, 16 heads, 32768 tokens, 256-token recent
+    window, T_c = 4, G = 32), every loop step, checked on sampled rows: indices and attention."""
+    cfg = loopvq_config("loopvq-b8-32k")
+    _run_parity(cfg, [(0, 0), (7, 15)], steps=range(cfg.T), splits=(0,), only_needed_blocks=True)
+
+
+def test_full_deep_ragged_sampled():
+    """The deep-loop ragged batch at full size (batch 128, 8 heads, 32 loop steps, lengths log-uniform in
+    [1024, 16384], random page order), loop steps 0, 15 and 31, checked on the longest and the shortest
+    request: indices of the blocks those steps read, and attention."""
+    import synth.loopvq as syn
+    cfg = loopvq_config("loopvq-deep-ragged")
+    lengths = syn.lengths(cfg)
+    rows = [(int(np.argmax(lengths)), 0), (int(np.argmin(lengths)), cfg.H - 1)]
+    _run_parity(cfg, rows, steps=[0, 15, 31], splits=(0,), only_needed_blocks=True)
 
 
 def test_request_order_sorts_by_length():

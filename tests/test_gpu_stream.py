@@ -1,15 +1,22 @@
 """Streaming decode (the LoopVQ page, Figure 5): tokens appended one at a time to the bf16 window, the
-oldest page encoded every 8 tokens from the window ring, attention at every loop step.  The state after
-streaming must equal, byte for byte, the state a prefill of the same tokens builds (whose indices and
-attention the parity tests check against the oracle), and so must the attention output."""
+oldest page encoded every 8 tokens from the window ring, attention at every loop step.  Checked against the
+oracle: every index the stream writes, and every attention call along the way (at its length then).  The
+state after streaming must also equal, byte for byte, the state a prefill of the same tokens builds, and so
+must the attention output."""
 
 import sys
+
+import types
 
 import numpy as np
 import pytest
 import torch
 
+from oracle import loopvq as lv
 from synth.configs import loopvq_config
+
+REL_TOL = 2e-3
+LSE_TOL = 2e-3
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +39,33 @@ def test_stream_equals_prefill(name, over):
     cfg = loopvq_config(name, **over)
     N = 40                                              # tokens streamed per request (5 pages)
     _say(f"[stream] {cfg.name} B={cfg.B} prefill reference")
-    ref = harness.build_loopvq(cfg)                     # the final state, by prefill
+    rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    ref = harness.build_loopvq(cfg, keep=rows)          # the final state, by prefill
+    geo = lv.Geometry(D=cfg.D, T=cfg.T, Tc=cfg.Tc, G=cfg.G, K=cfg.K, sink=cfg.sink, window=cfg.window,
+                      page=cfg.page)
+    # the oracle's indices of every row at its final length (a shorter length's are a prefix: the encode is
+    # per token)
+    oidx = {(kind, b, h): lv.encode_request(ref.raw[(kind, b, h)], harness.host_codebooks(ref, h, kind), geo,
+                                            ref.lengths[b])
+            for kind in ("k", "v") for (b, h) in rows}
+
+    def check_attend(t, out, lse, lengths):
+        """Every row of an attention call against the oracle at the row's current length."""
+        for (b, h) in rows:
+            L = lengths[b]
+            _, q_lo, q_hi = lv.cache_regions(L, geo)
+            n = q_hi - q_lo
+            q = ref.q[t, b, h].float().cpu().numpy().astype(np.float64)
+            o_ref, l_ref = lv.decode_step(q, t, ref.raw[("k", b, h)], ref.raw[("v", b, h)],
+                                          oidx[("k", b, h)][:, :n], oidx[("v", b, h)][:, :n],
+                                          harness.host_codebooks(ref, h, "k"), harness.host_codebooks(ref, h, "v"),
+                                          geo, L, ref.sm_scale, cfg.rope_base)
+            o = out[b, h].double().cpu().numpy()
+            err = np.abs(o - o_ref).max() / np.abs(o_ref).max()
+            assert err <= REL_TOL, f"step {t} row ({b},{h}) L={L}: rel err {err:.3e}"
+            if lse is not None:
+                assert abs(float(lse[b, h]) - l_ref) <= LSE_TOL, f"step {t} row ({b},{h}): lse {float(lse[b, h])} vs {l_ref}"
+
     g, final = ref.g, ref.lengths
     start = [L - N for L in final]
     total = sum(n_index_pages(L, g) for L in final)
@@ -59,12 +92,21 @@ def test_stream_equals_prefill(name, over):
             v = xs["v"][beta][bidx, :, pos, m].contiguous()
             st.append(t, k, v)
             if i % 13 == 0 or i == N - 1:
-                st.attend(t, ref.q[t].contiguous())
+                lse_i = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device="cuda")
+                out_i, _ = st.attend(t, ref.q[t].contiguous(), lse_out=lse_i)
+                torch.cuda.synchronize()
+                check_attend(t, out_i, lse_i, list(st.len))
     torch.cuda.synchronize()
     assert encoded == sum(n_index_pages(L, g) - n_index_pages(L0, g) for L, L0 in zip(final, start))
     _say(f"[stream] {encoded} pages encoded from the window; compare with the prefill state")
     assert list(st.len) == list(final)
     assert torch.equal(cache.seq_len, ref.cache.seq_len)
+    # every index of the streamed pool against the oracle
+    streamed = types.SimpleNamespace(g=g, cache=cache)
+    for (b, h) in rows:
+        for kind in ("k", "v"):
+            np.testing.assert_array_equal(harness.gpu_indices(streamed, b, h, kind), oidx[(kind, b, h)],
+                                          err_msg=f"streamed indices of ({b},{h}) {kind}")
     for b in range(cfg.B):
         pages = torch.as_tensor(cache.page_table_host[b, :n_index_pages(final[b], g)], dtype=torch.long,
                                 device="cuda")
