@@ -13,6 +13,7 @@ from __future__ import annotations
 import ctypes as C
 from typing import Optional, Tuple
 
+import numpy as np
 import torch
 
 from ._lib import LVQ_BF16, LVQ_FP32, LvqError, check, kivi_cache, kivi_geom, lib, lvq_geom  # noqa: F401
@@ -20,7 +21,8 @@ from . import layout  # noqa: F401
 
 __all__ = [
     "LvqError", "lvq_geom", "kivi_geom", "make_geom", "make_kivi_geom",
-    "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_decode_attn_noalloc", "lvq_request_order", "lvq_window_append",
+    "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_channel_perm_check", "lvq_rope_table_perm",
+    "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_decode_attn_noalloc", "lvq_request_order", "lvq_window_append",
     "lvq_codebook_update",
     "lvq_decode_attn_splits", "lvq_quant_partial", "lvq_quant_partial_workspace", "lvq_window_partial", "splitk_lse_merge", "kivi_append",
     "kivi_decode_attn_workspace", "kivi_decode_attn", "KiviCache", "kivi_widths", "layout",
@@ -99,6 +101,31 @@ def lvq_rope_table_f16(length: int, D: int = 128, base: float = 10000.0, device=
     check(lib.lvq_rope_table_f16(int(length), int(D), float(base), out.data_ptr(), _stream(stream)),
           "lvq_rope_table_f16")
     return out
+
+
+def _perm_array(perm) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(perm, dtype=np.int32))
+
+
+def lvq_channel_perm_check(g: lvq_geom, perm) -> int:
+    """Status of a channel permutation (stored channel j holds original channel perm[j]): LVQ_OK when it maps
+    RoPE pairs to RoPE pairs, else LVQ_ERR_UNSUPPORTED / LVQ_ERR_INVALID_ARG (include/lvq.h)."""
+    p = _perm_array(perm)
+    return int(lib.lvq_channel_perm_check(C.byref(g), p.ctypes.data))
+
+
+def lvq_rope_table_perm(g: lvq_geom, perm, length: int, base: float = 10000.0, device="cuda", packed=True,
+                        stream=None):
+    """(cos, sin, packed fp16 or None) for a channel permutation accepted by lvq_channel_perm_check:
+    frequency column j holds frequency perm[j]."""
+    p = _perm_array(perm)
+    cos = torch.empty((length, g.D // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    f16 = torch.empty((length, 32, 8), dtype=torch.float16, device=device) if packed else None
+    check(lib.lvq_rope_table_perm(C.byref(g), p.ctypes.data, int(length), float(base), cos.data_ptr(),
+                                  sin.data_ptr(), f16.data_ptr() if packed else None, _stream(stream)),
+          "lvq_rope_table_perm")
+    return cos, sin, f16
 
 
 def _rope_f16_ptr(rope_f16: Optional[torch.Tensor], rope_cos: torch.Tensor):

@@ -11,7 +11,8 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblvq.so")
 
 EXPORTS = (
-    "lvq_last_error", "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode",
+    "lvq_last_error", "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_channel_perm_check",
+    "lvq_rope_table_perm", "lvq_encode",
     "lvq_decode_attn_workspace", "lvq_decode_attn_splits", "lvq_decode_attn", "lvq_decode_attn_noalloc",
     "lvq_request_order",
     "lvq_window_append", "lvq_codebook_update",
@@ -58,6 +59,8 @@ def _load():
     lib.lvq_slice_codebooks.argtypes = [C.POINTER(lvq_geom), _P, _P, _P]
     lib.lvq_rope_table.argtypes = [_I, _I, C.c_double, _P, _P, _P]
     lib.lvq_rope_table_f16.argtypes = [_I, _I, C.c_double, _P, _P]
+    lib.lvq_channel_perm_check.argtypes = [C.POINTER(lvq_geom), _P]
+    lib.lvq_rope_table_perm.argtypes = [C.POINTER(lvq_geom), _P, _I, C.c_double, _P, _P, _P, _P]
     lib.lvq_encode.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, C.POINTER(C.c_int64), _P, _P, _P, _P, _I,
                                _P, _P, _I, _I, _P]
     lib.lvq_decode_attn_workspace.restype = _S
@@ -85,7 +88,8 @@ def _load():
     lib.kivi_decode_attn_workspace.argtypes = [C.POINTER(kivi_geom), _I, _I, _I]
     lib.kivi_decode_attn.argtypes = [C.POINTER(kivi_geom), _P, C.POINTER(kivi_cache), _I, C.c_float, _P, _P, _P,
                                      _S, _I, _I, _P]
-    for name in ("lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_encode", "lvq_decode_attn",
+    for name in ("lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_channel_perm_check",
+                 "lvq_rope_table_perm", "lvq_encode", "lvq_decode_attn",
                  "lvq_decode_attn_noalloc",
                  "lvq_request_order", "lvq_window_append", "lvq_codebook_update", "lvq_quant_partial",
                  "lvq_window_partial", "splitk_lse_merge",

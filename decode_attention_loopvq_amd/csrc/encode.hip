@@ -5,6 +5,8 @@
 // index cache, encode after the block's last loop step, one page every 8
 // generated tokens), step 5 (per-step codebook slice B_t cut once at load);
 // background "RoPE" (precomputed cos/sin table).
+#include <vector>
+
 #include "common.h"
 
 #include <cmath>
@@ -37,13 +39,26 @@ __global__ void slice_kernel(const E* __restrict__ cb, E* __restrict__ out, int 
 // ---------------------------------------------------------------------------
 // RoPE table in fp64, rounded once to fp32.
 // ---------------------------------------------------------------------------
+// Frequency of each column of a RoPE table: column i holds frequency f[i] (i itself without a channel
+// permutation).
+constexpr int kMaxHalf = 256;
+struct FreqMap {
+    int16_t f[kMaxHalf];
+};
+
+FreqMap identity_freqs() {
+    FreqMap fm;
+    for (int i = 0; i < kMaxHalf; ++i) fm.f[i] = int16_t(i);
+    return fm;
+}
+
 __global__ void rope_table_kernel(int len, int D, double base, float* __restrict__ cs,
-                                  float* __restrict__ sn) {
+                                  float* __restrict__ sn, const FreqMap fm) {
     const int half = D / 2;
     const long total = long(len) * half;
     for (long e = blockIdx.x * long(blockDim.x) + threadIdx.x; e < total; e += long(gridDim.x) * blockDim.x) {
         const int p = int(e / half), i = int(e % half);
-        const double theta = pow(base, -2.0 * double(i) / double(D));
+        const double theta = pow(base, -2.0 * double(fm.f[i]) / double(D));
         const double a = double(p) * theta;
         cs[e] = float(cos(a));
         sn[e] = float(sin(a));
@@ -68,11 +83,11 @@ __device__ __forceinline__ _Float16 f64_to_f16_rn(double x) {
     return (_Float16)f;
 }
 
-__global__ void rope_f16_kernel(int len, double base, _Float16* __restrict__ out) {
+__global__ void rope_f16_kernel(int len, double base, _Float16* __restrict__ out, const FreqMap fm) {
     const long total = long(len) * 64;
     for (long e = blockIdx.x * long(blockDim.x) + threadIdx.x; e < total; e += long(gridDim.x) * blockDim.x) {
         const int p = int(e / 64), i = int(e % 64);
-        const double theta = pow(base, -2.0 * double(i) / 128.0);
+        const double theta = pow(base, -2.0 * double(fm.f[i]) / 128.0);
         const double ang = double(p) * theta;
         const int m = i >> 2, k = i & 3;
         _Float16* o = out + (long(p) * 32 + m) * 8;
@@ -542,9 +557,10 @@ extern "C" lvq_status lvq_rope_table(int32_t len, int32_t D, double base, float*
     LVQ_REQUIRE(len > 0 && D > 0 && D % 2 == 0, LVQ_ERR_INVALID_ARG, "lvq_rope_table: bad len=%d D=%d", len, D);
     LVQ_REQUIRE(base > 1.0, LVQ_ERR_INVALID_ARG, "lvq_rope_table: base must exceed 1");
     LVQ_REQUIRE(cos_out && sin_out, LVQ_ERR_INVALID_ARG, "lvq_rope_table: NULL pointer");
+    LVQ_REQUIRE(D / 2 <= kMaxHalf, LVQ_ERR_UNSUPPORTED, "lvq_rope_table: D=%d (at most %d)", D, 2 * kMaxHalf);
     const long total = long(len) * (D / 2);
     hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, len, D, base,
-                       cos_out, sin_out);
+                       cos_out, sin_out, identity_freqs());
     return check_launch("lvq_rope_table");
 }
 
@@ -554,8 +570,81 @@ extern "C" lvq_status lvq_rope_table_f16(int32_t len, int32_t D, double base, vo
     LVQ_REQUIRE(base > 1.0, LVQ_ERR_INVALID_ARG, "lvq_rope_table_f16: base must exceed 1");
     LVQ_REQUIRE(out, LVQ_ERR_INVALID_ARG, "lvq_rope_table_f16: NULL pointer");
     hipLaunchKernelGGL(rope_f16_kernel, dim3(grid_for(long(len) * 64, 256)), dim3(256), 0, stream, len, base,
-                       static_cast<_Float16*>(out));
+                       static_cast<_Float16*>(out), identity_freqs());
     return check_launch("lvq_rope_table_f16");
+}
+
+namespace lvq {
+namespace {
+// The checks of lvq_channel_perm_check with error messages naming `fn`.
+lvq_status check_channel_perm(const char* fn, const Geo& g, const int32_t* perm) {
+    LVQ_REQUIRE(perm, LVQ_ERR_INVALID_ARG, "%s: NULL permutation", fn);
+    const int D = g.D, half = D / 2;
+    std::vector<int> seen(D, 0);
+    for (int j = 0; j < D; ++j) {
+        LVQ_REQUIRE(perm[j] >= 0 && perm[j] < D && !seen[perm[j]], LVQ_ERR_INVALID_ARG,
+                    "%s: not a permutation of 0..%d (entry %d = %d)", fn, D - 1, j, perm[j]);
+        seen[perm[j]] = 1;
+    }
+    for (int j = 0; j < half; ++j) {
+        if (perm[j] < half && perm[j + half] == perm[j] + half) continue;
+        // where do the two channels of the RoPE pair of stored channel j sit?
+        const int i = perm[j] < half ? perm[j] : perm[j] - half;
+        int a = -1, b = -1;
+        for (int k = 0; k < D; ++k) {
+            if (perm[k] == i) a = k;
+            if (perm[k] == i + half) b = k;
+        }
+        LVQ_REQUIRE(a / g.c != b / g.c, LVQ_ERR_UNSUPPORTED,
+                    "%s: stored channels %d and %d (RoPE pair %d, %d) fall in one index group of %d channels; "
+                    "the kernels rotate channel j with channel j + %d, a different group", fn, a, b, i, i + half,
+                    g.c, half);
+        LVQ_REQUIRE(false, LVQ_ERR_UNSUPPORTED,
+                    "%s: stored channels %d and %d (RoPE pair %d, %d) are not j and j + %d with the lower one "
+                    "first", fn, a, b, i, i + half, half);
+    }
+    return LVQ_OK;
+}
+}  // namespace
+}  // namespace lvq
+
+extern "C" lvq_status lvq_channel_perm_check(const lvq_geom* gp, const int32_t* perm) {
+    lvq::Geo g;
+    lvq_status st = lvq::validate_geom(gp, &g);
+    if (st != LVQ_OK) return st;
+    return lvq::check_channel_perm("lvq_channel_perm_check", g, perm);
+}
+
+extern "C" lvq_status lvq_rope_table_perm(const lvq_geom* gp, const int32_t* perm, int32_t len, double base,
+                                          float* cos_out, float* sin_out, void* f16_out, hipStream_t stream) {
+    lvq::Geo g;
+    lvq_status st = lvq::validate_geom(gp, &g);
+    if (st != LVQ_OK) return st;
+    st = lvq::check_channel_perm("lvq_rope_table_perm", g, perm);
+    if (st != LVQ_OK) return st;
+    LVQ_REQUIRE(len > 0, LVQ_ERR_INVALID_ARG, "lvq_rope_table_perm: bad len=%d", len);
+    LVQ_REQUIRE(base > 1.0, LVQ_ERR_INVALID_ARG, "lvq_rope_table_perm: base must exceed 1");
+    LVQ_REQUIRE((cos_out != nullptr) == (sin_out != nullptr) && (cos_out || f16_out), LVQ_ERR_INVALID_ARG,
+                "lvq_rope_table_perm: give cos and sin tables, a packed table, or both");
+    LVQ_REQUIRE(g.D / 2 <= kMaxHalf, LVQ_ERR_UNSUPPORTED, "lvq_rope_table_perm: D=%d (at most %d)", g.D,
+                2 * kMaxHalf);
+    LVQ_REQUIRE(!f16_out || g.D == 128, LVQ_ERR_UNSUPPORTED, "lvq_rope_table_perm: packed table for D=%d "
+                "(128 supported)", g.D);
+    FreqMap fm = identity_freqs();
+    for (int j = 0; j < g.D / 2; ++j) fm.f[j] = int16_t(perm[j]);
+    if (cos_out) {
+        const long total = long(len) * (g.D / 2);
+        hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, len, g.D, base,
+                           cos_out, sin_out, fm);
+        st = check_launch("lvq_rope_table_perm");
+        if (st != LVQ_OK) return st;
+    }
+    if (f16_out) {
+        hipLaunchKernelGGL(rope_f16_kernel, dim3(grid_for(long(len) * 64, 256)), dim3(256), 0, stream, len,
+                           base, static_cast<_Float16*>(f16_out), fm);
+        st = check_launch("lvq_rope_table_perm");
+    }
+    return st;
 }
 
 extern "C" lvq_status lvq_encode(const lvq_geom* g, int32_t block, const void* x_k, const void* x_v,

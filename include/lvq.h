@@ -145,6 +145,36 @@ LVQ_API lvq_status lvq_rope_table(int32_t len, int32_t D, double base, float* co
 LVQ_API lvq_status lvq_rope_table_f16(int32_t len, int32_t D, double base, void* out, hipStream_t stream);
 
 /*
+ * Channel permutation P of the cached keys and values (LoopVQ page,
+ * "technical novelty", system level: combined with TaSQ, LoopVQ optimises a
+ * channel permutation P jointly with the grouping).  perm (host, D int32):
+ * stored channel j holds original channel perm[j].  The library serves a
+ * permutation that maps RoPE pairs to RoPE pairs in its rotate-half pairing:
+ * perm[j] < D/2 and perm[j + D/2] == perm[j] + D/2 for every j < D/2.  The
+ * caller then passes permuted keys and values to lvq_encode / the window,
+ * the permuted query q'[j] = q[perm[j]], and RoPE tables whose frequency
+ * column j is frequency perm[j] (lvq_rope_table_perm); attention output
+ * channel j is original value channel perm[j].  The scores are unchanged:
+ * the pair (j, j + D/2) rotates by the angle of original pair perm[j].
+ * Returns LVQ_OK for such a permutation; LVQ_ERR_UNSUPPORTED for any other
+ * permutation, with a message saying so when it puts both channels of a
+ * RoPE pair in one index group (the form the kernels cannot serve: they
+ * rotate group x against group x + NG/2); LVQ_ERR_INVALID_ARG when perm is
+ * NULL or not a permutation of 0 .. D-1.  Host only: touches no device.
+ */
+LVQ_API lvq_status lvq_channel_perm_check(const lvq_geom* g, const int32_t* perm);
+
+/*
+ * lvq_rope_table and (f16_out != NULL) lvq_rope_table_f16 for a channel
+ * permutation that lvq_channel_perm_check accepts: frequency column j
+ * holds frequency perm[j] (cos/sin of p * base^(-2 perm[j] / D)).  cos_out
+ * and sin_out are both given or both NULL; the packed table needs D = 128.
+ * Errors as lvq_channel_perm_check, then as the two table calls.
+ */
+LVQ_API lvq_status lvq_rope_table_perm(const lvq_geom* g, const int32_t* perm, int32_t len, double base,
+                                       float* cos_out, float* sin_out, void* f16_out, hipStream_t stream);
+
+/*
  * Encode index pages of loop block `block` ("method steps", step 4; Figure 5):
  * for each request b and each logical page lp in
  * [first_page[b], first_page[b] + n_pages[b]), the 8 tokens of the page are

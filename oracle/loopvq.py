@@ -302,6 +302,26 @@ def decode_step(q: np.ndarray, t: int, raw_k: np.ndarray, raw_v: np.ndarray,
     return attention(q, k, v, sm_scale)
 
 
+def decode_step_permuted(q: np.ndarray, t: int, raw_k: np.ndarray, raw_v: np.ndarray,
+                         idx_k: np.ndarray, idx_v: np.ndarray, E_k: np.ndarray, E_v: np.ndarray,
+                         geo: Geometry, L: int, sm_scale: float, base: float, perm: np.ndarray
+                         ) -> Tuple[np.ndarray, float]:
+    """decode_step for a cache kept in a permuted channel order (LoopVQ page, technical novelty: with TaSQ, a
+    channel permutation P is optimised together with the grouping).  perm[j] is the original channel stored
+    at channel j; raw_k/raw_v, idx_k/idx_v and E_k/E_v describe the stored channels, q and the returned output
+    are in the original channel order.  The keys and values are rebuilt in the stored order, put back in the
+    original order, and then rotated and attended exactly as in decode_step."""
+    perm = np.asarray(perm)
+    k_st = assemble_step(t, raw_k, idx_k, E_k, geo, L)
+    v_st = assemble_step(t, raw_v, idx_v, E_v, geo, L)
+    k = np.empty_like(k_st)
+    v = np.empty_like(v_st)
+    k[:, perm] = k_st                                   # original channel perm[j] <- stored channel j
+    v[:, perm] = v_st
+    k = apply_rope(k, np.arange(L), base)
+    return attention(q, k, v, sm_scale)
+
+
 def decode_step_two_part(q, t, raw_k, raw_v, idx_k, idx_v, E_k, E_v, geo, L, sm_scale, base=10000.0):
     """The same result computed the way Figure 5 splits it: one partial over
     the index pages, one over the bf16 sinks and recent tokens, then `merge`."""

@@ -239,3 +239,37 @@ def test_noalloc_rejects_before_touching_the_device():
     assert "16777216" in _lib.lib.lvq_last_error().decode()
     assert call(step=9) == INVALID
     assert call(B=0) == OK
+
+
+def test_channel_perm_check():
+    """lvq_channel_perm_check (host only): a permutation that maps RoPE pairs to RoPE pairs passes; swapping a
+    pair's halves, putting both channels of a pair in one index group, or any other break of the pairing is
+    unsupported; a non-permutation or NULL is an argument error.  lvq_rope_table_perm refuses the unsupported
+    forms before touching the device."""
+    import numpy as np
+    g = _geom()
+    f = _lib.lib.lvq_channel_perm_check
+
+    def status(perm):
+        p = np.ascontiguousarray(np.asarray(perm, dtype=np.int32))
+        return f(C.byref(g), p.ctypes.data)
+
+    rng = np.random.default_rng(4)
+    pi = rng.permutation(64)
+    assert status(np.arange(128)) == 0
+    assert status(np.concatenate([pi, pi + 64])) == 0
+    assert status(np.concatenate([np.arange(64, 128), np.arange(64)])) == UNSUPPORTED     # halves swapped
+    # the pair-in-group form: stored channels 2u, 2u + 1 hold RoPE pair (u, u + 64)
+    in_group = np.empty(128, dtype=np.int32)
+    in_group[0::2], in_group[1::2] = np.arange(64), np.arange(64, 128)
+    assert status(in_group) == UNSUPPORTED
+    assert b"one index group" in _lib.lib.lvq_last_error()
+    broken = np.concatenate([pi, pi + 64])
+    broken[[64, 65]] = broken[[65, 64]]                                                      # hi halves crossed
+    assert status(broken) == UNSUPPORTED
+    dup = np.arange(128)
+    dup[5] = 6
+    assert status(dup) == INVALID
+    assert f(C.byref(g), None) == INVALID
+    p = np.ascontiguousarray(in_group)
+    assert _lib.lib.lvq_rope_table_perm(C.byref(g), p.ctypes.data, 100, 10000.0, FAKE, FAKE, FAKE, None) == UNSUPPORTED

@@ -353,6 +353,42 @@ def test_full_deep_ragged_sampled():
     _run_parity(cfg, rows, steps=[0, 15, 31], splits=(0,), only_needed_blocks=True)
 
 
+def test_channel_permutation():
+    """A cache kept in a permuted channel order that maps RoPE pairs to pairs (LoopVQ page, technical novelty:
+    TaSQ+LoopVQ's channel permutation P; a random permutation of the 64 frequencies): the synthetic keys,
+    values and queries taken as the stored channels, RoPE tables from lvq_rope_table_perm.  Every step against
+    the oracle's decode_step_permuted, whose query and output are in the original channel order."""
+    import dataclasses
+
+    import decode_attention_loopvq_amd as lvq
+    from tests import harness
+    cfg = loopvq_config("loopvq-b64-6k", B=3, H=2, L=700)
+    geo = _geo(cfg)
+    rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    p = harness.build_loopvq(cfg, keep=rows)
+    pi = np.random.default_rng(7).permutation(64)
+    perm = np.concatenate([pi, pi + 64]).astype(np.int32)
+    assert lvq.lvq_channel_perm_check(p.g, perm) == 0
+    cos, sin, f16 = lvq.lvq_rope_table_perm(p.g, perm, p.rope_cos.shape[0], cfg.rope_base)
+    pp = dataclasses.replace(p, rope_cos=cos, rope_sin=sin, rope16=f16)
+    idx = {r: _check_indices(p, r[0], r[1], geo) for r in rows}
+    for t in range(cfg.T):
+        lse = torch.empty((cfg.B, cfg.H), dtype=torch.float32, device="cuda")
+        out, _ = harness.run_step(pp, t, lse=lse)
+        torch.cuda.synchronize()
+        for (b, h) in rows:
+            q_orig = np.empty(cfg.D)
+            q_orig[perm] = p.q[t, b, h].float().cpu().numpy().astype(np.float64)
+            o_ref, l_ref = lv.decode_step_permuted(q_orig, t, p.raw[("k", b, h)], p.raw[("v", b, h)],
+                                                   idx[(b, h)]["k"], idx[(b, h)]["v"], lv_cb(p, h, "k"),
+                                                   lv_cb(p, h, "v"), geo, p.lengths[b], p.sm_scale, cfg.rope_base,
+                                                   perm)
+            o = out[b, h].double().cpu().numpy()
+            err = np.abs(o - o_ref[perm]).max() / np.abs(o_ref).max()
+            assert err <= REL_TOL, f"step {t} row ({b},{h}): rel err {err:.3e}"
+            assert abs(float(lse[b, h]) - l_ref) <= LSE_TOL, (t, b, h)
+
+
 def test_request_order_sorts_by_length():
     """lvq_request_order against a stable host sort of the clamped lengths (longest first, ties by index)."""
     import decode_attention_loopvq_amd as lvq

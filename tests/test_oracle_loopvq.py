@@ -412,6 +412,63 @@ def test_lossless_cache_equals_textbook_attention():
 
 
 # ---------------------------------------------------------------------------
+# Channel permutation P (TaSQ+LoopVQ plumbing)
+# ---------------------------------------------------------------------------
+
+def _perm_problem(seed, geo, L):
+    rng = np.random.default_rng(seed)
+    raw_k = _bf16(rng.standard_normal((L, geo.T, geo.D)))
+    raw_v = _bf16(rng.standard_normal((L, geo.T, geo.D)))
+    E_k = _bf16(rng.standard_normal((geo.NB, geo.NG, 256, geo.G)))
+    E_v = _bf16(rng.standard_normal((geo.NB, geo.NG, 256, geo.G)))
+    q = rng.standard_normal(geo.D)
+    return rng, raw_k, raw_v, E_k, E_v, q
+
+
+def test_permuted_decode_with_identity_is_decode_step():
+    """decode_step_permuted with the identity permutation is decode_step (up to the last bit of the BLAS
+    products, which may depend on array layout)."""
+    geo = lv.Geometry(D=128, T=4, Tc=2, G=16)
+    L = 8 + 64 + 8 * 12 + 3
+    _, raw_k, raw_v, E_k, E_v, q = _perm_problem(21, geo, L)
+    idx_k, idx_v = lv.encode_request(raw_k, E_k, geo, L), lv.encode_request(raw_v, E_v, geo, L)
+    for t in range(geo.T):
+        o1, l1 = lv.decode_step(q, t, raw_k, raw_v, idx_k, idx_v, E_k, E_v, geo, L, 0.09, 10000.0)
+        o2, l2 = lv.decode_step_permuted(q, t, raw_k, raw_v, idx_k, idx_v, E_k, E_v, geo, L, 0.09, 10000.0,
+                                         np.arange(geo.D))
+        np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-15)
+        assert abs(l1 - l2) <= 1e-13 * abs(l1)
+
+
+@pytest.mark.parametrize("T,Tc,G", [(4, 2, 16), (4, 4, 32)])
+def test_permuted_cache_of_whole_groups_is_the_same_attention(T, Tc, G):
+    """A permutation that moves whole index groups and maps RoPE pairs to pairs (stored group g' holds original
+    group s(g'), stored group g' + NG/2 original group s(g') + NG/2, s not an involution): storing the cache
+    in that order (raw values, codebooks and indices moved with their groups) and the query in the original
+    order gives the unpermuted attention (up to the last bit of the BLAS products)."""
+    geo = lv.Geometry(D=128, T=T, Tc=Tc, G=G)
+    L = 8 + 64 + 8 * 12 + 3
+    rng, raw_k, raw_v, E_k, E_v, q = _perm_problem(22, geo, L)
+    idx_k, idx_v = lv.encode_request(raw_k, E_k, geo, L), lv.encode_request(raw_v, E_v, geo, L)
+    c, NG = geo.c, geo.NG
+    half = NG // 2
+    lo = rng.permutation(half)
+    while np.all(lo[lo] == np.arange(half)):            # not an involution, so a transposed use differs
+        lo = rng.permutation(half)
+    sigma = np.concatenate([lo, lo + half])             # stored group -> original group
+    perm = (sigma[:, None] * c + np.arange(c)[None, :]).reshape(-1)   # stored channel -> original channel
+    assert np.array_equal(perm[64:], perm[:64] + 64)
+    st = dict(raw_k=raw_k[:, :, perm], raw_v=raw_v[:, :, perm], E_k=E_k[:, sigma], E_v=E_v[:, sigma],
+              idx_k=idx_k[:, :, sigma], idx_v=idx_v[:, :, sigma])
+    for t in range(geo.T):
+        o1, l1 = lv.decode_step(q, t, raw_k, raw_v, idx_k, idx_v, E_k, E_v, geo, L, 0.09, 10000.0)
+        o2, l2 = lv.decode_step_permuted(q, t, st["raw_k"], st["raw_v"], st["idx_k"], st["idx_v"], st["E_k"],
+                                         st["E_v"], geo, L, 0.09, 10000.0, perm)
+        np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-15)
+        assert abs(l1 - l2) <= 1e-13 * abs(l1)
+
+
+# ---------------------------------------------------------------------------
 # Key scale stream (TaSQ+LoopVQ plumbing)
 # ---------------------------------------------------------------------------
 
