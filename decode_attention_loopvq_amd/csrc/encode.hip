@@ -328,6 +328,10 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
     __shared__ __align__(16) uint8_t idx[kEncTile * kEncTilesPerWg][8];
     // per wave and tile, the tokens whose best two scores lie within the error bound (bit n: token t0 + n)
     __shared__ uint16_t near_tok[8][kEncTilesPerWg];
+    // the operand chunks (lane q's 8 coordinates) of the first such token of a wave's first kStash tiles
+    // that have one, in tile order
+    constexpr int kStash = 8;
+    __shared__ __align__(16) uint4 zstash[8][kStash][4];
     // -||e_r||^2 / 2 of the wave's group in codeword order (each wave writes and reads only its own row)
     __shared__ __align__(16) float cnorm[8][256];
     {
@@ -338,8 +342,9 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
     // Error bound of a score (sums in fp32; products of bf16 values exact): |s^ - s| <= eps =
     // kScoreErr * (||z|| E + E^2), E the largest codeword norm of the group.  kScoreErr is twice the fp32
     // bound gamma_32 = 32 * 2^-24 / (1 - 32 * 2^-24) of a 33-term sum, which also covers an accumulation that
-    // does not round to nearest.  Where the best and second-best scores of a token differ by more than 2 eps,
-    // the best is the exact nearest codeword.
+    // does not round to nearest, plus 5% for the rounding of eps itself (zsq, the square root); E^2 in place
+    // of E^2 / 2 covers the rounding of the norms.  Where the best and second-best scores of a token differ
+    // by more than 2 eps, the best is the exact nearest codeword.
     constexpr float kScoreErr = 4.0e-6f;
     float e2max = 0.f;
 #pragma unroll
@@ -347,33 +352,104 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
     e2max = __builtin_amdgcn_readfirstlane(wave_max(e2max));
     const float emax = __builtin_amdgcn_readfirstlane(sqrtf(e2max));
     // Tile of 16 tokens with the codewords as rows: lane (q, n) gets the scores of token t0 + n for
-    // codewords 16t + 4q + i (t < 16, i < 4), keeps its best (scanning in increasing codeword order with a
-    // strict >, so the lowest index wins equal values) and its second best (a median of three), then the best
-    // two of the 4 lanes n, n + 16, n + 32, n + 48 through two lane swaps.  Tokens whose best two lie within
-    // 2 eps are decided again by exact distances (recheck).
+    // codewords 16t + 4q + i (t < 16, i < 4) and keeps its best two: per MFMA output the maximum of its 4
+    // scores against the running best, the 4 scores of the best output so far kept, and the second best
+    // among the other outputs' maxima (a median of three); at the end the best and second of the kept 4
+    // resolve the lane's pair.  Then the best two of the 4 lanes n, n + 16, n + 32, n + 48 through two lane
+    // swaps.  Equal scores need no order here: a token whose best two lie within 2 eps (equal ones
+    // included) is decided again by exact distances (recheck).
     auto merge = [](float& best, float& second, int& r, float ob, float os, int orr) {
-        const bool take = ob > best || (ob == best && orr < r);
+        const bool take = ob > best;                     // (equal scores: flagged, so either index serves)
         second = __builtin_amdgcn_fmed3f(best, ob, fmaxf(second, os));   // max(min(best, ob), second, os)
         best = take ? ob : best;
         r = take ? orr : r;
     };
+    // The nearest codeword of one token by direct differences in fp64, from registers: lane (q, n) takes its
+    // 16 codewords 16 t + n over coordinates 8 q .. 8 q + 7 (its operand fragments), summed in coordinate
+    // order, against the token's same coordinates (zw, as the tile's operand); the four chunks of each
+    // codeword are added across the lanes n, n + 16, n + 32, n + 48 in a fixed order; then the minimum over
+    // the 256 codewords, the lowest index among equal distances.
+    auto recheck = [&](const uint4& zw) {
+        const uint32_t zc[4] = {zw.x, zw.y, zw.z, zw.w};
+        double zd[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) zd[u] = double((u & 1) ? bf16_hi(zc[u >> 1]) : bf16_lo(zc[u >> 1]));
+        double bd = 0.0;
+        int br = -1;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            // opaque copy: the conversions below stay here instead of being hoisted out of the callers' loops
+            // as 256 doubles held in registers
+            const uint4 ew = __builtin_bit_cast(uint4, bfr[t]);
+            uint32_t e4[4] = {ew.x, ew.y, ew.z, ew.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(e4[u]));
+            double d = 0.0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const double diff = zd[u] - double((u & 1) ? bf16_hi(e4[u >> 1]) : bf16_lo(e4[u >> 1]));
+                d = fma(diff, diff, d);
+            }
+            // chunks q and q ^ 2 (lane swap of 32), then the pairs (lane swap of 16): ((d0 + d2) + (d1 + d3))
+            const uint64_t db = __builtin_bit_cast(uint64_t, d);
+            const auto l32 = __builtin_amdgcn_permlane32_swap(uint32_t(db), uint32_t(db), false, false);
+            const auto h32 = __builtin_amdgcn_permlane32_swap(uint32_t(db >> 32), uint32_t(db >> 32), false, false);
+            const double a0 = __builtin_bit_cast(double, (uint64_t(uint32_t(h32[0])) << 32) | uint32_t(l32[0]));
+            const double a1 = __builtin_bit_cast(double, (uint64_t(uint32_t(h32[1])) << 32) | uint32_t(l32[1]));
+            const double s2 = q < 2 ? a0 + a1 : a1 + a0;           // chunk q first: the same sum in both lanes
+            const uint64_t sb = __builtin_bit_cast(uint64_t, s2);
+            const auto l16 = __builtin_amdgcn_permlane16_swap(uint32_t(sb), uint32_t(sb), false, false);
+            const auto h16 = __builtin_amdgcn_permlane16_swap(uint32_t(sb >> 32), uint32_t(sb >> 32), false, false);
+            const double b0 = __builtin_bit_cast(double, (uint64_t(uint32_t(h16[0])) << 32) | uint32_t(l16[0]));
+            const double b1 = __builtin_bit_cast(double, (uint64_t(uint32_t(h16[1])) << 32) | uint32_t(l16[1]));
+            const double tot = (q & 1) == 0 ? b0 + b1 : b1 + b0;
+            if (br < 0 || tot < bd) { bd = tot; br = 16 * t + n; }
+            __builtin_amdgcn_sched_barrier(0);           // one codeword row at a time: few live registers
+        }
+        // across the 16 codeword rows n of a row of lanes (the q copies agree): partners l ^ 1, l ^ 2 (quad
+        // permutes), then 7 - l and 15 - l within the row (half-row and row mirrors); the lexicographic
+        // minimum of (distance, index) is symmetric, so both lanes of a pair keep the same result
+        auto step = [&](auto partner) {
+            const uint64_t db = __builtin_bit_cast(uint64_t, bd);
+            const double od = __builtin_bit_cast(double, (uint64_t(uint32_t(partner(int(db >> 32)))) << 32) |
+                                                         uint32_t(partner(int(uint32_t(db)))));
+            const int orr = partner(br);
+            const bool take = od < bd || (od == bd && orr < br);
+            bd = take ? od : bd;
+            br = take ? orr : br;
+        };
+        step([](int x) { return dpp_i<0xB1>(x); });      // quad_perm [1, 0, 3, 2]
+        step([](int x) { return dpp_i<0x4E>(x); });      // quad_perm [2, 3, 0, 1]
+        step([](int x) { return dpp_i<0x141>(x); });     // row_half_mirror
+        step([](int x) { return dpp_i<0x140>(x); });     // row_mirror
+        return __builtin_amdgcn_readfirstlane(br);
+    };
+    uint64_t any_near = 0;                               // some token of the wave's tiles near a tie
+    int n_tiles_near = 0;                                // tiles with such tokens so far (wave-uniform)
     auto tile_fn = [&](int t0, const RawA& raw) {
         const bf16x8_t Bcur = build_a(raw);
         const float* cn = &cnorm[tid >> 6][4 * q];
         // each tile of scores is scanned four MFMAs after it is issued, so that few accumulators are live
         constexpr int kLag = 4;
         f32x4_t acc[16];
-        float best = -INFINITY, second = -INFINITY;
-        int r = 4 * q;
+        float best = -INFINITY, sec = -INFINITY;
+        float w0 = -INFINITY, w1 = -INFINITY, w2 = -INFINITY, w3 = -INFINITY;
+        int rt = 0;
+        // maxima as medians with +inf: three-way ones become single max3 instructions (a two-way maximum of
+        // raw MFMA results would be preceded by canonicalising moves)
+        auto fmax2 = [](float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); };
         auto scan = [&](int t) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = acc[t][i];
-                const bool gt = v > best;
-                second = __builtin_amdgcn_fmed3f(best, second, v);
-                r = gt ? 16 * t + 4 * q + i : r;
-                best = gt ? v : best;
-            }
+            const float v0 = acc[t][0], v1 = acc[t][1], v2 = acc[t][2], v3 = acc[t][3];
+            const float m3 = fmax2(fmax2(v0, v1), v2);
+            const float nb = fmax2(fmax2(best, m3), v3);         // max(best, the output's maximum)
+            const bool gt = nb > best;
+            sec = gt ? best : fmax2(fmax2(sec, m3), v3);
+            best = nb;
+            rt = gt ? t : rt;
+            w0 = gt ? v0 : w0;
+            w1 = gt ? v1 : w1;
+            w2 = gt ? v2 : w2;
+            w3 = gt ? v3 : w3;
         };
 #pragma unroll
         for (int t = 0; t < 16 + kLag; ++t) {
@@ -382,6 +458,17 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[t], Bcur, ci, 0, 0, 0);
             }
             if (t >= kLag) scan(t - kLag);
+        }
+        // the lane's best two: the kept output's largest (its index) and the larger of its second largest
+        // and the other outputs' best
+        float second;
+        int r;
+        {
+            const float a01 = fmax2(w0, w1), a23 = fmax2(w2, w3);
+            const float b01 = fminf(w0, w1), b23 = fminf(w2, w3);
+            second = fmax2(sec, __builtin_amdgcn_fmed3f(a01, a23, fmax2(b01, b23)));
+            const int i = a01 >= a23 ? (w0 >= w1 ? 0 : 1) : (w2 >= w3 ? 2 : 3);
+            r = 16 * rt + 4 * q + i;
         }
         {   // lanes l and l ^ 32, then l and l ^ 16 (the combine is symmetric, so both lanes of a pair agree)
             const auto bv = __builtin_amdgcn_permlane32_swap(__float_as_uint(best), __float_as_uint(best), false, false);
@@ -413,13 +500,22 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
                 zsq = fmaf(bf16_lo(w4[u]), bf16_lo(w4[u]), zsq);
                 zsq = fmaf(bf16_hi(w4[u]), bf16_hi(w4[u]), zsq);
             }
-            zsq += __shfl_xor(zsq, 16, 64);
-            zsq += __shfl_xor(zsq, 32, 64);
+            // the column's other lanes (l ^ 32, l ^ 16) through lane swaps, no LDS traffic
+            const auto a32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(zsq), __float_as_uint(zsq), false, false);
+            zsq = __uint_as_float(a32[0]) + __uint_as_float(a32[1]);
+            const auto a16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(zsq), __float_as_uint(zsq), false, false);
+            zsq = __uint_as_float(a16[0]) + __uint_as_float(a16[1]);
         }
-        const float eps = kScoreErr * (sqrtf(zsq) * emax + e2max);
+        const float eps = kScoreErr * (__builtin_amdgcn_sqrtf(zsq) * emax + e2max);
         const uint64_t near = __builtin_amdgcn_ballot_w64(q == 0 && best - second <= 2.f * eps);
         if (q == 0) idx[(t0 - tok_base) + n][grp & 7] = uint8_t(r);
         if (lane == 0) near_tok[tid >> 6][(t0 - tok_base) / kEncTile] = uint16_t(near);
+        any_near |= near;
+        // (straight-line code: a loop here would make the compiler wait for the next tile's loads)
+        if (near != 0 && n_tiles_near < kStash) {       // rare: the tile's first such token stashed
+            if (n == int(__builtin_ctzll(near))) zstash[tid >> 6][n_tiles_near][q] = bw;
+            ++n_tiles_near;
+        }
     };
     // two alternating buffers: the loads of tile k+1 are in flight while tile k computes
     RawA rawA = load_a(tok_base + n), rawB;
@@ -431,53 +527,17 @@ __global__ void __launch_bounds__(512) encode_mfma_kernel(EncArgs a) {
         rawA = load_a(t0 + 2 * kEncTile + n);
         tile_fn(t0 + kEncTile, rawB);
     }
-    // The tokens marked near a tie: the nearest codeword again, by direct differences in fp64 summed in
-    // coordinate order (as the definition writes it) over all 256 codewords; lane k < G loads coordinate k of
-    // the coupled vector, each lane takes codewords lane + 64 i, then the wave's minimum, the lowest index
-    // among equal distances.
-    for (int tt = 0; tt * kEncTile < t_end - tok_base; ++tt) {
+    // The tokens marked near a tie, decided again (rare), in tile order: stashed chunks where there are,
+    // the coordinates loaded again for the others.
+    for (int tt = 0, k = 0; any_near != 0 && tt * kEncTile < t_end - tok_base; ++tt) {
         uint32_t near = near_tok[tid >> 6][tt];
-        while (near != 0) {
-            const int nf = __builtin_ctz(near);
-            near &= near - 1;
-            const int j = tok_base + tt * kEncTile + nf;
-            const uint16_t* xr = nullptr;
-            if constexpr (XREQ) {
-                int bu, ju;
-                if (!slot(j, bu, ju)) continue;             // a slot without a token: nothing to decide
-                xr = x + xbase + long(bu) * a.s0 + ((a.tok0 ? a.tok0[bu] : 0) + ju) * a.s2;
-            } else {
-                xr = x + xbase + (row0 + j) * a.s2;
-            }
-            // xbase points at this lane's first coordinate (8 q / TC channels in); step back to the group's
-            const uint16_t* xg = xr - (kin ? (8 * q) / TC : 0);
-            const int kl = lane < G ? lane : 0;
-            const float zl = bf16_to_f32(xg[long(kl % TC) * a.s3 + kl / TC]);
-            const uint16_t* eg = a.cb + ((((long(a.block) * g.H + h) * 2 + kv) * g.NG + grp) * g.K) * long(G);
-            double bd = 0.0;
-            int br = -1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = lane + 64 * i;
-                const uint16_t* er = eg + long(rr) * G;
-                double d = 0.0;
-#pragma unroll
-                for (int k = 0; k < 32; ++k) {
-                    if (k < G) {
-                        const float zk = __shfl(zl, k, 64);
-                        const double diff = double(zk) - double(bf16_to_f32(er[k]));
-                        d = fma(diff, diff, d);
-                    }
-                }
-                if (br < 0 || d < bd) { bd = d; br = rr; }
-            }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const double od = __shfl_xor(bd, off, 64);
-                const int orr = __shfl_xor(br, off, 64);
-                if (od < bd || (od == bd && orr < br)) { bd = od; br = orr; }
-            }
-            if (lane == 0) idx[j - tok_base][grp & 7] = uint8_t(br);
+        for (bool first = true; near != 0; near &= near - 1, first = false) {
+            const int j = tok_base + tt * kEncTile + __builtin_ctz(near);
+            const bool stashed = first && k < kStash;
+            k += first ? 1 : 0;
+            const uint4 zw = stashed ? zstash[tid >> 6][max(k - 1, 0)][q] : __builtin_bit_cast(uint4, build_a(load_a(j)));
+            const int rx = recheck(zw);
+            if (lane == 0) idx[j - tok_base][grp & 7] = uint8_t(rx);
         }
     }
     __syncthreads();
