@@ -96,8 +96,8 @@ def lvq_rope_table(length: int, D: int = 128, base: float = 10000.0, device="cud
 
 def lvq_rope_table_f16(length: int, D: int = 128, base: float = 10000.0, device="cuda",
                        stream=None) -> torch.Tensor:
-    """Packed fp16 cos/sin [length][32][8] for the index-page pass (layout in include/lvq.h)."""
-    out = torch.empty((length, 32, 8), dtype=torch.float16, device=device)
+    """Packed fp16 cos/sin for the index-page pass, 384 halves per position (layout in include/lvq.h)."""
+    out = torch.empty((length * 384,), dtype=torch.float16, device=device)
     check(lib.lvq_rope_table_f16(int(length), int(D), float(base), out.data_ptr(), _stream(stream)),
           "lvq_rope_table_f16")
     return out
@@ -121,7 +121,7 @@ def lvq_rope_table_perm(g: lvq_geom, perm, length: int, base: float = 10000.0, d
     p = _perm_array(perm)
     cos = torch.empty((length, g.D // 2), dtype=torch.float32, device=device)
     sin = torch.empty_like(cos)
-    f16 = torch.empty((length, 32, 8), dtype=torch.float16, device=device) if packed else None
+    f16 = torch.empty((length * 384,), dtype=torch.float16, device=device) if packed else None
     check(lib.lvq_rope_table_perm(C.byref(g), p.ctypes.data, int(length), float(base), cos.data_ptr(),
                                   sin.data_ptr(), f16.data_ptr() if packed else None, _stream(stream)),
           "lvq_rope_table_perm")
@@ -132,8 +132,8 @@ def _rope_f16_ptr(rope_f16: Optional[torch.Tensor], rope_cos: torch.Tensor):
     if rope_f16 is None:
         return None
     _need(rope_f16, "rope_f16", torch.float16)
-    if tuple(rope_f16.shape) != (rope_cos.shape[0], 32, 8):
-        raise ValueError("rope_f16 must be [rope_len][32][8] with the rope_cos length")
+    if rope_f16.numel() != rope_cos.shape[0] * 384:
+        raise ValueError("rope_f16 must hold 384 halves per position of rope_cos (lvq_rope_table_f16)")
     return rope_f16.data_ptr()
 
 
@@ -225,7 +225,8 @@ def lvq_decode_attn(g: lvq_geom, step: int, q: torch.Tensor, pool: torch.Tensor,
                     stream=None, rope_f16: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None,
                     k_scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Decode attention of loop step `step`; returns (out [B][H][D] fp32, lse [B][H] or None).
-    rope_f16 (lvq_rope_table_f16) is required with bf16 codebooks; order (int32 [B], e.g. from
+    rope_f16 (lvq_rope_table_f16) is optional: without it, bf16 codebooks have the packed table built from
+    rope_cos / rope_sin in the workspace on every call; order (int32 [B], e.g. from
     lvq_request_order) groups the requests into workgroups (None: in batch order); k_scales (fp16
     [physical pages][T][8]) is the key scale stream of the index tokens (None: no scales)."""
     _need(q, "q", torch.bfloat16)

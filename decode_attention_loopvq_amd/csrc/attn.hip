@@ -46,7 +46,7 @@ struct AttnArgs {
     const uint16_t* kscale;     // key scale stream fp16 [physical page][T][8] (NULL: none)
     int rope_len;
     const uint32_t* qpack;      // [B*H][64] packed fp16 query rows (written and read by index_attn_kernel)
-    const uint4* rope16;        // [16][rope_len] packed fp16 cos/sin chunks (lvq_rope_table_f16)
+    const uint4* rope16;        // packed fp16 cos/sin (lvq_rope_table_f16; parts A and B, common.h)
     int fix_bits;               // fixed-point fraction bits of the softmax weights in the V bins
 };
 
@@ -604,11 +604,12 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
 
     // ---- scores ----
     uint4 tr[16];                                   // cos/sin of the lane's position, 4 frequencies each
+    const uint4* rope_b = a.rope16 + long(a.rope_len) * 32;   // the table's chunk-major part
     auto load_tr = [&](int c, auto qc) {
         constexpr int qq = decltype(qc)::value;
         const int p = min(g.sink + c * kChunk + lane, a.rope_len - 1);
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) tr[4 * qq + mm] = a.rope16[long(p) * 32 + 4 * qq + mm];
+        for (int mm = 0; mm < 4; ++mm) tr[4 * qq + mm] = rope_b[long(4 * qq + mm) * a.rope_len + p];
     };
     // Group of the i-th codeword gathered in quarter qq: lo groups first, then the hi groups holding
     // channels 64 + (the same frequencies).
@@ -1660,6 +1661,12 @@ int pages_per_split(int max_pages, int S) { return max_pages > 0 ? ceil_div(ceil
 // Scratch of the index-page partial (bf16 codebooks): the packed query rows, 256 B per (request, head).
 size_t quant_scratch_bytes(const Geo& g, int B) { return size_t(B) * g.H * 64 * sizeof(uint32_t); }
 
+// Bytes of the packed fp16 RoPE table built in the workspace for a call given none (bf16 codebooks),
+// positions 0 .. max_len - 1, rounded up to 256.
+size_t rope_scratch_bytes(const Geo& g, int max_len) {
+    return g.cb == LVQ_BF16 ? (size_t(max_len) * kRopeF16HalvesPerPos * 2 + 255) / 256 * 256 : 0;
+}
+
 // Bytes of the partials (part_o, part_lse) of S_tot slots per row, rounded up to 256 so that the
 // scratch after them starts on a whole cache line.
 size_t partials_bytes(const Geo& g, int B, int S_tot) {
@@ -1687,13 +1694,13 @@ extern "C" size_t lvq_decode_attn_workspace(const lvq_geom* gp, int32_t B, int32
     Geo g;
     if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 0 || num_splits < 0) return 0;
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
-    return partials_bytes(g, B, S + 1) + quant_scratch_bytes(g, B);
+    return partials_bytes(g, B, S + 1) + quant_scratch_bytes(g, B) + rope_scratch_bytes(g, max_len);
 }
 
 extern "C" size_t lvq_quant_partial_workspace(const lvq_geom* gp, int32_t B, int32_t max_len) {
     Geo g;
     if (validate_geom(gp, &g) != LVQ_OK || B < 0 || max_len < 0) return 0;
-    return quant_scratch_bytes(g, B);
+    return quant_scratch_bytes(g, B) + rope_scratch_bytes(g, max_len);
 }
 
 namespace lvq {
@@ -1703,7 +1710,7 @@ namespace {
 // except the partial buffers.
 lvq_status prepare(const char* fn, const lvq_geom* gp, int32_t step, const void* q, const int32_t* seq_len,
                    int32_t max_len, const float* rope_cos, const float* rope_sin, const void* rope_f16,
-                   int32_t rope_len, float sm_scale, int32_t B, AttnArgs* a, bool need_f16 = true) {
+                   int32_t rope_len, float sm_scale, int32_t B, AttnArgs* a) {
     Geo& g = a->geo;
     lvq_status st = validate_geom(gp, &g);
     if (st != LVQ_OK) return st;
@@ -1714,20 +1721,40 @@ lvq_status prepare(const char* fn, const lvq_geom* gp, int32_t step, const void*
     LVQ_REQUIRE(std::isfinite(sm_scale), LVQ_ERR_INVALID_ARG, "%s: sm_scale not finite", fn);
     LVQ_REQUIRE(B <= 65535, LVQ_ERR_UNSUPPORTED, "%s: batch too large", fn);
     LVQ_REQUIRE(B == 0 || (q && seq_len && rope_cos && rope_sin), LVQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-    LVQ_REQUIRE(B == 0 || !need_f16 || g.cb != LVQ_BF16 || rope_f16, LVQ_ERR_INVALID_ARG,
-                "%s: bf16 codebooks need the packed fp16 RoPE table", fn);
     a->step = step;
     a->beta = step / g.Tc;
     a->q = static_cast<const uint16_t*>(q);
     a->seq_len = seq_len;
     a->rc = rope_cos;
     a->rs = rope_sin;
-    a->rope16 = static_cast<const uint4*>(rope_f16);
+    a->rope16 = g.cb == LVQ_BF16 ? static_cast<const uint4*>(rope_f16) : nullptr;
     a->scale_log2 = sm_scale * kLog2e;
     a->B = B;
     a->max_len = max_len;
     a->rope_len = rope_len;
     return LVQ_OK;
+}
+
+// The packed fp16 RoPE table (common.h) from the caller's fp32 cos/sin, for a call given none: each value
+// rounded once from fp32 to binary16 (which can differ from the fp64 value rounded once, as
+// lvq_rope_table_f16 builds it, only where the fp32 value lies on a binary16 rounding midpoint).
+__global__ void rope_pack_kernel(const float* __restrict__ rc, const float* __restrict__ rs, int len,
+                                 _Float16* __restrict__ out) {
+    const long total = long(len) * 64;
+    for (long e = blockIdx.x * long(blockDim.x) + threadIdx.x; e < total; e += long(gridDim.x) * blockDim.x)
+        store_rope_f16(out, len, e >> 6, int(e & 63), (_Float16)rc[e], (_Float16)rs[e]);
+}
+
+// For bf16 codebooks without a packed table: builds one for positions 0 .. max_len - 1 at `table`
+// (rope_scratch_bytes) and points the kernels at it.
+lvq_status pack_rope_if_needed(AttnArgs& a, void* table, hipStream_t stream) {
+    if (a.geo.cb != LVQ_BF16 || a.rope16) return LVQ_OK;
+    const long total = long(a.max_len) * 64;
+    hipLaunchKernelGGL(rope_pack_kernel, dim3(unsigned(std::min<long>((total + 255) / 256, 2048))), dim3(256), 0,
+                       stream, a.rc, a.rs, a.max_len, static_cast<_Float16*>(table));
+    a.rope16 = static_cast<const uint4*>(table);
+    a.rope_len = a.max_len;
+    return check_launch("packed RoPE table");
 }
 
 // Launches the index-page partial; `scratch` (256-byte aligned) holds the packed query rows.
@@ -1799,9 +1826,9 @@ extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const 
     if (B == 0) return LVQ_OK;
     const int max_pages = max_index_pages(g, max_len);
     LVQ_REQUIRE(slices && part_o && part_lse && ws, LVQ_ERR_INVALID_ARG, "lvq_quant_partial: NULL pointer");
-    LVQ_REQUIRE(ws_bytes >= lvq_quant_partial_workspace(gp, B, max_len), LVQ_ERR_WORKSPACE,
-                "lvq_quant_partial: workspace %zu < %zu bytes", ws_bytes,
-                lvq_quant_partial_workspace(gp, B, max_len));
+    const size_t need = quant_scratch_bytes(g, B) + (a.rope16 ? 0 : rope_scratch_bytes(g, max_len));
+    LVQ_REQUIRE(ws_bytes >= need, LVQ_ERR_WORKSPACE, "lvq_quant_partial: workspace %zu < %zu bytes", ws_bytes,
+                need);
     LVQ_REQUIRE(max_pages == 0 || (pool && page_table), LVQ_ERR_INVALID_ARG,
                 "lvq_quant_partial: NULL pool or page table");
     LVQ_REQUIRE(pt_stride >= max_pages, LVQ_ERR_INVALID_ARG, "lvq_quant_partial: pt_stride %d < %d pages",
@@ -1820,6 +1847,8 @@ extern "C" lvq_status lvq_quant_partial(const lvq_geom* gp, int32_t step, const 
     a.S_tot = S_tot;
     a.num_splits = num_splits;
     a.pps = pages_per_split(max_pages, num_splits);
+    if ((st = pack_rope_if_needed(a, static_cast<unsigned char*>(ws) + quant_scratch_bytes(g, B), stream)) != LVQ_OK)
+        return st;
     return launch_quant(a, ws, stream);
 }
 
@@ -1830,7 +1859,7 @@ extern "C" lvq_status lvq_window_partial(const lvq_geom* gp, int32_t step, const
                                          int32_t S_tot, int32_t B, hipStream_t stream) {
     AttnArgs a{};
     lvq_status st = prepare("lvq_window_partial", gp, step, q, seq_len, max_len, rope_cos, rope_sin, nullptr,
-                            rope_len, sm_scale, B, &a, false);
+                            rope_len, sm_scale, B, &a);
     if (st != LVQ_OK) return st;
     LVQ_REQUIRE(slot >= 0 && slot < S_tot, LVQ_ERR_INVALID_ARG, "lvq_window_partial: slot %d of %d", slot, S_tot);
     if (B == 0) return LVQ_OK;
@@ -1872,7 +1901,9 @@ lvq_status decode_attn_impl(const char* fn, const lvq_geom* gp, int32_t step, co
     const int S = num_splits > 0 ? num_splits : choose_splits(g, B, max_len);
     LVQ_REQUIRE(splits_fit(g, max_pages, S), LVQ_ERR_INVALID_ARG,
                 "%s: %d splits of %d index pages exceed %d tokens per split", fn, S, max_pages, kMaxSplitTok);
-    const size_t need = lvq_decode_attn_workspace(gp, B, max_len, num_splits);
+    // (the room for a packed RoPE table only when the call brings none)
+    const size_t need = partials_bytes(g, B, S + 1) + quant_scratch_bytes(g, B) +
+                        (a.rope16 ? 0 : rope_scratch_bytes(g, max_len));
     if (provider && (st = provider(need, &ws, &ws_bytes)) != LVQ_OK) return st;
     LVQ_REQUIRE(ws, LVQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     LVQ_REQUIRE(ws_bytes >= need, LVQ_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
@@ -1891,8 +1922,9 @@ lvq_status decode_attn_impl(const char* fn, const lvq_geom* gp, int32_t step, co
     a.S_tot = S + 1;
     a.num_splits = S;
     a.pps = pages_per_split(max_pages, S);
-    if ((st = launch_quant(a, static_cast<unsigned char*>(ws) + partials_bytes(g, B, S + 1), stream)) != LVQ_OK)
-        return st;
+    unsigned char* scratch = static_cast<unsigned char*>(ws) + partials_bytes(g, B, S + 1);
+    if ((st = pack_rope_if_needed(a, scratch + quant_scratch_bytes(g, B), stream)) != LVQ_OK) return st;
+    if ((st = launch_quant(a, scratch, stream)) != LVQ_OK) return st;
     return launch_window(a, out, lse_out, stream);
 }
 

@@ -49,6 +49,27 @@ __device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
     return h;
 }
 
+// ---------------------------------------------------------------------------
+// The packed fp16 RoPE table of the index-page kernels (D = 128), 384 halves (768 B) per position, in two
+// parts: part A [rope_len][32 chunks][8] (chunk m < 16 of position p: cos of frequencies
+// 4m .. 4m+3, then sin of the same; chunk 16 + m: the same with the sines negated), read by the c = 8
+// kernel, whose lanes take a position's chunks together; part B [16 chunks][rope_len][8] (chunks m < 16
+// again, chunk-major), read by the c = 4 kernel, whose lanes of one load hold consecutive positions.
+// ---------------------------------------------------------------------------
+constexpr long kRopeF16HalvesPerPos = 384;
+__device__ __forceinline__ void store_rope_f16(_Float16* __restrict__ out, long len, long p, int i, _Float16 c,
+                                               _Float16 s) {
+    const int m = i >> 2, k = i & 3;
+    _Float16* a = out + (p * 32 + m) * 8;
+    a[k] = c;
+    a[4 + k] = s;
+    a[16 * 8 + k] = c;
+    a[16 * 8 + 4 + k] = -s;
+    _Float16* b = out + len * 256 + (m * len + p) * 8;
+    b[k] = c;
+    b[4 + k] = s;
+}
+
 // Wave64 reductions through cross-lane moves.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -89,13 +89,7 @@ __global__ void rope_f16_kernel(int len, double base, _Float16* __restrict__ out
         const int p = int(e / 64), i = int(e % 64);
         const double theta = pow(base, -2.0 * double(fm.f[i]) / 128.0);
         const double ang = double(p) * theta;
-        const int m = i >> 2, k = i & 3;
-        _Float16* o = out + (long(p) * 32 + m) * 8;
-        const _Float16 c = f64_to_f16_rn(cos(ang)), sn = f64_to_f16_rn(sin(ang));
-        o[k] = c;
-        o[4 + k] = sn;
-        o[16 * 8 + k] = c;
-        o[16 * 8 + 4 + k] = -sn;
+        store_rope_f16(out, len, p, i, f64_to_f16_rn(cos(ang)), f64_to_f16_rn(sin(ang)));
     }
 }
 

@@ -109,10 +109,14 @@ LVQ_API const char* lvq_last_error(void);
  *             K (and separately V) of every loop step; position p < sink sits
  *             in slot p, position p >= sink in slot sink + (p - sink) % (W + page)
  *  rope       cos, sin fp32 [rope_len][D/2]: cos/sin(p * base^(-2i/D))
- *  rope_f16   packed fp16 copy for the index-page kernels (D = 128):
- *             [rope_len][32 chunks][8 halves]; chunk m < 16 of position p
- *             holds cos of frequencies 4m..4m+3, then sin of the same four;
- *             chunk 16 + m the same with the sines negated
+ *  rope_f16   packed fp16 copy for the index-page kernels (D = 128), 384
+ *             halves (768 bytes) per position in two parts: part A
+ *             [rope_len][32 chunks][8 halves], where chunk m < 16 of position
+ *             p holds cos of frequencies 4m..4m+3, then sin of the same four,
+ *             and chunk 16 + m the same with the sines negated; then part B
+ *             [16 chunks][rope_len][8 halves], chunks m < 16 again, chunk-major
+ *             (part A serves kernels whose lanes take one position's chunks
+ *             together, part B kernels whose lanes hold consecutive positions)
  */
 typedef struct {
     int32_t D, T, Tc, G, K, page, sink, window, H, cb_dtype;
@@ -138,7 +142,7 @@ LVQ_API lvq_status lvq_rope_table(int32_t len, int32_t D, double base, float* co
 /*
  * The packed fp16 RoPE table (layout rope_f16 above): each cos/sin is
  * evaluated in fp64 and rounded once to binary16.  D must be 128.  out holds
- * len * 256 bytes.  The index-page pass forms its scores from it in packed
+ * len * 768 bytes.  The index-page pass forms its scores from it in packed
  * half precision (q turned back by the key's angle, dotted with the key in
  * fp32 accumulation).
  */
@@ -243,7 +247,9 @@ LVQ_API lvq_status lvq_codebook_update(const lvq_geom* g, int32_t block, const v
 /*
  * Bytes of workspace lvq_decode_attn needs for B requests of length at most
  * max_len with the given split count (0 = the library's choice); 0 for
- * invalid arguments.
+ * invalid arguments.  With bf16 codebooks this counts the room for a packed
+ * fp16 RoPE table of the positions below max_len (768 B each), which a call
+ * given rope_f16 does not use.
  */
 LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t max_len, int32_t num_splits);
 
@@ -289,12 +295,17 @@ LVQ_API size_t lvq_decode_attn_workspace(const lvq_geom* g, int32_t B, int32_t m
  *             slice to fp16 (exact for |x| >= 2^-14, absolute error below
  *             2^-25 under that).
  *  rope_cos, rope_sin  fp32 tables (lvq_rope_table), rope_len rows each.
- *  rope_f16   packed fp16 table (lvq_rope_table_f16) with the same rope_len;
- *             required for bf16 codebooks, ignored (may be NULL) for fp32.
+ *  rope_f16   packed fp16 table (lvq_rope_table_f16) with the same rope_len,
+ *             or NULL: with bf16 codebooks the call then builds the table
+ *             for positions below max_len from rope_cos / rope_sin in the
+ *             workspace (each fp32 value rounded once to binary16; one more
+ *             small launch per call).  Ignored for fp32 codebooks.
  *  out        fp32 [B][H][D];  lse_out fp32 [B][H] or NULL.
- *  ws         device workspace of at least lvq_decode_attn_workspace() bytes,
- *             256-byte aligned (LVQ_ERR_INVALID_ARG otherwise); contents
- *             need no initialisation and are scratch after the call.
+ *  ws         device workspace of at least lvq_decode_attn_workspace() bytes
+ *             (which counts the room for a packed table; a call given
+ *             rope_f16 needs that much less), 256-byte aligned
+ *             (LVQ_ERR_INVALID_ARG otherwise); contents need no
+ *             initialisation and are scratch after the call.
  *  num_splits 0 lets the library choose; otherwise
  *             1..1024, and with bf16 codebooks large enough that a split
  *             holds at most 192 index pages:
@@ -378,7 +389,9 @@ LVQ_API lvq_status lvq_request_order(const int32_t* seq_len, int32_t B, int32_t 
  *   pages each (later ones may be empty; with bf16 codebooks at most 192, as
  *   for lvq_decode_attn).  ws is 256-byte aligned device scratch of at least
  *   lvq_quant_partial_workspace(g, B, max_len) bytes: the query rows repacked
- *   as fp16 (pre-scaled by sm_scale * log2 e), 256 B per (request, head).
+ *   as fp16 (pre-scaled by sm_scale * log2 e), 256 B per (request, head),
+ *   then, with bf16 codebooks, room for the packed RoPE table of positions
+ *   below max_len (768 B each; used only when rope_f16 is NULL).
  * lvq_window_partial: the sink and recent bf16 tokens of step `step`, written
  *   to slot `slot` (< S_tot).  Never empty for seq_len >= 1.
  * Other arguments as for lvq_decode_attn.

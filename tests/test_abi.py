@@ -61,7 +61,6 @@ def _attn(g, **over):
     (dict(splits=2000), INVALID), (dict(splits=-2), INVALID), (dict(q=None), INVALID), (dict(ws=None), INVALID),
     (dict(pool=None), INVALID), (dict(pt_stride=3), INVALID), (dict(scale=float("nan")), INVALID),
     (dict(ws_bytes=16), WORKSPACE),
-    (dict(rope16=None), INVALID),              # bf16 codebooks need the packed fp16 RoPE table
     (dict(max_len=2048, splits=1), INVALID),   # 247 index pages in one split: over 1536 tokens per split
     (dict(ws=C.c_void_p(4096 + 16)), INVALID),  # workspace not 256-byte aligned
     (dict(splits=-1), INVALID),                # no single-pass kernel
@@ -82,6 +81,15 @@ def test_geometry_rejects(kw, status):
     assert _attn(None) == INVALID
 
 
+def test_decode_attn_without_packed_table_needs_room_for_one():
+    """Called without the packed fp16 RoPE table, lvq_decode_attn builds one in the workspace (768 B per
+    position below max_len), so the workspace query counts it and a workspace short of it is refused."""
+    g = _geom()
+    need = _lib.lib.lvq_decode_attn_workspace(C.byref(g), 4, 1024, 0)
+    assert _attn(g, rope16=None, ws_bytes=need - 256) == WORKSPACE
+    assert "workspace" in _lib.lib.lvq_last_error().decode()
+
+
 def test_decode_attn_empty_batch_is_a_no_op():
     assert _attn(_geom(), B=0, q=None, ws=None) == OK
 
@@ -90,10 +98,14 @@ def test_workspace_query():
     g = _geom()
     n = _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 3)
     # partials of 3 + 1 slots (rounded up to 256 B) + the packed fp16 query rows, 256 B per (request, head)
+    # + room for a packed fp16 RoPE table of the positions below max_len, 768 B each (used by calls given none)
     scratch = 64 * 2 * 64 * 4
-    assert n == 64 * 2 * 4 * (128 + 1) * 4 + scratch
-    assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 3, 6144, 1) == (3 * 2 * 2 * 129 * 4 + 255) // 256 * 256 + 3 * 2 * 256
-    assert _lib.lib.lvq_quant_partial_workspace(C.byref(g), 64, 6144) == scratch
+    table = 6144 * 768
+    assert n == 64 * 2 * 4 * (128 + 1) * 4 + scratch + table
+    assert (_lib.lib.lvq_decode_attn_workspace(C.byref(g), 3, 6144, 1) ==
+            (3 * 2 * 2 * 129 * 4 + 255) // 256 * 256 + 3 * 2 * 256 + table)
+    assert _lib.lib.lvq_quant_partial_workspace(C.byref(g), 64, 6144) == scratch + table
+    assert _lib.lib.lvq_quant_partial_workspace(C.byref(g), 64, 1001) == scratch + (1001 * 768 + 255) // 256 * 256
     g32 = _geom(cb_dtype="fp32")
     assert _attn(g32, rope16=None, B=0) == OK
     assert _lib.lib.lvq_decode_attn_workspace(C.byref(g), 64, 6144, 0) > 0

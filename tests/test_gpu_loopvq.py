@@ -102,13 +102,18 @@ def lv_cb(p, h, kind):
     return harness.host_codebooks(p, h, kind)
 
 
-def _run_parity(cfg, rows, steps, splits=(0,), only_needed_blocks=False):
+def _run_parity(cfg, rows, steps, splits=(0,), only_needed_blocks=False, packed_table=True):
     """Indices and attention of `rows` against the oracle at loop steps `steps`.  only_needed_blocks: the
-    indices of the loop blocks those steps read only (long contexts)."""
+    indices of the loop blocks those steps read only (long contexts).  packed_table=False: the calls pass no
+    packed fp16 RoPE table (the library builds it from the fp32 tables)."""
+    import dataclasses
+
     from tests import harness
     geo = _geo(cfg)
     _say(f"[build] {cfg.name} B={cfg.B} H={cfg.H} L={cfg.L} T={cfg.T} Tc={cfg.Tc} G={cfg.G} rows={len(rows)}")
     p = harness.build_loopvq(cfg, keep=rows)
+    if not packed_table:
+        p = dataclasses.replace(p, rope16=None)
     blocks = sorted({t // cfg.Tc for t in steps}) if only_needed_blocks else None
     idx = {}
     for (b, h) in rows:
@@ -137,19 +142,24 @@ def test_rope_table_matches_fp64():
 
 
 def test_rope_table_f16_layout_and_rounding():
-    """Packed fp16 table: chunk m < 16 of position p holds cos then sin of frequencies 4m..4m+3, chunk 16 + m
-    the same with the sines negated, each the fp64 value rounded once to binary16."""
+    """Packed fp16 table: in part A [n][32][8], chunk m < 16 of position p holds cos then sin of frequencies
+    4m..4m+3 and chunk 16 + m the same with the sines negated; part B [16][n][8] holds chunks m < 16 again,
+    chunk-major; each value is the fp64 one rounded once to binary16."""
     import decode_attention_loopvq_amd as lvq
     n = 9000
-    t = lvq.lvq_rope_table_f16(n, 128, 10000.0).cpu().numpy()          # [n][32][8] fp16
+    t = lvq.lvq_rope_table_f16(n, 128, 10000.0).cpu().numpy()          # [n * 384] fp16
+    ta = t[:n * 256].reshape(n, 32, 8)
+    tb = t[n * 256:].reshape(16, n, 8)
     phi = lv.rope_angles(np.arange(n), 128, 10000.0)                  # [n][64]
     for m in range(16):
         c16 = np.cos(phi[:, 4 * m:4 * m + 4]).astype(np.float16)
         s16 = np.sin(phi[:, 4 * m:4 * m + 4]).astype(np.float16)
-        np.testing.assert_array_equal(t[:, m, :4], c16)
-        np.testing.assert_array_equal(t[:, m, 4:], s16)
-        np.testing.assert_array_equal(t[:, 16 + m, :4], c16)
-        np.testing.assert_array_equal(t[:, 16 + m, 4:], -s16)
+        np.testing.assert_array_equal(ta[:, m, :4], c16)
+        np.testing.assert_array_equal(ta[:, m, 4:], s16)
+        np.testing.assert_array_equal(ta[:, 16 + m, :4], c16)
+        np.testing.assert_array_equal(ta[:, 16 + m, 4:], -s16)
+        np.testing.assert_array_equal(tb[m, :, :4], c16)
+        np.testing.assert_array_equal(tb[m, :, 4:], s16)
 
 
 @pytest.mark.parametrize("cb", ["bf16", "fp32"])
@@ -276,9 +286,22 @@ def test_encode_decode_page():
     assert not pool2[rest].any(), "bytes written outside the encoded pages"
 
 
-def test_partial_entry_points_compose():
+@pytest.mark.parametrize("name,over", [
+    ("loopvq-b64-6k", dict(B=5, H=2, L=700, ragged=(1, 700), random_pages=True, seed=5)),
+    ("loopvq-deep-ragged", dict(B=5, H=2, L=600, ragged=(1, 600), seed=6)),
+], ids=["c8", "c4"])
+def test_decode_without_packed_table(name, over):
+    """lvq_decode_attn given only the fp32 cos/sin tables (no packed fp16 table: the library builds one in
+    the workspace on every call), every row and the loop steps 0, 1 and the last, against the oracle."""
+    cfg = loopvq_config(name, **over)
+    rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    _run_parity(cfg, rows, [0, 1, cfg.T - 1], splits=(0, 3), packed_table=False)
+
+
+@pytest.mark.parametrize("packed_table", [True, False], ids=["table", "no-table"])
+def test_partial_entry_points_compose(packed_table):
     """lvq_quant_partial + lvq_window_partial + splitk_lse_merge give the attention of the oracle (the
-    standalone path that lvq_decode_attn fuses)."""
+    standalone path that lvq_decode_attn fuses), with and without the packed fp16 RoPE table."""
     import decode_attention_loopvq_amd as lvq
     from tests import harness
     cfg = loopvq_config("loopvq-b64-6k", B=5, H=2, L=700)
@@ -294,7 +317,7 @@ def test_partial_entry_points_compose():
         pl = torch.empty((cfg.B * cfg.H, S + 1), dtype=torch.float32, device="cuda")
         q = p.q[t].contiguous()
         lvq.lvq_quant_partial(p.g, t, q, c.pool, c.page_table, c.seq_len, c.max_len, p.slices, p.rope_cos,
-                              p.rope_sin, p.sm_scale, po, pl, S, rope_f16=p.rope16)
+                              p.rope_sin, p.sm_scale, po, pl, S, rope_f16=p.rope16 if packed_table else None)
         lvq.lvq_window_partial(p.g, t, q, c.seq_len, c.max_len, c.win_k, c.win_v, p.rope_cos, p.rope_sin,
                                p.sm_scale, po, pl, slot=S)
         out, lse = lvq.splitk_lse_merge(po, pl)
