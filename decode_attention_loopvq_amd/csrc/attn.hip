@@ -320,36 +320,8 @@ __global__ void __launch_bounds__(256) quant_partial_kernel(AttnArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// Index-page partial for bf16 codebooks.
-//
-// RoPE score without rotating keys: with the rotate-half pairing (channel i
-// with i + 64, angle p*th_i), q . R(p) k = k . psi(p) where
-//   psi_i      = cos(p th_i) q_i + sin(p th_i) q_{i+64}
-//   psi_{i+64} = cos(p th_i) q_{i+64} - sin(p th_i) q_i      (i < 64),
-// i.e. the query turned back by the key's angle.  psi is formed per
-// (request, position) in packed fp16 and dotted with the key rebuilt from
-// the step's K slice (fp16 in LDS) with fp32 accumulation.  The query is
-// pre-scaled by sm_scale * log2(e) so scores come out in log2 units.
-//
-// V is never rebuilt per token: the softmax weight of each token is added,
-// in fixed point, to one bin per (group, codeword) of its V indices, and the
-// partial output is sum_r bin[g][r] * B_t^V[g][r] at the end (exact up to
-// the weights' rounding).  Weights need the split's running maximum, so each
-// segment of tokens is scored first, the maximum taken, the bins rescaled if
-// it grew, and the weights then binned.
-//
-// Workgroup: R requests x one head x one split, 512 threads, one lane per
-// token position.  A position's cos/sin (packed fp16, 256 B) is loaded once
-// and serves all R requests; the K slice staged once serves all of them.
-//
-// LDS (bytes):  [0, 64K)    K slice as fp16 [NG][256][C]  (later: V slice)
-//               [64K, 128K) bins u32 [256 codewords][R*NG slots]
-//               then page ids of the segment and reduction scratch.
-// Bin slot of (request j, group g) is j*NG + g; row r holds slot s at
-// byte r*256 + 4*s.  The V index bytes of a token sit XOR-rotated by
-// (token & 15) in the pool (byte m holds group m ^ (token & 15)), so at
-// step m the 16 lanes of each LDS phase hit 16 distinct groups and thus 16
-// distinct banks.
+// Helpers of the bf16 index-page kernels (index_attn_kernel, index_mfma_kernel; their own comments
+// describe them).
 // ---------------------------------------------------------------------------
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
