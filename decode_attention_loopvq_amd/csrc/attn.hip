@@ -956,10 +956,31 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     // so that the loads issue together)
     int lo[R], hi[R];
     bool any = false;
-    {
-        int len[R];
+    int len[R];
 #pragma unroll
-        for (int j = 0; j < R; ++j) len[j] = a.seq_len[min(rq[j], a.B - 1)];
+    for (int j = 0; j < R; ++j) len[j] = a.seq_len[min(rq[j], a.B - 1)];
+    // Loads that need no length are issued before the lengths are waited for: the step's K slice of head h
+    // (16-byte chunk e = tid + NT * i is codeword e >> 4 of group e & 15 of the global layout
+    // [group][codeword][8]; it goes to LDS byte 16 e = 256 * codeword + 16 * group) and the query element this
+    // thread packs (wave w converts request w's row, one dword = two channels per lane, into qf16).  A
+    // workgroup without work leaves them unused.
+    uint4 stage[16];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_k) +
+                                                          h * a.slice_hstride);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = tid + NT * i;
+            stage[i] = src[(e & 15) * K + (e >> 4)];
+        }
+    }
+    static_assert(R * D / 2 == NT, "one query dword per thread");
+    int qrow = rq[0];
+#pragma unroll
+    for (int j = 1; j < R; ++j)
+        if (wave == j) qrow = rq[j];
+    const uint32_t qraw = reinterpret_cast<const uint32_t*>(a.q + (long(min(qrow, a.B - 1)) * g.H + h) * D)[lane];
+    {
         const int split_tok = a.pps * 8;
 #pragma unroll
         for (int j = 0; j < R; ++j) {
@@ -971,6 +992,11 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         }
     }
     if (!any) {
+        // (the early loads are consumed on this path too, so that the compiler issues them above the
+        // lengths' wait instead of sinking them below this branch)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(stage[i].x));
+        asm volatile("" ::"v"(qraw));
         for (int e = tid; e < R * D; e += NT) {
             const int j = e / D, d = e % D, rb = rq[j];
             if (rb >= a.B) continue;
@@ -988,10 +1014,8 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
             t_hi = max(t_hi, hi[j]);
         }
     }
-    // Setup loads, in the order they are needed (the vector loads complete in order): the split's page-table
-    // entries (page ids, per request: a page past a request's range holds its last index page, a request
-    // without index pages physical page 0, so that every load below reads valid memory), the query rows, then
-    // the step's K slice of head h.
+    // The split's page-table entries (page ids, per request: a page past a request's range holds its last index
+    // page, a request without index pages physical page 0, so that every load below reads valid memory).
     constexpr int kPt = R * (kMaxSplitTok / 8) / NT;   // page-table entries per thread
     static_assert(R * (kMaxSplitTok / 8) % NT == 0, "page-table fill");
     uint32_t ptv[kPt];
@@ -1009,30 +1033,11 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         const uint32_t v = uint32_t(a.pt[long(row) * a.pt_stride + page]);
         ptv[i] = hij > 0 ? v : 0u;
     }
-    // The query rows: wave w converts request w's row, one dword (two channels) per lane, into qf16.
-    static_assert(R * D / 2 == NT, "one query dword per thread");
-    int qrow = rq[0];
-#pragma unroll
-    for (int j = 1; j < R; ++j)
-        if (wave == j) qrow = rq[j];
-    const uint32_t qraw = reinterpret_cast<const uint32_t*>(a.q + (long(min(qrow, a.B - 1)) * g.H + h) * D)[lane];
     // The lane's query: blocks f1 = ((2 kb) ^ n) & 7 and f2 = f1 ^ 1 of 8 frequencies, qa = the half of
     // slot 0's group, qb the partner half (read from qf16 once the first score loads are issued).
     const int hl = (n >> 3) & 1;
     const int f1 = ((2 * kb) ^ n) & 7;
     uint32_t qa[R][2][4], qb[R][2][4];
-    // K slice of head h: 16-byte chunk e = tid + NT * i is codeword e >> 4 of group e & 15 (global layout
-    // [group][codeword][8]); it goes to LDS byte 16 e = 256 * codeword + 16 * group.
-    uint4 stage[16];
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.slice_k) +
-                                                          h * a.slice_hstride);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int e = tid + NT * i;
-            stage[i] = src[(e & 15) * K + (e >> 4)];
-        }
-    }
 #pragma unroll
     for (int i = 0; i < kPt; ++i) {
         const int e = tid + NT * i;
