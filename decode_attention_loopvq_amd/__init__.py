@@ -22,7 +22,7 @@ from . import layout  # noqa: F401
 __all__ = [
     "LvqError", "lvq_geom", "kivi_geom", "make_geom", "make_kivi_geom",
     "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_channel_perm_check", "lvq_rope_table_perm",
-    "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_decode_attn_noalloc", "lvq_request_order", "lvq_window_append",
+    "lvq_encode", "lvq_decode_attn_workspace", "lvq_decode_attn", "lvq_decode_attn_noalloc", "lvq_request_order", "lvq_check_pages", "lvq_window_append",
     "lvq_codebook_update",
     "lvq_decode_attn_splits", "lvq_quant_partial", "lvq_quant_partial_workspace", "lvq_window_partial", "splitk_lse_merge", "kivi_append",
     "kivi_decode_attn_workspace", "kivi_decode_attn", "KiviCache", "kivi_widths", "layout",
@@ -338,6 +338,24 @@ def lvq_request_order(seq_len: torch.Tensor, max_len: int, out: Optional[torch.T
     check(lib.lvq_request_order(seq_len.data_ptr(), int(B), int(max_len), out.data_ptr(), _stream(stream)),
           "lvq_request_order")
     return out
+
+
+def lvq_check_pages(g: lvq_geom, page_table: torch.Tensor, seq_len: torch.Tensor, max_len: int,
+                    n_pool_pages: int, stream=None) -> Tuple[int, int, int]:
+    """Debug check of a batch's page table and lengths (include/lvq.h): (offending page-table entries, the
+    lowest request holding one or -1, requests whose seq_len lies outside [0, max_len]).  Waits for the
+    result."""
+    _need(page_table, "page_table", torch.int32)
+    _need(seq_len, "seq_len", torch.int32)
+    B = seq_len.numel()
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B][pt_stride] with the seq_len batch")
+    bad = torch.zeros(3, dtype=torch.int32, device=seq_len.device)
+    check(lib.lvq_check_pages(C.byref(g), page_table.data_ptr(), int(page_table.shape[1]), seq_len.data_ptr(),
+                              int(max_len), int(n_pool_pages), int(B), bad.data_ptr(), _stream(stream)),
+          "lvq_check_pages")
+    n_bad, first, n_len = bad.tolist()
+    return n_bad, first, n_len
 
 
 def lvq_window_append(g: lvq_geom, step: int, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],

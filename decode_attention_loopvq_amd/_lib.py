@@ -14,7 +14,7 @@ EXPORTS = (
     "lvq_last_error", "lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_channel_perm_check",
     "lvq_rope_table_perm", "lvq_encode",
     "lvq_decode_attn_workspace", "lvq_decode_attn_splits", "lvq_decode_attn", "lvq_decode_attn_noalloc",
-    "lvq_request_order",
+    "lvq_request_order", "lvq_check_pages",
     "lvq_window_append", "lvq_codebook_update",
     "lvq_quant_partial",
     "lvq_quant_partial_workspace",
@@ -70,6 +70,7 @@ def _load():
     lib.lvq_decode_attn_noalloc.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P,
                                             _P, _P, _P, _I, C.c_float, _P, _P, _I, _I, _P]
     lib.lvq_request_order.argtypes = [_P, _I, _I, _P, _P]
+    lib.lvq_check_pages.argtypes = [C.POINTER(lvq_geom), _P, _I, _P, _I, _I, _I, _P, _P]
     lib.lvq_window_append.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, _P, _P, _P, _I, _I, _P]
     lib.lvq_codebook_update.argtypes = [C.POINTER(lvq_geom), _I, _P, _P, C.POINTER(C.c_int64), _P, _P, _P,
                                         C.POINTER(C.c_int64), _P, _P, _P, _I, _P, _P, _I, _I, _P]
@@ -91,7 +92,7 @@ def _load():
     for name in ("lvq_slice_codebooks", "lvq_rope_table", "lvq_rope_table_f16", "lvq_channel_perm_check",
                  "lvq_rope_table_perm", "lvq_encode", "lvq_decode_attn",
                  "lvq_decode_attn_noalloc",
-                 "lvq_request_order", "lvq_window_append", "lvq_codebook_update", "lvq_quant_partial",
+                 "lvq_request_order", "lvq_check_pages", "lvq_window_append", "lvq_codebook_update", "lvq_quant_partial",
                  "lvq_window_partial", "splitk_lse_merge",
                  "kivi_append", "kivi_decode_attn"):
         getattr(lib, name).restype = C.c_int

@@ -1989,6 +1989,67 @@ extern "C" lvq_status lvq_request_order(const int32_t* seq_len, int32_t B, int32
 }
 
 // ---------------------------------------------------------------------------
+// Debug check of the page table and lengths the attention and encode kernels take on trust: one workgroup;
+// wave w takes requests w, w + 16, ..., its lanes the request's index pages; counts in LDS.
+// ---------------------------------------------------------------------------
+namespace lvq {
+namespace {
+constexpr int kCheckThreads = 1024;
+
+__global__ void __launch_bounds__(kCheckThreads) check_pages_kernel(Geo g, const int32_t* __restrict__ pt,
+                                                                     int pt_stride,
+                                                                     const int32_t* __restrict__ seq_len, int B,
+                                                                     int max_len, int n_pool,
+                                                                     int32_t* __restrict__ bad) {
+    __shared__ int n_bad, first_bad, n_len;
+    if (threadIdx.x == 0) {
+        n_bad = 0;
+        first_bad = 0x7fffffff;
+        n_len = 0;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kCheckThreads / 64;
+    for (int b = wave; b < B; b += nw) {
+        const int L0 = seq_len[b];
+        if (lane == 0 && (L0 < 0 || L0 > max_len)) atomicAdd(&n_len, 1);
+        const int np = n_index_pages(min(max(L0, 0), max_len), g);
+        for (int lp = lane; lp < np; lp += 64) {
+            const int v = pt[long(b) * pt_stride + lp];
+            if (v < 0 || v >= n_pool) {
+                atomicAdd(&n_bad, 1);
+                atomicMin(&first_bad, b);
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        bad[0] = n_bad;
+        bad[1] = first_bad == 0x7fffffff ? -1 : first_bad;
+        bad[2] = n_len;
+    }
+}
+}  // namespace
+}  // namespace lvq
+
+extern "C" lvq_status lvq_check_pages(const lvq_geom* gp, const int32_t* page_table, int32_t pt_stride,
+                                      const int32_t* seq_len, int32_t max_len, int32_t n_pool_pages, int32_t B,
+                                      int32_t* bad, hipStream_t stream) {
+    Geo g;
+    const lvq_status st = validate_geom(gp, &g);
+    if (st != LVQ_OK) return st;
+    LVQ_REQUIRE(B >= 0 && max_len >= 1 && n_pool_pages >= 1, LVQ_ERR_INVALID_ARG,
+                "lvq_check_pages: B=%d max_len=%d n_pool_pages=%d", B, max_len, n_pool_pages);
+    const int max_pages = max_index_pages(g, max_len);
+    LVQ_REQUIRE(pt_stride >= max_pages, LVQ_ERR_INVALID_ARG, "lvq_check_pages: pt_stride %d < %d pages", pt_stride,
+                max_pages);
+    LVQ_REQUIRE(bad && (B == 0 || (seq_len && (max_pages == 0 || page_table))), LVQ_ERR_INVALID_ARG,
+                "lvq_check_pages: NULL pointer");
+    hipLaunchKernelGGL(check_pages_kernel, dim3(1), dim3(kCheckThreads), 0, stream, g, page_table, pt_stride, seq_len,
+                       B, max_len, n_pool_pages, bad);
+    return check_launch("lvq_check_pages");
+}
+
+// ---------------------------------------------------------------------------
 // Window append (LoopVQ page, Figure 5: each generated token's bf16 K and V of a loop step go into the
 // recent window; the oldest page leaves it for the index pool every 8 tokens).  Position
 // p = seq_len[b] - 1 (the caller has counted the new token) goes to window slot p for p < sink, else

@@ -375,6 +375,25 @@ LVQ_API lvq_status lvq_request_order(const int32_t* seq_len, int32_t B, int32_t 
                                      hipStream_t stream);
 
 /*
+ * Debug check of what the attention and encode kernels take on trust (they
+ * clamp lengths to max_len but dereference page ids as given): for every
+ * request b, each of its index pages lp < n_pages(min(max(seq_len[b], 0),
+ * max_len)), n_pages(L) = max(0, floor((L - sink - window) / page)), must name
+ * a physical page in [0, n_pool_pages).  Writes bad (device int32 [3]):
+ * bad[0] = the number of offending page-table entries, bad[1] = the lowest
+ * request holding one (-1 if none), bad[2] = the number of requests whose
+ * seq_len lies outside [0, max_len] (the kernels clamp those; reported for
+ * information).  Reads only those page-table entries; one kernel launch of
+ * one workgroup, meant for debug builds and tests (the caller reads bad).
+ *  page_table [B][pt_stride] int32, seq_len [B] int32 (device).
+ * Errors: LVQ_ERR_INVALID_ARG for B < 0, max_len < 1, n_pool_pages < 1,
+ * pt_stride below the page count of max_len, or NULL pointers.
+ */
+LVQ_API lvq_status lvq_check_pages(const lvq_geom* g, const int32_t* page_table, int32_t pt_stride,
+                                   const int32_t* seq_len, int32_t max_len, int32_t n_pool_pages, int32_t B,
+                                   int32_t* bad, hipStream_t stream);
+
+/*
  * The two partial passes lvq_decode_attn is made of, callable on their own
  * (Figure 5 of the LoopVQ page: one kernel attends the index pages, another
  * the bf16 pages, and their outputs are merged).  Both write normalised

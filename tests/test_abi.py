@@ -253,6 +253,20 @@ def test_noalloc_rejects_before_touching_the_device():
     assert call(B=0) == OK
 
 
+def test_check_pages_rejects():
+    """lvq_check_pages validates its sizes and pointers before launching anything."""
+    g = _geom()
+    f = _lib.lib.lvq_check_pages
+    # 6K context: 759 index pages per request
+    assert f(C.byref(g), FAKE, 758, FAKE, 6144, 100, 4, FAKE, None) == INVALID      # pt_stride below the pages
+    assert f(C.byref(g), FAKE, 759, FAKE, 6144, 0, 4, FAKE, None) == INVALID        # no pool pages
+    assert f(C.byref(g), None, 759, FAKE, 6144, 100, 4, FAKE, None) == INVALID      # NULL page table
+    assert f(C.byref(g), FAKE, 759, FAKE, 6144, 100, 4, None, None) == INVALID      # NULL result
+    assert f(C.byref(g), FAKE, 759, FAKE, 0, 100, 4, FAKE, None) == INVALID         # max_len < 1
+    assert "lvq_check_pages" in _lib.lib.lvq_last_error().decode()
+    assert f(None, FAKE, 759, FAKE, 6144, 100, 4, FAKE, None) == INVALID
+
+
 def test_channel_perm_check():
     """lvq_channel_perm_check (host only): a permutation that maps RoPE pairs to RoPE pairs passes; swapping a
     pair's halves, putting both channels of a pair in one index group, or any other break of the pairing is

@@ -412,6 +412,39 @@ def test_channel_permutation():
             assert abs(float(lse[b, h]) - l_ref) <= LSE_TOL, (t, b, h)
 
 
+def test_check_pages():
+    """lvq_check_pages, the debug check of what the kernels take on trust: a valid cache gives no finding;
+    page ids outside [0, pool pages) planted inside requests' index ranges are each counted, with the lowest
+    such request, while entries past a request's range are not read; lengths outside [0, max_len] are
+    counted."""
+    import decode_attention_loopvq_amd as lvq
+    from decode_attention_loopvq_amd.layout import LoopVQCache
+    g = lvq.make_geom(H=2)
+    lengths = [700, 75, 300, 1, 512]
+    c = LoopVQCache(g, lengths, device="cuda")
+    P = c.pool.shape[0]
+    assert lvq.lvq_check_pages(g, c.page_table, c.seq_len, c.max_len, P) == (0, -1, 0)
+    pt = c.page_table.clone()
+    # pt_stride wider than needed, the spare columns holding garbage that must not be read
+    wide = torch.full((c.B, pt.shape[1] + 5), -7, dtype=torch.int32, device="cuda")
+    wide[:, :pt.shape[1]] = pt
+    assert lvq.lvq_check_pages(g, wide, c.seq_len, c.max_len, P) == (0, -1, 0)
+    # request 1 has no index page (75 tokens): a bad entry in its row is outside its range
+    wide[1, 0] = P + 3
+    wide[2, c.n_pages[2] - 1] = P                   # last index page of request 2
+    wide[4, 0] = -1                                 # first index page of request 4
+    wide[4, 3] = 1 << 30
+    wide[0, c.n_pages[0]] = -5                      # just past request 0's range: not read
+    assert lvq.lvq_check_pages(g, wide, c.seq_len, c.max_len, P) == (3, 2, 0)
+    # lengths past max_len are clamped by the kernels and reported here; negative ones too
+    sl = c.seq_len.clone()
+    sl[3] = c.max_len + 9
+    sl[0] = -4
+    assert lvq.lvq_check_pages(g, c.page_table, sl, c.max_len, P) == (0, -1, 2)
+    # a pool smaller than the table's ids
+    assert lvq.lvq_check_pages(g, c.page_table, c.seq_len, c.max_len, 1)[0] == sum(c.n_pages) - 1
+
+
 def test_request_order_sorts_by_length():
     """lvq_request_order against a stable host sort of the clamped lengths (longest first, ties by index)."""
     import decode_attention_loopvq_amd as lvq
