@@ -1085,16 +1085,27 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     auto read_pids = [&](int k) {
         return *reinterpret_cast<const uint4*>(&pid_lds[(tau0_of(k) - t_lo) >> 4][n >> 3][0]);
     };
-    // key-row dwords of a block from its page ids: dword kb of token n ^ 4 j of request j
-    auto issue_ik = [&](const uint4& pd, uint32_t (&ik)[R]) {
+    // key-row dwords of a block from its page ids: dword kb of token n ^ 4 j of request j; with a key scale
+    // stream (KS) also the scale of the lane's own (request ro, token n), whose page is request ro's entry of
+    // the page half n >> 3: the lane's own for ro < 2, else the one lane n ^ 8 holds for its request ro ^ 2
+    // (brought by a row rotation), so that no LDS read waits in the score loop.  The scale stays fp16 bits
+    // until its block is scored: converting it here would wait for the load at once.
+    auto issue_ik = [&](const uint4& pd, uint32_t (&ik)[R], uint32_t& ksv) {
         const uint32_t pid[R] = {pd.x, pd.y, pd.z, pd.w};
 #pragma unroll
         for (int j = 0; j < R; ++j)
             ik[j] = *reinterpret_cast<const uint32_t*>(kbase[j] + uint64_t(pid[j]) * page_bytes);
+        if constexpr (KS) {
+            const uint32_t x01 = br0 ? pd.y : pd.x, x23 = br0 ? pd.w : pd.z;
+            const uint32_t own = br1 ? x23 : x01, other = br1 ? x01 : x23;   // requests ro and ro ^ 2
+            const uint32_t rot = uint32_t(__builtin_amdgcn_update_dpp(int(other), int(other), 0x128, 0xf, 0xf, false));
+            const uint32_t pid_own = br1 ? rot : own;                          // row_ror:8, from lane n ^ 8
+            ksv = a.kscale[(uint64_t(pid_own) * g.T + a.step) * 8 + (n & 7)];
+        }
     };
-    auto load_ik = [&](int k, uint32_t (&ik)[R]) { issue_ik(read_pids(k), ik); };
-    // cos/sin chunks of the lane's token (block f1: 2, block f2: 2) and its key scale (KS)
-    struct CsBuf { uint4 cs[4]; float ks; };
+    auto load_ik = [&](int k, uint32_t (&ik)[R], uint32_t& ksv) { issue_ik(read_pids(k), ik, ksv); };
+    // cos/sin chunks of the lane's token (block f1: 2, block f2: 2)
+    struct CsBuf { uint4 cs[4]; };
     auto load_cs = [&](int k, CsBuf& b) {
         const int tau0 = tau0_of(k);
         const uint32_t p = uint32_t(min(g.sink + tau0 + n, a.rope_len - 1));
@@ -1104,10 +1115,6 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         b.cs[1] = r1[1];
         b.cs[2] = r2[0];
         b.cs[3] = r2[1];
-        if constexpr (KS) {
-            const uint32_t pid = pid_of(ro, (tau0 + n - t_lo) >> 3);
-            b.ks = f16_to_f32(a.kscale[(uint64_t(pid) * g.T + a.step) * 8 + ((tau0 + n) & 7)]);
-        }
     };
     float sreg[NB];
 #pragma unroll
@@ -1156,14 +1163,15 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     // The loads for later blocks are issued inside: the page ids of block k + 4 before the gathers of request
     // 2 (so that waiting for them never waits for gathers issued after them), block k + 4's key-row dwords into
     // ik once its last gathers are issued, block k + 2's cos/sin into b once psi is formed.
-    auto score_blk = [&](int k, uint32_t (&ik)[R], CsBuf& b, uint4 (&G0)[4], const uint32_t (&ikn)[R]) {
+    auto score_blk = [&](int k, uint32_t (&ik)[R], uint32_t& ksv, CsBuf& b, uint4 (&G0)[4],
+                         const uint32_t (&ikn)[R]) {
         uint32_t c[2][4], s[2][4];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             c[u][0] = b.cs[2 * u].x; c[u][1] = b.cs[2 * u].y; c[u][2] = b.cs[2 * u + 1].x; c[u][3] = b.cs[2 * u + 1].y;
             s[u][0] = b.cs[2 * u].z; s[u][1] = b.cs[2 * u].w; s[u][2] = b.cs[2 * u + 1].z; s[u][3] = b.cs[2 * u + 1].w;
         }
-        const float ks = KS ? b.ks : 1.f;
+        const uint32_t ks_bits = ksv;                   // (read before the set is reloaded)
         f32x4_t acc[R];
         uint4 G1[4], G2[4], G3[4];
         gather(J1{}, ik[1], G1);
@@ -1172,7 +1180,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         gather(J2{}, ik[2], G2);
         acc[1] = request_mfma(J1{}, G1, c, s);
         gather(J3{}, ik[3], G3);
-        issue_ik(pd, ik);
+        issue_ik(pd, ik, ksv);
         acc[2] = request_mfma(J2{}, G2, c, s);
         gather(J0{}, ikn[0], G0);
         acc[3] = request_mfma(J3{}, G3, c, s);
@@ -1188,7 +1196,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         const float e01 = bn0 ? e[1] : e[0];
         const float e23 = bn0 ? e[3] : e[2];
         float sc = bn1 ? e23 : e01;
-        if constexpr (KS) sc *= ks;
+        if constexpr (KS) sc *= f16_to_f32(uint16_t(ks_bits));
         const int tau = t_lo + kMBlk * (wave + NW * k) + n;
         sc = (k < nk && tau >= lo_o && tau < hi_o) ? sc : -INFINITY;
         rmax = fmaxf(rmax, sc);
@@ -1198,12 +1206,13 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
     // key-row dwords four blocks ahead (set k % 4), cos/sin two blocks ahead (set k % 2); each set is reloaded
     // while its block is scored.  The first loads are issued before the K slice is stored to LDS.
     uint32_t IK0[R], IK1[R], IK2[R], IK3[R];
+    uint32_t KS0 = 0u, KS1 = 0u, KS2 = 0u, KS3 = 0u;
     CsBuf C0, C1;
     if (nk > 0) {
-        load_ik(0, IK0);
-        load_ik(1, IK1);
-        load_ik(2, IK2);
-        load_ik(3, IK3);
+        load_ik(0, IK0, KS0);
+        load_ik(1, IK1, KS1);
+        load_ik(2, IK2, KS2);
+        load_ik(3, IK3, KS3);
         load_cs(0, C0);
         load_cs(1, C1);
     }
@@ -1231,10 +1240,10 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         // whole rounds of four blocks: a round's blocks past the wave's last one rescore that block with their
         // scores discarded (the loop has one exit, so the loads in flight are counted across iterations)
         for (int k = 0; k < nk; k += 4) {
-            score_blk(k, IK0, C0, G0, IK1);
-            score_blk(k + 1, IK1, C1, G0, IK2);
-            score_blk(k + 2, IK2, C0, G0, IK3);
-            score_blk(k + 3, IK3, C1, G0, IK0);
+            score_blk(k, IK0, KS0, C0, G0, IK1);
+            score_blk(k + 1, IK1, KS1, C1, G0, IK2);
+            score_blk(k + 2, IK2, KS2, C0, G0, IK3);
+            score_blk(k + 3, IK3, KS3, C1, G0, IK0);
         }
     }
     // value rows of the lane's own (request, token) of the wave's k-th block, the first four loaded now
