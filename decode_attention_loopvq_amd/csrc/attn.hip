@@ -1406,7 +1406,7 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
 // otherwise it is written to slot num_splits.
 // ---------------------------------------------------------------------------
 constexpr int kWinBatch = 5;
-constexpr int kWinPrefetch = 8;                   // index-page partials loaded at the start of the merge
+constexpr int kWinPrefetch = 4;                   // index-page partials loaded at the start of the merge
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -1431,7 +1431,8 @@ struct WinRow {
     long wbase;                                    // element offset of the row's (request, step, head) buffer
     const float* rc;                               // cos and sin of the lane's frequencies at position 0
     const float* rs;
-    float ql[4], qh[4];                            // the lane's query channels (i, then i + 64), times sm_scale * log2 e
+    uint2 qlo, qhi;                                // the lane's query channels (i, then i + 64), bf16 bits: converted
+                                                   // once the window loads are issued, not at once after their load
 };
 
 __device__ __forceinline__ WinRow window_setup(const AttnArgs& a, int rb, int h, bool live, int c16) {
@@ -1447,11 +1448,8 @@ __device__ __forceinline__ WinRow window_setup(const AttnArgs& a, int rb, int h,
     w.rc = a.rc + 4 * c16;
     w.rs = a.rs + 4 * c16;
     const uint16_t* qp = a.q + (long(rb) * g.H + h) * D + 4 * c16;
-    const uint2 lo = *reinterpret_cast<const uint2*>(qp), hi = *reinterpret_cast<const uint2*>(qp + 64);
-    w.ql[0] = bf16_lo(lo.x) * a.scale_log2; w.ql[1] = bf16_hi(lo.x) * a.scale_log2;
-    w.ql[2] = bf16_lo(lo.y) * a.scale_log2; w.ql[3] = bf16_hi(lo.y) * a.scale_log2;
-    w.qh[0] = bf16_lo(hi.x) * a.scale_log2; w.qh[1] = bf16_hi(hi.x) * a.scale_log2;
-    w.qh[2] = bf16_lo(hi.y) * a.scale_log2; w.qh[3] = bf16_hi(hi.y) * a.scale_log2;
+    w.qlo = *reinterpret_cast<const uint2*>(qp);
+    w.qhi = *reinterpret_cast<const uint2*>(qp + 64);
     return w;
 }
 
@@ -1481,6 +1479,16 @@ __device__ __forceinline__ void window_batch(const AttnArgs& a, const WinRow& w,
         cs[i] = *reinterpret_cast<const float4*>(w.rc + long(p) * (D / 2));
         sn[i] = *reinterpret_cast<const float4*>(w.rs + long(p) * (D / 2));
     }
+    // the query times sm_scale * log2 e, formed here (an opaque copy keeps the conversion, and so the wait for
+    // the query's load, below this batch's loads rather than hoisted above the first batch)
+    uint32_t qw[4] = {w.qlo.x, w.qlo.y, w.qhi.x, w.qhi.y};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(qw[u]));
+    float ql[4], qh[4];
+    ql[0] = bf16_lo(qw[0]) * a.scale_log2; ql[1] = bf16_hi(qw[0]) * a.scale_log2;
+    ql[2] = bf16_lo(qw[1]) * a.scale_log2; ql[3] = bf16_hi(qw[1]) * a.scale_log2;
+    qh[0] = bf16_lo(qw[2]) * a.scale_log2; qh[1] = bf16_hi(qw[2]) * a.scale_log2;
+    qh[2] = bf16_lo(qw[3]) * a.scale_log2; qh[3] = bf16_hi(qw[3]) * a.scale_log2;
     float s[NB];
     float mb = m;
 #pragma unroll
@@ -1492,8 +1500,8 @@ __device__ __forceinline__ void window_batch(const AttnArgs& a, const WinRow& w,
         float part = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const float psl = fmaf(w.ql[u], c4[u], w.qh[u] * s4[u]);
-            const float psh = fmaf(w.qh[u], c4[u], -(w.ql[u] * s4[u]));
+            const float psl = fmaf(ql[u], c4[u], qh[u] * s4[u]);
+            const float psh = fmaf(qh[u], c4[u], -(ql[u] * s4[u]));
             part = fmaf(k_lo[u], psl, part);
             part = fmaf(k_hi[u], psh, part);
         }
