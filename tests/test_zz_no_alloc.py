@@ -1,5 +1,6 @@
 """lvq_decode_attn_noalloc (the entry point for callers that cannot allocate) against lvq_decode_attn on
-the same inputs: two calls in a row, the second on a smaller batch and context, both through the C ABI.
+the same inputs: two calls in a row, the second on a smaller batch and context, both through the C ABI, with
+and without the packed fp16 RoPE table.
 The two share their kernels, so the outputs are expected bit for bit equal; the bar written here is the
 attention bar (2e-3 relative per (request, head) row, lse within 2e-3) plus that equality."""
 
@@ -60,3 +61,8 @@ def test_noalloc_matches_decode_attn_on_two_calls():
         _check(*_both(ps, t))
     _say("[noalloc] big, 3 splits")
     _check(*_both(pb, 1, num_splits=3))
+    # without the packed fp16 RoPE table both calls build it in their workspace from the fp32 tables
+    import dataclasses
+    _say("[noalloc] big and small without the packed table")
+    _check(*_both(dataclasses.replace(pb, rope16=None), 2))
+    _check(*_both(dataclasses.replace(ps, rope16=None), 2))
