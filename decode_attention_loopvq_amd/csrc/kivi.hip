@@ -386,6 +386,7 @@ __global__ void decode_counters_kernel(KArgs a, int B) {
 // query head are combined through LDS.
 // ---------------------------------------------------------------------------
 constexpr int kKiviLaneGroups = 32;
+constexpr int kKiviD = 128;          // head dimension of the attention kernels
 
 template <int CTRL>
 __device__ __forceinline__ float kdpp(float x) {
@@ -450,17 +451,18 @@ __device__ __forceinline__ void half8(uint4 w, float* out) {
     }
 }
 
-template <int KB, int VB, int HPL>
-__global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, const uint16_t* __restrict__ q,
-                                                                   float scale_log2, int S_tot,
-                                                                   int max_len, float* __restrict__ po,
-                                                                   float* __restrict__ pl) {
-    constexpr int D = 128, NLG = kKiviLaneGroups;
+// The body of the kernel for one (split, KV head, request); red is the workgroup's combine buffer.  FAST =
+// false leaves out the whole-key-group path (a split holding only the rows past them).
+template <int KB, int VB, int HPL, bool FAST = true>
+__device__ __forceinline__ void kivi_attn_rows(const KArgs& a, const uint16_t* __restrict__ q, float scale_log2,
+                                               int S_tot, int max_len, float* __restrict__ po,
+                                               float* __restrict__ pl, int split, int h, int b,
+                                               float (*red)[kKiviD + 2]) {
+    constexpr int D = kKiviD, NLG = kKiviLaneGroups;
     // tokens whose codes are held at once: fewer with 4-bit codes or several heads per lane group
     static_assert(HPL == 1 || HPL == 2, "one or two heads per lane group (four spill registers)");
     constexpr int TB = HPL == 2 ? 8 : (KB == 4 || VB == 4) ? 16 : 32;
     constexpr int KROW = D * KB / 8, VROW = D * VB / 8;  // code bytes per token
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, c8 = tid & 7, lg = tid >> 3;
     // The nrep query heads of KV head h form nset = nrep / HPL sets of HPL heads; lane group lg serves
     // set lg % nset (heads h*nrep + set*HPL + u) and takes every (32 / nset)-th token range.
@@ -511,8 +513,8 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
     const long cb = row * a.cap;
 
     // ---- fast path: whole key groups inside [0, min(nk, nv)) ----
-    const int f_hi = min(t_hi, q_end);
-    for (int t0 = t_lo + 32 * tl; t0 + 32 <= f_hi; t0 += 32 * NT) {
+    const int f_hi = FAST ? min(t_hi, q_end) : t_lo;
+    for (int t0 = t_lo + 32 * tl; FAST && t0 + 32 <= f_hi; t0 += 32 * NT) {
         float w[HPL][16], bk[HPL];
         {
             const long pidx = (row * (a.cap / 32) + t0 / 32) * D + ch0;
@@ -592,55 +594,83 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
         }
     }
 
-    // ---- generic path: the rest of the split, one token per lane group at a time ----
+    // ---- generic path: the rest of the split, GB tokens per lane group at a time (the loads of all are
+    // issued before any is worked, raw; a token past the range repeats the first).  Two in the kernel's
+    // own tail; one where the body is the residual slot of the matrix-core kernel, whose registers it
+    // would otherwise raise. ----
     const int g_lo = max(t_lo, f_hi);
-    for (int tok = g_lo + tl; tok < t_hi; tok += NT) {
-        float kf[16], vf[16];
-        if (tok < nk) {
-            float c[16], s16[16], z16[16];
-            codes16<KB>(load_codes16<KB>(a.c.k_codes + (cb + tok) * KROW, c8), c);
-            const long pidx = (row * (a.cap / 32) + tok / 32) * D + ch0;
-            const uint4* sp = reinterpret_cast<const uint4*>(U16(a.c.k_scale) + pidx);
-            const uint4* zp = reinterpret_cast<const uint4*>(U16(a.c.k_zero) + pidx);
-            half8(sp[0], s16); half8(sp[1], s16 + 8);
-            half8(zp[0], z16); half8(zp[1], z16 + 8);
+    constexpr int GB = FAST ? 2 : 1;
+    for (int tok0 = g_lo + tl; tok0 < t_hi; tok0 += GB * NT) {
+        uint4 kw[GB][4], vw[GB][2];               // key scale and zero (quantized) or key row; value row
+        Codes16<KB> kc[GB];
+        Codes16<VB> vc[GB];
+        uint16_t vs[GB], vz[GB];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) kf[j] = s16[j] * (c[j] - z16[j]);
-        } else {
-            const uint4* r = reinterpret_cast<const uint4*>(U16(a.c.k_res) + (row * a.ring + tok % a.ring) * D + ch0);
-            half8(r[0], kf); half8(r[1], kf + 8);
+        for (int j = 0; j < GB; ++j) {
+            const int tok = tok0 + j * NT < t_hi ? tok0 + j * NT : tok0;
+            if (tok < nk) {
+                kc[j] = load_codes16<KB>(a.c.k_codes + (cb + tok) * KROW, c8);
+                const long pidx = (row * (a.cap / 32) + tok / 32) * D + ch0;
+                const uint4* sp = reinterpret_cast<const uint4*>(U16(a.c.k_scale) + pidx);
+                const uint4* zp = reinterpret_cast<const uint4*>(U16(a.c.k_zero) + pidx);
+                kw[j][0] = sp[0]; kw[j][1] = sp[1]; kw[j][2] = zp[0]; kw[j][3] = zp[1];
+            } else {
+                const uint4* r = reinterpret_cast<const uint4*>(U16(a.c.k_res) + (row * a.ring + tok % a.ring) * D + ch0);
+                kw[j][0] = r[0]; kw[j][1] = r[1];
+            }
+            if (tok < nv) {
+                vc[j] = load_codes16<VB>(a.c.v_codes + (cb + tok) * VROW, c8);
+                vs[j] = U16(a.c.v_scale)[(cb + tok) * (D / 32) + vg];
+                vz[j] = U16(a.c.v_zero)[(cb + tok) * (D / 32) + vg];
+            } else {
+                const uint4* r = reinterpret_cast<const uint4*>(U16(a.c.v_res) + (row * a.ring + tok % a.ring) * D + ch0);
+                vw[j][0] = r[0]; vw[j][1] = r[1];
+            }
         }
-        if (tok < nv) {
-            float c[16];
-            codes16<VB>(load_codes16<VB>(a.c.v_codes + (cb + tok) * VROW, c8), c);
-            const float s1 = f16_to_f32(U16(a.c.v_scale)[(cb + tok) * (D / 32) + vg]);
-            const float z1 = f16_to_f32(U16(a.c.v_zero)[(cb + tok) * (D / 32) + vg]);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) vf[j] = s1 * (c[j] - z1);
-        } else {
-            const uint4* r = reinterpret_cast<const uint4*>(U16(a.c.v_res) + (row * a.ring + tok % a.ring) * D + ch0);
-            half8(r[0], vf); half8(r[1], vf + 8);
-        }
+        for (int j = 0; j < GB; ++j) {
+            const int tok = tok0 + j * NT;
+            if (tok >= t_hi) break;
+            float kf[16], vf[16];
+            if (tok < nk) {
+                float c[16], s16[16], z16[16];
+                codes16<KB>(kc[j], c);
+                half8(kw[j][0], s16); half8(kw[j][1], s16 + 8);
+                half8(kw[j][2], z16); half8(kw[j][3], z16 + 8);
 #pragma unroll
-        for (int u = 0; u < HPL; ++u) {
-            float qv[16];
-            load_q(u, qv);
-            float part = 0.f;
+                for (int i = 0; i < 16; ++i) kf[i] = s16[i] * (c[i] - z16[i]);
+            } else {
+                half8(kw[j][0], kf); half8(kw[j][1], kf + 8);
+            }
+            if (tok < nv) {
+                float c[16];
+                codes16<VB>(vc[j], c);
+                const float s1 = f16_to_f32(vs[j]), z1 = f16_to_f32(vz[j]);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) part = fmaf(qv[j], kf[j], part);
-            const float s = sum8(part);
-            const float m_new = fmaxf(m[u], s);
-            const float alpha = __builtin_amdgcn_exp2f(m[u] - m_new), p = __builtin_amdgcn_exp2f(s - m_new);
-            l[u] = l[u] * alpha + p;
-            ob[u] *= alpha;
+                for (int i = 0; i < 16; ++i) vf[i] = s1 * (c[i] - z1);
+            } else {
+                half8(vw[j][0], vf); half8(vw[j][1], vf + 8);
+            }
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[u][j] = fmaf(p, vf[j], o[u][j] * alpha);
-            m[u] = m_new;
+            for (int u = 0; u < HPL; ++u) {
+                float qv[16];
+                load_q(u, qv);
+                float part = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) part = fmaf(qv[i], kf[i], part);
+                const float sc = sum8(part);
+                const float m_new = fmaxf(m[u], sc);
+                const float alpha = __builtin_amdgcn_exp2f(m[u] - m_new), p = __builtin_amdgcn_exp2f(sc - m_new);
+                l[u] = l[u] * alpha + p;
+                ob[u] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[u][i] = fmaf(p, vf[i], o[u][i] * alpha);
+                m[u] = m_new;
+            }
         }
     }
 
     // ---- combine the lane groups of each query head, one head of every set per round ----
-    __shared__ float red[NLG][D + 2];
 #pragma unroll
     for (int u = 0; u < HPL; ++u) {
         if (u > 0) __syncthreads();                  // the previous round has read red
@@ -673,24 +703,417 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
     }
 }
 
-__global__ void kivi_merge_kernel(const float* __restrict__ po, const float* __restrict__ pl, int S, int D,
-                                  float* __restrict__ out, float* __restrict__ lse_out) {
-    const long n = blockIdx.x;
+template <int KB, int VB, int HPL>
+__global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, const uint16_t* __restrict__ q,
+                                                                   float scale_log2, int S_tot,
+                                                                   int max_len, float* __restrict__ po,
+                                                                   float* __restrict__ pl) {
+    __shared__ float red[kKiviLaneGroups][kKiviD + 2];
+    kivi_attn_rows<KB, VB, HPL>(a, q, scale_log2, S_tot, max_len, po, pl, blockIdx.x, blockIdx.y, blockIdx.z, red);
+}
+
+// ---------------------------------------------------------------------------
+// KIVI decode attention for grouped queries on the matrix cores (4 <= nrep <= 16 query heads per KV head, HPL
+// = 2 sets for the residual slot).  One workgroup per (split, KV head, request), 4 waves; wave w takes the key
+// groups (32 tokens, both sides quantized) w, w + 4, ... of the split and the last split slot runs the
+// per-token body above over the rows past them.  With W[n][c] = q_n[c] s_k[c] (exact: the product of two fp16
+// values is the sum of its fp16 rounding and the fma remainder, two chains) and the codes as exact fp16
+// integers,
+//   logit(t, n) = sm_scale (sum_c code[t][c] W[n][c] - sum_c z_k[c] W[n][c])          (KIVI page, keys)
+// is one v_mfma_f32_16x16x32_f16 chain per 16 tokens (rows = tokens, columns = the nrep heads, K = channels)
+// plus one chain with z_k as every row (the bias), and with P'_g[t][n] = p(t, n) s_v[t][g] (fp16),
+//   o[n][c] = sum_t code_v[t][c] P'_g[t][n] - sum_t z_v[t][g] P'_g[t][n],    g = c / 32   (values)
+// is one chain per 16 channels (rows = channels, columns = heads, K = the group's 32 tokens); the second
+// sum is kept per lane with dot2.  MFMA lane l = (n, kb) = (l & 15, l >> 4) holds row / column n and
+// k-slots 8 kb .. 8 kb + 7.
+//  - Keys: lane (m, kb) of a token tile holds token m's channels 32 kb .. 32 kb + 31 (one 8- or 16-byte
+//    load); a k-block takes their codes in the order the conversion gives them.  2-bit codes: x &
+//    0x33333333 (and the same of x >> 2) leaves one code per nibble and v_cvt_scalef32_pk_f16_fp4 turns
+//    the two nibbles of a byte into two exact fp16 values (an fp4 E2M1 nibble k < 4 is k / 2, scaled by
+//    2); 4-bit codes: one code per byte and v_cvt_scalef32_pk_f16_fp8 (an fp8 E4M3 byte k < 16 is
+//    k * 2^-9, scaled by 512).  So k-slot pair d of k-block kk holds channels 32 kb + gq_kchan(kk, d,
+//    0 / 1); W and z_k follow the same order (staged in LDS as pairs).
+//  - Values: the value contraction's k-slot s holds token gq_tok(s), chosen so that lane (n, kb) of the
+//    key tiles already holds the weights of slots 8 kb .. 8 kb + 7 (tile 0 rows 4 kb + i, tile 1 rows
+//    16 + 4 kb + i).  The key group's value codes are byte-transposed into LDS ([code byte][slot]: a lane
+//    loads one dword of four consecutive tokens and transposes the 4 x 4 bytes with v_perm), so a lane
+//    reads the 8 slots of one code byte with one 8-byte load; 16-channel tile (g, p) puts lane m on
+//    channel gq_vchan(g, p, m), all in value group g.
+// Online softmax per head in log2 units; a wave rescales only when some lane's maximum grew.  The waves'
+// states are combined through LDS.
+// ---------------------------------------------------------------------------
+typedef _Float16 kh8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 kh2_t __attribute__((ext_vector_type(2)));
+typedef float kf4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kGqWaves = 4;
+constexpr int kVtStride = 40;         // bytes per row of the transposed value codes (32 slots, padded)
+
+// channel (relative to 32 kb) of half e of k-slot pair d of k-block kk, key codes of BITS bits
+template <int BITS>
+__host__ __device__ constexpr int gq_kchan(int kk, int d, int e) {
+    return BITS == 2 ? 16 * (kk >> 1) + 4 * d + (kk & 1) + 2 * e : 8 * kk + 4 * (d & 1) + 2 * e + (d >> 1);
+}
+// channel of row m of value tile (g, p)
+template <int BITS>
+__host__ __device__ constexpr int gq_vchan(int g, int p, int m) {
+    return BITS == 2 ? 32 * g + 4 * (m & 7) + 2 * p + (m >> 3) : 32 * g + 16 * p + 2 * (m & 7) + (m >> 3);
+}
+// value k-slot of token tau of a key group, and back
+__host__ __device__ constexpr int gq_slot(int tau) { return 8 * ((tau & 15) >> 2) + 4 * (tau >> 4) + (tau & 3); }
+__host__ __device__ constexpr int gq_tok(int s) { return ((s & 4) << 2) + 4 * (s >> 3) + (s & 3); }
+
+// bytes 2W, 2W + 1 of x (values < 16: an fp8 E4M3 byte k < 16 is k * 2^-9) as fp16, times 2^-9 * scale
+template <int W>
+__device__ __forceinline__ uint32_t code_pair(uint32_t x, float scale = 512.f) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, scale, W != 0));
+}
+// the two nibbles of byte B of x (values < 4: an fp4 E2M1 nibble k < 4 is k / 2) as exact fp16
+template <int B>
+__device__ __forceinline__ uint32_t nib_pair(uint32_t x) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.f, B));
+}
+__device__ __forceinline__ float fmax2(float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); }
+// four 16-bit halves of w (16 dwords, natural order) as two dwords: halves r0, r1 -> one dword
+__device__ __forceinline__ uint32_t half_pair(const uint32_t* w, int r0, int r1) {
+    const uint32_t lo = (w[r0 >> 1] >> (16 * (r0 & 1))) & 0xffffu, hi = (w[r1 >> 1] >> (16 * (r1 & 1))) & 0xffffu;
+    return lo | (hi << 16);
+}
+
+struct GqStage {
+    unsigned char vt[64 * kVtStride];   // value codes [code byte][slot]
+    uint32_t skp[64], zkp[64];          // key scale / zero point pairs [kb][kk][d]
+    uint16_t sv[4][32], zv[4][32];      // value scale / zero point [group][slot]
+};
+union GqLds {
+    GqStage st[kGqWaves];
+    float cmb[kGqWaves][16][kKiviD + 2];
+    float red[kKiviLaneGroups][kKiviD + 2];
+};
+
+template <int KB, int VB>
+__global__ void __launch_bounds__(256, 2) kivi_attn_mfma_kernel(KArgs a, const uint16_t* __restrict__ q,
+                                                                float scale_log2, int S_tot, int max_len,
+                                                                float* __restrict__ po, float* __restrict__ pl) {
+    constexpr int D = kKiviD;
+    constexpr int KROW = D * KB / 8, VROW = D * VB / 8;
+    constexpr int KW = KB == 2 ? 2 : 4, VW = VB == 2 ? 4 : 8;    // key dwords per lane and tile, value dwords per lane
+    __shared__ __align__(16) GqLds lds;
+    // The residual slots take the first B * H workgroups, so that they all start in the first round beside
+    // the others (their per-token path is latency-bound); then (split, KV head, request), split fastest.
+    const int nq = S_tot - 1;
+    const int lin = blockIdx.x + S_tot * (blockIdx.y + gridDim.y * blockIdx.z), nres = gridDim.y * gridDim.z;
+    if (lin < nres) {
+        kivi_attn_rows<KB, VB, 2, false>(a, q, scale_log2, S_tot, max_len, po, pl, nq, lin % gridDim.y,
+                                         lin / gridDim.y, lds.red);
+        return;
+    }
+    const int split = (lin - nres) % nq, h = ((lin - nres) / nq) % gridDim.y, b = (lin - nres) / (nq * gridDim.y);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, kb = lane >> 4;
+    const int L = min(max(a.c.len[b], 0), max_len);
+    const int nk = min(a.c.n_kq[b], L), nv = min(a.c.n_vq[b], L);
+    const int q_end = min(nk, nv) & ~31;
+    const int tq = ((q_end + nq - 1) / nq + 31) & ~31;
+    const int t_lo = min(q_end, split * tq), t_hi = min(q_end, (split + 1) * tq);
+    const long row = long(b) * a.H + h;
+    const long cb = row * a.cap;
+    const int nch = (t_hi - t_lo) >> 5;
+    const int nmine = wave < nch ? (nch - wave + kGqWaves - 1) / kGqWaves : 0;
+    GqStage& st = lds.st[wave];
+
+    // the lane's query pairs (head n, channels 32 kb + gq_kchan), zero for n >= nrep
+    uint32_t qp[4][4];
+    {
+        uint32_t w[16];
+        const uint4* src = reinterpret_cast<const uint4*>(
+            q + ((long(b) * a.H + h) * a.nrep + min(n, a.nrep - 1)) * D + 32 * kb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = src[i];
+            w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                qp[kk][d] = n < a.nrep ? half_pair(w, gq_kchan<KB>(kk, d, 0), gq_kchan<KB>(kk, d, 1)) : 0u;
+    }
+    // staging positions of the lane's halves: key scale / zero channels 2 lane + e, value scale / zero of
+    // token lane >> 1, groups 2 (lane & 1) + e
+    int kpos[2], vpos[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int c = 2 * lane + e, kbc = c >> 5, r = c & 31;
+        int kk, d, ee;
+        if constexpr (KB == 2) {
+            ee = (r >> 1) & 1; kk = 2 * (r >> 4) + (r & 1); d = (r >> 2) & 3;
+        } else {
+            const int w = (r >> 2) & 1, u = r & 1;
+            ee = (r >> 1) & 1; kk = r >> 3; d = 2 * u + w;
+        }
+        kpos[e] = ((kbc * 4 + kk) * 4 + d) * 2 + ee;
+        vpos[e] = (2 * (lane & 1) + e) * 32 + gq_slot(lane >> 1);
+    }
+
+    struct Loads {
+        uint32_t kc[2][KW];
+        uint32_t sk, zk, sv, zv;
+        uint32_t vc[VW];
+    };
+    // per-lane byte offsets from the key group's first token (the bases are wave-uniform)
+    const int koff = n * KROW + 4 * KW * kb, voff = 4 * (lane >> 3) * VROW + 4 * (lane & 7);
+    auto issue = [&](int k, Loads& ld) {
+        const int t0 = __builtin_amdgcn_readfirstlane(t_lo + 32 * (wave + kGqWaves * min(k, nmine - 1)));
+        const uint8_t* kg = a.c.k_codes + (cb + t0) * KROW;
+        const uint8_t* vg = a.c.v_codes + (cb + t0) * VROW;
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            const uint8_t* kr = kg + 16 * T * KROW + koff;
+            if constexpr (KB == 2) {
+                const uint2 v = *reinterpret_cast<const uint2*>(kr);
+                ld.kc[T][0] = v.x; ld.kc[T][1] = v.y;
+            } else {
+                const uint4 v = *reinterpret_cast<const uint4*>(kr);
+                ld.kc[T][0] = v.x; ld.kc[T][1] = v.y; ld.kc[T][2] = v.z; ld.kc[T][3] = v.w;
+            }
+        }
+        const long gidx = (row * (a.cap / 32) + t0 / 32) * D;
+        ld.sk = reinterpret_cast<const uint32_t*>(U16(a.c.k_scale) + gidx)[lane];
+        ld.zk = reinterpret_cast<const uint32_t*>(U16(a.c.k_zero) + gidx)[lane];
+        ld.sv = reinterpret_cast<const uint32_t*>(U16(a.c.v_scale) + (cb + t0) * 4)[lane];
+        ld.zv = reinterpret_cast<const uint32_t*>(U16(a.c.v_zero) + (cb + t0) * 4)[lane];
+#pragma unroll
+        for (int i = 0; i < VW; ++i)     // token 4 (lane >> 3) + (i & 3), dword (lane & 7) + 8 (i >> 2)
+            ld.vc[i] = *reinterpret_cast<const uint32_t*>(vg + voff + (i & 3) * VROW + 32 * (i >> 2));
+    };
+    auto stage = [&](const Loads& ld) {
+        uint16_t* skh = reinterpret_cast<uint16_t*>(st.skp);
+        uint16_t* zkh = reinterpret_cast<uint16_t*>(st.zkp);
+        uint16_t* svh = &st.sv[0][0];
+        uint16_t* zvh = &st.zv[0][0];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            skh[kpos[e]] = uint16_t(ld.sk >> (16 * e));
+            zkh[kpos[e]] = uint16_t(ld.zk >> (16 * e));
+            svh[vpos[e]] = uint16_t(ld.sv >> (16 * e));
+            zvh[vpos[e]] = uint16_t(ld.zv >> (16 * e));
+        }
+        const int q4 = lane >> 3, sb = 8 * (q4 & 3) + 4 * (q4 >> 2);
+#pragma unroll
+        for (int hh = 0; hh < VW / 4; ++hh) {
+            const uint32_t x0 = ld.vc[4 * hh], x1 = ld.vc[4 * hh + 1], x2 = ld.vc[4 * hh + 2], x3 = ld.vc[4 * hh + 3];
+            const uint32_t p01l = __builtin_amdgcn_perm(x1, x0, 0x05010400u), p01h = __builtin_amdgcn_perm(x1, x0, 0x07030602u);
+            const uint32_t p23l = __builtin_amdgcn_perm(x3, x2, 0x05010400u), p23h = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+            const uint32_t y[4] = {__builtin_amdgcn_perm(p23l, p01l, 0x05040100u), __builtin_amdgcn_perm(p23l, p01l, 0x07060302u),
+                                   __builtin_amdgcn_perm(p23h, p01h, 0x05040100u), __builtin_amdgcn_perm(p23h, p01h, 0x07060302u)};
+            const int d = (lane & 7) + 8 * hh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(&st.vt[(4 * d + e) * kVtStride + sb]) = y[e];
+        }
+        asm volatile("" ::: "memory");
+    };
+
+    const uint32_t vmask = n < 8 ? 0x03030303u : 0x0c0c0c0cu;     // 2-bit value codes: see the value tiles
+    const float vscale = n < 8 ? 512.f : 128.f;
+    float m = -INFINITY, l = 0.f, vbias[4] = {0.f, 0.f, 0.f, 0.f};
+    kf4_t acc[4][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = kf4_t{0.f, 0.f, 0.f, 0.f};
+    const kf4_t zero4 = kf4_t{0.f, 0.f, 0.f, 0.f};
+
+    Loads cur, nxt;
+    if (nmine > 0) issue(0, cur);
+    for (int k = 0; k < nmine; ++k) {
+        stage(cur);
+        issue(k + 1, nxt);
+        // scores: bias chain and the two token tiles
+        kf4_t dz = zero4, dt[2] = {zero4, zero4};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const uint4 sp = *reinterpret_cast<const uint4*>(&st.skp[(kb * 4 + kk) * 4]);
+            const uint4 zp = *reinterpret_cast<const uint4*>(&st.zkp[(kb * 4 + kk) * 4]);
+            const uint32_t spw[4] = {sp.x, sp.y, sp.z, sp.w};
+            uint32_t wh[4], wl[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const kh2_t qh = __builtin_bit_cast(kh2_t, qp[kk][d]), sh = __builtin_bit_cast(kh2_t, spw[d]);
+                const kh2_t hi = qh * sh;
+                wh[d] = __builtin_bit_cast(uint32_t, hi);
+                wl[d] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qh, sh, -hi));
+            }
+            const kh8_t W = __builtin_bit_cast(kh8_t, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+            const kh8_t Wl = __builtin_bit_cast(kh8_t, make_uint4(wl[0], wl[1], wl[2], wl[3]));
+            dz = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(kh8_t, zp), Wl, dz, 0, 0, 0);
+            dz = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(kh8_t, zp), W, dz, 0, 0, 0);
+#pragma unroll
+            for (int T = 0; T < 2; ++T) {
+                uint32_t c[4];
+                if constexpr (KB == 2) {
+                    // byte d of y: channels 4 d + u' (low nibble) and 4 d + u' + 2 (high), u' = kk & 1
+                    const uint32_t X = cur.kc[T][kk >> 1];
+                    const uint32_t y = (kk & 1 ? X >> 2 : X) & 0x33333333u;
+                    c[0] = nib_pair<0>(y); c[1] = nib_pair<1>(y); c[2] = nib_pair<2>(y); c[3] = nib_pair<3>(y);
+                } else {
+                    const uint32_t X = cur.kc[T][kk];
+                    const uint32_t y0 = X & 0x0f0f0f0fu, y1 = (X >> 4) & 0x0f0f0f0fu;
+                    c[0] = code_pair<0>(y0); c[1] = code_pair<1>(y0); c[2] = code_pair<0>(y1); c[3] = code_pair<1>(y1);
+                }
+                const kh8_t Ac = __builtin_bit_cast(kh8_t, make_uint4(c[0], c[1], c[2], c[3]));
+                dt[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ac, Wl, dt[T], 0, 0, 0);
+                dt[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ac, W, dt[T], 0, 0, 0);
+            }
+        }
+        // online softmax (log2 units): lane (n, kb) holds tokens 4 kb + i (tile 0) and 16 + 4 kb + i (tile 1)
+        float mx = fmax2(fmax2(fmax2(dt[0][0], dt[0][1]), dt[0][2]), fmax2(fmax2(dt[0][3], dt[1][0]), dt[1][1]));
+        mx = fmax2(fmax2(mx, dt[1][2]), dt[1][3]);
+        mx = rows4_reduce(mx, [](float x, float y) { return fmax2(x, y); });
+        const float m_new = fmax2(m, scale_log2 * (mx - dz[0]));
+        if (__builtin_amdgcn_ballot_w64(m_new > m)) {
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                vbias[g] *= alpha;
+                acc[g][0] *= alpha;
+                acc[g][1] *= alpha;
+            }
+            m = m_new;
+        }
+        const float cz = fmaf(scale_log2, dz[0], m);
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(fmaf(scale_log2, dt[i >> 2][i & 3], -cz));
+            l += p[i];
+        }
+        uint32_t P[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const kh2_t v = {(_Float16)p[2 * d], (_Float16)p[2 * d + 1]};
+            P[d] = __builtin_bit_cast(uint32_t, v);
+        }
+        // values
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint4 sv = *reinterpret_cast<const uint4*>(&st.sv[g][8 * kb]);
+            const uint4 zv = *reinterpret_cast<const uint4*>(&st.zv[g][8 * kb]);
+            const uint32_t svw[4] = {sv.x, sv.y, sv.z, sv.w}, zvw[4] = {zv.x, zv.y, zv.z, zv.w};
+            uint32_t pg[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const kh2_t w = __builtin_bit_cast(kh2_t, P[d]) * __builtin_bit_cast(kh2_t, svw[d]);
+                pg[d] = __builtin_bit_cast(uint32_t, w);
+                vbias[g] = __builtin_amdgcn_fdot2(w, __builtin_bit_cast(kh2_t, zvw[d]), vbias[g], false);
+            }
+            const kh8_t Bg = __builtin_bit_cast(kh8_t, make_uint4(pg[0], pg[1], pg[2], pg[3]));
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                uint32_t y0, y1;
+                float vsc = 512.f;
+                if constexpr (VB == 2) {
+                    // channel u = 2 pp + (n >> 3) of the byte: bits 2 u; u odd is masked in place (byte values
+                    // 0, 4, 8, 12, converted with a quarter of the scale)
+                    const uint2 Y = *reinterpret_cast<const uint2*>(&st.vt[(8 * g + (n & 7)) * kVtStride + 8 * kb]);
+                    const uint32_t x0 = pp ? Y.x >> 4 : Y.x, x1 = pp ? Y.y >> 4 : Y.y;
+                    y0 = x0 & vmask; y1 = x1 & vmask;
+                    vsc = vscale;
+                } else {
+                    const uint2 Y = *reinterpret_cast<const uint2*>(&st.vt[(16 * g + 8 * pp + (n & 7)) * kVtStride + 8 * kb]);
+                    const int sh = 4 * (n >> 3);
+                    y0 = (Y.x >> sh) & 0x0f0f0f0fu; y1 = (Y.y >> sh) & 0x0f0f0f0fu;
+                }
+                const uint4 A = make_uint4(code_pair<0>(y0, vsc), code_pair<1>(y0, vsc), code_pair<0>(y1, vsc),
+                                           code_pair<1>(y1, vsc));
+                acc[g][pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(kh8_t, A), Bg, acc[g][pp], 0, 0, 0);
+            }
+        }
+        cur = nxt;
+    }
+
+    // ---- combine the waves: lane (n, kb) holds channels gq_vchan(g, p, 4 kb + i) of head n ----
+    l = rows4_reduce(l, [](float x, float y) { return x + y; });
+#pragma unroll
+    for (int g = 0; g < 4; ++g) vbias[g] = rows4_reduce(vbias[g], [](float x, float y) { return x + y; });
+    __syncthreads();                                  // every wave is done with its staging area
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds.cmb[wave][n][gq_vchan<VB>(g, pp, 4 * kb + i)] = acc[g][pp][i] - vbias[g];
+    if (kb == 0) {
+        lds.cmb[wave][n][D] = m;
+        lds.cmb[wave][n][D + 1] = l;
+    }
+    __syncthreads();
+    for (int e = tid; e < a.nrep * D; e += 256) {
+        const int hn = e / D, d = e % D;
+        const long orow = (row * a.nrep + hn) * S_tot + split;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kGqWaves; ++w) M = fmaxf(M, lds.cmb[w][hn][D]);
+        if (M == -INFINITY) {
+            po[orow * D + d] = 0.f;
+            if (d == 0) pl[orow] = -INFINITY;
+            continue;
+        }
+        float Ls = 0.f, ov = 0.f;
+#pragma unroll
+        for (int w = 0; w < kGqWaves; ++w) {
+            const float mw = lds.cmb[w][hn][D];
+            const float fw = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+            Ls += lds.cmb[w][hn][D + 1] * fw;
+            ov += lds.cmb[w][hn][d] * fw;
+        }
+        po[orow * D + d] = ov / Ls;
+        if (d == 0) pl[orow] = (M + log2f(Ls)) * kLn2;
+    }
+}
+
+// One wave per output row (request, query head): the splits' lse spread over the lanes for the maximum and
+// the sum, then the row's 128 channels two per lane, the loads of several splits in flight together.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__global__ void __launch_bounds__(256) kivi_merge_kernel(const float* __restrict__ po, const float* __restrict__ pl,
+                                                         int n_rows, int S, float* __restrict__ out,
+                                                         float* __restrict__ lse_out) {
+    constexpr int D = kKiviD;
+    const int lane = threadIdx.x & 63;
+    const long n = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (n >= n_rows) return;
     const float* lr = pl + n * S;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, lr[s]);
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, lr[s]);
+    M = wave_max(M);
     float L = 0.f;
     if (M != -INFINITY)
-        for (int s = 0; s < S; ++s) L += (lr[s] == -INFINITY) ? 0.f : __expf(lr[s] - M);
+        for (int s = lane; s < S; s += 64) L += (lr[s] == -INFINITY) ? 0.f : __expf(lr[s] - M);
+    L = wave_sum(L);
     const float lse = (M == -INFINITY) ? -INFINITY : M + __logf(L);
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float o = 0.f;
-        if (M != -INFINITY)
-            for (int s = 0; s < S; ++s)
-                if (lr[s] != -INFINITY) o += __expf(lr[s] - lse) * po[(n * S + s) * D + d];
-        out[n * D + d] = o;
+    float2 o = make_float2(0.f, 0.f);
+    if (M != -INFINITY) {
+        const float2* pp = reinterpret_cast<const float2*>(po + n * S * D) + lane;
+#pragma unroll 4
+        for (int s = 0; s < S; ++s) {
+            const float ls = lr[s];
+            const float2 v = pp[long(s) * (D / 2)];
+            const float w = ls == -INFINITY ? 0.f : __expf(ls - lse);
+            o.x += w * v.x;
+            o.y += w * v.y;
+        }
     }
-    if (lse_out && threadIdx.x == 0) lse_out[n] = lse;
+    reinterpret_cast<float2*>(out + n * D)[lane] = o;
+    if (lse_out && lane == 0) lse_out[n] = lse;
 }
 
 lvq_status validate_kivi(const kivi_geom* g, const kivi_cache* c) {
@@ -725,10 +1148,15 @@ KArgs make_args(const kivi_geom* g, const kivi_cache* c) {
     return a;
 }
 
+// grouped queries with 4 to 16 query heads per KV head take the matrix-core kernel
+bool kivi_use_mfma(const KArgs& a) { return a.res_slot && a.nrep >= 4 && a.nrep <= 16 && a.nrep % 2 == 0; }
+
 template <int KB, int VB>
 void launch_kivi_attn(int hpl, dim3 grid, hipStream_t stream, const KArgs& a, const uint16_t* q, float sl2,
                       int S_tot, int max_len, float* po, float* pl) {
-    if (hpl == 2)
+    if (kivi_use_mfma(a))
+        hipLaunchKernelGGL((kivi_attn_mfma_kernel<KB, VB>), grid, dim3(256), 0, stream, a, q, sl2, S_tot, max_len, po, pl);
+    else if (hpl == 2)
         hipLaunchKernelGGL((kivi_attn_partial_kernel<KB, VB, 2>), grid, dim3(256), 0, stream, a, q, sl2, S_tot, max_len, po, pl);
     else
         hipLaunchKernelGGL((kivi_attn_partial_kernel<KB, VB, 1>), grid, dim3(256), 0, stream, a, q, sl2, S_tot, max_len, po, pl);
@@ -846,6 +1274,7 @@ extern "C" lvq_status kivi_decode_attn(const kivi_geom* g, const void* q, const 
     else if (a.vb == 2) launch_kivi_attn<4, 2>(hpl, grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
     else launch_kivi_attn<4, 4>(hpl, grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
     if ((st = check_launch("kivi_decode_attn: partial")) != LVQ_OK) return st;
-    hipLaunchKernelGGL(kivi_merge_kernel, dim3(B * Hq), dim3(128), 0, stream, po, pl, S_tot, g->D, out, lse_out);
+    hipLaunchKernelGGL(kivi_merge_kernel, dim3(ceil_div(B * Hq, 4)), dim3(256), 0, stream, po, pl, B * Hq, S_tot, out,
+                       lse_out);
     return check_launch("kivi_decode_attn: merge");
 }
