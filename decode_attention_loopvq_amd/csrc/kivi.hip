@@ -23,7 +23,6 @@ struct KArgs {
     int D, H, G, R, cap, ring;
     int kb, vb;           // key and value code widths (2 or 4 bits)
     int nrep;             // query heads per KV head
-    bool res_slot;        // attention: the last split slot holds only the rows past the quantized key groups
     kivi_cache c;
 };
 
@@ -365,7 +364,8 @@ __global__ void decode_counters_kernel(KArgs a, int B) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode attention partial: grid (split, KV head h, B), 256 threads in 32 lane
+// Decode attention partial on the VALU, per token (the kernel for 32 query heads per KV head, and the body
+// of the residual slot of the matrix-core kernel further below): grid (split, KV head h, B), 256 threads in 32 lane
 // groups of 8; lane c of a group owns channels 16c .. 16c+15 (16 * bits bits
 // of codes per token: one dword at 2 bits, two at 4).  The nrep query heads of
 // KV head h share the workgroup in sets of HPL (2 when nrep is even, else 1): lane group lg
@@ -381,7 +381,7 @@ __global__ void decode_counters_kernel(KArgs a, int B) {
 // (rescaling its running softmax per batch):
 //   o_d += p_t s_t (c_td - z_t)  =  sum_t (p_t s_t) c_td - sum_t p_t s_t z_t,
 // the second sum kept once per lane.  Tokens past the quantized range (the
-// fp16 residual, a partial group) take a generic path, one token per lane
+// fp16 residual, a partial group) take a generic path, one or two tokens per lane
 // group at a time.  Each lane group keeps its own softmax state; those of one
 // query head are combined through LDS.
 // ---------------------------------------------------------------------------
@@ -469,19 +469,13 @@ __device__ __forceinline__ void kivi_attn_rows(const KArgs& a, const uint16_t* _
     const int nset = a.nrep / HPL, hset = lg % nset, tl = lg / nset, NT = NLG / nset;
     const int L = min(max(a.c.len[b], 0), max_len);
     const int nk = min(a.c.n_kq[b], L), nv = min(a.c.n_vq[b], L);
-    // With grouped queries (a.res_slot) splits 0 .. S_tot-2 share the whole key groups of [0, q_end) (both
-    // sides quantized) evenly and the last slot takes the rest (fp16 residual rows, a partial group), so
-    // that it runs beside the quantized splits instead of after one of them (a lane group walks those
-    // rows one at a time for all its heads).  Otherwise the S_tot splits share [0, L) in whole key
-    // groups and the last one also takes the rest.
+    // Splits 0 .. S_tot-2 share the whole key groups of [0, q_end) (both sides quantized) evenly and the last
+    // slot takes the rest (fp16 residual rows, a partial group), so that it runs beside the quantized splits
+    // instead of after one of them (a lane group walks those rows one at a time for all its heads).
     const int q_end = min(nk, nv) & ~31;
-    const int nq = a.res_slot ? S_tot - 1 : S_tot;
+    const int nq = S_tot - 1;
     int t_lo, t_hi;
-    if (!a.res_slot) {
-        const int tq = ((L + S_tot - 1) / S_tot + 31) & ~31;
-        t_lo = min(L, split * tq);
-        t_hi = min(L, (split + 1) * tq);
-    } else if (split < nq) {
+    if (split < nq) {
         const int tq = ((q_end + nq - 1) / nq + 31) & ~31;   // whole key groups per split
         t_lo = min(q_end, split * tq);
         t_hi = min(q_end, (split + 1) * tq);
@@ -713,8 +707,9 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
 }
 
 // ---------------------------------------------------------------------------
-// KIVI decode attention for grouped queries on the matrix cores (4 <= nrep <= 16 query heads per KV head, HPL
-// = 2 sets for the residual slot).  One workgroup per (split, KV head, request), 4 waves; wave w takes the key
+// KIVI decode attention on the matrix cores, for 1 to 16 query heads per KV head (nrep; the residual slot
+// runs the per-token body with HPL = 2 when nrep is even, else 1).  One workgroup per (split, KV head,
+// request), 4 waves; wave w takes the key
 // groups (32 tokens, both sides quantized) w, w + 4, ... of the split and the last split slot runs the
 // per-token body above over the rows past them.  With W[n][c] = q_n[c] s_k[c] (exact: the product of two fp16
 // values is the sum of its fp16 rounding and the fma remainder, two chains) and the codes as exact fp16
@@ -804,8 +799,12 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_mfma_kernel(KArgs a, const u
     const int nq = S_tot - 1;
     const int lin = blockIdx.x + S_tot * (blockIdx.y + gridDim.y * blockIdx.z), nres = gridDim.y * gridDim.z;
     if (lin < nres) {
-        kivi_attn_rows<KB, VB, 2, false>(a, q, scale_log2, S_tot, max_len, po, pl, nq, lin % gridDim.y,
-                                         lin / gridDim.y, lds.red);
+        if (a.nrep % 2)
+            kivi_attn_rows<KB, VB, 1, false>(a, q, scale_log2, S_tot, max_len, po, pl, nq, lin % gridDim.y,
+                                             lin / gridDim.y, lds.red);
+        else
+            kivi_attn_rows<KB, VB, 2, false>(a, q, scale_log2, S_tot, max_len, po, pl, nq, lin % gridDim.y,
+                                             lin / gridDim.y, lds.red);
         return;
     }
     const int split = (lin - nres) % nq, h = ((lin - nres) / nq) % gridDim.y, b = (lin - nres) / (nq * gridDim.y);
@@ -1137,36 +1136,38 @@ lvq_status validate_kivi(const kivi_geom* g, const kivi_cache* c) {
     return LVQ_OK;
 }
 
+// query heads per KV head
+int kivi_nrep(const kivi_geom* g) { return g->Hq ? g->Hq / g->H : 1; }
+
 KArgs make_args(const kivi_geom* g, const kivi_cache* c) {
     KArgs a;
     a.D = g->D; a.H = g->H; a.G = g->group; a.R = g->R; a.cap = g->cap; a.ring = g->R + g->group;
     a.kb = g->bits;
     a.vb = g->v_bits ? g->v_bits : g->bits;
-    a.nrep = g->Hq ? g->Hq / g->H : 1;
-    a.res_slot = a.nrep > 1;
+    a.nrep = kivi_nrep(g);
     a.c = *c;
     return a;
 }
 
-// grouped queries with 4 to 16 query heads per KV head take the matrix-core kernel
-bool kivi_use_mfma(const KArgs& a) { return a.res_slot && a.nrep >= 4 && a.nrep <= 16 && a.nrep % 2 == 0; }
+// up to 16 query heads per KV head take the matrix-core kernel (one MFMA column tile of heads), 32 the
+// per-token kernel
+bool kivi_use_mfma(const KArgs& a) { return a.nrep <= 16; }
 
 template <int KB, int VB>
-void launch_kivi_attn(int hpl, dim3 grid, hipStream_t stream, const KArgs& a, const uint16_t* q, float sl2,
-                      int S_tot, int max_len, float* po, float* pl) {
+void launch_kivi_attn(dim3 grid, hipStream_t stream, const KArgs& a, const uint16_t* q, float sl2, int S_tot,
+                      int max_len, float* po, float* pl) {
     if (kivi_use_mfma(a))
         hipLaunchKernelGGL((kivi_attn_mfma_kernel<KB, VB>), grid, dim3(256), 0, stream, a, q, sl2, S_tot, max_len, po, pl);
-    else if (hpl == 2)
+    else   // 32 query heads per KV head: two per lane group
         hipLaunchKernelGGL((kivi_attn_partial_kernel<KB, VB, 2>), grid, dim3(256), 0, stream, a, q, sl2, S_tot, max_len, po, pl);
-    else
-        hipLaunchKernelGGL((kivi_attn_partial_kernel<KB, VB, 1>), grid, dim3(256), 0, stream, a, q, sl2, S_tot, max_len, po, pl);
 }
 
 int choose_kivi_splits(const kivi_geom* g, int B, int max_len) {
     const int wgs = B * g->H;
     int s = ceil_div(1024, std::max(1, wgs));
-    // Splits of up to 2048 tokens (64 key groups, two per lane group): fewer, longer workgroups amortise the
-    // combine of the 32 lane groups (measured on the 4K batch-16 workload: 2 splits 69.7 us, 4 splits 75.5).
+    // About 1024 workgroups, splits of at most 2048 tokens (measured with the matrix-core kernel on the 4K
+    // batch-16 workloads: 2-bit, 32 KV heads: 1 split 75.4 us, 2 59.5, 4 59.9; 32 query heads over 8 KV
+    // heads: 4 splits 24.3, 8 24.5).
     s = std::max(s, ceil_div(max_len, 2048));
     s = std::min(s, std::max(1, ceil_div(max_len, 64)));
     return std::max(1, std::min(s, 1024));
@@ -1238,8 +1239,8 @@ extern "C" lvq_status kivi_append(const kivi_geom* g, const void* k_new, const v
 extern "C" size_t kivi_decode_attn_workspace(const kivi_geom* g, int32_t B, int32_t max_len, int32_t num_splits) {
     if (!g || B < 0 || max_len < 0 || num_splits < 0 || g->H <= 0 || g->D <= 0) return 0;
     if (g->Hq < 0 || (g->Hq && g->Hq % g->H)) return 0;
-    const bool res_slot = g->Hq > g->H;              // grouped queries: a slot of its own for the residual rows
-    const int S = (num_splits > 0 ? num_splits : choose_kivi_splits(g, B, max_len)) + (res_slot ? 1 : 0);
+    // the splits and one slot of its own for the rows past the whole key groups
+    const int S = (num_splits > 0 ? num_splits : choose_kivi_splits(g, B, max_len)) + 1;
     const size_t rows = size_t(B) * (g->Hq ? g->Hq : g->H) * S;     // (request, query head, split)
     return rows * g->D * sizeof(float) + rows * sizeof(float);
 }
@@ -1261,18 +1262,17 @@ extern "C" lvq_status kivi_decode_attn(const kivi_geom* g, const void* q, const 
     LVQ_REQUIRE(ws_bytes >= need, LVQ_ERR_WORKSPACE, "kivi_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
     KArgs a = make_args(g, c);
     const int Hq = g->H * a.nrep;
-    const int S_tot = S + (a.res_slot ? 1 : 0);                   // with grouped queries: + the residual slot
+    const int S_tot = S + 1;                                      // + the residual slot
     const size_t rows = size_t(B) * Hq * S_tot;
     float* po = static_cast<float*>(ws);
     float* pl = po + rows * g->D;
     const dim3 grid(S_tot, g->H, B);
     const auto* qp = static_cast<const uint16_t*>(q);
     const float sl2 = sm_scale * kLog2e;
-    const int hpl = a.nrep % 2 == 0 ? 2 : 1;       // heads per lane group
-    if (a.kb == 2 && a.vb == 2) launch_kivi_attn<2, 2>(hpl, grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
-    else if (a.kb == 2) launch_kivi_attn<2, 4>(hpl, grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
-    else if (a.vb == 2) launch_kivi_attn<4, 2>(hpl, grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
-    else launch_kivi_attn<4, 4>(hpl, grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
+    if (a.kb == 2 && a.vb == 2) launch_kivi_attn<2, 2>(grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
+    else if (a.kb == 2) launch_kivi_attn<2, 4>(grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
+    else if (a.vb == 2) launch_kivi_attn<4, 2>(grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
+    else launch_kivi_attn<4, 4>(grid, stream, a, qp, sl2, S_tot, max_len, po, pl);
     if ((st = check_launch("kivi_decode_attn: partial")) != LVQ_OK) return st;
     hipLaunchKernelGGL(kivi_merge_kernel, dim3(ceil_div(B * Hq, 4)), dim3(256), 0, stream, po, pl, B * Hq, S_tot, out,
                        lse_out);

@@ -512,11 +512,10 @@ LVQ_API size_t kivi_decode_attn_workspace(const kivi_geom* g, int32_t B, int32_t
  *  (Hq = H when the geometry's Hq is 0).  Query head j attends over KV head
  *  j / (Hq / H).
  *  max_len (host) bounds len[b]; num_splits 0 = the library's choice, else
- *  the number of splits of each request's tokens.  With grouped queries
- *  (Hq > H) the splits share only the key groups quantized on both sides and
- *  one more workgroup per (request, KV head) takes the rest (the fp16
- *  residual rows, a partial group); kivi_decode_attn_workspace then counts
- *  num_splits + 1 partial slots.
+ *  the number of splits of each request's tokens.  The splits share only the
+ *  key groups quantized on both sides and one more workgroup per (request,
+ *  KV head) takes the rest (the fp16 residual rows, a partial group);
+ *  kivi_decode_attn_workspace counts num_splits + 1 partial slots.
  */
 LVQ_API lvq_status kivi_decode_attn(const kivi_geom* g, const void* q, const kivi_cache* c, int32_t max_len,
                             float sm_scale, float* out, float* lse_out, void* ws, size_t ws_bytes,

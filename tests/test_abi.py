@@ -155,9 +155,11 @@ def test_kivi_rejects():
                dict(Hq=2 * 3), dict(Hq=-2)):
         bad = lvq.make_kivi_geom(H=2, **kw)
         assert f(C.byref(bad), FAKE, FAKE, strides, 1, 0, C.byref(c), 4, None) == UNSUPPORTED, kw
-    assert _lib.lib.kivi_decode_attn_workspace(C.byref(lvq.make_kivi_geom(H=2)), 4, 4096, 2) == 4 * 2 * 2 * 129 * 4
+    # 2 splits + the residual slot, per (request, query head)
+    assert _lib.lib.kivi_decode_attn_workspace(C.byref(lvq.make_kivi_geom(H=2)), 4, 4096, 2) == \
+        4 * 2 * (2 + 1) * (128 + 1) * 4
     assert _lib.lib.kivi_decode_attn_workspace(C.byref(lvq.make_kivi_geom(H=2, Hq=8)), 4, 4096, 2) == \
-        4 * 8 * (2 + 1) * (128 + 1) * 4          # grouped queries: 2 splits + the residual slot
+        4 * 8 * (2 + 1) * (128 + 1) * 4
     bad = lvq.make_kivi_geom(H=2, R=100)
     assert f(C.byref(bad), FAKE, FAKE, strides, 1, 0, C.byref(c), 4, None) == INVALID
     c.len = None
