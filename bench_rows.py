@@ -207,6 +207,21 @@ def attn_row(name, cfg_name, steps, reps, kscale=False, **over):
          token_heads_per_s=round(sum(p.lengths) * cfg.H / t, 1), **extra)
 
 
+def kivi_call(g, q, cache, max_len, sm_scale, out, ws):
+    """A prebuilt kivi_decode_attn call (ctypes arguments made once, as for the LoopVQ attention rows: the
+    binding's checks would add host time comparable to a call's GPU time)."""
+    import ctypes as C
+    import torch
+    from decode_attention_loopvq_amd._lib import lib
+    args = (C.byref(g), q.data_ptr(), C.byref(cache.c), int(max_len), C.c_float(sm_scale), out.data_ptr(), None,
+            ws.data_ptr(), ws.numel(), 0, int(cache.B), torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        if lib.kivi_decode_attn(*args) != 0:
+            raise RuntimeError(lib.lvq_last_error().decode())
+    return run
+
+
 def kivi_rows(reps):
     import torch
     import decode_attention_loopvq_amd as lvq
@@ -240,9 +255,7 @@ def kivi_rows(reps):
     # max_len: the longest request after the prefill (what a server knows on the host), not the capacity
     ws = torch.empty(lvq.kivi_decode_attn_workspace(g, cfg.B, cfg.L), dtype=torch.uint8, device="cuda")
 
-    def attn():
-        lvq.kivi_decode_attn(g, q, cache, cfg.L, synk.softmax_scale(cfg), out=out, ws=ws)
-
+    attn = kivi_call(g, q, cache, cfg.L, synk.softmax_scale(cfg), out, ws)
     t = timed(attn, reps * 10)
     per_bh = n_q * cfg.D // 4 * 2 + (n_q // cfg.group) * cfg.D * 4 + n_q * (cfg.D // cfg.group) * 4 \
         + cfg.R * cfg.D * 2 * 2
@@ -280,9 +293,7 @@ def kivi_variant_row(row, name, reps):
     out = torch.empty((cfg.B, Hq, cfg.D), dtype=torch.float32, device="cuda")
     ws = torch.empty(lvq.kivi_decode_attn_workspace(g, cfg.B, cfg.L), dtype=torch.uint8, device="cuda")
 
-    def attn():
-        lvq.kivi_decode_attn(g, p.q, p.cache, cfg.L, p.sm_scale, out=out, ws=ws)
-
+    attn = kivi_call(g, p.q, p.cache, cfg.L, p.sm_scale, out, ws)
     t = timed(attn, reps * 10)
     n_q = cfg.L - cfg.R
     per_kv = (n_q * cfg.D * kb // 8 + (n_q // cfg.group) * cfg.D * 4 + n_q * cfg.D * vb // 8
