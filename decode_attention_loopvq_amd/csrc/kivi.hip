@@ -1071,8 +1071,10 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_mfma_kernel(KArgs a, const u
     }
 }
 
-// One wave per output row (request, query head): the splits' lse spread over the lanes for the maximum and
-// the sum, then the row's 128 channels two per lane, the loads of several splits in flight together.
+// One wave per output row (request, query head), the row's 128 channels two per lane.  Up to 16 splits
+// every load of the row is issued at once (the splits' lse are the same for all lanes: scalar loads, the
+// maximum and the sum taken in every lane); more splits, the lse spread over the lanes for the maximum and
+// the sum, then the partial rows.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -1083,6 +1085,7 @@ __device__ __forceinline__ float wave_sum(float x) {
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
     return x;
 }
+constexpr int kMergeRegs = 16;
 __global__ void __launch_bounds__(256) kivi_merge_kernel(const float* __restrict__ po, const float* __restrict__ pl,
                                                          int n_rows, int S, float* __restrict__ out,
                                                          float* __restrict__ lse_out) {
@@ -1091,24 +1094,50 @@ __global__ void __launch_bounds__(256) kivi_merge_kernel(const float* __restrict
     const long n = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (n >= n_rows) return;
     const float* lr = pl + n * S;
-    float M = -INFINITY;
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, lr[s]);
-    M = wave_max(M);
-    float L = 0.f;
-    if (M != -INFINITY)
-        for (int s = lane; s < S; s += 64) L += (lr[s] == -INFINITY) ? 0.f : __expf(lr[s] - M);
-    L = wave_sum(L);
-    const float lse = (M == -INFINITY) ? -INFINITY : M + __logf(L);
+    const float2* pp = reinterpret_cast<const float2*>(po + n * S * D) + lane;
     float2 o = make_float2(0.f, 0.f);
-    if (M != -INFINITY) {
-        const float2* pp = reinterpret_cast<const float2*>(po + n * S * D) + lane;
+    float lse;
+    if (S <= kMergeRegs) {
+        float ls[kMergeRegs];
+        float2 v[kMergeRegs];
+#pragma unroll
+        for (int s = 0; s < kMergeRegs; ++s) {
+            ls[s] = s < S ? lr[s] : -INFINITY;
+            v[s] = s < S ? pp[long(s) * (D / 2)] : make_float2(0.f, 0.f);
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < kMergeRegs; ++s) M = fmaxf(M, ls[s]);
+        float L = 0.f;
+#pragma unroll
+        for (int s = 0; s < kMergeRegs; ++s) L += (ls[s] == -INFINITY) ? 0.f : __expf(ls[s] - M);
+        lse = (M == -INFINITY) ? -INFINITY : M + __logf(L);
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int s = 0; s < kMergeRegs; ++s) {
+                const float w = ls[s] == -INFINITY ? 0.f : __expf(ls[s] - lse);
+                o.x += w * v[s].x;
+                o.y += w * v[s].y;
+            }
+        }
+    } else {
+        float M = -INFINITY;
+        for (int s = lane; s < S; s += 64) M = fmaxf(M, lr[s]);
+        M = wave_max(M);
+        float L = 0.f;
+        if (M != -INFINITY)
+            for (int s = lane; s < S; s += 64) L += (lr[s] == -INFINITY) ? 0.f : __expf(lr[s] - M);
+        L = wave_sum(L);
+        lse = (M == -INFINITY) ? -INFINITY : M + __logf(L);
+        if (M != -INFINITY) {
 #pragma unroll 4
-        for (int s = 0; s < S; ++s) {
-            const float ls = lr[s];
-            const float2 v = pp[long(s) * (D / 2)];
-            const float w = ls == -INFINITY ? 0.f : __expf(ls - lse);
-            o.x += w * v.x;
-            o.y += w * v.y;
+            for (int s = 0; s < S; ++s) {
+                const float ls = lr[s];
+                const float2 v = pp[long(s) * (D / 2)];
+                const float w = ls == -INFINITY ? 0.f : __expf(ls - lse);
+                o.x += w * v.x;
+                o.y += w * v.y;
+            }
         }
     }
     reinterpret_cast<float2*>(out + n * D)[lane] = o;
