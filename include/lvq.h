@@ -515,7 +515,8 @@ LVQ_API size_t kivi_decode_attn_workspace(const kivi_geom* g, int32_t B, int32_t
  *  the number of splits of each request's tokens.  The splits share only the
  *  key groups quantized on both sides and one more workgroup per (request,
  *  KV head) takes the rest (the fp16 residual rows, a partial group);
- *  kivi_decode_attn_workspace counts num_splits + 1 partial slots.
+ *  kivi_decode_attn_workspace counts num_splits + 1 partial slots.  A
+ *  request holding no tokens gets out = 0, lse = -inf.
  */
 LVQ_API lvq_status kivi_decode_attn(const kivi_geom* g, const void* q, const kivi_cache* c, int32_t max_len,
                             float sm_scale, float* out, float* lse_out, void* ws, size_t ws_bytes,

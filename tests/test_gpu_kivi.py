@@ -231,3 +231,82 @@ def test_variant_workloads_full_size_sampled(name):
         _compare_state(prob.cache, prob.g, b, h, states[(b, h)])
     worst = _check_attn(prob, rows, states)
     _say(f"[kivi full] {name} worst rel err {worst:.3e}")
+
+
+def _pack(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[n][D] codes -> [n][D*b/8] bytes, channel d at bits b*(d % (8/b)) of byte d*b/8 (inverse of _unpack)."""
+    n, D = codes.shape
+    per = 8 // bits
+    out = np.zeros((n, D // per), dtype=np.uint8)
+    for u in range(per):
+        out |= (codes[:, u::per].astype(np.uint8) << (bits * u)).astype(np.uint8)
+    return out
+
+
+def _put_state(cache, g, b, h, st: kv.KiviState):
+    """Write one (request, KV head)'s state, as the oracle holds it, into the device cache (layout in lvq.h)."""
+    import decode_attention_loopvq_amd as lvq
+    kb, vb, _ = lvq.kivi_widths(g)
+    ring = g.R + g.group
+    nk, nv, L = st.n_kq, st.n_vq, st.length
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(cache.k_codes.device)
+    if nk:
+        cache.k_codes[b, h, :nk] = t(_pack(np.concatenate(st.k_codes), kb))
+        cache.k_scale[b, h, :nk // g.group] = t(np.stack(st.k_s).astype(np.float16))
+        cache.k_zero[b, h, :nk // g.group] = t(np.stack(st.k_z).astype(np.float16))
+    if nv:
+        cache.v_codes[b, h, :nv] = t(_pack(np.stack(st.v_codes), vb))
+        cache.v_scale[b, h, :nv] = t(np.stack(st.v_s).astype(np.float16))
+        cache.v_zero[b, h, :nv] = t(np.stack(st.v_z).astype(np.float16))
+    for j, p in enumerate(range(nk, L)):
+        cache.k_res[b, h, p % ring] = t(st.k_res[j])
+    for j, p in enumerate(range(nv, L)):
+        cache.v_res[b, h, p % ring] = t(st.v_res[j])
+
+
+# A ragged batch in one call ("core design": each request's quantized groups and fp16 residual): requests of
+# 1000, 5, 0, 300, 37 and 700 tokens, each (request, head) state built by the oracle's prefill and written
+# into the cache (the append path cannot make lengths differ within a batch).  Every query head against the
+# oracle; the empty request gives out = 0, lse = -inf.
+@pytest.mark.parametrize("bits,v_bits,Hq", [(2, 0, 0), (2, 0, 8), (4, 2, 4)], ids=["k2v2", "k2v2-gqa4", "k4v2-gqa2"])
+def test_ragged_batch_from_oracle_state(bits, v_bits, Hq):
+    import decode_attention_loopvq_amd as lvq
+    import synth.kivi as synk
+    lengths = [1000, 5, 0, 300, 37, 700]
+    B, H, L = len(lengths), 2, max(lengths)
+    cfg = kivi_config("kivi-b16-4k", B=B, H=H, L=L, bits=bits, v_bits=v_bits, Hq=Hq)
+    _say(f"[kivi ragged] k{bits} v{v_bits or bits} Hq={Hq or H} lengths {lengths}")
+    cap = ((L + 256 + cfg.group - 1) // cfg.group) * cfg.group
+    g = lvq.make_kivi_geom(D=cfg.D, H=H, bits=bits, group=cfg.group, R=cfg.R, cap=cap, v_bits=v_bits, Hq=Hq)
+    cache = lvq.KiviCache(g, B)
+    k, v = synk.raw_kv(cfg, "cpu")
+    q = synk.queries(cfg, "cuda")[0].contiguous()
+    sm = synk.softmax_scale(cfg)
+    states = {}
+    for b, Lb in enumerate(lengths):
+        for h in range(H):
+            st = kv.KiviState(D=cfg.D, group=cfg.group, R=cfg.R, bits=bits, v_bits=v_bits)
+            if Lb:
+                st.prefill(k[b, h, :Lb].numpy(), v[b, h, :Lb].numpy())
+            _put_state(cache, g, b, h, st)
+            states[(b, h)] = st
+        cache.len[b], cache.n_kq[b], cache.n_vq[b] = Lb, states[(b, 0)].n_kq, states[(b, 0)].n_vq
+    nrep = lvq.kivi_widths(g)[2] // H
+    worst = 0.0
+    for ns in (0, 1, 3):
+        lse = torch.empty((B, nrep * H), dtype=torch.float32, device="cuda")
+        out, _ = lvq.kivi_decode_attn(g, q, cache, L, sm, lse_out=lse, num_splits=ns)
+        torch.cuda.synchronize()
+        for b, Lb in enumerate(lengths):
+            for hq in range(nrep * H):
+                o = out[b, hq].double().cpu().numpy()
+                if Lb == 0:
+                    assert np.all(o == 0.0) and float(lse[b, hq]) == -np.inf, f"empty request {b}, head {hq}"
+                    continue
+                qv = q[b, hq].float().cpu().numpy().astype(np.float64)
+                o_ref, lse_ref = kv.attention(qv, states[(b, hq // nrep)], sm)
+                err = np.abs(o - o_ref).max() / np.abs(o_ref).max()
+                worst = max(worst, err)
+                assert err <= REL_TOL, f"request {b} (length {Lb}), head {hq}, splits {ns}: rel err {err:.3e}"
+                assert abs(float(lse[b, hq]) - lse_ref) <= 2e-3
+    _say(f"[kivi ragged] worst rel err {worst:.3e}")
