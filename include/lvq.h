@@ -517,6 +517,11 @@ LVQ_API size_t kivi_decode_attn_workspace(const kivi_geom* g, int32_t B, int32_t
  *  KV head) takes the rest (the fp16 residual rows, a partial group);
  *  kivi_decode_attn_workspace counts num_splits + 1 partial slots.  A
  *  request holding no tokens gets out = 0, lse = -inf.
+ *  Numerics: with up to 16 query heads per KV head the scores take each
+ *  query element times its channel's key scale as an fp16 product (held
+ *  exactly as a rounding plus its remainder), so |q[d] * s_k[d]| must stay
+ *  within the fp16 range (65504); the value sums take p * s_v in fp16.
+ *  Everything is accumulated in fp32.
  */
 LVQ_API lvq_status kivi_decode_attn(const kivi_geom* g, const void* q, const kivi_cache* c, int32_t max_len,
                             float sm_scale, float* out, float* lse_out, void* ws, size_t ws_bytes,
