@@ -709,9 +709,9 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
 // ---------------------------------------------------------------------------
 // KIVI decode attention on the matrix cores, for 1 to 16 query heads per KV head (nrep; the residual slot
 // runs the per-token body with HPL = 2 when nrep is even, else 1).  One workgroup per (split, KV head,
-// request), 4 waves; wave w takes the key
-// groups (32 tokens, both sides quantized) w, w + 4, ... of the split and the last split slot runs the
-// per-token body above over the rows past them.  With W[n][c] = q_n[c] s_k[c] (exact: the product of two fp16
+// request), 4 waves; wave w takes the key groups (32 tokens, both sides quantized) w, w + 4, ... of the
+// split, and the residual slot (the last split slot, run by the first B * H workgroups so that they all
+// start in the first round) runs the per-token body above over the rows past them.  With W[n][c] = q_n[c] s_k[c] (exact: the product of two fp16
 // values is the sum of its fp16 rounding and the fma remainder, two chains) and the codes as exact fp16
 // integers,
 //   logit(t, n) = sm_scale (sum_c code[t][c] W[n][c] - sum_c z_k[c] W[n][c])          (KIVI page, keys)
@@ -733,7 +733,9 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_partial_kernel(KArgs a, cons
 //    16 + 4 kb + i).  The key group's value codes are byte-transposed into LDS ([code byte][slot]: a lane
 //    loads one dword of four consecutive tokens and transposes the 4 x 4 bytes with v_perm), so a lane
 //    reads the 8 slots of one code byte with one 8-byte load; 16-channel tile (g, p) puts lane m on
-//    channel gq_vchan(g, p, m), all in value group g.
+//    channel gq_vchan(g, p, m), all in value group g.  Value codes go through the fp8 conversion: 2-bit
+//    codes at bits 2 u of a byte are masked in place for odd u (byte values 0, 4, 8, 12, a quarter of
+//    the scale) and shifted by 4 first for u >= 2.
 // Online softmax per head in log2 units; a wave rescales only when some lane's maximum grew.  The waves'
 // states are combined through LDS.
 // ---------------------------------------------------------------------------
@@ -749,6 +751,21 @@ template <int BITS>
 __host__ __device__ constexpr int gq_kchan(int kk, int d, int e) {
     return BITS == 2 ? 16 * (kk >> 1) + 4 * d + (kk & 1) + 2 * e : 8 * kk + 4 * (d & 1) + 2 * e + (d >> 1);
 }
+// the inverse: (kk * 4 + d) * 2 + e of channel r (relative to 32 kb)
+template <int BITS>
+__host__ __device__ constexpr int gq_kslot(int r) {
+    return BITS == 2 ? ((2 * (r >> 4) + (r & 1)) * 4 + ((r >> 2) & 3)) * 2 + ((r >> 1) & 1)
+                     : ((r >> 3) * 4 + 2 * (r & 1) + ((r >> 2) & 1)) * 2 + ((r >> 1) & 1);
+}
+template <int BITS>
+constexpr bool gq_kslots_inverse() {
+    for (int kk = 0; kk < 4; ++kk)
+        for (int d = 0; d < 4; ++d)
+            for (int e = 0; e < 2; ++e)
+                if (gq_kslot<BITS>(gq_kchan<BITS>(kk, d, e)) != (kk * 4 + d) * 2 + e) return false;
+    return true;
+}
+static_assert(gq_kslots_inverse<2>() && gq_kslots_inverse<4>(), "gq_kslot inverts gq_kchan");
 // channel of row m of value tile (g, p)
 template <int BITS>
 __host__ __device__ constexpr int gq_vchan(int g, int p, int m) {
@@ -757,6 +774,12 @@ __host__ __device__ constexpr int gq_vchan(int g, int p, int m) {
 // value k-slot of token tau of a key group, and back
 __host__ __device__ constexpr int gq_slot(int tau) { return 8 * ((tau & 15) >> 2) + 4 * (tau >> 4) + (tau & 3); }
 __host__ __device__ constexpr int gq_tok(int s) { return ((s & 4) << 2) + 4 * (s >> 3) + (s & 3); }
+constexpr bool gq_slots_inverse() {
+    for (int t = 0; t < 32; ++t)
+        if (gq_tok(gq_slot(t)) != t) return false;
+    return true;
+}
+static_assert(gq_slots_inverse(), "gq_slot and gq_tok are inverse permutations of the 32 tokens");
 
 // bytes 2W, 2W + 1 of x (values < 16: an fp8 E4M3 byte k < 16 is k * 2^-9) as fp16, times 2^-9 * scale
 template <int W>
@@ -769,7 +792,7 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t x) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.f, B));
 }
 __device__ __forceinline__ float fmax2(float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); }
-// four 16-bit halves of w (16 dwords, natural order) as two dwords: halves r0, r1 -> one dword
+// halves r0 and r1 of w (16 dwords, half i of dword i / 2 in natural order) as one dword, r0 in the low half
 __device__ __forceinline__ uint32_t half_pair(const uint32_t* w, int r0, int r1) {
     const uint32_t lo = (w[r0 >> 1] >> (16 * (r0 & 1))) & 0xffffu, hi = (w[r1 >> 1] >> (16 * (r1 & 1))) & 0xffffu;
     return lo | (hi << 16);
@@ -844,15 +867,8 @@ __global__ void __launch_bounds__(256, 2) kivi_attn_mfma_kernel(KArgs a, const u
     int kpos[2], vpos[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int c = 2 * lane + e, kbc = c >> 5, r = c & 31;
-        int kk, d, ee;
-        if constexpr (KB == 2) {
-            ee = (r >> 1) & 1; kk = 2 * (r >> 4) + (r & 1); d = (r >> 2) & 3;
-        } else {
-            const int w = (r >> 2) & 1, u = r & 1;
-            ee = (r >> 1) & 1; kk = r >> 3; d = 2 * u + w;
-        }
-        kpos[e] = ((kbc * 4 + kk) * 4 + d) * 2 + ee;
+        const int c = 2 * lane + e;
+        kpos[e] = 32 * (c >> 5) + gq_kslot<KB>(c & 31);     // [kb][kk][d] pairs, half e
         vpos[e] = (2 * (lane & 1) + e) * 32 + gq_slot(lane >> 1);
     }
 
