@@ -194,7 +194,8 @@ def test_prefill_strided_inputs(layout, bits, v_bits):
 # the oracle over its KV head.
 @pytest.mark.parametrize("bits,v_bits,H,Hq", [
     (4, 0, 2, 0), (4, 2, 2, 0), (2, 4, 2, 0), (2, 0, 2, 8), (4, 4, 1, 32), (2, 4, 2, 4), (4, 2, 1, 16),
-], ids=["k4v4", "k4v2", "k2v4", "k2v2-gqa4", "k4v4-gqa32", "k2v4-gqa2", "k4v2-gqa16"])
+    (4, 4, 2, 16),
+], ids=["k4v4", "k4v2", "k2v4", "k2v2-gqa4", "k4v4-gqa32", "k2v4-gqa2", "k4v2-gqa16", "k4v4-gqa8"])
 def test_widths_and_grouped_queries(bits, v_bits, H, Hq):
     import decode_attention_loopvq_amd as lvq
     import synth.kivi as synk
