@@ -311,3 +311,48 @@ def test_ragged_batch_from_oracle_state(bits, v_bits, Hq):
                 assert err <= REL_TOL, f"request {b} (length {Lb}), head {hq}, splits {ns}: rel err {err:.3e}"
                 assert abs(float(lse[b, hq]) - lse_ref) <= 2e-3
     _say(f"[kivi ragged] worst rel err {worst:.3e}")
+
+
+# Attention while the cache grows ("core design": appends flush whole key groups and single value rows):
+# a prefill of 150 tokens (R = 128: no key group is quantized on both sides yet, the residual slot takes
+# every row) and 100 single-token appends, attention checked against the oracle every 10 tokens at the
+# library's split count and at 3 splits, so the whole-key-group range and the residual slot move across
+# key flushes.
+@pytest.mark.parametrize("Hq", [0, 8], ids=["mha", "gqa4"])
+def test_attention_while_appending(Hq):
+    import decode_attention_loopvq_amd as lvq
+    import synth.kivi as synk
+    from tests import harness
+    cfg = kivi_config("kivi-b16-4k", B=2, H=2, L=150, Hq=Hq)
+    _say(f"[kivi grow] Hq={Hq or cfg.H}: prefill 150, 100 appends")
+    prob = harness.build_kivi(cfg, cap=((150 + 100 + 256 + 31) // 32) * 32)
+    rows = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    states = _states(prob, rows)
+    kn, vn = synk.new_tokens(cfg, 100, "cuda")
+    kn_h, vn_h = kn.cpu().numpy(), vn.cpu().numpy()
+    Hq_ = lvq.kivi_widths(prob.g)[2]
+    nrep = Hq_ // cfg.H
+    checked = 0
+    for i in range(100):
+        lvq.kivi_append(prob.g, kn[i][:, :, None, :], vn[i][:, :, None, :], prob.cache, prefill=False)
+        for (b, h) in rows:
+            states[(b, h)].append(kn_h[i, b, h], vn_h[i, b, h])
+        if (i + 1) % 10:
+            continue
+        L = int(prob.cache.len.max())
+        for ns in (0, 3):
+            lse = torch.empty((cfg.B, Hq_), dtype=torch.float32, device="cuda")
+            out, _ = lvq.kivi_decode_attn(prob.g, prob.q, prob.cache, L, prob.sm_scale, lse_out=lse, num_splits=ns)
+            torch.cuda.synchronize()
+            for (b, h) in rows:
+                for hq in range(h * nrep, (h + 1) * nrep):
+                    qv = prob.q[b, hq].float().cpu().numpy().astype(np.float64)
+                    o_ref, lse_ref = kv.attention(qv, states[(b, h)], prob.sm_scale)
+                    o = out[b, hq].double().cpu().numpy()
+                    err = np.abs(o - o_ref).max() / np.abs(o_ref).max()
+                    st = states[(b, h)]
+                    assert err <= REL_TOL, (f"after {i + 1} appends (L={st.length}, n_kq={st.n_kq}, n_vq={st.n_vq}), "
+                                            f"row ({b},{hq}), splits {ns}: rel err {err:.3e}")
+                    assert abs(float(lse[b, hq]) - lse_ref) <= 2e-3
+                    checked += 1
+    _say(f"[kivi grow] {checked} rows checked")
