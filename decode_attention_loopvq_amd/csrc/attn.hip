@@ -607,10 +607,16 @@ __global__ void __launch_bounds__(kIThreads, 2) index_attn_kernel(AttnArgs a) {
     const_ptr<uint32_t> qrow[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) qrow[j] = as_const(a.qpack + srow[j] * 64);
+    // The rows are loop-invariant, so the compiler would hoist all 128 dwords out of the chunk loop and
+    // park most of them in VGPR lanes (a v_readlane per use); the empty asm keeps each step's 16 loads
+    // in the step that issues them.
     auto load_q = [&](auto qc, auto jc, uint32_t (&qs)[16]) {
         constexpr int qq = decltype(qc)::value, j = decltype(jc)::value;
+        uint64_t pv = reinterpret_cast<uint64_t>(qrow[j]);
+        asm volatile("" : "+s"(pv));
+        const const_ptr<uint32_t> p = reinterpret_cast<const_ptr<uint32_t>>(pv);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) qs[u] = qrow[j][16 * qq + u];
+        for (int u = 0; u < 16; ++u) qs[u] = p[16 * qq + u];
     };
     float acc[R][2];
     float rmax[R];                                  // the lane's running maximum per request
