@@ -980,6 +980,24 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
             stage[i] = src[(e & 15) * K + (e >> 4)];
         }
     }
+    // The split's page-table entries (page ids, per request), also issued before the lengths: a request with
+    // work starts its range at the split's first page, so entry pp is page split * pps + pp of its row,
+    // clamped to the row (in bounds whatever the lengths); pages past a request's range are replaced by
+    // physical page 0 once the lengths are known, so that every pool load below reads valid memory (their
+    // tokens are masked).
+    constexpr int kPt = R * (kMaxSplitTok / 8) / NT;   // page-table entries per thread
+    static_assert(R * (kMaxSplitTok / 8) % NT == 0, "page-table fill");
+    uint32_t ptv[kPt];
+#pragma unroll
+    for (int i = 0; i < kPt; ++i) {
+        const int e = tid + NT * i;
+        const int j = e / (kMaxSplitTok / 8), pp = e % (kMaxSplitTok / 8);
+        int row = min(rq[0], a.B - 1);
+#pragma unroll
+        for (int jj = 1; jj < R; ++jj)
+            if (j == jj) row = min(rq[jj], a.B - 1);
+        ptv[i] = uint32_t(a.pt[long(row) * a.pt_stride + min(split * a.pps + pp, a.pt_stride - 1)]);
+    }
     static_assert(R * D / 2 == NT, "one query dword per thread");
     int qrow = rq[0];
 #pragma unroll
@@ -1002,6 +1020,8 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
         // lengths' wait instead of sinking them below this branch)
 #pragma unroll
         for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(stage[i].x));
+#pragma unroll
+        for (int i = 0; i < kPt; ++i) asm volatile("" ::"v"(ptv[i]));
         asm volatile("" ::"v"(qraw));
         for (int e = tid; e < R * D; e += NT) {
             const int j = e / D, d = e % D, rb = rq[j];
@@ -1020,24 +1040,16 @@ __global__ void __launch_bounds__(kIThreads, 2) index_mfma_kernel(AttnArgs a) {
             t_hi = max(t_hi, hi[j]);
         }
     }
-    // The split's page-table entries (page ids, per request: a page past a request's range holds its last index
-    // page, a request without index pages physical page 0, so that every load below reads valid memory).
-    constexpr int kPt = R * (kMaxSplitTok / 8) / NT;   // page-table entries per thread
-    static_assert(R * (kMaxSplitTok / 8) % NT == 0, "page-table fill");
-    uint32_t ptv[kPt];
+    // page ids past each request's range (its index tokens end at hi[j]) -> physical page 0
 #pragma unroll
     for (int i = 0; i < kPt; ++i) {
-        // one unconditional load from the table's base (page 0 of its row when the request has no index
-        // pages: in bounds, as some request of the workgroup has index pages, so rows hold >= 1 entry)
         const int e = tid + NT * i;
         const int j = e / (kMaxSplitTok / 8), pp = e % (kMaxSplitTok / 8);
-        int row = min(rq[0], a.B - 1), hij = hi[0];
+        int hij = hi[0];
 #pragma unroll
         for (int jj = 1; jj < R; ++jj)
-            if (j == jj) { row = min(rq[jj], a.B - 1); hij = hi[jj]; }
-        const int page = hij > 0 ? max(min(t_lo + 8 * pp, hij - 1), 0) >> 3 : 0;
-        const uint32_t v = uint32_t(a.pt[long(row) * a.pt_stride + page]);
-        ptv[i] = hij > 0 ? v : 0u;
+            if (j == jj) hij = hi[jj];
+        if (8 * (split * a.pps + pp) >= hij) ptv[i] = 0u;
     }
     // The lane's query: blocks f1 = ((2 kb) ^ n) & 7 and f2 = f1 ^ 1 of 8 frequencies, qa = the half of
     // slot 0's group, qb the partner half (read from qf16 once the first score loads are issued).
